@@ -1,0 +1,23 @@
+"""CPU oracle for the W4A16 GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite (tests/), the smoke check in __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import or call anything in this package.  The
+library and its Python binding never do: the product path runs entirely in the
+HIP kernels and fails loudly when they are missing.
+
+The oracle shares no code with the HIP path.  See w4a16_ref.py for the
+definitions it implements and the passages they follow.
+"""
+from .w4a16_ref import (  # noqa: F401
+    accept,
+    check_24,
+    dequant,
+    dequant_fp16,
+    error_bound,
+    gemm,
+    gemm_exact,
+    gemm_sampled,
+    unpack_codes_k,
+    unpack_codes_n,
+    zero_points,
+)

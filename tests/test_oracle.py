@@ -1,0 +1,480 @@
+"""Pins for the CPU oracle (runs without a GPU).
+
+Each test checks the oracle against something other than itself: hand-derived
+fixtures under tests/golden/, exhaustive tables, exact-rational brute force,
+closed forms and invariants.  test_planted_mistakes_are_caught plants the
+plausible mistakes (dropped term, wrong sign, wrong index, transposed operand)
+in copies of the oracle and shows that at least one pin fails for each.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import w4a16_ref as ref
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---- independent helpers (Python integers only) ------------------------------
+def words_from_codes_k(q):
+    """Pack [K, N] codes along K with Python integer arithmetic."""
+    K, N = q.shape
+    out = np.zeros((K // 8, N), dtype=np.int64)
+    for i in range(K // 8):
+        for n in range(N):
+            w = 0
+            for j in range(8):
+                w += int(q[8 * i + j, n]) * (16 ** j)
+            out[i, n] = w
+    return out.astype(np.uint32).view(np.int32)
+
+
+def words_from_codes_n(z):
+    G, N = z.shape
+    out = np.zeros((G, N // 8), dtype=np.int64)
+    for g in range(G):
+        for c in range(N // 8):
+            w = 0
+            for j in range(8):
+                w += int(z[g, 8 * c + j]) * (16 ** j)
+            out[g, c] = w
+    return out.astype(np.uint32).view(np.int32)
+
+
+def read_fixture(name):
+    d = {}
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            d[key] = vals
+    return d
+
+
+# ---- step 1/2: unpack -----------------------------------------------------------
+def test_nibble_words_fixture():
+    rows = []
+    with open(os.path.join(GOLD, "nibble_words.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                parts = line.split()
+                rows.append((int(parts[0], 16), [int(v) for v in parts[1:]]))
+    Qp = np.array([[w for w, _ in rows]], dtype=np.uint32).view(np.int32)  # [1, N]
+    q = oracle.unpack_codes_k(Qp, 8)
+    for n, (_, codes) in enumerate(rows):
+        assert list(q[:, n]) == codes
+    # the same words read as zero-point words (packed along N): codes run along columns
+    z = oracle.unpack_codes_n(Qp.reshape(len(rows), 1), 8)
+    for g, (_, codes) in enumerate(rows):
+        assert list(z[g, :]) == codes
+
+
+def test_unpack_every_value_every_position():
+    # word = v << 4j must give code v at row j and 0 elsewhere, for all v and j
+    words = []
+    expect = []
+    for j in range(8):
+        for v in range(16):
+            words.append((v << (4 * j)) & 0xFFFFFFFF)
+            e = [0] * 8
+            e[j] = v
+            expect.append(e)
+    Qp = np.array([words], dtype=np.uint32).view(np.int32)
+    q = oracle.unpack_codes_k(Qp, 8)
+    assert np.array_equal(q.T, np.array(expect, dtype=np.uint8))
+
+
+def test_unpack_all_halfword_patterns():
+    p = np.arange(1 << 16, dtype=np.uint32)
+    for shift, rows in ((0, range(0, 4)), (16, range(4, 8))):
+        Qp = (p << np.uint32(shift)).reshape(1, -1).view(np.int32)
+        q = oracle.unpack_codes_k(Qp, 8)
+        for j, r in enumerate(rows):
+            expect = np.array([(int(x) // (16 ** j)) % 16 for x in p], dtype=np.uint8)
+            assert np.array_equal(q[r], expect)
+        other = [r for r in range(8) if r not in rows]
+        assert not q[other].any()
+
+
+def test_pack_unpack_roundtrip_random():
+    rng = np.random.default_rng(7)
+    q = rng.integers(0, 16, size=(64, 24), dtype=np.uint8)
+    Qp = words_from_codes_k(q)
+    assert np.array_equal(oracle.unpack_codes_k(Qp, 64), q)
+    z = rng.integers(0, 16, size=(5, 24), dtype=np.uint8)
+    assert np.array_equal(oracle.unpack_codes_n(words_from_codes_n(z), 24), z)
+
+
+def test_generator_packing_matches_independent_packer():
+    # the shared input generator must produce the canonical format
+    from gen import pack_nibbles_along_k, pack_nibbles_along_n
+    rng = np.random.default_rng(11)
+    q = rng.integers(0, 16, size=(32, 16), dtype=np.uint8)
+    assert np.array_equal(pack_nibbles_along_k(q), words_from_codes_k(q))
+    z = rng.integers(0, 16, size=(3, 16), dtype=np.uint8)
+    assert np.array_equal(pack_nibbles_along_n(z), words_from_codes_n(z))
+
+
+# ---- step 3: dequant ---------------------------------------------------------
+SCALES = [1.0, 0.5, 0.002, 0.02, 0.0010004, 2.0 ** -14, 65504.0, 0.0999755859375]
+
+
+@pytest.mark.parametrize("sv", SCALES)
+def test_dequant_exhaustive_closed_form(sv):
+    # all 16 x 16 (q, z) pairs, one group of 128 rows x 16 columns, so row k holds q = k % 16
+    s16 = np.float16(sv)
+    K, N, g = 128, 16, 128
+    q = np.array([[k % 16] * N for k in range(K)], dtype=np.uint8)
+    z = np.array([list(range(16))], dtype=np.uint8)  # z[0, n] = n
+    Qp = words_from_codes_k(q)
+    Zp = words_from_codes_n(z)
+    s = np.full((1, N), s16, dtype=np.float16)
+    W = oracle.dequant(Qp, s, Zp, K, N, g)
+    for k in range(K):
+        for n in range(N):
+            exact = (Fraction(k % 16) - Fraction(n)) * Fraction(float(s16))
+            assert Fraction(W[k, n]) == exact
+    Wsym = oracle.dequant(Qp, s, None, K, N, g)
+    for k in range(16):
+        assert Fraction(Wsym[k, 0]) == (Fraction(k) - 8) * Fraction(float(s16))
+
+
+def test_dequant_group_indexing():
+    # scale of group G applies exactly to rows G*g .. G*g+g-1
+    K, N, g = 384, 8, 128
+    q = np.full((K, N), 9, dtype=np.uint8)  # q - 8 = 1
+    s = np.array([[1.0] * N, [2.0] * N, [4.0] * N], dtype=np.float16)
+    W = oracle.dequant(words_from_codes_k(q), s, None, K, N, g)
+    assert np.all(W[:128] == 1.0) and np.all(W[128:256] == 2.0) and np.all(W[256:] == 4.0)
+
+
+def test_dequant_fp16_is_rne_of_exact():
+    # (q - z) * s rounded once to fp16; 3 * 0.0999755859375 lies between two fp16 values
+    K, N, g = 128, 8, 128
+    q = np.full((K, N), 11, dtype=np.uint8)
+    s = np.full((1, N), np.float16(0.0999755859375), dtype=np.float16)
+    W16 = oracle.dequant_fp16(words_from_codes_k(q), s, None, K, N, g)
+    exact = 3 * Fraction(float(np.float16(0.0999755859375)))
+    lo = np.float16(float(exact))
+    # check it is one of the two neighbours and the nearer one
+    cands = [lo, np.nextafter(lo, np.float16(1)), np.nextafter(lo, np.float16(0))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - exact), int(c.view(np.uint16)) & 1))
+    assert W16[0, 0] == best
+
+
+# ---- steps 4-5: products -------------------------------------------------------
+@pytest.mark.parametrize("M,K,N,asym,g", [(1, 128, 8, False, 128), (3, 256, 16, True, 128),
+                                          (16, 128, 8, True, 128), (2, 256, 8, False, 256)])
+def test_gemm_vs_exact_rationals(M, K, N, asym, g):
+    rng = np.random.default_rng(M * 1000 + K + N)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    Qp = words_from_codes_k(q)
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    Zp = words_from_codes_n(rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)) if asym else None
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    Y = oracle.gemm(X, Qp, s, Zp, g)
+    B = oracle.error_bound(X, Qp, s, Zp, g)
+    E = oracle.gemm_exact(X, Qp, s, Zp, g)
+    for m in range(M):
+        for n in range(N):
+            err = abs(Fraction(Y[m, n]) - E[m][n])
+            assert err <= Fraction((K + 2) * 2.0 ** -53) * Fraction(B[m, n])
+
+
+def test_golden_colsum():
+    d = read_fixture("colsum_k128.txt")
+    K, N = int(d["K"][0]), int(d["N"][0])
+    q = np.array([[(k + n) % 16 for n in range(N)] for k in range(K)], dtype=np.uint8)
+    s = np.full((1, N), float(d["s"][0]), dtype=np.float16)
+    X = np.ones((1, K), dtype=np.float16)
+    Y = oracle.gemm(X, words_from_codes_k(q), s, None, int(d["group"][0]))
+    assert np.array_equal(Y[0], np.array([float(v) for v in d["Y"]]))
+
+
+def test_golden_asym_onehot():
+    d = read_fixture("asym_onehot.txt")
+    K, N, g = int(d["K"][0]), int(d["N"][0]), int(d["group"][0])
+    q = np.array([[15 - n for n in range(N)] for _ in range(K)], dtype=np.uint8)
+    Zp = np.array([[0], [int(d["Zp_row1_hex"][0], 16)]], dtype=np.uint32).view(np.int32)
+    s = np.array([[1.0] * N, [0.25] * N], dtype=np.float16)
+    X = np.zeros((1, K), dtype=np.float16)
+    X[0, int(d["onehot_k"][0])] = 1
+    Y = oracle.gemm(X, words_from_codes_k(q), s, Zp, g)
+    assert np.array_equal(Y[0], np.array([float(v) for v in d["Y"]]))
+
+
+def test_onehot_rows_select_weight_rows():
+    # X = e_k selects row k of W: pins which k and which n every nibble means
+    K, N, g = 256, 16, 128
+    q = np.array([[(3 * k + 5 * n) % 16 for n in range(N)] for k in range(K)], dtype=np.uint8)
+    rng = np.random.default_rng(3)
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    ks = [0, 1, 7, 8, 127, 128, 200, 255]
+    X = np.zeros((len(ks), K), dtype=np.float16)
+    for m, k in enumerate(ks):
+        X[m, k] = 1
+    Y = oracle.gemm(X, words_from_codes_k(q), s, None, g)
+    for m, k in enumerate(ks):
+        for n in range(N):
+            assert Y[m, n] == ((3 * k + 5 * n) % 16 - 8) * float(s[k // g, n])
+
+
+def test_integer_matmul_special_case():
+    # s = 1, z = 8, one group spanning K: Y = X (Q - 8), an integer matmul
+    K, N, M = 256, 16, 4
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    Xi = rng.integers(-4, 5, size=(M, K))
+    Y = oracle.gemm(Xi.astype(np.float16), words_from_codes_k(q), np.ones((1, N), np.float16), None, K)
+    assert np.array_equal(Y, (Xi @ (q.astype(np.int64) - 8)).astype(np.float64))
+
+
+def test_zero_weights_give_exact_zero():
+    K, N, M, g = 256, 16, 3, 128
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    Y = oracle.gemm(X, words_from_codes_k(np.full((K, N), 8, np.uint8)), s, None, g)
+    assert np.all(Y == 0)
+    z = rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)
+    q = z[np.arange(K) // g, :]
+    Y = oracle.gemm(X, words_from_codes_k(q), s, words_from_codes_n(z), g)
+    assert np.all(Y == 0)
+
+
+def test_scale_power_of_two_is_exact():
+    K, N, M, g = 512, 16, 5, 128
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    Y1 = oracle.gemm(X, Qp, s, None, g)
+    for j in (1, 3, -2):
+        Yj = oracle.gemm(X, Qp, (s.astype(np.float32) * 2.0 ** j).astype(np.float16), None, g)
+        assert np.array_equal(Yj, Y1 * 2.0 ** j)
+
+
+def test_linear_in_x_exact():
+    K, N, g = 128, 8, 128
+    rng = np.random.default_rng(17)
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    s = rng.uniform(0.002, 0.02, size=(1, N)).astype(np.float16)
+    X1 = rng.integers(-8, 9, size=(1, K)).astype(np.float16)
+    X2 = rng.integers(-8, 9, size=(1, K)).astype(np.float16)
+    a, b = 3, -2
+    X3 = (a * X1.astype(np.float64) + b * X2.astype(np.float64)).astype(np.float16)
+    E1, E2, E3 = (oracle.gemm_exact(X, Qp, s, None, g) for X in (X1, X2, X3))
+    for n in range(N):
+        assert E3[0][n] == a * E1[0][n] + b * E2[0][n]
+    Y1, Y2, Y3 = (oracle.gemm(X, Qp, s, None, g) for X in (X1, X2, X3))
+    Bd = oracle.error_bound(X3, Qp, s, None, g)
+    assert np.all(np.abs(Y3 - (a * Y1 + b * Y2)) <= 4 * (K + 2) * 2.0 ** -53 * (Bd + 1))
+
+
+def test_row_permutation():
+    K, N, M, g = 256, 16, 6, 128
+    rng = np.random.default_rng(19)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    P = rng.permutation(M)
+    Y = oracle.gemm(X, Qp, s, None, g)
+    YP = oracle.gemm(X[P], Qp, s, None, g)
+    B = oracle.error_bound(X, Qp, s, None, g)
+    assert np.all(np.abs(YP - Y[P]) <= (K + 2) * 2.0 ** -53 * B[P])
+
+
+def test_sampled_matches_full():
+    K, N, M, g = 256, 32, 7, 128
+    rng = np.random.default_rng(23)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    Zp = words_from_codes_n(rng.integers(0, 16, size=(K // g, N), dtype=np.uint8))
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    Y = oracle.gemm(X, Qp, s, Zp, g)
+    B = oracle.error_bound(X, Qp, s, Zp, g)
+    rows, cols = [0, 3, 6], [1, 8, 31, 17]
+    Ys, Bs = oracle.gemm_sampled(X, Qp, s, Zp, g, rows, cols)
+    assert np.array_equal(Ys, Y[np.ix_(rows, cols)])
+    assert np.array_equal(Bs, B[np.ix_(rows, cols)])
+
+
+# ---- step 6: acceptance ------------------------------------------------------
+def _case(M=8, K=1024, N=64, g=128, seed=29):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    return X, Qp, s, g
+
+
+def test_accept_admits_fp32_accumulation_with_fp16_weights():
+    # an implementation that rounds W to fp16, sums in fp32 and rounds Y to fp16
+    X, Qp, s, g = _case()
+    K, N = X.shape[1], Qp.shape[1]
+    W16 = oracle.dequant_fp16(Qp, s, None, K, N, g).astype(np.float32)
+    acc = np.zeros((X.shape[0], N), np.float32)
+    for k in range(K):  # sequential fp32 accumulation, worst-case-ish order
+        acc += X[:, k:k + 1].astype(np.float32) * W16[k:k + 1, :]
+    Y = acc.astype(np.float16)
+    ok, info = oracle.accept(Y, oracle.gemm(X, Qp, s, None, g), oracle.error_bound(X, Qp, s, None, g))
+    assert ok, info
+
+
+def test_accept_rejects_wrong_results():
+    X, Qp, s, g = _case()
+    Yref = oracle.gemm(X, Qp, s, None, g)
+    B = oracle.error_bound(X, Qp, s, None, g)
+    Y = Yref.astype(np.float16)
+    assert oracle.accept(Y, Yref, B)[0]
+    bad = Y.copy()
+    bad[3, 5] = np.float16(float(bad[3, 5]) + 0.05 * float(B[3, 5]) + 0.01)
+    assert not oracle.accept(bad, Yref, B)[0]
+    nan = Y.copy()
+    nan[0, 0] = np.nan
+    assert not oracle.accept(nan, Yref, B)[0]
+    # dropping the last group is a 1/8 relative error: rejected
+    K = X.shape[1]
+    Xt = X.copy()
+    Xt[:, K - g:] = 0
+    assert not oracle.accept(oracle.gemm(Xt, Qp, s, None, g).astype(np.float16), Yref, B)[0]
+
+
+def test_check_24():
+    K, N = 128, 8
+    q = np.full((K, N), 8, np.uint8)
+    q[0, :] = 3
+    q[1, :] = 15  # 2 nonzero in the first run
+    assert oracle.check_24(words_from_codes_k(q), K)
+    q[2, 4] = 1  # 3 nonzero in the run of column 4
+    assert not oracle.check_24(words_from_codes_k(q), K)
+
+
+def test_generator_24_structure_and_distribution():
+    from gen import Workload, weights
+    w = Workload(cfg=4, M=16, K=256, N=64, sparse24=True)
+    d = weights(w)
+    assert oracle.check_24(d["Qp"], w.K)
+    keep = d["keep"].reshape(w.K // 4, 4, w.N)
+    assert np.all(keep.sum(axis=1) == 2)
+    assert np.all(d["q"][~d["keep"]] == 8)
+
+
+# ---- planted mistakes --------------------------------------------------------
+def _pins_pass(mod):
+    """Run a subset of the pins above against a (possibly mutated) oracle module."""
+    checks = []
+    # one-hot selection
+    K, N, g = 256, 16, 128
+    q = np.array([[(3 * k + 5 * n) % 16 for n in range(N)] for k in range(K)], dtype=np.uint8)
+    s = np.random.default_rng(3).uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    X = np.zeros((3, K), dtype=np.float16)
+    ks = [1, 130, 255]
+    for m, k in enumerate(ks):
+        X[m, k] = 1
+    Y = mod.gemm(X, words_from_codes_k(q), s, None, g)
+    checks.append(all(Y[m, n] == ((3 * k + 5 * n) % 16 - 8) * float(s[k // g, n])
+                      for m, k in enumerate(ks) for n in range(N)))
+    # asym golden
+    d = read_fixture("asym_onehot.txt")
+    K2, N2 = int(d["K"][0]), int(d["N"][0])
+    q2 = np.array([[15 - n for n in range(N2)] for _ in range(K2)], dtype=np.uint8)
+    Zp = np.array([[0], [0x76543210]], dtype=np.uint32).view(np.int32)
+    s2 = np.array([[1.0] * N2, [0.25] * N2], dtype=np.float16)
+    X2 = np.zeros((1, K2), dtype=np.float16)
+    X2[0, 130] = 1
+    Y2 = mod.gemm(X2, words_from_codes_k(q2), s2, Zp, 128)
+    checks.append(np.array_equal(Y2[0], np.array([float(v) for v in d["Y"]])))
+    # non-square tiny brute force
+    rng = np.random.default_rng(31)
+    M3, K3, N3 = 2, 256, 8
+    X3 = rng.standard_normal((M3, K3)).astype(np.float16)
+    Qp3 = words_from_codes_k(rng.integers(0, 16, size=(K3, N3), dtype=np.uint8))
+    s3 = rng.uniform(0.002, 0.02, size=(2, N3)).astype(np.float16)
+    Y3 = mod.gemm(X3, Qp3, s3, None, 128)
+    E3 = oracle.gemm_exact(X3, Qp3, s3, None, 128)
+    checks.append(all(abs(Fraction(Y3[m, n]) - E3[m][n]) < Fraction(1, 10 ** 9)
+                      for m in range(M3) for n in range(N3)))
+    return all(checks)
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    import types
+    assert _pins_pass(ref)
+
+    def mutant(**overrides):
+        m = types.ModuleType("mutant")
+        m.__dict__.update({k: getattr(ref, k) for k in dir(ref) if not k.startswith("__")})
+        m.__dict__.update(overrides)
+        # rebind the functions so that they see the overrides
+        for name in ("dequant", "gemm"):
+            f = getattr(ref, name)
+            if name not in overrides:
+                m.__dict__[name] = types.FunctionType(f.__code__, m.__dict__, name, f.__defaults__)
+        return m
+
+    def unpack_msb_first(Qp, K, cols=None):
+        U = np.ascontiguousarray(Qp).view(np.uint32)
+        if cols is not None:
+            U = U[:, np.asarray(cols)]
+        q = np.empty((K, U.shape[1]), dtype=np.uint8)
+        for k in range(8):
+            q[k::8] = ((U >> np.uint32(4 * (7 - k))) & np.uint32(15)).astype(np.uint8)
+        return q
+
+    def unpack_signed(Qp, K, cols=None):  # arithmetic shift on int32: wrong high nibble handling
+        U = np.ascontiguousarray(Qp).view(np.int32).astype(np.int64)
+        if cols is not None:
+            U = U[:, np.asarray(cols)]
+        q = np.empty((K, U.shape[1]), dtype=np.uint8)
+        for k in range(8):
+            q[k::8] = ((U >> (4 * k)) & (15 if k < 7 else 7)).astype(np.uint8)
+        return q
+
+    def zero_points_sign(G, N, Zp):
+        z = ref.zero_points(G, N, Zp)
+        return (16 - z.astype(np.int64)).astype(np.uint8) % 16
+
+    def zero_points_transposed(G, N, Zp):
+        if Zp is None:
+            return np.full((G, N), 8, dtype=np.uint8)
+        z = ref.unpack_codes_n(Zp, N)
+        return z[::-1].copy()
+
+    def dequant_drop_zero(Qp, s, Zp, K, N, group, cols=None):
+        q = ref.unpack_codes_k(Qp, K, cols).astype(np.float64)
+        s64 = np.asarray(s, dtype=np.float16).astype(np.float64)
+        if cols is not None:
+            s64 = s64[:, np.asarray(cols)]
+        return q * s64[np.arange(K) // group, :]
+
+    def dequant_wrong_group(Qp, s, Zp, K, N, group, cols=None):
+        q = ref.unpack_codes_k(Qp, K, cols).astype(np.float64)
+        z = ref.zero_points(K // group, N, Zp).astype(np.float64)
+        s64 = np.asarray(s, dtype=np.float16).astype(np.float64)
+        r = np.minimum(np.arange(K) // (group * 2), K // group - 1)
+        return (q - z[r, :]) * s64[r, :]
+
+    def gemm_transposed_operand(X, Qp, s, Zp, group, rows_per_chunk=1024):
+        K = X.shape[1]
+        N = Qp.shape[1]
+        W = ref.dequant(Qp, s, Zp, K, N, group)
+        W = W.reshape(N, K).T if W.shape[0] == W.shape[1] else W[::-1]
+        return X.astype(np.float64) @ W
+
+    mutants = [
+        mutant(unpack_codes_k=unpack_msb_first),
+        mutant(unpack_codes_k=unpack_signed),
+        mutant(zero_points=zero_points_sign),
+        mutant(zero_points=zero_points_transposed),
+        mutant(dequant=dequant_drop_zero),
+        mutant(dequant=dequant_wrong_group),
+        mutant(gemm=gemm_transposed_operand),
+    ]
+    for i, m in enumerate(mutants):
+        assert not _pins_pass(m), f"mutant {i} survived the pins"
