@@ -1,0 +1,143 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) W4A16 mixed-precision GEMM library.
+ *
+ * Computes Y[M,N] = X[M,K] * dequant(W), X and Y fp16, W 4-bit codes with one
+ * fp16 scale (and optionally one 4-bit zero-point) per group of `group`
+ * consecutive K per output column, accumulated in fp32.
+ *
+ * Pages this interface follows (all three describe the Marlin FP16xINT4 kernel):
+ *   [P1] "Marlin", Spark Notes, dingiv.github.io/ai/compute/kernel/marlin
+ *   [P2] "Marlin / GPTQ-Marlin", brain.gartu.xyz/ia/llm/quantification/optimisations/marlin/
+ *   [P3] "Marlin Project Overview", vecbase.com/en/p/IST-DASLab/marlin
+ *
+ * General rules for every entry point below:
+ *   - Pointers named as "device" must be device memory on the current HIP
+ *     device (hipMalloc, or a torch CUDA tensor).  The caller allocates and
+ *     frees every buffer it passes; the library never frees caller memory.
+ *   - fp16 values travel as uint16_t bit patterns.  All arrays are dense
+ *     row-major with no padding.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously on it; no entry point synchronizes the host, except
+ *     w4a16_sparse24_repack (see there).
+ *   - Arguments are validated synchronously on the host before anything is
+ *     enqueued; on error nothing is enqueued and a negative code is returned.
+ *     Faults inside a kernel surface at the caller's next synchronization.
+ *   - Functions are thread-safe.  Concurrent calls on different streams are
+ *     safe; the library keeps one reduction workspace per (device, stream).
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------------- */
+#define W4A16_OK              0
+#define W4A16_ERR_NULL       -1  /* a required pointer is NULL                      */
+#define W4A16_ERR_SHAPE      -2  /* M,N,K <= 0; K % group; group % 128; N % 16 ...  */
+#define W4A16_ERR_ALIGN      -3  /* a pointer is not 16-byte aligned                */
+#define W4A16_ERR_DEVICE     -4  /* no HIP device, or the current device is not gfx950 */
+#define W4A16_ERR_LAUNCH     -5  /* the HIP runtime reported a launch error         */
+#define W4A16_ERR_WORKSPACE  -6  /* the reduction workspace could not be allocated  */
+#define W4A16_ERR_NOT24      -7  /* sparse repack input is not 2:4 along K          */
+#define W4A16_ERR_ARG        -8  /* an enumerated argument is out of range          */
+
+/* Layout version of the repacked buffers produced by w4a16_repack and
+ * w4a16_sparse24_repack.  Stored blobs from a different version must be
+ * repacked again from the canonical format. */
+int w4a16_layout_version(void);
+
+/* Static English description of a return code (never NULL). */
+const char* w4a16_strerror(int code);
+
+/* ---- sizes ------------------------------------------------------------------- */
+#define W4A16_BUF_W        0  /* dense repacked codes         : K*N/2 bytes              */
+#define W4A16_BUF_S        1  /* dense repacked scales        : 2*(K/group)*N bytes      */
+#define W4A16_BUF_Z        2  /* dense repacked zero-points   : (K/group)*N/2 bytes      */
+#define W4A16_BUF_SPARSE_V 3  /* 2:4 kept codes               : K*N/4 bytes              */
+#define W4A16_BUF_SPARSE_I 4  /* 2:4 position metadata        : K*N/8 bytes              */
+#define W4A16_BUF_SPARSE_S 5  /* 2:4 repacked scales          : 2*(K/group)*N bytes      */
+/* Bytes of buffer `which` for a K x N weight; 0 if the shape is invalid. */
+size_t w4a16_packed_bytes(int K, int N, int group, int which);
+
+/* ---- offline repack ([P2] "2. Tiled layout et repacking"; [P3] "Key Techniques",
+ *      reshuffling of weights and scales) -------------------------------------------
+ * Converts the canonical group-quantized format into the kernel layout, once,
+ * at load time; inference never touches the canonical format again.
+ *
+ *   q  (device, in)  int32 [K/8][N]: 8 codes per word packed along K,
+ *                    nibble j of q[i][n] is the code of row 8i+j (unsigned).
+ *   s  (device, in)  fp16  [K/group][N]: scale of (group, column).
+ *   z  (device, in)  int32 [K/group][N/8] packed along N (nibble j of z[G][c]
+ *                    is the zero-point of column 8c+j), or NULL for the
+ *                    symmetric format (zero-point 8).
+ *   wp (device, out) W4A16_BUF_W bytes; sp (device, out) W4A16_BUF_S bytes;
+ *   zp (device, out) W4A16_BUF_Z bytes, must be NULL exactly when z is NULL.
+ * Shape rules: K > 0, N > 0, group % 128 == 0, K % group == 0, N % 16 == 0.
+ * All pointers 16-byte aligned.  Input and output must not overlap.
+ */
+int w4a16_repack(const int32_t* q, const uint16_t* s, const int32_t* z,
+                 void* wp, uint16_t* sp, void* zp,
+                 int K, int N, int group, void* stream);
+
+/* Exact inverse of w4a16_repack (for round-trip checks): rewrites q, s and,
+ * when zp is not NULL, z in the canonical format.  Same shapes and rules. */
+int w4a16_unpack(const void* wp, const uint16_t* sp, const void* zp,
+                 int32_t* q, uint16_t* s, int32_t* z,
+                 int K, int N, int group, void* stream);
+
+/* ---- fused GEMM ([P1] "反量化与 GEMM 融合", "Striped 划分与流水线";
+ *      [P2] "Architecture générale"; [P3] "Key Techniques") --------------------------
+ * Y = X * W with W = (q - z) * s never written to memory: packed codes are read
+ * from HBM once, turned into fp16 in registers, multiplied on the matrix cores
+ * with fp32 accumulation, and Y is rounded once to fp16 (nearest-even).
+ *
+ *   X  (device, in)  fp16 [M][K];  wp, sp, zp as produced by w4a16_repack
+ *                    (zp NULL for the symmetric format);
+ *   Y  (device, out) fp16 [M][N], fully overwritten.
+ * Shape rules: M >= 1 plus the repack rules.  X, Y, wp, sp, zp 16-byte aligned.
+ * Results are bitwise reproducible from run to run for a given shape.
+ * The first call for a (device, stream) may allocate the reduction workspace
+ * (hipMalloc); later calls allocate only when a larger shape needs more.
+ */
+int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+               uint16_t* Y, int M, int N, int K, int group, void* stream);
+
+/* Same as w4a16_gemm with an explicit kernel plan (tuning and tests):
+ *   variant : -1 = automatic, else an index < w4a16_gemm_variants();
+ *   splits  : 0 = automatic, else the number of K slices reduced across
+ *             workgroups (clamped to the number of 128-row blocks per wave). */
+int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+                    uint16_t* Y, int M, int N, int K, int group,
+                    int variant, int splits, void* stream);
+
+/* Number of fused-kernel variants, and a static name for one (NULL if out of range). */
+int w4a16_gemm_variants(void);
+const char* w4a16_gemm_variant_name(int variant);
+
+/* Describe the automatic plan for a shape: out[0] = variant, out[1] = splits,
+ * out[2] = workgroups launched, out[3] = threads per workgroup.  Host only. */
+int w4a16_gemm_describe(int M, int N, int K, int group, int* out4);
+
+/* ---- unfused baseline ([P1] "反量化与 GEMM 融合": dequantize, write back, then
+ *      a plain GEMM; [P2] "Le problème") ---------------------------------------------
+ * w4a16_dequant: Wt (device, out) fp16 [N][K] with Wt[n][k] = RNE((q[k][n] -
+ *   z[k/group][n]) * s[k/group][n]) from the canonical q, s, z (z NULL =
+ *   symmetric).  Wt is stored output-major like a torch Linear weight.  Shape
+ *   rules as w4a16_repack.
+ * w4a16_fp16_gemm: Y (device, out) fp16 [M][N] = X [M][K] * Wt[N][K]^T with
+ *   fp32 accumulation.  Rules: M, N, K >= 1, K % 128 == 0, N % 16 == 0, 16-byte
+ *   aligned pointers.  Uses the same per-stream workspace as w4a16_gemm. */
+int w4a16_dequant(const int32_t* q, const uint16_t* s, const int32_t* z, uint16_t* Wt,
+                  int K, int N, int group, void* stream);
+int w4a16_fp16_gemm(const uint16_t* X, const uint16_t* Wt, uint16_t* Y,
+                    int M, int N, int K, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_H */

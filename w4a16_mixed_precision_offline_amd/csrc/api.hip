@@ -1,0 +1,259 @@
+// C ABI of libw4a16: argument validation (pure host code, runs before any HIP
+// call), device check, per-(device, stream) split-K workspace, and dispatch to
+// the kernels.  The interface and its rules are documented in include/w4a16.h.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/w4a16.h"
+#include "internal.h"
+
+using namespace w4a16;
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape rules shared by the weight-format entry points.
+int check_weight_shape(int K, int N, int group) {
+  if (K <= 0 || N <= 0 || group <= 0) return W4A16_ERR_SHAPE;
+  if (group % KBLK != 0 || K % group != 0 || N % NTILE != 0) return W4A16_ERR_SHAPE;
+  // word and block indices are 32-bit inside the kernels' per-dimension math
+  if ((long long)K * N / 8 > (1LL << 31) - 1) return W4A16_ERR_SHAPE;
+  return W4A16_OK;
+}
+
+// Device check: the current device must exist and be a gfx950.  Cached per device.
+std::mutex g_mu;
+std::map<int, int> g_dev_ok;  // device -> 1 ok / 0 not gfx950
+
+int check_device(int* dev_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return W4A16_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_dev_ok.find(dev);
+  if (it == g_dev_ok.end()) {
+    hipDeviceProp_t prop;
+    int ok = 0;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    else
+      (void)hipGetLastError();
+    it = g_dev_ok.emplace(dev, ok).first;
+  }
+  if (dev_out) *dev_out = dev;
+  return it->second ? W4A16_OK : W4A16_ERR_DEVICE;
+}
+
+// Split-K workspace: [counters (ints, zero at rest) | partials (floats)], one per
+// (device, stream).  Counters are reset by the kernels themselves, so the buffer
+// is cleared only when it is (re)allocated.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t counter_ints = 0;
+  size_t part_floats = 0;
+};
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(int dev, hipStream_t st, size_t counters, size_t floats, int** cnt,
+                  float** part) {
+  *cnt = nullptr;
+  *part = nullptr;
+  if (counters == 0 && floats == 0) return W4A16_OK;
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace& ws = g_ws[std::make_pair(dev, st)];
+  if (ws.ptr == nullptr || ws.counter_ints < counters || ws.part_floats < floats) {
+    size_t c = counters > ws.counter_ints ? counters : ws.counter_ints;
+    size_t f = floats > ws.part_floats ? floats : ws.part_floats;
+    c = (c + 63) / 64 * 64;  // keep the partials 256-byte aligned
+    if (ws.ptr) {
+      // earlier launches on this stream may still read the old buffer
+      if (hipStreamSynchronize(st) != hipSuccess || hipFree(ws.ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        ws = Workspace();
+        return W4A16_ERR_WORKSPACE;
+      }
+      ws = Workspace();
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, c * sizeof(int) + f * sizeof(float)) != hipSuccess) {
+      (void)hipGetLastError();
+      return W4A16_ERR_WORKSPACE;
+    }
+    if (hipMemsetAsync(p, 0, c * sizeof(int), st) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(p);
+      return W4A16_ERR_WORKSPACE;
+    }
+    ws.ptr = p;
+    ws.counter_ints = c;
+    ws.part_floats = f;
+  }
+  *cnt = static_cast<int*>(ws.ptr);
+  *part = reinterpret_cast<float*>(static_cast<int*>(ws.ptr) + ws.counter_ints);
+  return W4A16_OK;
+}
+
+inline int launched(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return W4A16_ERR_LAUNCH;
+  }
+  return W4A16_OK;
+}
+
+int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
+               uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
+               void* stream) {
+  SkinnyPlan plan;
+  int rc = skinny_make_plan(M, N, K, group, mode, variant, splits, &plan);
+  if (rc) return rc;
+  int dev;
+  if ((rc = check_device(&dev))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int* cnt;
+  float* part;
+  if ((rc = get_workspace(dev, st, plan.counters, plan.part_floats, &cnt, &part))) return rc;
+  return launched(skinny_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, cnt,
+                                M, N, K, group, st));
+}
+
+int check_gemm_args(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+                    const uint16_t* Y, int M, int N, int K, int group) {
+  if (!X || !wp || !sp || !Y) return W4A16_ERR_NULL;
+  int rc = check_weight_shape(K, N, group);
+  if (rc) return rc;
+  if (M <= 0) return W4A16_ERR_SHAPE;
+  if ((long long)M * K > (1LL << 40) || (long long)M * N > (1LL << 40)) return W4A16_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(wp) || !aligned16(sp) || !aligned16(Y) ||
+      (zp && !aligned16(zp)))
+    return W4A16_ERR_ALIGN;
+  return W4A16_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_layout_version(void) { return LAYOUT_VERSION; }
+
+const char* w4a16_strerror(int code) {
+  switch (code) {
+    case W4A16_OK: return "success";
+    case W4A16_ERR_NULL: return "a required pointer is NULL";
+    case W4A16_ERR_SHAPE: return "invalid shape (M,N,K >= 1, group % 128 == 0, K % group == 0, N % 16 == 0)";
+    case W4A16_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case W4A16_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
+    case W4A16_ERR_LAUNCH: return "kernel launch failed";
+    case W4A16_ERR_WORKSPACE: return "workspace allocation failed";
+    case W4A16_ERR_NOT24: return "weights are not 2:4 sparse along K";
+    case W4A16_ERR_ARG: return "an enumerated argument is out of range";
+    default: return "unknown error code";
+  }
+}
+
+size_t w4a16_packed_bytes(int K, int N, int group, int which) {
+  if (check_weight_shape(K, N, group)) return 0;
+  const size_t KN = (size_t)K * N, G = (size_t)(K / group);
+  switch (which) {
+    case W4A16_BUF_W: return KN / 2;
+    case W4A16_BUF_S: return 2 * G * N;
+    case W4A16_BUF_Z: return G * N / 2;
+    case W4A16_BUF_SPARSE_V: return KN / 4;
+    case W4A16_BUF_SPARSE_I: return KN / 8;
+    case W4A16_BUF_SPARSE_S: return 2 * G * N;
+    default: return 0;
+  }
+}
+
+int w4a16_repack(const int32_t* q, const uint16_t* s, const int32_t* z, void* wp, uint16_t* sp,
+                 void* zp, int K, int N, int group, void* stream) {
+  if (!q || !s || !wp || !sp) return W4A16_ERR_NULL;
+  if ((z == nullptr) != (zp == nullptr)) return W4A16_ERR_NULL;
+  int rc = check_weight_shape(K, N, group);
+  if (rc) return rc;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(wp) || !aligned16(sp) ||
+      (z && (!aligned16(z) || !aligned16(zp))))
+    return W4A16_ERR_ALIGN;
+  if ((rc = check_device(nullptr))) return rc;
+  return launched(launch_repack(q, s, z, static_cast<uint32_t*>(wp), sp,
+                                static_cast<uint32_t*>(zp), K, N, group,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_unpack(const void* wp, const uint16_t* sp, const void* zp, int32_t* q, uint16_t* s,
+                 int32_t* z, int K, int N, int group, void* stream) {
+  if (!q || !s || !wp || !sp) return W4A16_ERR_NULL;
+  if ((z == nullptr) != (zp == nullptr)) return W4A16_ERR_NULL;
+  int rc = check_weight_shape(K, N, group);
+  if (rc) return rc;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(wp) || !aligned16(sp) ||
+      (z && (!aligned16(z) || !aligned16(zp))))
+    return W4A16_ERR_ALIGN;
+  if ((rc = check_device(nullptr))) return rc;
+  return launched(launch_unpack(static_cast<const uint32_t*>(wp), sp,
+                                static_cast<const uint32_t*>(zp), q, s, z, K, N, group,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+               uint16_t* Y, int M, int N, int K, int group, void* stream) {
+  int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
+  if (rc) return rc;
+  return run_skinny(zp ? W_ASYM : W_SYM, X, wp, sp, zp, Y, M, N, K, group, -1, 0, stream);
+}
+
+int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+                    uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
+                    void* stream) {
+  int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
+  if (rc) return rc;
+  if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
+  return run_skinny(zp ? W_ASYM : W_SYM, X, wp, sp, zp, Y, M, N, K, group, variant, splits,
+                    stream);
+}
+
+int w4a16_gemm_variants(void) { return skinny_variant_count(); }
+const char* w4a16_gemm_variant_name(int variant) { return skinny_variant_name(variant); }
+
+int w4a16_gemm_describe(int M, int N, int K, int group, int* out4) {
+  if (!out4) return W4A16_ERR_NULL;
+  int rc = check_weight_shape(K, N, group);
+  if (rc) return rc;
+  if (M <= 0) return W4A16_ERR_SHAPE;
+  SkinnyPlan p;
+  if ((rc = skinny_make_plan(M, N, K, group, W_SYM, -1, 0, &p))) return rc;
+  out4[0] = p.variant;
+  out4[1] = p.splits;
+  out4[2] = p.wgs;
+  out4[3] = p.threads;
+  return W4A16_OK;
+}
+
+int w4a16_dequant(const int32_t* q, const uint16_t* s, const int32_t* z, uint16_t* Wt, int K,
+                  int N, int group, void* stream) {
+  if (!q || !s || !Wt) return W4A16_ERR_NULL;
+  int rc = check_weight_shape(K, N, group);
+  if (rc) return rc;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(Wt) || (z && !aligned16(z)))
+    return W4A16_ERR_ALIGN;
+  if ((rc = check_device(nullptr))) return rc;
+  return launched(launch_dequant(q, s, z, Wt, K, N, group, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_fp16_gemm(const uint16_t* X, const uint16_t* Wt, uint16_t* Y, int M, int N, int K,
+                    void* stream) {
+  if (!X || !Wt || !Y) return W4A16_ERR_NULL;
+  if (M <= 0 || N <= 0 || K <= 0 || K % KBLK != 0 || N % NTILE != 0) return W4A16_ERR_SHAPE;
+  if ((long long)N * K > (1LL << 40) || (long long)M * K > (1LL << 40)) return W4A16_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(Wt) || !aligned16(Y)) return W4A16_ERR_ALIGN;
+  return run_skinny(W_FP16, X, Wt, nullptr, nullptr, Y, M, N, K, KBLK, -1, 0, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal declarations shared by the HIP translation units of libw4a16.
+//
+// Repacked weight layout (layout version 1), own design for gfx950:
+//   A "block" covers 16 output columns (a tile t: n = 16t .. 16t+15) and 128
+//   consecutive K (a k-block kb: k = 128kb .. 128kb+127) and takes 1 KiB.
+//   Blocks are stored tile-major, K fastest: block index = t * (K/128) + kb.
+//   Inside a block, lane l (0..63) of a wave owns bytes [16l, 16l+16): four
+//   32-bit words, word j (0..3) holding the 8 codes of column 16t + (l % 16)
+//   for rows k = 128kb + 32j + 8(l/16) + e, e = 0..7.  A word therefore holds
+//   exactly the 8 K-values one lane feeds to one v_mfma_f32_16x16x32_f16 as its
+//   B operand, and one 16-byte load per lane fetches the operands of the four
+//   MFMAs that cover the 128-row block.
+//   Inside a word, row e sits at nibble pos(e) = e/2 + 4*(e%2), i.e. nibbles
+//   hold rows [0,2,4,6,1,3,5,7]; then (word & 0x000F000F) holds the pair
+//   (row 0, row 1) in its two 16-bit halves, (word & 0x00F000F0) the pair
+//   (2, 3) scaled by 16, and the same two masks on word >> 8 give (4, 5) and
+//   (6, 7).  Each such half becomes an exact fp16 by OR-ing in 0x6400 (1024.0),
+//   see dequant_word() in gemm_skinny.hip.
+//   Because 8 consecutive K of one column always sit in one canonical word
+//   (canonical words pack rows 8i..8i+7), every repacked word is one canonical
+//   word with its nibbles permuted.
+//
+// Scales: sp[(t * G + g) * 16 + c] = s[g][16t + c], G = K/group (fp16 bits).
+// Zero-points: zp32[(t * G + g) * 2 + h] = z_canonical[g][2t + h], i.e. the 16
+//   zero-points of a tile and group as one 64-bit word, nibble c = column 16t+c.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+constexpr int KBLK = 128;   // K rows per repacked block
+constexpr int NTILE = 16;   // columns per repacked tile
+constexpr int LAYOUT_VERSION = 1;
+
+// Position of row e (0..7 within a canonical word) inside a repacked word.
+__host__ __device__ constexpr int nib_pos(int e) { return (e >> 1) + 4 * (e & 1); }
+
+// ---- launchers (each validates nothing; the C ABI layer validated already) ----
+hipError_t launch_repack(const int32_t* q, const uint16_t* s, const int32_t* z,
+                         uint32_t* wp, uint16_t* sp, uint32_t* zp,
+                         int K, int N, int group, hipStream_t st);
+hipError_t launch_unpack(const uint32_t* wp, const uint16_t* sp, const uint32_t* zp,
+                         int32_t* q, uint16_t* s, int32_t* z,
+                         int K, int N, int group, hipStream_t st);
+hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
+                          uint16_t* W, int K, int N, int group, hipStream_t st);
+
+// Fused skinny GEMM.  `part` / `counters` form the split-K workspace.
+enum WMode { W_SYM = 0, W_ASYM = 1, W_FP16 = 2 };  // weight format of a launch
+struct SkinnyPlan {
+  int variant;   // index into the variant table
+  int mode;      // WMode
+  int MT, NT, WK;
+  int splits;
+  int mblocks, nblocks;
+  int wgs, threads;
+  size_t part_floats;  // workspace floats needed for partials
+  int counters;        // workspace ints needed for arrival counters
+};
+int skinny_variant_count();
+const char* skinny_variant_name(int v);
+// Fills `p` for a shape; variant < 0 or splits <= 0 mean automatic.  Returns 0 or a
+// negative W4A16 error code for an unusable (variant, shape) pair.
+int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int splits,
+                     SkinnyPlan* p);
+// w: repacked codes (W_SYM / W_ASYM) or fp16 Wt[N][K] (W_FP16, sp = zp = NULL).
+hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
+                         const uint16_t* sp, const uint32_t* zp, uint16_t* Y, float* part,
+                         int* counters, int M, int N, int K, int group, hipStream_t st);
+
+}  // namespace w4a16

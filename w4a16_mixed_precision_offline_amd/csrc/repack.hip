@@ -1,0 +1,161 @@
+// Offline repack of group-quantized INT4 weights into the MFMA-fragment layout,
+// its exact inverse, and the unfused baseline's dequantization.
+//
+// The pages describe a one-time, load-time reshuffle of weights and scales into
+// a tiled layout that suits the matrix instructions ("Marlin / GPTQ-Marlin",
+// brain.gartu.xyz, section "2. Tiled layout et repacking"; "Marlin Project
+// Overview", vecbase.com, "Key Techniques": reshuffling for access patterns).
+// The layout itself is this library's own (described in internal.h): each
+// repacked word is one canonical word with its nibbles permuted, so the repack
+// is a gather plus an in-register nibble shuffle, reading and writing every
+// byte exactly once.
+#include "internal.h"
+
+namespace w4a16 {
+
+namespace {
+
+// canonical word (rows 8i+e at nibble e) -> repacked word (row e at nib_pos(e))
+__device__ __forceinline__ uint32_t shuffle_to_repacked(uint32_t v) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r |= ((v >> (4 * e)) & 15u) << (4 * nib_pos(e));
+  return r;
+}
+__device__ __forceinline__ uint32_t shuffle_to_canonical(uint32_t v) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r |= ((v >> (4 * nib_pos(e))) & 15u) << (4 * e);
+  return r;
+}
+
+// Repacked word index o -> canonical word index (row i of q[K/8][N], column n).
+__device__ __forceinline__ void repacked_to_canonical(long o, int Gk, int N, long* ci) {
+  const int j = (int)(o & 3);
+  const int l = (int)((o >> 2) & 63);
+  const long b = o >> 8;
+  const long t = b / Gk;
+  const int kb = (int)(b - t * Gk);
+  const long i = 16L * kb + 4 * j + (l >> 4);
+  const long n = 16L * t + (l & 15);
+  *ci = i * N + n;
+}
+
+template <bool TO_REPACKED>
+__global__ void codes_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                             long total, int Gk, int N) {
+  for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    long ci;
+    repacked_to_canonical(o, Gk, N, &ci);
+    if (TO_REPACKED) dst[o] = shuffle_to_repacked(src[ci]);
+    else dst[ci] = shuffle_to_canonical(src[o]);
+  }
+}
+
+// scales: repacked index o = (t*G + g)*16 + c  <->  canonical g*N + 16t + c
+template <bool TO_REPACKED>
+__global__ void scales_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                              long total, int G, int N) {
+  for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int c = (int)(o & 15);
+    const long tg = o >> 4;
+    const long t = tg / G;
+    const long g = tg - t * G;
+    const long ci = g * N + 16 * t + c;
+    if (TO_REPACKED) dst[o] = src[ci];
+    else dst[ci] = src[o];
+  }
+}
+
+// zero-points: repacked word o = (t*G + g)*2 + h  <->  canonical word g*(N/8) + 2t + h
+template <bool TO_REPACKED>
+__global__ void zeros_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                             long total, int G, int N) {
+  for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int h = (int)(o & 1);
+    const long tg = o >> 1;
+    const long t = tg / G;
+    const long g = tg - t * G;
+    const long ci = g * (N / 8) + 2 * t + h;
+    if (TO_REPACKED) dst[o] = src[ci];
+    else dst[ci] = src[o];
+  }
+}
+
+// Unfused baseline dequantization: Wt[n][k] = RNE((q[k][n] - z[k/g][n]) * s[k/g][n]).
+// One thread per canonical word (8 rows of one column).  (q - z) * s is exact in
+// fp32 (a 5-bit integer times an 11-bit significand), so the single conversion to
+// fp16 rounds the exact value to nearest-even.
+__global__ void dequant_kernel(const uint32_t* __restrict__ q, const uint16_t* __restrict__ s,
+                               const uint32_t* __restrict__ z, uint16_t* __restrict__ Wt,
+                               long total, int K, int N, int group) {
+  for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const long i = o / N;          // canonical row of words
+    const int n = (int)(o - i * N);
+    const int g = (int)((8 * i) / group);
+    const uint32_t v = q[o];
+    const float sc = (float)__builtin_bit_cast(_Float16, s[(long)g * N + n]);
+    int zz = 8;
+    if (z) zz = (int)((z[(long)g * (N / 8) + n / 8] >> (4 * (n & 7))) & 15u);
+    uint16_t out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int qq = (int)((v >> (4 * e)) & 15u);
+      out[e] = __builtin_bit_cast(uint16_t, (_Float16)((float)(qq - zz) * sc));
+    }
+    uint4 pk;
+    pk.x = out[0] | ((uint32_t)out[1] << 16);
+    pk.y = out[2] | ((uint32_t)out[3] << 16);
+    pk.z = out[4] | ((uint32_t)out[5] << 16);
+    pk.w = out[6] | ((uint32_t)out[7] << 16);
+    *reinterpret_cast<uint4*>(Wt + (long)n * K + 8 * i) = pk;
+  }
+}
+
+inline int grid_for(long total, int threads) {
+  long b = (total + threads - 1) / threads;
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_repack(const int32_t* q, const uint16_t* s, const int32_t* z, uint32_t* wp,
+                         uint16_t* sp, uint32_t* zp, int K, int N, int group, hipStream_t st) {
+  const int Gk = K / KBLK, G = K / group;
+  const long wtot = (long)K * N / 8, stot = (long)G * N, ztot = (long)G * N / 8;
+  codes_kernel<true><<<grid_for(wtot, 256), 256, 0, st>>>(
+      reinterpret_cast<const uint32_t*>(q), wp, wtot, Gk, N);
+  scales_kernel<true><<<grid_for(stot, 256), 256, 0, st>>>(s, sp, stot, G, N);
+  if (z) zeros_kernel<true><<<grid_for(ztot, 256), 256, 0, st>>>(
+      reinterpret_cast<const uint32_t*>(z), zp, ztot, G, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint32_t* wp, const uint16_t* sp, const uint32_t* zp, int32_t* q,
+                         uint16_t* s, int32_t* z, int K, int N, int group, hipStream_t st) {
+  const int Gk = K / KBLK, G = K / group;
+  const long wtot = (long)K * N / 8, stot = (long)G * N, ztot = (long)G * N / 8;
+  codes_kernel<false><<<grid_for(wtot, 256), 256, 0, st>>>(
+      wp, reinterpret_cast<uint32_t*>(q), wtot, Gk, N);
+  scales_kernel<false><<<grid_for(stot, 256), 256, 0, st>>>(sp, s, stot, G, N);
+  if (zp) zeros_kernel<false><<<grid_for(ztot, 256), 256, 0, st>>>(
+      zp, reinterpret_cast<uint32_t*>(z), ztot, G, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z, uint16_t* Wt,
+                          int K, int N, int group, hipStream_t st) {
+  const long tot = (long)K * N / 8;
+  dequant_kernel<<<grid_for(tot, 256), 256, 0, st>>>(
+      reinterpret_cast<const uint32_t*>(q), s, reinterpret_cast<const uint32_t*>(z), Wt, tot, K,
+      N, group);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16
