@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused W4A16 GEMM on one MI355X.
+
+Workload (one "step"): the 7B-class decode sweep -- every (K, N) in
+{(4096,4096), (4096,12288), (4096,11008), (11008,4096)} times every M in
+{1,2,4,8,16,32}, group 128 along K, symmetric INT4, fp16 activations ~N(0,1),
+scales uniform in [0.002, 0.02]: 24 launches of w4a16_gemm through the C ABI.
+Inputs are seeded, synthetic, repacked once and resident in HBM before timing.
+
+Weights are rotated over enough distinct device copies that no launch reads
+weights an earlier launch left in L2 or the 256 MiB Infinity Cache (every weight
+byte a launch reads was last touched more than 1 GiB of weight traffic earlier),
+as in decoding where each layer's weights are read once per token.  Activations
+may stay cached.
+
+Prints ONE JSON line.  `value` is the packed-weight HBM throughput of the whole
+step (weight bytes of the 24 GEMMs / step time); the same line carries TFLOP/s,
+the per-launch roofline figure, the fp16 (dequantize-then-GEMM) baseline on the
+same shapes, and the CPU oracle timed on this host over one step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+FP16_PEAK_TFLOPS = 2516.6
+ROTATE_BYTES = 1 << 30
+
+
+def algorithmic(M, K, N, group=128):
+    """Bytes and flops the method must move / compute for one GEMM."""
+    wbytes = K * N // 2 + 2 * (K // group) * N
+    return wbytes, wbytes + 2 * M * K + 2 * M * N, 2 * M * N * K
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in ("gemm_skinny.hip", "internal.h"):
+        with open(os.path.join(ROOT, "w4a16_mixed_precision_offline_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "w4a16_gemm_decode_sweep_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
+    ap.add_argument("--no-baseline", action="store_true", help="skip the fp16 baseline")
+    ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant (tuning)")
+    ap.add_argument("--splits", type=int, default=0, help="force split-K slices (tuning)")
+    ap.add_argument("--detail", default=None, help="write per-launch detail JSON here")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only; the W4A16 GEMM has no multi-GPU "
+              "path here (it would shard by output columns with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import w4a16_mixed_precision_offline_amd as w4
+    from gen import CONFIGS, activations, config_runs, weights
+
+    torch.cuda.set_device(0)
+    runs = config_runs(1)
+    shapes = []
+    for w in runs:
+        if (w.K, w.N) not in shapes:
+            shapes.append((w.K, w.N))
+    Ms = CONFIGS[1]["Ms"]
+    group = 128
+
+    # ---- inputs, resident in HBM -----------------------------------------------------
+    step_wbytes = sum(algorithmic(1, K, N)[0] for (K, N) in shapes)
+    copies_per_step = len(Ms)  # each launch of a shape within a step uses a distinct copy
+    steps_per_cycle = max(1, -(-ROTATE_BYTES // (step_wbytes * copies_per_step)))
+    R = copies_per_step * steps_per_cycle
+    host = {}
+    packed = {}
+    for (K, N) in shapes:
+        w = next(r for r in runs if (r.K, r.N) == (K, N))
+        d = weights(w)
+        host[(K, N)] = d
+        q = torch.from_numpy(d["Qp"]).cuda()
+        s = torch.from_numpy(d["s"]).cuda()
+        wp, sp, _ = w4.alloc_packed(K, N, group, False)
+        w4.w4a16_repack(q, s, None, wp, sp, None, K, N, group)
+        packed[(K, N)] = [(wp, sp)] + [(wp.clone(), sp.clone()) for _ in range(R - 1)]
+        del q, s
+    Xs, Ys, Xh = {}, {}, {}
+    for w in runs:
+        X = activations(w)
+        Xh[(w.M, w.K, w.N)] = X
+        Xs[(w.M, w.K, w.N)] = torch.from_numpy(X).cuda()
+        Ys[(w.M, w.K, w.N)] = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+
+    # launch list of one step: M outer, shape inner; copy index advances per launch
+    def step_launches(step_idx):
+        out = []
+        cyc = step_idx % steps_per_cycle
+        for i, M in enumerate(Ms):
+            for (K, N) in shapes:
+                out.append((M, K, N, cyc * copies_per_step + i))
+        return out
+
+    def run_step_w4(step_idx):
+        for (M, K, N, c) in step_launches(step_idx):
+            wp, sp = packed[(K, N)][c]
+            w4.w4a16_gemm_plan(Xs[(M, K, N)], wp, sp, None, Ys[(M, K, N)], M, N, K, group,
+                               args.variant, args.splits)
+
+    stream = torch.cuda.Stream()
+
+    def time_steps(run_step, nsteps, warmup, use_graph):
+        """Returns (seconds per step, mode)."""
+        with torch.cuda.stream(stream):
+            for i in range(max(warmup, steps_per_cycle if use_graph else 0)):
+                run_step(i)
+        torch.cuda.synchronize()
+        graphs = None
+        if use_graph:
+            try:
+                graphs = []
+                for c in range(steps_per_cycle):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=stream):
+                        run_step(c)
+                    graphs.append(g)
+                torch.cuda.synchronize()
+                with torch.cuda.stream(stream):
+                    for i in range(warmup):
+                        graphs[i % steps_per_cycle].replay()
+                torch.cuda.synchronize()
+            except Exception as e:  # capture unsupported: fall back to eager launches
+                print(f"bench.py: graph capture failed ({e}); timing eager launches",
+                      file=sys.stderr)
+                graphs = None
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(nsteps):
+                if graphs is not None:
+                    graphs[i % steps_per_cycle].replay()
+                else:
+                    run_step(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / nsteps, ("hip_graph" if graphs is not None else "eager")
+
+    t_step, mode = time_steps(run_step_w4, args.steps, args.warmup, not args.no_graph)
+
+    # ---- per-launch durations (eager, launches queued behind a spin so that the GPU
+    #      runs them back to back), for the per-shape table ----------------------------
+    per_launch = []
+    with torch.cuda.stream(stream):
+        launches = step_launches(0)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+        torch.cuda.synchronize()
+        try:
+            torch.cuda._sleep(20_000_000)
+        except Exception:
+            pass
+        evs[0].record(stream)
+        for i, (M, K, N, c) in enumerate(launches):
+            wp, sp = packed[(K, N)][c]
+            w4.w4a16_gemm_plan(Xs[(M, K, N)], wp, sp, None, Ys[(M, K, N)], M, N, K, group,
+                               args.variant, args.splits)
+            evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    for i, (M, K, N, c) in enumerate(launches):
+        us = evs[i].elapsed_time(evs[i + 1]) * 1e3
+        wb, ab, fl = algorithmic(M, K, N)
+        plan = w4.w4a16_gemm_describe(M, N, K, group)
+        per_launch.append(dict(M=M, K=K, N=N, us=round(us, 3), weight_GBps=round(wb / us / 1e3, 1),
+                               TFLOPs=round(fl / us / 1e6, 2), hbm_frac=round(ab / us / 1e3 / HBM_PEAK_GBPS, 4),
+                               plan=plan["name"], splits=plan["splits"]))
+
+    n_launch = len(launches)
+    step_w = sum(algorithmic(M, K, N)[0] for (M, K, N, _) in launches)
+    step_alg = sum(algorithmic(M, K, N)[1] for (M, K, N, _) in launches)
+    step_fl = sum(algorithmic(M, K, N)[2] for (M, K, N, _) in launches)
+    value = step_w / t_step / 1e9
+    avg_launch_s = t_step / n_launch
+    achieved = step_alg / n_launch / avg_launch_s / 1e9
+    traffic = traffic_from_profiles()
+
+    # ---- fp16 baseline: hand-written dequant once, then the hand-written fp16 GEMM ----
+    baseline = None
+    if not args.no_baseline:
+        Wt = {}
+        for (K, N) in shapes:
+            d = host[(K, N)]
+            t0 = torch.empty((N, K), dtype=torch.float16, device="cuda")
+            w4.w4a16_dequant(torch.from_numpy(d["Qp"]).cuda(), torch.from_numpy(d["s"]).cuda(),
+                             None, t0, K, N, group)
+            Wt[(K, N)] = [t0] + [t0.clone() for _ in range(copies_per_step - 1)]
+        torch.cuda.synchronize()
+
+        def run_step_fp16(step_idx):
+            for i, M in enumerate(Ms):
+                for (K, N) in shapes:
+                    w4.w4a16_fp16_gemm(Xs[(M, K, N)], Wt[(K, N)][i], Ys[(M, K, N)], M, N, K)
+
+        t16, _ = time_steps(run_step_fp16, max(5, args.steps // 2), 2, not args.no_graph)
+
+        def run_step_torch(step_idx):
+            for i, M in enumerate(Ms):
+                for (K, N) in shapes:
+                    torch.nn.functional.linear(Xs[(M, K, N)], Wt[(K, N)][i])
+
+        ttorch, _ = time_steps(run_step_torch, max(5, args.steps // 2), 2, False)
+        baseline = dict(kind="w4a16_dequant + w4a16_fp16_gemm (hand-written, fp16 weights)",
+                        ms_per_step=round(t16 * 1e3, 4),
+                        fp16_weight_GBps=round(sum(2 * K * N for (_, K, N, _) in launches) / t16 / 1e9, 1),
+                        w4_speedup=round(t16 / t_step, 3),
+                        speedup_ceiling_bytes=round(16 / (4 + 16 / 128), 3),
+                        torch_matmul_ms_per_step=round(ttorch * 1e3, 4),
+                        w4_speedup_vs_torch_matmul=round(ttorch / t_step, 3))
+        del Wt
+
+    # ---- CPU oracle on this host over one step (bounded sample) -----------------------
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        # repeat whole steps until at least 10 s of oracle work (bounded at 30 s)
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            for (M, K, N, _) in launches:
+                d = host[(K, N)]
+                oracle.gemm(Xh[(M, K, N)], d["Qp"], d["s"], None, group)
+            passes += 1
+            tc = time.perf_counter() - t0
+            if tc >= 10.0 or tc * (passes + 1) / passes > 30.0:
+                break
+        cpu = dict(value=round(passes * step_w / tc / 1e9, 4), unit="GB/s", cores=threads,
+                   kind="oracle",
+                   sample=f"{passes} full step(s) of the decode sweep (24 GEMMs each): unpack + "
+                          "exact fp64 dequant + fp64 matmul, NumPy/OpenBLAS",
+                   seconds=round(tc, 3))
+
+    line = {
+        "metric": "W4A16 GEMM TFLOP/s + weight HBM GB/s vs M (1..4096), % of roofline",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "value_is": "packed INT4 weights + fp16 scales of the 24 GEMMs / step time",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode-shape sweep, 7B-class linear layers: (K,N) in "
+                        "{(4096,4096),(4096,12288),(4096,11008),(11008,4096)} x M in "
+                        "{1,2,4,8,16,32}, group 128 along K, symmetric INT4, fp16 X ~ N(0,1), "
+                        "scales U[0.002,0.02]; 24 GEMMs per step",
+            "launch": mode,
+            "weight_copies_rotated": R,
+            "parallelism": "single GPU",
+        },
+        "tflops": round(step_fl / t_step / 1e12, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "w4a16 fused GEMM (skinny_kernel), mean over the 24 launches of a step",
+            "algorithmic_bytes_per_launch": int(step_alg / n_launch),
+            "avg_launch_us": round(avg_launch_s * 1e6, 3),
+        },
+        "cpu_baseline": cpu,
+        "fp16_baseline": baseline,
+        "per_launch_us": [[p["M"], p["K"], p["N"], p["us"]] for p in per_launch],
+    }
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump(dict(line=line, per_launch=per_launch, kernel_sha=kernel_sha()), f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -71,7 +71,7 @@ def test_describe_plans(raw):
                       (48, 3072, 768)]:
         assert raw.w4a16_gemm_describe(M, N, K, 128, out) == 0
         assert 0 <= out[0] < raw.w4a16_gemm_variants()
-        assert out[1] >= 1 and out[2] >= 1 and out[3] in (64, 128, 256, 512)
+        assert out[1] >= 1 and out[2] >= 1 and out[3] in (64, 128, 256, 512, 1024)
     assert raw.w4a16_gemm_describe(0, 4096, 4096, 128, out) == -2
     assert raw.w4a16_gemm_describe(1, 4096, 4096, 128, None) == -1
 

@@ -81,7 +81,7 @@ def test_onehot_rows_bit_exact(gh, asym, splits):
         X[m, k] = 1
     W16 = oracle.dequant_fp16(d["Qp"], d["s"], d["Zp"], K, N, 128)
     packed = gh.repack(d, K, N)
-    Y = gh.gemm(gh.dev(X), packed, 16, N, K, variant=gh.variant_index("skinny_mt1_nt2_wk4"),
+    Y = gh.gemm(gh.dev(X), packed, 16, N, K, variant=gh.variant_index("skinny_mt1_nt2_wk8_d2"),
                 splits=splits)
     Yh = gh.host(Y)
     exp = W16[ks]
@@ -251,3 +251,38 @@ def test_error_codes_on_device(gh):
     with pytest.raises(w4.W4A16Error) as e:
         w4.w4a16_gemm(X[:, 1:], wp, sp, None, Y, 4, 1024, 1024, 128)
     assert e.value.code == -3
+
+
+def test_hip_graph_replays_match_eager(gh):
+    """The bench times captured HIP graphs: every replay (with eager work and
+    synchronizations in between) must reproduce the eager result bit for bit,
+    including launches that use the split-K counters."""
+    import torch
+    shapes = [(1, 4096, 4096), (16, 4096, 11008), (32, 11008, 4096)]
+    st = torch.cuda.Stream()
+    cases = []
+    for (M, K, N) in shapes:
+        _, d, X = _case(M, K, N)
+        cases.append((M, K, N, gh.dev(X), gh.repack(d, K, N),
+                      torch.empty((M, N), dtype=torch.float16, device="cuda")))
+    with torch.cuda.stream(st):
+        for (M, K, N, Xd, packed, Y) in cases:
+            gh.gemm(Xd, packed, M, N, K, Y=Y)
+    torch.cuda.synchronize()
+    eager = [gh.host(c[5]).view(np.uint16).copy() for c in cases]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        for (M, K, N, Xd, packed, Y) in cases:
+            gh.gemm(Xd, packed, M, N, K, Y=Y)
+    torch.cuda.synchronize()
+    for rep in range(5):
+        for c in cases:
+            c[5].fill_(0)
+        junk = gh.gemm(cases[0][3], cases[0][4], 1, 4096, 4096)  # eager work in between
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            g.replay()
+        torch.cuda.synchronize()
+        for c, e in zip(cases, eager):
+            assert np.array_equal(gh.host(c[5]).view(np.uint16), e), rep
+        del junk

@@ -160,7 +160,22 @@ __device__ __forceinline__ void compute_stage(const Stage<MT, NT, MODE>& S, floa
   }
 }
 
-template <int MT, int NT, int WK, int MODE>
+// Split-K hand-off between workgroups on different XCDs.  Each XCD has its own
+// L2, so ordinary stores may sit in one L2 while another XCD reads stale data.
+// Relaxed agent-scope atomic loads and stores compile to sc1 accesses, which are
+// coherent across XCDs by themselves; what an agent-scope release/acquire adds on
+// top (an L2 write-back / invalidate) is only needed for ordinary accesses and is
+// expensive.  So partials are written and read exclusively with sc1 accesses, and
+// the release is "all sc1 stores complete (s_waitcnt vmcnt(0)) before the counter
+// increment"; the acquire is "partials are read only after the increment returned".
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int MT, int NT, int WK, int D, int MODE>
 __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     const uint16_t* __restrict__ X, const uint4* __restrict__ W, const uint16_t* __restrict__ Sp,
     const uint2* __restrict__ Zp, uint16_t* __restrict__ Y, float* __restrict__ part,
@@ -174,8 +189,12 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   const int mb = bid / nblocks;
   const int Gk = K / KBLK;
   const int G = Gk / gpb;
+  // K range of this workgroup's slice, then this wave's contiguous chunk of it
   const int kb0 = (int)(((long)Gk * sl) / splits);
   const int kb1 = (int)(((long)Gk * (sl + 1)) / splits);
+  const int nk_wg = kb1 - kb0;
+  const int kw0 = kb0 + (nk_wg * wave) / WK;
+  const int nk = kb0 + (nk_wg * (wave + 1)) / WK - kw0;
   const int t0 = nb * NT;
   const int m0 = mb * MT * 16;
   int mtiles_live = (M - m0 + 15) / 16;
@@ -196,33 +215,31 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  Stage<MT, NT, MODE> A, B;
-  int kb = kb0 + wave;
-  if (kb < kb1) load_stage(A, kb, lane, t0, Gk, G, gpb, K, W, Sp, Zp, xrow, xok);
-  while (kb < kb1) {
-    int kn = kb + WK;
-    if (kn < kb1) load_stage(B, kn, lane, t0, Gk, G, gpb, K, W, Sp, Zp, xrow, xok);
-    compute_stage(A, acc, lane, mtiles_live);
-    kb = kn;
-    if (kb >= kb1) break;
-    kn = kb + WK;
-    if (kn < kb1) load_stage(A, kn, lane, t0, Gk, G, gpb, K, W, Sp, Zp, xrow, xok);
-    compute_stage(B, acc, lane, mtiles_live);
-    kb = kn;
+  // register ring of D stages: D k-blocks in flight ahead of the one being computed
+  Stage<MT, NT, MODE> S[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nk) load_stage(S[d], kw0 + d, lane, t0, Gk, G, gpb, K, W, Sp, Zp, xrow, xok);
+  for (int i = 0; i < nk; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (i + d < nk) {
+        compute_stage(S[d], acc, lane, mtiles_live);
+        if (i + d + D < nk)
+          load_stage(S[d], kw0 + i + d + D, lane, t0, Gk, G, gpb, K, W, Sp, Zp, xrow, xok);
+      }
+    }
   }
 
   // ---- in-workgroup reduction over the WK waves, fixed order 0, 1, ..., WK-1 ----
   constexpr int NACC = NT * MT * 4;
   if (WK > 1) {
-    __shared__ float red[(WK > 1 ? WK - 1 : 1) * NACC * 64];
+    __shared__ float4v red[(WK > 1 ? WK - 1 : 1) * 64 * NT * MT];  // [wave-1][lane][t][mt]
     if (wave > 0) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            red[((wave - 1) * NACC + (t * MT + mt) * 4 + r) * 64 + lane] = acc[t][mt][r];
+        for (int mt = 0; mt < MT; ++mt) red[((wave - 1) * 64 + lane) * NT * MT + t * MT + mt] = acc[t][mt];
     }
     __syncthreads();
     if (wave > 0) return;
@@ -231,13 +248,10 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[t][mt][r] += red[((w - 1) * NACC + (t * MT + mt) * 4 + r) * 64 + lane];
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] += red[((w - 1) * 64 + lane) * NT * MT + t * MT + mt];
   }
 
-  // ---- split-K: partial, arrival counter, last arriver reduces in slice order ----
+  // ---- split-K: coherent partial, arrival counter, last arriver sums in slice order ----
   if (splits > 1) {
     const long tile_id = (long)mb * nblocks + nb;
     float* mypart = part + (tile_id * splits + sl) * (NACC * 64);
@@ -246,13 +260,17 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mypart[((t * MT + mt) * 4 + r) * 64 + lane] = acc[t][mt][r];
-    __threadfence();
+        for (int r = 0; r < 4; ++r)
+          store_coherent(mypart + ((t * MT + mt) * 4 + r) * 64 + lane, acc[t][mt][r]);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);  // every sc1 store of this wave has completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     int old = 0;
-    if (lane == 0) old = atomicAdd(counters + tile_id, 1);
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(counters + tile_id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (old != splits - 1) return;
-    __threadfence();
     const float* base = part + tile_id * splits * (NACC * 64);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -262,10 +280,11 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
         for (int r = 0; r < 4; ++r) {
           float v = 0.f;
           for (int s2 = 0; s2 < splits; ++s2)
-            v += base[(long)s2 * (NACC * 64) + ((t * MT + mt) * 4 + r) * 64 + lane];
+            v += load_coherent(base + (long)s2 * (NACC * 64) + ((t * MT + mt) * 4 + r) * 64 + lane);
           acc[t][mt][r] = v;
         }
-    if (lane == 0) counters[tile_id] = 0;
+    if (lane == 0)
+      __hip_atomic_store(counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue: lane holds rows 4*(lane/16)+r of each m-tile, column lane%16 ----
@@ -286,28 +305,32 @@ typedef void (*KernelFn)(const uint16_t*, const uint4*, const uint16_t*, const u
                          float*, int*, int, int, int, int, int, int);
 
 struct Variant {
-  int MT, NT, WK;
+  int MT, NT, WK, D;
   KernelFn sym, asym, f16;
   const char* name;
 };
 
-#define W4A16_VARIANT(MT, NT, WK)                                                   \
-  Variant {                                                                         \
-    MT, NT, WK, skinny_kernel<MT, NT, WK, W_SYM>, skinny_kernel<MT, NT, WK, W_ASYM>, \
-        skinny_kernel<MT, NT, WK, W_FP16>, "skinny_mt" #MT "_nt" #NT "_wk" #WK      \
+#define W4A16_VARIANT(MT, NT, WK, D)                                                     \
+  Variant {                                                                              \
+    MT, NT, WK, D, skinny_kernel<MT, NT, WK, D, W_SYM>, skinny_kernel<MT, NT, WK, D, W_ASYM>, \
+        skinny_kernel<MT, NT, WK, D, W_FP16>,                                            \
+        "skinny_mt" #MT "_nt" #NT "_wk" #WK "_d" #D                                      \
   }
 
 const Variant kVariants[] = {
-    W4A16_VARIANT(1, 1, 4), W4A16_VARIANT(1, 2, 4), W4A16_VARIANT(1, 4, 4),
-    W4A16_VARIANT(2, 1, 4), W4A16_VARIANT(2, 2, 4), W4A16_VARIANT(4, 1, 4),
-    W4A16_VARIANT(4, 2, 4), W4A16_VARIANT(1, 2, 2), W4A16_VARIANT(1, 2, 8),
-    W4A16_VARIANT(2, 2, 8),
+    W4A16_VARIANT(1, 1, 16, 2), W4A16_VARIANT(1, 1, 8, 2), W4A16_VARIANT(1, 1, 8, 4),
+    W4A16_VARIANT(1, 1, 4, 4),  W4A16_VARIANT(1, 2, 8, 2), W4A16_VARIANT(1, 2, 4, 4),
+    W4A16_VARIANT(1, 2, 16, 2), W4A16_VARIANT(2, 1, 8, 2), W4A16_VARIANT(2, 1, 16, 2),
+    W4A16_VARIANT(2, 2, 8, 2),  W4A16_VARIANT(2, 1, 4, 4), W4A16_VARIANT(4, 1, 4, 2),
+    W4A16_VARIANT(4, 1, 8, 2),  W4A16_VARIANT(4, 2, 4, 2),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-int find_variant(int MT, int NT, int WK) {
+int find_variant(int MT, int NT, int WK, int D) {
   for (int i = 0; i < kNumVariants; ++i)
-    if (kVariants[i].MT == MT && kVariants[i].NT == NT && kVariants[i].WK == WK) return i;
+    if (kVariants[i].MT == MT && kVariants[i].NT == NT && kVariants[i].WK == WK &&
+        kVariants[i].D == D)
+      return i;
   return -1;
 }
 
@@ -322,10 +345,18 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
                      SkinnyPlan* p) {
   (void)group;
   if (variant < 0) {
-    const int MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    int NT = mode == W_FP16 ? 1 : 2;
-    if (N % (16 * NT) != 0) NT = 1;
-    variant = find_variant(MT, NT, 4);
+    // measured on MI355X over the decode shapes: 16 waves per 16-column tile while the
+    // tiles alone fill the 256 compute units, else two tiles per wave to halve the
+    // activation loads per weight byte
+    const long tiles = N / 16;
+    const bool few = tiles <= 256;
+    if (M <= 16)
+      variant = few ? find_variant(1, 1, 16, 2)
+                    : (N % 32 == 0 ? find_variant(1, 2, 8, 2) : find_variant(1, 1, 4, 4));
+    else if (M <= 32)
+      variant = (few || N % 32) ? find_variant(2, 1, 8, 2) : find_variant(2, 2, 8, 2);
+    else
+      variant = find_variant(4, 1, 8, 2);
   }
   if (variant < 0 || variant >= kNumVariants) return -8;
   const Variant& v = kVariants[variant];
@@ -341,8 +372,9 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
   int maxs = Gk / v.WK;
   if (maxs < 1) maxs = 1;
   if (splits <= 0) {
+    // split K only when the column tiles cannot give every compute unit a workgroup
     const long base = (long)p->mblocks * p->nblocks;
-    const long target = 1024;
+    const long target = 256;
     long sp = (target + base - 1) / base;
     splits = (int)(sp < 1 ? 1 : sp);
   }
