@@ -56,11 +56,13 @@ const char* w4a16_strerror(int code);
 
 /* ---- sizes ------------------------------------------------------------------- */
 #define W4A16_BUF_W        0  /* dense repacked codes         : K*N/2 bytes              */
-#define W4A16_BUF_S        1  /* dense repacked scales        : 2*(K/group)*N bytes      */
-#define W4A16_BUF_Z        2  /* dense repacked zero-points   : (K/group)*N/2 bytes      */
+#define W4A16_BUF_S        1  /* dense repacked scales        : 2*(K/128)*N bytes        */
+#define W4A16_BUF_Z        2  /* dense repacked zero-points   : (K/128)*N/2 bytes        */
 #define W4A16_BUF_SPARSE_V 3  /* 2:4 kept codes               : K*N/4 bytes              */
 #define W4A16_BUF_SPARSE_I 4  /* 2:4 position metadata        : K*N/8 bytes              */
-#define W4A16_BUF_SPARSE_S 5  /* 2:4 repacked scales          : 2*(K/group)*N bytes      */
+#define W4A16_BUF_SPARSE_S 5  /* 2:4 repacked scales          : 2*(K/128)*N bytes        */
+/* (repacked scales and zero-points hold one row per 128 rows of K, so a group of
+ *  256 or more rows is stored once per 128-row block it spans) */
 /* Bytes of buffer `which` for a K x N weight; 0 if the shape is invalid. */
 size_t w4a16_packed_bytes(int K, int N, int group, int which);
 

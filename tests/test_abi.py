@@ -56,6 +56,8 @@ def test_queries(raw):
     assert raw.w4a16_packed_bytes(4096, 4096, 128, 0) == 4096 * 4096 // 2
     assert raw.w4a16_packed_bytes(4096, 4096, 128, 1) == 2 * 32 * 4096
     assert raw.w4a16_packed_bytes(4096, 4096, 128, 2) == 32 * 4096 // 2
+    assert raw.w4a16_packed_bytes(4096, 4096, 256, 1) == 2 * 32 * 4096   # one row per 128 K
+    assert raw.w4a16_packed_bytes(4096, 4096, 256, 2) == 32 * 4096 // 2
     assert raw.w4a16_packed_bytes(4096, 4096, 128, 3) == 4096 * 4096 // 4
     assert raw.w4a16_packed_bytes(4096, 4096, 128, 4) == 4096 * 4096 // 8
     assert raw.w4a16_packed_bytes(4096, 4096, 128, 9) == 0

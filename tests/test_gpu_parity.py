@@ -81,7 +81,7 @@ def test_onehot_rows_bit_exact(gh, asym, splits):
         X[m, k] = 1
     W16 = oracle.dequant_fp16(d["Qp"], d["s"], d["Zp"], K, N, 128)
     packed = gh.repack(d, K, N)
-    Y = gh.gemm(gh.dev(X), packed, 16, N, K, variant=gh.variant_index("skinny_mt1_nt2_wk8_d2"),
+    Y = gh.gemm(gh.dev(X), packed, 16, N, K, variant=gh.variant_index("skinny_xr16_nt2_wk8_d2"),
                 splits=splits)
     Yh = gh.host(Y)
     exp = W16[ks]

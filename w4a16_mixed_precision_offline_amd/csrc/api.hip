@@ -160,14 +160,14 @@ const char* w4a16_strerror(int code) {
 
 size_t w4a16_packed_bytes(int K, int N, int group, int which) {
   if (check_weight_shape(K, N, group)) return 0;
-  const size_t KN = (size_t)K * N, G = (size_t)(K / group);
+  const size_t KN = (size_t)K * N, Gk = (size_t)(K / KBLK);
   switch (which) {
     case W4A16_BUF_W: return KN / 2;
-    case W4A16_BUF_S: return 2 * G * N;
-    case W4A16_BUF_Z: return G * N / 2;
+    case W4A16_BUF_S: return 2 * Gk * N;
+    case W4A16_BUF_Z: return Gk * N / 2;
     case W4A16_BUF_SPARSE_V: return KN / 4;
     case W4A16_BUF_SPARSE_I: return KN / 8;
-    case W4A16_BUF_SPARSE_S: return 2 * G * N;
+    case W4A16_BUF_SPARSE_S: return 2 * Gk * N;
     default: return 0;
   }
 }

@@ -16,23 +16,29 @@
 //     as few global reduction steps as possible.
 //
 // How this kernel maps that onto CDNA4 (own design):
-//   * One wave owns NT tiles of 16 columns and MT tiles of 16 rows.  A 128-row
-//     k-block of one tile is 1 KiB of packed codes in the repacked layout, one
-//     16-byte non-temporal load per lane (see internal.h).
+//   * One wave owns NT tiles of 16 columns and the XR-row block of X (XR = 4, 8,
+//     16, 32 or 64; MT = ceil(XR/16) MFMA row tiles).  A 128-row k-block of one
+//     tile is 1 KiB of packed codes in the repacked layout: one 16-byte
+//     non-temporal buffer load per lane (layout in internal.h).
+//   * Activations are loaded as whole rows (each instruction covers 4 rows x 256
+//     bytes, lanes past M read zeros through the buffer bounds) and re-laid into
+//     MFMA fragments through a wave-private LDS tile.  Loading the fragments
+//     straight from memory touches 16 rows x 64 bytes per instruction and was
+//     measured 2.6x slower from L2 on MI355X than the row-contiguous pattern.
 //   * Dequantization uses the 0x6400 exponent trick: OR-ing a nibble into the
 //     mantissa of 1024.0 gives the exact fp16 1024+q (or 1024+16q for the high
 //     nibble of a byte), and one packed fp16 add / fma removes the offset and the
 //     zero-point, giving the exact integer q - z.  The scale is applied after the
 //     four v_mfma_f32_16x16x32_f16 of the k-block, in fp32, on the 4 accumulators
 //     of the lane (1 fma per output instead of 1 multiply per weight).
-//   * The WK waves of a workgroup take interleaved k-blocks of the same output
-//     tile and reduce through LDS in a fixed order.
+//   * The WK waves of a workgroup take contiguous chunks of the K range of the
+//     same output tiles and reduce through LDS in a fixed order.
 //   * When a tile's K range is cut into `splits` slices owned by different
 //     workgroups, each writes an fp32 partial, bumps an arrival counter, and the
 //     last to arrive sums the slices in slice order (deterministic) and writes
 //     Y; it also resets the counter for the next launch, so no memset is needed.
-//   * Weight registers are double-buffered: the next k-block's loads are in
-//     flight while the current one is dequantized and multiplied.
+//   * Each wave keeps D k-blocks of loads in flight in a register ring; the loop
+//     is branch-free so that the compiler's wait counts stay exact.
 #include "internal.h"
 
 namespace w4a16 {
@@ -52,16 +58,42 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Buffer resources: the uniform part of an address goes to the scalar offset, the
+// per-lane part to a fixed VGPR offset, and lanes whose offset is past num_records
+// read zeros without touching memory (used for rows of X beyond M), so no branch
+// is needed around any load.  Word 3 (0x00020000) is the gfx9-family raw-buffer
+// format.  Each resource covers one workgroup's region, so offsets stay small.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                          0x00020000);
+}
+template <bool STREAM>
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, STREAM ? 2 : 0));
+}
+
+
+// (w & mask) | magic in one VALU op.  The compiler otherwise emits an and and an
+// or, because gfx9 VOP3 can read only one scalar/literal operand: keep the mask
+// in an SGPR and the magic number in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+  return r;
+}
 
 // 8 codes of one repacked word -> 8 exact fp16 (q - z), in row order 0..7.
 // c0 = -(1024 + z) and c1 = -(64 + z) in both halves.
-__device__ __forceinline__ half8 dequant_word(uint32_t w, half2v c0, half2v c1) {
+__device__ __forceinline__ half8 dequant_word(uint32_t w, half2v c0, half2v c1, uint32_t magic) {
   const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const uint32_t w8 = w >> 8;
-  const uint32_t t0 = (w & 0x000F000Fu) | 0x64006400u;   // 1024+q0 | 1024+q1
-  const uint32_t t1 = (w & 0x00F000F0u) | 0x64006400u;   // 1024+16q2 | 1024+16q3
-  const uint32_t t2 = (w8 & 0x000F000Fu) | 0x64006400u;  // 1024+q4 | 1024+q5
-  const uint32_t t3 = (w8 & 0x00F000F0u) | 0x64006400u;  // 1024+16q6 | 1024+16q7
+  const uint32_t t0 = and_or(w, 0x000F000Fu, magic);   // 1024+q0 | 1024+q1
+  const uint32_t t1 = and_or(w, 0x00F000F0u, magic);   // 1024+16q2 | 1024+16q3
+  const uint32_t t2 = and_or(w8, 0x000F000Fu, magic);  // 1024+q4 | 1024+q5
+  const uint32_t t3 = and_or(w8, 0x00F000F0u, magic);  // 1024+16q6 | 1024+16q7
   const half2v h0 = __builtin_bit_cast(half2v, t0) + c0;
   const half2v h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2v, t1), sixteenth, c1);
   const half2v h2 = __builtin_bit_cast(half2v, t2) + c0;
@@ -72,47 +104,70 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, half2v c0, half2v c1) 
   return r;
 }
 
-template <int MT, int NT, int MODE>
+constexpr int XSTRIDE = 272;  // bytes per X row in the LDS tile (256 + 16 against bank conflicts)
+
+template <int XR, int NT, int MODE>
 struct Stage {
   u32x4 w[NT][MODE == W_FP16 ? 4 : 1];  // packed codes (or fp16 rows for the baseline)
-  uint32_t s[NT];                       // fp16 scale bits of the lane's column
+  uint16_t s[NT];                       // fp16 scale bits of the lane's column
   uint2 z[NT];                          // 16 zero-points of the tile (ASYM)
-  u32x4 x[MT][4];                       // X fragments for the four 32-row steps
+  u32x4 x[XR / 4];                      // X rows 4c + lane/16, 16-byte chunk lane%16
 };
 
-template <int MT, int NT, int MODE>
-__device__ __forceinline__ void load_stage(Stage<MT, NT, MODE>& S, int kb, int lane, int t0,
-                                           int Gk, int G, int gpb, int K,
-                                           const uint4* __restrict__ W,
-                                           const uint16_t* __restrict__ Sp,
-                                           const uint2* __restrict__ Zp,
-                                           const uint16_t* const xrow[MT], const bool xok[MT]) {
-  const int g = kb / gpb;
+// Loads of one k-block.  kb is wave-uniform, so every scalar offset below is
+// formed on the scalar unit; the per-lane offsets were computed once.
+struct Rsrc {
+  rsrc_t w, s, z, x;
+  uint32_t lane_w;  // byte offset of the lane inside a weight block (or fp16 row slice)
+};
+
+// `live` is wave-uniform: past the wave's last k-block every load goes through a
+// resource of zero size, which returns zeros without a memory request, so the
+// pipelined loop below needs no branch (branches would make the compiler's wait
+// counts conservative and serialize the prefetch).
+template <int XR, int NT, int MODE>
+__device__ __forceinline__ void load_stage(Stage<XR, NT, MODE>& S, int kb, bool live, int lane,
+                                           int Gk, int K, const Rsrc& R0, const Rsrc& Rnull,
+                                           const uint32_t xoff[XR / 4]) {
+  const Rsrc& R = live ? R0 : Rnull;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (MODE == W_FP16) {
-      // baseline: W is fp16 [N][K]; the lane's column n, rows 32j + 8(lane/16) + 0..7
-      const uint16_t* row = reinterpret_cast<const uint16_t*>(W) +
-                            (long)((t0 + t) * 16 + (lane & 15)) * K + kb * KBLK + 8 * (lane >> 4);
+      // baseline: W is fp16 [N][K]; the lane's column, rows 32j + 8(lane/16) + 0..7
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S.w[t][j] = load16_nt(row + 32 * j);
+      for (int j = 0; j < 4; ++j)
+        S.w[t][j] = bload16<true>(R.w, R.lane_w + (uint32_t)(t * 16 * K * 2 + 64 * j),
+                                  (uint32_t)kb * KBLK * 2);
     } else {
-      S.w[t][0] = load16_nt(W + ((long)(t0 + t) * Gk + kb) * 64 + lane);
-      S.s[t] = Sp[((long)(t0 + t) * G + g) * 16 + (lane & 15)];
-      if (MODE == W_ASYM) S.z[t] = Zp[(long)(t0 + t) * G + g];
+      const uint32_t blk = (uint32_t)(t * Gk + kb);
+      S.w[t][0] = bload16<true>(R.w, R.lane_w, blk * 1024u);
+      S.s[t] = __builtin_amdgcn_raw_buffer_load_b16(R.s, (uint32_t)(lane & 15) * 2, blk * 32u, 0);
+      if (MODE == W_ASYM)
+        S.z[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R.z, 0u, blk * 8u, 0));
     }
   }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const uint16_t* p = xrow[mt] + kb * KBLK;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) S.x[mt][j] = xok[mt] ? load16(p + 32 * j) : u32x4{0, 0, 0, 0};
-  }
+  for (int c = 0; c < XR / 4; ++c) S.x[c] = bload16<false>(R.x, xoff[c], (uint32_t)kb * KBLK * 2);
 }
 
-template <int MT, int NT, int MODE>
-__device__ __forceinline__ void compute_stage(const Stage<MT, NT, MODE>& S, float4v (&acc)[NT][MT],
-                                              int lane, int mtiles_live) {
+// Compute one k-block: lay the X rows into the wave's LDS tile, read them back as
+// MFMA fragments (lane l: row 16mt + l%16, 8 halves at 32j + 8(l/16)), dequantize
+// the codes and run the four MFMAs per (row tile, column tile).
+template <int XR, int NT, int MODE>
+__device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
+                                              float4v (&acc)[NT][(XR + 15) / 16], int lane,
+                                              uint32_t magic, char* xlds) {
+  constexpr int MT = (XR + 15) / 16;
+#pragma unroll
+  for (int c = 0; c < XR / 4; ++c)
+    *reinterpret_cast<u32x4*>(xlds + (4 * c + (lane >> 4)) * XSTRIDE + (lane & 15) * 16) = S.x[c];
+  half8 a[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[mt][j] = *reinterpret_cast<const half8*>(xlds + (mt * 16 + (lane & 15)) * XSTRIDE +
+                                                  64 * j + 16 * (lane >> 4));
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     half8 b[4];
@@ -133,28 +188,25 @@ __device__ __forceinline__ void compute_stage(const Stage<MT, NT, MODE>& S, floa
         c0 = half2v{(_Float16)-1032.0f, (_Float16)-1032.0f};
         c1 = half2v{(_Float16)-72.0f, (_Float16)-72.0f};
       }
-      b[0] = dequant_word(S.w[t][0].x, c0, c1);
-      b[1] = dequant_word(S.w[t][0].y, c0, c1);
-      b[2] = dequant_word(S.w[t][0].z, c0, c1);
-      b[3] = dequant_word(S.w[t][0].w, c0, c1);
+      b[0] = dequant_word(S.w[t][0].x, c0, c1, magic);
+      b[1] = dequant_word(S.w[t][0].y, c0, c1, magic);
+      b[2] = dequant_word(S.w[t][0].z, c0, c1, magic);
+      b[3] = dequant_word(S.w[t][0].w, c0, c1, magic);
     }
+    // row tiles past M hold zero activations and add exactly zero; no branch here
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      if (mt < mtiles_live) {
-        if (MODE == W_FP16) {
+      if (MODE == W_FP16) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(half8, S.x[mt][j]), b[j], acc[t][mt], 0, 0, 0);
-        } else {
-          float4v g = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j)
+          acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][j], b[j], acc[t][mt], 0, 0, 0);
+      } else {
+        float4v g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            g = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, S.x[mt][j]),
-                                                       b[j], g, 0, 0, 0);
-          const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)S.s[t]);
-          acc[t][mt] += sc * g;
-        }
+        for (int j = 0; j < 4; ++j)
+          g = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][j], b[j], g, 0, 0, 0);
+        const float sc = (float)__builtin_bit_cast(_Float16, S.s[t]);
+        acc[t][mt] += sc * g;
       }
     }
   }
@@ -175,20 +227,24 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int MT, int NT, int WK, int D, int MODE>
+template <int XR, int NT, int WK, int D, int MODE>
 __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     const uint16_t* __restrict__ X, const uint4* __restrict__ W, const uint16_t* __restrict__ Sp,
     const uint2* __restrict__ Zp, uint16_t* __restrict__ Y, float* __restrict__ part,
-    int* __restrict__ counters, int M, int N, int K, int gpb, int splits, int nblocks) {
+    int* __restrict__ counters, int M, int N, int K, int splits, int nblocks) {
+  constexpr int MT = (XR + 15) / 16;
+  constexpr int XTILE = MT * 16 * XSTRIDE;  // bytes of one wave's X tile
+  // per-wave X tiles; after the main loop the same memory holds the reduction
+  __shared__ __attribute__((aligned(16))) char lds[WK * XTILE];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index made uniform so that all k-block bookkeeping stays on the scalar unit
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int bid = blockIdx.x;
   const int sl = bid % splits;
   bid /= splits;
   const int nb = bid % nblocks;
   const int mb = bid / nblocks;
   const int Gk = K / KBLK;
-  const int G = Gk / gpb;
   // K range of this workgroup's slice, then this wave's contiguous chunk of it
   const int kb0 = (int)(((long)Gk * sl) / splits);
   const int kb1 = (int)(((long)Gk * (sl + 1)) / splits);
@@ -196,18 +252,38 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   const int kw0 = kb0 + (nk_wg * wave) / WK;
   const int nk = kb0 + (nk_wg * (wave + 1)) / WK - kw0;
   const int t0 = nb * NT;
-  const int m0 = mb * MT * 16;
-  int mtiles_live = (M - m0 + 15) / 16;
-  if (mtiles_live > MT) mtiles_live = MT;
+  const int m0 = mb * XR;
+  char* xlds = lds + wave * XTILE;
 
-  const uint16_t* xrow[MT];
-  bool xok[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int r = m0 + mt * 16 + (lane & 15);
-    xok[mt] = r < M;
-    xrow[mt] = X + (long)(xok[mt] ? r : 0) * K + 8 * (lane >> 4);
+  // buffer resources over this workgroup's tiles and rows
+  Rsrc R;
+  if (MODE == W_FP16) {
+    const char* wbase = reinterpret_cast<const char*>(W) + (size_t)t0 * 16 * K * 2;
+    R.w = make_rsrc(wbase, (uint32_t)(NT * 16 * K * 2));
+    R.lane_w = (uint32_t)(((lane & 15) * K + 8 * (lane >> 4)) * 2);
+  } else {
+    R.w = make_rsrc(reinterpret_cast<const char*>(W) + (size_t)t0 * Gk * 1024,
+                    (uint32_t)(NT * Gk * 1024));
+    R.s = make_rsrc(Sp + (size_t)t0 * Gk * 16, (uint32_t)(NT * Gk * 32));
+    if (MODE == W_ASYM) R.z = make_rsrc(Zp + (size_t)t0 * Gk, (uint32_t)(NT * Gk * 8));
+    R.lane_w = (uint32_t)lane * 16;
   }
+  const int rows = M - m0 < XR ? M - m0 : XR;  // valid rows of this block of X
+  R.x = make_rsrc(X + (size_t)m0 * K, (uint32_t)(rows * K * 2));
+  // per-lane byte offsets of the X row loads: row 4c + lane/16, 16 bytes at
+  // column 8(lane%16); rows past M read zeros
+  uint32_t xoff[XR / 4];
+#pragma unroll
+  for (int c = 0; c < XR / 4; ++c) {
+    const int r = 4 * c + (lane >> 4);
+    xoff[c] = r < rows ? (uint32_t)((r * K + 8 * (lane & 15)) * 2) : kOutOfRange;
+  }
+  // rows XR..15 of the LDS tile are never written by the loads: keep them zero
+  if (XR % 16 != 0) {
+    for (int i = lane; i < (16 - XR) * XSTRIDE / 16; i += 64)
+      *reinterpret_cast<u32x4*>(xlds + XR * XSTRIDE + 16 * i) = u32x4{0, 0, 0, 0};
+  }
+  const uint32_t magic = 0x64006400u;
 
   float4v acc[NT][MT];
 #pragma unroll
@@ -215,26 +291,40 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // register ring of D stages: D k-blocks in flight ahead of the one being computed
-  Stage<MT, NT, MODE> S[D];
+  // a resource of zero size: loads through it return zeros and touch no memory
+  Rsrc Rnull;
+  Rnull.w = make_rsrc(W, 0);
+  Rnull.s = make_rsrc(Sp, 0);
+  Rnull.z = make_rsrc(Zp, 0);
+  Rnull.x = make_rsrc(X, 0);
+  Rnull.lane_w = R.lane_w;
+
+  // register ring of D stages: D k-blocks in flight ahead of the one being computed.
+  // The trip count is rounded up to a multiple of D; stages past the wave's range
+  // hold zeros and add exactly zero.
+  Stage<XR, NT, MODE> S[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < nk) load_stage(S[d], kw0 + d, lane, t0, Gk, G, gpb, K, W, Sp, Zp, xrow, xok);
+  for (int d = 0; d < D; ++d) {
+    load_stage(S[d], kw0 + d, d < nk, lane, Gk, K, R, Rnull, xoff);
+    __builtin_amdgcn_sched_barrier(0);  // issue the stages in order
+  }
   for (int i = 0; i < nk; i += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (i + d < nk) {
-        compute_stage(S[d], acc, lane, mtiles_live);
-        if (i + d + D < nk)
-          load_stage(S[d], kw0 + i + d + D, lane, t0, Gk, G, gpb, K, W, Sp, Zp, xrow, xok);
-      }
+      compute_stage(S[d], acc, lane, magic, xlds);
+      load_stage(S[d], kw0 + i + d + D, i + d + D < nk, lane, Gk, K, R, Rnull, xoff);
+      // keep stage order: the compiler would otherwise merge the stages and wait
+      // for every outstanding load before the first one is computed
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // ---- in-workgroup reduction over the WK waves, fixed order 0, 1, ..., WK-1 ----
+  // (reuses the X tiles: wait until every wave is done with its tile)
   constexpr int NACC = NT * MT * 4;
   if (WK > 1) {
-    __shared__ float4v red[(WK > 1 ? WK - 1 : 1) * 64 * NT * MT];  // [wave-1][lane][t][mt]
+    float4v* red = reinterpret_cast<float4v*>(lds);  // [wave-1][lane][t][mt]
+    __syncthreads();
     if (wave > 0) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
@@ -288,6 +378,8 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   }
 
   // ---- epilogue: lane holds rows 4*(lane/16)+r of each m-tile, column lane%16 ----
+  // (only the XR rows of this block: with XR < 16 the rest of the MFMA tile is padding)
+  const int row_end = M < m0 + XR ? M : m0 + XR;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -296,39 +388,41 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + mt * 16 + 4 * (lane >> 4) + r;
         const int col = (t0 + t) * 16 + (lane & 15);
-        if (row < M)
+        if (row < row_end)
           Y[(long)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[t][mt][r]);
       }
 }
 
 typedef void (*KernelFn)(const uint16_t*, const uint4*, const uint16_t*, const uint2*, uint16_t*,
-                         float*, int*, int, int, int, int, int, int);
+                         float*, int*, int, int, int, int, int);
 
 struct Variant {
-  int MT, NT, WK, D;
+  int XR, NT, WK, D;
   KernelFn sym, asym, f16;
   const char* name;
 };
 
-#define W4A16_VARIANT(MT, NT, WK, D)                                                     \
+#define W4A16_VARIANT(XR, NT, WK, D)                                                     \
   Variant {                                                                              \
-    MT, NT, WK, D, skinny_kernel<MT, NT, WK, D, W_SYM>, skinny_kernel<MT, NT, WK, D, W_ASYM>, \
-        skinny_kernel<MT, NT, WK, D, W_FP16>,                                            \
-        "skinny_mt" #MT "_nt" #NT "_wk" #WK "_d" #D                                      \
+    XR, NT, WK, D, skinny_kernel<XR, NT, WK, D, W_SYM>, skinny_kernel<XR, NT, WK, D, W_ASYM>, \
+        skinny_kernel<XR, NT, WK, D, W_FP16>,                                            \
+        "skinny_xr" #XR "_nt" #NT "_wk" #WK "_d" #D                                      \
   }
 
 const Variant kVariants[] = {
-    W4A16_VARIANT(1, 1, 16, 2), W4A16_VARIANT(1, 1, 8, 2), W4A16_VARIANT(1, 1, 8, 4),
-    W4A16_VARIANT(1, 1, 4, 4),  W4A16_VARIANT(1, 2, 8, 2), W4A16_VARIANT(1, 2, 4, 4),
-    W4A16_VARIANT(1, 2, 16, 2), W4A16_VARIANT(2, 1, 8, 2), W4A16_VARIANT(2, 1, 16, 2),
-    W4A16_VARIANT(2, 2, 8, 2),  W4A16_VARIANT(2, 1, 4, 4), W4A16_VARIANT(4, 1, 4, 2),
-    W4A16_VARIANT(4, 1, 8, 2),  W4A16_VARIANT(4, 2, 4, 2),
+    W4A16_VARIANT(4, 1, 4, 4),   W4A16_VARIANT(4, 1, 8, 4),   W4A16_VARIANT(4, 2, 4, 4),
+    W4A16_VARIANT(4, 1, 16, 2),  W4A16_VARIANT(8, 1, 4, 4),   W4A16_VARIANT(8, 2, 4, 4),
+    W4A16_VARIANT(8, 1, 8, 4),   W4A16_VARIANT(16, 1, 4, 4),  W4A16_VARIANT(16, 2, 4, 4),
+    W4A16_VARIANT(16, 1, 8, 2),  W4A16_VARIANT(16, 2, 8, 2),  W4A16_VARIANT(16, 1, 16, 2),
+    W4A16_VARIANT(32, 1, 4, 2),  W4A16_VARIANT(32, 2, 4, 2),  W4A16_VARIANT(32, 1, 8, 2),
+    W4A16_VARIANT(32, 2, 8, 2),  W4A16_VARIANT(64, 1, 4, 2),  W4A16_VARIANT(64, 2, 4, 2),
+    W4A16_VARIANT(64, 1, 8, 2),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-int find_variant(int MT, int NT, int WK, int D) {
+int find_variant(int XR, int NT, int WK, int D) {
   for (int i = 0; i < kNumVariants; ++i)
-    if (kVariants[i].MT == MT && kVariants[i].NT == NT && kVariants[i].WK == WK &&
+    if (kVariants[i].XR == XR && kVariants[i].NT == NT && kVariants[i].WK == WK &&
         kVariants[i].D == D)
       return i;
   return -1;
@@ -345,29 +439,37 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
                      SkinnyPlan* p) {
   (void)group;
   if (variant < 0) {
-    // measured on MI355X over the decode shapes: 16 waves per 16-column tile while the
-    // tiles alone fill the 256 compute units, else two tiles per wave to halve the
-    // activation loads per weight byte
-    const long tiles = N / 16;
-    const bool few = tiles <= 256;
-    if (M <= 16)
-      variant = few ? find_variant(1, 1, 16, 2)
-                    : (N % 32 == 0 ? find_variant(1, 2, 8, 2) : find_variant(1, 1, 4, 4));
-    else if (M <= 32)
-      variant = (few || N % 32) ? find_variant(2, 1, 8, 2) : find_variant(2, 2, 8, 2);
-    else
-      variant = find_variant(4, 1, 8, 2);
+    // Chosen from sweeps over the decode shapes on MI355X.  `wide`: enough 16-column
+    // tiles to give every compute unit more than one, so a wave can take two tiles
+    // and halve the activation reads per weight byte; `longk`: many 128-row blocks
+    // per tile, so more waves share a tile's K range.
+    const int XR = M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : M <= 32 ? 32 : 64;
+    const bool wide = N % 32 == 0 && N / 16 > 256;
+    const bool longk = K / KBLK > 48;
+    if (XR <= 8) {
+      if (wide) variant = find_variant(XR, 1, 4, 4);
+      else if (XR == 4) variant = longk ? find_variant(4, 1, 16, 2) : find_variant(4, 1, 8, 4);
+      else variant = longk ? find_variant(8, 1, 8, 4) : find_variant(8, 1, 4, 4);
+    } else if (XR == 16) {
+      variant = wide ? find_variant(16, 2, 4, 4)
+                     : (longk ? find_variant(16, 1, 8, 2) : find_variant(16, 1, 4, 4));
+    } else if (XR == 32) {
+      variant = wide ? find_variant(32, 2, 4, 2) : find_variant(32, 1, 4, 2);
+    } else {
+      variant = find_variant(64, 1, 4, 2);
+    }
   }
   if (variant < 0 || variant >= kNumVariants) return -8;
   const Variant& v = kVariants[variant];
   if (N % (16 * v.NT) != 0) return -2;
   const int Gk = K / KBLK;
+  const int MT = (v.XR + 15) / 16;
   p->variant = variant;
   p->mode = mode;
-  p->MT = v.MT;
+  p->MT = MT;
   p->NT = v.NT;
   p->WK = v.WK;
-  p->mblocks = (M + 16 * v.MT - 1) / (16 * v.MT);
+  p->mblocks = (M + v.XR - 1) / v.XR;
   p->nblocks = N / (16 * v.NT);
   int maxs = Gk / v.WK;
   if (maxs < 1) maxs = 1;
@@ -383,7 +485,7 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
   p->splits = splits;
   p->wgs = p->mblocks * p->nblocks * splits;
   p->threads = 64 * v.WK;
-  p->part_floats = splits > 1 ? (size_t)p->mblocks * p->nblocks * splits * v.NT * v.MT * 256 : 0;
+  p->part_floats = splits > 1 ? (size_t)p->mblocks * p->nblocks * splits * v.NT * MT * 256 : 0;
   p->counters = splits > 1 ? p->mblocks * p->nblocks : 0;
   return 0;
 }
@@ -395,7 +497,7 @@ hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
   KernelFn fn = p.mode == W_FP16 ? v.f16 : (p.mode == W_ASYM ? v.asym : v.sym);
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint4*>(w), sp, reinterpret_cast<const uint2*>(zp), Y,
-                     part, counters, M, N, K, group / KBLK, p.splits, p.nblocks);
+                     part, counters, M, N, K, p.splits, p.nblocks);
   return hipGetLastError();
 }
 

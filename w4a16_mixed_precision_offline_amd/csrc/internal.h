@@ -20,9 +20,11 @@
 //   (canonical words pack rows 8i..8i+7), every repacked word is one canonical
 //   word with its nibbles permuted.
 //
-// Scales: sp[(t * G + g) * 16 + c] = s[g][16t + c], G = K/group (fp16 bits).
-// Zero-points: zp32[(t * G + g) * 2 + h] = z_canonical[g][2t + h], i.e. the 16
-//   zero-points of a tile and group as one 64-bit word, nibble c = column 16t+c.
+// Scales, one row per 128-row block so that the kernels never divide by the group:
+//   sp[(t * Gk + kb) * 16 + c] = s[kb / (group/128)][16t + c], Gk = K/128 (fp16 bits);
+//   a group of 256 or more rows is stored once per 128-row block it spans.
+// Zero-points, likewise per block: zp32[(t * Gk + kb) * 2 + h] = z[kb / (group/128)][2t + h],
+//   i.e. the 16 zero-points of a tile as one 64-bit word, nibble c = column 16t+c.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

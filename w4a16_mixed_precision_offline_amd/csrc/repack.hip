@@ -53,35 +53,37 @@ __global__ void codes_kernel(const uint32_t* __restrict__ src, uint32_t* __restr
   }
 }
 
-// scales: repacked index o = (t*G + g)*16 + c  <->  canonical g*N + 16t + c
+// scales: repacked index o = (t*Gk + kb)*16 + c  <->  canonical s[kb/gpb][16t + c]
+// (one row per 128-row block; a group spanning gpb blocks is stored gpb times, and
+// the inverse reads the first copy)
 template <bool TO_REPACKED>
 __global__ void scales_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                              long total, int G, int N) {
+                              long total, int Gk, int gpb, int N) {
   for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
        o += (long)gridDim.x * blockDim.x) {
     const int c = (int)(o & 15);
-    const long tg = o >> 4;
-    const long t = tg / G;
-    const long g = tg - t * G;
-    const long ci = g * N + 16 * t + c;
+    const long tk = o >> 4;
+    const long t = tk / Gk;
+    const int kb = (int)(tk - t * Gk);
+    const long ci = (long)(kb / gpb) * N + 16 * t + c;
     if (TO_REPACKED) dst[o] = src[ci];
-    else dst[ci] = src[o];
+    else if (kb % gpb == 0) dst[ci] = src[o];
   }
 }
 
-// zero-points: repacked word o = (t*G + g)*2 + h  <->  canonical word g*(N/8) + 2t + h
+// zero-points: repacked word o = (t*Gk + kb)*2 + h  <->  canonical word [kb/gpb][2t + h]
 template <bool TO_REPACKED>
 __global__ void zeros_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
-                             long total, int G, int N) {
+                             long total, int Gk, int gpb, int N) {
   for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
        o += (long)gridDim.x * blockDim.x) {
     const int h = (int)(o & 1);
-    const long tg = o >> 1;
-    const long t = tg / G;
-    const long g = tg - t * G;
-    const long ci = g * (N / 8) + 2 * t + h;
+    const long tk = o >> 1;
+    const long t = tk / Gk;
+    const int kb = (int)(tk - t * Gk);
+    const long ci = (long)(kb / gpb) * (N / 8) + 2 * t + h;
     if (TO_REPACKED) dst[o] = src[ci];
-    else dst[ci] = src[o];
+    else if (kb % gpb == 0) dst[ci] = src[o];
   }
 }
 
@@ -127,25 +129,25 @@ inline int grid_for(long total, int threads) {
 
 hipError_t launch_repack(const int32_t* q, const uint16_t* s, const int32_t* z, uint32_t* wp,
                          uint16_t* sp, uint32_t* zp, int K, int N, int group, hipStream_t st) {
-  const int Gk = K / KBLK, G = K / group;
-  const long wtot = (long)K * N / 8, stot = (long)G * N, ztot = (long)G * N / 8;
+  const int Gk = K / KBLK, gpb = group / KBLK;
+  const long wtot = (long)K * N / 8, stot = (long)Gk * N, ztot = (long)Gk * N / 8;
   codes_kernel<true><<<grid_for(wtot, 256), 256, 0, st>>>(
       reinterpret_cast<const uint32_t*>(q), wp, wtot, Gk, N);
-  scales_kernel<true><<<grid_for(stot, 256), 256, 0, st>>>(s, sp, stot, G, N);
+  scales_kernel<true><<<grid_for(stot, 256), 256, 0, st>>>(s, sp, stot, Gk, gpb, N);
   if (z) zeros_kernel<true><<<grid_for(ztot, 256), 256, 0, st>>>(
-      reinterpret_cast<const uint32_t*>(z), zp, ztot, G, N);
+      reinterpret_cast<const uint32_t*>(z), zp, ztot, Gk, gpb, N);
   return hipGetLastError();
 }
 
 hipError_t launch_unpack(const uint32_t* wp, const uint16_t* sp, const uint32_t* zp, int32_t* q,
                          uint16_t* s, int32_t* z, int K, int N, int group, hipStream_t st) {
-  const int Gk = K / KBLK, G = K / group;
-  const long wtot = (long)K * N / 8, stot = (long)G * N, ztot = (long)G * N / 8;
+  const int Gk = K / KBLK, gpb = group / KBLK;
+  const long wtot = (long)K * N / 8, stot = (long)Gk * N, ztot = (long)Gk * N / 8;
   codes_kernel<false><<<grid_for(wtot, 256), 256, 0, st>>>(
       wp, reinterpret_cast<uint32_t*>(q), wtot, Gk, N);
-  scales_kernel<false><<<grid_for(stot, 256), 256, 0, st>>>(sp, s, stot, G, N);
+  scales_kernel<false><<<grid_for(stot, 256), 256, 0, st>>>(sp, s, stot, Gk, gpb, N);
   if (zp) zeros_kernel<false><<<grid_for(ztot, 256), 256, 0, st>>>(
-      zp, reinterpret_cast<uint32_t*>(z), ztot, G, N);
+      zp, reinterpret_cast<uint32_t*>(z), ztot, Gk, gpb, N);
   return hipGetLastError();
 }
 
