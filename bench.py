@@ -60,6 +60,56 @@ def traffic_from_profiles():
     return t.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "w4a16_gemm_decode_sweep_traffic.json")
+
+
+def pmc_summary(fetch_csv, write_csv):
+    """HBM bytes per fused-GEMM launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by the factor that makes the same counter read the known
+    size of a plain 256 MiB device copy in the same run."""
+    import csv
+
+    def per_dispatch(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = out.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "v": 0.0})
+            d["v"] += float(r["Counter_Value"])
+        return out
+
+    res = {}
+    for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        disp = per_dispatch(path, counter)
+        copies = [d["v"] for d in disp.values() if "copyBuffer" in d["name"]]
+        gemms = [d["v"] for d in disp.values() if "skinny_kernel" in d["name"]]
+        if not copies or not gemms:
+            raise SystemExit(f"{path}: no copy or no GEMM dispatches with {counter}")
+        # the copies are the largest copyBuffer dispatches (the known-size calibration)
+        copies.sort()
+        calib = copies[-3:]
+        factor = (COPY_BYTES / 1024.0) / (sum(calib) / len(calib))
+        res[tag] = dict(factor=factor, kib_per_launch=sum(gemms) / len(gemms), launches=len(gemms),
+                        copy_kib=sum(calib) / len(calib))
+    hbm = (res["fetch"]["kib_per_launch"] * res["fetch"]["factor"] +
+           res["write"]["kib_per_launch"] * res["write"]["factor"]) * 1024.0
+    out = dict(kernel_sha=kernel_sha(), hbm_bytes_per_launch=int(hbm),
+               fetch_factor=round(res["fetch"]["factor"], 4), write_factor=round(res["write"]["factor"], 4),
+               fetch_kib_per_launch=round(res["fetch"]["kib_per_launch"], 1),
+               write_kib_per_launch=round(res["write"]["kib_per_launch"], 1),
+               launches=res["fetch"]["launches"],
+               commands=["rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- "
+                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph --copy-calibration",
+                         "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- "
+                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph --copy-calibration",
+                         "python bench.py --pmc-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
+                         "gpurun_out/pmc_write/run_counter_collection.csv"])
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -71,7 +121,15 @@ def main():
     ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant (tuning)")
     ap.add_argument("--splits", type=int, default=0, help="force split-K slices (tuning)")
     ap.add_argument("--detail", default=None, help="write per-launch detail JSON here")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain device copies of known size (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "this script into profiles/ and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -174,6 +232,14 @@ def main():
             e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / nsteps, ("hip_graph" if graphs is not None else "eager")
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     t_step, mode = time_steps(run_step_w4, args.steps, args.warmup, not args.no_graph)
 
