@@ -139,6 +139,37 @@ int w4a16_dequant(const int32_t* q, const uint16_t* s, const int32_t* z, uint16_
 int w4a16_fp16_gemm(const uint16_t* X, const uint16_t* Wt, uint16_t* Y,
                     int M, int N, int K, void* stream);
 
+/* ---- 2:4 structured sparsity ([P1] "支持 2:4 稀疏加速"; [P2] "4. Support de la
+ *      sparsité 2:4") ----------------------------------------------------------------
+ * Weights whose every aligned run of 4 rows (along K) per column holds at most two
+ * non-zero codes (zero = code 8, symmetric format only) are stored as the two kept
+ * codes per run plus their 2-bit positions, and multiplied on the gfx950 sparse
+ * matrix instructions (v_smfmac_f32_16x16x64_f16): half the code bytes, half the
+ * matrix work.
+ *
+ * w4a16_sparse24_repack: compress the canonical q (same format as w4a16_repack, z
+ *   implied 8) into vp (W4A16_BUF_SPARSE_V bytes, kept codes), idx
+ *   (W4A16_BUF_SPARSE_I bytes, positions) and sp (W4A16_BUF_SPARSE_S bytes, scales).
+ *   Kept positions are the non-zero ones, topped up with the lowest free positions.
+ *   This call synchronizes `stream`: it returns W4A16_ERR_NOT24 when some run holds
+ *   more than two non-zero codes (the outputs are then incomplete).  Offline step.
+ * w4a16_sparse24_unpack: exact inverse: rewrites the canonical q (code 8 at pruned
+ *   positions) and s.
+ * w4a16_sparse24_gemm: Y = X * W from the compressed weights, same rules and
+ *   guarantees as w4a16_gemm (idx 16-byte aligned as well).
+ * w4a16_sparse24_gemm_plan: the same with an explicit plan, as w4a16_gemm_plan.
+ * Shape rules as w4a16_repack. */
+int w4a16_sparse24_repack(const int32_t* q, const uint16_t* s, void* vp, void* idx,
+                          uint16_t* sp, int K, int N, int group, void* stream);
+int w4a16_sparse24_unpack(const void* vp, const void* idx, const uint16_t* sp,
+                          int32_t* q, uint16_t* s, int K, int N, int group, void* stream);
+int w4a16_sparse24_gemm(const uint16_t* X, const void* vp, const void* idx,
+                        const uint16_t* sp, uint16_t* Y, int M, int N, int K, int group,
+                        void* stream);
+int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
+                             const uint16_t* sp, uint16_t* Y, int M, int N, int K, int group,
+                             int variant, int splits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

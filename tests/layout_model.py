@@ -39,3 +39,55 @@ def repack_zeros(Zp: np.ndarray, N: int, blocks_per_group: int = 1) -> np.ndarra
     U = np.repeat(np.ascontiguousarray(Zp).view(np.uint32), blocks_per_group, axis=0)
     G = U.shape[0]
     return np.ascontiguousarray(U.reshape(G, N // 16, 2).transpose(1, 0, 2)).reshape(-1)
+
+
+# ---- 2:4 sparse layout -------------------------------------------------------------
+# Per (tile t, block kb), lane l owns column 16t + l%16 and, for half h, the dense rows
+# 128kb + 64h + 16(l//16) + [0, 16) = four aligned runs g of 4.  From each run it keeps
+# two positions (the non-zero codes, topped up with the lowest free positions,
+# ascending) as elements 2g, 2g+1 of a word (element e at nibble e//2 + 4(e%2)); the
+# positions are 2-bit fields at bits 16h + 2e of the lane's metadata word.
+def _keep_table():
+    table = {}
+    for mask in range(16):
+        nz = [p for p in range(4) if mask >> p & 1]
+        if len(nz) > 2:
+            table[mask] = None
+            continue
+        keep = list(nz)
+        for p in range(4):
+            if len(keep) == 2:
+                break
+            if p not in keep:
+                keep.append(p)
+        table[mask] = tuple(sorted(keep))
+    return table
+
+
+def sparse24_compress(q: np.ndarray, K: int, N: int):
+    """q: codes [K, N] (uint8), every aligned run of 4 along K with <= 2 codes != 8.
+    Returns (vp uint32 [N/16, K/128, 64, 2], meta uint32 [N/16, K/128, 64])."""
+    T, Gk = N // 16, K // 128
+    table = _keep_table()
+    vp = np.zeros((T, Gk, 64, 2), dtype=np.uint32)
+    meta = np.zeros((T, Gk, 64), dtype=np.uint32)
+    for h in range(2):
+        for qg in range(4):          # lane group l // 16
+            for g in range(4):
+                rows = (np.arange(Gk)[:, None] * 128 + 64 * h + 16 * qg + 4 * g +
+                        np.arange(4)[None, :])                      # [Gk, 4]
+                codes = q[rows.reshape(-1), :].reshape(Gk, 4, T, 16)  # [Gk, p, T, c]
+                mask = sum(((codes[:, p] != 8).astype(np.int64) << p) for p in range(4))  # [Gk, T, c]
+                assert all(table[m] is not None for m in np.unique(mask)), "not 2:4"
+                keep = np.array([table[m] for m in range(16)], dtype=object)
+                k0 = np.vectorize(lambda m: table[m][0])(mask)
+                k1 = np.vectorize(lambda m: table[m][1])(mask)
+                for u, kk in ((0, k0), (1, k1)):
+                    e = 2 * g + u
+                    c = np.take_along_axis(codes, kk[:, None], axis=1)[:, 0]   # [Gk, T, c]
+                    lanes = 16 * qg + np.arange(16)
+                    vp[:, :, lanes, h] |= (c.transpose(1, 0, 2).astype(np.uint32)
+                                           << np.uint32(4 * nib_pos(e)))
+                    meta[:, :, lanes] |= (kk.transpose(1, 0, 2).astype(np.uint32)
+                                          << np.uint32(16 * h + 2 * e))
+    return vp, meta

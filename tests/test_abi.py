@@ -139,3 +139,21 @@ def test_plan_validation(raw):
     assert f(A, A, A, None, A, 16, 1024, 1024, 128, -2, 0, None) == -8
     assert f(A, A, A, None, A, 16, 1024, 1024, 128, -1, -1, None) == -8
     assert f(None, A, A, None, A, 16, 1024, 1024, 128, -1, 0, None) == -1
+
+
+def test_sparse_validation(raw):
+    f = raw.w4a16_sparse24_gemm
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    assert f(A, A, None, A, A, 16, 1024, 1024, 128, None) == -1   # no positions
+    assert f(A, A, A, A, A, 0, 1024, 1024, 128, None) == -2
+    assert f(A, A, MIS, A, A, 16, 1024, 1024, 128, None) == -3
+    r = raw.w4a16_sparse24_repack
+    r.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+    assert r(A, A, A, None, A, 1024, 1024, 128, None) == -1
+    assert r(A, A, A, A, A, 1000, 1024, 128, None) == -2
+    u = raw.w4a16_sparse24_unpack
+    u.argtypes = r.argtypes
+    assert u(A, A, A, None, A, 1024, 1024, 128, None) == -1
+    p = raw.w4a16_sparse24_gemm_plan
+    p.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
+    assert p(A, A, A, A, A, 16, 1024, 1024, 128, 999, 0, None) == -8

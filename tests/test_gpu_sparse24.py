@@ -1,0 +1,146 @@
+"""GPU parity of the 2:4-structured-sparse path (compress, decompress, smfmac GEMM)
+against the CPU oracle.  The oracle of a 2:4 weight is the dense oracle on the
+pruned codes (pruned positions carry the zero code 8)."""
+import numpy as np
+import pytest
+
+import oracle
+from gen import Workload, activations, config_runs, weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gh(lib):
+    import gpu_helpers
+    return gpu_helpers
+
+
+def _case(M, K, N, seed=0):
+    w = Workload(cfg=9, M=M, K=K, N=N, sparse24=True)
+    d = weights(w, seed=3000 + seed + K + N)
+    X = activations(w, seed=4000 + seed + M)
+    assert oracle.check_24(d["Qp"], K)
+    return w, d, X
+
+
+def _compress(gh, d, K, N):
+    import w4a16_mixed_precision_offline_amd as w4
+    vp, idx, sp = w4.alloc_sparse24(K, N, 128)
+    w4.w4a16_sparse24_repack(gh.dev(d["Qp"]), gh.dev(d["s"]), vp, idx, sp, K, N, 128)
+    return vp, idx, sp
+
+
+def _sgemm(gh, X, comp, M, N, K, variant=-1, splits=0, Y=None):
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    vp, idx, sp = comp
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    if variant == -1 and splits == 0:
+        w4.w4a16_sparse24_gemm(X, vp, idx, sp, Y, M, N, K, 128)
+    else:
+        w4.w4a16_sparse24_gemm_plan(X, vp, idx, sp, Y, M, N, K, 128, variant, splits)
+    return Y
+
+
+@pytest.mark.parametrize("K,N", [(256, 32), (1024, 512), (1152, 48)])
+def test_compress_matches_layout_model(gh, K, N):
+    import layout_model as lm
+    _, d, _ = _case(1, K, N)
+    vp, idx, sp = _compress(gh, d, K, N)
+    mvp, mmeta = lm.sparse24_compress(d["q"], K, N)
+    assert np.array_equal(gh.host(vp).view(np.uint32), mvp.reshape(-1))
+    assert np.array_equal(gh.host(idx).view(np.uint32), mmeta.reshape(-1))
+    assert np.array_equal(gh.host(sp).view(np.uint16), lm.repack_scales(d["s"], N).view(np.uint16))
+
+
+@pytest.mark.parametrize("K,N", [(4096, 4096), (1152, 48)])
+def test_compress_decompress_roundtrip(gh, K, N):
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, _ = _case(1, K, N)
+    vp, idx, sp = _compress(gh, d, K, N)
+    q = torch.zeros((K // 8, N), dtype=torch.int32, device="cuda")
+    s = torch.zeros((K // 128, N), dtype=torch.float16, device="cuda")
+    w4.w4a16_sparse24_unpack(vp, idx, sp, q, s, K, N, 128)
+    assert np.array_equal(gh.host(q), d["Qp"])
+    assert np.array_equal(gh.host(s).view(np.uint16), d["s"].view(np.uint16))
+
+
+def test_not_24_is_rejected(gh):
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, _ = _case(1, 256, 32)
+    q = d["q"].copy()
+    # make three non-zero codes in one run: positions 0..2 of column 5
+    q[0:3, 5] = [1, 2, 3]
+    from gen import pack_nibbles_along_k
+    d2 = dict(d, Qp=pack_nibbles_along_k(q))
+    assert not oracle.check_24(d2["Qp"], 256)
+    with pytest.raises(w4.W4A16Error) as e:
+        _compress(gh, d2, 256, 32)
+    assert e.value.code == -7
+
+
+def test_onehot_rows_bit_exact(gh):
+    K, N = 1024, 256
+    _, d, _ = _case(16, K, N)
+    ks = [0, 1, 2, 3, 4, 63, 64, 127, 128, 300, 511, 512, 777, 900, 1022, 1023]
+    X = np.zeros((16, K), np.float16)
+    for m, k in enumerate(ks):
+        X[m, k] = 1
+    W16 = oracle.dequant_fp16(d["Qp"], d["s"], None, K, N, 128)
+    Y = gh.host(_sgemm(gh, gh.dev(X), _compress(gh, d, K, N), 16, N, K))
+    assert np.array_equal(Y.astype(np.float64), W16[ks].astype(np.float64))
+
+
+SMALL = [(1, 1024, 512), (5, 1152, 512), (16, 1024, 512), (33, 1280, 512), (64, 1024, 512),
+         (100, 1536, 512), (16, 2048, 528), (3, 384, 48)]
+
+
+@pytest.mark.parametrize("M,K,N", SMALL)
+def test_parity_every_variant_and_split(gh, M, K, N):
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, X = _case(M, K, N)
+    comp = _compress(gh, d, K, N)
+    Xd = gh.dev(X)
+    Yref = oracle.gemm(X, d["Qp"], d["s"], None, 128)
+    B = oracle.error_bound(X, d["Qp"], d["s"], None, 128)
+    ran = 0
+    for v in range(w4.w4a16_gemm_variants()):
+        name = w4.w4a16_gemm_variant_name(v)
+        nt = int(name.split("_nt")[1].split("_")[0])
+        for splits in (1, 2, 3):
+            Y = gh.nan_filled(M, N)
+            if N % (16 * nt):
+                with pytest.raises(w4.W4A16Error):
+                    _sgemm(gh, Xd, comp, M, N, K, variant=v, splits=splits, Y=Y)
+                continue
+            _sgemm(gh, Xd, comp, M, N, K, variant=v, splits=splits, Y=Y)
+            ok, info = oracle.accept(gh.host(Y), Yref, B)
+            assert ok, (name, splits, info)
+            ran += 1
+    assert ran > 0
+
+
+def test_config4_sparse_and_dense_on_same_weights(gh):
+    """Every run of the 2:4 configuration at full size, sparse kernel and dense kernel
+    on the same pruned weights; both against the oracle (sampled for large outputs)."""
+    rng = np.random.default_rng(4)
+    cache = {}
+    for w in config_runs(4):
+        if (w.K, w.N) not in cache:
+            cache.clear()
+            d = weights(w)
+            cache[(w.K, w.N)] = (d, _compress(gh, d, w.K, w.N), gh.repack(d, w.K, w.N))
+        d, comp, dense = cache[(w.K, w.N)]
+        X = activations(w)
+        Xd = gh.dev(X)
+        Ys = gh.host(_sgemm(gh, Xd, comp, w.M, w.N, w.K))
+        Yd = gh.host(gh.gemm(Xd, dense, w.M, w.N, w.K))
+        rows = sorted(set([0, w.M - 1]) | set(rng.choice(w.M, size=min(w.M, 16), replace=False).tolist()))
+        cols = sorted(set([0, w.N - 1]) | set(rng.choice(w.N, size=64, replace=False).tolist()))
+        Yref, Bd = oracle.gemm_sampled(X, d["Qp"], d["s"], None, 128, rows, cols)
+        for Y in (Ys, Yd):
+            ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, Bd)
+            assert ok, (w.name, info)

@@ -43,3 +43,29 @@ def test_scale_and_zero_models():
     for t in range(N // 16):
         for g in range(G):
             assert list(zp[t, g]) == [g * (N // 8) + 2 * t, g * (N // 8) + 2 * t + 1]
+
+
+def test_sparse24_model_roundtrip_by_hand():
+    # decompress the model's output by hand and compare with the input codes
+    from gen import Workload, weights
+    w = Workload(cfg=4, M=1, K=256, N=32, sparse24=True)
+    d = weights(w)
+    vp, meta = lm.sparse24_compress(d["q"], w.K, w.N)
+    q = np.full((w.K, w.N), 8, dtype=np.uint8)
+    for t in range(w.N // 16):
+        for kb in range(w.K // 128):
+            for l in range(64):
+                n = 16 * t + l % 16
+                for h in range(2):
+                    word = int(vp[t, kb, l, h])
+                    for e in range(8):
+                        p = (int(meta[t, kb, l]) >> (16 * h + 2 * e)) & 3
+                        k = kb * 128 + 64 * h + 16 * (l // 16) + 4 * (e // 2) + p
+                        q[k, n] = (word >> (4 * lm.nib_pos(e))) & 15
+    assert np.array_equal(q, d["q"])
+    # positions within a run are ascending and distinct
+    for h in range(2):
+        for g in range(4):
+            p0 = (meta >> np.uint32(16 * h + 4 * g)) & np.uint32(3)
+            p1 = (meta >> np.uint32(16 * h + 4 * g + 2)) & np.uint32(3)
+            assert np.all(p0 < p1)

@@ -36,6 +36,10 @@ _SIGS = {
     "w4a16_gemm_describe": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I)]),
     "w4a16_dequant": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
     "w4a16_fp16_gemm": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "w4a16_sparse24_repack": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "w4a16_sparse24_unpack": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "w4a16_sparse24_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "w4a16_sparse24_gemm_plan": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -137,6 +141,28 @@ def w4a16_fp16_gemm(X, Wt, Y, M, N, K, stream=None):
                                                    _stream(stream)))
 
 
+def w4a16_sparse24_repack(q, s, vp, idx, sp, K, N, group, stream=None):
+    _check("w4a16_sparse24_repack", _lib.w4a16_sparse24_repack(
+        _ptr(q), _ptr(s), _ptr(vp), _ptr(idx), _ptr(sp), K, N, group, _stream(stream)))
+
+
+def w4a16_sparse24_unpack(vp, idx, sp, q, s, K, N, group, stream=None):
+    _check("w4a16_sparse24_unpack", _lib.w4a16_sparse24_unpack(
+        _ptr(vp), _ptr(idx), _ptr(sp), _ptr(q), _ptr(s), K, N, group, _stream(stream)))
+
+
+def w4a16_sparse24_gemm(X, vp, idx, sp, Y, M, N, K, group, stream=None):
+    _check("w4a16_sparse24_gemm", _lib.w4a16_sparse24_gemm(
+        _ptr(X), _ptr(vp), _ptr(idx), _ptr(sp), _ptr(Y), M, N, K, group, _stream(stream)))
+
+
+def w4a16_sparse24_gemm_plan(X, vp, idx, sp, Y, M, N, K, group, variant=-1, splits=0,
+                             stream=None):
+    _check("w4a16_sparse24_gemm_plan", _lib.w4a16_sparse24_gemm_plan(
+        _ptr(X), _ptr(vp), _ptr(idx), _ptr(sp), _ptr(Y), M, N, K, group, variant, splits,
+        _stream(stream)))
+
+
 # ---- allocation helper (device memory through torch) ---------------------------
 def alloc_packed(K: int, N: int, group: int, asym: bool, device="cuda"):
     """Empty device buffers (torch uint8) for the repacked wp, sp and zp."""
@@ -146,3 +172,11 @@ def alloc_packed(K: int, N: int, group: int, asym: bool, device="cuda"):
     zp = (torch.empty(w4a16_packed_bytes(K, N, group, BUF_Z), dtype=torch.uint8, device=device)
           if asym else None)
     return wp, sp, zp
+
+
+def alloc_sparse24(K: int, N: int, group: int, device="cuda"):
+    """Empty device buffers (torch uint8) for the compressed vp, idx and sp."""
+    import torch
+    mk = lambda which: torch.empty(w4a16_packed_bytes(K, N, group, which), dtype=torch.uint8,
+                                   device=device)
+    return mk(BUF_SPARSE_V), mk(BUF_SPARSE_I), mk(BUF_SPARSE_S)

@@ -256,4 +256,77 @@ int w4a16_fp16_gemm(const uint16_t* X, const uint16_t* Wt, uint16_t* Y, int M, i
   return run_skinny(W_FP16, X, Wt, nullptr, nullptr, Y, M, N, K, KBLK, -1, 0, stream);
 }
 
+// ---- 2:4 structured sparsity ----------------------------------------------------------
+namespace {
+std::map<int, int*> g_bad;  // per-device counter of runs that are not 2:4
+}
+
+int w4a16_sparse24_repack(const int32_t* q, const uint16_t* s, void* vp, void* idx, uint16_t* sp,
+                          int K, int N, int group, void* stream) {
+  if (!q || !s || !vp || !idx || !sp) return W4A16_ERR_NULL;
+  int rc = check_weight_shape(K, N, group);
+  if (rc) return rc;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(vp) || !aligned16(idx) || !aligned16(sp))
+    return W4A16_ERR_ALIGN;
+  int dev;
+  if ((rc = check_device(&dev))) return rc;
+  int* bad = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_bad.find(dev);
+    if (it == g_bad.end()) {
+      if (hipMalloc(&bad, sizeof(int)) != hipSuccess) {
+        (void)hipGetLastError();
+        return W4A16_ERR_WORKSPACE;
+      }
+      g_bad[dev] = bad;
+    } else {
+      bad = it->second;
+    }
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = launched(launch_sparse_compress(q, s, static_cast<uint32_t*>(vp),
+                                            static_cast<uint32_t*>(idx), sp, bad, K, N, group,
+                                            st))))
+    return rc;
+  int h = 0;
+  if (hipMemcpyAsync(&h, bad, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return W4A16_ERR_LAUNCH;
+  }
+  return h ? W4A16_ERR_NOT24 : W4A16_OK;
+}
+
+int w4a16_sparse24_unpack(const void* vp, const void* idx, const uint16_t* sp, int32_t* q,
+                          uint16_t* s, int K, int N, int group, void* stream) {
+  if (!q || !s || !vp || !idx || !sp) return W4A16_ERR_NULL;
+  int rc = check_weight_shape(K, N, group);
+  if (rc) return rc;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(vp) || !aligned16(idx) || !aligned16(sp))
+    return W4A16_ERR_ALIGN;
+  if ((rc = check_device(nullptr))) return rc;
+  return launched(launch_sparse_decompress(static_cast<const uint32_t*>(vp),
+                                           static_cast<const uint32_t*>(idx), sp, q, s, K, N,
+                                           group, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_sparse24_gemm(const uint16_t* X, const void* vp, const void* idx, const uint16_t* sp,
+                        uint16_t* Y, int M, int N, int K, int group, void* stream) {
+  if (!idx) return W4A16_ERR_NULL;
+  int rc = check_gemm_args(X, vp, sp, idx, Y, M, N, K, group);
+  if (rc) return rc;
+  return run_skinny(W_SP24, X, vp, sp, idx, Y, M, N, K, group, -1, 0, stream);
+}
+
+int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
+                             const uint16_t* sp, uint16_t* Y, int M, int N, int K, int group,
+                             int variant, int splits, void* stream) {
+  if (!idx) return W4A16_ERR_NULL;
+  int rc = check_gemm_args(X, vp, sp, idx, Y, M, N, K, group);
+  if (rc) return rc;
+  if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
+  return run_skinny(W_SP24, X, vp, sp, idx, Y, M, N, K, group, variant, splits, stream);
+}
+
 }  // extern "C"

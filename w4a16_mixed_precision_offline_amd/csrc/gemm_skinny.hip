@@ -49,6 +49,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half16 __attribute__((ext_vector_type(16)));
 
 // 16-byte loads: streamed (non-temporal) for weights, cached for activations
 __device__ __forceinline__ u32x4 load16_nt(const void* p) {
@@ -108,9 +109,11 @@ constexpr int XSTRIDE = 272;  // bytes per X row in the LDS tile (256 + 16 again
 
 template <int XR, int NT, int MODE>
 struct Stage {
-  u32x4 w[NT][MODE == W_FP16 ? 4 : 1];  // packed codes (or fp16 rows for the baseline)
+  u32x4 w[NT][MODE == W_FP16 ? 4 : 1];  // packed codes (fp16 rows for the baseline; for 2:4,
+                                        // .x/.y = kept codes of the two halves, .z = positions)
   uint16_t s[NT];                       // fp16 scale bits of the lane's column
   uint2 z[NT];                          // 16 zero-points of the tile (ASYM)
+  uint2 s4[NT];                         // 2:4: the four scales of the lane's four columns
   u32x4 x[XR / 4];                      // X rows 4c + lane/16, 16-byte chunk lane%16
 };
 
@@ -138,6 +141,15 @@ __device__ __forceinline__ void load_stage(Stage<XR, NT, MODE>& S, int kb, bool 
       for (int j = 0; j < 4; ++j)
         S.w[t][j] = bload16<true>(R.w, R.lane_w + (uint32_t)(t * 16 * K * 2 + 64 * j),
                                   (uint32_t)kb * KBLK * 2);
+    } else if (MODE == W_SP24) {
+      const uint32_t blk = (uint32_t)(t * Gk + kb);
+      const uint2 c = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(R.w, R.lane_w, blk * 512u, 2));
+      S.w[t][0].x = c.x;
+      S.w[t][0].y = c.y;
+      S.w[t][0].z = __builtin_amdgcn_raw_buffer_load_b32(R.z, (uint32_t)lane * 4, blk * 256u, 2);
+      S.s4[t] = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(R.s, (uint32_t)(lane >> 4) * 8, blk * 32u, 0));
     } else {
       const uint32_t blk = (uint32_t)(t * Gk + kb);
       S.w[t][0] = bload16<true>(R.w, R.lane_w, blk * 1024u);
@@ -168,6 +180,33 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
     for (int j = 0; j < 4; ++j)
       a[mt][j] = *reinterpret_cast<const half8*>(xlds + (mt * 16 + (lane & 15)) * XSTRIDE +
                                                   64 * j + 16 * (lane >> 4));
+  if (MODE == W_SP24) {
+    // 2:4: W is the sparse A operand (lane: column 4(l/16)+r ... see the epilogue), X the
+    // dense B operand: its 16 halves for half h are the fragments 2h and 2h+1 above.
+    const half2v c0 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    const half2v c1 = {(_Float16)-72.0f, (_Float16)-72.0f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const half8 w0 = dequant_word(S.w[t][0].x, c0, c1, magic);
+      const half8 w1 = dequant_word(S.w[t][0].y, c0, c1, magic);
+      const int meta = (int)S.w[t][0].z;
+      const half2v s01 = __builtin_bit_cast(half2v, S.s4[t].x);
+      const half2v s23 = __builtin_bit_cast(half2v, S.s4[t].y);
+      const float4v sc = {(float)s01[0], (float)s01[1], (float)s23[0], (float)s23[1]};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const half16 xb0 = __builtin_shufflevector(a[mt][0], a[mt][1], 0, 1, 2, 3, 4, 5, 6, 7, 8,
+                                                   9, 10, 11, 12, 13, 14, 15);
+        const half16 xb1 = __builtin_shufflevector(a[mt][2], a[mt][3], 0, 1, 2, 3, 4, 5, 6, 7, 8,
+                                                   9, 10, 11, 12, 13, 14, 15);
+        float4v g = {0.f, 0.f, 0.f, 0.f};
+        g = __builtin_amdgcn_smfmac_f32_16x16x64_f16(w0, xb0, g, meta, 0, 0);
+        g = __builtin_amdgcn_smfmac_f32_16x16x64_f16(w1, xb1, g, meta, 0, 1);
+        acc[t][mt] += sc * g;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     half8 b[4];
@@ -261,6 +300,14 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     const char* wbase = reinterpret_cast<const char*>(W) + (size_t)t0 * 16 * K * 2;
     R.w = make_rsrc(wbase, (uint32_t)(NT * 16 * K * 2));
     R.lane_w = (uint32_t)(((lane & 15) * K + 8 * (lane >> 4)) * 2);
+  } else if (MODE == W_SP24) {
+    // kept codes (512 B per block), positions (256 B per block, passed as Zp), scales
+    R.w = make_rsrc(reinterpret_cast<const char*>(W) + (size_t)t0 * Gk * 512,
+                    (uint32_t)(NT * Gk * 512));
+    R.z = make_rsrc(reinterpret_cast<const char*>(Zp) + (size_t)t0 * Gk * 256,
+                    (uint32_t)(NT * Gk * 256));
+    R.s = make_rsrc(Sp + (size_t)t0 * Gk * 16, (uint32_t)(NT * Gk * 32));
+    R.lane_w = (uint32_t)lane * 8;
   } else {
     R.w = make_rsrc(reinterpret_cast<const char*>(W) + (size_t)t0 * Gk * 1024,
                     (uint32_t)(NT * Gk * 1024));
@@ -380,6 +427,26 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   // ---- epilogue: lane holds rows 4*(lane/16)+r of each m-tile, column lane%16 ----
   // (only the XR rows of this block: with XR < 16 the rest of the MFMA tile is padding)
   const int row_end = M < m0 + XR ? M : m0 + XR;
+  if (MODE == W_SP24) {
+    // 2:4 kernels compute Y^T: the lane holds row 16mt + lane%16 and the four
+    // consecutive columns 4(lane/16) .. +3 of the tile (one 8-byte store)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = m0 + mt * 16 + (lane & 15);
+        const int col = (t0 + t) * 16 + 4 * (lane >> 4);
+        if (row < row_end) {
+          uint2 v;
+          v.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[t][mt][0]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[t][mt][1]) << 16);
+          v.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[t][mt][2]) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)acc[t][mt][3]) << 16);
+          *reinterpret_cast<uint2*>(Y + (long)row * N + col) = v;
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -398,14 +465,14 @@ typedef void (*KernelFn)(const uint16_t*, const uint4*, const uint16_t*, const u
 
 struct Variant {
   int XR, NT, WK, D;
-  KernelFn sym, asym, f16;
+  KernelFn sym, asym, f16, sp24;
   const char* name;
 };
 
 #define W4A16_VARIANT(XR, NT, WK, D)                                                     \
   Variant {                                                                              \
     XR, NT, WK, D, skinny_kernel<XR, NT, WK, D, W_SYM>, skinny_kernel<XR, NT, WK, D, W_ASYM>, \
-        skinny_kernel<XR, NT, WK, D, W_FP16>,                                            \
+        skinny_kernel<XR, NT, WK, D, W_FP16>, skinny_kernel<XR, NT, WK, D, W_SP24>,      \
         "skinny_xr" #XR "_nt" #NT "_wk" #WK "_d" #D                                      \
   }
 
@@ -494,7 +561,10 @@ hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                          const uint16_t* sp, const uint32_t* zp, uint16_t* Y, float* part,
                          int* counters, int M, int N, int K, int group, hipStream_t st) {
   const Variant& v = kVariants[p.variant];
-  KernelFn fn = p.mode == W_FP16 ? v.f16 : (p.mode == W_ASYM ? v.asym : v.sym);
+  KernelFn fn = p.mode == W_FP16 ? v.f16
+               : p.mode == W_ASYM ? v.asym
+               : p.mode == W_SP24 ? v.sp24
+                                  : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint4*>(w), sp, reinterpret_cast<const uint2*>(zp), Y,
                      part, counters, M, N, K, p.splits, p.nblocks);

@@ -45,11 +45,19 @@ hipError_t launch_repack(const int32_t* q, const uint16_t* s, const int32_t* z,
 hipError_t launch_unpack(const uint32_t* wp, const uint16_t* sp, const uint32_t* zp,
                          int32_t* q, uint16_t* s, int32_t* z,
                          int K, int N, int group, hipStream_t st);
+// 2:4 sparse compress (counts runs with more than two non-zero codes into *bad)
+// and its inverse; scales are repacked as for the dense layout.
+hipError_t launch_sparse_compress(const int32_t* q, const uint16_t* s, uint32_t* vp,
+                                  uint32_t* meta, uint16_t* sp, int* bad, int K, int N, int group,
+                                  hipStream_t st);
+hipError_t launch_sparse_decompress(const uint32_t* vp, const uint32_t* meta, const uint16_t* sp,
+                                    int32_t* q, uint16_t* s, int K, int N, int group,
+                                    hipStream_t st);
 hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
                           uint16_t* W, int K, int N, int group, hipStream_t st);
 
 // Fused skinny GEMM.  `part` / `counters` form the split-K workspace.
-enum WMode { W_SYM = 0, W_ASYM = 1, W_FP16 = 2 };  // weight format of a launch
+enum WMode { W_SYM = 0, W_ASYM = 1, W_FP16 = 2, W_SP24 = 3 };  // weight format of a launch
 struct SkinnyPlan {
   int variant;   // index into the variant table
   int mode;      // WMode

@@ -118,6 +118,99 @@ __global__ void dequant_kernel(const uint32_t* __restrict__ q, const uint16_t* _
   }
 }
 
+// ---- 2:4 sparse compress / decompress (symmetric codes, zero code 8) ----------------
+// Layout (own design, follows the operand semantics of v_smfmac_f32_16x16x64_f16,
+// measured on MI355X): per (tile t, 128-row block kb), lane l owns column
+// n = 16t + l%16 and, for each half h (0, 1) of the block, the 16 dense rows
+// kb*128 + 64h + 16(l/16) + [0, 16), i.e. four aligned runs of 4.  From run g it keeps
+// two codes (the non-zero ones, topped up with the lowest free positions), in
+// ascending position, as elements 2g and 2g+1 of a word (nibble order as the dense
+// layout: element e at nibble e/2 + 4(e%2)), and writes the positions as 2-bit fields
+// at bits 16h + 2e of one metadata word per lane and block.
+//   vp  : [N/16][K/128][64 lanes][2 words]   idx : [N/16][K/128][64 lanes] words
+__global__ void sparse_compress_kernel(const uint32_t* __restrict__ q, uint32_t* __restrict__ vp,
+                                       uint32_t* __restrict__ meta, int* __restrict__ bad,
+                                       long total, int Gk, int N) {
+  for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int l = (int)(o & 63);
+    const long b = o >> 6;
+    const long t = b / Gk;
+    const int kb = (int)(b - t * Gk);
+    const long n = 16 * t + (l & 15);
+    uint32_t mw = 0;
+    int nbad = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // canonical words holding rows kb*128 + 64h + 16(l/16) + 0..7 and 8..15
+      const long i0 = (long)kb * 16 + 8 * h + 2 * (l >> 4);
+      const uint64_t codes = (uint64_t)q[i0 * N + n] | ((uint64_t)q[(i0 + 1) * N + n] << 32);
+      uint32_t word = 0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        int keep[2] = {0, 0}, nk = 0;
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t c = (uint32_t)(codes >> (4 * (4 * g + p))) & 15u;
+          if (c != 8u) {
+            if (nk < 2) keep[nk] = p;
+            ++nk;
+          }
+        }
+        if (nk > 2) ++nbad;
+        // top up with the lowest positions not already kept (ascending order kept)
+        for (int p = 0; nk < 2 && p < 4; ++p) {
+          if (nk == 1 && keep[0] == p) continue;
+          if (nk == 1 && p < keep[0]) { keep[1] = keep[0]; keep[0] = p; }
+          else keep[nk] = p;
+          ++nk;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = 2 * g + u;
+          const uint32_t c = (uint32_t)(codes >> (4 * (4 * g + keep[u]))) & 15u;
+          word |= c << (4 * nib_pos(e));
+          mw |= (uint32_t)keep[u] << (16 * h + 2 * e);
+        }
+      }
+      vp[o * 2 + h] = word;
+    }
+    meta[o] = mw;
+    if (nbad) atomicAdd(bad, nbad);
+  }
+}
+
+__global__ void sparse_decompress_kernel(const uint32_t* __restrict__ vp,
+                                         const uint32_t* __restrict__ meta,
+                                         uint32_t* __restrict__ q, long total, int Gk, int N) {
+  for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int l = (int)(o & 63);
+    const long b = o >> 6;
+    const long t = b / Gk;
+    const int kb = (int)(b - t * Gk);
+    const long n = 16 * t + (l & 15);
+    const uint32_t mw = meta[o];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t word = vp[o * 2 + h];
+      uint64_t codes = 0x8888888888888888ull;  // every position zero (code 8) ...
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {             // ... except the kept ones
+        const int g = e >> 1;
+        const int p = (int)((mw >> (16 * h + 2 * e)) & 3u);
+        const uint64_t c = (word >> (4 * nib_pos(e))) & 15u;
+        const int sh = 4 * (4 * g + p);
+        codes = (codes & ~(15ull << sh)) | (c << sh);
+      }
+      const long i0 = (long)kb * 16 + 8 * h + 2 * (l >> 4);
+      q[i0 * N + n] = (uint32_t)codes;
+      q[(i0 + 1) * N + n] = (uint32_t)(codes >> 32);
+    }
+  }
+}
+
+__global__ void zero_int_kernel(int* p) { *p = 0; }
+
 inline int grid_for(long total, int threads) {
   long b = (total + threads - 1) / threads;
   if (b > 65536) b = 65536;
@@ -148,6 +241,29 @@ hipError_t launch_unpack(const uint32_t* wp, const uint16_t* sp, const uint32_t*
   scales_kernel<false><<<grid_for(stot, 256), 256, 0, st>>>(sp, s, stot, Gk, gpb, N);
   if (zp) zeros_kernel<false><<<grid_for(ztot, 256), 256, 0, st>>>(
       zp, reinterpret_cast<uint32_t*>(z), ztot, Gk, gpb, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_compress(const int32_t* q, const uint16_t* s, uint32_t* vp,
+                                  uint32_t* meta, uint16_t* sp, int* bad, int K, int N, int group,
+                                  hipStream_t st) {
+  const int Gk = K / KBLK, gpb = group / KBLK;
+  const long tot = (long)(N / 16) * Gk * 64, stot = (long)Gk * N;
+  zero_int_kernel<<<1, 1, 0, st>>>(bad);
+  sparse_compress_kernel<<<grid_for(tot, 256), 256, 0, st>>>(
+      reinterpret_cast<const uint32_t*>(q), vp, meta, bad, tot, Gk, N);
+  scales_kernel<true><<<grid_for(stot, 256), 256, 0, st>>>(s, sp, stot, Gk, gpb, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_decompress(const uint32_t* vp, const uint32_t* meta, const uint16_t* sp,
+                                    int32_t* q, uint16_t* s, int K, int N, int group,
+                                    hipStream_t st) {
+  const int Gk = K / KBLK, gpb = group / KBLK;
+  const long tot = (long)(N / 16) * Gk * 64, stot = (long)Gk * N;
+  sparse_decompress_kernel<<<grid_for(tot, 256), 256, 0, st>>>(
+      vp, meta, reinterpret_cast<uint32_t*>(q), tot, Gk, N);
+  scales_kernel<false><<<grid_for(stot, 256), 256, 0, st>>>(sp, s, stot, Gk, gpb, N);
   return hipGetLastError();
 }
 
