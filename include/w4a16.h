@@ -111,8 +111,14 @@ int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void
 
 /* Same as w4a16_gemm with an explicit kernel plan (tuning and tests):
  *   variant : -1 = automatic, else an index < w4a16_gemm_variants();
- *   splits  : 0 = automatic, else the number of K slices reduced across
- *             workgroups (clamped to the number of 128-row blocks per wave). */
+ *   splits  : 0 = automatic.  For a "skinny_*" variant (one workgroup per
+ *             (row block, column block, K slice)), the number of K slices reduced
+ *             across workgroups, clamped to the number of 128-row blocks per wave.
+ *             For a "tiled_*" variant (persistent workgroups over tiles, the
+ *             (tile, k-block) work cut into equal stripes), the number of
+ *             workgroups.
+ * Automatic plans use the tiled kernel from M = 128 rows on.  The tiled variants
+ * take the symmetric and zero-point formats only (W4A16_ERR_ARG for 2:4). */
 int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                     uint16_t* Y, int M, int N, int K, int group,
                     int variant, int splits, void* stream);
@@ -121,7 +127,8 @@ int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const
 int w4a16_gemm_variants(void);
 const char* w4a16_gemm_variant_name(int variant);
 
-/* Describe the automatic plan for a shape: out[0] = variant, out[1] = splits,
+/* Describe the automatic plan for a shape: out[0] = variant, out[1] = the splits
+ * value that reproduces it in w4a16_gemm_plan,
  * out[2] = workgroups launched, out[3] = threads per workgroup.  Host only. */
 int w4a16_gemm_describe(int M, int N, int K, int group, int* out4);
 

@@ -119,7 +119,8 @@ def test_parity_every_variant_and_split(gh, M, K, N, asym):
     ran = 0
     for v in range(w4.w4a16_gemm_variants()):
         name = w4.w4a16_gemm_variant_name(v)
-        nt = int(name.split("_nt")[1].split("_")[0])
+        # tiled variants take any N % 16; their `splits` is the number of workgroups
+        nt = 1 if name.startswith("tiled") else int(name.split("_nt")[1].split("_")[0])
         for splits in (1, 2, 3, 7):
             Y = gh.nan_filled(M, N)
             if N % (16 * nt):
@@ -131,6 +132,57 @@ def test_parity_every_variant_and_split(gh, M, K, N, asym):
             assert ok, (name, splits, info)
             ran += 1
     assert ran > 0
+
+
+# ---- tiled kernel: several row tiles, ragged M and N, stream-K stripes ----------------
+TILED = [(300, 2048, 1040, False), (257, 1536, 512, True), (128, 1024, 768, False),
+         (1000, 1024, 2048, True), (130, 3072, 272, False)]
+
+
+@pytest.mark.parametrize("M,K,N,asym", TILED)
+def test_tiled_parity_grids(gh, M, K, N, asym):
+    """Every tiled variant at several workgroup counts: grids that leave whole tiles
+    data-parallel, grids that cut tiles into stripes at odd k-blocks, and the automatic
+    plan.  Each grid is run twice and must repeat bit for bit."""
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, X = _case(M, K, N, asym)
+    packed = gh.repack(d, K, N)
+    Xd = gh.dev(X)
+    Yref = oracle.gemm(X, d["Qp"], d["s"], d["Zp"], 128)
+    B = oracle.error_bound(X, d["Qp"], d["s"], d["Zp"], 128)
+    tiled = [v for v in range(w4.w4a16_gemm_variants())
+             if w4.w4a16_gemm_variant_name(v).startswith("tiled")]
+    assert tiled
+    for v in tiled:
+        for grid in (0, 1, 3, 5, 8, 16, 24):
+            Y = gh.nan_filled(M, N)
+            gh.gemm(Xd, packed, M, N, K, variant=v, splits=grid, Y=Y)
+            first = gh.host(Y).view(np.uint16).copy()
+            ok, info = oracle.accept(first.view(np.float16), Yref, B)
+            assert ok, (w4.w4a16_gemm_variant_name(v), grid, info)
+            Y2 = gh.nan_filled(M, N)
+            gh.gemm(Xd, packed, M, N, K, variant=v, splits=grid, Y=Y2)
+            assert np.array_equal(gh.host(Y2).view(np.uint16), first), (v, grid)
+
+
+def test_tiled_one_hot_is_exact(gh):
+    """One-hot activation rows select weight rows: through the tiled kernel (stripes
+    included) Y[m, :] must equal RNE((q - z) * s) of row k_m bit for bit."""
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 200, 1024, 528
+    _, d, _ = _case(M, K, N, True)
+    rng = np.random.default_rng(7)
+    ks = rng.integers(0, K, size=M)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    W16 = oracle.dequant_fp16(d["Qp"], d["s"], d["Zp"], K, N, 128)
+    packed = gh.repack(d, K, N)
+    for v in range(w4.w4a16_gemm_variants()):
+        if not w4.w4a16_gemm_variant_name(v).startswith("tiled"):
+            continue
+        for grid in (1, 7):
+            Y = gh.host(gh.gemm(gh.dev(X), packed, M, N, K, variant=v, splits=grid))
+            assert np.array_equal(Y.view(np.uint16), W16[ks].view(np.uint16)), (v, grid)
 
 
 def test_config0(gh):

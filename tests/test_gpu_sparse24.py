@@ -109,6 +109,10 @@ def test_parity_every_variant_and_split(gh, M, K, N):
     ran = 0
     for v in range(w4.w4a16_gemm_variants()):
         name = w4.w4a16_gemm_variant_name(v)
+        if name.startswith("tiled"):   # dense formats only
+            with pytest.raises(w4.W4A16Error):
+                _sgemm(gh, Xd, comp, M, N, K, variant=v, splits=1, Y=gh.nan_filled(M, N))
+            continue
         nt = int(name.split("_nt")[1].split("_")[0])
         for splits in (1, 2, 3):
             Y = gh.nan_filled(M, N)

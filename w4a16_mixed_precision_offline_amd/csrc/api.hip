@@ -124,6 +124,37 @@ int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, c
                                 M, N, K, group, st));
 }
 
+// Batches of at least this many rows go to the tiled kernel; smaller ones to the
+// skinny (memory-bound) kernel.
+constexpr int kTiledMinM = 128;
+
+int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
+              uint16_t* Y, int M, int N, int K, int variant, int grid, void* stream) {
+  TiledPlan plan;
+  int rc = tiled_make_plan(M, N, K, mode, variant, grid, &plan);
+  if (rc) return rc;
+  int dev;
+  if ((rc = check_device(&dev))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int* cnt;
+  float* part;
+  if ((rc = get_workspace(dev, st, plan.counters, plan.part_floats, &cnt, &part))) return rc;
+  return launched(tiled_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, cnt, st));
+}
+
+// Variant numbering of the ABI: the skinny variants first, then the tiled ones.
+// For a tiled variant the `splits` argument is the number of persistent workgroups.
+int run_fused(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
+              uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
+              void* stream) {
+  const int ns = skinny_variant_count();
+  if (variant >= ns)
+    return run_tiled(mode, X, w, sp, zp, Y, M, N, K, variant - ns, splits, stream);
+  if (variant < 0 && splits == 0 && M >= kTiledMinM && (mode == W_SYM || mode == W_ASYM))
+    return run_tiled(mode, X, w, sp, zp, Y, M, N, K, -1, 0, stream);
+  return run_skinny(mode, X, w, sp, zp, Y, M, N, K, group, variant, splits, stream);
+}
+
 int check_gemm_args(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                     const uint16_t* Y, int M, int N, int K, int group) {
   if (!X || !wp || !sp || !Y) return W4A16_ERR_NULL;
@@ -206,7 +237,7 @@ int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void
                uint16_t* Y, int M, int N, int K, int group, void* stream) {
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
-  return run_skinny(zp ? W_ASYM : W_SYM, X, wp, sp, zp, Y, M, N, K, group, -1, 0, stream);
+  return run_fused(zp ? W_ASYM : W_SYM, X, wp, sp, zp, Y, M, N, K, group, -1, 0, stream);
 }
 
 int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
@@ -214,19 +245,31 @@ int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const
                     void* stream) {
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
-  if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
-  return run_skinny(zp ? W_ASYM : W_SYM, X, wp, sp, zp, Y, M, N, K, group, variant, splits,
-                    stream);
+  if (variant < -1 || variant >= w4a16_gemm_variants() || splits < 0) return W4A16_ERR_ARG;
+  return run_fused(zp ? W_ASYM : W_SYM, X, wp, sp, zp, Y, M, N, K, group, variant, splits,
+                   stream);
 }
 
-int w4a16_gemm_variants(void) { return skinny_variant_count(); }
-const char* w4a16_gemm_variant_name(int variant) { return skinny_variant_name(variant); }
+int w4a16_gemm_variants(void) { return skinny_variant_count() + tiled_variant_count(); }
+const char* w4a16_gemm_variant_name(int variant) {
+  const int ns = skinny_variant_count();
+  return variant >= ns ? tiled_variant_name(variant - ns) : skinny_variant_name(variant);
+}
 
 int w4a16_gemm_describe(int M, int N, int K, int group, int* out4) {
   if (!out4) return W4A16_ERR_NULL;
   int rc = check_weight_shape(K, N, group);
   if (rc) return rc;
   if (M <= 0) return W4A16_ERR_SHAPE;
+  if (M >= kTiledMinM) {
+    TiledPlan t;
+    if ((rc = tiled_make_plan(M, N, K, W_SYM, -1, 0, &t))) return rc;
+    out4[0] = skinny_variant_count() + t.variant;
+    out4[1] = t.args.grid;
+    out4[2] = t.wgs;
+    out4[3] = t.threads;
+    return W4A16_OK;
+  }
   SkinnyPlan p;
   if ((rc = skinny_make_plan(M, N, K, group, W_SYM, -1, 0, &p))) return rc;
   out4[0] = p.variant;
@@ -325,7 +368,9 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
   if (!idx) return W4A16_ERR_NULL;
   int rc = check_gemm_args(X, vp, sp, idx, Y, M, N, K, group);
   if (rc) return rc;
-  if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
+  if (variant < -1 || variant >= w4a16_gemm_variants() || splits < 0) return W4A16_ERR_ARG;
+  // only the skinny variants implement the 2:4 format
+  if (variant >= skinny_variant_count()) return W4A16_ERR_ARG;
   return run_skinny(W_SP24, X, vp, sp, idx, Y, M, N, K, group, variant, splits, stream);
 }
 

@@ -79,4 +79,30 @@ hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                          const uint16_t* sp, const uint32_t* zp, uint16_t* Y, float* part,
                          int* counters, int M, int N, int K, int group, hipStream_t st);
 
+// Fused tiled GEMM for larger M (sym / asym weights only).  Tile geometry and the
+// data-parallel / stream-K work split are fixed by the plan.
+struct TiledArgs {
+  int M, N, K;
+  int tiles_m, tiles_n, group_m;
+  int grid;        // persistent workgroups
+  int dp_rounds;   // rounds of whole tiles handed out data-parallel
+  long long sk_units;   // (tile, k-block) units of the remaining tiles
+  long long sk_per_wg;  // units per workgroup stripe
+};
+struct TiledPlan {
+  int variant;  // index into the tiled variant table
+  int mode;     // W_SYM or W_ASYM
+  TiledArgs args;
+  int wgs, threads;
+  size_t part_floats;  // workspace floats for partial tiles (two slots per workgroup)
+  int counters;        // arrival counters (one per stream-K tile)
+};
+int tiled_variant_count();
+const char* tiled_variant_name(int v);
+// variant < 0: automatic; grid <= 0: automatic number of workgroups.
+int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p);
+hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
+                        const uint32_t* zp, uint16_t* Y, float* part, int* counters,
+                        hipStream_t st);
+
 }  // namespace w4a16
