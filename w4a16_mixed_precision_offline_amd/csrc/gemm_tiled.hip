@@ -52,12 +52,40 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // cache-policy bits of buffer instructions on gfx950
-constexpr int kNT = 2;    // streamed (non-temporal)
 constexpr int kSC1 = 16;  // coherent across the XCDs' L2s (relaxed agent-scope access)
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                           0x00020000);
+}
+
+// Direct-to-LDS loads.  The 128-bit buffer descriptor is built by hand (raw
+// buffer, stride 0, num_records = bytes) so that it can be handed to inline asm;
+// lane L of a 16-byte (4-byte) load writes LDS bytes [16L, 16L+16) ([4L, 4L+4))
+// after the base held in M0, and lanes out of range write zeros.  The loads are
+// issued from inline asm because the compiler, unable to tell the destination
+// stage from the stage being read, would otherwise wait for every just-issued
+// load before the next LDS read and serialize loading with computing; their
+// completion is ordered explicitly (s_waitcnt vmcnt + s_barrier) by the caller.
+// Writing M0 needs one wait state before the load that uses it.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, 0x00020000u};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+__device__ __forceinline__ void dma16(u32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+#endif
+}
+__device__ __forceinline__ void dma4(u32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+#endif
 }
 
 __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
@@ -87,93 +115,118 @@ __device__ __forceinline__ half8 dequant_scaled(uint32_t w, half2v c0, half2v c1
   return r;
 }
 
-constexpr int XSTRIDE = 272;  // bytes per activation row in LDS (256 + 16 against bank conflicts)
 constexpr int WAVES = 4;
 
-// Weights of one k-block for the NTW column tiles of a wave.
-template <int NTW, int MODE>
-struct WStage {
-  u32x4 w[NTW];
-  uint16_t s[NTW];
-  uint2 z[NTW];
-};
-
-// Per-wave view of the current tile's weights: resources cover the wave's valid
-// column tiles; the per-lane offsets hold the column-tile part of the address
-// (kOutOfRange for tiles past N, which then read zeros), the scalar offset the
-// k-block part.
+// Per-wave weight sources of the current tile: resources over the wave's valid
+// column tiles, per-lane offsets of the column-tile part of each address
+// (kOutOfRange for tiles past N and for idle lanes: they read zeros), the
+// k-block part goes to the scalar offset.
 template <int NTW>
-struct WRsrc {
-  rsrc_t w, s, z;
-  uint32_t wo[NTW], so[NTW], zo[NTW];
+struct WSrc {
+  u32x4 w, s, z;
+  uint32_t wo[NTW];  // codes: tile t, 16 bytes of lane L
+  uint32_t so;       // scales: lane L < 8*NTW loads the scale pair 2(L%8), +1 of tile L/8
+  uint32_t zo;       // zero-points: lane L < 2*NTW loads half L%2 of tile L/2's 64-bit word
+};
+
+// LDS of one pipeline stage, per wave: NTW 1 KiB code blocks, then 256 bytes of
+// scales (tile t, column c at 32t + 2c; the DMA writes 4 bytes per lane, so the
+// slot spans all 64 lanes) and 256 bytes of zero-points (tile t at 8t).
+template <int NTW>
+struct WLds {
+  static constexpr int CODES = NTW * 1024;
+  static constexpr int SCALES = CODES;
+  static constexpr int ZEROS = CODES + 256;
+  static constexpr int BYTES = CODES + 512;
 };
 
 template <int NTW, int MODE>
-__device__ __forceinline__ void load_w(WStage<NTW, MODE>& S, const WRsrc<NTW>& R, int kb) {
+__device__ __forceinline__ void dma_w(uint32_t wl, const WSrc<NTW>& R, int kb) {
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    S.w[t] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.w, R.wo[t], (uint32_t)kb * 1024u, kNT));
-    S.s[t] = __builtin_amdgcn_raw_buffer_load_b16(R.s, R.so[t], (uint32_t)kb * 32u, 0);
-    if (MODE == W_ASYM)
-      S.z[t] = __builtin_bit_cast(
-          uint2, __builtin_amdgcn_raw_buffer_load_b64(R.z, R.zo[t], (uint32_t)kb * 8u, 0));
-  }
+  for (int t = 0; t < NTW; ++t) dma16(R.w, wl + t * 1024, R.wo[t], (uint32_t)kb * 1024u);
+  dma4(R.s, wl + WLds<NTW>::SCALES, R.so, (uint32_t)kb * 32u);
+  if (MODE == W_ASYM) dma4(R.z, wl + WLds<NTW>::ZEROS, R.zo, (uint32_t)kb * 8u);
 }
 
-// Activation rows of one k-block: thread tid loads rows tid/16 + 16c, bytes
-// 16(tid%16) .. +15 of the block's 256 bytes.
+// Activation tile in LDS: BM rows of 256 bytes (one 128-row k-block of X), no
+// padding; the 16-byte chunk c of row r sits at chunk position c ^ (r % 16), so
+// that the 16 lanes of a fragment read (16 rows, one chunk) hit 16 different
+// chunk positions, i.e. all 64 banks once.
+__device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 256 + ((c ^ (r & 15)) << 4)); }
+
+// Direct-to-LDS loads of one k-block of X: each wave instruction writes 1 KiB of
+// LDS (lane L -> bytes 16L..16L+15 after the destination base), i.e. 4 rows; lane L
+// of instruction c therefore fetches row 4(wave*MT + c) + L/16 and the global chunk
+// that belongs at chunk position L%16.  Rows past M read zeros (out of range).
 template <int MT>
-__device__ __forceinline__ void load_x(u32x4 (&xr)[MT], rsrc_t rx, const uint32_t (&xoff)[MT],
-                                       int kb) {
+__device__ __forceinline__ void dma_x(uint32_t buf, u32x4 rx, const uint32_t (&xoff)[MT], int wave,
+                                      int kb) {
 #pragma unroll
-  for (int c = 0; c < MT; ++c)
-    xr[c] = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[c], (uint32_t)kb * 256u, 0));
+  for (int c = 0; c < MT; ++c) dma16(rx, buf + (wave * MT + c) * 1024, xoff[c], (uint32_t)kb * 256u);
 }
 
-template <int MT>
-__device__ __forceinline__ void store_x(char* buf, const u32x4 (&xr)[MT], int tid) {
-#pragma unroll
-  for (int c = 0; c < MT; ++c)
-    *reinterpret_cast<u32x4*>(buf + ((tid >> 4) + 16 * c) * XSTRIDE + (tid & 15) * 16) = xr[c];
-}
-
-// One k-block: 4 k-steps of 32; per step the wave unpacks its NTW weight
-// fragments once and runs them against the MT activation fragments.
+// One k-block: the wave's weight codes, scales (and zero-points) come from its
+// LDS slot, the activation fragments from the shared tile; 4 k-steps of 32.
+// Software pipeline, one group per (k-step j, row tile i): the group issues the
+// LDS read of the fragment two groups ahead, unpacks one column tile of step
+// j+1, and runs the NTW MFMAs of (j, i).  Scheduling barriers between the groups
+// keep that order, so LDS latency hides behind the matrix work.
 template <int MT, int NTW, int MODE>
-__device__ __forceinline__ void compute_kblock(const char* buf, const WStage<NTW, MODE>& S,
-                                               float4v (&acc)[MT][NTW], int lane, uint32_t magic) {
+__device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
+                                               float4v (&acc)[MT][NTW], const uint32_t (&aoff)[4],
+                                               int lane, uint32_t magic) {
+  static_assert(MT >= NTW, "one column tile is unpacked per row-tile group");
+  constexpr int G = 4 * MT;  // groups per k-block
+  u32x4 wv[NTW];
   half2v c0[NTW], c1[NTW], s2[NTW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
+    wv[t] = *reinterpret_cast<const u32x4*>(wl + t * 1024 + lane * 16);
+    const _Float16 sc =
+        *reinterpret_cast<const _Float16*>(wl + WLds<NTW>::SCALES + t * 32 + (lane & 15) * 2);
+    s2[t] = half2v{sc, sc};
     int zq = 8;
     if (MODE == W_ASYM) {
       const int c = lane & 15;
-      const uint32_t zw = c < 8 ? S.z[t].x : S.z[t].y;
+      const uint32_t zw =
+          *reinterpret_cast<const uint32_t*>(wl + WLds<NTW>::ZEROS + t * 8 + (c >> 3) * 4);
       zq = (int)((zw >> (4 * (c & 7))) & 15u);
     }
     const _Float16 a0 = (_Float16)(float)(-1024 - zq);
     const _Float16 a1 = (_Float16)(float)(-64 - zq);
     c0[t] = half2v{a0, a0};
     c1[t] = half2v{a1, a1};
-    const _Float16 sc = __builtin_bit_cast(_Float16, S.s[t]);
-    s2[t] = half2v{sc, sc};
   }
+  half8 ar[3];
+  ar[0] = *reinterpret_cast<const half8*>(xb + aoff[0]);
+  ar[1] = *reinterpret_cast<const half8*>(xb + aoff[0] + 4096);
+  half8 b[2][NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) b[0][t] = dequant_scaled(wv[t][0], c0[t], c1[t], s2[t], magic);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    half8 b[NTW];
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) b[t] = dequant_scaled(S.w[t][j], c0[t], c1[t], s2[t], magic);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      const half8 a = *reinterpret_cast<const half8*>(buf + (16 * i + (lane & 15)) * XSTRIDE +
-                                                      64 * j + 16 * (lane >> 4));
+      const int g = j * MT + i;
+      if (g + 2 < G) {
+        const int gj = (g + 2) / MT, gi = (g + 2) % MT;
+        ar[(g + 2) % 3] = *reinterpret_cast<const half8*>(xb + aoff[gj] + gi * 4096);
+      }
+      if (j < 3 && i < NTW)
+        b[(j + 1) & 1][i] = dequant_scaled(wv[i][j + 1], c0[i], c1[i], s2[i], magic);
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
-        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[t], a, acc[i][t], 0, 0, 0);
+        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j & 1][t], ar[g % 3], acc[i][t], 0,
+                                                          0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+}
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding)
+__device__ __forceinline__ constexpr int vmcnt_enc(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
@@ -201,9 +254,12 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     float* __restrict__ part, int* __restrict__ counters, TiledArgs a) {
   constexpr int BM = 16 * MT;
   constexpr int BN = WAVES * 16 * NTW;
-  constexpr int XBUF = BM * XSTRIDE;
-  constexpr int PIECE = BM * BN;  // floats of one partial tile
-  __shared__ __attribute__((aligned(16))) char lds[2 * XBUF];
+  constexpr int XBUF = BM * 256;   // one k-block of the activation tile
+  constexpr int NSTAGE = 3;        // LDS buffers / weight register stages
+  constexpr int PIECE = BM * BN;   // floats of one partial tile
+  constexpr int STAGE = XBUF + WAVES * WLds<NTW>::BYTES;  // LDS bytes of one stage
+  constexpr int NV = MT + NTW + (MODE == W_ASYM ? 2 : 1);  // loads per stage per thread
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];
   __shared__ int s_old;
 
   const int tid = threadIdx.x;
@@ -212,6 +268,11 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
   const int Gk = a.K / KBLK;
   const int ntiles16 = a.N / 16;
   const uint32_t magic = 0x64006400u;
+  // per-lane LDS offsets of the fragment reads of k-step j (row tile 0; row tile i
+  // adds 16 rows = 4096 bytes): row lane%16, chunk 4j + lane/16
+  uint32_t aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) aoff[j] = swz(lane & 15, 4 * j + (lane >> 4));
 
   // logical workgroup index: consecutive indices on one XCD (the hardware deals
   // workgroups to the 8 XCDs round-robin)
@@ -224,38 +285,43 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     tile_coords(tt, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
     const int m0 = tm * BM;
     const int rows = a.M - m0 < BM ? a.M - m0 : BM;
-    const rsrc_t rx = make_rsrc(X + (size_t)m0 * a.K, (uint32_t)((size_t)rows * a.K * 2));
+    const u32x4 rx = rsrc_words(X + (size_t)m0 * a.K, (uint32_t)((size_t)rows * a.K * 2));
     uint32_t xoff[MT];
 #pragma unroll
     for (int c = 0; c < MT; ++c) {
-      const int r = (tid >> 4) + 16 * c;
-      xoff[c] = r < rows ? (uint32_t)(((size_t)r * a.K + 8 * (tid & 15)) * 2) : kOutOfRange;
+      const int r = 4 * (wave * MT + c) + (lane >> 4);
+      const int cg = (lane & 15) ^ (r & 15);  // global chunk stored at position lane%16
+      xoff[c] = r < rows ? (uint32_t)(((size_t)r * a.K + 8 * cg) * 2) : kOutOfRange;
     }
     const int t_first = tn * (BN / 16) + wave * NTW;  // first 16-column tile of this wave
     int nvalid = ntiles16 - t_first;
     nvalid = nvalid < 0 ? 0 : (nvalid > NTW ? NTW : nvalid);
-    WRsrc<NTW> R;
-    R.w = make_rsrc(reinterpret_cast<const char*>(W) + (size_t)t_first * Gk * 1024,
-                    (uint32_t)(nvalid * Gk * 1024));
-    R.s = make_rsrc(Sp + (size_t)t_first * Gk * 16, (uint32_t)(nvalid * Gk * 32));
+    WSrc<NTW> R;
+    R.w = rsrc_words(reinterpret_cast<const char*>(W) + (size_t)t_first * Gk * 1024,
+                     (uint32_t)(nvalid * Gk * 1024));
+    R.s = rsrc_words(Sp + (size_t)t_first * Gk * 16, (uint32_t)(nvalid * Gk * 32));
     if (MODE == W_ASYM)
-      R.z = make_rsrc(reinterpret_cast<const char*>(Zp) + (size_t)t_first * Gk * 8,
-                      (uint32_t)(nvalid * Gk * 8));
+      R.z = rsrc_words(reinterpret_cast<const char*>(Zp) + (size_t)t_first * Gk * 8,
+                       (uint32_t)(nvalid * Gk * 8));
     else
       R.z = R.s;
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const bool ok = t < nvalid;
-      R.wo[t] = ok ? (uint32_t)(t * Gk * 1024 + lane * 16) : kOutOfRange;
-      R.so[t] = ok ? (uint32_t)(t * Gk * 32 + (lane & 15) * 2) : kOutOfRange;
-      R.zo[t] = ok ? (uint32_t)(t * Gk * 8) : kOutOfRange;
+    for (int t = 0; t < NTW; ++t)
+      R.wo[t] = t < nvalid ? (uint32_t)(t * Gk * 1024 + lane * 16) : kOutOfRange;
+    {
+      const int ts = lane >> 3, tz = lane >> 1;
+      R.so = (lane < 8 * NTW && ts < nvalid) ? (uint32_t)(ts * Gk * 32 + (lane & 7) * 4)
+                                             : kOutOfRange;
+      R.zo = (lane < 2 * NTW && tz < nvalid) ? (uint32_t)(tz * Gk * 8 + (lane & 1) * 4)
+                                             : kOutOfRange;
     }
-    // zero-size resources: loads past the segment return zeros without a request,
-    // which keeps the pipelined loop free of branches
-    const rsrc_t rx0 = make_rsrc(X, 0);
-    WRsrc<NTW> R0 = R;
-    R0.w = make_rsrc(W, 0);
-    R0.s = make_rsrc(Sp, 0);
+    // zero-size resources: loads past the segment return zeros without a memory
+    // request (their LDS destination still receives zeros), so the number of loads
+    // in flight is the same in every iteration and the wait counts below are static
+    const u32x4 rx0 = rsrc_words(X, 0);
+    WSrc<NTW> R0 = R;
+    R0.w = rsrc_words(W, 0);
+    R0.s = rsrc_words(Sp, 0);
     R0.z = R0.s;
 
 #pragma unroll
@@ -264,39 +330,49 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       for (int t = 0; t < NTW; ++t) acc[i][t] = float4v{0.f, 0.f, 0.f, 0.f};
 
     const int nk = kb1 - kb0;
-    WStage<NTW, MODE> S0, S1;
-    u32x4 xr[MT];
-    // prologue: block kb0 into LDS buffer 0 and registers S0; block kb0+1 in flight
-    load_x<MT>(xr, rx, xoff, kb0);
-    load_w(S0, R, kb0);
-    __syncthreads();  // the previous segment's last reads of the LDS buffers are done
-    store_x<MT>(lds, xr, tid);
-    load_x<MT>(xr, nk > 1 ? rx : rx0, xoff, kb0 + 1);
-    load_w(S1, nk > 1 ? R : R0, kb0 + 1);
-    __syncthreads();
+    const uint32_t lds0 = lds_addr(lds);
+    const uint32_t wl0 = lds0 + XBUF + wave * WLds<NTW>::BYTES;  // this wave's weight slot, stage 0
+    // every wave is done with the LDS buffers of the previous segment
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // prologue: k-blocks kb0 and kb0+1 in flight
+    dma_x<MT>(lds0, rx, xoff, wave, kb0);
+    dma_w<NTW, MODE>(wl0, R, kb0);
+    dma_x<MT>(lds0 + STAGE, nk > 1 ? rx : rx0, xoff, wave, kb0 + 1);
+    dma_w<NTW, MODE>(wl0 + STAGE, nk > 1 ? R : R0, kb0 + 1);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // k-block i is in LDS buffer i%2 and in S(i%2); the activation registers hold
-    // block i+1, the other weight stage block i+1 as well
+    // step d of the ring handles k-block kbi, held in stage d; k-block kbi + 2 is
+    // issued into stage (d+2)%3.  At the wait, the loads of kbi and kbi + 1 are in
+    // flight (NV per stage, oldest first); after it, every wave's loads of kbi have
+    // landed once all waves pass the barrier, and every wave has finished reading
+    // the stage about to be refilled.
+    auto step = [&](int d, int kbi, bool issue_live) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(NV));
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_sched_barrier(0);
+      const int dn = (d + 2) % NSTAGE;
+      dma_x<MT>(lds0 + dn * STAGE, issue_live ? rx : rx0, xoff, wave, kbi + 2);
+      dma_w<NTW, MODE>(wl0 + dn * STAGE, issue_live ? R : R0, kbi + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_kblock<MT, NTW, MODE>(lds + d * STAGE,
+                                    lds + d * STAGE + XBUF + wave * WLds<NTW>::BYTES, acc, aoff,
+                                    lane, magic);
+      __builtin_amdgcn_sched_barrier(0);
+    };
     int i = 0;
-    for (; i + 1 < nk; i += 2) {
-      compute_kblock<MT, NTW, MODE>(lds, S0, acc, lane, magic);
-      store_x<MT>(lds + XBUF, xr, tid);
-      {
-        const bool live = i + 2 < nk;
-        load_x<MT>(xr, live ? rx : rx0, xoff, kb0 + i + 2);
-        load_w(S0, live ? R : R0, kb0 + i + 2);
-      }
-      __syncthreads();
-      compute_kblock<MT, NTW, MODE>(lds + XBUF, S1, acc, lane, magic);
-      store_x<MT>(lds, xr, tid);
-      {
-        const bool live = i + 3 < nk;
-        load_x<MT>(xr, live ? rx : rx0, xoff, kb0 + i + 3);
-        load_w(S1, live ? R : R0, kb0 + i + 3);
-      }
-      __syncthreads();
+    for (; i + 2 < nk; i += 3) {
+      step(0, kb0 + i, i + 2 < nk);
+      step(1, kb0 + i + 1, i + 3 < nk);
+      step(2, kb0 + i + 2, i + 4 < nk);
     }
-    if (i < nk) compute_kblock<MT, NTW, MODE>(lds, S0, acc, lane, magic);
+    if (i < nk) step(0, kb0 + i, false);
+    if (i + 1 < nk) step(1, kb0 + i + 1, false);
+    // drain: no load of this segment is left in flight
+    __builtin_amdgcn_s_waitcnt(0);
   };
 
   // Y store of a finished tile: lane holds row 16i + lane%16 and the four columns
