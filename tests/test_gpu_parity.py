@@ -136,14 +136,16 @@ def test_parity_every_variant_and_split(gh, M, K, N, asym):
 
 # ---- tiled kernel: several row tiles, ragged M and N, stream-K stripes ----------------
 TILED = [(300, 2048, 1040, False), (257, 1536, 512, True), (128, 1024, 768, False),
-         (1000, 1024, 2048, True), (130, 3072, 272, False)]
+         (1000, 1024, 2048, True), (130, 3072, 272, False), (1, 1024, 512, False),
+         (130, 1024, 512, True)]
 
 
 @pytest.mark.parametrize("M,K,N,asym", TILED)
 def test_tiled_parity_grids(gh, M, K, N, asym):
     """Every tiled variant at several workgroup counts: grids that leave whole tiles
-    data-parallel, grids that cut tiles into stripes at odd k-blocks, and the automatic
-    plan.  Each grid is run twice and must repeat bit for bit."""
+    data-parallel, grids that cut tiles into stripes at odd k-blocks (so that one
+    workgroup finishes a partial tile and then starts another), and the automatic plan.
+    Each grid is run twice and must repeat bit for bit."""
     import w4a16_mixed_precision_offline_amd as w4
     _, d, X = _case(M, K, N, asym)
     packed = gh.repack(d, K, N)
@@ -154,7 +156,7 @@ def test_tiled_parity_grids(gh, M, K, N, asym):
              if w4.w4a16_gemm_variant_name(v).startswith("tiled")]
     assert tiled
     for v in tiled:
-        for grid in (0, 1, 3, 5, 8, 16, 24):
+        for grid in (0, 1, 3, 5, 6, 8, 16, 24):
             Y = gh.nan_filled(M, N)
             gh.gemm(Xd, packed, M, N, K, variant=v, splits=grid, Y=Y)
             first = gh.host(Y).view(np.uint16).copy()

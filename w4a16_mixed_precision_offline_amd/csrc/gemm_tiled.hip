@@ -165,6 +165,34 @@ __device__ __forceinline__ void dma_x(uint32_t buf, u32x4 rx, const uint32_t (&x
   for (int c = 0; c < MT; ++c) dma16(rx, buf + (wave * MT + c) * 1024, xoff[c], (uint32_t)kb * 256u);
 }
 
+// The direct-to-LDS loads of one k-block for one wave, as a list of NV single
+// instructions (MT activation quarters-of-rows blocks, NTW code blocks, the
+// scales and, for zero-points, one more) so that they can be spread over the
+// matrix work of the preceding k-block instead of being issued in one burst
+// (a burst of 4 waves x NV loads fills the address queue of the CU and stalls
+// the waves before their MFMAs start).
+template <int MT, int NTW, int MODE>
+struct DmaPlan {
+  static constexpr int NV = MT + NTW + (MODE == W_ASYM ? 2 : 1);
+  u32x4 rx;
+  uint32_t xoff[MT];
+  WSrc<NTW> R;
+  uint32_t xdst, wdst;  // LDS addresses: activation stage, this wave's weight slot
+  int wave, kb;
+  __device__ __forceinline__ void issue(int q) const {
+    if (q < MT) {
+      dma16(rx, xdst + (wave * MT + q) * 1024, xoff[q], (uint32_t)kb * 256u);
+    } else if (q < MT + NTW) {
+      const int t = q - MT;
+      dma16(R.w, wdst + t * 1024, R.wo[t], (uint32_t)kb * 1024u);
+    } else if (q == MT + NTW) {
+      dma4(R.s, wdst + WLds<NTW>::SCALES, R.so, (uint32_t)kb * 32u);
+    } else if (MODE == W_ASYM && q == MT + NTW + 1) {
+      dma4(R.z, wdst + WLds<NTW>::ZEROS, R.zo, (uint32_t)kb * 8u);
+    }
+  }
+};
+
 // One k-block: the wave's weight codes, scales (and zero-points) come from its
 // LDS slot, the activation fragments from the shared tile; 4 k-steps of 32.
 // Software pipeline, one group per (k-step j, row tile i): the group issues the
@@ -174,8 +202,10 @@ __device__ __forceinline__ void dma_x(uint32_t buf, u32x4 rx, const uint32_t (&x
 template <int MT, int NTW, int MODE>
 __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
                                                float4v (&acc)[MT][NTW], const uint32_t (&aoff)[4],
-                                               int lane, uint32_t magic) {
+                                               int lane, uint32_t magic,
+                                               const DmaPlan<MT, NTW, MODE>& dma) {
   static_assert(MT >= NTW, "one column tile is unpacked per row-tile group");
+  static_assert(DmaPlan<MT, NTW, MODE>::NV <= 4 * MT, "one load per group");
   constexpr int G = 4 * MT;  // groups per k-block
   u32x4 wv[NTW];
   half2v c0[NTW], c1[NTW], s2[NTW];
@@ -209,6 +239,7 @@ __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int g = j * MT + i;
+      if (g < DmaPlan<MT, NTW, MODE>::NV) dma.issue(g);  // one load of a later k-block
       if (g + 2 < G) {
         const int gj = (g + 2) / MT, gi = (g + 2) % MT;
         ar[(g + 2) % 3] = *reinterpret_cast<const half8*>(xb + aoff[gj] + gi * 4096);
@@ -243,8 +274,9 @@ __device__ __forceinline__ void tile_coords(int tt, int tiles_m, int tiles_n, in
   const int first = g * group_m;
   const int gm = tiles_m - first < group_m ? tiles_m - first : group_m;
   const int r = tt - g * per_group;
-  tm = first + r % gm;
-  tn = r / gm;
+  // integer division runs on the vector unit; the results are uniform, say so
+  tm = __builtin_amdgcn_readfirstlane(first + r % gm);
+  tn = __builtin_amdgcn_readfirstlane(r / gm);
 }
 
 template <int MT, int NTW, int MODE>
@@ -355,12 +387,18 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_sched_barrier(0);
       const int dn = (d + 2) % NSTAGE;
-      dma_x<MT>(lds0 + dn * STAGE, issue_live ? rx : rx0, xoff, wave, kbi + 2);
-      dma_w<NTW, MODE>(wl0 + dn * STAGE, issue_live ? R : R0, kbi + 2);
-      __builtin_amdgcn_sched_barrier(0);
+      DmaPlan<MT, NTW, MODE> plan;
+      plan.rx = issue_live ? rx : rx0;
+#pragma unroll
+      for (int c = 0; c < MT; ++c) plan.xoff[c] = xoff[c];
+      plan.R = issue_live ? R : R0;
+      plan.xdst = lds0 + dn * STAGE;
+      plan.wdst = wl0 + dn * STAGE;
+      plan.wave = wave;
+      plan.kb = kbi + 2;
       compute_kblock<MT, NTW, MODE>(lds + d * STAGE,
                                     lds + d * STAGE + XBUF + wave * WLds<NTW>::BYTES, acc, aoff,
-                                    lane, magic);
+                                    lane, magic, plan);
       __builtin_amdgcn_sched_barrier(0);
     };
     int i = 0;
@@ -411,24 +449,28 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
   if (a.sk_units == 0) return;
 
   // ---- stream-K stripe [u0, u1) over the remaining tiles' (tile, k-block) units ----
-  const long u0 = (long)w * a.sk_per_wg;
-  long u1 = u0 + a.sk_per_wg;
-  if (u1 > a.sk_units) u1 = a.sk_units;
-  for (long u = u0; u < u1;) {
-    const int tl = (int)(u / Gk);  // tile index inside the stream-K part
-    const int kb0 = (int)(u - (long)tl * Gk);
-    const long rest = u1 - u;
-    const int kb1 = rest < Gk - kb0 ? kb0 + (int)rest : Gk;
+  // (32-bit bookkeeping, bounded by the plan; every quantity is uniform)
+  const uint32_t U = (uint32_t)a.sk_per_wg;
+  const uint32_t nunits = (uint32_t)a.sk_units;
+  const uint32_t u0 = (uint32_t)w * U;
+  const uint32_t u1 = u0 + U < nunits ? u0 + U : nunits;
+  for (uint32_t u = u0; u < u1;) {
+    const int tl = __builtin_amdgcn_readfirstlane((int)(u / (uint32_t)Gk));  // tile in the stream-K part
+    const int kb0 = __builtin_amdgcn_readfirstlane((int)(u - (uint32_t)tl * Gk));
+    const uint32_t rest = u1 - u;
+    const int kb1 = rest < (uint32_t)(Gk - kb0) ? kb0 + (int)rest : Gk;
     const int tt = a.dp_rounds * a.grid + tl;
     run_segment(tt, kb0, kb1, acc);
     const bool first_seg = (u == u0);
-    u += kb1 - kb0;
+    u += (uint32_t)(kb1 - kb0);
     if (kb0 == 0 && kb1 == Gk) {
       store_y(tt, acc);
       continue;
     }
-    // partial tile: write this piece, count it, and finish the tile if last
-    const int slot = 2 * w + (first_seg ? 0 : 1);
+    // partial tile: write this piece, count it, and finish the tile if last.
+    // (Slot indices are made explicitly uniform: a descriptor the compiler cannot
+    // prove uniform is wrapped in a per-lane loop around every access.)
+    const int slot = __builtin_amdgcn_readfirstlane(2 * w + (first_seg ? 0 : 1));
     {
       const rsrc_t rp = make_rsrc(part + (size_t)slot * PIECE, PIECE * 4);
 #pragma unroll
@@ -439,8 +481,8 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
               __builtin_bit_cast(u32x4, acc[i][t]), rp,
               (uint32_t)((((wave * MT + i) * NTW + t) * 64 + lane) * 16), 0u, kSC1);
     }
-    const int w_first = (int)(((long)tl * Gk) / a.sk_per_wg);
-    const int w_last = (int)(((long)(tl + 1) * Gk - 1) / a.sk_per_wg);
+    const int w_first = __builtin_amdgcn_readfirstlane((int)(((uint32_t)tl * Gk) / U));
+    const int w_last = __builtin_amdgcn_readfirstlane((int)(((uint32_t)(tl + 1) * Gk - 1) / U));
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's sc1 stores have completed
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -448,12 +490,12 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     if (tid == 0)
       s_old = __hip_atomic_fetch_add(counters + tl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int old = s_old;
+    const int old = __builtin_amdgcn_readfirstlane(s_old);
     if (old != w_last - w_first) continue;
     // last arriver: sum the pieces in stripe order w_first .. w_last
     for (int wp = w_first; wp <= w_last; ++wp) {
-      const int first_tile_of_wp = (int)(((long)wp * a.sk_per_wg) / Gk);
-      const int sl = 2 * wp + (tl == first_tile_of_wp ? 0 : 1);
+      const int first_tile_of_wp = (int)(((uint32_t)wp * U) / (uint32_t)Gk);
+      const int sl = __builtin_amdgcn_readfirstlane(2 * wp + (tl == first_tile_of_wp ? 0 : 1));
       const rsrc_t rp = make_rsrc(part + (size_t)sl * PIECE, PIECE * 4);
 #pragma unroll
       for (int i = 0; i < MT; ++i)
@@ -531,6 +573,8 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   q.args.sk_units = (long long)sk_tiles * Gk;
   q.args.sk_per_wg = (q.args.sk_units + grid - 1) / grid;
   if (q.args.sk_per_wg < 1) q.args.sk_per_wg = 1;
+  // the kernel keeps its stripe bookkeeping in 32 bits
+  if (q.args.sk_units + q.args.sk_per_wg + Gk >= (1LL << 31)) return -2;
   q.counters = (int)sk_tiles;
   q.part_floats = sk_tiles ? (size_t)2 * grid * BM * BN : 0;
   q.wgs = grid;
