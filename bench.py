@@ -110,6 +110,61 @@ def pmc_summary(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
+def large_m_sweep(w4, torch, group):
+    """TFLOP/s of w4a16_gemm (automatic plan) on the 70B-class shapes at M >= 256, next to
+    torch's fp16 matmul on the dequantized weights (context).  Inputs are seeded and
+    synthetic with the workload's distributions (codes uniform 0..15, scales U[0.001,
+    0.01], X ~ N(0,1)), generated on the device; each shape is timed over back-to-back
+    launches after a warmup."""
+    shapes = [(8192, 28672), (28672, 8192), (8192, 10240)]
+    Ms = [256, 1024, 4096]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2024)
+    out = []
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    for (K, N) in shapes:
+        q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
+                          generator=gen)
+        s = (torch.rand((K // group, N), device="cuda", generator=gen) * 0.009 + 0.001).half()
+        wp, sp, _ = w4.alloc_packed(K, N, group, False)
+        w4.w4a16_repack(q, s, None, wp, sp, None, K, N, group)
+        Wt = torch.empty((N, K), dtype=torch.float16, device="cuda")
+        w4.w4a16_dequant(q, s, None, Wt, K, N, group)
+        del q
+        for M in Ms:
+            X = torch.randn((M, K), device="cuda", generator=gen).half()
+            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            fl = 2.0 * M * N * K
+            reps = max(3, min(50, int(2e13 / fl)))
+            t = timed(lambda: w4.w4a16_gemm(X, wp, sp, None, Y, M, N, K, group), reps)
+            tt = timed(lambda: torch.nn.functional.linear(X, Wt), reps)
+            plan = w4.w4a16_gemm_describe(M, N, K, group)
+            out.append(dict(M=M, K=K, N=N, us=round(t * 1e6, 2), TFLOPs=round(fl / t / 1e12, 1),
+                            mfma_frac=round(fl / t / 1e12 / FP16_PEAK_TFLOPS, 4),
+                            plan=plan["name"], torch_fp16_TFLOPs=round(fl / tt / 1e12, 1)))
+            del X, Y
+        del wp, sp, s, Wt
+    torch.cuda.synchronize()
+    big = [r for r in out if r["M"] >= 1024]
+    return dict(peak_TFLOPs=FP16_PEAK_TFLOPS, unit="TFLOP/s",
+                min_mfma_frac_M_ge_1024=min(r["mfma_frac"] for r in big),
+                mean_mfma_frac_M_ge_1024=round(sum(r["mfma_frac"] for r in big) / len(big), 4),
+                runs=out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +176,8 @@ def main():
     ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant (tuning)")
     ap.add_argument("--splits", type=int, default=0, help="force split-K slices (tuning)")
     ap.add_argument("--detail", default=None, help="write per-launch detail JSON here")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the large-M (70B-class, MFMA-bound) sweep")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain device copies of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -312,6 +369,11 @@ def main():
                         w4_speedup_vs_torch_matmul=round(ttorch / t_step, 3))
         del Wt
 
+    # ---- large-M sweep: 70B-class single-GPU shapes, where the matrix cores bound ------
+    large = None
+    if not args.no_large:
+        large = large_m_sweep(w4, torch, group)
+
     # ---- CPU oracle on this host over one step (bounded sample) -----------------------
     cpu = None
     if not args.no_cpu:
@@ -375,6 +437,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "fp16_baseline": baseline,
+        "large_m_sweep": large,
         "per_launch_us": [[p["M"], p["K"], p["N"], p["us"]] for p in per_launch],
     }
     if args.detail:

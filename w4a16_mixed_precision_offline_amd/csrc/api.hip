@@ -124,9 +124,17 @@ int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, c
                                 M, N, K, group, st));
 }
 
-// Batches of at least this many rows go to the tiled kernel; smaller ones to the
-// skinny (memory-bound) kernel.
-constexpr int kTiledMinM = 128;
+// Which kernel an automatic plan uses, from sweeps on MI355X: the tiled kernel once
+// the batch gives each unpacked weight enough reuse and the weight matrix is large
+// enough to fill the chip with 64-row tiles; the skinny (memory-bound) kernel
+// otherwise.
+bool use_tiled(int M, int N, int K) {
+  const long long kn = (long long)K * N;
+  if (M >= 256) return true;
+  if (M >= 96 && kn >= (32LL << 20)) return true;
+  if (M >= 48 && kn >= (128LL << 20)) return true;
+  return false;
+}
 
 int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
               uint16_t* Y, int M, int N, int K, int variant, int grid, void* stream) {
@@ -150,7 +158,7 @@ int run_fused(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
   const int ns = skinny_variant_count();
   if (variant >= ns)
     return run_tiled(mode, X, w, sp, zp, Y, M, N, K, variant - ns, splits, stream);
-  if (variant < 0 && splits == 0 && M >= kTiledMinM && (mode == W_SYM || mode == W_ASYM))
+  if (variant < 0 && splits == 0 && use_tiled(M, N, K) && (mode == W_SYM || mode == W_ASYM))
     return run_tiled(mode, X, w, sp, zp, Y, M, N, K, -1, 0, stream);
   return run_skinny(mode, X, w, sp, zp, Y, M, N, K, group, variant, splits, stream);
 }
@@ -261,7 +269,7 @@ int w4a16_gemm_describe(int M, int N, int K, int group, int* out4) {
   int rc = check_weight_shape(K, N, group);
   if (rc) return rc;
   if (M <= 0) return W4A16_ERR_SHAPE;
-  if (M >= kTiledMinM) {
+  if (use_tiled(M, N, K)) {
     TiledPlan t;
     if ((rc = tiled_make_plan(M, N, K, W_SYM, -1, 0, &t))) return rc;
     out4[0] = skinny_variant_count() + t.variant;

@@ -279,7 +279,7 @@ __device__ __forceinline__ void tile_coords(int tt, int tiles_m, int tiles_n, in
   tn = __builtin_amdgcn_readfirstlane(r / gm);
 }
 
-template <int MT, int NTW, int MODE>
+template <int MT, int NTW, int NS, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,
     const uint16_t* __restrict__ Sp, const uint32_t* __restrict__ Zp, uint16_t* __restrict__ Y,
@@ -287,7 +287,8 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
   constexpr int BM = 16 * MT;
   constexpr int BN = WAVES * 16 * NTW;
   constexpr int XBUF = BM * 256;   // one k-block of the activation tile
-  constexpr int NSTAGE = 3;        // LDS buffers / weight register stages
+  constexpr int NSTAGE = NS;       // LDS pipeline stages
+  constexpr int AHEAD = NS - 1;    // k-blocks in flight ahead of the one computed
   constexpr int PIECE = BM * BN;   // floats of one partial tile
   constexpr int STAGE = XBUF + WAVES * WLds<NTW>::BYTES;  // LDS bytes of one stage
   constexpr int NV = MT + NTW + (MODE == W_ASYM ? 2 : 1);  // loads per stage per thread
@@ -368,25 +369,27 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // prologue: k-blocks kb0 and kb0+1 in flight
-    dma_x<MT>(lds0, rx, xoff, wave, kb0);
-    dma_w<NTW, MODE>(wl0, R, kb0);
-    dma_x<MT>(lds0 + STAGE, nk > 1 ? rx : rx0, xoff, wave, kb0 + 1);
-    dma_w<NTW, MODE>(wl0 + STAGE, nk > 1 ? R : R0, kb0 + 1);
+    // prologue: k-blocks kb0 .. kb0 + AHEAD - 1 in flight
+#pragma unroll
+    for (int p = 0; p < AHEAD; ++p) {
+      const bool live = p < nk;
+      dma_x<MT>(lds0 + p * STAGE, live ? rx : rx0, xoff, wave, kb0 + p);
+      dma_w<NTW, MODE>(wl0 + p * STAGE, live ? R : R0, kb0 + p);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
-    // step d of the ring handles k-block kbi, held in stage d; k-block kbi + 2 is
-    // issued into stage (d+2)%3.  At the wait, the loads of kbi and kbi + 1 are in
-    // flight (NV per stage, oldest first); after it, every wave's loads of kbi have
-    // landed once all waves pass the barrier, and every wave has finished reading
-    // the stage about to be refilled.
+    // step d of the ring handles k-block kbi, held in stage d; k-block kbi + AHEAD is
+    // issued into stage (d + AHEAD) % NS, one load per fragment group of the compute.
+    // At the wait, the loads of kbi .. kbi + AHEAD - 1 are in flight (NV per stage,
+    // oldest first); after it, every wave's loads of kbi have landed once all waves
+    // pass the barrier, and every wave has finished reading the stage to be refilled.
     auto step = [&](int d, int kbi, bool issue_live) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_waitcnt(vmcnt_enc(NV));
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc((AHEAD - 1) * NV));
       __builtin_amdgcn_s_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_sched_barrier(0);
-      const int dn = (d + 2) % NSTAGE;
+      const int dn = (d + AHEAD) % NSTAGE;
       DmaPlan<MT, NTW, MODE> plan;
       plan.rx = issue_live ? rx : rx0;
 #pragma unroll
@@ -395,20 +398,21 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       plan.xdst = lds0 + dn * STAGE;
       plan.wdst = wl0 + dn * STAGE;
       plan.wave = wave;
-      plan.kb = kbi + 2;
+      plan.kb = kbi + AHEAD;
       compute_kblock<MT, NTW, MODE>(lds + d * STAGE,
                                     lds + d * STAGE + XBUF + wave * WLds<NTW>::BYTES, acc, aoff,
                                     lane, magic, plan);
       __builtin_amdgcn_sched_barrier(0);
     };
     int i = 0;
-    for (; i + 2 < nk; i += 3) {
-      step(0, kb0 + i, i + 2 < nk);
-      step(1, kb0 + i + 1, i + 3 < nk);
-      step(2, kb0 + i + 2, i + 4 < nk);
+    for (; i + NS <= nk; i += NS) {
+#pragma unroll
+      for (int d = 0; d < NS; ++d) step(d, kb0 + i + d, i + d + AHEAD < nk);
     }
-    if (i < nk) step(0, kb0 + i, false);
-    if (i + 1 < nk) step(1, kb0 + i + 1, false);
+    // tail: fewer than NS k-blocks left, nothing more to load
+#pragma unroll
+    for (int d = 0; d < NS - 1; ++d)
+      if (i + d < nk) step(d, kb0 + i + d, false);
     // drain: no load of this segment is left in flight
     __builtin_amdgcn_s_waitcnt(0);
   };
@@ -518,17 +522,20 @@ typedef void (*TiledFn)(const uint16_t*, const uint32_t*, const uint16_t*, const
                         uint16_t*, float*, int*, TiledArgs);
 
 struct TVariant {
-  int MT, NTW;
+  int MT, NTW, NS;
   TiledFn sym, asym;
   const char* name;
 };
 
-#define W4A16_TILED(MT, NTW, NAME) \
-  TVariant { MT, NTW, tiled_kernel<MT, NTW, W_SYM>, tiled_kernel<MT, NTW, W_ASYM>, NAME }
+#define W4A16_TILED(MT, NTW, NS, NAME)                                                       \
+  TVariant {                                                                               \
+    MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>, NAME \
+  }
 
 const TVariant kTiled[] = {
-    W4A16_TILED(8, 4, "tiled_bm128_bn256"),
-    W4A16_TILED(4, 4, "tiled_bm64_bn256"),
+    W4A16_TILED(8, 4, 3, "tiled_bm128_bn256_s3"),
+    W4A16_TILED(4, 4, 4, "tiled_bm64_bn256_s4"),
+    W4A16_TILED(4, 4, 3, "tiled_bm64_bn256_s3"),
 };
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
 
@@ -539,7 +546,9 @@ const char* tiled_variant_name(int v) { return (v >= 0 && v < kNumTiled) ? kTile
 
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p) {
   if (mode != W_SYM && mode != W_ASYM) return -8;
-  if (variant < 0) variant = M > 64 ? 0 : 1;
+  // measured on MI355X: the 128-row tile wins from M = 256 on (more reuse of each
+  // unpacked weight); at M <= 128 the 64-row tile with a 4-deep ring does
+  if (variant < 0) variant = M > 128 ? 0 : 1;
   if (variant >= kNumTiled) return -8;
   const TVariant& v = kTiled[variant];
   const int BM = 16 * v.MT, BN = WAVES * 16 * v.NTW;
