@@ -52,7 +52,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // cache-policy bits of buffer instructions on gfx950
-constexpr int kSC1 = 16;  // coherent across the XCDs' L2s (relaxed agent-scope access)
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -279,6 +278,42 @@ __device__ __forceinline__ void tile_coords(int tt, int tiles_m, int tiles_n, in
   tn = __builtin_amdgcn_readfirstlane(r / gm);
 }
 
+// Y store of a finished tile tt: lane holds row 16i + lane%16 and the four columns
+// 16t + 4(lane/16) .. +3 of each of the wave's NTW column tiles.
+template <int MT, int NTW>
+__device__ __forceinline__ void store_tile(uint16_t* __restrict__ Y, const TiledArgs& a, int tt,
+                                           int wave, int lane, const float4v (&acc)[MT][NTW]) {
+  constexpr int BM = 16 * MT;
+  constexpr int BN = WAVES * 16 * NTW;
+  int tm, tn;
+  tile_coords(tt, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
+  const int m0 = tm * BM;
+  const int rows = a.M - m0 < BM ? a.M - m0 : BM;
+  const rsrc_t ry = make_rsrc(Y + (size_t)m0 * a.N, (uint32_t)((size_t)rows * a.N * 2));
+  const int t_first = tn * (BN / 16) + wave * NTW;
+  const int ntiles16 = a.N / 16;
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    if (t_first + t >= ntiles16) break;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int r = 16 * i + (lane & 15);
+      const uint32_t off = r < rows ? (uint32_t)(((size_t)r * a.N + (t_first + t) * 16 +
+                                                  4 * (lane >> 4)) * 2)
+                                    : kOutOfRange;
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v = {pack_h2(acc[i][t][0], acc[i][t][1]), pack_h2(acc[i][t][2], acc[i][t][3])};
+      __builtin_amdgcn_raw_buffer_store_b64(v, ry, off, 0u, 0);
+    }
+  }
+}
+
+// Byte offset of one lane's float4 of (row tile i, column tile t) inside a partial piece.
+template <int MT, int NTW>
+__device__ __forceinline__ uint32_t piece_off(int wave, int i, int t, int lane) {
+  return (uint32_t)((((wave * MT + i) * NTW + t) * 64 + lane) * 16);
+}
+
 template <int MT, int NTW, int NS, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,
@@ -293,7 +328,6 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
   constexpr int STAGE = XBUF + WAVES * WLds<NTW>::BYTES;  // LDS bytes of one stage
   constexpr int NV = MT + NTW + (MODE == W_ASYM ? 2 : 1);  // loads per stage per thread
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];
-  __shared__ int s_old;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -384,6 +418,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     // oldest first); after it, every wave's loads of kbi have landed once all waves
     // pass the barrier, and every wave has finished reading the stage to be refilled.
     auto step = [&](int d, int kbi, bool issue_live) {
+      d = __builtin_amdgcn_readfirstlane(d);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(vmcnt_enc((AHEAD - 1) * NV));
       __builtin_amdgcn_s_barrier();
@@ -404,43 +439,23 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
                                     lane, magic, plan);
       __builtin_amdgcn_sched_barrier(0);
     };
-    int i = 0;
-    for (; i + NS <= nk; i += NS) {
-#pragma unroll
-      for (int d = 0; d < NS; ++d) step(d, kb0 + i + d, i + d + AHEAD < nk);
+    // one k-block per trip with a rotating stage index: stages are LDS addresses, so
+    // nothing needs unrolling, and the accumulators keep their registers across the
+    // back-edge (an unrolled body made the allocator shuffle them every trip)
+    int d = 0;
+#pragma nounroll
+    for (int i = 0; i < nk; ++i) {
+      step(d, kb0 + i, i + AHEAD < nk);
+      d = d + 1 == NS ? 0 : d + 1;
     }
-    // tail: fewer than NS k-blocks left, nothing more to load
-#pragma unroll
-    for (int d = 0; d < NS - 1; ++d)
-      if (i + d < nk) step(d, kb0 + i + d, false);
     // drain: no load of this segment is left in flight
     __builtin_amdgcn_s_waitcnt(0);
   };
 
-  // Y store of a finished tile: lane holds row 16i + lane%16 and the four columns
-  // 16t + 4(lane/16) .. +3 of each of the wave's column tiles
   auto store_y = [&](int tt, const float4v (&acc)[MT][NTW]) {
-    int tm, tn;
-    tile_coords(tt, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
-    const int m0 = tm * BM;
-    const int rows = a.M - m0 < BM ? a.M - m0 : BM;
-    const rsrc_t ry = make_rsrc(Y + (size_t)m0 * a.N, (uint32_t)((size_t)rows * a.N * 2));
-    const int t_first = tn * (BN / 16) + wave * NTW;
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      if (t_first + t >= ntiles16) break;  // wave-uniform
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const int r = 16 * i + (lane & 15);
-        const uint32_t off = r < rows ? (uint32_t)(((size_t)r * a.N + (t_first + t) * 16 +
-                                                    4 * (lane >> 4)) * 2)
-                                      : kOutOfRange;
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 v = {pack_h2(acc[i][t][0], acc[i][t][1]), pack_h2(acc[i][t][2], acc[i][t][3])};
-        __builtin_amdgcn_raw_buffer_store_b64(v, ry, off, 0u, 0);
-      }
-    }
+    store_tile<MT, NTW>(Y, a, tt, wave, lane, acc);
   };
+
 
   float4v acc[MT][NTW];
 
@@ -471,65 +486,69 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       store_y(tt, acc);
       continue;
     }
-    // partial tile: write this piece, count it, and finish the tile if last.
-    // (Slot indices are made explicitly uniform: a descriptor the compiler cannot
-    // prove uniform is wrapped in a per-lane loop around every access.)
+    // a tile cut by a stripe boundary: store this piece (two slots per workgroup: its
+    // first and its last segment); the second pass sums the pieces and writes Y
     const int slot = __builtin_amdgcn_readfirstlane(2 * w + (first_seg ? 0 : 1));
-    {
-      const rsrc_t rp = make_rsrc(part + (size_t)slot * PIECE, PIECE * 4);
+    const rsrc_t rp = make_rsrc(part + (size_t)slot * PIECE, PIECE * 4);
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int t = 0; t < NTW; ++t)
-          __builtin_amdgcn_raw_buffer_store_b128(
-              __builtin_bit_cast(u32x4, acc[i][t]), rp,
-              (uint32_t)((((wave * MT + i) * NTW + t) * 64 + lane) * 16), 0u, kSC1);
-    }
-    const int w_first = __builtin_amdgcn_readfirstlane((int)(((uint32_t)tl * Gk) / U));
-    const int w_last = __builtin_amdgcn_readfirstlane((int)(((uint32_t)(tl + 1) * Gk - 1) / U));
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's sc1 stores have completed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __syncthreads();  // ... and so have every other thread's
-    if (tid == 0)
-      s_old = __hip_atomic_fetch_add(counters + tl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int old = __builtin_amdgcn_readfirstlane(s_old);
-    if (old != w_last - w_first) continue;
-    // last arriver: sum the pieces in stripe order w_first .. w_last
-    for (int wp = w_first; wp <= w_last; ++wp) {
-      const int first_tile_of_wp = (int)(((uint32_t)wp * U) / (uint32_t)Gk);
-      const int sl = __builtin_amdgcn_readfirstlane(2 * wp + (tl == first_tile_of_wp ? 0 : 1));
-      const rsrc_t rp = make_rsrc(part + (size_t)sl * PIECE, PIECE * 4);
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-          const float4v v = __builtin_bit_cast(
-              float4v, __builtin_amdgcn_raw_buffer_load_b128(
-                           rp, (uint32_t)((((wave * MT + i) * NTW + t) * 64 + lane) * 16), 0u,
-                           kSC1));
-          acc[i][t] = wp == w_first ? v : acc[i][t] + v;
-        }
-    }
-    if (tid == 0)
-      __hip_atomic_store(counters + tl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    store_y(tt, acc);
+      for (int t = 0; t < NTW; ++t)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][t]), rp,
+                                               piece_off<MT, NTW>(wave, i, t, lane), 0u, 0);
   }
+}
+
+// Second pass of the stream-K split: one workgroup per tile of the stream-K part;
+// a tile cut into pieces by stripe boundaries gets the pieces summed in stripe order
+// (a fixed order, so results are bitwise reproducible) and written to Y.  Tiles done
+// by a single workgroup were stored by it directly.
+template <int MT, int NTW>
+__global__ __launch_bounds__(64 * WAVES) void tiled_fixup_kernel(const float* __restrict__ part,
+                                                                 uint16_t* __restrict__ Y,
+                                                                 TiledArgs a) {
+  constexpr int PIECE = 16 * MT * WAVES * 16 * NTW;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tl = blockIdx.x;
+  const uint32_t Gk = (uint32_t)(a.K / KBLK);
+  const uint32_t U = (uint32_t)a.sk_per_wg;
+  const int w_first = __builtin_amdgcn_readfirstlane((int)(((uint32_t)tl * Gk) / U));
+  const int w_last = __builtin_amdgcn_readfirstlane((int)(((uint32_t)(tl + 1) * Gk - 1) / U));
+  if (w_first == w_last) return;
+  float4v sum[MT][NTW];
+  for (int wp = w_first; wp <= w_last; ++wp) {
+    const int first_tile_of_wp = (int)(((uint32_t)wp * U) / Gk);
+    const int sl = __builtin_amdgcn_readfirstlane(2 * wp + (tl == first_tile_of_wp ? 0 : 1));
+    const rsrc_t rp = make_rsrc(part + (size_t)sl * PIECE, PIECE * 4);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const float4v v = __builtin_bit_cast(
+            float4v, __builtin_amdgcn_raw_buffer_load_b128(rp, piece_off<MT, NTW>(wave, i, t, lane),
+                                                           0u, 0));
+        sum[i][t] = wp == w_first ? v : sum[i][t] + v;
+      }
+  }
+  store_tile<MT, NTW>(Y, a, a.dp_rounds * a.grid + tl, wave, lane, sum);
 }
 
 typedef void (*TiledFn)(const uint16_t*, const uint32_t*, const uint16_t*, const uint32_t*,
                         uint16_t*, float*, int*, TiledArgs);
+typedef void (*FixupFn)(const float*, uint16_t*, TiledArgs);
 
 struct TVariant {
   int MT, NTW, NS;
   TiledFn sym, asym;
+  FixupFn fixup;
   const char* name;
 };
 
 #define W4A16_TILED(MT, NTW, NS, NAME)                                                       \
   TVariant {                                                                               \
-    MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>, NAME \
+    MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>,       \
+        tiled_fixup_kernel<MT, NTW>, NAME                                                   \
   }
 
 const TVariant kTiled[] = {
@@ -584,7 +603,8 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   if (q.args.sk_per_wg < 1) q.args.sk_per_wg = 1;
   // the kernel keeps its stripe bookkeeping in 32 bits
   if (q.args.sk_units + q.args.sk_per_wg + Gk >= (1LL << 31)) return -2;
-  q.counters = (int)sk_tiles;
+  q.counters = 0;
+  q.fixup_wgs = (int)sk_tiles;
   q.part_floats = sk_tiles ? (size_t)2 * grid * BM * BN : 0;
   q.wgs = grid;
   q.threads = 64 * WAVES;
@@ -599,6 +619,11 @@ hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, co
   TiledFn fn = p.mode == W_ASYM ? v.asym : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint32_t*>(w), sp, zp, Y, part, counters, p.args);
+  if (p.fixup_wgs > 0) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(v.fixup, dim3(p.fixup_wgs), dim3(p.threads), 0, st, part, Y, p.args);
+  }
   return hipGetLastError();
 }
 

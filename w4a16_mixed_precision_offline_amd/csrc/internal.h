@@ -95,7 +95,8 @@ struct TiledPlan {
   TiledArgs args;
   int wgs, threads;
   size_t part_floats;  // workspace floats for partial tiles (two slots per workgroup)
-  int counters;        // arrival counters (one per stream-K tile)
+  int counters;        // arrival counters (none: the second pass needs no hand-off)
+  int fixup_wgs;       // workgroups of the second pass (stream-K tiles), 0 if none
 };
 int tiled_variant_count();
 const char* tiled_variant_name(int v);
