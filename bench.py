@@ -123,9 +123,13 @@ def large_m_sweep(w4, torch, group):
     out = []
 
     def timed(fn, reps):
-        for _ in range(2):
+        # warm up for ~50 ms: the clock ramps under sustained matrix load
+        t0 = time.perf_counter()
+        while True:
             fn()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 > 0.05:
+                break
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()

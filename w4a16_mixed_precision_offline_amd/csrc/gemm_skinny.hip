@@ -483,7 +483,9 @@ const Variant kVariants[] = {
     W4A16_VARIANT(16, 1, 8, 2),  W4A16_VARIANT(16, 2, 8, 2),  W4A16_VARIANT(16, 1, 16, 2),
     W4A16_VARIANT(32, 1, 4, 2),  W4A16_VARIANT(32, 2, 4, 2),  W4A16_VARIANT(32, 1, 8, 2),
     W4A16_VARIANT(32, 2, 8, 2),  W4A16_VARIANT(64, 1, 4, 2),  W4A16_VARIANT(64, 2, 4, 2),
-    W4A16_VARIANT(64, 1, 8, 2),
+    W4A16_VARIANT(64, 1, 8, 2),  W4A16_VARIANT(8, 4, 4, 2),   W4A16_VARIANT(16, 4, 4, 2),
+    W4A16_VARIANT(32, 4, 4, 2),  W4A16_VARIANT(16, 4, 2, 2),  W4A16_VARIANT(32, 4, 2, 2),
+    W4A16_VARIANT(16, 8, 2, 2),  W4A16_VARIANT(8, 8, 2, 2),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -511,17 +513,20 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
     // and halve the activation reads per weight byte; `longk`: many 128-row blocks
     // per tile, so more waves share a tile's K range.
     const int XR = M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : M <= 32 ? 32 : 64;
-    const bool wide = N % 32 == 0 && N / 16 > 256;
+    const bool wide = N % 64 == 0 && N / 16 > 256;
     const bool longk = K / KBLK > 48;
-    if (XR <= 8) {
-      if (wide) variant = find_variant(XR, 1, 4, 4);
-      else if (XR == 4) variant = longk ? find_variant(4, 1, 16, 2) : find_variant(4, 1, 8, 4);
-      else variant = longk ? find_variant(8, 1, 8, 4) : find_variant(8, 1, 4, 4);
+    // From 8 rows on, wide layers give each wave four column tiles: the activation
+    // rows a wave loads are then reused over 64 columns instead of 16-32.
+    if (XR == 4) {
+      variant = wide ? find_variant(4, 1, 4, 4)
+                     : (longk ? find_variant(4, 1, 16, 2) : find_variant(4, 1, 8, 4));
+    } else if (XR == 8) {
+      variant = wide ? find_variant(8, 4, 4, 2) : find_variant(8, 1, 8, 4);
     } else if (XR == 16) {
-      variant = wide ? find_variant(16, 2, 4, 4)
+      variant = wide ? find_variant(16, 4, 4, 2)
                      : (longk ? find_variant(16, 1, 8, 2) : find_variant(16, 1, 4, 4));
     } else if (XR == 32) {
-      variant = wide ? find_variant(32, 2, 4, 2) : find_variant(32, 1, 4, 2);
+      variant = wide ? find_variant(32, 4, 4, 2) : find_variant(32, 1, 4, 2);
     } else {
       variant = find_variant(64, 1, 4, 2);
     }

@@ -195,16 +195,15 @@ struct DmaPlan {
 // One k-block: the wave's weight codes, scales (and zero-points) come from its
 // LDS slot, the activation fragments from the shared tile; 4 k-steps of 32.
 // Software pipeline, one group per (k-step j, row tile i): the group issues the
-// LDS read of the fragment two groups ahead, unpacks one column tile of step
-// j+1, and runs the NTW MFMAs of (j, i).  Scheduling barriers between the groups
+// LDS read of the fragment three groups ahead, unpacks its share of the column tiles
+// of step j+1 (tiles t = i, i + MT, ...), and runs the NTW MFMAs of (j, i).  Scheduling barriers between the groups
 // keep that order, so LDS latency hides behind the matrix work.
 template <int MT, int NTW, int MODE>
 __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
                                                float4v (&acc)[MT][NTW], const uint32_t (&aoff)[4],
                                                int lane, uint32_t magic,
                                                const DmaPlan<MT, NTW, MODE>& dma) {
-  static_assert(MT >= NTW, "one column tile is unpacked per row-tile group");
-  static_assert(DmaPlan<MT, NTW, MODE>::NV <= 4 * MT, "one load per group");
+  constexpr int NVL = DmaPlan<MT, NTW, MODE>::NV;
   constexpr int G = 4 * MT;  // groups per k-block
   u32x4 wv[NTW];
   half2v c0[NTW], c1[NTW], s2[NTW];
@@ -226,9 +225,12 @@ __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
     c0[t] = half2v{a0, a0};
     c1[t] = half2v{a1, a1};
   }
-  half8 ar[3];
-  ar[0] = *reinterpret_cast<const half8*>(xb + aoff[0]);
-  ar[1] = *reinterpret_cast<const half8*>(xb + aoff[0] + 4096);
+  // fragment ring: group g's activation fragment is read PF groups ahead
+  constexpr int PF = 3;
+  half8 ar[PF + 1];
+#pragma unroll
+  for (int g = 0; g < PF; ++g)
+    if (g < G) ar[g] = *reinterpret_cast<const half8*>(xb + aoff[g / MT] + (g % MT) * 4096);
   half8 b[2][NTW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) b[0][t] = dequant_scaled(wv[t][0], c0[t], c1[t], s2[t], magic);
@@ -238,17 +240,23 @@ __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int g = j * MT + i;
-      if (g < DmaPlan<MT, NTW, MODE>::NV) dma.issue(g);  // one load of a later k-block
-      if (g + 2 < G) {
-        const int gj = (g + 2) / MT, gi = (g + 2) % MT;
-        ar[(g + 2) % 3] = *reinterpret_cast<const half8*>(xb + aoff[gj] + gi * 4096);
+      // loads of a later k-block: q = g, g + G, ... (one per group when NV <= G)
+#pragma unroll
+      for (int q = g; q < NVL; q += G) dma.issue(q);
+      if (g + PF < G) {
+        const int gj = (g + PF) / MT, gi = (g + PF) % MT;
+        ar[(g + PF) % (PF + 1)] = *reinterpret_cast<const half8*>(xb + aoff[gj] + gi * 4096);
       }
-      if (j < 3 && i < NTW)
-        b[(j + 1) & 1][i] = dequant_scaled(wv[i][j + 1], c0[i], c1[i], s2[i], magic);
+      // unpack the column tiles t = i, i + MT, ... of step j + 1
+      if (j < 3) {
+#pragma unroll
+        for (int t = i; t < NTW; t += MT)
+          b[(j + 1) & 1][t] = dequant_scaled(wv[t][j + 1], c0[t], c1[t], s2[t], magic);
+      }
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
-        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j & 1][t], ar[g % 3], acc[i][t], 0,
-                                                          0, 0);
+        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j & 1][t], ar[g % (PF + 1)],
+                                                          acc[i][t], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -555,6 +563,8 @@ const TVariant kTiled[] = {
     W4A16_TILED(8, 4, 3, "tiled_bm128_bn256_s3"),
     W4A16_TILED(4, 4, 4, "tiled_bm64_bn256_s4"),
     W4A16_TILED(4, 4, 3, "tiled_bm64_bn256_s3"),
+    W4A16_TILED(2, 4, 4, "tiled_bm32_bn256_s4"),
+    W4A16_TILED(1, 4, 4, "tiled_bm16_bn256_s4"),
 };
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
 
