@@ -169,6 +169,102 @@ def large_m_sweep(w4, torch, group):
                 runs=out)
 
 
+def time_rotated(torch, calls, min_reps=20, target_s=0.02):
+    """Seconds per call, cycling through `calls` (one per weight copy) back to back
+    after a 20 ms warmup."""
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < 0.02:
+        calls[i % len(calls)]()
+        i += 1
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = max(min_reps, len(calls))
+    e0.record()
+    for r in range(reps):
+        calls[r % len(calls)]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
+
+
+def config_legs(w4, torch, group):
+    """Config 4 (2:4 sparse): w4a16_sparse24_gemm against w4a16_gemm on the same pruned
+    weights (the dense kernel reads them repacked, code 8 at pruned positions).
+    Config 3 (zero-points, awkward shapes): w4a16_gemm with per-group zero-points.
+    Seeded inputs from gen/ at the workloads' shapes; weights rotate over copies
+    totalling at least 512 MiB so that no launch finds its weights in the 256 MiB
+    Infinity Cache."""
+    from gen import activations, config_runs, weights
+    rot = 512 << 20
+    sp_runs = []
+    cache = {}
+    for w in config_runs(4):
+        K, N, M = w.K, w.N, w.M
+        if (K, N) not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            d = weights(w)
+            q = torch.from_numpy(d["Qp"]).cuda()
+            s = torch.from_numpy(d["s"]).cuda()
+            dense = w4.alloc_packed(K, N, group, False)
+            w4.w4a16_repack(q, s, None, dense[0], dense[1], None, K, N, group)
+            sparse = w4.alloc_sparse24(K, N, group)
+            w4.w4a16_sparse24_repack(q, s, *sparse, K, N, group)
+            del q, s
+            nd = max(2, -(-rot // (K * N // 2)))
+            ns = max(2, -(-rot // (K * N // 4 + K * N // 8)))
+            cache[(K, N)] = ([dense] + [tuple(t.clone() if t is not None else None for t in dense)
+                                        for _ in range(nd - 1)],
+                             [sparse] + [tuple(t.clone() for t in sparse) for _ in range(ns - 1)])
+        dcopies, scopies = cache[(K, N)]
+        X = torch.from_numpy(activations(w)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        td = time_rotated(torch, [lambda c=c: w4.w4a16_gemm(X, c[0], c[1], None, Y, M, N, K, group)
+                                  for c in dcopies])
+        ts = time_rotated(torch, [lambda c=c: w4.w4a16_sparse24_gemm(X, c[0], c[1], c[2], Y, M, N, K,
+                                                                     group) for c in scopies])
+        sbytes = K * N // 4 + K * N // 8 + 2 * (K // group) * N
+        sp_runs.append(dict(M=M, K=K, N=N, dense_us=round(td * 1e6, 2), sparse_us=round(ts * 1e6, 2),
+                            speedup=round(td / ts, 3),
+                            sparse_weight_GBps=round(sbytes / ts / 1e9, 1),
+                            dense_plan=w4.w4a16_gemm_describe(M, N, K, group)["name"]))
+    del cache
+    torch.cuda.empty_cache()
+    sp = dict(kernel="w4a16_sparse24_gemm (v_smfmac_f32_16x16x64_f16) vs w4a16_gemm",
+              mean_speedup=round(sum(r["speedup"] for r in sp_runs) / len(sp_runs), 3),
+              runs=sp_runs)
+
+    as_runs = []
+    cache = {}
+    for w in config_runs(3):
+        K, N, M = w.K, w.N, w.M
+        if (K, N) not in cache:
+            cache.clear()
+            d = weights(w)
+            q = torch.from_numpy(d["Qp"]).cuda()
+            s = torch.from_numpy(d["s"]).cuda()
+            z = torch.from_numpy(d["Zp"]).cuda()
+            pk = w4.alloc_packed(K, N, group, True)
+            w4.w4a16_repack(q, s, z, *pk, K, N, group)
+            n = max(2, -(-rot // (K * N // 2)))
+            cache[(K, N)] = [pk] + [tuple(t.clone() for t in pk) for _ in range(n - 1)]
+        copies = cache[(K, N)]
+        X = torch.from_numpy(activations(w)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        t = time_rotated(torch, [lambda c=c: w4.w4a16_gemm(X, c[0], c[1], c[2], Y, M, N, K, group)
+                                 for c in copies])
+        wb = K * N // 2 + 2 * (K // group) * N + (K // group) * N // 2
+        as_runs.append(dict(M=M, K=K, N=N, us=round(t * 1e6, 2),
+                            TFLOPs=round(2.0 * M * N * K / t / 1e12, 2),
+                            weight_GBps=round(wb / t / 1e9, 1),
+                            plan=w4.w4a16_gemm_describe(M, N, K, group)["name"]))
+    del cache
+    torch.cuda.empty_cache()
+    return sp, dict(kernel="w4a16_gemm with 4-bit zero-points", runs=as_runs)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +278,8 @@ def main():
     ap.add_argument("--detail", default=None, help="write per-launch detail JSON here")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the large-M (70B-class, MFMA-bound) sweep")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the 2:4-sparse and zero-point workload legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain device copies of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -378,6 +476,11 @@ def main():
     if not args.no_large:
         large = large_m_sweep(w4, torch, group)
 
+    # ---- 2:4 sparse vs dense on the same pruned weights; zero-point workload ---------
+    sparse24 = asym = None
+    if not args.no_configs:
+        sparse24, asym = config_legs(w4, torch, group)
+
     # ---- CPU oracle on this host over one step (bounded sample) -----------------------
     cpu = None
     if not args.no_cpu:
@@ -442,6 +545,8 @@ def main():
         "cpu_baseline": cpu,
         "fp16_baseline": baseline,
         "large_m_sweep": large,
+        "sparse24_vs_dense": sparse24,
+        "asym_zero_point": asym,
         "per_launch_us": [[p["M"], p["K"], p["N"], p["us"]] for p in per_launch],
     }
     if args.detail:

@@ -546,10 +546,12 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
   int maxs = Gk / v.WK;
   if (maxs < 1) maxs = 1;
   if (splits <= 0) {
-    // split K only when the column tiles cannot give every compute unit a workgroup
+    // split K only when the column tiles leave more than a third of the compute units
+    // without a workgroup; the reduction costs more than a partly idle chip above that
+    // (measured: 192 four-tile workgroups beat 384 split ones by 2x on 4096x12288)
     const long base = (long)p->mblocks * p->nblocks;
     const long target = 256;
-    long sp = (target + base - 1) / base;
+    long sp = base >= 160 ? 1 : (target + base - 1) / base;
     splits = (int)(sp < 1 ? 1 : sp);
   }
   if (splits > maxs) splits = maxs;
