@@ -119,8 +119,7 @@ int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void
  *             workgroups.
  * Automatic plans use the tiled kernel for larger batches (M >= 256, or M >= 96
  * with K*N >= 32 Mi, or M >= 48 with K*N >= 128 Mi) and the skinny kernel otherwise.
- * The tiled variants take the symmetric and zero-point formats only
- * (W4A16_ERR_ARG for 2:4). */
+ * The same variants and rules apply to the 2:4 format (w4a16_sparse24_gemm_plan). */
 int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                     uint16_t* Y, int M, int N, int K, int group,
                     int variant, int splits, void* stream);

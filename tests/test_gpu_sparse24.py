@@ -109,11 +109,8 @@ def test_parity_every_variant_and_split(gh, M, K, N):
     ran = 0
     for v in range(w4.w4a16_gemm_variants()):
         name = w4.w4a16_gemm_variant_name(v)
-        if name.startswith("tiled"):   # dense formats only
-            with pytest.raises(w4.W4A16Error):
-                _sgemm(gh, Xd, comp, M, N, K, variant=v, splits=1, Y=gh.nan_filled(M, N))
-            continue
-        nt = int(name.split("_nt")[1].split("_")[0])
+        # tiled variants take any N % 16; their `splits` is the number of workgroups
+        nt = 1 if name.startswith("tiled") else int(name.split("_nt")[1].split("_")[0])
         for splits in (1, 2, 3):
             Y = gh.nan_filled(M, N)
             if N % (16 * nt):
@@ -148,3 +145,48 @@ def test_config4_sparse_and_dense_on_same_weights(gh):
         for Y in (Ys, Yd):
             ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, Bd)
             assert ok, (w.name, info)
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 2048, 1040), (130, 1024, 512), (1, 1024, 512)])
+def test_tiled_sparse_grids(gh, M, K, N):
+    """The tiled kernels in the 2:4 format, at several workgroup counts (stripes cut
+    tiles at odd k-blocks); each run repeats bit for bit."""
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, X = _case(M, K, N)
+    comp = _compress(gh, d, K, N)
+    Xd = gh.dev(X)
+    Yref = oracle.gemm(X, d["Qp"], d["s"], None, 128)
+    B = oracle.error_bound(X, d["Qp"], d["s"], None, 128)
+    tiled = [v for v in range(w4.w4a16_gemm_variants())
+             if w4.w4a16_gemm_variant_name(v).startswith("tiled")]
+    assert tiled
+    for v in tiled:
+        for grid in (0, 1, 3, 6, 16):
+            Y = gh.nan_filled(M, N)
+            _sgemm(gh, Xd, comp, M, N, K, variant=v, splits=grid, Y=Y)
+            first = gh.host(Y).view(np.uint16).copy()
+            ok, info = oracle.accept(first.view(np.float16), Yref, B)
+            assert ok, (w4.w4a16_gemm_variant_name(v), grid, info)
+            Y2 = gh.nan_filled(M, N)
+            _sgemm(gh, Xd, comp, M, N, K, variant=v, splits=grid, Y=Y2)
+            assert np.array_equal(gh.host(Y2).view(np.uint16), first), (v, grid)
+
+
+def test_tiled_sparse_onehot_exact(gh):
+    """One-hot activation rows through the tiled 2:4 kernel select fp16 weight rows
+    exactly: RNE((q - 8) * s) of row k_m."""
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 200, 1024, 528
+    _, d, _ = _case(M, K, N)
+    rng = np.random.default_rng(11)
+    ks = rng.integers(0, K, size=M)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    W16 = oracle.dequant_fp16(d["Qp"], d["s"], None, K, N, 128)
+    comp = _compress(gh, d, K, N)
+    for v in range(w4.w4a16_gemm_variants()):
+        if not w4.w4a16_gemm_variant_name(v).startswith("tiled"):
+            continue
+        for grid in (1, 7):
+            Y = gh.host(_sgemm(gh, gh.dev(X), comp, M, N, K, variant=v, splits=grid))
+            assert np.array_equal(Y.view(np.uint16), W16[ks].view(np.uint16)), (v, grid)

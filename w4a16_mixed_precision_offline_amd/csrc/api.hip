@@ -158,7 +158,7 @@ int run_fused(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
   const int ns = skinny_variant_count();
   if (variant >= ns)
     return run_tiled(mode, X, w, sp, zp, Y, M, N, K, variant - ns, splits, stream);
-  if (variant < 0 && splits == 0 && use_tiled(M, N, K) && (mode == W_SYM || mode == W_ASYM))
+  if (variant < 0 && splits == 0 && use_tiled(M, N, K) && mode != W_FP16)
     return run_tiled(mode, X, w, sp, zp, Y, M, N, K, -1, 0, stream);
   return run_skinny(mode, X, w, sp, zp, Y, M, N, K, group, variant, splits, stream);
 }
@@ -367,7 +367,7 @@ int w4a16_sparse24_gemm(const uint16_t* X, const void* vp, const void* idx, cons
   if (!idx) return W4A16_ERR_NULL;
   int rc = check_gemm_args(X, vp, sp, idx, Y, M, N, K, group);
   if (rc) return rc;
-  return run_skinny(W_SP24, X, vp, sp, idx, Y, M, N, K, group, -1, 0, stream);
+  return run_fused(W_SP24, X, vp, sp, idx, Y, M, N, K, group, -1, 0, stream);
 }
 
 int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
@@ -377,9 +377,7 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
   int rc = check_gemm_args(X, vp, sp, idx, Y, M, N, K, group);
   if (rc) return rc;
   if (variant < -1 || variant >= w4a16_gemm_variants() || splits < 0) return W4A16_ERR_ARG;
-  // only the skinny variants implement the 2:4 format
-  if (variant >= skinny_variant_count()) return W4A16_ERR_ARG;
-  return run_skinny(W_SP24, X, vp, sp, idx, Y, M, N, K, group, variant, splits, stream);
+  return run_fused(W_SP24, X, vp, sp, idx, Y, M, N, K, group, variant, splits, stream);
 }
 
 }  // extern "C"

@@ -48,6 +48,7 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half16 __attribute__((ext_vector_type(16)));
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOutOfRange = 0x80000000u;
@@ -131,21 +132,18 @@ struct WSrc {
 // LDS of one pipeline stage, per wave: NTW 1 KiB code blocks, then 256 bytes of
 // scales (tile t, column c at 32t + 2c; the DMA writes 4 bytes per lane, so the
 // slot spans all 64 lanes) and 256 bytes of zero-points (tile t at 8t).
-template <int NTW>
+template <int NTW, int MODE>
 struct WLds {
-  static constexpr int CODES = NTW * 1024;
+  // dense: NTW 1 KiB code blocks.  2:4: NTW 512-byte blocks of kept codes (lane l's
+  // two words at 8l), then NTW 256-byte blocks of positions (lane l's word at 4l).
+  static constexpr bool SP = MODE == W_SP24;
+  static constexpr int META = NTW * 512;
+  static constexpr int CODES = SP ? NTW * 768 : NTW * 1024;
   static constexpr int SCALES = CODES;
   static constexpr int ZEROS = CODES + 256;
   static constexpr int BYTES = CODES + 512;
 };
 
-template <int NTW, int MODE>
-__device__ __forceinline__ void dma_w(uint32_t wl, const WSrc<NTW>& R, int kb) {
-#pragma unroll
-  for (int t = 0; t < NTW; ++t) dma16(R.w, wl + t * 1024, R.wo[t], (uint32_t)kb * 1024u);
-  dma4(R.s, wl + WLds<NTW>::SCALES, R.so, (uint32_t)kb * 32u);
-  if (MODE == W_ASYM) dma4(R.z, wl + WLds<NTW>::ZEROS, R.zo, (uint32_t)kb * 8u);
-}
 
 // Activation tile in LDS: BM rows of 256 bytes (one 128-row k-block of X), no
 // padding; the 16-byte chunk c of row r sits at chunk position c ^ (r % 16), so
@@ -157,12 +155,6 @@ __device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 25
 // LDS (lane L -> bytes 16L..16L+15 after the destination base), i.e. 4 rows; lane L
 // of instruction c therefore fetches row 4(wave*MT + c) + L/16 and the global chunk
 // that belongs at chunk position L%16.  Rows past M read zeros (out of range).
-template <int MT>
-__device__ __forceinline__ void dma_x(uint32_t buf, u32x4 rx, const uint32_t (&xoff)[MT], int wave,
-                                      int kb) {
-#pragma unroll
-  for (int c = 0; c < MT; ++c) dma16(rx, buf + (wave * MT + c) * 1024, xoff[c], (uint32_t)kb * 256u);
-}
 
 // The direct-to-LDS loads of one k-block for one wave, as a list of NV single
 // instructions (MT activation quarters-of-rows blocks, NTW code blocks, the
@@ -172,22 +164,30 @@ __device__ __forceinline__ void dma_x(uint32_t buf, u32x4 rx, const uint32_t (&x
 // the waves before their MFMAs start).
 template <int MT, int NTW, int MODE>
 struct DmaPlan {
-  static constexpr int NV = MT + NTW + (MODE == W_ASYM ? 2 : 1);
+  // 2:4: two tiles' kept codes per 16-byte load, all four tiles' positions in one
+  static constexpr int NW = MODE == W_SP24 ? NTW / 2 + NTW / 4 : NTW;
+  static constexpr int NV = MT + NW + (MODE == W_ASYM ? 2 : 1);
   u32x4 rx;
   uint32_t xoff[MT];
   WSrc<NTW> R;
   uint32_t xdst, wdst;  // LDS addresses: activation stage, this wave's weight slot
   int wave, kb;
   __device__ __forceinline__ void issue(int q) const {
+    typedef WLds<NTW, MODE> L;
     if (q < MT) {
       dma16(rx, xdst + (wave * MT + q) * 1024, xoff[q], (uint32_t)kb * 256u);
-    } else if (q < MT + NTW) {
+    } else if (MODE == W_SP24 && q < MT + NTW / 2) {
+      const int c = q - MT;  // kept codes of tiles 2c, 2c+1
+      dma16(R.w, wdst + c * 1024, R.wo[c], (uint32_t)kb * 512u);
+    } else if (MODE == W_SP24 && q < MT + NW) {
+      dma16(R.z, wdst + L::META + (q - MT - NTW / 2) * 1024, R.zo, (uint32_t)kb * 256u);
+    } else if (MODE != W_SP24 && q < MT + NTW) {
       const int t = q - MT;
       dma16(R.w, wdst + t * 1024, R.wo[t], (uint32_t)kb * 1024u);
-    } else if (q == MT + NTW) {
-      dma4(R.s, wdst + WLds<NTW>::SCALES, R.so, (uint32_t)kb * 32u);
-    } else if (MODE == W_ASYM && q == MT + NTW + 1) {
-      dma4(R.z, wdst + WLds<NTW>::ZEROS, R.zo, (uint32_t)kb * 8u);
+    } else if (q == MT + NW) {
+      dma4(R.s, wdst + L::SCALES, R.so, (uint32_t)kb * 32u);
+    } else if (MODE == W_ASYM && q == MT + NW + 1) {
+      dma4(R.z, wdst + L::ZEROS, R.zo, (uint32_t)kb * 8u);
     }
   }
 };
@@ -211,13 +211,13 @@ __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
   for (int t = 0; t < NTW; ++t) {
     wv[t] = *reinterpret_cast<const u32x4*>(wl + t * 1024 + lane * 16);
     const _Float16 sc =
-        *reinterpret_cast<const _Float16*>(wl + WLds<NTW>::SCALES + t * 32 + (lane & 15) * 2);
+        *reinterpret_cast<const _Float16*>(wl + WLds<NTW, MODE>::SCALES + t * 32 + (lane & 15) * 2);
     s2[t] = half2v{sc, sc};
     int zq = 8;
     if (MODE == W_ASYM) {
       const int c = lane & 15;
       const uint32_t zw =
-          *reinterpret_cast<const uint32_t*>(wl + WLds<NTW>::ZEROS + t * 8 + (c >> 3) * 4);
+          *reinterpret_cast<const uint32_t*>(wl + WLds<NTW, MODE>::ZEROS + t * 8 + (c >> 3) * 4);
       zq = (int)((zw >> (4 * (c & 7))) & 15u);
     }
     const _Float16 a0 = (_Float16)(float)(-1024 - zq);
@@ -257,6 +257,73 @@ __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
       for (int t = 0; t < NTW; ++t)
         acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j & 1][t], ar[g % (PF + 1)],
                                                           acc[i][t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// One k-block of the 2:4 format: per column tile, lane l holds two words of kept
+// codes (half h = 0, 1 of the block's 64-row halves; column l%16) and one word of
+// positions (two 16-bit sets, selected by the instruction's abid).  Each group
+// (half h, row tile i) reads the two 32-row activation fragments 2h and 2h+1 of
+// row tile i and runs v_smfmac_f32_16x16x64_f16 with the unpacked weights as the
+// sparse operand: half the matrix instructions and half the unpacking of the dense
+// format for the same k-block.
+template <int MT, int NTW>
+__device__ __forceinline__ void compute_kblock_sp24(const char* xb, const char* wl,
+                                                    float4v (&acc)[MT][NTW],
+                                                    const uint32_t (&aoff)[4], int lane,
+                                                    uint32_t magic,
+                                                    const DmaPlan<MT, NTW, W_SP24>& dma) {
+  typedef WLds<NTW, W_SP24> L;
+  constexpr int G = 2 * MT;  // groups per k-block
+  constexpr int NVL = DmaPlan<MT, NTW, W_SP24>::NV;
+  uint2 wv[NTW];
+  int meta[NTW];
+  half2v s2[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    wv[t] = *reinterpret_cast<const uint2*>(wl + t * 512 + lane * 8);
+    meta[t] = *reinterpret_cast<const int*>(wl + L::META + t * 256 + lane * 4);
+    const _Float16 sc =
+        *reinterpret_cast<const _Float16*>(wl + L::SCALES + t * 32 + (lane & 15) * 2);
+    s2[t] = half2v{sc, sc};
+  }
+  const half2v c0 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const half2v c1 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  // fragment pairs (2h, i), (2h+1, i) of group g = h*MT + i, read one group ahead
+  half8 ar[2][2];
+  ar[0][0] = *reinterpret_cast<const half8*>(xb + aoff[0]);
+  ar[0][1] = *reinterpret_cast<const half8*>(xb + aoff[1]);
+  half8 b[2][NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) b[0][t] = dequant_scaled(wv[t].x, c0, c1, s2[t], magic);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int g = h * MT + i;
+#pragma unroll
+      for (int q = g; q < NVL; q += G) dma.issue(q);
+      if (g + 1 < G) {
+        const int gh = (g + 1) / MT, gi = (g + 1) % MT;
+        ar[(g + 1) & 1][0] = *reinterpret_cast<const half8*>(xb + aoff[2 * gh] + gi * 4096);
+        ar[(g + 1) & 1][1] = *reinterpret_cast<const half8*>(xb + aoff[2 * gh + 1] + gi * 4096);
+      }
+      if (h == 0) {
+#pragma unroll
+        for (int t = i; t < NTW; t += MT) b[1][t] = dequant_scaled(wv[t].y, c0, c1, s2[t], magic);
+      }
+      const half16 xbv = __builtin_shufflevector(ar[g & 1][0], ar[g & 1][1], 0, 1, 2, 3, 4, 5, 6,
+                                                 7, 8, 9, 10, 11, 12, 13, 14, 15);
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        if (h == 0)
+          acc[i][t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(b[0][t], xbv, acc[i][t], meta[t], 0, 0);
+        else
+          acc[i][t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(b[1][t], xbv, acc[i][t], meta[t], 0, 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -333,8 +400,8 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
   constexpr int NSTAGE = NS;       // LDS pipeline stages
   constexpr int AHEAD = NS - 1;    // k-blocks in flight ahead of the one computed
   constexpr int PIECE = BM * BN;   // floats of one partial tile
-  constexpr int STAGE = XBUF + WAVES * WLds<NTW>::BYTES;  // LDS bytes of one stage
-  constexpr int NV = MT + NTW + (MODE == W_ASYM ? 2 : 1);  // loads per stage per thread
+  constexpr int STAGE = XBUF + WAVES * WLds<NTW, MODE>::BYTES;  // LDS bytes of one stage
+  constexpr int NV = DmaPlan<MT, NTW, MODE>::NV;  // loads per stage per thread
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];
 
   const int tid = threadIdx.x;
@@ -372,23 +439,42 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     int nvalid = ntiles16 - t_first;
     nvalid = nvalid < 0 ? 0 : (nvalid > NTW ? NTW : nvalid);
     WSrc<NTW> R;
-    R.w = rsrc_words(reinterpret_cast<const char*>(W) + (size_t)t_first * Gk * 1024,
-                     (uint32_t)(nvalid * Gk * 1024));
     R.s = rsrc_words(Sp + (size_t)t_first * Gk * 16, (uint32_t)(nvalid * Gk * 32));
-    if (MODE == W_ASYM)
-      R.z = rsrc_words(reinterpret_cast<const char*>(Zp) + (size_t)t_first * Gk * 8,
-                       (uint32_t)(nvalid * Gk * 8));
-    else
-      R.z = R.s;
-#pragma unroll
-    for (int t = 0; t < NTW; ++t)
-      R.wo[t] = t < nvalid ? (uint32_t)(t * Gk * 1024 + lane * 16) : kOutOfRange;
     {
-      const int ts = lane >> 3, tz = lane >> 1;
+      const int ts = lane >> 3;
       R.so = (lane < 8 * NTW && ts < nvalid) ? (uint32_t)(ts * Gk * 32 + (lane & 7) * 4)
                                              : kOutOfRange;
-      R.zo = (lane < 2 * NTW && tz < nvalid) ? (uint32_t)(tz * Gk * 8 + (lane & 1) * 4)
-                                             : kOutOfRange;
+    }
+    if (MODE == W_SP24) {
+      // kept codes (512 B per block; lanes 32c.. load tiles 2c, 2c+1) and positions
+      // (256 B per block, passed in Zp; lane L loads tile L/16)
+      R.w = rsrc_words(reinterpret_cast<const char*>(W) + (size_t)t_first * Gk * 512,
+                       (uint32_t)(nvalid * Gk * 512));
+      R.z = rsrc_words(reinterpret_cast<const char*>(Zp) + (size_t)t_first * Gk * 256,
+                       (uint32_t)(nvalid * Gk * 256));
+#pragma unroll
+      for (int c = 0; c < NTW / 2; ++c) {
+        const int t = 2 * c + (lane >> 5);
+        R.wo[c] = t < nvalid ? (uint32_t)(t * Gk * 512 + (lane & 31) * 16) : kOutOfRange;
+      }
+      const int tz = lane >> 4;
+      R.zo = tz < nvalid ? (uint32_t)(tz * Gk * 256 + (lane & 15) * 16) : kOutOfRange;
+    } else {
+      R.w = rsrc_words(reinterpret_cast<const char*>(W) + (size_t)t_first * Gk * 1024,
+                       (uint32_t)(nvalid * Gk * 1024));
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        R.wo[t] = t < nvalid ? (uint32_t)(t * Gk * 1024 + lane * 16) : kOutOfRange;
+      if (MODE == W_ASYM) {
+        R.z = rsrc_words(reinterpret_cast<const char*>(Zp) + (size_t)t_first * Gk * 8,
+                         (uint32_t)(nvalid * Gk * 8));
+        const int tz = lane >> 1;
+        R.zo = (lane < 2 * NTW && tz < nvalid) ? (uint32_t)(tz * Gk * 8 + (lane & 1) * 4)
+                                               : kOutOfRange;
+      } else {
+        R.z = R.s;
+        R.zo = kOutOfRange;
+      }
     }
     // zero-size resources: loads past the segment return zeros without a memory
     // request (their LDS destination still receives zeros), so the number of loads
@@ -406,7 +492,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
 
     const int nk = kb1 - kb0;
     const uint32_t lds0 = lds_addr(lds);
-    const uint32_t wl0 = lds0 + XBUF + wave * WLds<NTW>::BYTES;  // this wave's weight slot, stage 0
+    const uint32_t wl0 = lds0 + XBUF + wave * WLds<NTW, MODE>::BYTES;  // this wave's weight slot, stage 0
     // every wave is done with the LDS buffers of the previous segment
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
@@ -415,8 +501,17 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
 #pragma unroll
     for (int p = 0; p < AHEAD; ++p) {
       const bool live = p < nk;
-      dma_x<MT>(lds0 + p * STAGE, live ? rx : rx0, xoff, wave, kb0 + p);
-      dma_w<NTW, MODE>(wl0 + p * STAGE, live ? R : R0, kb0 + p);
+      DmaPlan<MT, NTW, MODE> plan;
+      plan.rx = live ? rx : rx0;
+#pragma unroll
+      for (int c = 0; c < MT; ++c) plan.xoff[c] = xoff[c];
+      plan.R = live ? R : R0;
+      plan.xdst = lds0 + p * STAGE;
+      plan.wdst = wl0 + p * STAGE;
+      plan.wave = wave;
+      plan.kb = kb0 + p;
+#pragma unroll
+      for (int q = 0; q < DmaPlan<MT, NTW, MODE>::NV; ++q) plan.issue(q);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -442,9 +537,14 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       plan.wdst = wl0 + dn * STAGE;
       plan.wave = wave;
       plan.kb = kbi + AHEAD;
-      compute_kblock<MT, NTW, MODE>(lds + d * STAGE,
-                                    lds + d * STAGE + XBUF + wave * WLds<NTW>::BYTES, acc, aoff,
-                                    lane, magic, plan);
+      if constexpr (MODE == W_SP24)
+        compute_kblock_sp24<MT, NTW>(lds + d * STAGE,
+                                     lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES, acc,
+                                     aoff, lane, magic, plan);
+      else
+        compute_kblock<MT, NTW, MODE>(lds + d * STAGE,
+                                      lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES, acc,
+                                      aoff, lane, magic, plan);
       __builtin_amdgcn_sched_barrier(0);
     };
     // one k-block per trip with a rotating stage index: stages are LDS addresses, so
@@ -548,7 +648,7 @@ typedef void (*FixupFn)(const float*, uint16_t*, TiledArgs);
 
 struct TVariant {
   int MT, NTW, NS;
-  TiledFn sym, asym;
+  TiledFn sym, asym, sp24;
   FixupFn fixup;
   const char* name;
 };
@@ -556,6 +656,7 @@ struct TVariant {
 #define W4A16_TILED(MT, NTW, NS, NAME)                                                       \
   TVariant {                                                                               \
     MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>,       \
+        tiled_kernel<MT, NTW, NS, W_SP24>,                                                  \
         tiled_fixup_kernel<MT, NTW>, NAME                                                   \
   }
 
@@ -574,7 +675,7 @@ int tiled_variant_count() { return kNumTiled; }
 const char* tiled_variant_name(int v) { return (v >= 0 && v < kNumTiled) ? kTiled[v].name : nullptr; }
 
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p) {
-  if (mode != W_SYM && mode != W_ASYM) return -8;
+  if (mode != W_SYM && mode != W_ASYM && mode != W_SP24) return -8;
   // measured on MI355X: the 128-row tile wins from M = 256 on (more reuse of each
   // unpacked weight); at M <= 128 the 64-row tile with a 4-deep ring does
   if (variant < 0) variant = M > 128 ? 0 : 1;
@@ -629,7 +730,7 @@ hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, co
                         const uint32_t* zp, uint16_t* Y, float* part, int* counters,
                         hipStream_t st) {
   const TVariant& v = kTiled[p.variant];
-  TiledFn fn = p.mode == W_ASYM ? v.asym : v.sym;
+  TiledFn fn = p.mode == W_ASYM ? v.asym : p.mode == W_SP24 ? v.sp24 : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint32_t*>(w), sp, zp, Y, part, counters, p.args);
   if (p.fixup_wgs > 0) {
