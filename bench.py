@@ -112,7 +112,8 @@ def pmc_summary(fetch_csv, write_csv):
 
 def large_m_sweep(w4, torch, group):
     """TFLOP/s of w4a16_gemm (automatic plan) on the 70B-class shapes at M >= 256, next to
-    torch's fp16 matmul on the dequantized weights (context).  Inputs are seeded and
+    the hand-written fp16 GEMM on the dequantized weights (w4a16_fp16_gemm, the unfused
+    baseline's GEMM) and torch's fp16 matmul on the same weights (context).  Inputs are seeded and
     synthetic with the workload's distributions (codes uniform 0..15, scales U[0.001,
     0.01], X ~ N(0,1)), generated on the device; each shape is timed over back-to-back
     launches after a warmup."""
@@ -154,11 +155,14 @@ def large_m_sweep(w4, torch, group):
             fl = 2.0 * M * N * K
             reps = max(3, min(50, int(2e13 / fl)))
             t = timed(lambda: w4.w4a16_gemm(X, wp, sp, None, Y, M, N, K, group), reps)
+            tb = timed(lambda: w4.w4a16_fp16_gemm(X, Wt, Y, M, N, K), reps)
             tt = timed(lambda: torch.nn.functional.linear(X, Wt), reps)
             plan = w4.w4a16_gemm_describe(M, N, K, group)
             out.append(dict(M=M, K=K, N=N, us=round(t * 1e6, 2), TFLOPs=round(fl / t / 1e12, 1),
                             mfma_frac=round(fl / t / 1e12 / FP16_PEAK_TFLOPS, 4),
-                            plan=plan["name"], torch_fp16_TFLOPs=round(fl / tt / 1e12, 1)))
+                            plan=plan["name"],
+                            fp16_baseline_TFLOPs=round(fl / tb / 1e12, 1),
+                            torch_fp16_TFLOPs=round(fl / tt / 1e12, 1)))
             del X, Y
         del wp, sp, s, Wt
     torch.cuda.synchronize()

@@ -141,11 +141,21 @@ int w4a16_gemm_describe(int M, int N, int K, int group, int* out4);
  *   rules as w4a16_repack.
  * w4a16_fp16_gemm: Y (device, out) fp16 [M][N] = X [M][K] * Wt[N][K]^T with
  *   fp32 accumulation.  Rules: M, N, K >= 1, K % 128 == 0, N % 16 == 0, 16-byte
- *   aligned pointers.  Uses the same per-stream workspace as w4a16_gemm. */
+ *   aligned pointers.  Uses the same per-stream workspace as w4a16_gemm and the
+ *   same kernel choice (skinny kernel for small batches, tiled kernel with fp16
+ *   weight tiles for the larger ones, by the rule of w4a16_gemm_plan). */
 int w4a16_dequant(const int32_t* q, const uint16_t* s, const int32_t* z, uint16_t* Wt,
                   int K, int N, int group, void* stream);
 int w4a16_fp16_gemm(const uint16_t* X, const uint16_t* Wt, uint16_t* Y,
                     int M, int N, int K, void* stream);
+/* w4a16_fp16_gemm with an explicit plan: variant -1 = automatic, else an index <
+ * w4a16_fp16_gemm_variants(); the skinny variants come first (same names as for
+ * w4a16_gemm), then the fp16 tiled ones ("tiled_f16_*"); `splits` as in
+ * w4a16_gemm_plan.  Names are static strings (NULL if out of range). */
+int w4a16_fp16_gemm_plan(const uint16_t* X, const uint16_t* Wt, uint16_t* Y,
+                         int M, int N, int K, int variant, int splits, void* stream);
+int w4a16_fp16_gemm_variants(void);
+const char* w4a16_fp16_gemm_variant_name(int variant);
 
 /* ---- 2:4 structured sparsity ([P1] "支持 2:4 稀疏加速"; [P2] "4. Support de la
  *      sparsité 2:4") ----------------------------------------------------------------

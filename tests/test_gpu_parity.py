@@ -293,6 +293,59 @@ def test_fp16_gemm_parity(gh, M, K, N):
     assert ok, info
 
 
+F16_TILED = [(300, 2048, 1040), (257, 1536, 528), (130, 1024, 272), (1, 1024, 512),
+             (64, 3072, 128)]
+
+
+@pytest.mark.parametrize("M,K,N", F16_TILED)
+def test_fp16_tiled_parity_grids(gh, M, K, N):
+    """The fp16 baseline's tiled variants (fp16 weight tiles, no unpacking) at several
+    workgroup counts, ragged M and N included, plus the automatic plan; each grid
+    repeats bit for bit."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, X = _case(M, K, N)
+    Wt = torch.empty((N, K), dtype=torch.float16, device="cuda")
+    w4.w4a16_dequant(gh.dev(d["Qp"]), gh.dev(d["s"]), None, Wt, K, N, 128)
+    Xd = gh.dev(X)
+    Yref = oracle.gemm(X, d["Qp"], d["s"], d["Zp"], 128)
+    B = oracle.error_bound(X, d["Qp"], d["s"], d["Zp"], 128)
+    tiled = [v for v in range(w4.w4a16_fp16_gemm_variants())
+             if w4.w4a16_fp16_gemm_variant_name(v).startswith("tiled_f16")]
+    assert len(tiled) >= 2
+    runs = [(-1, 0)] + [(v, g) for v in tiled for g in (0, 1, 3, 5, 8, 24)]
+    for v, grid in runs:
+        Y = gh.nan_filled(M, N)
+        w4.w4a16_fp16_gemm_plan(Xd, Wt, Y, M, N, K, v, grid)
+        first = gh.host(Y).view(np.uint16).copy()
+        ok, info = oracle.accept(first.view(np.float16), Yref, B)
+        assert ok, (w4.w4a16_fp16_gemm_variant_name(v) if v >= 0 else "auto", grid, info)
+        Y2 = gh.nan_filled(M, N)
+        w4.w4a16_fp16_gemm_plan(Xd, Wt, Y2, M, N, K, v, grid)
+        assert np.array_equal(gh.host(Y2).view(np.uint16), first), (v, grid)
+
+
+def test_fp16_tiled_one_hot_is_exact(gh):
+    """One-hot rows through the fp16 tiled variants return the fp16 weight rows exactly."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 200, 1024, 528
+    _, d, _ = _case(M, K, N)
+    rng = np.random.default_rng(8)
+    ks = rng.integers(0, K, size=M)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    W16 = oracle.dequant_fp16(d["Qp"], d["s"], None, K, N, 128)
+    Wt = torch.from_numpy(np.ascontiguousarray(W16.T)).cuda()
+    for v in range(w4.w4a16_fp16_gemm_variants()):
+        if not w4.w4a16_fp16_gemm_variant_name(v).startswith("tiled_f16"):
+            continue
+        for grid in (1, 7):
+            Y = gh.nan_filled(M, N)
+            w4.w4a16_fp16_gemm_plan(gh.dev(X), Wt, Y, M, N, K, v, grid)
+            assert np.array_equal(gh.host(Y).view(np.uint16), W16[ks].view(np.uint16)), (v, grid)
+
+
 def test_error_codes_on_device(gh):
     import torch
     import w4a16_mixed_precision_offline_amd as w4

@@ -36,6 +36,9 @@ _SIGS = {
     "w4a16_gemm_describe": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I)]),
     "w4a16_dequant": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
     "w4a16_fp16_gemm": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "w4a16_fp16_gemm_plan": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "w4a16_fp16_gemm_variants": (_I, []),
+    "w4a16_fp16_gemm_variant_name": (ctypes.c_char_p, [_I]),
     "w4a16_sparse24_repack": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "w4a16_sparse24_unpack": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "w4a16_sparse24_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -102,6 +105,15 @@ def w4a16_gemm_variant_name(v: int):
     return None if r is None else r.decode()
 
 
+def w4a16_fp16_gemm_variants() -> int:
+    return _lib.w4a16_fp16_gemm_variants()
+
+
+def w4a16_fp16_gemm_variant_name(v: int):
+    r = _lib.w4a16_fp16_gemm_variant_name(v)
+    return None if r is None else r.decode()
+
+
 def w4a16_gemm_describe(M: int, N: int, K: int, group: int) -> dict:
     out = (_I * 4)()
     _check("w4a16_gemm_describe", _lib.w4a16_gemm_describe(M, N, K, group, out))
@@ -139,6 +151,11 @@ def w4a16_dequant(q, s, z, Wt, K, N, group, stream=None):
 def w4a16_fp16_gemm(X, Wt, Y, M, N, K, stream=None):
     _check("w4a16_fp16_gemm", _lib.w4a16_fp16_gemm(_ptr(X), _ptr(Wt), _ptr(Y), M, N, K,
                                                    _stream(stream)))
+
+
+def w4a16_fp16_gemm_plan(X, Wt, Y, M, N, K, variant=-1, splits=0, stream=None):
+    _check("w4a16_fp16_gemm_plan", _lib.w4a16_fp16_gemm_plan(
+        _ptr(X), _ptr(Wt), _ptr(Y), M, N, K, variant, splits, _stream(stream)))
 
 
 def w4a16_sparse24_repack(q, s, vp, idx, sp, K, N, group, stream=None):

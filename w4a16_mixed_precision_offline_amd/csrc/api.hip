@@ -158,8 +158,12 @@ int run_fused(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
   const int ns = skinny_variant_count();
   if (variant >= ns)
     return run_tiled(mode, X, w, sp, zp, Y, M, N, K, variant - ns, splits, stream);
-  if (variant < 0 && splits == 0 && use_tiled(M, N, K) && mode != W_FP16)
-    return run_tiled(mode, X, w, sp, zp, Y, M, N, K, -1, 0, stream);
+  if (variant < 0 && splits == 0 && use_tiled(M, N, K)) {
+    // shapes whose tiles would need buffer offsets past 2 GiB stay on the skinny kernel
+    TiledPlan t;
+    if (tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0)
+      return run_tiled(mode, X, w, sp, zp, Y, M, N, K, -1, 0, stream);
+  }
   return run_skinny(mode, X, w, sp, zp, Y, M, N, K, group, variant, splits, stream);
 }
 
@@ -258,10 +262,10 @@ int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const
                    stream);
 }
 
-int w4a16_gemm_variants(void) { return skinny_variant_count() + tiled_variant_count(); }
+int w4a16_gemm_variants(void) { return skinny_variant_count() + tiled_variant_count(W_SYM); }
 const char* w4a16_gemm_variant_name(int variant) {
   const int ns = skinny_variant_count();
-  return variant >= ns ? tiled_variant_name(variant - ns) : skinny_variant_name(variant);
+  return variant >= ns ? tiled_variant_name(W_SYM, variant - ns) : skinny_variant_name(variant);
 }
 
 int w4a16_gemm_describe(int M, int N, int K, int group, int* out4) {
@@ -269,9 +273,8 @@ int w4a16_gemm_describe(int M, int N, int K, int group, int* out4) {
   int rc = check_weight_shape(K, N, group);
   if (rc) return rc;
   if (M <= 0) return W4A16_ERR_SHAPE;
-  if (use_tiled(M, N, K)) {
-    TiledPlan t;
-    if ((rc = tiled_make_plan(M, N, K, W_SYM, -1, 0, &t))) return rc;
+  TiledPlan t;
+  if (use_tiled(M, N, K) && tiled_make_plan(M, N, K, W_SYM, -1, 0, &t) == 0) {
     out4[0] = skinny_variant_count() + t.variant;
     out4[1] = t.args.grid;
     out4[2] = t.wgs;
@@ -298,13 +301,40 @@ int w4a16_dequant(const int32_t* q, const uint16_t* s, const int32_t* z, uint16_
   return launched(launch_dequant(q, s, z, Wt, K, N, group, static_cast<hipStream_t>(stream)));
 }
 
-int w4a16_fp16_gemm(const uint16_t* X, const uint16_t* Wt, uint16_t* Y, int M, int N, int K,
-                    void* stream) {
+namespace {
+int check_fp16_args(const uint16_t* X, const uint16_t* Wt, const uint16_t* Y, int M, int N,
+                    int K) {
   if (!X || !Wt || !Y) return W4A16_ERR_NULL;
   if (M <= 0 || N <= 0 || K <= 0 || K % KBLK != 0 || N % NTILE != 0) return W4A16_ERR_SHAPE;
-  if ((long long)N * K > (1LL << 40) || (long long)M * K > (1LL << 40)) return W4A16_ERR_SHAPE;
+  if ((long long)N * K > (1LL << 40) || (long long)M * K > (1LL << 40) ||
+      (long long)M * N > (1LL << 40))
+    return W4A16_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(Wt) || !aligned16(Y)) return W4A16_ERR_ALIGN;
-  return run_skinny(W_FP16, X, Wt, nullptr, nullptr, Y, M, N, K, KBLK, -1, 0, stream);
+  return W4A16_OK;
+}
+}  // namespace
+
+int w4a16_fp16_gemm(const uint16_t* X, const uint16_t* Wt, uint16_t* Y, int M, int N, int K,
+                    void* stream) {
+  int rc = check_fp16_args(X, Wt, Y, M, N, K);
+  if (rc) return rc;
+  return run_fused(W_FP16, X, Wt, nullptr, nullptr, Y, M, N, K, KBLK, -1, 0, stream);
+}
+
+int w4a16_fp16_gemm_variants(void) {
+  return skinny_variant_count() + tiled_variant_count(W_FP16);
+}
+const char* w4a16_fp16_gemm_variant_name(int variant) {
+  const int ns = skinny_variant_count();
+  return variant >= ns ? tiled_variant_name(W_FP16, variant - ns) : skinny_variant_name(variant);
+}
+
+int w4a16_fp16_gemm_plan(const uint16_t* X, const uint16_t* Wt, uint16_t* Y, int M, int N, int K,
+                         int variant, int splits, void* stream) {
+  int rc = check_fp16_args(X, Wt, Y, M, N, K);
+  if (rc) return rc;
+  if (variant < -1 || variant >= w4a16_fp16_gemm_variants() || splits < 0) return W4A16_ERR_ARG;
+  return run_fused(W_FP16, X, Wt, nullptr, nullptr, Y, M, N, K, KBLK, variant, splits, stream);
 }
 
 // ---- 2:4 structured sparsity ----------------------------------------------------------

@@ -138,7 +138,8 @@ struct WLds {
   // two words at 8l), then NTW 256-byte blocks of positions (lane l's word at 4l).
   static constexpr bool SP = MODE == W_SP24;
   static constexpr int META = NTW * 512;
-  static constexpr int CODES = SP ? NTW * 768 : NTW * 1024;
+  // fp16 weights (baseline): per column tile four 1 KiB fragments (k-steps 0..3)
+  static constexpr int CODES = SP ? NTW * 768 : MODE == W_FP16 ? NTW * 4096 : NTW * 1024;
   static constexpr int SCALES = CODES;
   static constexpr int ZEROS = CODES + 256;
   static constexpr int BYTES = CODES + 512;
@@ -165,8 +166,8 @@ __device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 25
 template <int MT, int NTW, int MODE>
 struct DmaPlan {
   // 2:4: two tiles' kept codes per 16-byte load, all four tiles' positions in one
-  static constexpr int NW = MODE == W_SP24 ? NTW / 2 + NTW / 4 : NTW;
-  static constexpr int NV = MT + NW + (MODE == W_ASYM ? 2 : 1);
+  static constexpr int NW = MODE == W_SP24 ? NTW / 2 + NTW / 4 : MODE == W_FP16 ? 4 * NTW : NTW;
+  static constexpr int NV = MT + NW + (MODE == W_ASYM ? 2 : MODE == W_FP16 ? 0 : 1);
   u32x4 rx;
   uint32_t xoff[MT];
   WSrc<NTW> R;
@@ -181,10 +182,13 @@ struct DmaPlan {
       dma16(R.w, wdst + c * 1024, R.wo[c], (uint32_t)kb * 512u);
     } else if (MODE == W_SP24 && q < MT + NW) {
       dma16(R.z, wdst + L::META + (q - MT - NTW / 2) * 1024, R.zo, (uint32_t)kb * 256u);
-    } else if (MODE != W_SP24 && q < MT + NTW) {
+    } else if (MODE == W_FP16 && q < MT + NW) {
+      const int t = (q - MT) >> 2, j = (q - MT) & 3;  // rows 32j.. of column tile t
+      dma16(R.w, wdst + (t * 4 + j) * 1024, R.wo[t], (uint32_t)kb * 256u + 64u * j);
+    } else if (MODE != W_SP24 && MODE != W_FP16 && q < MT + NTW) {
       const int t = q - MT;
       dma16(R.w, wdst + t * 1024, R.wo[t], (uint32_t)kb * 1024u);
-    } else if (q == MT + NW) {
+    } else if (MODE != W_FP16 && q == MT + NW) {
       dma4(R.s, wdst + L::SCALES, R.so, (uint32_t)kb * 32u);
     } else if (MODE == W_ASYM && q == MT + NW + 1) {
       dma4(R.z, wdst + L::ZEROS, R.zo, (uint32_t)kb * 8u);
@@ -329,6 +333,50 @@ __device__ __forceinline__ void compute_kblock_sp24(const char* xb, const char* 
   }
 }
 
+// One k-block of the fp16 baseline: weight fragments come straight from LDS (no
+// unpacking); same group pipeline as the packed formats.
+template <int MT, int NTW>
+__device__ __forceinline__ void compute_kblock_fp16(const char* xb, const char* wl,
+                                                    float4v (&acc)[MT][NTW],
+                                                    const uint32_t (&aoff)[4], int lane,
+                                                    const DmaPlan<MT, NTW, W_FP16>& dma) {
+  constexpr int G = 4 * MT;
+  constexpr int NVL = DmaPlan<MT, NTW, W_FP16>::NV;
+  constexpr int PF = 3;
+  half8 ar[PF + 1];
+#pragma unroll
+  for (int g = 0; g < PF; ++g)
+    if (g < G) ar[g] = *reinterpret_cast<const half8*>(xb + aoff[g / MT] + (g % MT) * 4096);
+  half8 b[2][NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t)
+    b[0][t] = *reinterpret_cast<const half8*>(wl + (t * 4) * 1024 + lane * 16);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int g = j * MT + i;
+#pragma unroll
+      for (int q = g; q < NVL; q += G) dma.issue(q);
+      if (g + PF < G) {
+        const int gj = (g + PF) / MT, gi = (g + PF) % MT;
+        ar[(g + PF) % (PF + 1)] = *reinterpret_cast<const half8*>(xb + aoff[gj] + gi * 4096);
+      }
+      if (j < 3) {
+#pragma unroll
+        for (int t = i; t < NTW; t += MT)
+          b[(j + 1) & 1][t] = *reinterpret_cast<const half8*>(wl + (t * 4 + j + 1) * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j & 1][t], ar[g % (PF + 1)],
+                                                          acc[i][t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // vmcnt(n) with the other counters left alone (gfx9 encoding)
 __device__ __forceinline__ constexpr int vmcnt_enc(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
@@ -439,13 +487,27 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     int nvalid = ntiles16 - t_first;
     nvalid = nvalid < 0 ? 0 : (nvalid > NTW ? NTW : nvalid);
     WSrc<NTW> R;
-    R.s = rsrc_words(Sp + (size_t)t_first * Gk * 16, (uint32_t)(nvalid * Gk * 32));
-    {
+    if (MODE != W_FP16) {
+      R.s = rsrc_words(Sp + (size_t)t_first * Gk * 16, (uint32_t)(nvalid * Gk * 32));
       const int ts = lane >> 3;
       R.so = (lane < 8 * NTW && ts < nvalid) ? (uint32_t)(ts * Gk * 32 + (lane & 7) * 4)
                                              : kOutOfRange;
+    } else {
+      R.s = rsrc_words(W, 0);  // no scales
+      R.so = kOutOfRange;
     }
-    if (MODE == W_SP24) {
+    if (MODE == W_FP16) {
+      // fp16 rows of the wave's columns: lane L of the load for (tile t, k-step j) reads
+      // 16 bytes of row 16t + L%16 at column 128kb + 32j + 8(L/16)
+      R.w = rsrc_words(reinterpret_cast<const char*>(W) + (size_t)t_first * 16 * a.K * 2,
+                       (uint32_t)((size_t)nvalid * 16 * a.K * 2));
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        R.wo[t] = t < nvalid ? (uint32_t)(((16 * t + (lane & 15)) * (size_t)a.K + 8 * (lane >> 4)) * 2)
+                             : kOutOfRange;
+      R.z = R.s;
+      R.zo = kOutOfRange;
+    } else if (MODE == W_SP24) {
       // kept codes (512 B per block; lanes 32c.. load tiles 2c, 2c+1) and positions
       // (256 B per block, passed in Zp; lane L loads tile L/16)
       R.w = rsrc_words(reinterpret_cast<const char*>(W) + (size_t)t_first * Gk * 512,
@@ -482,7 +544,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     const u32x4 rx0 = rsrc_words(X, 0);
     WSrc<NTW> R0 = R;
     R0.w = rsrc_words(W, 0);
-    R0.s = rsrc_words(Sp, 0);
+    R0.s = rsrc_words(W, 0);
     R0.z = R0.s;
 
 #pragma unroll
@@ -537,7 +599,11 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       plan.wdst = wl0 + dn * STAGE;
       plan.wave = wave;
       plan.kb = kbi + AHEAD;
-      if constexpr (MODE == W_SP24)
+      if constexpr (MODE == W_FP16)
+        compute_kblock_fp16<MT, NTW>(lds + d * STAGE,
+                                     lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES, acc,
+                                     aoff, lane, plan);
+      else if constexpr (MODE == W_SP24)
         compute_kblock_sp24<MT, NTW>(lds + d * STAGE,
                                      lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES, acc,
                                      aoff, lane, magic, plan);
@@ -648,7 +714,7 @@ typedef void (*FixupFn)(const float*, uint16_t*, TiledArgs);
 
 struct TVariant {
   int MT, NTW, NS;
-  TiledFn sym, asym, sp24;
+  TiledFn sym, asym, sp24, f16;
   FixupFn fixup;
   const char* name;
 };
@@ -656,8 +722,13 @@ struct TVariant {
 #define W4A16_TILED(MT, NTW, NS, NAME)                                                       \
   TVariant {                                                                               \
     MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>,       \
-        tiled_kernel<MT, NTW, NS, W_SP24>,                                                  \
-        tiled_fixup_kernel<MT, NTW>, NAME                                                   \
+        tiled_kernel<MT, NTW, NS, W_SP24>, nullptr, tiled_fixup_kernel<MT, NTW>, NAME        \
+  }
+// the fp16 baseline moves four times the weight bytes: its own LDS-sized tiles
+#define W4A16_TILED_F16(MT, NTW, NS, NAME)                                                    \
+  TVariant {                                                                               \
+    MT, NTW, NS, nullptr, nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_FP16>,              \
+        tiled_fixup_kernel<MT, NTW>, NAME                                                  \
   }
 
 const TVariant kTiled[] = {
@@ -668,19 +739,30 @@ const TVariant kTiled[] = {
     W4A16_TILED(1, 4, 4, "tiled_bm16_bn256_s4"),
 };
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
+const TVariant kTiledF16[] = {
+    W4A16_TILED_F16(8, 2, 2, "tiled_f16_bm128_bn128_s2"),
+    W4A16_TILED_F16(4, 2, 3, "tiled_f16_bm64_bn128_s3"),
+};
+constexpr int kNumTiledF16 = sizeof(kTiledF16) / sizeof(kTiledF16[0]);
 
 }  // namespace
 
-int tiled_variant_count() { return kNumTiled; }
-const char* tiled_variant_name(int v) { return (v >= 0 && v < kNumTiled) ? kTiled[v].name : nullptr; }
+int tiled_variant_count(int mode) { return mode == W_FP16 ? kNumTiledF16 : kNumTiled; }
+const char* tiled_variant_name(int mode, int v) {
+  if (v < 0 || v >= tiled_variant_count(mode)) return nullptr;
+  return mode == W_FP16 ? kTiledF16[v].name : kTiled[v].name;
+}
 
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p) {
-  if (mode != W_SYM && mode != W_ASYM && mode != W_SP24) return -8;
+  if (mode != W_SYM && mode != W_ASYM && mode != W_SP24 && mode != W_FP16) return -8;
+  const bool f16 = mode == W_FP16;
+  const TVariant* table = f16 ? kTiledF16 : kTiled;
+  const int count = f16 ? kNumTiledF16 : kNumTiled;
   // measured on MI355X: the 128-row tile wins from M = 256 on (more reuse of each
   // unpacked weight); at M <= 128 the 64-row tile with a 4-deep ring does
   if (variant < 0) variant = M > 128 ? 0 : 1;
-  if (variant >= kNumTiled) return -8;
-  const TVariant& v = kTiled[variant];
+  if (variant >= count) return -8;
+  const TVariant& v = table[variant];
   const int BM = 16 * v.MT, BN = WAVES * 16 * v.NTW;
   const int Gk = K / KBLK;
   TiledPlan q;
@@ -694,6 +776,10 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   q.args.group_m = 8;
   const long T = (long)q.args.tiles_m * q.args.tiles_n;
   if (T > (1L << 30)) return -2;
+  // buffer offsets are 32-bit: the rows of X and Y one tile touches, and the fp16
+  // weight rows of one wave, must stay below 2 GiB from their base
+  const long long xrows = BM > 16 * v.NTW ? BM : 16 * v.NTW;
+  if (xrows * K * 2 >= (1LL << 31) || (long long)BM * N * 2 >= (1LL << 31)) return -2;
   if (grid <= 0) {
     // one workgroup per compute unit; fewer for small problems, so that a stripe
     // holds at least a few k-blocks
@@ -729,8 +815,11 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
                         const uint32_t* zp, uint16_t* Y, float* part, int* counters,
                         hipStream_t st) {
-  const TVariant& v = kTiled[p.variant];
-  TiledFn fn = p.mode == W_ASYM ? v.asym : p.mode == W_SP24 ? v.sp24 : v.sym;
+  const TVariant& v = p.mode == W_FP16 ? kTiledF16[p.variant] : kTiled[p.variant];
+  TiledFn fn = p.mode == W_ASYM   ? v.asym
+               : p.mode == W_SP24 ? v.sp24
+               : p.mode == W_FP16 ? v.f16
+                                  : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint32_t*>(w), sp, zp, Y, part, counters, p.args);
   if (p.fixup_wgs > 0) {

@@ -79,7 +79,7 @@ hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                          const uint16_t* sp, const uint32_t* zp, uint16_t* Y, float* part,
                          int* counters, int M, int N, int K, int group, hipStream_t st);
 
-// Fused tiled GEMM for larger M (sym / asym weights only).  Tile geometry and the
+// Tiled GEMM for larger M (packed weights, dense or 2:4, and the fp16 baseline).  Tile geometry and the
 // data-parallel / stream-K work split are fixed by the plan.
 struct TiledArgs {
   int M, N, K;
@@ -91,15 +91,16 @@ struct TiledArgs {
 };
 struct TiledPlan {
   int variant;  // index into the tiled variant table
-  int mode;     // W_SYM or W_ASYM
+  int mode;     // WMode
   TiledArgs args;
   int wgs, threads;
   size_t part_floats;  // workspace floats for partial tiles (two slots per workgroup)
   int counters;        // arrival counters (none: the second pass needs no hand-off)
   int fixup_wgs;       // workgroups of the second pass (stream-K tiles), 0 if none
 };
-int tiled_variant_count();
-const char* tiled_variant_name(int v);
+// The fp16 baseline (W_FP16) has its own variant table; the packed formats share one.
+int tiled_variant_count(int mode);
+const char* tiled_variant_name(int mode, int v);
 // variant < 0: automatic; grid <= 0: automatic number of workgroups.
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p);
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
