@@ -74,6 +74,12 @@ def test_describe_plans(raw):
         assert raw.w4a16_gemm_describe(M, N, K, 128, out) == 0
         assert 0 <= out[0] < raw.w4a16_gemm_variants()
         assert out[1] >= 1 and out[2] >= 1 and out[3] in (64, 128, 256, 512, 1024)
+    # wide layers: three column tiles per wave where that fills the 256 compute units
+    # better (N = 12288: 256 workgroups), else four (N = 11008: 172)
+    raw.w4a16_gemm_variant_name.restype = ctypes.c_char_p
+    for (N, name) in [(12288, b"skinny_xr16_nt3_wk4_d2"), (11008, b"skinny_xr16_nt4_wk4_d2")]:
+        assert raw.w4a16_gemm_describe(16, N, 4096, 128, out) == 0
+        assert raw.w4a16_gemm_variant_name(out[0]) == name
     assert raw.w4a16_gemm_describe(0, 4096, 4096, 128, out) == -2
     assert raw.w4a16_gemm_describe(1, 4096, 4096, 128, None) == -1
 

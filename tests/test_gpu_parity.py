@@ -70,10 +70,14 @@ def test_repack_unpack_roundtrip(gh, K, N, asym):
 # ---- bit-exact pins ---------------------------------------------------------------
 @pytest.mark.parametrize("asym", [False, True])
 @pytest.mark.parametrize("splits", [1, 3])
-def test_onehot_rows_bit_exact(gh, asym, splits):
-    # a one-hot row of X selects one weight row: Y must equal RNE((q - z) * s) exactly
+@pytest.mark.parametrize("variant", ["skinny_xr16_nt2_wk8_d2", "skinny_xr16_nt3_wk4_d2",
+                                     "skinny_xr16_nt4_wk4_d2"])
+def test_onehot_rows_bit_exact(gh, asym, splits, variant):
+    # a one-hot row of X selects one weight row: Y must equal RNE((q - z) * s) exactly,
+    # whether the scale is applied to the fp32 sums (one or two column tiles per wave)
+    # or to the fp16 weights (three or more)
     import torch
-    K, N = 1024, 256
+    K, N = 1024, 768
     _, d, _ = _case(16, K, N, asym)
     ks = [0, 1, 7, 8, 9, 127, 128, 255, 300, 511, 512, 640, 777, 900, 1022, 1023]
     X = np.zeros((16, K), np.float16)
@@ -81,8 +85,7 @@ def test_onehot_rows_bit_exact(gh, asym, splits):
         X[m, k] = 1
     W16 = oracle.dequant_fp16(d["Qp"], d["s"], d["Zp"], K, N, 128)
     packed = gh.repack(d, K, N)
-    Y = gh.gemm(gh.dev(X), packed, 16, N, K, variant=gh.variant_index("skinny_xr16_nt2_wk8_d2"),
-                splits=splits)
+    Y = gh.gemm(gh.dev(X), packed, 16, N, K, variant=gh.variant_index(variant), splits=splits)
     Yh = gh.host(Y)
     exp = W16[ks]
     assert np.array_equal(Yh.astype(np.float64), exp.astype(np.float64))

@@ -28,9 +28,12 @@
 //   * Dequantization uses the 0x6400 exponent trick: OR-ing a nibble into the
 //     mantissa of 1024.0 gives the exact fp16 1024+q (or 1024+16q for the high
 //     nibble of a byte), and one packed fp16 add / fma removes the offset and the
-//     zero-point, giving the exact integer q - z.  The scale is applied after the
-//     four v_mfma_f32_16x16x32_f16 of the k-block, in fp32, on the 4 accumulators
-//     of the lane (1 fma per output instead of 1 multiply per weight).
+//     zero-point, giving the exact integer q - z.  With one or two column tiles per
+//     wave the scale is applied after the four v_mfma_f32_16x16x32_f16 of the
+//     k-block, in fp32, on the 4 accumulators of the lane (1 fma per output instead
+//     of 1 multiply per weight); with three or more, the weights are multiplied by
+//     the scale in fp16 (one rounding, as in the dequantized fp16 weight) and the
+//     matrix instructions accumulate straight into the output registers.
 //   * The WK waves of a workgroup take contiguous chunks of the K range of the
 //     same output tiles and reduce through LDS in a fixed order.
 //   * When a tile's K range is cut into `splits` slices owned by different
@@ -231,6 +234,21 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
       b[1] = dequant_word(S.w[t][0].y, c0, c1, magic);
       b[2] = dequant_word(S.w[t][0].z, c0, c1, magic);
       b[3] = dequant_word(S.w[t][0].w, c0, c1, magic);
+    }
+    if constexpr (NT >= 3 && MODE != W_FP16) {
+      // many column tiles per wave: multiply the weights by the scale in fp16 (one
+      // rounding of W, the fp16 dequantized weight) and accumulate straight into acc;
+      // measured faster than rescaling the fp32 partial sum of every (tile, row tile)
+      const _Float16 sh = __builtin_bit_cast(_Float16, S.s[t]);
+      const half8 s8 = {sh, sh, sh, sh, sh, sh, sh, sh};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = b[j] * s8;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][j], b[j], acc[t][mt], 0, 0, 0);
+      continue;
     }
     // row tiles past M hold zero activations and add exactly zero; no branch here
 #pragma unroll
@@ -485,7 +503,10 @@ const Variant kVariants[] = {
     W4A16_VARIANT(32, 2, 8, 2),  W4A16_VARIANT(64, 1, 4, 2),  W4A16_VARIANT(64, 2, 4, 2),
     W4A16_VARIANT(64, 1, 8, 2),  W4A16_VARIANT(8, 4, 4, 2),   W4A16_VARIANT(16, 4, 4, 2),
     W4A16_VARIANT(32, 4, 4, 2),  W4A16_VARIANT(16, 4, 2, 2),  W4A16_VARIANT(32, 4, 2, 2),
-    W4A16_VARIANT(16, 8, 2, 2),  W4A16_VARIANT(8, 8, 2, 2),
+    W4A16_VARIANT(16, 8, 2, 2),  W4A16_VARIANT(8, 8, 2, 2),   W4A16_VARIANT(4, 2, 8, 4),
+    W4A16_VARIANT(8, 2, 8, 4),   W4A16_VARIANT(8, 4, 8, 2),   W4A16_VARIANT(16, 4, 8, 2),
+    W4A16_VARIANT(32, 4, 8, 2),  W4A16_VARIANT(8, 3, 4, 2),   W4A16_VARIANT(16, 3, 4, 2),
+    W4A16_VARIANT(32, 3, 4, 2),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -515,18 +536,25 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
     const int XR = M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : M <= 32 ? 32 : 64;
     const bool wide = N % 64 == 0 && N / 16 > 256;
     const bool longk = K / KBLK > 48;
-    // From 8 rows on, wide layers give each wave four column tiles: the activation
-    // rows a wave loads are then reused over 64 columns instead of 16-32.
+    // From 8 rows on, wide layers give each wave four column tiles (three when that
+    // fills the 256 compute units more evenly, e.g. N = 12288: 256 workgroups instead
+    // of 192): the activation rows a wave loads are then reused over 48-64 columns
+    // instead of 16-32.
+    int ntw = 4;
+    if (wide && N % 48 == 0) {
+      auto fill = [](long wgs) { return (double)wgs / (256.0 * ((wgs + 255) / 256)); };
+      if (fill(N / 48) > fill(N / 64)) ntw = 3;
+    }
     if (XR == 4) {
       variant = wide ? find_variant(4, 1, 4, 4)
                      : (longk ? find_variant(4, 1, 16, 2) : find_variant(4, 1, 8, 4));
     } else if (XR == 8) {
-      variant = wide ? find_variant(8, 4, 4, 2) : find_variant(8, 1, 8, 4);
+      variant = wide ? find_variant(8, ntw, 4, 2) : find_variant(8, 1, 8, 4);
     } else if (XR == 16) {
-      variant = wide ? find_variant(16, 4, 4, 2)
+      variant = wide ? find_variant(16, ntw, 4, 2)
                      : (longk ? find_variant(16, 1, 8, 2) : find_variant(16, 1, 4, 4));
     } else if (XR == 32) {
-      variant = wide ? find_variant(32, 4, 4, 2) : find_variant(32, 1, 4, 2);
+      variant = wide ? find_variant(32, ntw, 4, 2) : find_variant(32, 1, 4, 2);
     } else {
       variant = find_variant(64, 1, 4, 2);
     }
