@@ -100,9 +100,9 @@ def pmc_summary(fetch_csv, write_csv):
                write_kib_per_launch=round(res["write"]["kib_per_launch"], 1),
                launches=res["fetch"]["launches"],
                commands=["rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- "
-                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph --no-large --copy-calibration",
+                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph --no-large --no-configs --copy-calibration",
                          "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- "
-                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph --no-large --copy-calibration",
+                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph --no-large --no-configs --copy-calibration",
                          "python bench.py --pmc-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
                          "gpurun_out/pmc_write/run_counter_collection.csv"])
     with open(TRAFFIC_JSON, "w") as f:

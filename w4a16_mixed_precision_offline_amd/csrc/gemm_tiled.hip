@@ -401,11 +401,13 @@ __device__ __forceinline__ void tile_coords(int tt, int tiles_m, int tiles_n, in
   tn = __builtin_amdgcn_readfirstlane(r / gm);
 }
 
-// Y store of a finished tile tt: lane holds row 16i + lane%16 and the four columns
-// 16t + 4(lane/16) .. +3 of each of the wave's NTW column tiles.
-template <int MT, int NTW>
-__device__ __forceinline__ void store_tile(uint16_t* __restrict__ Y, const TiledArgs& a, int tt,
-                                           int wave, int lane, const float4v (&acc)[MT][NTW]) {
+// Y store of row tiles i0 .. i0 + NI - 1 of a finished tile tt: lane holds row 16i +
+// lane%16 and the four columns 16t + 4(lane/16) .. +3 of each of the wave's NTW column
+// tiles.
+template <int MT, int NTW, int NI>
+__device__ __forceinline__ void store_rows(uint16_t* __restrict__ Y, const TiledArgs& a, int tt,
+                                           int i0, int wave, int lane,
+                                           const float4v (&acc)[NI][NTW]) {
   constexpr int BM = 16 * MT;
   constexpr int BN = WAVES * 16 * NTW;
   int tm, tn;
@@ -419,16 +421,21 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ Y, const Tiled
   for (int t = 0; t < NTW; ++t) {
     if (t_first + t >= ntiles16) break;  // wave-uniform
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int r = 16 * i + (lane & 15);
+    for (int ii = 0; ii < NI; ++ii) {
+      const int r = 16 * (i0 + ii) + (lane & 15);
       const uint32_t off = r < rows ? (uint32_t)(((size_t)r * a.N + (t_first + t) * 16 +
                                                   4 * (lane >> 4)) * 2)
                                     : kOutOfRange;
       typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 v = {pack_h2(acc[i][t][0], acc[i][t][1]), pack_h2(acc[i][t][2], acc[i][t][3])};
+      const u32x2 v = {pack_h2(acc[ii][t][0], acc[ii][t][1]), pack_h2(acc[ii][t][2], acc[ii][t][3])};
       __builtin_amdgcn_raw_buffer_store_b64(v, ry, off, 0u, 0);
     }
   }
+}
+template <int MT, int NTW>
+__device__ __forceinline__ void store_tile(uint16_t* __restrict__ Y, const TiledArgs& a, int tt,
+                                           int wave, int lane, const float4v (&acc)[MT][NTW]) {
+  store_rows<MT, NTW, MT>(Y, a, tt, 0, wave, lane, acc);
 }
 
 // Byte offset of one lane's float4 of (row tile i, column tile t) inside a partial piece.
@@ -673,39 +680,51 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
   }
 }
 
-// Second pass of the stream-K split: one workgroup per tile of the stream-K part;
-// a tile cut into pieces by stripe boundaries gets the pieces summed in stripe order
-// (a fixed order, so results are bitwise reproducible) and written to Y.  Tiles done
-// by a single workgroup were stored by it directly.
+// Second pass of the stream-K split: one workgroup per (tile of the stream-K part, row
+// tile of 16 rows); a tile cut into pieces by stripe boundaries gets the pieces summed in
+// stripe order (a fixed order, so results are bitwise reproducible) and written to Y.
+// Tiles done by a single workgroup were stored by it directly.  The loads of up to four
+// pieces are in flight together.
 template <int MT, int NTW>
 __global__ __launch_bounds__(64 * WAVES) void tiled_fixup_kernel(const float* __restrict__ part,
                                                                  uint16_t* __restrict__ Y,
                                                                  TiledArgs a) {
   constexpr int PIECE = 16 * MT * WAVES * 16 * NTW;
+  constexpr int CH = 4;  // pieces per batch of loads
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tl = blockIdx.x;
+  const int tl = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / MT));
+  const int i = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % MT));
   const uint32_t Gk = (uint32_t)(a.K / KBLK);
   const uint32_t U = (uint32_t)a.sk_per_wg;
   const int w_first = __builtin_amdgcn_readfirstlane((int)(((uint32_t)tl * Gk) / U));
   const int w_last = __builtin_amdgcn_readfirstlane((int)(((uint32_t)(tl + 1) * Gk - 1) / U));
   if (w_first == w_last) return;
-  float4v sum[MT][NTW];
-  for (int wp = w_first; wp <= w_last; ++wp) {
-    const int first_tile_of_wp = (int)(((uint32_t)wp * U) / Gk);
-    const int sl = __builtin_amdgcn_readfirstlane(2 * wp + (tl == first_tile_of_wp ? 0 : 1));
-    const rsrc_t rp = make_rsrc(part + (size_t)sl * PIECE, PIECE * 4);
+  float4v sum[1][NTW];
+  for (int wp = w_first; wp <= w_last; wp += CH) {
+    float4v v[CH][NTW];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int c = 0; c < CH; ++c) {
+      const int wq = wp + c;
+      const bool live = wq <= w_last;  // uniform; past the last piece: zero-size reads
+      const int first_tile_of_wq = (int)(((uint32_t)wq * U) / Gk);
+      const int sl = __builtin_amdgcn_readfirstlane(
+          live ? 2 * wq + (tl == first_tile_of_wq ? 0 : 1) : 0);
+      const rsrc_t rp = make_rsrc(part + (size_t)sl * PIECE, live ? PIECE * 4 : 0);
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        const float4v v = __builtin_bit_cast(
+      for (int t = 0; t < NTW; ++t)
+        v[c][t] = __builtin_bit_cast(
             float4v, __builtin_amdgcn_raw_buffer_load_b128(rp, piece_off<MT, NTW>(wave, i, t, lane),
                                                            0u, 0));
-        sum[i][t] = wp == w_first ? v : sum[i][t] + v;
-      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (wp + c > w_last) break;  // uniform
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) sum[0][t] = wp + c == w_first ? v[c][t] : sum[0][t] + v[c][t];
+    }
   }
-  store_tile<MT, NTW>(Y, a, a.dp_rounds * a.grid + tl, wave, lane, sum);
+  store_rows<MT, NTW, 1>(Y, a, a.dp_rounds * a.grid + tl, i, wave, lane, sum);
 }
 
 typedef void (*TiledFn)(const uint16_t*, const uint32_t*, const uint16_t*, const uint32_t*,
@@ -787,6 +806,7 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     long g = (T * Gk + min_units - 1) / min_units;
     grid = (int)(g < 256 ? (g < 1 ? 1 : g) : 256);
   }
+  if ((long long)grid > (long long)T * Gk) grid = (int)(T * Gk);  // at least one unit each
   q.args.grid = grid;
   // all but the last one or two rounds of tiles are data-parallel; the rest (between
   // one and two rounds' worth) is striped.  Measured: striping only the remainder
@@ -804,7 +824,8 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   // the kernel keeps its stripe bookkeeping in 32 bits
   if (q.args.sk_units + q.args.sk_per_wg + Gk >= (1LL << 31)) return -2;
   q.counters = 0;
-  q.fixup_wgs = (int)sk_tiles;
+  if ((long long)sk_tiles * v.MT > (1LL << 30)) return -2;
+  q.fixup_wgs = (int)sk_tiles * v.MT;  // one workgroup per (stream-K tile, row tile)
   q.part_floats = sk_tiles ? (size_t)2 * grid * BM * BN : 0;
   q.wgs = grid;
   q.threads = 64 * WAVES;

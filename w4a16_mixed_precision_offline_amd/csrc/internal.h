@@ -96,7 +96,7 @@ struct TiledPlan {
   int wgs, threads;
   size_t part_floats;  // workspace floats for partial tiles (two slots per workgroup)
   int counters;        // arrival counters (none: the second pass needs no hand-off)
-  int fixup_wgs;       // workgroups of the second pass (stream-K tiles), 0 if none
+  int fixup_wgs;       // workgroups of the second pass (stream-K tiles x row tiles), 0 if none
 };
 // The fp16 baseline (W_FP16) has its own variant table; the packed formats share one.
 int tiled_variant_count(int mode);
