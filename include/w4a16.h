@@ -128,6 +128,14 @@ int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const
 int w4a16_gemm_variants(void);
 const char* w4a16_gemm_variant_name(int variant);
 
+/* Bytes of device workspace the automatic plans of w4a16_gemm, w4a16_sparse24_gemm and
+ * w4a16_fp16_gemm need for an (M, N, K) GEMM on one stream (the largest over the weight
+ * formats; 0 when no plan for the shape reduces across workgroups, or for an invalid
+ * shape).  The library allocates this itself, per (device, stream), on the first call
+ * that needs it and keeps it for later calls; the query lets a caller budget device
+ * memory ahead of time.  Host only. */
+size_t w4a16_workspace_bytes(int M, int N, int K);
+
 /* Describe the automatic plan for a shape: out[0] = variant, out[1] = the splits
  * value that reproduces it in w4a16_gemm_plan,
  * out[2] = workgroups launched, out[3] = threads per workgroup.  Host only. */

@@ -125,6 +125,37 @@ def test_repack_validation(raw):
     assert g(A, A, None, A, A, None, 0, 1024, 128, None) == -2
 
 
+def test_workspace_bytes(raw):
+    f = raw.w4a16_workspace_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int] * 3
+    assert f(0, 4096, 4096) == 0 and f(16, 4000, 4096) == 0 and f(16, 4096, 100) == 0
+    # a wide decode layer runs without cross-workgroup reduction
+    assert f(1, 12288, 4096) == 0
+    # 8192 x 28672 at M = 256: 224 tiles of 128 x 256 on 256 workgroups, all striped:
+    # two fp32 partial tiles per workgroup
+    assert f(256, 28672, 8192) >= 2 * 256 * 128 * 256 * 4
+    # M = 4096 on the same layer: 14 (fp16 tiles: 28) whole rounds of tiles, no stripes
+    assert f(4096, 28672, 8192) == 0
+
+
+def test_fp16_plan_validation(raw):
+    f = raw.w4a16_fp16_gemm_plan
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    raw.w4a16_fp16_gemm_variant_name.restype = ctypes.c_char_p
+    n = raw.w4a16_fp16_gemm_variants()
+    assert n > raw.w4a16_gemm_variants() - 5  # skinny variants plus the fp16 tiled ones
+    names = [raw.w4a16_fp16_gemm_variant_name(v) for v in range(n)]
+    assert all(names) and raw.w4a16_fp16_gemm_variant_name(n) is None
+    assert sum(nm.startswith(b"tiled_f16") for nm in names) >= 2
+    assert f(None, A, A, 1, 16, 128, -1, 0, None) == -1
+    assert f(A, A, A, 1, 16, 100, -1, 0, None) == -2
+    assert f(A, A, A, 1, 16, 128, n, 0, None) == -8
+    assert f(A, A, A, 1, 16, 128, -2, 0, None) == -8
+    assert f(A, A, A, 1, 16, 128, 0, -1, None) == -8
+    assert f(A, MIS, A, 1, 16, 128, -1, 0, None) == -3
+
+
 def test_baseline_validation(raw):
     f = raw.w4a16_fp16_gemm
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]

@@ -34,6 +34,7 @@ _SIGS = {
     "w4a16_gemm_variants": (_I, []),
     "w4a16_gemm_variant_name": (ctypes.c_char_p, [_I]),
     "w4a16_gemm_describe": (_I, [_I, _I, _I, _I, ctypes.POINTER(_I)]),
+    "w4a16_workspace_bytes": (_SZ, [_I, _I, _I]),
     "w4a16_dequant": (_I, [_P, _P, _P, _P, _I, _I, _I, _P]),
     "w4a16_fp16_gemm": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "w4a16_fp16_gemm_plan": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
@@ -112,6 +113,10 @@ def w4a16_fp16_gemm_variants() -> int:
 def w4a16_fp16_gemm_variant_name(v: int):
     r = _lib.w4a16_fp16_gemm_variant_name(v)
     return None if r is None else r.decode()
+
+
+def w4a16_workspace_bytes(M: int, N: int, K: int) -> int:
+    return _lib.w4a16_workspace_bytes(M, N, K)
 
 
 def w4a16_gemm_describe(M: int, N: int, K: int, group: int) -> dict:

@@ -290,6 +290,31 @@ int w4a16_gemm_describe(int M, int N, int K, int group, int* out4) {
   return W4A16_OK;
 }
 
+size_t w4a16_workspace_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % KBLK != 0 || N % NTILE != 0) return 0;
+  // the automatic plan of every weight format (the largest need), laid out as
+  // get_workspace lays it out: counters rounded up to 64 ints, then the partials
+  size_t need = 0;
+  const int modes[] = {W_SYM, W_ASYM, W_SP24, W_FP16};
+  for (int mode : modes) {
+    size_t counters = 0, floats = 0;
+    TiledPlan t;
+    if (use_tiled(M, N, K) && tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0) {
+      counters = (size_t)t.counters;
+      floats = t.part_floats;
+    } else {
+      SkinnyPlan p;
+      if (skinny_make_plan(M, N, K, KBLK, mode, -1, 0, &p) != 0) continue;
+      counters = (size_t)p.counters;
+      floats = p.part_floats;
+    }
+    if (counters == 0 && floats == 0) continue;
+    const size_t bytes = (counters + 63) / 64 * 64 * sizeof(int) + floats * sizeof(float);
+    if (bytes > need) need = bytes;
+  }
+  return need;
+}
+
 int w4a16_dequant(const int32_t* q, const uint16_t* s, const int32_t* z, uint16_t* Wt, int K,
                   int N, int group, void* stream) {
   if (!q || !s || !Wt) return W4A16_ERR_NULL;

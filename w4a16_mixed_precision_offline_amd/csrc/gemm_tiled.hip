@@ -777,9 +777,10 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   const bool f16 = mode == W_FP16;
   const TVariant* table = f16 ? kTiledF16 : kTiled;
   const int count = f16 ? kNumTiledF16 : kNumTiled;
-  // measured on MI355X: the 128-row tile wins from M = 256 on (more reuse of each
-  // unpacked weight); at M <= 128 the 64-row tile with a 4-deep ring does
-  if (variant < 0) variant = M > 128 ? 0 : 1;
+  // measured on MI355X: the 128-row tile wins from M = 128 on (more reuse of each
+  // unpacked weight; 11% at M = 128 on 8192 x 28672); above 64 rows both tiles compute
+  // 128 padded rows, so the 64-row tile with a 4-deep ring is kept for M <= 64 only
+  if (variant < 0) variant = M > 64 ? 0 : 1;
   if (variant >= count) return -8;
   const TVariant& v = table[variant];
   const int BM = 16 * v.MT, BN = WAVES * 16 * v.NTW;
