@@ -16,28 +16,30 @@
 //     columns; the waves split the columns (wave w: 16*NTW columns) and share the
 //     rows, so each weight byte is loaded and unpacked by exactly one wave, and
 //     the activation tile is shared through LDS.
-//   * Per 128-row k-block the activation tile (BM x 128 fp16) is loaded row-
-//     contiguously (16 threads per 256-byte row) into registers and written into
-//     one of two LDS buffers (rows padded to 272 bytes); a wave reads MFMA
-//     fragments from it (lane l: row 16i + l%16, 8 halves at 32j + 8(l/16)).
-//   * The weights of a wave's column tiles arrive as one 16-byte load per lane
-//     per 1 KiB repacked block, which is already the operand fragment of the four
-//     v_mfma_f32_16x16x32_f16 of the block.  Codes become exact fp16 (q - z) with
-//     the 0x6400 exponent trick and are multiplied by the fp16 scale (one
-//     rounding of W, as in the dequantized fp16 weight), so the accumulators need
-//     no per-block rescaling.
+//   * Per 128-row k-block the activation tile (BM x 128 fp16) and each wave's
+//     weight blocks, scales (and zero-points) are loaded straight into LDS
+//     (direct-to-LDS buffer loads) into a ring of NS stages; loads for k-block
+//     kb + NS - 1 are issued, one per matrix-instruction group, while kb is
+//     computed.  The activation tile is XOR-swizzled by 16-byte chunk so that a
+//     fragment read (lane l: row 16i + l%16, 8 halves at 32j + 8(l/16)) hits every
+//     LDS bank once.
+//   * A wave's weight block is 1 KiB in the repacked layout: lane l's 16 bytes are
+//     already the operand fragment of the four v_mfma_f32_16x16x32_f16 of the
+//     block.  Codes become exact fp16 (q - z) with the 0x6400 exponent trick and
+//     are multiplied by the fp16 scale (one rounding of W, as in the dequantized
+//     fp16 weight), so the accumulators need no per-block rescaling.
 //   * W is the MFMA's A operand and X its B operand: a lane's accumulator then
 //     holds four consecutive columns of one row of Y (one 8-byte store).
-//   * Loads for k-block kb+2 are issued while kb is computed (two register stages
-//     for the weights, LDS double buffer for the activations).
 //   * Work split: the first full rounds of tiles are handed out data-parallel (one
 //     tile per workgroup per round, full K); the remaining tiles' (tile, k-block)
 //     units are cut into equal contiguous stripes over all workgroups (stream-K).
-//     A tile cut by a stripe boundary is finished by the last of its pieces to
-//     arrive: every piece writes its fp32 partial with cross-XCD coherent (sc1)
-//     stores and bumps the tile's arrival counter; the last arriver reads all
-//     pieces back in stripe order (a fixed order, hence deterministic results),
-//     writes Y and resets the counter for the next launch.
+//     A workgroup stores the fp32 partial tile of its first and last stripe
+//     segment when the segment does not cover the whole K range; a second kernel
+//     sums each cut tile's pieces in stripe order (a fixed order, hence bitwise
+//     reproducible results) and writes Y.
+//   * The same skeleton runs the 2:4 format (kept codes and positions in LDS,
+//     v_smfmac_f32_16x16x64_f16) and the fp16 baseline (fp16 weight fragments,
+//     no unpacking).
 #include "internal.h"
 
 namespace w4a16 {
