@@ -140,6 +140,13 @@ def large_m_sweep(w4, torch, group):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3 / reps
 
+    # measured ceiling: dense fp16 matrix instructions with no memory traffic, after the
+    # same 50 ms warmup (the clock settles lower under sustained matrix load)
+    probe_out = torch.zeros(4, dtype=torch.float32, device="cuda")
+    pw, pi = 1024, 2000  # about 0.4 ms per launch
+    tp = timed(lambda: w4.w4a16_probe_mfma(pw, pi, probe_out), 5)
+    mfma_probe = w4.w4a16_probe_mfma_flops(pw, pi) / tp / 1e12
+
     for (K, N) in shapes:
         q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
                           generator=gen)
@@ -160,6 +167,7 @@ def large_m_sweep(w4, torch, group):
             plan = w4.w4a16_gemm_describe(M, N, K, group)
             out.append(dict(M=M, K=K, N=N, us=round(t * 1e6, 2), TFLOPs=round(fl / t / 1e12, 1),
                             mfma_frac=round(fl / t / 1e12 / FP16_PEAK_TFLOPS, 4),
+                            frac_of_mfma_probe=round(fl / t / 1e12 / mfma_probe, 4),
                             plan=plan["name"],
                             fp16_baseline_TFLOPs=round(fl / tb / 1e12, 1),
                             torch_fp16_TFLOPs=round(fl / tt / 1e12, 1)))
@@ -168,6 +176,7 @@ def large_m_sweep(w4, torch, group):
     torch.cuda.synchronize()
     big = [r for r in out if r["M"] >= 1024]
     return dict(peak_TFLOPs=FP16_PEAK_TFLOPS, unit="TFLOP/s",
+                mfma_probe_TFLOPs=round(mfma_probe, 1),
                 min_mfma_frac_M_ge_1024=min(r["mfma_frac"] for r in big),
                 mean_mfma_frac_M_ge_1024=round(sum(r["mfma_frac"] for r in big) / len(big), 4),
                 runs=out)
@@ -475,6 +484,30 @@ def main():
                         w4_speedup_vs_torch_matmul=round(ttorch / t_step, 3))
         del Wt
 
+    # ---- measured ceiling: a plain streaming read of each launch's packed codes -------
+    # (calibration kernel of the library, same launch list, weight rotation and HIP
+    # graphs): at 8-25 MiB per launch, launch and ramp keep any kernel far below the
+    # 8 TB/s spec, so the GEMM is also set against what a read-only kernel achieves
+    plain_read = None
+    if not args.no_baseline:
+        probe_out = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+        def run_step_read(step_idx):
+            cyc = step_idx % steps_per_cycle
+            for i, M in enumerate(Ms):
+                for (K, N) in shapes:
+                    wp, _ = packed[(K, N)][cyc * copies_per_step + i]
+                    w4.w4a16_probe_read(wp, K * N // 2, probe_out)
+
+        tread, _ = time_steps(run_step_read, max(5, args.steps // 2), 2, not args.no_graph)
+        code_bytes = sum(K * N // 2 for (_, K, N, _) in launches)
+        plain_read = dict(kernel="w4a16_probe_read over each launch's packed codes (16-byte "
+                                 "non-temporal streaming read, nothing else)",
+                          GBps=round(code_bytes / tread / 1e9, 1),
+                          us_per_launch=round(tread / n_launch * 1e6, 3),
+                          frac_of_peak=round(code_bytes / tread / 1e9 / HBM_PEAK_GBPS, 4),
+                          gemm_time_over_read_time=round(t_step / tread, 3))
+
     # ---- large-M sweep: 70B-class single-GPU shapes, where the matrix cores bound ------
     large = None
     if not args.no_large:
@@ -545,6 +578,7 @@ def main():
             "kernel": "w4a16 fused GEMM (skinny_kernel), mean over the 24 launches of a step",
             "algorithmic_bytes_per_launch": int(step_alg / n_launch),
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "measured_ceiling": plain_read,
         },
         "cpu_baseline": cpu,
         "fp16_baseline": baseline,

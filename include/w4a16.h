@@ -196,6 +196,23 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
                              const uint16_t* sp, uint16_t* Y, int M, int N, int K, int group,
                              int variant, int splits, void* stream);
 
+/* ---- calibration kernels (measurement only) ---------------------------------------
+ * The achievable ceilings the GEMM's rates are set against, beside the published peaks.
+ * w4a16_probe_read: one plain streaming read of `bytes` bytes at device pointer p
+ *   (16-byte aligned, bytes a positive multiple of 16) with 16-byte non-temporal loads.
+ *   The data is XOR-folded per thread; out (device, one uint32) is written only when a
+ *   thread's fold equals 0x9E3779B9, otherwise left untouched.
+ * w4a16_probe_mfma: `workgroups` workgroups of 4 waves, each wave running `iters`
+ *   rounds of 4 independent v_mfma_f32_32x32x16_f16 on register operands (no memory
+ *   traffic); out (device, one float) is never written in practice.
+ *   w4a16_probe_mfma_flops gives the flops of such a launch (host only).
+ * Both return the usual codes: W4A16_ERR_NULL, W4A16_ERR_SHAPE (read size),
+ * W4A16_ERR_ALIGN, W4A16_ERR_ARG (workgroups outside 1..65536 or iters < 1),
+ * W4A16_ERR_DEVICE, W4A16_ERR_LAUNCH. */
+int w4a16_probe_read(const void* p, size_t bytes, uint32_t* out, void* stream);
+int w4a16_probe_mfma(int workgroups, int iters, float* out, void* stream);
+double w4a16_probe_mfma_flops(int workgroups, int iters);
+
 #ifdef __cplusplus
 }
 #endif

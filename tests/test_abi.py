@@ -156,6 +156,25 @@ def test_fp16_plan_validation(raw):
     assert f(A, MIS, A, 1, 16, 128, -1, 0, None) == -3
 
 
+def test_probe_validation(raw):
+    f = raw.w4a16_probe_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 16, A, None) == -1
+    assert f(A, 16, None, None) == -1
+    assert f(A, 0, A, None) == -2
+    assert f(A, 24, A, None) == -2
+    assert f(MIS, 16, A, None) == -3
+    g = raw.w4a16_probe_mfma
+    g.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert g(1, 1, None, None) == -1
+    assert g(0, 1, A, None) == -8 and g(65537, 1, A, None) == -8 and g(1, 0, A, None) == -8
+    h = raw.w4a16_probe_mfma_flops
+    h.restype = ctypes.c_double
+    h.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert h(256, 10) == 256 * 4 * 10 * 4 * 2 * 32 * 32 * 16
+    assert h(0, 10) == 0.0
+
+
 def test_baseline_validation(raw):
     f = raw.w4a16_fp16_gemm
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]

@@ -44,6 +44,9 @@ _SIGS = {
     "w4a16_sparse24_unpack": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "w4a16_sparse24_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "w4a16_sparse24_gemm_plan": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "w4a16_probe_read": (_I, [_P, _SZ, _P, _P]),
+    "w4a16_probe_mfma": (_I, [_I, _I, _P, _P]),
+    "w4a16_probe_mfma_flops": (ctypes.c_double, [_I, _I]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -183,6 +186,19 @@ def w4a16_sparse24_gemm_plan(X, vp, idx, sp, Y, M, N, K, group, variant=-1, spli
     _check("w4a16_sparse24_gemm_plan", _lib.w4a16_sparse24_gemm_plan(
         _ptr(X), _ptr(vp), _ptr(idx), _ptr(sp), _ptr(Y), M, N, K, group, variant, splits,
         _stream(stream)))
+
+
+# ---- calibration kernels ---------------------------------------------------------
+def w4a16_probe_read(p, nbytes, out, stream=None):
+    _check("w4a16_probe_read", _lib.w4a16_probe_read(_ptr(p), nbytes, _ptr(out), _stream(stream)))
+
+
+def w4a16_probe_mfma(workgroups, iters, out, stream=None):
+    _check("w4a16_probe_mfma", _lib.w4a16_probe_mfma(workgroups, iters, _ptr(out), _stream(stream)))
+
+
+def w4a16_probe_mfma_flops(workgroups: int, iters: int) -> float:
+    return _lib.w4a16_probe_mfma_flops(workgroups, iters)
 
 
 # ---- allocation helper (device memory through torch) ---------------------------

@@ -436,3 +436,26 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
 }
 
 }  // extern "C"
+
+// ---- calibration kernels -------------------------------------------------------------
+int w4a16_probe_read(const void* p, size_t bytes, uint32_t* out, void* stream) {
+  if (!p || !out) return W4A16_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return W4A16_ERR_SHAPE;
+  if (!aligned16(p)) return W4A16_ERR_ALIGN;
+  int rc;
+  if ((rc = check_device(nullptr))) return rc;
+  return launched(launch_probe_read(p, bytes, out, static_cast<hipStream_t>(stream)));
+}
+
+int w4a16_probe_mfma(int workgroups, int iters, float* out, void* stream) {
+  if (!out) return W4A16_ERR_NULL;
+  if (workgroups < 1 || workgroups > 65536 || iters < 1) return W4A16_ERR_ARG;
+  int rc;
+  if ((rc = check_device(nullptr))) return rc;
+  return launched(launch_probe_mfma(workgroups, iters, out, static_cast<hipStream_t>(stream)));
+}
+
+double w4a16_probe_mfma_flops(int workgroups, int iters) {
+  if (workgroups < 1 || iters < 1) return 0.0;
+  return probe_mfma_flops(workgroups, iters);
+}

@@ -107,4 +107,9 @@ hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, co
                         const uint32_t* zp, uint16_t* Y, float* part, int* counters,
                         hipStream_t st);
 
+// Calibration kernels (probes.hip).
+hipError_t launch_probe_read(const void* p, size_t bytes, uint32_t* out, hipStream_t st);
+hipError_t launch_probe_mfma(int workgroups, int iters, float* out, hipStream_t st);
+double probe_mfma_flops(int workgroups, int iters);
+
 }  // namespace w4a16
