@@ -146,8 +146,8 @@ int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   int* cnt;
   float* part;
-  if ((rc = get_workspace(dev, st, plan.counters, plan.part_floats, &cnt, &part))) return rc;
-  return launched(tiled_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, cnt, st));
+  if ((rc = get_workspace(dev, st, 0, plan.part_floats, &cnt, &part))) return rc;
+  return launched(tiled_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, st));
 }
 
 // Variant numbering of the ABI: the skinny variants first, then the tiled ones.
@@ -300,7 +300,6 @@ size_t w4a16_workspace_bytes(int M, int N, int K) {
     size_t counters = 0, floats = 0;
     TiledPlan t;
     if (use_tiled(M, N, K) && tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0) {
-      counters = (size_t)t.counters;
       floats = t.part_floats;
     } else {
       SkinnyPlan p;

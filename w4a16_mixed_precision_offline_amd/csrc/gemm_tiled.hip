@@ -450,7 +450,7 @@ template <int MT, int NTW, int NS, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,
     const uint16_t* __restrict__ Sp, const uint32_t* __restrict__ Zp, uint16_t* __restrict__ Y,
-    float* __restrict__ part, int* __restrict__ counters, TiledArgs a) {
+    float* __restrict__ part, TiledArgs a) {
   constexpr int BM = 16 * MT;
   constexpr int BN = WAVES * 16 * NTW;
   constexpr int XBUF = BM * 256;   // one k-block of the activation tile
@@ -730,7 +730,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_fixup_kernel(const float* __
 }
 
 typedef void (*TiledFn)(const uint16_t*, const uint32_t*, const uint16_t*, const uint32_t*,
-                        uint16_t*, float*, int*, TiledArgs);
+                        uint16_t*, float*, TiledArgs);
 typedef void (*FixupFn)(const float*, uint16_t*, TiledArgs);
 
 struct TVariant {
@@ -826,7 +826,6 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   if (q.args.sk_per_wg < 1) q.args.sk_per_wg = 1;
   // the kernel keeps its stripe bookkeeping in 32 bits
   if (q.args.sk_units + q.args.sk_per_wg + Gk >= (1LL << 31)) return -2;
-  q.counters = 0;
   if ((long long)sk_tiles * v.MT > (1LL << 30)) return -2;
   q.fixup_wgs = (int)sk_tiles * v.MT;  // one workgroup per (stream-K tile, row tile)
   q.part_floats = sk_tiles ? (size_t)2 * grid * BM * BN : 0;
@@ -837,15 +836,14 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
 }
 
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
-                        const uint32_t* zp, uint16_t* Y, float* part, int* counters,
-                        hipStream_t st) {
+                        const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st) {
   const TVariant& v = p.mode == W_FP16 ? kTiledF16[p.variant] : kTiled[p.variant];
   TiledFn fn = p.mode == W_ASYM   ? v.asym
                : p.mode == W_SP24 ? v.sp24
                : p.mode == W_FP16 ? v.f16
                                   : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
-                     reinterpret_cast<const uint32_t*>(w), sp, zp, Y, part, counters, p.args);
+                     reinterpret_cast<const uint32_t*>(w), sp, zp, Y, part, p.args);
   if (p.fixup_wgs > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -95,7 +95,6 @@ struct TiledPlan {
   TiledArgs args;
   int wgs, threads;
   size_t part_floats;  // workspace floats for partial tiles (two slots per workgroup)
-  int counters;        // arrival counters (none: the second pass needs no hand-off)
   int fixup_wgs;       // workgroups of the second pass (stream-K tiles x row tiles), 0 if none
 };
 // The fp16 baseline (W_FP16) has its own variant table; the packed formats share one.
@@ -104,8 +103,7 @@ const char* tiled_variant_name(int mode, int v);
 // variant < 0: automatic; grid <= 0: automatic number of workgroups.
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p);
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
-                        const uint32_t* zp, uint16_t* Y, float* part, int* counters,
-                        hipStream_t st);
+                        const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st);
 
 // Calibration kernels (probes.hip).
 hipError_t launch_probe_read(const void* p, size_t bytes, uint32_t* out, hipStream_t st);
