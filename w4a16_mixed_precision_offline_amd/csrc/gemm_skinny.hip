@@ -34,7 +34,7 @@
 //     of 1 multiply per weight); with three or more, the weights are multiplied by
 //     the scale in fp16 (one rounding, as in the dequantized fp16 weight) and the
 //     matrix instructions accumulate straight into the output registers.
-//   * The WK waves of a workgroup take contiguous chunks of the K range of the
+//   * The WK waves of a workgroup take interleaved k-blocks of the K range of the
 //     same output tiles and reduce through LDS in a fixed order.
 //   * When a tile's K range is cut into `splits` slices owned by different
 //     workgroups, each writes an fp32 partial, bumps an arrival counter, and the
@@ -306,8 +306,11 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   const int kb0 = (int)(((long)Gk * sl) / splits);
   const int kb1 = (int)(((long)Gk * (sl + 1)) / splits);
   const int nk_wg = kb1 - kb0;
-  const int kw0 = kb0 + (nk_wg * wave) / WK;
-  const int nk = kb0 + (nk_wg * (wave + 1)) / WK - kw0;
+  // wave w takes the k-blocks kb0 + w, kb0 + w + WK, ...: the waves of a workgroup read
+  // neighbouring 1 KiB blocks at the same time (measured 1-6% faster on the decode
+  // shapes than contiguous chunks per wave)
+  const int kw0 = kb0 + wave;
+  const int nk = nk_wg > wave ? (nk_wg - wave + WK - 1) / WK : 0;
   const int t0 = nb * NT;
   const int m0 = mb * XR;
   char* xlds = lds + wave * XTILE;
@@ -370,14 +373,14 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   Stage<XR, NT, MODE> S[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    load_stage(S[d], kw0 + d, d < nk, lane, Gk, K, R, Rnull, xoff);
+    load_stage(S[d], kw0 + d * WK, d < nk, lane, Gk, K, R, Rnull, xoff);
     __builtin_amdgcn_sched_barrier(0);  // issue the stages in order
   }
   for (int i = 0; i < nk; i += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       compute_stage(S[d], acc, lane, magic, xlds);
-      load_stage(S[d], kw0 + i + d + D, i + d + D < nk, lane, Gk, K, R, Rnull, xoff);
+      load_stage(S[d], kw0 + (i + d + D) * WK, i + d + D < nk, lane, Gk, K, R, Rnull, xoff);
       // keep stage order: the compiler would otherwise merge the stages and wait
       // for every outstanding load before the first one is computed
       __builtin_amdgcn_sched_barrier(0);
