@@ -302,7 +302,7 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   const int nb = bid % nblocks;
   const int mb = bid / nblocks;
   const int Gk = K / KBLK;
-  // K range of this workgroup's slice, then this wave's contiguous chunk of it
+  // K range of this workgroup's slice, then this wave's k-blocks in it
   const int kb0 = (int)(((long)Gk * sl) / splits);
   const int kb1 = (int)(((long)Gk * (sl + 1)) / splits);
   const int nk_wg = kb1 - kb0;
