@@ -117,8 +117,8 @@ int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void
  *             For a "tiled_*" variant (persistent workgroups over tiles, the
  *             (tile, k-block) work cut into equal stripes), the number of
  *             workgroups.
- * Automatic plans use the tiled kernel for larger batches (M >= 256, or M >= 96
- * with K*N >= 32 Mi, or M >= 48 with K*N >= 128 Mi) and the skinny kernel otherwise.
+ * Automatic plans use the skinny kernel for M <= 32 and the tiled kernel above,
+ * except for 33 <= M < 256 on layers with K*N < 32 Mi and N >= 2048 (skinny).
  * The same variants and rules apply to the 2:4 format (w4a16_sparse24_gemm_plan). */
 int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                     uint16_t* Y, int M, int N, int K, int group,

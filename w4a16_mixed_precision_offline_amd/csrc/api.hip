@@ -124,16 +124,17 @@ int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, c
                                 M, N, K, group, st));
 }
 
-// Which kernel an automatic plan uses, from sweeps on MI355X: the tiled kernel once
-// the batch gives each unpacked weight enough reuse and the weight matrix is large
-// enough to fill the chip with 64-row tiles; the skinny (memory-bound) kernel
-// otherwise.
+// Which kernel an automatic plan uses, from sweeps on MI355X: the skinny (memory-bound)
+// kernel up to 32 rows; above that the tiled kernel (1.6-2.1x faster at M = 48-64 on
+// layers of 70-235 Mi weights, and on narrow layers such as 3072 x 768), except on
+// layers under 32 Mi weights with at least 2048 columns (2560 x 2560, 4096 x 4096),
+// where the tiled kernel has too few tiles and the skinny kernel's one workgroup per
+// column tile still fills the chip.
 bool use_tiled(int M, int N, int K) {
   const long long kn = (long long)K * N;
+  if (M <= 32) return false;
   if (M >= 256) return true;
-  if (M >= 96 && kn >= (32LL << 20)) return true;
-  if (M >= 48 && kn >= (128LL << 20)) return true;
-  return false;
+  return !(kn < (32LL << 20) && N >= 2048);
 }
 
 int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,

@@ -781,8 +781,10 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   const int count = f16 ? kNumTiledF16 : kNumTiled;
   // measured on MI355X: the 128-row tile wins from M = 128 on (more reuse of each
   // unpacked weight; 11% at M = 128 on 8192 x 28672); above 64 rows both tiles compute
-  // 128 padded rows, so the 64-row tile with a 4-deep ring is kept for M <= 64 only
-  if (variant < 0) variant = M > 64 ? 0 : 1;
+  // 128 padded rows, so the 64-row tile (3-deep ring: 1-4% faster than 4-deep at
+  // M = 48-64) is kept for M <= 64 only.  The fp16 baseline's table: 128 x 128 above
+  // 64 rows, 64 x 128 up to 64.
+  if (variant < 0) variant = M > 64 ? 0 : (f16 ? 1 : 2);
   if (variant >= count) return -8;
   const TVariant& v = table[variant];
   const int BM = 16 * v.MT, BN = WAVES * 16 * v.NTW;
