@@ -808,7 +808,10 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   q.args.K = K;
   q.args.tiles_m = (M + BM - 1) / BM;
   q.args.tiles_n = (N + BN - 1) / BN;
-  q.args.group_m = 8;
+  // tiles are handed out in groups of 4 row tiles (then the next column tiles): the 32
+  // workgroups of an XCD then share 4 row tiles of X and 8 column tiles of W in its L2
+  // (measured 0-8% faster than groups of 8 on the 70B-class layers)
+  q.args.group_m = 4;
   const long T = (long)q.args.tiles_m * q.args.tiles_n;
   if (T > (1L << 30)) return -2;
   // buffer offsets are 32-bit: the rows of X and Y one tile touches, and the fp16
