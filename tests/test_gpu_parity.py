@@ -396,3 +396,100 @@ def test_hip_graph_replays_match_eager(gh):
         for c, e in zip(cases, eager):
             assert np.array_equal(gh.host(c[5]).view(np.uint16), e), rep
         del junk
+
+
+# ---- degenerate and boundary cases ----------------------------------------------------
+def _pack_k(q: np.ndarray) -> np.ndarray:
+    """uint8 codes [K, N] -> int32 [K/8, N], nibble j of word i = row 8i + j."""
+    K, N = q.shape
+    w = np.zeros((K // 8, N), np.uint32)
+    for j in range(8):
+        w |= q[j::8].astype(np.uint32) << np.uint32(4 * j)
+    return w.view(np.int32)
+
+
+def _pack_n(z: np.ndarray) -> np.ndarray:
+    """uint8 zero-points [G, N] -> int32 [G, N/8], nibble j of word c = column 8c + j."""
+    G, N = z.shape
+    w = np.zeros((G, N // 8), np.uint32)
+    for j in range(8):
+        w |= z[:, j::8].astype(np.uint32) << np.uint32(4 * j)
+    return w.view(np.int32)
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_codes_equal_to_zero_points_give_exact_zero(gh, asym):
+    """q = z everywhere makes W = 0: Y must be exactly zero on every kernel path (skinny
+    with and without a K split, tiled with stream-K pieces), for any activations."""
+    import w4a16_mixed_precision_offline_amd as w4
+    K, N = 2048, 528
+    rng = np.random.default_rng(11)
+    G = K // 128
+    z = rng.integers(0, 16, size=(G, N), dtype=np.uint8) if asym else np.full((G, N), 8, np.uint8)
+    q = np.repeat(z, 128, axis=0)
+    s = rng.uniform(0.002, 0.02, size=(G, N)).astype(np.float32).astype(np.float16)
+    d = dict(Qp=_pack_k(q), s=s, Zp=_pack_n(z) if asym else None)
+    packed = gh.repack(d, K, N)
+    tiled = [v for v in range(w4.w4a16_gemm_variants())
+             if w4.w4a16_gemm_variant_name(v).startswith("tiled")]
+    for M in (1, 16, 300):
+        X = rng.standard_normal((M, K), dtype=np.float32).astype(np.float16)
+        Xd = gh.dev(X)
+        runs = [(-1, 0), (gh.variant_index("skinny_xr16_nt1_wk4_d4"), 3)] + [(v, 7) for v in tiled]
+        for v, sp in runs:
+            Y = gh.nan_filled(M, N)
+            gh.gemm(Xd, packed, M, N, K, variant=v, splits=sp, Y=Y)
+            assert np.all(gh.host(Y).astype(np.float32) == 0.0), (M, v, sp)
+
+
+@pytest.mark.parametrize("M,K,N,asym", [(1, 128, 16, False), (300, 128, 16, True), (17, 256, 32, False)])
+def test_minimal_shapes_every_variant(gh, M, K, N, asym):
+    """One 128-row group and one or two 16-column tiles, through every variant that
+    accepts the shape (a tile of 16 columns, a single k-block, ragged rows)."""
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, X = _case(M, K, N, asym)
+    packed = gh.repack(d, K, N)
+    Xd = gh.dev(X)
+    Yref = oracle.gemm(X, d["Qp"], d["s"], d["Zp"], 128)
+    B = oracle.error_bound(X, d["Qp"], d["s"], d["Zp"], 128)
+    ran = 0
+    for v in range(w4.w4a16_gemm_variants()):
+        name = w4.w4a16_gemm_variant_name(v)
+        nt = 1 if name.startswith("tiled") else int(name.split("_nt")[1].split("_")[0])
+        if N % (16 * nt):
+            continue
+        for splits in (0, 1, 2):
+            Y = gh.nan_filled(M, N)
+            gh.gemm(Xd, packed, M, N, K, variant=v, splits=splits, Y=Y)
+            ok, info = oracle.accept(gh.host(Y), Yref, B)
+            assert ok, (name, splits, info)
+            ran += 1
+    assert ran > 0
+
+
+def test_offsets_past_2_gib_use_the_skinny_kernel(gh):
+    """K = 2^23 at M = 256: a 128-row tile of X spans 2 GiB, past the tiled kernel's 32-bit
+    buffer offsets, so the automatic plan runs the skinny kernel (64-row blocks, K split
+    across workgroups); sampled outputs against the oracle."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 256, 1 << 23, 16
+    plan = w4.w4a16_gemm_describe(M, N, K, 128)
+    assert plan["name"].startswith("skinny"), plan
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    X = torch.randn((M, K), device="cuda", generator=g).half()
+    q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda", generator=g)
+    s = (torch.rand((K // 128, N), device="cuda", generator=g) * 0.018 + 0.002).half()
+    wp, sp, _ = w4.alloc_packed(K, N, 128, False)
+    w4.w4a16_repack(q, s, None, wp, sp, None, K, N, 128)
+    Y = gh.nan_filled(M, N)
+    w4.w4a16_gemm(X, wp, sp, None, Y, M, N, K, 128)
+    rows = [0, 63, 64, 255]
+    Xr = gh.host(X[rows])
+    del X
+    Qp, sh = gh.host(q), gh.host(s)
+    Yref, B = oracle.gemm_sampled(Xr, Qp, sh, None, 128, list(range(4)),
+                                  list(range(N)))
+    ok, info = oracle.accept(gh.host(Y)[rows], Yref, B)
+    assert ok, info
