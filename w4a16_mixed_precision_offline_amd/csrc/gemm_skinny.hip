@@ -54,14 +54,6 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half16 __attribute__((ext_vector_type(16)));
 
-// 16-byte loads: streamed (non-temporal) for weights, cached for activations
-__device__ __forceinline__ u32x4 load16_nt(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ u32x4 load16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
 // Buffer resources: the uniform part of an address goes to the scalar offset, the
 // per-lane part to a fixed VGPR offset, and lanes whose offset is past num_records
 // read zeros without touching memory (used for rows of X beyond M), so no branch
@@ -604,6 +596,7 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
 hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                          const uint16_t* sp, const uint32_t* zp, uint16_t* Y, float* part,
                          int* counters, int M, int N, int K, int group, hipStream_t st) {
+  (void)group;  // the repacked layout stores one scale row per 128-row block
   const Variant& v = kVariants[p.variant];
   KernelFn fn = p.mode == W_FP16 ? v.f16
                : p.mode == W_ASYM ? v.asym

@@ -81,12 +81,16 @@ __device__ __forceinline__ void dma16(u32x4 r, uint32_t lds, uint32_t voff, uint
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+#else
+  (void)r, (void)lds, (void)voff, (void)soff;  // host pass: device-only instruction
 #endif
 }
 __device__ __forceinline__ void dma4(u32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+#else
+  (void)r, (void)lds, (void)voff, (void)soff;  // host pass: device-only instruction
 #endif
 }
 
