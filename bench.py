@@ -278,6 +278,51 @@ def config_legs(w4, torch, group):
     return sp, dict(kernel="w4a16_gemm with 4-bit zero-points", runs=as_runs)
 
 
+def group64_leg(w4, torch):
+    """Groups of 64 rows (two scale rows per 128-row block) against groups of 128 on the
+    same codes: decode shapes from the 7B-class sweep and one large-M layer, symmetric
+    and with zero-points.  Seeded synthetic weights (codes uniform 0..15, scales
+    U[0.002, 0.02], zero-points uniform 0..15) generated on the device; weights rotate
+    over copies totalling at least 512 MiB."""
+    rot = 512 << 20
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(64)
+    runs = []
+    for (K, N, Ms) in [(4096, 11008, (1, 16, 32)), (8192, 10240, (1024,))]:
+        q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
+                          generator=gen)
+        packs = {}
+        for g in (128, 64):
+            s = (torch.rand((K // g, N), device="cuda", generator=gen) * 0.018 + 0.002).half()
+            z = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // g, N // 8), dtype=torch.int32,
+                              device="cuda", generator=gen)
+            for asym in (False, True):
+                pk = w4.alloc_packed(K, N, g, asym)
+                w4.w4a16_repack(q, s, z if asym else None, *pk, K, N, g)
+                n = max(2, -(-rot // (K * N // 2)))
+                packs[(g, asym)] = [pk] + [tuple(t.clone() if t is not None else None for t in pk)
+                                           for _ in range(n - 1)]
+        for M in Ms:
+            X = torch.randn((M, K), device="cuda", generator=gen).half()
+            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            for asym in (False, True):
+                t = {}
+                for g in (128, 64):
+                    t[g] = time_rotated(torch, [lambda c=c, g=g: w4.w4a16_gemm(X, c[0], c[1], c[2], Y,
+                                                                             M, N, K, g)
+                                                for c in packs[(g, asym)]])
+                wb64 = K * N // 2 + 4 * (K // 128) * N + ((K // 64) * N // 2 if asym else 0)
+                runs.append(dict(M=M, K=K, N=N, zero_points=asym, g128_us=round(t[128] * 1e6, 2),
+                                 g64_us=round(t[64] * 1e6, 2),
+                                 g64_over_g128_time=round(t[64] / t[128], 3),
+                                 g64_weight_GBps=round(wb64 / t[64] / 1e9, 1),
+                                 g64_TFLOPs=round(2.0 * M * N * K / t[64] / 1e12, 1)))
+            del X, Y
+        del q, packs
+        torch.cuda.empty_cache()
+    return dict(kernel="w4a16_gemm with groups of 64 rows vs 128", runs=runs)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -518,6 +563,10 @@ def main():
     if not args.no_configs:
         sparse24, asym = config_legs(w4, torch, group)
 
+    group64 = None
+    if not args.no_configs:
+        group64 = group64_leg(w4, torch)
+
     # ---- CPU oracle on this host over one step (bounded sample) -----------------------
     cpu = None
     if not args.no_cpu:
@@ -585,6 +634,7 @@ def main():
         "large_m_sweep": large,
         "sparse24_vs_dense": sparse24,
         "asym_zero_point": asym,
+        "group64": group64,
         "per_launch_us": [[p["M"], p["K"], p["N"], p["us"]] for p in per_launch],
     }
     if args.detail:

@@ -38,7 +38,7 @@ extern "C" {
 /* ---- return codes ---------------------------------------------------------- */
 #define W4A16_OK              0
 #define W4A16_ERR_NULL       -1  /* a required pointer is NULL                      */
-#define W4A16_ERR_SHAPE      -2  /* M,N,K <= 0; K % group; group % 128; N % 16 ...  */
+#define W4A16_ERR_SHAPE      -2  /* M,N,K <= 0; K % 128; K % group; group not 64 or 128j; N % 16 ... */
 #define W4A16_ERR_ALIGN      -3  /* a pointer is not 16-byte aligned                */
 #define W4A16_ERR_DEVICE     -4  /* no HIP device, or the current device is not gfx950 */
 #define W4A16_ERR_LAUNCH     -5  /* the HIP runtime reported a launch error         */
@@ -56,13 +56,15 @@ const char* w4a16_strerror(int code);
 
 /* ---- sizes ------------------------------------------------------------------- */
 #define W4A16_BUF_W        0  /* dense repacked codes         : K*N/2 bytes              */
-#define W4A16_BUF_S        1  /* dense repacked scales        : 2*(K/128)*N bytes        */
-#define W4A16_BUF_Z        2  /* dense repacked zero-points   : (K/128)*N/2 bytes        */
+#define W4A16_BUF_S        1  /* dense repacked scales        : 2*(K/128)*N bytes (x2 for group 64) */
+#define W4A16_BUF_Z        2  /* dense repacked zero-points   : (K/128)*N/2 bytes (x2 for group 64) */
 #define W4A16_BUF_SPARSE_V 3  /* 2:4 kept codes               : K*N/4 bytes              */
 #define W4A16_BUF_SPARSE_I 4  /* 2:4 position metadata        : K*N/8 bytes              */
 #define W4A16_BUF_SPARSE_S 5  /* 2:4 repacked scales          : 2*(K/128)*N bytes        */
 /* (repacked scales and zero-points hold one row per 128 rows of K, so a group of
- *  256 or more rows is stored once per 128-row block it spans) */
+ *  256 or more rows is stored once per 128-row block it spans; with groups of 64
+ *  rows they hold two rows per block.  The 2:4 buffers need group % 128 == 0 and are
+ *  0 bytes for group 64.) */
 /* Bytes of buffer `which` for a K x N weight; 0 if the shape is invalid. */
 size_t w4a16_packed_bytes(int K, int N, int group, int which);
 
@@ -79,8 +81,9 @@ size_t w4a16_packed_bytes(int K, int N, int group, int which);
  *                    symmetric format (zero-point 8).
  *   wp (device, out) W4A16_BUF_W bytes; sp (device, out) W4A16_BUF_S bytes;
  *   zp (device, out) W4A16_BUF_Z bytes, must be NULL exactly when z is NULL.
- * Shape rules: K > 0, N > 0, group % 128 == 0, K % group == 0, N % 16 == 0.
- * All pointers 16-byte aligned.  Input and output must not overlap.
+ * Shape rules: K > 0, N > 0, K % 128 == 0, group == 64 or group % 128 == 0,
+ * K % group == 0, N % 16 == 0.  All pointers 16-byte aligned.  Input and output must
+ * not overlap.
  */
 int w4a16_repack(const int32_t* q, const uint16_t* s, const int32_t* z,
                  void* wp, uint16_t* sp, void* zp,
@@ -184,6 +187,8 @@ const char* w4a16_fp16_gemm_variant_name(int variant);
  * w4a16_sparse24_gemm: Y = X * W from the compressed weights, same rules and
  *   guarantees as w4a16_gemm (idx 16-byte aligned as well).
  * w4a16_sparse24_gemm_plan: the same with an explicit plan, as w4a16_gemm_plan.
+ * The 2:4 format takes groups that are whole multiples of 128 rows (W4A16_ERR_SHAPE
+ * for group 64).
  * Shape rules as w4a16_repack. */
 int w4a16_sparse24_repack(const int32_t* q, const uint16_t* s, void* vp, void* idx,
                           uint16_t* sp, int K, int N, int group, void* stream);

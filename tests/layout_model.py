@@ -6,7 +6,9 @@ Spec: block (t, kb) = 16 columns x 128 rows, 1 KiB, block index t*(K/128)+kb;
 lane l, word j holds column 16t + l%16, rows 128kb + 32j + 8(l//16) + e (e=0..7),
 row e at nibble e//2 + 4*(e%2).  Scales [N/16][K/128][16], row kb holding the
 scales of group kb // (group/128); zero-point words [N/16][K/128][2] equal to the
-canonical words z[G][2t], z[G][2t+1] of that group.
+canonical words z[G][2t], z[G][2t+1] of that group.  Groups of 64 rows: two scale
+rows per block interleaved per column ([N/16][K/128][16][2]) and two zero-point
+word pairs per block ([N/16][K/128][2][2]), half h = rows 64h .. 64h+63.
 """
 import numpy as np
 
@@ -39,6 +41,21 @@ def repack_zeros(Zp: np.ndarray, N: int, blocks_per_group: int = 1) -> np.ndarra
     U = np.repeat(np.ascontiguousarray(Zp).view(np.uint32), blocks_per_group, axis=0)
     G = U.shape[0]
     return np.ascontiguousarray(U.reshape(G, N // 16, 2).transpose(1, 0, 2)).reshape(-1)
+
+
+def repack_scales64(s: np.ndarray, N: int) -> np.ndarray:
+    """Groups of 64 rows: [N/16][K/128][16 columns][2 halves], half h of block kb holding
+    group 2kb + h."""
+    G = s.shape[0]
+    return np.ascontiguousarray(s.reshape(G // 2, 2, N // 16, 16).transpose(2, 0, 3, 1)).reshape(-1)
+
+
+def repack_zeros64(Zp: np.ndarray, N: int) -> np.ndarray:
+    """Groups of 64 rows: [N/16][K/128][2 halves][2 words], half h of block kb holding the
+    canonical words z[2kb + h][2t], z[2kb + h][2t + 1]."""
+    U = np.ascontiguousarray(Zp).view(np.uint32)
+    G = U.shape[0]
+    return np.ascontiguousarray(U.reshape(G // 2, 2, N // 16, 2).transpose(2, 0, 1, 3)).reshape(-1)
 
 
 # ---- 2:4 sparse layout -------------------------------------------------------------

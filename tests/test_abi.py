@@ -63,7 +63,14 @@ def test_queries(raw):
     assert raw.w4a16_packed_bytes(4096, 4096, 128, 9) == 0
     assert raw.w4a16_packed_bytes(4096, 4104, 128, 0) == 0   # N % 16
     assert raw.w4a16_packed_bytes(4000, 4096, 128, 0) == 0   # K % group
-    assert raw.w4a16_packed_bytes(4096, 4096, 64, 0) == 0    # group % 128
+    assert raw.w4a16_packed_bytes(4096, 4096, 32, 0) == 0    # group neither 64 nor 128j
+    assert raw.w4a16_packed_bytes(4096, 4096, 192, 0) == 0
+    # groups of 64 rows: two scale (and zero-point) rows per 128-row block; no 2:4 format
+    assert raw.w4a16_packed_bytes(4096, 4096, 64, 0) == 4096 * 4096 // 2
+    assert raw.w4a16_packed_bytes(4096, 4096, 64, 1) == 2 * 64 * 4096
+    assert raw.w4a16_packed_bytes(4096, 4096, 64, 2) == 64 * 4096 // 2
+    assert raw.w4a16_packed_bytes(4096, 4096, 64, 3) == 0
+    assert raw.w4a16_packed_bytes(4096, 4096, 64, 5) == 0
     assert raw.w4a16_gemm_variants() >= 1
 
 
@@ -114,7 +121,8 @@ def test_gemm_validation(raw):
     assert gemm(raw, M=0) == -2
     assert gemm(raw, N=1000) == -2       # N % 16
     assert gemm(raw, K=1000) == -2       # K % 128
-    assert gemm(raw, g=64) == -2         # group % 128
+    assert gemm(raw, g=32) == -2         # group neither 64 nor a multiple of 128
+    assert gemm(raw, g=192) == -2
     assert gemm(raw, g=384) == -2        # K % group
     assert gemm(raw, K=-128) == -2
     assert gemm(raw, X=MIS) == -3

@@ -493,3 +493,92 @@ def test_offsets_past_2_gib_use_the_skinny_kernel(gh):
                                   list(range(N)))
     ok, info = oracle.accept(gh.host(Y)[rows], Yref, B)
     assert ok, info
+
+
+# ---- groups of 64 rows (two scale / zero-point rows per 128-row block) -------------------
+def _case64(M, K, N, asym=False, seed=0):
+    w = Workload(cfg=9, M=M, K=K, N=N, group=64, asym=asym)
+    d = weights(w, seed=3000 + seed + K + N)
+    X = activations(w, seed=4000 + seed + M)
+    return w, d, X
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_group64_repack_layout_and_roundtrip(gh, asym):
+    import torch
+    import layout_model as lm
+    import w4a16_mixed_precision_offline_amd as w4
+    K, N = 1152, 528
+    _, d, _ = _case64(1, K, N, asym)
+    wp, sp, zp = gh.repack(d, K, N, 64)
+    assert np.array_equal(gh.host(wp).view(np.uint32), lm.repack_codes(d["Qp"], K, N))
+    assert np.array_equal(gh.host(sp).view(np.uint16), lm.repack_scales64(d["s"], N).view(np.uint16))
+    if asym:
+        assert np.array_equal(gh.host(zp).view(np.uint32), lm.repack_zeros64(d["Zp"], N))
+    q = torch.zeros((K // 8, N), dtype=torch.int32, device="cuda")
+    s = torch.zeros((K // 64, N), dtype=torch.float16, device="cuda")
+    z = torch.zeros((K // 64, N // 8), dtype=torch.int32, device="cuda") if asym else None
+    w4.w4a16_unpack(wp, sp, zp, q, s, z, K, N, 64)
+    assert np.array_equal(gh.host(q), d["Qp"])
+    assert np.array_equal(gh.host(s).view(np.uint16), d["s"].view(np.uint16))
+    if asym:
+        assert np.array_equal(gh.host(z), d["Zp"])
+
+
+@pytest.mark.parametrize("M,K,N,asym", [(5, 1152, 528, True), (33, 1024, 512, False),
+                                        (300, 2048, 1040, True), (1, 256, 48, False)])
+def test_group64_every_variant(gh, M, K, N, asym):
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, X = _case64(M, K, N, asym)
+    packed = gh.repack(d, K, N, 64)
+    Xd = gh.dev(X)
+    Yref = oracle.gemm(X, d["Qp"], d["s"], d["Zp"], 64)
+    B = oracle.error_bound(X, d["Qp"], d["s"], d["Zp"], 64)
+    ran = 0
+    for v in [-1] + list(range(w4.w4a16_gemm_variants())):
+        name = w4.w4a16_gemm_variant_name(v) if v >= 0 else "auto"
+        nt = 1 if not name.startswith("skinny") else int(name.split("_nt")[1].split("_")[0])
+        if N % (16 * nt):
+            continue
+        for splits in ((0,) if v < 0 else (1, 3)):
+            Y = gh.nan_filled(M, N)
+            gh.gemm(Xd, packed, M, N, K, group=64, variant=v, splits=splits, Y=Y)
+            ok, info = oracle.accept(gh.host(Y), Yref, B)
+            assert ok, (name, splits, info)
+            ran += 1
+    assert ran > 1
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_group64_onehot_exact(gh, asym):
+    """One-hot rows in both 64-row halves of a block select RNE((q - z) * s) of their own
+    group, through the fp32-rescale and the fp16-scaled-weight skinny paths and the tiled
+    kernel."""
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 16, 1024, 768
+    _, d, _ = _case64(M, K, N, asym)
+    ks = [0, 1, 63, 64, 65, 127, 128, 191, 192, 300, 511, 512, 575, 640, 1000, 1023]
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    W16 = oracle.dequant_fp16(d["Qp"], d["s"], d["Zp"], K, N, 64)
+    packed = gh.repack(d, K, N, 64)
+    names = ["skinny_xr16_nt2_wk8_d2", "skinny_xr16_nt3_wk4_d2", "skinny_xr16_nt4_wk4_d2",
+             "tiled_bm128_bn256_s3", "tiled_bm64_bn256_s3", "tiled_bm16_bn256_s4"]
+    for nm in names:
+        for splits in (1, 3):
+            Y = gh.host(gh.gemm(gh.dev(X), packed, M, N, K, group=64,
+                                variant=gh.variant_index(nm), splits=splits))
+            assert np.array_equal(Y.view(np.uint16), W16[ks].view(np.uint16)), (nm, splits)
+
+
+@pytest.mark.parametrize("M,K,N,asym", [(1, 4096, 11008, False), (16, 4096, 11008, True),
+                                        (32, 11008, 4096, False), (1024, 8192, 10240, True)])
+def test_group64_full_size(gh, M, K, N, asym):
+    _, d, X = _case64(M, K, N, asym)
+    Y = gh.host(gh.gemm(gh.dev(X), gh.repack(d, K, N, 64), M, N, K, group=64))
+    rng = np.random.default_rng(M + K)
+    rows = _sample_idx(rng, M, 24)
+    cols = _sample_idx(rng, N, 48)
+    Yref, B = oracle.gemm_sampled(X, d["Qp"], d["s"], d["Zp"], 64, rows, cols)
+    ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, B)
+    assert ok, info

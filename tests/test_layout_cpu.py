@@ -45,6 +45,23 @@ def test_scale_and_zero_models():
             assert list(zp[t, g]) == [g * (N // 8) + 2 * t, g * (N // 8) + 2 * t + 1]
 
 
+def test_scale_and_zero_models_group64():
+    # two rows per 128-row block: half h of block kb holds group 2kb + h
+    Gk, N = 3, 48
+    G = 2 * Gk
+    s = np.arange(G * N, dtype=np.uint16).reshape(G, N).view(np.float16)
+    sp = lm.repack_scales64(s, N).view(np.uint16)
+    Zp = np.arange(G * N // 8, dtype=np.uint32).reshape(G, N // 8).view(np.int32)
+    zp = lm.repack_zeros64(Zp, N).view(np.uint32)
+    for t in range(N // 16):
+        for kb in range(Gk):
+            for h in range(2):
+                for c in range(16):
+                    assert sp[((t * Gk + kb) * 16 + c) * 2 + h] == (2 * kb + h) * N + 16 * t + c
+                for w in range(2):
+                    assert zp[((t * Gk + kb) * 2 + h) * 2 + w] == (2 * kb + h) * (N // 8) + 2 * t + w
+
+
 def test_sparse24_model_roundtrip_by_hand():
     # decompress the model's output by hand and compare with the input codes
     from gen import Workload, weights

@@ -144,13 +144,14 @@ def test_dequant_exhaustive_closed_form(sv):
         assert Fraction(Wsym[k, 0]) == (Fraction(k) - 8) * Fraction(float(s16))
 
 
-def test_dequant_group_indexing():
+@pytest.mark.parametrize("g", [64, 128])
+def test_dequant_group_indexing(g):
     # scale of group G applies exactly to rows G*g .. G*g+g-1
-    K, N, g = 384, 8, 128
+    K, N = 3 * g, 8
     q = np.full((K, N), 9, dtype=np.uint8)  # q - 8 = 1
     s = np.array([[1.0] * N, [2.0] * N, [4.0] * N], dtype=np.float16)
     W = oracle.dequant(words_from_codes_k(q), s, None, K, N, g)
-    assert np.all(W[:128] == 1.0) and np.all(W[128:256] == 2.0) and np.all(W[256:] == 4.0)
+    assert np.all(W[:g] == 1.0) and np.all(W[g:2 * g] == 2.0) and np.all(W[2 * g:] == 4.0)
 
 
 def test_dequant_fp16_is_rne_of_exact():
@@ -169,7 +170,8 @@ def test_dequant_fp16_is_rne_of_exact():
 
 # ---- steps 4-5: products -------------------------------------------------------
 @pytest.mark.parametrize("M,K,N,asym,g", [(1, 128, 8, False, 128), (3, 256, 16, True, 128),
-                                          (16, 128, 8, True, 128), (2, 256, 8, False, 256)])
+                                          (16, 128, 8, True, 128), (2, 256, 8, False, 256),
+                                          (3, 256, 16, True, 64), (2, 128, 8, False, 64)])
 def test_gemm_vs_exact_rationals(M, K, N, asym, g):
     rng = np.random.default_rng(M * 1000 + K + N)
     q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)

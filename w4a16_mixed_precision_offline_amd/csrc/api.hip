@@ -20,7 +20,9 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // Shape rules shared by the weight-format entry points.
 int check_weight_shape(int K, int N, int group) {
   if (K <= 0 || N <= 0 || group <= 0) return W4A16_ERR_SHAPE;
-  if (group % KBLK != 0 || K % group != 0 || N % NTILE != 0) return W4A16_ERR_SHAPE;
+  // groups of 64 rows, or whole multiples of the 128-row block
+  if ((group != 64 && group % KBLK != 0) || K % KBLK != 0 || K % group != 0 || N % NTILE != 0)
+    return W4A16_ERR_SHAPE;
   // word and block indices are 32-bit inside the kernels' per-dimension math
   if ((long long)K * N / 8 > (1LL << 31) - 1) return W4A16_ERR_SHAPE;
   return W4A16_OK;
@@ -98,6 +100,11 @@ int get_workspace(int dev, hipStream_t st, size_t counters, size_t floats, int**
   *cnt = static_cast<int*>(ws.ptr);
   *part = reinterpret_cast<float*>(static_cast<int*>(ws.ptr) + ws.counter_ints);
   return W4A16_OK;
+}
+
+// Weight format of a dense launch: zero-points or not, groups of 64 rows or not.
+inline int dense_mode(bool asym, int group) {
+  return group == 64 ? (asym ? W_ASYM64 : W_SYM64) : (asym ? W_ASYM : W_SYM);
 }
 
 inline int launched(hipError_t e) {
@@ -191,7 +198,7 @@ const char* w4a16_strerror(int code) {
   switch (code) {
     case W4A16_OK: return "success";
     case W4A16_ERR_NULL: return "a required pointer is NULL";
-    case W4A16_ERR_SHAPE: return "invalid shape (M,N,K >= 1, group % 128 == 0, K % group == 0, N % 16 == 0)";
+    case W4A16_ERR_SHAPE: return "invalid shape (M,N,K >= 1, K % 128 == 0, group 64 or a multiple of 128 dividing K, N % 16 == 0)";
     case W4A16_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case W4A16_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
     case W4A16_ERR_LAUNCH: return "kernel launch failed";
@@ -204,14 +211,15 @@ const char* w4a16_strerror(int code) {
 
 size_t w4a16_packed_bytes(int K, int N, int group, int which) {
   if (check_weight_shape(K, N, group)) return 0;
-  const size_t KN = (size_t)K * N, Gk = (size_t)(K / KBLK);
+  const size_t KN = (size_t)K * N, Gk = (size_t)(K / KBLK), SH = group == 64 ? 2 : 1;
+  const bool sparse_ok = group != 64;
   switch (which) {
     case W4A16_BUF_W: return KN / 2;
-    case W4A16_BUF_S: return 2 * Gk * N;
-    case W4A16_BUF_Z: return Gk * N / 2;
-    case W4A16_BUF_SPARSE_V: return KN / 4;
-    case W4A16_BUF_SPARSE_I: return KN / 8;
-    case W4A16_BUF_SPARSE_S: return 2 * Gk * N;
+    case W4A16_BUF_S: return 2 * Gk * N * SH;
+    case W4A16_BUF_Z: return Gk * N / 2 * SH;
+    case W4A16_BUF_SPARSE_V: return sparse_ok ? KN / 4 : 0;
+    case W4A16_BUF_SPARSE_I: return sparse_ok ? KN / 8 : 0;
+    case W4A16_BUF_SPARSE_S: return sparse_ok ? 2 * Gk * N : 0;
     default: return 0;
   }
 }
@@ -250,7 +258,8 @@ int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void
                uint16_t* Y, int M, int N, int K, int group, void* stream) {
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
-  return run_fused(zp ? W_ASYM : W_SYM, X, wp, sp, zp, Y, M, N, K, group, -1, 0, stream);
+  return run_fused(dense_mode(zp != nullptr, group), X, wp, sp, zp, Y, M, N, K, group, -1, 0,
+                   stream);
 }
 
 int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
@@ -259,8 +268,8 @@ int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
   if (variant < -1 || variant >= w4a16_gemm_variants() || splits < 0) return W4A16_ERR_ARG;
-  return run_fused(zp ? W_ASYM : W_SYM, X, wp, sp, zp, Y, M, N, K, group, variant, splits,
-                   stream);
+  return run_fused(dense_mode(zp != nullptr, group), X, wp, sp, zp, Y, M, N, K, group, variant,
+                   splits, stream);
 }
 
 int w4a16_gemm_variants(void) { return skinny_variant_count() + tiled_variant_count(W_SYM); }
@@ -372,6 +381,7 @@ int w4a16_sparse24_repack(const int32_t* q, const uint16_t* s, void* vp, void* i
   if (!q || !s || !vp || !idx || !sp) return W4A16_ERR_NULL;
   int rc = check_weight_shape(K, N, group);
   if (rc) return rc;
+  if (group == 64) return W4A16_ERR_SHAPE;  // 2:4 format: groups of 128 rows or more
   if (!aligned16(q) || !aligned16(s) || !aligned16(vp) || !aligned16(idx) || !aligned16(sp))
     return W4A16_ERR_ALIGN;
   int dev;
@@ -409,6 +419,7 @@ int w4a16_sparse24_unpack(const void* vp, const void* idx, const uint16_t* sp, i
   if (!q || !s || !vp || !idx || !sp) return W4A16_ERR_NULL;
   int rc = check_weight_shape(K, N, group);
   if (rc) return rc;
+  if (group == 64) return W4A16_ERR_SHAPE;  // 2:4 format: groups of 128 rows or more
   if (!aligned16(q) || !aligned16(s) || !aligned16(vp) || !aligned16(idx) || !aligned16(sp))
     return W4A16_ERR_ALIGN;
   if ((rc = check_device(nullptr))) return rc;
@@ -422,6 +433,7 @@ int w4a16_sparse24_gemm(const uint16_t* X, const void* vp, const void* idx, cons
   if (!idx) return W4A16_ERR_NULL;
   int rc = check_gemm_args(X, vp, sp, idx, Y, M, N, K, group);
   if (rc) return rc;
+  if (group == 64) return W4A16_ERR_SHAPE;
   return run_fused(W_SP24, X, vp, sp, idx, Y, M, N, K, group, -1, 0, stream);
 }
 
@@ -431,6 +443,7 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
   if (!idx) return W4A16_ERR_NULL;
   int rc = check_gemm_args(X, vp, sp, idx, Y, M, N, K, group);
   if (rc) return rc;
+  if (group == 64) return W4A16_ERR_SHAPE;
   if (variant < -1 || variant >= w4a16_gemm_variants() || splits < 0) return W4A16_ERR_ARG;
   return run_fused(W_SP24, X, vp, sp, idx, Y, M, N, K, group, variant, splits, stream);
 }

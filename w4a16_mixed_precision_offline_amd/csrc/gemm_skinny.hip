@@ -108,6 +108,8 @@ struct Stage {
                                         // .x/.y = kept codes of the two halves, .z = positions)
   uint16_t s[NT];                       // fp16 scale bits of the lane's column
   uint2 z[NT];                          // 16 zero-points of the tile (ASYM)
+  uint32_t s64[NT];                     // groups of 64: the scales of both halves (low: rows 0-63)
+  u32x4 z64[NT];                        // groups of 64: zero-points, .xy half 0, .zw half 1
   uint2 s4[NT];                         // 2:4: the four scales of the lane's four columns
   u32x4 x[XR / 4];                      // X rows 4c + lane/16, 16-byte chunk lane%16
 };
@@ -148,9 +150,15 @@ __device__ __forceinline__ void load_stage(Stage<XR, NT, MODE>& S, int kb, bool 
     } else {
       const uint32_t blk = (uint32_t)(t * Gk + kb);
       S.w[t][0] = bload16<true>(R.w, R.lane_w, blk * 1024u);
-      S.s[t] = __builtin_amdgcn_raw_buffer_load_b16(R.s, (uint32_t)(lane & 15) * 2, blk * 32u, 0);
-      if (MODE == W_ASYM)
-        S.z[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R.z, 0u, blk * 8u, 0));
+      if constexpr (mode_g64(MODE)) {
+        S.s64[t] = __builtin_amdgcn_raw_buffer_load_b32(R.s, (uint32_t)(lane & 15) * 4, blk * 64u, 0);
+        if (mode_asym(MODE))
+          S.z64[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.z, 0u, blk * 16u, 0));
+      } else {
+        S.s[t] = __builtin_amdgcn_raw_buffer_load_b16(R.s, (uint32_t)(lane & 15) * 2, blk * 32u, 0);
+        if (MODE == W_ASYM)
+          S.z[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R.z, 0u, blk * 8u, 0));
+      }
     }
   }
 #pragma unroll
@@ -209,32 +217,47 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = __builtin_bit_cast(half8, S.w[t][j]);
     } else {
-      half2v c0, c1;
-      if (MODE == W_ASYM) {
-        const int c = lane & 15;
-        const uint32_t zw = c < 8 ? S.z[t].x : S.z[t].y;
-        const int zq = (int)((zw >> (4 * (c & 7))) & 15u);
+      // the offsets -(1024 + z), -(64 + z) of each half (both halves alike unless the
+      // groups are 64 rows): words j = 0, 1 are rows 0-63 of the block, j = 2, 3 rows 64-127
+      constexpr int SH = mode_g64(MODE) ? 2 : 1;
+      half2v c0[SH], c1[SH];
+#pragma unroll
+      for (int h = 0; h < SH; ++h) {
+        int zq = 8;
+        if constexpr (mode_asym(MODE)) {
+          const int c = lane & 15;
+          uint32_t zw;
+          if constexpr (SH == 2) zw = h == 0 ? (c < 8 ? S.z64[t].x : S.z64[t].y)
+                                             : (c < 8 ? S.z64[t].z : S.z64[t].w);
+          else zw = c < 8 ? S.z[t].x : S.z[t].y;
+          zq = (int)((zw >> (4 * (c & 7))) & 15u);
+        }
         const _Float16 a0 = (_Float16)(float)(-1024 - zq);
         const _Float16 a1 = (_Float16)(float)(-64 - zq);
-        c0 = half2v{a0, a0};
-        c1 = half2v{a1, a1};
-      } else {
-        c0 = half2v{(_Float16)-1032.0f, (_Float16)-1032.0f};
-        c1 = half2v{(_Float16)-72.0f, (_Float16)-72.0f};
+        c0[h] = half2v{a0, a0};
+        c1[h] = half2v{a1, a1};
       }
-      b[0] = dequant_word(S.w[t][0].x, c0, c1, magic);
-      b[1] = dequant_word(S.w[t][0].y, c0, c1, magic);
-      b[2] = dequant_word(S.w[t][0].z, c0, c1, magic);
-      b[3] = dequant_word(S.w[t][0].w, c0, c1, magic);
+      b[0] = dequant_word(S.w[t][0].x, c0[0], c1[0], magic);
+      b[1] = dequant_word(S.w[t][0].y, c0[0], c1[0], magic);
+      b[2] = dequant_word(S.w[t][0].z, c0[SH - 1], c1[SH - 1], magic);
+      b[3] = dequant_word(S.w[t][0].w, c0[SH - 1], c1[SH - 1], magic);
     }
     if constexpr (NT >= 3 && MODE != W_FP16) {
       // many column tiles per wave: multiply the weights by the scale in fp16 (one
       // rounding of W, the fp16 dequantized weight) and accumulate straight into acc;
       // measured faster than rescaling the fp32 partial sum of every (tile, row tile)
-      const _Float16 sh = __builtin_bit_cast(_Float16, S.s[t]);
-      const half8 s8 = {sh, sh, sh, sh, sh, sh, sh, sh};
+      _Float16 sh0, sh1;
+      if constexpr (mode_g64(MODE)) {
+        const half2v s01 = __builtin_bit_cast(half2v, S.s64[t]);
+        sh0 = s01[0];
+        sh1 = s01[1];
+      } else {
+        sh0 = sh1 = __builtin_bit_cast(_Float16, S.s[t]);
+      }
+      const half8 s8a = {sh0, sh0, sh0, sh0, sh0, sh0, sh0, sh0};
+      const half8 s8b = {sh1, sh1, sh1, sh1, sh1, sh1, sh1, sh1};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = b[j] * s8;
+      for (int j = 0; j < 4; ++j) b[j] = b[j] * (j < 2 ? s8a : s8b);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -249,6 +272,15 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][j], b[j], acc[t][mt], 0, 0, 0);
+      } else if constexpr (mode_g64(MODE)) {
+        // one fp32 partial per 64-row half, each rescaled by its own group's scale
+        float4v g0 = {0.f, 0.f, 0.f, 0.f}, g1 = {0.f, 0.f, 0.f, 0.f};
+        g0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][0], b[0], g0, 0, 0, 0);
+        g0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][1], b[1], g0, 0, 0, 0);
+        g1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][2], b[2], g1, 0, 0, 0);
+        g1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][3], b[3], g1, 0, 0, 0);
+        const half2v s01 = __builtin_bit_cast(half2v, S.s64[t]);
+        acc[t][mt] += (float)s01[0] * g0 + (float)s01[1] * g1;
       } else {
         float4v g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -322,10 +354,11 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     R.s = make_rsrc(Sp + (size_t)t0 * Gk * 16, (uint32_t)(NT * Gk * 32));
     R.lane_w = (uint32_t)lane * 8;
   } else {
+    constexpr int SH = mode_g64(MODE) ? 2 : 1;  // scale / zero-point rows per block
     R.w = make_rsrc(reinterpret_cast<const char*>(W) + (size_t)t0 * Gk * 1024,
                     (uint32_t)(NT * Gk * 1024));
-    R.s = make_rsrc(Sp + (size_t)t0 * Gk * 16, (uint32_t)(NT * Gk * 32));
-    if (MODE == W_ASYM) R.z = make_rsrc(Zp + (size_t)t0 * Gk, (uint32_t)(NT * Gk * 8));
+    R.s = make_rsrc(Sp + (size_t)t0 * Gk * 16 * SH, (uint32_t)(NT * Gk * 32 * SH));
+    if (mode_asym(MODE)) R.z = make_rsrc(Zp + (size_t)t0 * Gk * SH, (uint32_t)(NT * Gk * 8 * SH));
     R.lane_w = (uint32_t)lane * 16;
   }
   const int rows = M - m0 < XR ? M - m0 : XR;  // valid rows of this block of X
@@ -478,7 +511,7 @@ typedef void (*KernelFn)(const uint16_t*, const uint4*, const uint16_t*, const u
 
 struct Variant {
   int XR, NT, WK, D;
-  KernelFn sym, asym, f16, sp24;
+  KernelFn sym, asym, f16, sp24, sym64, asym64;
   const char* name;
 };
 
@@ -486,6 +519,7 @@ struct Variant {
   Variant {                                                                              \
     XR, NT, WK, D, skinny_kernel<XR, NT, WK, D, W_SYM>, skinny_kernel<XR, NT, WK, D, W_ASYM>, \
         skinny_kernel<XR, NT, WK, D, W_FP16>, skinny_kernel<XR, NT, WK, D, W_SP24>,      \
+        skinny_kernel<XR, NT, WK, D, W_SYM64>, skinny_kernel<XR, NT, WK, D, W_ASYM64>,   \
         "skinny_xr" #XR "_nt" #NT "_wk" #WK "_d" #D                                      \
   }
 
@@ -598,10 +632,12 @@ hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                          int* counters, int M, int N, int K, int group, hipStream_t st) {
   (void)group;  // the repacked layout stores one scale row per 128-row block
   const Variant& v = kVariants[p.variant];
-  KernelFn fn = p.mode == W_FP16 ? v.f16
-               : p.mode == W_ASYM ? v.asym
-               : p.mode == W_SP24 ? v.sp24
-                                  : v.sym;
+  KernelFn fn = p.mode == W_FP16     ? v.f16
+               : p.mode == W_ASYM   ? v.asym
+               : p.mode == W_SP24   ? v.sp24
+               : p.mode == W_SYM64  ? v.sym64
+               : p.mode == W_ASYM64 ? v.asym64
+                                    : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint4*>(w), sp, reinterpret_cast<const uint2*>(zp), Y,
                      part, counters, M, N, K, p.splits, p.nblocks);

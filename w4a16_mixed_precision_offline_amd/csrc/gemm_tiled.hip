@@ -136,8 +136,9 @@ struct WSrc {
 };
 
 // LDS of one pipeline stage, per wave: NTW 1 KiB code blocks, then 256 bytes of
-// scales (tile t, column c at 32t + 2c; the DMA writes 4 bytes per lane, so the
-// slot spans all 64 lanes) and 256 bytes of zero-points (tile t at 8t).
+// scales (tile t, column c at 32t + 2c; with groups of 64 rows, half h at
+// 64t + 4c + 2h; the DMA writes 4 bytes per lane, so the slot spans all 64 lanes) and
+// 256 bytes of zero-points (tile t at 8t; with groups of 64, half h at 16t + 8h).
 template <int NTW, int MODE>
 struct WLds {
   // dense: NTW 1 KiB code blocks.  2:4: NTW 512-byte blocks of kept codes (lane l's
@@ -173,7 +174,8 @@ template <int MT, int NTW, int MODE>
 struct DmaPlan {
   // 2:4: two tiles' kept codes per 16-byte load, all four tiles' positions in one
   static constexpr int NW = MODE == W_SP24 ? NTW / 2 + NTW / 4 : MODE == W_FP16 ? 4 * NTW : NTW;
-  static constexpr int NV = MT + NW + (MODE == W_ASYM ? 2 : MODE == W_FP16 ? 0 : 1);
+  static constexpr int NV = MT + NW + (mode_asym(MODE) ? 2 : MODE == W_FP16 ? 0 : 1);
+  static constexpr uint32_t SH = mode_g64(MODE) ? 2u : 1u;  // scale / zero rows per block
   u32x4 rx;
   uint32_t xoff[MT];
   WSrc<NTW> R;
@@ -191,13 +193,13 @@ struct DmaPlan {
     } else if (MODE == W_FP16 && q < MT + NW) {
       const int t = (q - MT) >> 2, j = (q - MT) & 3;  // rows 32j.. of column tile t
       dma16(R.w, wdst + (t * 4 + j) * 1024, R.wo[t], (uint32_t)kb * 256u + 64u * j);
-    } else if (MODE != W_SP24 && MODE != W_FP16 && q < MT + NTW) {
+    } else if (mode_dense4(MODE) && q < MT + NTW) {
       const int t = q - MT;
       dma16(R.w, wdst + t * 1024, R.wo[t], (uint32_t)kb * 1024u);
     } else if (MODE != W_FP16 && q == MT + NW) {
-      dma4(R.s, wdst + L::SCALES, R.so, (uint32_t)kb * 32u);
-    } else if (MODE == W_ASYM && q == MT + NW + 1) {
-      dma4(R.z, wdst + L::ZEROS, R.zo, (uint32_t)kb * 8u);
+      dma4(R.s, wdst + L::SCALES, R.so, (uint32_t)kb * 32u * SH);
+    } else if (mode_asym(MODE) && q == MT + NW + 1) {
+      dma4(R.z, wdst + L::ZEROS, R.zo, (uint32_t)kb * 8u * SH);
     }
   }
 };
@@ -218,23 +220,31 @@ __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
   u32x4 wv[NTW];
   half2v c0[NTW], c1[NTW], s2[NTW];
 #pragma unroll
-  for (int t = 0; t < NTW; ++t) {
-    wv[t] = *reinterpret_cast<const u32x4*>(wl + t * 1024 + lane * 16);
-    const _Float16 sc =
-        *reinterpret_cast<const _Float16*>(wl + WLds<NTW, MODE>::SCALES + t * 32 + (lane & 15) * 2);
-    s2[t] = half2v{sc, sc};
-    int zq = 8;
-    if (MODE == W_ASYM) {
+  for (int t = 0; t < NTW; ++t) wv[t] = *reinterpret_cast<const u32x4*>(wl + t * 1024 + lane * 16);
+  // scale and zero-point offsets of half h of the block for every column tile (with
+  // groups of 64 rows the second half's values replace the first's once step 1 has
+  // been unpacked: steps 0, 1 are rows 0-63, steps 2, 3 rows 64-127)
+  auto load_consts = [&](int h) {
+    constexpr bool G64 = mode_g64(MODE);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
       const int c = lane & 15;
-      const uint32_t zw =
-          *reinterpret_cast<const uint32_t*>(wl + WLds<NTW, MODE>::ZEROS + t * 8 + (c >> 3) * 4);
-      zq = (int)((zw >> (4 * (c & 7))) & 15u);
+      const _Float16 sc = *reinterpret_cast<const _Float16*>(
+          wl + WLds<NTW, MODE>::SCALES + (G64 ? t * 64 + c * 4 + h * 2 : t * 32 + c * 2));
+      s2[t] = half2v{sc, sc};
+      int zq = 8;
+      if (mode_asym(MODE)) {
+        const uint32_t zw = *reinterpret_cast<const uint32_t*>(
+            wl + WLds<NTW, MODE>::ZEROS + (G64 ? t * 16 + h * 8 : t * 8) + (c >> 3) * 4);
+        zq = (int)((zw >> (4 * (c & 7))) & 15u);
+      }
+      const _Float16 a0 = (_Float16)(float)(-1024 - zq);
+      const _Float16 a1 = (_Float16)(float)(-64 - zq);
+      c0[t] = half2v{a0, a0};
+      c1[t] = half2v{a1, a1};
     }
-    const _Float16 a0 = (_Float16)(float)(-1024 - zq);
-    const _Float16 a1 = (_Float16)(float)(-64 - zq);
-    c0[t] = half2v{a0, a0};
-    c1[t] = half2v{a1, a1};
-  }
+  };
+  load_consts(0);
   // fragment ring: group g's activation fragment is read PF groups ahead
   constexpr int PF = 3;
   half8 ar[PF + 1];
@@ -257,6 +267,7 @@ __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
         const int gj = (g + PF) / MT, gi = (g + PF) % MT;
         ar[(g + PF) % (PF + 1)] = *reinterpret_cast<const half8*>(xb + aoff[gj] + gi * 4096);
       }
+      if (mode_g64(MODE) && j == 1 && i == 0) load_consts(1);
       // unpack the column tiles t = i, i + MT, ... of step j + 1
       if (j < 3) {
 #pragma unroll
@@ -500,11 +511,14 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     int nvalid = ntiles16 - t_first;
     nvalid = nvalid < 0 ? 0 : (nvalid > NTW ? NTW : nvalid);
     WSrc<NTW> R;
+    constexpr int SH = mode_g64(MODE) ? 2 : 1;  // scale / zero-point rows per block
     if (MODE != W_FP16) {
-      R.s = rsrc_words(Sp + (size_t)t_first * Gk * 16, (uint32_t)(nvalid * Gk * 32));
-      const int ts = lane >> 3;
-      R.so = (lane < 8 * NTW && ts < nvalid) ? (uint32_t)(ts * Gk * 32 + (lane & 7) * 4)
-                                             : kOutOfRange;
+      // scales: lane L < 8*SH*NTW loads bytes 4(L % 8SH) .. +3 of tile L / 8SH's row(s)
+      R.s = rsrc_words(Sp + (size_t)t_first * Gk * 16 * SH, (uint32_t)(nvalid * Gk * 32 * SH));
+      const int ts = lane / (8 * SH);
+      R.so = (lane < 8 * SH * NTW && ts < nvalid)
+                 ? (uint32_t)(ts * Gk * 32 * SH + (lane % (8 * SH)) * 4)
+                 : kOutOfRange;
     } else {
       R.s = rsrc_words(W, 0);  // no scales
       R.so = kOutOfRange;
@@ -540,12 +554,14 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
         R.wo[t] = t < nvalid ? (uint32_t)(t * Gk * 1024 + lane * 16) : kOutOfRange;
-      if (MODE == W_ASYM) {
-        R.z = rsrc_words(reinterpret_cast<const char*>(Zp) + (size_t)t_first * Gk * 8,
-                         (uint32_t)(nvalid * Gk * 8));
-        const int tz = lane >> 1;
-        R.zo = (lane < 2 * NTW && tz < nvalid) ? (uint32_t)(tz * Gk * 8 + (lane & 1) * 4)
-                                               : kOutOfRange;
+      if (mode_asym(MODE)) {
+        // zero-points: lane L < 2*SH*NTW loads word L % 2SH of tile L / 2SH
+        R.z = rsrc_words(reinterpret_cast<const char*>(Zp) + (size_t)t_first * Gk * 8 * SH,
+                         (uint32_t)(nvalid * Gk * 8 * SH));
+        const int tz = lane / (2 * SH);
+        R.zo = (lane < 2 * SH * NTW && tz < nvalid)
+                   ? (uint32_t)(tz * Gk * 8 * SH + (lane % (2 * SH)) * 4)
+                   : kOutOfRange;
       } else {
         R.z = R.s;
         R.zo = kOutOfRange;
@@ -739,7 +755,7 @@ typedef void (*FixupFn)(const float*, uint16_t*, TiledArgs);
 
 struct TVariant {
   int MT, NTW, NS;
-  TiledFn sym, asym, sp24, f16;
+  TiledFn sym, asym, sp24, f16, sym64, asym64;
   FixupFn fixup;
   const char* name;
 };
@@ -747,13 +763,14 @@ struct TVariant {
 #define W4A16_TILED(MT, NTW, NS, NAME)                                                       \
   TVariant {                                                                               \
     MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>,       \
-        tiled_kernel<MT, NTW, NS, W_SP24>, nullptr, tiled_fixup_kernel<MT, NTW>, NAME        \
+        tiled_kernel<MT, NTW, NS, W_SP24>, nullptr, tiled_kernel<MT, NTW, NS, W_SYM64>,     \
+        tiled_kernel<MT, NTW, NS, W_ASYM64>, tiled_fixup_kernel<MT, NTW>, NAME              \
   }
 // the fp16 baseline moves four times the weight bytes: its own LDS-sized tiles
 #define W4A16_TILED_F16(MT, NTW, NS, NAME)                                                    \
   TVariant {                                                                               \
-    MT, NTW, NS, nullptr, nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_FP16>,              \
-        tiled_fixup_kernel<MT, NTW>, NAME                                                  \
+    MT, NTW, NS, nullptr, nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_FP16>, nullptr,     \
+        nullptr, tiled_fixup_kernel<MT, NTW>, NAME                                         \
   }
 
 const TVariant kTiled[] = {
@@ -779,7 +796,7 @@ const char* tiled_variant_name(int mode, int v) {
 }
 
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p) {
-  if (mode != W_SYM && mode != W_ASYM && mode != W_SP24 && mode != W_FP16) return -8;
+  if (!mode_dense4(mode) && mode != W_SP24 && mode != W_FP16) return -8;
   const bool f16 = mode == W_FP16;
   const TVariant* table = f16 ? kTiledF16 : kTiled;
   const int count = f16 ? kNumTiledF16 : kNumTiled;
@@ -858,10 +875,12 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
                         const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st) {
   const TVariant& v = p.mode == W_FP16 ? kTiledF16[p.variant] : kTiled[p.variant];
-  TiledFn fn = p.mode == W_ASYM   ? v.asym
-               : p.mode == W_SP24 ? v.sp24
-               : p.mode == W_FP16 ? v.f16
-                                  : v.sym;
+  TiledFn fn = p.mode == W_ASYM     ? v.asym
+               : p.mode == W_SP24   ? v.sp24
+               : p.mode == W_FP16   ? v.f16
+               : p.mode == W_SYM64  ? v.sym64
+               : p.mode == W_ASYM64 ? v.asym64
+                                    : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint32_t*>(w), sp, zp, Y, part, p.args);
   if (p.fixup_wgs > 0) {

@@ -20,11 +20,15 @@
 //   (canonical words pack rows 8i..8i+7), every repacked word is one canonical
 //   word with its nibbles permuted.
 //
-// Scales, one row per 128-row block so that the kernels never divide by the group:
-//   sp[(t * Gk + kb) * 16 + c] = s[kb / (group/128)][16t + c], Gk = K/128 (fp16 bits);
-//   a group of 256 or more rows is stored once per 128-row block it spans.
-// Zero-points, likewise per block: zp32[(t * Gk + kb) * 2 + h] = z[kb / (group/128)][2t + h],
-//   i.e. the 16 zero-points of a tile as one 64-bit word, nibble c = column 16t+c.
+// Scales, SH rows per 128-row block (SH = 2 for a group of 64 rows, else 1) so that the
+// kernels never divide by the group:
+//   sp[((t * Gk + kb) * 16 + c) * SH + h] = s[(128 kb + 64 h) / group][16t + c],
+//   Gk = K/128 (fp16 bits); a group of 256 or more rows is stored once per 128-row
+//   block it spans; with groups of 64 the two halves of a column sit side by side.
+// Zero-points, likewise: zp32[((t * Gk + kb) * SH + h) * 2 + w] =
+//   z[(128 kb + 64 h) / group][2t + w], i.e. the 16 zero-points of a tile as one 64-bit
+//   word per half, nibble c = column 16t+c.  Half h covers rows 64h .. 64h + 63 of the
+//   block: the words j = 2h, 2h + 1 of a lane.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -57,7 +61,14 @@ hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
                           uint16_t* W, int K, int N, int group, hipStream_t st);
 
 // Fused skinny GEMM.  `part` / `counters` form the split-K workspace.
-enum WMode { W_SYM = 0, W_ASYM = 1, W_FP16 = 2, W_SP24 = 3 };  // weight format of a launch
+// weight format of a launch; the *64 modes are the same formats with groups of 64 rows
+enum WMode { W_SYM = 0, W_ASYM = 1, W_FP16 = 2, W_SP24 = 3, W_SYM64 = 4, W_ASYM64 = 5 };
+__host__ __device__ constexpr bool mode_asym(int m) { return m == W_ASYM || m == W_ASYM64; }
+__host__ __device__ constexpr bool mode_g64(int m) { return m == W_SYM64 || m == W_ASYM64; }
+// packed 4-bit codes with scales (and zero-points): the dense repacked formats
+__host__ __device__ constexpr bool mode_dense4(int m) {
+  return m == W_SYM || m == W_ASYM || m == W_SYM64 || m == W_ASYM64;
+}
 struct SkinnyPlan {
   int variant;   // index into the variant table
   int mode;      // WMode

@@ -53,37 +53,47 @@ __global__ void codes_kernel(const uint32_t* __restrict__ src, uint32_t* __restr
   }
 }
 
-// scales: repacked index o = (t*Gk + kb)*16 + c  <->  canonical s[kb/gpb][16t + c]
-// (one row per 128-row block; a group spanning gpb blocks is stored gpb times, and
-// the inverse reads the first copy)
+// Canonical group row of half h of 128-row block kb: SH = 2 for groups of 64 rows,
+// otherwise gpb = group / 128 blocks per group.
+__device__ __forceinline__ long group_row(int kb, int h, int SH, int gpb) {
+  return SH == 2 ? 2L * kb + h : (long)(kb / gpb);
+}
+
+// scales: repacked index o = ((t*Gk + kb)*16 + c)*SH + h  <->  canonical s[row][16t + c]
+// (a group spanning gpb blocks is stored gpb times, and the inverse reads the first copy)
 template <bool TO_REPACKED>
 __global__ void scales_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                              long total, int Gk, int gpb, int N) {
+                              long total, int Gk, int gpb, int SH, int N) {
   for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
        o += (long)gridDim.x * blockDim.x) {
-    const int c = (int)(o & 15);
-    const long tk = o >> 4;
+    const int h = SH == 2 ? (int)(o & 1) : 0;
+    const long oc = SH == 2 ? o >> 1 : o;
+    const int c = (int)(oc & 15);
+    const long tk = oc >> 4;
     const long t = tk / Gk;
     const int kb = (int)(tk - t * Gk);
-    const long ci = (long)(kb / gpb) * N + 16 * t + c;
+    const long ci = group_row(kb, h, SH, gpb) * N + 16 * t + c;
     if (TO_REPACKED) dst[o] = src[ci];
-    else if (kb % gpb == 0) dst[ci] = src[o];
+    else if (SH == 2 || kb % gpb == 0) dst[ci] = src[o];
   }
 }
 
-// zero-points: repacked word o = (t*Gk + kb)*2 + h  <->  canonical word [kb/gpb][2t + h]
+// zero-points: repacked word o = ((t*Gk + kb)*SH + h)*2 + w  <->  canonical word
+// [row][2t + w]
 template <bool TO_REPACKED>
 __global__ void zeros_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
-                             long total, int Gk, int gpb, int N) {
+                             long total, int Gk, int gpb, int SH, int N) {
   for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
        o += (long)gridDim.x * blockDim.x) {
-    const int h = (int)(o & 1);
-    const long tk = o >> 1;
+    const int w = (int)(o & 1);
+    const long oh = o >> 1;
+    const int h = SH == 2 ? (int)(oh & 1) : 0;
+    const long tk = SH == 2 ? oh >> 1 : oh;
     const long t = tk / Gk;
     const int kb = (int)(tk - t * Gk);
-    const long ci = (long)(kb / gpb) * (N / 8) + 2 * t + h;
+    const long ci = group_row(kb, h, SH, gpb) * (N / 8) + 2 * t + w;
     if (TO_REPACKED) dst[o] = src[ci];
-    else if (kb % gpb == 0) dst[ci] = src[o];
+    else if (SH == 2 || kb % gpb == 0) dst[ci] = src[o];
   }
 }
 
@@ -222,25 +232,25 @@ inline int grid_for(long total, int threads) {
 
 hipError_t launch_repack(const int32_t* q, const uint16_t* s, const int32_t* z, uint32_t* wp,
                          uint16_t* sp, uint32_t* zp, int K, int N, int group, hipStream_t st) {
-  const int Gk = K / KBLK, gpb = group / KBLK;
-  const long wtot = (long)K * N / 8, stot = (long)Gk * N, ztot = (long)Gk * N / 8;
+  const int Gk = K / KBLK, SH = group == 64 ? 2 : 1, gpb = SH == 2 ? 1 : group / KBLK;
+  const long wtot = (long)K * N / 8, stot = (long)Gk * N * SH, ztot = (long)Gk * N / 8 * SH;
   codes_kernel<true><<<grid_for(wtot, 256), 256, 0, st>>>(
       reinterpret_cast<const uint32_t*>(q), wp, wtot, Gk, N);
-  scales_kernel<true><<<grid_for(stot, 256), 256, 0, st>>>(s, sp, stot, Gk, gpb, N);
+  scales_kernel<true><<<grid_for(stot, 256), 256, 0, st>>>(s, sp, stot, Gk, gpb, SH, N);
   if (z) zeros_kernel<true><<<grid_for(ztot, 256), 256, 0, st>>>(
-      reinterpret_cast<const uint32_t*>(z), zp, ztot, Gk, gpb, N);
+      reinterpret_cast<const uint32_t*>(z), zp, ztot, Gk, gpb, SH, N);
   return hipGetLastError();
 }
 
 hipError_t launch_unpack(const uint32_t* wp, const uint16_t* sp, const uint32_t* zp, int32_t* q,
                          uint16_t* s, int32_t* z, int K, int N, int group, hipStream_t st) {
-  const int Gk = K / KBLK, gpb = group / KBLK;
-  const long wtot = (long)K * N / 8, stot = (long)Gk * N, ztot = (long)Gk * N / 8;
+  const int Gk = K / KBLK, SH = group == 64 ? 2 : 1, gpb = SH == 2 ? 1 : group / KBLK;
+  const long wtot = (long)K * N / 8, stot = (long)Gk * N * SH, ztot = (long)Gk * N / 8 * SH;
   codes_kernel<false><<<grid_for(wtot, 256), 256, 0, st>>>(
       wp, reinterpret_cast<uint32_t*>(q), wtot, Gk, N);
-  scales_kernel<false><<<grid_for(stot, 256), 256, 0, st>>>(sp, s, stot, Gk, gpb, N);
+  scales_kernel<false><<<grid_for(stot, 256), 256, 0, st>>>(sp, s, stot, Gk, gpb, SH, N);
   if (zp) zeros_kernel<false><<<grid_for(ztot, 256), 256, 0, st>>>(
-      zp, reinterpret_cast<uint32_t*>(z), ztot, Gk, gpb, N);
+      zp, reinterpret_cast<uint32_t*>(z), ztot, Gk, gpb, SH, N);
   return hipGetLastError();
 }
 
@@ -252,7 +262,7 @@ hipError_t launch_sparse_compress(const int32_t* q, const uint16_t* s, uint32_t*
   zero_int_kernel<<<1, 1, 0, st>>>(bad);
   sparse_compress_kernel<<<grid_for(tot, 256), 256, 0, st>>>(
       reinterpret_cast<const uint32_t*>(q), vp, meta, bad, tot, Gk, N);
-  scales_kernel<true><<<grid_for(stot, 256), 256, 0, st>>>(s, sp, stot, Gk, gpb, N);
+  scales_kernel<true><<<grid_for(stot, 256), 256, 0, st>>>(s, sp, stot, Gk, gpb, 1, N);
   return hipGetLastError();
 }
 
@@ -263,7 +273,7 @@ hipError_t launch_sparse_decompress(const uint32_t* vp, const uint32_t* meta, co
   const long tot = (long)(N / 16) * Gk * 64, stot = (long)Gk * N;
   sparse_decompress_kernel<<<grid_for(tot, 256), 256, 0, st>>>(
       vp, meta, reinterpret_cast<uint32_t*>(q), tot, Gk, N);
-  scales_kernel<false><<<grid_for(stot, 256), 256, 0, st>>>(sp, s, stot, Gk, gpb, N);
+  scales_kernel<false><<<grid_for(stot, 256), 256, 0, st>>>(sp, s, stot, Gk, gpb, 1, N);
   return hipGetLastError();
 }
 
