@@ -323,6 +323,41 @@ def group64_leg(w4, torch):
     return dict(kernel="w4a16_gemm with groups of 64 rows vs 128", runs=runs)
 
 
+def bf16_leg(w4, torch):
+    """bf16 activations (w4a16_gemm_bf16, skinny kernel for every M) against fp16
+    activations (w4a16_gemm) on the same repacked weights, at the decode-sweep shapes and
+    M = 1 / 16 / 32.  Seeded synthetic inputs on the device; weights rotate over copies
+    totalling at least 512 MiB."""
+    rot = 512 << 20
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(16)
+    runs = []
+    for (K, N) in [(4096, 4096), (4096, 12288), (11008, 4096)]:
+        q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
+                          generator=gen)
+        s = (torch.rand((K // 128, N), device="cuda", generator=gen) * 0.018 + 0.002).half()
+        pk = w4.alloc_packed(K, N, 128, False)
+        w4.w4a16_repack(q, s, None, *pk, K, N, 128)
+        n = max(2, -(-rot // (K * N // 2)))
+        copies = [pk] + [tuple(t.clone() if t is not None else None for t in pk) for _ in range(n - 1)]
+        for M in (1, 16, 32):
+            x = torch.randn((M, K), device="cuda", generator=gen)
+            Xh, Xb = x.half(), x.bfloat16()
+            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            Yb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            th = time_rotated(torch, [lambda c=c: w4.w4a16_gemm(Xh, c[0], c[1], None, Y, M, N, K, 128)
+                                      for c in copies])
+            tb = time_rotated(torch, [lambda c=c: w4.w4a16_gemm_bf16(Xb, c[0], c[1], None, Yb, M, N, K,
+                                                                     128) for c in copies])
+            wb = K * N // 2 + 2 * (K // 128) * N
+            runs.append(dict(M=M, K=K, N=N, fp16_us=round(th * 1e6, 2), bf16_us=round(tb * 1e6, 2),
+                             bf16_over_fp16_time=round(tb / th, 3),
+                             bf16_weight_GBps=round(wb / tb / 1e9, 1)))
+        del q, s, pk, copies
+        torch.cuda.empty_cache()
+    return dict(kernel="w4a16_gemm_bf16 vs w4a16_gemm (same weights)", runs=runs)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -563,9 +598,10 @@ def main():
     if not args.no_configs:
         sparse24, asym = config_legs(w4, torch, group)
 
-    group64 = None
+    group64 = bf16 = None
     if not args.no_configs:
         group64 = group64_leg(w4, torch)
+        bf16 = bf16_leg(w4, torch)
 
     # ---- CPU oracle on this host over one step (bounded sample) -----------------------
     cpu = None
@@ -635,6 +671,7 @@ def main():
         "sparse24_vs_dense": sparse24,
         "asym_zero_point": asym,
         "group64": group64,
+        "bf16_activations": bf16,
         "per_launch_us": [[p["M"], p["K"], p["N"], p["us"]] for p in per_launch],
     }
     if args.detail:

@@ -9,6 +9,7 @@ from .inputs import (  # noqa: F401
     CONFIGS,
     Workload,
     activations,
+    activations_bf16,
     config_runs,
     pack_nibbles_along_k,
     pack_nibbles_along_n,

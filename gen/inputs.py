@@ -147,3 +147,15 @@ def activations(w: Workload, seed: Optional[int] = None) -> np.ndarray:
     rng = np.random.Generator(np.random.PCG64(
         seed_for_activations(w.cfg, w.M, w.K, w.N) if seed is None else seed))
     return rng.standard_normal((w.M, w.K), dtype=np.float32).astype(np.float16)
+
+
+def activations_bf16(w: Workload, seed: Optional[int] = None):
+    """X [M, K] bf16 for the bf16-activation entry points: N(0,1) drawn in fp32, rounded
+    to nearest-even bf16.  Returns (bits uint16 [M, K], values float32 [M, K])."""
+    rng = np.random.Generator(np.random.PCG64(
+        seed_for_activations(w.cfg, w.M, w.K, w.N) if seed is None else seed))
+    x = rng.standard_normal((w.M, w.K), dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return bits, (bits.astype(np.uint32) << 16).view(np.float32)
+

@@ -201,6 +201,21 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
                              const uint16_t* sp, uint16_t* Y, int M, int N, int K, int group,
                              int variant, int splits, void* stream);
 
+/* ---- bf16 activations ---------------------------------------------------------------
+ * w4a16_gemm_bf16: Y (device, out) bf16 [M][N] = X (device, in) bf16 [M][K] * dequant(W),
+ *   same repacked weights and rules as w4a16_gemm except: group is a multiple of 128
+ *   (W4A16_ERR_SHAPE for 64), and every M runs on the skinny kernel.  The weights enter
+ *   the bf16 matrix instructions as the exact integers 128 + q; the offset 128 + z is
+ *   removed and the scale applied in fp32 per 128-row block, and Y is rounded once to
+ *   bf16 (nearest-even).  Bitwise reproducible like w4a16_gemm.
+ * w4a16_gemm_bf16_plan: the same with an explicit skinny variant (< the number of
+ *   "skinny_*" variants of w4a16_gemm_variants) and `splits` as in w4a16_gemm_plan. */
+int w4a16_gemm_bf16(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+                    uint16_t* Y, int M, int N, int K, int group, void* stream);
+int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+                         uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
+                         void* stream);
+
 /* ---- calibration kernels (measurement only) ---------------------------------------
  * The achievable ceilings the GEMM's rates are set against, beside the published peaks.
  * w4a16_probe_read: one plain streaming read of `bytes` bytes at device pointer p

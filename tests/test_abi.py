@@ -195,6 +195,19 @@ def test_probe_validation(raw):
     assert h(0, 10) == 0.0
 
 
+def test_bf16_validation(raw):
+    f = raw.w4a16_gemm_bf16_plan
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
+    assert f(None, A, A, None, A, 16, 1024, 1024, 128, -1, 0, None) == -1
+    assert f(A, A, A, None, A, 16, 1024, 1024, 64, -1, 0, None) == -2   # groups of 64: fp16 only
+    assert f(A, A, A, None, A, 16, 1000, 1024, 128, -1, 0, None) == -2
+    raw.w4a16_gemm_variant_name.restype = ctypes.c_char_p
+    nskinny = sum(1 for v in range(raw.w4a16_gemm_variants())
+                  if not raw.w4a16_gemm_variant_name(v).startswith(b"tiled"))
+    assert f(A, A, A, None, A, 16, 1024, 1024, 128, nskinny, 0, None) == -8  # tiled: not bf16
+    assert f(A, A, A, None, A, 16, 1024, 1024, 128, -2, 0, None) == -8
+
+
 def test_baseline_validation(raw):
     f = raw.w4a16_fp16_gemm
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]

@@ -582,3 +582,88 @@ def test_group64_full_size(gh, M, K, N, asym):
     Yref, B = oracle.gemm_sampled(X, d["Qp"], d["s"], d["Zp"], 64, rows, cols)
     ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, B)
     assert ok, info
+
+
+# ---- bf16 activations (skinny kernel; Y rounded once to bf16) ---------------------------
+BF16_FRO = 4e-3  # one bf16 rounding of Y costs up to 2^-9 of |Y|: the Frobenius limit is 4x looser
+
+
+def _bf16_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _f32_bf16_rne(x: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _case_bf16(M, K, N, asym=False, seed=0):
+    from gen import activations_bf16
+    w = Workload(cfg=9, M=M, K=K, N=N, asym=asym)
+    d = weights(w, seed=5000 + seed + K + N)
+    bits, vals = activations_bf16(w, seed=6000 + seed + M)
+    return w, d, bits, vals
+
+
+def _gemm_bf16(gh, Xbits, packed, M, N, K, variant=-1, splits=0):
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    wp, sp, zp = packed
+    Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+    w4.w4a16_gemm_bf16_plan(gh.dev(Xbits.view(np.int16)), wp, sp, zp, Y, M, N, K, 128, variant, splits)
+    return gh.host(Y).view(np.uint16)
+
+
+@pytest.mark.parametrize("M,K,N,asym", [(5, 1152, 528, True), (16, 1024, 512, False),
+                                        (33, 2048, 1040, True), (300, 1024, 256, False)])
+def test_bf16_every_variant(gh, M, K, N, asym):
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, bits, vals = _case_bf16(M, K, N, asym)
+    packed = gh.repack(d, K, N)
+    Yref = oracle.gemm(vals, d["Qp"], d["s"], d["Zp"], 128)
+    B = oracle.error_bound(vals, d["Qp"], d["s"], d["Zp"], 128)
+    ran = 0
+    for v in [-1] + list(range(w4.w4a16_gemm_variants())):
+        name = w4.w4a16_gemm_variant_name(v) if v >= 0 else "auto"
+        if name.startswith("tiled"):
+            continue
+        nt = 1 if v < 0 else int(name.split("_nt")[1].split("_")[0])
+        if N % (16 * nt):
+            continue
+        for splits in ((0,) if v < 0 else (1, 3)):
+            Y = _bf16_f32(_gemm_bf16(gh, bits, packed, M, N, K, v, splits))
+            ok, info = oracle.accept(Y, Yref, B, rel_fro=BF16_FRO)
+            assert ok, (name, splits, info)
+            ran += 1
+    assert ran > 1
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_bf16_onehot_exact(gh, asym):
+    """One-hot bf16 rows select RNE_bf16((q - z) * s) bit for bit: the offset removal
+    with the activation row sums and the fp32 scale are exact for a single term."""
+    M, K, N = 16, 1024, 768
+    _, d, _, _ = _case_bf16(M, K, N, asym)
+    ks = [0, 1, 7, 8, 9, 127, 128, 255, 300, 511, 512, 640, 777, 900, 1022, 1023]
+    bits = np.zeros((M, K), np.uint16)
+    bits[np.arange(M), ks] = 0x3F80  # 1.0
+    W = oracle.dequant(d["Qp"], d["s"], d["Zp"], K, N, 128)  # exact (q - z) * s
+    exp = _f32_bf16_rne(W[ks].astype(np.float32))              # exact in fp32, one rounding
+    packed = gh.repack(d, K, N)
+    for nm, splits in [("skinny_xr16_nt1_wk8_d2", 1), ("skinny_xr16_nt4_wk4_d2", 3),
+                       ("skinny_xr16_nt2_wk8_d2", 2)]:
+        Y = _gemm_bf16(gh, bits, packed, M, N, K, gh.variant_index(nm), splits)
+        assert np.array_equal(Y, exp), nm
+
+
+@pytest.mark.parametrize("M,K,N,asym", [(1, 4096, 11008, False), (16, 4096, 11008, True),
+                                        (32, 11008, 4096, False)])
+def test_bf16_full_size(gh, M, K, N, asym):
+    _, d, bits, vals = _case_bf16(M, K, N, asym)
+    Y = _bf16_f32(_gemm_bf16(gh, bits, gh.repack(d, K, N), M, N, K))
+    rng = np.random.default_rng(M + N)
+    rows = _sample_idx(rng, M, 24)
+    cols = _sample_idx(rng, N, 48)
+    Yref, B = oracle.gemm_sampled(vals, d["Qp"], d["s"], d["Zp"], 128, rows, cols)
+    ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, B, rel_fro=BF16_FRO)
+    assert ok, info

@@ -450,6 +450,23 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
 
 }  // extern "C"
 
+// ---- bf16 activations ----------------------------------------------------------------
+int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+                         uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
+                         void* stream) {
+  int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
+  if (rc) return rc;
+  if (group == 64) return W4A16_ERR_SHAPE;  // bf16: groups of 128 rows or more
+  if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
+  return run_skinny(zp ? W_ASYMB : W_SYMB, X, wp, sp, zp, Y, M, N, K, group, variant, splits,
+                    stream);
+}
+
+int w4a16_gemm_bf16(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+                    uint16_t* Y, int M, int N, int K, int group, void* stream) {
+  return w4a16_gemm_bf16_plan(X, wp, sp, zp, Y, M, N, K, group, -1, 0, stream);
+}
+
 // ---- calibration kernels -------------------------------------------------------------
 int w4a16_probe_read(const void* p, size_t bytes, uint32_t* out, void* stream) {
   if (!p || !out) return W4A16_ERR_NULL;

@@ -100,6 +100,36 @@ __device__ __forceinline__ half8 dequant_word(uint32_t w, half2v c0, half2v c1, 
   return r;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 activations: 8 codes of one repacked word -> 8 exact bf16 values 128 + q, rows
+// 0..7.  OR-ing a nibble into the mantissa of 128.0 (0x4300; the bf16 ulp in [128, 256)
+// is 1) gives 128 + q exactly; the shifts bring each row pair's nibbles to bits 0-3 of
+// the two halves (bf16 has only 7 mantissa bits, so the 16q trick of fp16 does not
+// apply).  The offset 128 + z is removed after the matrix instruction, in fp32, with
+// the block's activation row sums (see compute_stage).
+__device__ __forceinline__ bf16x8 offset_codes_bf16(uint32_t w) {
+  const uint32_t magic = 0x43004300u;
+  const uint32_t t0 = and_or(w, 0x000F000Fu, magic);          // rows 0, 1
+  const uint32_t t1 = and_or(w >> 4, 0x000F000Fu, magic);     // rows 2, 3
+  const uint32_t t2 = and_or(w >> 8, 0x000F000Fu, magic);     // rows 4, 5
+  const uint32_t t3 = and_or(w >> 12, 0x000F000Fu, magic);    // rows 6, 7
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8, u32x4v{t0, t1, t2, t3});
+}
+
+// fp32 -> output bits: fp16 (round to nearest even), or bf16 (round to nearest even)
+template <int MODE>
+__device__ __forceinline__ uint16_t out_bits(float v) {
+  if constexpr (mode_bf16(MODE)) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+  } else {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+  }
+}
+
 constexpr int XSTRIDE = 272;  // bytes per X row in the LDS tile (256 + 16 against bank conflicts)
 
 template <int XR, int NT, int MODE>
@@ -156,7 +186,7 @@ __device__ __forceinline__ void load_stage(Stage<XR, NT, MODE>& S, int kb, bool 
           S.z64[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.z, 0u, blk * 16u, 0));
       } else {
         S.s[t] = __builtin_amdgcn_raw_buffer_load_b16(R.s, (uint32_t)(lane & 15) * 2, blk * 32u, 0);
-        if (MODE == W_ASYM)
+        if (mode_asym(MODE))
           S.z[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(R.z, 0u, blk * 8u, 0));
       }
     }
@@ -206,6 +236,49 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
         g = __builtin_amdgcn_smfmac_f32_16x16x64_f16(w0, xb0, g, meta, 0, 0);
         g = __builtin_amdgcn_smfmac_f32_16x16x64_f16(w1, xb1, g, meta, 0, 1);
         acc[t][mt] += sc * g;
+      }
+    }
+    return;
+  }
+  if constexpr (mode_bf16(MODE)) {
+    // bf16: the matrix instructions see the exact 128 + q; per (row tile, block) the
+    // sum of the activations over the block (one more matrix instruction per k-step
+    // against ones) removes the offset: sum x (q - z) = sum x (128 + q) - (128 + z) sum x.
+    // The weights stay exact integers and the scale applies in fp32, as in the fp16 path.
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                         0x3F803F80u});
+    float4v xs[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      xs[mt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][j]), ones,
+                                                          xs[mt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bf16x8 b[4];
+      b[0] = offset_codes_bf16(S.w[t][0].x);
+      b[1] = offset_codes_bf16(S.w[t][0].y);
+      b[2] = offset_codes_bf16(S.w[t][0].z);
+      b[3] = offset_codes_bf16(S.w[t][0].w);
+      int zq = 8;
+      if constexpr (mode_asym(MODE)) {
+        const int c = lane & 15;
+        const uint32_t zw = c < 8 ? S.z[t].x : S.z[t].y;
+        zq = (int)((zw >> (4 * (c & 7))) & 15u);
+      }
+      const float off = (float)(128 + zq);
+      const float sc = (float)__builtin_bit_cast(_Float16, S.s[t]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float4v g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][j]), b[j], g,
+                                                       0, 0, 0);
+        acc[t][mt] += sc * (g - off * xs[mt]);
       }
     }
     return;
@@ -502,7 +575,7 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
         const int row = m0 + mt * 16 + 4 * (lane >> 4) + r;
         const int col = (t0 + t) * 16 + (lane & 15);
         if (row < row_end)
-          Y[(long)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[t][mt][r]);
+          Y[(long)row * N + col] = out_bits<MODE>(acc[t][mt][r]);
       }
 }
 
@@ -511,7 +584,7 @@ typedef void (*KernelFn)(const uint16_t*, const uint4*, const uint16_t*, const u
 
 struct Variant {
   int XR, NT, WK, D;
-  KernelFn sym, asym, f16, sp24, sym64, asym64;
+  KernelFn sym, asym, f16, sp24, sym64, asym64, symb, asymb;
   const char* name;
 };
 
@@ -520,6 +593,7 @@ struct Variant {
     XR, NT, WK, D, skinny_kernel<XR, NT, WK, D, W_SYM>, skinny_kernel<XR, NT, WK, D, W_ASYM>, \
         skinny_kernel<XR, NT, WK, D, W_FP16>, skinny_kernel<XR, NT, WK, D, W_SP24>,      \
         skinny_kernel<XR, NT, WK, D, W_SYM64>, skinny_kernel<XR, NT, WK, D, W_ASYM64>,   \
+        skinny_kernel<XR, NT, WK, D, W_SYMB>, skinny_kernel<XR, NT, WK, D, W_ASYMB>,     \
         "skinny_xr" #XR "_nt" #NT "_wk" #WK "_d" #D                                      \
   }
 
@@ -637,6 +711,8 @@ hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                : p.mode == W_SP24   ? v.sp24
                : p.mode == W_SYM64  ? v.sym64
                : p.mode == W_ASYM64 ? v.asym64
+               : p.mode == W_SYMB   ? v.symb
+               : p.mode == W_ASYMB  ? v.asymb
                                     : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint4*>(w), sp, reinterpret_cast<const uint2*>(zp), Y,

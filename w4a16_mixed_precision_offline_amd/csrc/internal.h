@@ -61,13 +61,21 @@ hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
                           uint16_t* W, int K, int N, int group, hipStream_t st);
 
 // Fused skinny GEMM.  `part` / `counters` form the split-K workspace.
-// weight format of a launch; the *64 modes are the same formats with groups of 64 rows
-enum WMode { W_SYM = 0, W_ASYM = 1, W_FP16 = 2, W_SP24 = 3, W_SYM64 = 4, W_ASYM64 = 5 };
-__host__ __device__ constexpr bool mode_asym(int m) { return m == W_ASYM || m == W_ASYM64; }
+// weight format of a launch; the *64 modes are the same formats with groups of 64 rows,
+// the *B modes take bf16 activations and write bf16 outputs (skinny kernel only)
+enum WMode {
+  W_SYM = 0, W_ASYM = 1, W_FP16 = 2, W_SP24 = 3, W_SYM64 = 4, W_ASYM64 = 5, W_SYMB = 6,
+  W_ASYMB = 7
+};
+__host__ __device__ constexpr bool mode_asym(int m) {
+  return m == W_ASYM || m == W_ASYM64 || m == W_ASYMB;
+}
 __host__ __device__ constexpr bool mode_g64(int m) { return m == W_SYM64 || m == W_ASYM64; }
+__host__ __device__ constexpr bool mode_bf16(int m) { return m == W_SYMB || m == W_ASYMB; }
 // packed 4-bit codes with scales (and zero-points): the dense repacked formats
 __host__ __device__ constexpr bool mode_dense4(int m) {
-  return m == W_SYM || m == W_ASYM || m == W_SYM64 || m == W_ASYM64;
+  return m == W_SYM || m == W_ASYM || m == W_SYM64 || m == W_ASYM64 || m == W_SYMB ||
+         m == W_ASYMB;
 }
 struct SkinnyPlan {
   int variant;   // index into the variant table
