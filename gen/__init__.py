@@ -10,6 +10,7 @@ from .inputs import (  # noqa: F401
     Workload,
     activations,
     activations_bf16,
+    activations_fp8,
     config_runs,
     pack_nibbles_along_k,
     pack_nibbles_along_n,

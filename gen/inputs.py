@@ -159,3 +159,22 @@ def activations_bf16(w: Workload, seed: Optional[int] = None):
     bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
     return bits, (bits.astype(np.uint32) << 16).view(np.float32)
 
+
+
+def activations_fp8(w: Workload, seed: Optional[int] = None):
+    """X [M, K] as OCP FP8 E4M3 codes with one fp32 scale per row, for the W4A8 entry
+    points: x ~ N(0,1) drawn in fp32 (the same draw as `activations`), a[m] = max_k
+    |x[m, k]| / 448 (448 is the largest finite E4M3 value), codes = the E4M3 value
+    nearest to x / a (ties to even; torch's float8_e4m3fn cast).  This is the caller's
+    per-row quantization of its activations, not a step of the method.
+    Returns (codes uint8 [M, K], a float32 [M])."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(
+        seed_for_activations(w.cfg, w.M, w.K, w.N) if seed is None else seed))
+    x = rng.standard_normal((w.M, w.K), dtype=np.float32)
+    amax = np.abs(x).max(axis=1) if w.K else np.zeros(w.M, np.float32)
+    a = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    xs = torch.from_numpy(x / a[:, None])
+    codes = xs.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, a

@@ -10,13 +10,18 @@ definitions it implements and the passages they follow.
 """
 from .w4a16_ref import (  # noqa: F401
     accept,
+    activations_w4a8,
+    decode_e4m3,
     check_24,
     dequant,
     dequant_fp16,
     error_bound,
+    error_bound_w4a8,
     gemm,
     gemm_exact,
     gemm_sampled,
+    gemm_w4a8,
+    gemm_w4a8_sampled,
     unpack_codes_k,
     unpack_codes_n,
     zero_points,

@@ -27,6 +27,10 @@ Readings where the pages are silent (each is also listed in the design notes):
     applies to rows G*g .. G*g + g - 1 of column n.
   * A 2:4-sparse weight is an ordinary weight whose pruned positions carry the
     zero code (q = z), so its oracle is the dense oracle on the pruned codes.
+  * W4A8 (fp8 activations, [P1] section "CUTLASS W4A8（混合精度）"): the
+    activations are OCP E4M3 codes with an optional fp32 scale per row; the
+    product is the same definition on their exact values (decode_e4m3 and
+    gemm_w4a8 below).
 
 Pinned by tests/test_oracle.py (exhaustive nibble tables, exact-rational brute
 force, closed forms and invariants); no function here is "parity unpinned".
@@ -170,6 +174,67 @@ def gemm_exact(X: np.ndarray, Qp: np.ndarray, s: np.ndarray, Zp: Optional[np.nda
                 acc += Xf[m][k] * (q - z) * Sf[G][n]
             Y[m][n] = acc
     return Y
+
+
+# -- W4A8: fp8 (E4M3) activations ---------------------------------------------
+# [P1] section "CUTLASS W4A8（混合精度）" describes the neighbouring variant: INT4
+# weights times FP8 activations, so that the matrix product runs on FP8 matrix
+# units.  The pages fix neither the FP8 encoding nor how activations are scaled.
+# Readings taken: activations arrive as OCP FP8 E4M3 codes (the encoding of
+# the "FP8" of that section's hardware; 1 sign bit, 4 exponent bits with bias
+# 7, 3 mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448),
+# with an optional fp32 scale per activation row (None means 1); the weights
+# are the same (q - z) * s as above and the output is fp16.
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """Real values (float64) of OCP E4M3 byte codes.
+
+    exponent field e = 0: (-1)^sign * 2^-6 * m/8 (subnormal);
+    otherwise:            (-1)^sign * 2^(e-7) * (1 + m/8);
+    e = 15 and m = 7:     NaN.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = np.ldexp(m / 8.0, -6)
+    v = sign * np.where(e == 0, sub, normal)
+    return np.where((e == 15) & (c & 7 == 7), np.nan, v)
+
+
+def activations_w4a8(X8: np.ndarray, xscale: Optional[np.ndarray]) -> np.ndarray:
+    """Activation values a[m] * x[m, k] in float64 (exact: a 24-bit times a
+    4-bit significand fits in 53 bits)."""
+    Xv = decode_e4m3(X8)
+    if xscale is not None:
+        Xv = Xv * np.asarray(xscale, dtype=np.float32).astype(np.float64)[:, None]
+    return Xv
+
+
+def gemm_w4a8(X8: np.ndarray, xscale: Optional[np.ndarray], Qp: np.ndarray, s: np.ndarray,
+              Zp: Optional[np.ndarray], group: int) -> np.ndarray:
+    """Y[m, n] = a[m] * sum_k x8[m, k] * (q[k, n] - z) * s[k // g, n], float64 [M, N]."""
+    K = X8.shape[1]
+    N = Qp.shape[1]
+    return activations_w4a8(X8, xscale) @ dequant(Qp, s, Zp, K, N, group)
+
+
+def error_bound_w4a8(X8: np.ndarray, xscale: Optional[np.ndarray], Qp: np.ndarray,
+                     s: np.ndarray, Zp: Optional[np.ndarray], group: int) -> np.ndarray:
+    """Bnd[m, n] = sum_k |a[m] * x8[m, k] * W[k, n]|."""
+    K = X8.shape[1]
+    N = Qp.shape[1]
+    return np.abs(activations_w4a8(X8, xscale)) @ np.abs(dequant(Qp, s, Zp, K, N, group))
+
+
+def gemm_w4a8_sampled(X8, xscale, Qp, s, Zp, group, rows, cols):
+    """Y and Bnd of the W4A8 product at the cross product rows x cols only."""
+    K = X8.shape[1]
+    N = Qp.shape[1]
+    W = dequant(Qp, s, Zp, K, N, group, cols=cols)
+    r = np.asarray(rows)
+    Xr = activations_w4a8(X8[r], None if xscale is None else np.asarray(xscale)[r])
+    return Xr @ W, np.abs(Xr) @ np.abs(W)
 
 
 # -- step 6: acceptance -------------------------------------------------------

@@ -480,3 +480,184 @@ def test_planted_mistakes_are_caught(monkeypatch):
     ]
     for i, m in enumerate(mutants):
         assert not _pins_pass(m), f"mutant {i} survived the pins"
+
+
+# ---- W4A8: fp8 (E4M3) activations --------------------------------------------------
+def _e4m3_fixture():
+    out = []
+    with open(os.path.join(GOLD, "e4m3_values.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                code, val = line.split()
+                out.append((int(code, 16), float(val)))
+    return out
+
+
+def _torch_e4m3(codes):
+    import torch
+    c = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return c.view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_golden_fixture():
+    for code, val in _e4m3_fixture():
+        v = float(oracle.decode_e4m3(np.array([code], np.uint8))[0])
+        if np.isnan(val):
+            assert np.isnan(v), hex(code)
+        else:
+            assert v == val and np.signbit(v) == np.signbit(val), hex(code)
+
+
+def test_e4m3_exhaustive_vs_library():
+    # every byte code against torch's float8_e4m3fn (a library decode of the same format)
+    c = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(oracle.decode_e4m3(c), _torch_e4m3(c), equal_nan=True)
+
+
+def _w4a8_exact(X8, a, Qp, s, Zp, g):
+    """sum_k a[m] x[m,k] (q - z) s in exact rationals; x from the library decode,
+    codes read bit by bit from Python integers."""
+    M, K = X8.shape
+    N = Qp.shape[1]
+    xv = _torch_e4m3(X8)
+    Qw = [[int(v) & 0xFFFFFFFF for v in row] for row in np.asarray(Qp, dtype=np.int64)]
+    Zw = None if Zp is None else [[int(v) & 0xFFFFFFFF for v in row] for row in np.asarray(Zp, dtype=np.int64)]
+    out = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        am = Fraction(1) if a is None else Fraction(float(np.float32(a[m])))
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                q = (Qw[k // 8][n] >> (4 * (k % 8))) % 16
+                z = 8 if Zw is None else (Zw[k // g][n // 8] >> (4 * (n % 8))) % 16
+                acc += Fraction(float(xv[m, k])) * (q - z) * Fraction(float(s[k // g, n]))
+            out[m][n] = am * acc
+    return out
+
+
+def _random_e4m3(rng, shape):
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    return np.where((c & 0x7F) == 0x7F, np.uint8(0x38), c).astype(np.uint8)  # no NaN codes
+
+
+@pytest.mark.parametrize("M,K,N,asym,scaled", [(1, 128, 8, False, False), (3, 256, 16, True, True),
+                                               (4, 128, 8, True, False), (2, 256, 8, False, True)])
+def test_w4a8_gemm_vs_exact_rationals(M, K, N, asym, scaled):
+    rng = np.random.default_rng(7 * M + K + N)
+    g = 128
+    X8 = _random_e4m3(rng, (M, K))
+    a = rng.uniform(0.001, 0.01, size=M).astype(np.float32) if scaled else None
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    Zp = words_from_codes_n(rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)) if asym else None
+    Y = oracle.gemm_w4a8(X8, a, Qp, s, Zp, g)
+    B = oracle.error_bound_w4a8(X8, a, Qp, s, Zp, g)
+    E = _w4a8_exact(X8, a, Qp, s, Zp, g)
+    for m in range(M):
+        for n in range(N):
+            assert abs(Fraction(Y[m, n]) - E[m][n]) <= Fraction((K + 2) * 2.0 ** -53) * Fraction(B[m, n])
+
+
+def test_w4a8_onehot_rows_and_row_scale():
+    # x8 = 1.0 (code 0x38) at k, a = 2^j: row m of Y is exactly 2^j * W[k, :]
+    K, N, g = 256, 16, 128
+    q = np.array([[(5 * k + 3 * n) % 16 for n in range(N)] for k in range(K)], dtype=np.uint8)
+    s = np.random.default_rng(4).uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    ks = [0, 9, 127, 128, 255]
+    X8 = np.zeros((len(ks), K), dtype=np.uint8)
+    for m, k in enumerate(ks):
+        X8[m, k] = 0x38
+    a = np.array([1.0, 2.0, 0.5, 4.0, 0.25], dtype=np.float32)
+    Y = oracle.gemm_w4a8(X8, a, words_from_codes_k(q), s, None, g)
+    for m, k in enumerate(ks):
+        for n in range(N):
+            assert Y[m, n] == float(a[m]) * ((5 * k + 3 * n) % 16 - 8) * float(s[k // g, n])
+
+
+def test_w4a8_row_scale_is_per_row_and_exact():
+    rng = np.random.default_rng(21)
+    M, K, N, g = 5, 256, 16, 128
+    X8 = _random_e4m3(rng, (M, K))
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    Y1 = oracle.gemm_w4a8(X8, None, Qp, s, None, g)
+    assert np.array_equal(Y1, oracle.gemm_w4a8(X8, np.ones(M, np.float32), Qp, s, None, g))
+    p = np.array([2.0, 0.5, 8.0, 1.0, 0.125], dtype=np.float32)
+    assert np.array_equal(oracle.gemm_w4a8(X8, p, Qp, s, None, g), Y1 * p[:, None].astype(np.float64))
+
+
+def _pins_w4a8_pass(mod):
+    checks = []
+    for code, val in _e4m3_fixture():
+        v = float(mod.decode_e4m3(np.array([code], np.uint8))[0])
+        checks.append(np.isnan(v) if np.isnan(val) else v == val)
+    rng = np.random.default_rng(5)
+    M, K, N = 3, 256, 8
+    X8 = _random_e4m3(rng, (M, K))
+    a = np.array([0.5, 0.003, 7.0], dtype=np.float32)
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    s = rng.uniform(0.002, 0.02, size=(K // 128, N)).astype(np.float16)
+    Y = mod.gemm_w4a8(X8, a, Qp, s, None, 128)
+    E = _w4a8_exact(X8, a, Qp, s, None, 128)
+    checks.append(all(abs(Fraction(Y[m, n]) - E[m][n]) < Fraction(1, 10 ** 9)
+                      for m in range(M) for n in range(N)))
+    return all(checks)
+
+
+def test_w4a8_planted_mistakes_are_caught():
+    import types
+    assert _pins_w4a8_pass(ref)
+
+    def mutant(**overrides):
+        m = types.ModuleType("mutant")
+        m.__dict__.update({k: getattr(ref, k) for k in dir(ref) if not k.startswith("__")})
+        m.__dict__.update(overrides)
+        for name in ("activations_w4a8", "gemm_w4a8"):
+            if name not in overrides:
+                f = getattr(ref, name)
+                m.__dict__[name] = types.FunctionType(f.__code__, m.__dict__, name, f.__defaults__)
+        return m
+
+    def decode_bias8(codes):  # exponent bias 8 (the other FP8 E4M3 convention)
+        return ref.decode_e4m3(codes) / 2.0
+
+    def decode_no_subnormal(codes):  # e = 0 read as a normal number
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        v = ref.decode_e4m3(c)
+        e0 = ((c >> 3) & 15) == 0
+        mag = np.ldexp(1.0 + (c & 7) / 8.0, -7)
+        return np.where(e0 & ((c & 7) != 0), np.where(c >> 7, -mag, mag), v)
+
+    def decode_no_sign(codes):
+        return np.abs(ref.decode_e4m3(codes))
+
+    def acts_scale_by_column(X8, xscale):  # row scale applied along K instead of M
+        Xv = ref.decode_e4m3(X8)
+        if xscale is not None:
+            sc = np.resize(np.asarray(xscale, np.float64), Xv.shape[1])
+            Xv = Xv * sc[None, :]
+        return Xv
+
+    def acts_scale_dropped(X8, xscale):
+        return ref.decode_e4m3(X8)
+
+    mutants = [
+        mutant(decode_e4m3=decode_bias8),
+        mutant(decode_e4m3=decode_no_subnormal),
+        mutant(decode_e4m3=decode_no_sign),
+        mutant(activations_w4a8=acts_scale_by_column),
+        mutant(activations_w4a8=acts_scale_dropped),
+    ]
+    for i, m in enumerate(mutants):
+        assert not _pins_w4a8_pass(m), f"W4A8 mutant {i} survived the pins"
+
+
+def test_generator_fp8_activations():
+    from gen import Workload, activations_fp8
+    w = Workload(cfg=1, M=5, K=256, N=64)
+    codes, a = activations_fp8(w)
+    v = oracle.decode_e4m3(codes)
+    assert codes.dtype == np.uint8 and a.dtype == np.float32 and not np.isnan(v).any()
+    # every row uses the full E4M3 range: its largest magnitude is 448
+    assert np.all(np.abs(v).max(axis=1) == 448.0)
