@@ -216,6 +216,30 @@ int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, 
                          uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
                          void* stream);
 
+/* ---- fp8 activations: W4A8 ---------------------------------------------------------
+ * INT4 weights times FP8 activations, the mixed-precision variant that runs the product
+ * on FP8 matrix units (dingiv.github.io "Marlin", section "CUTLASS W4A8（混合精度）").
+ * w4a8_gemm: Y (device, out) fp16 [M][N] = diag(a) * X (device, in) * dequant(W), with
+ *   X8     (device, in)  [M][K] bytes, OCP FP8 E4M3 codes (bias 7, no infinities;
+ *          S.1111.111 is NaN, and NaN inputs give unspecified outputs), row-major;
+ *   xscale (device, in)  fp32 [M], the scale a[m] of activation row m, or NULL for 1;
+ *          4-byte aligned (W4A16_ERR_ALIGN otherwise);
+ *   wp, sp, zp           the repacked weights of w4a16_repack (zp NULL: symmetric, z = 8);
+ *   group  a multiple of 128 dividing K (W4A16_ERR_SHAPE for 64).
+ *   Every other rule (shapes, 16-byte alignment of X8, wp, sp, zp and Y, error codes,
+ *   asynchronous execution on `stream`, library-owned split-K workspace, Y fully
+ *   overwritten) is that of w4a16_gemm.  Every M runs on the skinny kernel.  The
+ *   weights enter v_mfma_f32_16x16x32_fp8_fp8 as the exact E4M3 integers q - z, the
+ *   scale s applies in fp32 per 128-row block, a[m] in fp32 before the one rounding of
+ *   Y to fp16 (nearest-even).  Bitwise reproducible like w4a16_gemm.
+ * w4a8_gemm_plan: the same with an explicit skinny variant (< the number of "skinny_*"
+ *   variants of w4a16_gemm_variants) and `splits` as in w4a16_gemm_plan. */
+int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,
+              const void* zp, uint16_t* Y, int M, int N, int K, int group, void* stream);
+int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,
+                   const void* zp, uint16_t* Y, int M, int N, int K, int group, int variant,
+                   int splits, void* stream);
+
 /* ---- calibration kernels (measurement only) ---------------------------------------
  * The achievable ceilings the GEMM's rates are set against, beside the published peaks.
  * w4a16_probe_read: one plain streaming read of `bytes` bytes at device pointer p

@@ -16,7 +16,7 @@ LIB = os.path.join(ROOT, "w4a16_mixed_precision_offline_amd", "libw4a16.so")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(w4a16_[a-z0-9_]+)\s*\(",
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(w4a(?:16|8)_[a-z0-9_]+)\s*\(",
                        src, flags=re.M)
     return sorted(set(names))
 
@@ -31,7 +31,8 @@ def raw():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("w4a16_repack", "w4a16_gemm", "w4a16_unpack", "w4a16_dequant",
-              "w4a16_fp16_gemm", "w4a16_packed_bytes", "w4a16_strerror"):
+              "w4a16_fp16_gemm", "w4a16_packed_bytes", "w4a16_strerror", "w4a8_gemm",
+              "w4a8_gemm_plan"):
         assert n in names
 
 
@@ -206,6 +207,27 @@ def test_bf16_validation(raw):
                   if not raw.w4a16_gemm_variant_name(v).startswith(b"tiled"))
     assert f(A, A, A, None, A, 16, 1024, 1024, 128, nskinny, 0, None) == -8  # tiled: not bf16
     assert f(A, A, A, None, A, 16, 1024, 1024, 128, -2, 0, None) == -8
+
+
+def test_w4a8_validation(raw):
+    f = raw.w4a8_gemm_plan
+    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
+    assert f(None, None, A, A, None, A, 16, 1024, 1024, 128, -1, 0, None) == -1
+    assert f(A, None, A, None, None, A, 16, 1024, 1024, 128, -1, 0, None) == -1  # no scales
+    assert f(A, None, A, A, None, A, 16, 1024, 1024, 64, -1, 0, None) == -2   # groups of 64
+    assert f(A, None, A, A, None, A, 16, 1000, 1024, 128, -1, 0, None) == -2
+    assert f(A, None, A, A, None, A, 0, 1024, 1024, 128, -1, 0, None) == -2
+    assert f(MIS, None, A, A, None, A, 16, 1024, 1024, 128, -1, 0, None) == -3
+    assert f(A, A + 2, A, A, None, A, 16, 1024, 1024, 128, -1, 0, None) == -3  # row scales
+    raw.w4a16_gemm_variant_name.restype = ctypes.c_char_p
+    nskinny = sum(1 for v in range(raw.w4a16_gemm_variants())
+                  if not raw.w4a16_gemm_variant_name(v).startswith(b"tiled"))
+    assert f(A, None, A, A, None, A, 16, 1024, 1024, 128, nskinny, 0, None) == -8  # skinny only
+    assert f(A, None, A, A, None, A, 16, 1024, 1024, 128, -1, -1, None) == -8
+    g = raw.w4a8_gemm
+    g.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    assert g(A, None, A, A, None, None, 16, 1024, 1024, 128, None) == -1   # no output
+    assert g(A, None, A, A, None, A, 16, 1024, 1000, 128, None) == -2
 
 
 def test_baseline_validation(raw):

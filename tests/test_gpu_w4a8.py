@@ -1,0 +1,185 @@
+"""GPU parity of the W4A8 entry points (INT4 weights x FP8 E4M3 activations with a
+per-row fp32 scale; dingiv.github.io "Marlin", section "CUTLASS W4A8（混合精度）")
+against the CPU oracle's fp64 definition on the activations' exact values.
+
+Bit-exact where the result has a single rounding (one-hot rows; unit versus absent
+row scales; doubled row scales); otherwise within the oracle's acceptance rule, the
+same as for fp16 activations: fp8 x (q - z) products are exact in fp32, so only the
+fp32 accumulation and the one fp16 rounding of Y remain.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gen import Workload, activations_fp8, config_runs, weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gh(lib):
+    import gpu_helpers
+    return gpu_helpers
+
+
+def _case(M, K, N, asym=False, seed=0, cfg=9):
+    w = Workload(cfg=cfg, M=M, K=K, N=N, asym=asym)
+    d = weights(w, seed=7000 + seed + K + N)
+    X8, a = activations_fp8(w, seed=8000 + seed + M)
+    return d, X8, a
+
+
+def _gemm8(gh, X8, a, packed, M, N, K, variant=-1, splits=0, rows_alloc=None):
+    """Run w4a8_gemm(_plan); Y is the first M rows of a NaN-filled buffer of
+    rows_alloc rows so that writes past row M-1 show up.  Returns (Y[:M], whole)."""
+    import w4a16_mixed_precision_offline_amd as w4
+    wp, sp, zp = packed
+    Yall = gh.nan_filled(rows_alloc or M, N)
+    Y = Yall[:M]
+    x = gh.dev(X8)
+    s = gh.dev(a) if a is not None else None
+    if variant == -1 and splits == 0:
+        w4.w4a8_gemm(x, s, wp, sp, zp, Y, M, N, K, 128)
+    else:
+        w4.w4a8_gemm_plan(x, s, wp, sp, zp, Y, M, N, K, 128, variant, splits)
+    whole = gh.host(Yall)
+    return whole[:M], whole
+
+
+def _accept(Y, X8, a, d, rows=None, cols=None):
+    if rows is None:
+        Yref = oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 128)
+        B = oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 128)
+        return oracle.accept(Y, Yref, B)
+    Yref, B = oracle.gemm_w4a8_sampled(X8, a, d["Qp"], d["s"], d["Zp"], 128, rows, cols)
+    return oracle.accept(Y[np.ix_(rows, cols)], Yref, B)
+
+
+def _sample_idx(rng, n, k):
+    idx = set([0, n - 1]) | set(rng.choice(n, size=min(n, k), replace=False).tolist())
+    return sorted(idx)
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_w4a8_onehot_exact(gh, asym):
+    """x8 = 1.0 (code 0x38) at one k per row and a power-of-two row scale select
+    RNE_fp16(a * (q - z) * s) bit for bit: the fp8 weights are the exact integers q - z
+    and a single term is exact in fp32."""
+    M, K, N = 16, 1024, 768
+    d, _, _ = _case(M, K, N, asym)
+    ks = [0, 1, 7, 8, 9, 127, 128, 255, 300, 511, 512, 640, 777, 900, 1022, 1023]
+    X8 = np.zeros((M, K), np.uint8)
+    X8[np.arange(M), ks] = 0x38
+    a = np.array([2.0 ** ((m % 5) - 2) for m in range(M)], dtype=np.float32)
+    W = oracle.dequant(d["Qp"], d["s"], d["Zp"], K, N, 128)       # exact (q - z) * s
+    exp = (W[ks] * a[:, None].astype(np.float64)).astype(np.float16)  # exact, one rounding
+    packed = gh.repack(d, K, N)
+    for nm, splits in [("skinny_xr16_nt1_wk8_d2", 1), ("skinny_xr16_nt4_wk4_d2", 3),
+                       ("skinny_xr16_nt2_wk8_d2", 2), ("skinny_xr16_nt3_wk4_d2", 1)]:
+        Y, _ = _gemm8(gh, X8, a, packed, M, N, K, gh.variant_index(nm), splits)
+        assert np.array_equal(Y.view(np.uint16), exp.view(np.uint16)), nm
+
+
+@pytest.mark.parametrize("M,K,N,asym", [(5, 1152, 528, True), (16, 1024, 512, False),
+                                        (33, 2048, 1040, True), (300, 1024, 256, False)])
+def test_w4a8_every_variant(gh, M, K, N, asym):
+    """Every skinny variant, with and without a K split, including row tails (M = 5,
+    33, 300) and column counts that are not a multiple of 64; rows past M untouched."""
+    import w4a16_mixed_precision_offline_amd as w4
+    d, X8, a = _case(M, K, N, asym)
+    packed = gh.repack(d, K, N)
+    Yref = oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 128)
+    B = oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 128)
+    ran = 0
+    for v in [-1] + list(range(w4.w4a16_gemm_variants())):
+        name = w4.w4a16_gemm_variant_name(v) if v >= 0 else "auto"
+        if name.startswith("tiled"):
+            continue
+        nt = 1 if v < 0 else int(name.split("_nt")[1].split("_")[0])
+        if N % (16 * nt):
+            continue
+        for splits in ((0,) if v < 0 else (1, 3)):
+            Y, whole = _gemm8(gh, X8, a, packed, M, N, K, v, splits, rows_alloc=M + 2)
+            ok, info = oracle.accept(Y, Yref, B)
+            assert ok, (name, splits, info)
+            assert np.all(np.isnan(whole[M:])), (name, splits)
+            ran += 1
+    assert ran > 1
+
+
+def test_w4a8_minimal_shapes(gh):
+    for M, K, N, asym in [(1, 128, 16, False), (1, 128, 16, True), (2, 256, 32, False)]:
+        d, X8, a = _case(M, K, N, asym)
+        Y, _ = _gemm8(gh, X8, a, gh.repack(d, K, N), M, N, K)
+        ok, info = _accept(Y, X8, a, d)
+        assert ok, (M, K, N, asym, info)
+
+
+def test_w4a8_row_scale_exact(gh):
+    """No row scale equals a unit one bit for bit, and doubling the row scales doubles Y
+    bit for bit wherever Y is a normal fp16 number."""
+    M, K, N = 16, 4096, 1024
+    d, X8, a = _case(M, K, N)
+    packed = gh.repack(d, K, N)
+    Y0, _ = _gemm8(gh, X8, None, packed, M, N, K)
+    Y1, _ = _gemm8(gh, X8, np.ones(M, np.float32), packed, M, N, K)
+    assert np.array_equal(Y0.view(np.uint16), Y1.view(np.uint16))
+    Ya, _ = _gemm8(gh, X8, a, packed, M, N, K)
+    Y2, _ = _gemm8(gh, X8, (a * 2).astype(np.float32), packed, M, N, K)
+    normal = (np.abs(Ya.astype(np.float32)) >= 2.0 ** -14) & np.isfinite(Y2)
+    assert normal.mean() > 0.99
+    assert np.array_equal(Y2[normal].astype(np.float32), 2 * Ya[normal].astype(np.float32))
+    ok, info = _accept(Ya, X8, a, d)
+    assert ok, info
+
+
+def test_w4a8_deterministic(gh):
+    M, K, N = 8, 11008, 4096
+    d, X8, a = _case(M, K, N)
+    packed = gh.repack(d, K, N)
+    ref, _ = _gemm8(gh, X8, a, packed, M, N, K)
+    for _ in range(10):
+        Y, _ = _gemm8(gh, X8, a, packed, M, N, K)
+        assert np.array_equal(Y.view(np.uint16), ref.view(np.uint16))
+    for splits in (2, 5):  # a K split summed across workgroups in slice order
+        v = gh.variant_index("skinny_xr8_nt1_wk8_d4")
+        Y1, _ = _gemm8(gh, X8, a, packed, M, N, K, v, splits)
+        Y2, _ = _gemm8(gh, X8, a, packed, M, N, K, v, splits)
+        assert np.array_equal(Y1.view(np.uint16), Y2.view(np.uint16))
+        ok, info = _accept(Y1, X8, a, d)
+        assert ok, (splits, info)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 3])
+def test_w4a8_config_shapes(gh, cfg):
+    """The tiny, decode-sweep and zero-point configurations' shapes at full size with fp8
+    activations (automatic plan, the one bench.py times): small outputs whole, larger
+    ones on sampled rows x columns."""
+    cache = {}
+    for w in config_runs(cfg):
+        key = (w.K, w.N)
+        if key not in cache:
+            d = weights(w)
+            cache.clear()
+            cache[key] = (d, gh.repack(d, w.K, w.N))
+        d, packed = cache[key]
+        X8, a = activations_fp8(w)
+        Y, _ = _gemm8(gh, X8, a, packed, w.M, w.N, w.K)
+        if w.M * w.N <= 16 * 4096:
+            ok, info = _accept(Y, X8, a, d)
+        else:
+            rng = np.random.default_rng(w.M + w.N)
+            ok, info = _accept(Y, X8, a, d, _sample_idx(rng, w.M, 24), _sample_idx(rng, w.N, 48))
+        assert ok, (w.name, info)
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 8192, 28672), (256, 8192, 10240), (64, 28672, 8192)])
+def test_w4a8_large_layers(gh, M, K, N):
+    """70B-class layer shapes (several 64-row blocks at M = 256), sampled outputs."""
+    w = Workload(cfg=2, M=M, K=K, N=N, s_lo=0.001, s_hi=0.01)
+    d = weights(w)
+    X8, a = activations_fp8(w)
+    Y, _ = _gemm8(gh, X8, a, gh.repack(d, K, N), M, N, K)
+    rng = np.random.default_rng(M + N)
+    ok, info = _accept(Y, X8, a, d, _sample_idx(rng, M, 24), _sample_idx(rng, N, 48))
+    assert ok, info

@@ -46,6 +46,8 @@ _SIGS = {
     "w4a16_sparse24_gemm_plan": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "w4a16_gemm_bf16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "w4a16_gemm_bf16_plan": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "w4a8_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "w4a8_gemm_plan": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "w4a16_probe_read": (_I, [_P, _SZ, _P, _P]),
     "w4a16_probe_mfma": (_I, [_I, _I, _P, _P]),
     "w4a16_probe_mfma_flops": (ctypes.c_double, [_I, _I]),
@@ -199,6 +201,19 @@ def w4a16_gemm_bf16_plan(X, wp, sp, zp, Y, M, N, K, group, variant=-1, splits=0,
     _check("w4a16_gemm_bf16_plan", _lib.w4a16_gemm_bf16_plan(
         _ptr(X), _ptr(wp), _ptr(sp), _ptr(zp), _ptr(Y), M, N, K, group, variant, splits,
         _stream(stream)))
+
+
+# ---- fp8 (E4M3) activations: W4A8 ---------------------------------------------------
+def w4a8_gemm(X8, xscale, wp, sp, zp, Y, M, N, K, group, stream=None):
+    _check("w4a8_gemm", _lib.w4a8_gemm(_ptr(X8), _ptr(xscale), _ptr(wp), _ptr(sp), _ptr(zp),
+                                       _ptr(Y), M, N, K, group, _stream(stream)))
+
+
+def w4a8_gemm_plan(X8, xscale, wp, sp, zp, Y, M, N, K, group, variant=-1, splits=0,
+                   stream=None):
+    _check("w4a8_gemm_plan", _lib.w4a8_gemm_plan(
+        _ptr(X8), _ptr(xscale), _ptr(wp), _ptr(sp), _ptr(zp), _ptr(Y), M, N, K, group, variant,
+        splits, _stream(stream)))
 
 
 # ---- calibration kernels ---------------------------------------------------------

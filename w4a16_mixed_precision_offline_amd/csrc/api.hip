@@ -117,7 +117,7 @@ inline int launched(hipError_t e) {
 
 int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
                uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
-               void* stream) {
+               void* stream, const float* xscale = nullptr) {
   SkinnyPlan plan;
   int rc = skinny_make_plan(M, N, K, group, mode, variant, splits, &plan);
   if (rc) return rc;
@@ -128,7 +128,7 @@ int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, c
   float* part;
   if ((rc = get_workspace(dev, st, plan.counters, plan.part_floats, &cnt, &part))) return rc;
   return launched(skinny_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, cnt,
-                                M, N, K, group, st));
+                                M, N, K, group, st, xscale));
 }
 
 // Which kernel an automatic plan uses, from sweeps on MI355X: the skinny (memory-bound)
@@ -321,6 +321,13 @@ size_t w4a16_workspace_bytes(int M, int N, int K) {
     const size_t bytes = (counters + 63) / 64 * 64 * sizeof(int) + floats * sizeof(float);
     if (bytes > need) need = bytes;
   }
+  // the bf16- and fp8-activation entry points run every M on the skinny kernel
+  SkinnyPlan p;
+  if (skinny_make_plan(M, N, K, KBLK, W_SYM8, -1, 0, &p) == 0) {
+    const size_t bytes =
+        ((size_t)p.counters + 63) / 64 * 64 * sizeof(int) + p.part_floats * sizeof(float);
+    if ((p.counters || p.part_floats) && bytes > need) need = bytes;
+  }
   return need;
 }
 
@@ -465,6 +472,25 @@ int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, 
 int w4a16_gemm_bf16(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                     uint16_t* Y, int M, int N, int K, int group, void* stream) {
   return w4a16_gemm_bf16_plan(X, wp, sp, zp, Y, M, N, K, group, -1, 0, stream);
+}
+
+// ---- fp8 (E4M3) activations: W4A8 ------------------------------------------------------
+int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,
+                   const void* zp, uint16_t* Y, int M, int N, int K, int group, int variant,
+                   int splits, void* stream) {
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(X8);
+  int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
+  if (rc) return rc;
+  if (group == 64) return W4A16_ERR_SHAPE;  // fp8 activations: groups of 128 rows or more
+  if (xscale && (reinterpret_cast<uintptr_t>(xscale) & 3u) != 0) return W4A16_ERR_ALIGN;
+  if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
+  return run_skinny(zp ? W_ASYM8 : W_SYM8, X, wp, sp, zp, Y, M, N, K, group, variant, splits,
+                    stream, xscale);
+}
+
+int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,
+              const void* zp, uint16_t* Y, int M, int N, int K, int group, void* stream) {
+  return w4a8_gemm_plan(X8, xscale, wp, sp, zp, Y, M, N, K, group, -1, 0, stream);
 }
 
 // ---- calibration kernels -------------------------------------------------------------

@@ -118,6 +118,25 @@ __device__ __forceinline__ bf16x8 offset_codes_bf16(uint32_t w) {
   return __builtin_bit_cast(bf16x8, u32x4v{t0, t1, t2, t3});
 }
 
+typedef short short2v __attribute__((ext_vector_type(2)));
+
+// fp8 activations: 8 codes of one repacked word -> 8 OCP E4M3 bytes of the exact integer
+// q - z, rows 0..7 in bytes 0..7 (the operand of one v_mfma_f32_16x16x32_fp8_fp8).  The
+// integers come out of dequant_word exactly in fp16; every integer in [-15, 15] is exact
+// in E4M3 (3 mantissa bits cover integers up to 16), so the conversion, a unit-scale
+// v_cvt_scalef32_pk_fp8_f16 per pair, is exact too.
+__device__ __forceinline__ uint64_t dequant_word_fp8(uint32_t w, half2v c0, half2v c1,
+                                                     uint32_t magic) {
+  const half8 h = dequant_word(w, c0, c1, magic);
+  short2v lo = {0, 0}, hi = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(lo, half2v{h[0], h[1]}, 1.0f, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(lo, half2v{h[2], h[3]}, 1.0f, true);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(hi, half2v{h[4], h[5]}, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(hi, half2v{h[6], h[7]}, 1.0f, true);
+  return (uint64_t)__builtin_bit_cast(uint32_t, lo) |
+         ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+}
+
 // fp32 -> output bits: fp16 (round to nearest even), or bf16 (round to nearest even)
 template <int MODE>
 __device__ __forceinline__ uint16_t out_bits(float v) {
@@ -132,6 +151,13 @@ __device__ __forceinline__ uint16_t out_bits(float v) {
 
 constexpr int XSTRIDE = 272;  // bytes per X row in the LDS tile (256 + 16 against bank conflicts)
 
+// 16-byte activation loads per k-block: one covers 4 rows x 256 bytes of fp16 / bf16, or
+// 8 rows x 128 bytes of fp8
+__host__ __device__ constexpr int x_loads(int XR, int MODE) {
+  return mode_fp8(MODE) ? (XR + 7) / 8 : XR / 4;
+}
+__host__ __device__ constexpr int x_elem_bytes(int MODE) { return mode_fp8(MODE) ? 1 : 2; }
+
 template <int XR, int NT, int MODE>
 struct Stage {
   u32x4 w[NT][MODE == W_FP16 ? 4 : 1];  // packed codes (fp16 rows for the baseline; for 2:4,
@@ -141,7 +167,8 @@ struct Stage {
   uint32_t s64[NT];                     // groups of 64: the scales of both halves (low: rows 0-63)
   u32x4 z64[NT];                        // groups of 64: zero-points, .xy half 0, .zw half 1
   uint2 s4[NT];                         // 2:4: the four scales of the lane's four columns
-  u32x4 x[XR / 4];                      // X rows 4c + lane/16, 16-byte chunk lane%16
+  u32x4 x[x_loads(XR, MODE)];           // X rows 4c + lane/16, 16-byte chunk lane%16 (fp8:
+                                        // rows 8c + lane/8, chunk lane%8)
 };
 
 // Loads of one k-block.  kb is wave-uniform, so every scalar offset below is
@@ -158,7 +185,7 @@ struct Rsrc {
 template <int XR, int NT, int MODE>
 __device__ __forceinline__ void load_stage(Stage<XR, NT, MODE>& S, int kb, bool live, int lane,
                                            int Gk, int K, const Rsrc& R0, const Rsrc& Rnull,
-                                           const uint32_t xoff[XR / 4]) {
+                                           const uint32_t xoff[x_loads(XR, MODE)]) {
   const Rsrc& R = live ? R0 : Rnull;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -192,7 +219,8 @@ __device__ __forceinline__ void load_stage(Stage<XR, NT, MODE>& S, int kb, bool 
     }
   }
 #pragma unroll
-  for (int c = 0; c < XR / 4; ++c) S.x[c] = bload16<false>(R.x, xoff[c], (uint32_t)kb * KBLK * 2);
+  for (int c = 0; c < x_loads(XR, MODE); ++c)
+    S.x[c] = bload16<false>(R.x, xoff[c], (uint32_t)kb * KBLK * x_elem_bytes(MODE));
 }
 
 // Compute one k-block: lay the X rows into the wave's LDS tile, read them back as
@@ -203,6 +231,49 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
                                               float4v (&acc)[NT][(XR + 15) / 16], int lane,
                                               uint32_t magic, char* xlds) {
   constexpr int MT = (XR + 15) / 16;
+  if constexpr (mode_fp8(MODE)) {
+    // fp8 activations: rows of 128 bytes; fragment (mt, j) of lane l is the 8 bytes of row
+    // 16mt + l%16 at 32j + 8(l/16), the k-slots of the word j of the lane's weight block.
+    // The weights enter v_mfma_f32_16x16x32_fp8_fp8 as the exact integers q - z and the
+    // scale applies in fp32 per block, for any number of column tiles.
+#pragma unroll
+    for (int c = 0; c < x_loads(XR, MODE); ++c)
+      *reinterpret_cast<u32x4*>(xlds + (8 * c + (lane >> 3)) * XSTRIDE + (lane & 7) * 16) = S.x[c];
+    long a8[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        a8[mt][j] = *reinterpret_cast<const long*>(xlds + (mt * 16 + (lane & 15)) * XSTRIDE +
+                                                    32 * j + 8 * (lane >> 4));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      int zq = 8;
+      if constexpr (mode_asym(MODE)) {
+        const int c = lane & 15;
+        const uint32_t zw = c < 8 ? S.z[t].x : S.z[t].y;
+        zq = (int)((zw >> (4 * (c & 7))) & 15u);
+      }
+      const _Float16 a0 = (_Float16)(float)(-1024 - zq);
+      const _Float16 a1 = (_Float16)(float)(-64 - zq);
+      const half2v c0 = {a0, a0}, c1 = {a1, a1};
+      long b[4];
+      b[0] = (long)dequant_word_fp8(S.w[t][0].x, c0, c1, magic);
+      b[1] = (long)dequant_word_fp8(S.w[t][0].y, c0, c1, magic);
+      b[2] = (long)dequant_word_fp8(S.w[t][0].z, c0, c1, magic);
+      b[3] = (long)dequant_word_fp8(S.w[t][0].w, c0, c1, magic);
+      const float sc = (float)__builtin_bit_cast(_Float16, S.s[t]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float4v g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          g = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8[mt][j], b[j], g, 0, 0, 0);
+        acc[t][mt] += sc * g;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < XR / 4; ++c)
     *reinterpret_cast<u32x4*>(xlds + (4 * c + (lane >> 4)) * XSTRIDE + (lane & 15) * 16) = S.x[c];
@@ -385,7 +456,8 @@ template <int XR, int NT, int WK, int D, int MODE>
 __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     const uint16_t* __restrict__ X, const uint4* __restrict__ W, const uint16_t* __restrict__ Sp,
     const uint2* __restrict__ Zp, uint16_t* __restrict__ Y, float* __restrict__ part,
-    int* __restrict__ counters, int M, int N, int K, int splits, int nblocks) {
+    int* __restrict__ counters, int M, int N, int K, int splits, int nblocks,
+    const float* __restrict__ xscale) {
   constexpr int MT = (XR + 15) / 16;
   constexpr int XTILE = MT * 16 * XSTRIDE;  // bytes of one wave's X tile
   // per-wave X tiles; after the main loop the same memory holds the reduction
@@ -435,14 +507,17 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     R.lane_w = (uint32_t)lane * 16;
   }
   const int rows = M - m0 < XR ? M - m0 : XR;  // valid rows of this block of X
-  R.x = make_rsrc(X + (size_t)m0 * K, (uint32_t)(rows * K * 2));
-  // per-lane byte offsets of the X row loads: row 4c + lane/16, 16 bytes at
-  // column 8(lane%16); rows past M read zeros
-  uint32_t xoff[XR / 4];
+  constexpr int XB = x_elem_bytes(MODE);
+  R.x = make_rsrc(reinterpret_cast<const char*>(X) + (size_t)m0 * K * XB, (uint32_t)(rows * K * XB));
+  // per-lane byte offsets of the X row loads: row 4c + lane/16, 16 bytes at byte
+  // 16(lane%16) of the row's k-block (fp8: row 8c + lane/8, byte 16(lane%8)); rows past M
+  // read zeros
+  uint32_t xoff[x_loads(XR, MODE)];
 #pragma unroll
-  for (int c = 0; c < XR / 4; ++c) {
-    const int r = 4 * c + (lane >> 4);
-    xoff[c] = r < rows ? (uint32_t)((r * K + 8 * (lane & 15)) * 2) : kOutOfRange;
+  for (int c = 0; c < x_loads(XR, MODE); ++c) {
+    const int r = mode_fp8(MODE) ? 8 * c + (lane >> 3) : 4 * c + (lane >> 4);
+    const int cb = mode_fp8(MODE) ? 16 * (lane & 7) : 16 * (lane & 15);
+    xoff[c] = r < rows ? (uint32_t)(r * K * XB + cb) : kOutOfRange;
   }
   // rows XR..15 of the LDS tile are never written by the loads: keep them zero
   if (XR % 16 != 0) {
@@ -574,17 +649,20 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + mt * 16 + 4 * (lane >> 4) + r;
         const int col = (t0 + t) * 16 + (lane & 15);
-        if (row < row_end)
-          Y[(long)row * N + col] = out_bits<MODE>(acc[t][mt][r]);
+        if (row < row_end) {
+          float v = acc[t][mt][r];
+          if (mode_fp8(MODE) && xscale != nullptr) v *= xscale[row];
+          Y[(long)row * N + col] = out_bits<MODE>(v);
+        }
       }
 }
 
 typedef void (*KernelFn)(const uint16_t*, const uint4*, const uint16_t*, const uint2*, uint16_t*,
-                         float*, int*, int, int, int, int, int);
+                         float*, int*, int, int, int, int, int, const float*);
 
 struct Variant {
   int XR, NT, WK, D;
-  KernelFn sym, asym, f16, sp24, sym64, asym64, symb, asymb;
+  KernelFn sym, asym, f16, sp24, sym64, asym64, symb, asymb, sym8, asym8;
   const char* name;
 };
 
@@ -594,6 +672,7 @@ struct Variant {
         skinny_kernel<XR, NT, WK, D, W_FP16>, skinny_kernel<XR, NT, WK, D, W_SP24>,      \
         skinny_kernel<XR, NT, WK, D, W_SYM64>, skinny_kernel<XR, NT, WK, D, W_ASYM64>,   \
         skinny_kernel<XR, NT, WK, D, W_SYMB>, skinny_kernel<XR, NT, WK, D, W_ASYMB>,     \
+        skinny_kernel<XR, NT, WK, D, W_SYM8>, skinny_kernel<XR, NT, WK, D, W_ASYM8>,     \
         "skinny_xr" #XR "_nt" #NT "_wk" #WK "_d" #D                                      \
   }
 
@@ -703,7 +782,8 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
 
 hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                          const uint16_t* sp, const uint32_t* zp, uint16_t* Y, float* part,
-                         int* counters, int M, int N, int K, int group, hipStream_t st) {
+                         int* counters, int M, int N, int K, int group, hipStream_t st,
+                         const float* xscale) {
   (void)group;  // the repacked layout stores one scale row per 128-row block
   const Variant& v = kVariants[p.variant];
   KernelFn fn = p.mode == W_FP16     ? v.f16
@@ -713,10 +793,12 @@ hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                : p.mode == W_ASYM64 ? v.asym64
                : p.mode == W_SYMB   ? v.symb
                : p.mode == W_ASYMB  ? v.asymb
+               : p.mode == W_SYM8   ? v.sym8
+               : p.mode == W_ASYM8  ? v.asym8
                                     : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint4*>(w), sp, reinterpret_cast<const uint2*>(zp), Y,
-                     part, counters, M, N, K, p.splits, p.nblocks);
+                     part, counters, M, N, K, p.splits, p.nblocks, xscale);
   return hipGetLastError();
 }
 

@@ -796,7 +796,8 @@ const char* tiled_variant_name(int mode, int v) {
 }
 
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p) {
-  if ((!mode_dense4(mode) && mode != W_SP24 && mode != W_FP16) || mode_bf16(mode)) return -8;
+  if ((!mode_dense4(mode) && mode != W_SP24 && mode != W_FP16) || mode_bf16(mode) || mode_fp8(mode))
+    return -8;
   const bool f16 = mode == W_FP16;
   const TVariant* table = f16 ? kTiledF16 : kTiled;
   const int count = f16 ? kNumTiledF16 : kNumTiled;

@@ -62,20 +62,23 @@ hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
 
 // Fused skinny GEMM.  `part` / `counters` form the split-K workspace.
 // weight format of a launch; the *64 modes are the same formats with groups of 64 rows,
-// the *B modes take bf16 activations and write bf16 outputs (skinny kernel only)
+// the *B modes take bf16 activations and write bf16 outputs, the *8 modes take fp8
+// (OCP E4M3) activations with an optional fp32 scale per row and write fp16 outputs
+// (both skinny kernel only)
 enum WMode {
   W_SYM = 0, W_ASYM = 1, W_FP16 = 2, W_SP24 = 3, W_SYM64 = 4, W_ASYM64 = 5, W_SYMB = 6,
-  W_ASYMB = 7
+  W_ASYMB = 7, W_SYM8 = 8, W_ASYM8 = 9
 };
 __host__ __device__ constexpr bool mode_asym(int m) {
-  return m == W_ASYM || m == W_ASYM64 || m == W_ASYMB;
+  return m == W_ASYM || m == W_ASYM64 || m == W_ASYMB || m == W_ASYM8;
 }
 __host__ __device__ constexpr bool mode_g64(int m) { return m == W_SYM64 || m == W_ASYM64; }
 __host__ __device__ constexpr bool mode_bf16(int m) { return m == W_SYMB || m == W_ASYMB; }
+__host__ __device__ constexpr bool mode_fp8(int m) { return m == W_SYM8 || m == W_ASYM8; }
 // packed 4-bit codes with scales (and zero-points): the dense repacked formats
 __host__ __device__ constexpr bool mode_dense4(int m) {
   return m == W_SYM || m == W_ASYM || m == W_SYM64 || m == W_ASYM64 || m == W_SYMB ||
-         m == W_ASYMB;
+         m == W_ASYMB || m == W_SYM8 || m == W_ASYM8;
 }
 struct SkinnyPlan {
   int variant;   // index into the variant table
@@ -94,9 +97,12 @@ const char* skinny_variant_name(int v);
 int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int splits,
                      SkinnyPlan* p);
 // w: repacked codes (W_SYM / W_ASYM) or fp16 Wt[N][K] (W_FP16, sp = zp = NULL).
+// X holds fp8 codes (one byte per element) in the fp8 modes; xscale is their optional
+// per-row fp32 scale (NULL: 1), ignored by every other mode.
 hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                          const uint16_t* sp, const uint32_t* zp, uint16_t* Y, float* part,
-                         int* counters, int M, int N, int K, int group, hipStream_t st);
+                         int* counters, int M, int N, int K, int group, hipStream_t st,
+                         const float* xscale = nullptr);
 
 // Tiled GEMM for larger M (packed weights, dense or 2:4, and the fp16 baseline).  Tile geometry and the
 // data-parallel / stream-K work split are fixed by the plan.
