@@ -358,6 +358,91 @@ def bf16_leg(w4, torch):
     return dict(kernel="w4a16_gemm_bf16 vs w4a16_gemm (same weights)", runs=runs)
 
 
+def w4a8_leg(w4, torch):
+    """FP8 E4M3 activations with per-row fp32 scales (w4a8_gemm, skinny kernel for every M)
+    against fp16 activations (w4a16_gemm, automatic plan) on the same repacked weights:
+    decode shapes at M = 1 / 16 / 32 and a 70B-class layer at M = 16 / 64 / 256.  Seeded
+    synthetic inputs (activations quantized per row on the host); weights rotate over
+    copies totalling at least 512 MiB."""
+    rot = 512 << 20
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(18)
+    runs = []
+    for (K, N), Ms in [((4096, 4096), (1, 16, 32)), ((4096, 12288), (1, 16, 32)),
+                       ((11008, 4096), (1, 16, 32)), ((8192, 28672), (16, 64, 256))]:
+        q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
+                          generator=gen)
+        s = (torch.rand((K // 128, N), device="cuda", generator=gen) * 0.018 + 0.002).half()
+        pk = w4.alloc_packed(K, N, 128, False)
+        w4.w4a16_repack(q, s, None, *pk, K, N, 128)
+        n = max(2, -(-rot // (K * N // 2)))
+        copies = [pk] + [tuple(t.clone() if t is not None else None for t in pk) for _ in range(n - 1)]
+        for M in Ms:
+            x = torch.randn((M, K), device="cuda", generator=gen)
+            Xh = x.half()
+            a = (x.abs().amax(dim=1) / 448.0).float()
+            X8 = (x / a[:, None]).cpu().to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            th = time_rotated(torch, [lambda c=c: w4.w4a16_gemm(Xh, c[0], c[1], None, Y, M, N, K, 128)
+                                      for c in copies])
+            t8 = time_rotated(torch, [lambda c=c: w4.w4a8_gemm(X8, a, c[0], c[1], None, Y, M, N, K, 128)
+                                      for c in copies])
+            wb = K * N // 2 + 2 * (K // 128) * N
+            runs.append(dict(M=M, K=K, N=N, fp16_us=round(th * 1e6, 2), fp8_us=round(t8 * 1e6, 2),
+                             fp8_over_fp16_time=round(t8 / th, 3),
+                             fp8_weight_GBps=round(wb / t8 / 1e9, 1),
+                             fp8_TFLOPs=round(2.0 * M * N * K / t8 / 1e12, 1)))
+        del q, s, pk, copies
+        torch.cuda.empty_cache()
+    return dict(kernel="w4a8_gemm (E4M3 activations, v_mfma_f32_16x16x32_fp8_fp8) vs w4a16_gemm "
+                       "(same weights)", runs=runs)
+
+
+def offline_leg(w4, torch):
+    """The load-time kernels, timed apart from the GEMM (they run once per weight
+    matrix): w4a16_repack (codes + scales, and zero-points), w4a16_unpack, the 2:4
+    compress w4a16_sparse24_repack (its call includes the read-back of the 2:4 check, a
+    host synchronization) and the baseline's w4a16_dequant.  Bytes are what each reads
+    plus what it writes, once; the rate is set against the 8 TB/s HBM peak."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(19)
+    runs = []
+    for (K, N) in [(4096, 4096), (4096, 12288), (11008, 4096), (8192, 28672)]:
+        G = K // 128
+        q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
+                          generator=gen)
+        s = (torch.rand((G, N), device="cuda", generator=gen) * 0.018 + 0.002).half()
+        z = torch.randint(-2 ** 31, 2 ** 31 - 1, (G, N // 8), dtype=torch.int32, device="cuda",
+                          generator=gen)
+        pk = w4.alloc_packed(K, N, 128, False)
+        pz = w4.alloc_packed(K, N, 128, True)
+        qb = torch.empty_like(q)
+        sb = torch.empty_like(s)
+        Wt = torch.empty((N, K), dtype=torch.float16, device="cuda")
+        q24 = q & torch.tensor(0x00FF00FF, dtype=torch.int32, device="cuda")  # 2 of 4 nibbles = 0...
+        q24 = q24 | torch.tensor(0x88008800 - (1 << 32), dtype=torch.int32, device="cuda")  # ...to code 8
+        sv = w4.alloc_sparse24(K, N, 128)
+        kn2, gn2 = K * N // 2, 2 * G * N
+        items = [
+            ("w4a16_repack", lambda: w4.w4a16_repack(q, s, None, *pk, K, N, 128), 2 * (kn2 + gn2)),
+            ("w4a16_repack_zero_points", lambda: w4.w4a16_repack(q, s, z, *pz, K, N, 128),
+             2 * (kn2 + gn2 + G * N // 2)),
+            ("w4a16_unpack", lambda: w4.w4a16_unpack(*pk, qb, sb, None, K, N, 128), 2 * (kn2 + gn2)),
+            ("w4a16_dequant", lambda: w4.w4a16_dequant(q, s, None, Wt, K, N, 128), kn2 + gn2 + 2 * K * N),
+            ("w4a16_sparse24_repack", lambda: w4.w4a16_sparse24_repack(q24, s, *sv, K, N, 128),
+             kn2 + gn2 + K * N // 4 + K * N // 8 + gn2),
+        ]
+        for name, fn, nbytes in items:
+            t = time_rotated(torch, [fn], min_reps=10)
+            runs.append(dict(kernel=name, K=K, N=N, us=round(t * 1e6, 2), bytes=nbytes,
+                             GBps=round(nbytes / t / 1e9, 1),
+                             frac_of_hbm_peak=round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 3)))
+        del q, s, z, pk, pz, qb, sb, Wt, q24, sv
+        torch.cuda.empty_cache()
+    return dict(note="load-time kernels (once per weight matrix), not part of the GEMM metric",
+                runs=runs)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -598,10 +683,12 @@ def main():
     if not args.no_configs:
         sparse24, asym = config_legs(w4, torch, group)
 
-    group64 = bf16 = None
+    group64 = bf16 = fp8 = offline = None
     if not args.no_configs:
         group64 = group64_leg(w4, torch)
         bf16 = bf16_leg(w4, torch)
+        fp8 = w4a8_leg(w4, torch)
+        offline = offline_leg(w4, torch)
 
     # ---- CPU oracle on this host over one step (bounded sample) -----------------------
     cpu = None
@@ -672,6 +759,8 @@ def main():
         "asym_zero_point": asym,
         "group64": group64,
         "bf16_activations": bf16,
+        "w4a8_fp8_activations": fp8,
+        "load_time_kernels": offline,
         "per_launch_us": [[p["M"], p["K"], p["N"], p["us"]] for p in per_launch],
     }
     if args.detail:
