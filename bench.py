@@ -39,6 +39,24 @@ def algorithmic(M, K, N, group=128):
     return wbytes, wbytes + 2 * M * K + 2 * M * N, 2 * M * N * K
 
 
+def roof(M, K, N, t, group=128, sparse=False, zero_points=False):
+    """Which roofline bounds one GEMM and the fraction of it reached in t seconds:
+    t_mem = algorithmic bytes / 8 TB/s, t_mfma = algorithmic flops / fp16 dense peak
+    (2:4: M*N*K useful flops; zero-points add K*N/256 weight bytes)."""
+    wb, ab, fl = algorithmic(M, K, N, group)
+    if zero_points:
+        wb += K * N // 256
+        ab += K * N // 256
+    if sparse:
+        wb = K * N // 4 + K * N // 8 + 2 * (K // group) * N
+        ab = wb + 2 * M * K + 2 * M * N
+        fl = M * N * K
+    t_mem = ab / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = fl / (FP16_PEAK_TFLOPS * 1e12)
+    return dict(bound="hbm" if t_mem >= t_mfma else "mfma",
+                roofline_frac=round(max(t_mem, t_mfma) / t, 4))
+
+
 def kernel_sha():
     h = hashlib.sha256()
     for f in ("gemm_skinny.hip", "internal.h"):
@@ -118,7 +136,7 @@ def large_m_sweep(w4, torch, group):
     0.01], X ~ N(0,1)), generated on the device; each shape is timed over back-to-back
     launches after a warmup."""
     shapes = [(8192, 28672), (28672, 8192), (8192, 10240)]
-    Ms = [256, 1024, 4096]
+    Ms = [16, 64, 256, 1024, 4096]
     gen = torch.Generator(device="cuda")
     gen.manual_seed(2024)
     out = []
@@ -156,29 +174,41 @@ def large_m_sweep(w4, torch, group):
         Wt = torch.empty((N, K), dtype=torch.float16, device="cuda")
         w4.w4a16_dequant(q, s, None, Wt, K, N, group)
         del q
+        # the memory-bound runs (M = 16, 64) rotate over weight copies totalling at least
+        # 512 MiB, so that no launch finds its weights in the 256 MiB Infinity Cache
+        ncop = max(2, -(-(512 << 20) // (K * N // 2)))
+        copies = [(wp, sp)] + [(wp.clone(), sp.clone()) for _ in range(ncop - 1)]
         for M in Ms:
             X = torch.randn((M, K), device="cuda", generator=gen).half()
             Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
             fl = 2.0 * M * N * K
             reps = max(3, min(50, int(2e13 / fl)))
-            t = timed(lambda: w4.w4a16_gemm(X, wp, sp, None, Y, M, N, K, group), reps)
+            if M < 256:
+                t = time_rotated(torch, [lambda c=c: w4.w4a16_gemm(X, c[0], c[1], None, Y, M, N, K,
+                                                                   group) for c in copies])
+            else:
+                t = timed(lambda: w4.w4a16_gemm(X, wp, sp, None, Y, M, N, K, group), reps)
             tb = timed(lambda: w4.w4a16_fp16_gemm(X, Wt, Y, M, N, K), reps)
             tt = timed(lambda: torch.nn.functional.linear(X, Wt), reps)
             plan = w4.w4a16_gemm_describe(M, N, K, group)
+            wbytes = algorithmic(M, K, N, group)[0]
             out.append(dict(M=M, K=K, N=N, us=round(t * 1e6, 2), TFLOPs=round(fl / t / 1e12, 1),
+                            weight_GBps=round(wbytes / t / 1e9, 1), **roof(M, K, N, t, group),
                             mfma_frac=round(fl / t / 1e12 / FP16_PEAK_TFLOPS, 4),
                             frac_of_mfma_probe=round(fl / t / 1e12 / mfma_probe, 4),
                             plan=plan["name"],
                             fp16_baseline_TFLOPs=round(fl / tb / 1e12, 1),
                             torch_fp16_TFLOPs=round(fl / tt / 1e12, 1)))
             del X, Y
-        del wp, sp, s, Wt
+        del wp, sp, s, Wt, copies
     torch.cuda.synchronize()
     big = [r for r in out if r["M"] >= 1024]
+    small = [r for r in out if r["M"] <= 32]
     return dict(peak_TFLOPs=FP16_PEAK_TFLOPS, unit="TFLOP/s",
                 mfma_probe_TFLOPs=round(mfma_probe, 1),
                 min_mfma_frac_M_ge_1024=min(r["mfma_frac"] for r in big),
                 mean_mfma_frac_M_ge_1024=round(sum(r["mfma_frac"] for r in big) / len(big), 4),
+                mean_hbm_frac_M_le_32=round(sum(r["roofline_frac"] for r in small) / len(small), 4),
                 runs=out)
 
 
@@ -242,6 +272,8 @@ def config_legs(w4, torch, group):
         sp_runs.append(dict(M=M, K=K, N=N, dense_us=round(td * 1e6, 2), sparse_us=round(ts * 1e6, 2),
                             speedup=round(td / ts, 3),
                             sparse_weight_GBps=round(sbytes / ts / 1e9, 1),
+                            sparse_roofline=roof(M, K, N, ts, group, sparse=True),
+                            dense_roofline=roof(M, K, N, td, group),
                             dense_plan=w4.w4a16_gemm_describe(M, N, K, group)["name"]))
     del cache
     torch.cuda.empty_cache()
@@ -271,11 +303,27 @@ def config_legs(w4, torch, group):
         wb = K * N // 2 + 2 * (K // group) * N + (K // group) * N // 2
         as_runs.append(dict(M=M, K=K, N=N, us=round(t * 1e6, 2),
                             TFLOPs=round(2.0 * M * N * K / t / 1e12, 2),
-                            weight_GBps=round(wb / t / 1e9, 1),
+                            weight_GBps=round(wb / t / 1e9, 1), **roof(M, K, N, t, group, zero_points=True),
                             plan=w4.w4a16_gemm_describe(M, N, K, group)["name"]))
     del cache
     torch.cuda.empty_cache()
-    return sp, dict(kernel="w4a16_gemm with 4-bit zero-points", runs=as_runs)
+    (w,) = config_runs(0)
+    d = weights(w)
+    pk = w4.alloc_packed(w.K, w.N, group, False)
+    w4.w4a16_repack(torch.from_numpy(d["Qp"]).cuda(), torch.from_numpy(d["s"]).cuda(), None,
+                    *pk, w.K, w.N, group)
+    copies = [pk] + [tuple(t.clone() if t is not None else None for t in pk) for _ in range(63)]
+    X = torch.from_numpy(activations(w)).cuda()
+    Y = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    t = time_rotated(torch, [lambda c=c: w4.w4a16_gemm(X, c[0], c[1], None, Y, w.M, w.N, w.K, group)
+                             for c in copies])
+    tiny = dict(M=w.M, K=w.K, N=w.N, us=round(t * 1e6, 2),
+                TFLOPs=round(2.0 * w.M * w.N * w.K / t / 1e12, 2),
+                weight_GBps=round(algorithmic(w.M, w.K, w.N, group)[0] / t / 1e9, 1),
+                **roof(w.M, w.K, w.N, t, group),
+                plan=w4.w4a16_gemm_describe(w.M, w.N, w.K, group)["name"])
+    del copies, pk
+    return sp, dict(kernel="w4a16_gemm with 4-bit zero-points", runs=as_runs), tiny
 
 
 def group64_leg(w4, torch):
@@ -679,9 +727,9 @@ def main():
         large = large_m_sweep(w4, torch, group)
 
     # ---- 2:4 sparse vs dense on the same pruned weights; zero-point workload ---------
-    sparse24 = asym = None
+    sparse24 = asym = tiny = None
     if not args.no_configs:
-        sparse24, asym = config_legs(w4, torch, group)
+        sparse24, asym, tiny = config_legs(w4, torch, group)
 
     group64 = bf16 = fp8 = offline = None
     if not args.no_configs:
@@ -757,11 +805,15 @@ def main():
         "large_m_sweep": large,
         "sparse24_vs_dense": sparse24,
         "asym_zero_point": asym,
+        "tiny_config": tiny,
         "group64": group64,
         "bf16_activations": bf16,
         "w4a8_fp8_activations": fp8,
         "load_time_kernels": offline,
         "per_launch_us": [[p["M"], p["K"], p["N"], p["us"]] for p in per_launch],
+        "decode_runs": [dict(M=p["M"], K=p["K"], N=p["N"], us=p["us"], weight_GBps=p["weight_GBps"],
+                             TFLOPs=p["TFLOPs"], bound="hbm", roofline_frac=p["hbm_frac"],
+                             plan=p["plan"]) for p in per_launch],
     }
     if args.detail:
         with open(args.detail, "w") as f:
