@@ -203,11 +203,11 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
 
 /* ---- bf16 activations ---------------------------------------------------------------
  * w4a16_gemm_bf16: Y (device, out) bf16 [M][N] = X (device, in) bf16 [M][K] * dequant(W),
- *   same repacked weights and rules as w4a16_gemm except: group is a multiple of 128
- *   (W4A16_ERR_SHAPE for 64), and every M runs on the skinny kernel.  The weights enter
- *   the bf16 matrix instructions as the exact integers 128 + q; the offset 128 + z is
- *   removed and the scale applied in fp32 per 128-row block, and Y is rounded once to
- *   bf16 (nearest-even).  Bitwise reproducible like w4a16_gemm.
+ *   same repacked weights and rules as w4a16_gemm (groups of 64 rows included) except
+ *   that every M runs on the skinny kernel.  The weights enter the bf16 matrix
+ *   instructions as the exact integers 128 + q; the offset 128 + z is removed and the
+ *   scale applied in fp32 per 128-row block (per 64-row half for groups of 64), and Y is
+ *   rounded once to bf16 (nearest-even).  Bitwise reproducible like w4a16_gemm.
  * w4a16_gemm_bf16_plan: the same with an explicit skinny variant (< the number of
  *   "skinny_*" variants of w4a16_gemm_variants) and `splits` as in w4a16_gemm_plan. */
 int w4a16_gemm_bf16(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
@@ -225,13 +225,14 @@ int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, 
  *   xscale (device, in)  fp32 [M], the scale a[m] of activation row m, or NULL for 1;
  *          4-byte aligned (W4A16_ERR_ALIGN otherwise);
  *   wp, sp, zp           the repacked weights of w4a16_repack (zp NULL: symmetric, z = 8);
- *   group  a multiple of 128 dividing K (W4A16_ERR_SHAPE for 64).
+ *   group  as for w4a16_gemm: 64, or a multiple of 128 dividing K.
  *   Every other rule (shapes, 16-byte alignment of X8, wp, sp, zp and Y, error codes,
  *   asynchronous execution on `stream`, library-owned split-K workspace, Y fully
  *   overwritten) is that of w4a16_gemm.  Every M runs on the skinny kernel.  The
  *   weights enter v_mfma_f32_16x16x32_fp8_fp8 as the exact E4M3 integers q - z, the
- *   scale s applies in fp32 per 128-row block, a[m] in fp32 before the one rounding of
- *   Y to fp16 (nearest-even).  Bitwise reproducible like w4a16_gemm.
+ *   scale s applies in fp32 per 128-row block (per 64-row half for groups of 64), and
+ *   a[m] in fp32 before the one rounding of Y to fp16 (nearest-even).  Bitwise
+ *   reproducible like w4a16_gemm.
  * w4a8_gemm_plan: the same with an explicit skinny variant (< the number of "skinny_*"
  *   variants of w4a16_gemm_variants) and `splits` as in w4a16_gemm_plan. */
 int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,

@@ -200,7 +200,7 @@ def test_bf16_validation(raw):
     f = raw.w4a16_gemm_bf16_plan
     f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
     assert f(None, A, A, None, A, 16, 1024, 1024, 128, -1, 0, None) == -1
-    assert f(A, A, A, None, A, 16, 1024, 1024, 64, -1, 0, None) == -2   # groups of 64: fp16 only
+    assert f(A, A, A, None, A, 16, 1024, 1024, 192, -1, 0, None) == -2  # not 64 nor 128j
     assert f(A, A, A, None, A, 16, 1000, 1024, 128, -1, 0, None) == -2
     raw.w4a16_gemm_variant_name.restype = ctypes.c_char_p
     nskinny = sum(1 for v in range(raw.w4a16_gemm_variants())
@@ -214,7 +214,7 @@ def test_w4a8_validation(raw):
     f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
     assert f(None, None, A, A, None, A, 16, 1024, 1024, 128, -1, 0, None) == -1
     assert f(A, None, A, None, None, A, 16, 1024, 1024, 128, -1, 0, None) == -1  # no scales
-    assert f(A, None, A, A, None, A, 16, 1024, 1024, 64, -1, 0, None) == -2   # groups of 64
+    assert f(A, None, A, A, None, A, 16, 1024, 1024, 192, -1, 0, None) == -2  # not 64 nor 128j
     assert f(A, None, A, A, None, A, 16, 1000, 1024, 128, -1, 0, None) == -2
     assert f(A, None, A, A, None, A, 0, 1024, 1024, 128, -1, 0, None) == -2
     assert f(MIS, None, A, A, None, A, 16, 1024, 1024, 128, -1, 0, None) == -3

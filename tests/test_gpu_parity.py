@@ -597,20 +597,21 @@ def _f32_bf16_rne(x: np.ndarray) -> np.ndarray:
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-def _case_bf16(M, K, N, asym=False, seed=0):
+def _case_bf16(M, K, N, asym=False, seed=0, group=128):
     from gen import activations_bf16
-    w = Workload(cfg=9, M=M, K=K, N=N, asym=asym)
+    w = Workload(cfg=9, M=M, K=K, N=N, asym=asym, group=group)
     d = weights(w, seed=5000 + seed + K + N)
     bits, vals = activations_bf16(w, seed=6000 + seed + M)
     return w, d, bits, vals
 
 
-def _gemm_bf16(gh, Xbits, packed, M, N, K, variant=-1, splits=0):
+def _gemm_bf16(gh, Xbits, packed, M, N, K, variant=-1, splits=0, group=128):
     import torch
     import w4a16_mixed_precision_offline_amd as w4
     wp, sp, zp = packed
     Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
-    w4.w4a16_gemm_bf16_plan(gh.dev(Xbits.view(np.int16)), wp, sp, zp, Y, M, N, K, 128, variant, splits)
+    w4.w4a16_gemm_bf16_plan(gh.dev(Xbits.view(np.int16)), wp, sp, zp, Y, M, N, K, group, variant,
+                            splits)
     return gh.host(Y).view(np.uint16)
 
 
@@ -667,3 +668,40 @@ def test_bf16_full_size(gh, M, K, N, asym):
     Yref, B = oracle.gemm_sampled(vals, d["Qp"], d["s"], d["Zp"], 128, rows, cols)
     ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, B, rel_fro=BF16_FRO)
     assert ok, info
+
+
+@pytest.mark.parametrize("M,K,N,asym", [(5, 1152, 528, True), (33, 2048, 1040, False),
+                                        (16, 4096, 11008, True)])
+def test_bf16_groups_of_64(gh, M, K, N, asym):
+    """bf16 activations with groups of 64 rows: activation sums, offsets and scales per
+    64-row half; automatic plan and a spread of explicit variants and K splits."""
+    _, d, bits, vals = _case_bf16(M, K, N, asym, group=64)
+    packed = gh.repack(d, K, N, 64)
+    Yref = oracle.gemm(vals, d["Qp"], d["s"], d["Zp"], 64)
+    B = oracle.error_bound(vals, d["Qp"], d["s"], d["Zp"], 64)
+    plans = [(-1, 0), (gh.variant_index("skinny_xr4_nt1_wk8_d4"), 3),
+             (gh.variant_index("skinny_xr16_nt2_wk8_d2"), 1),
+             (gh.variant_index("skinny_xr32_nt1_wk4_d2"), 2),
+             (gh.variant_index("skinny_xr64_nt1_wk4_d2"), 1)]
+    for v, splits in plans:
+        if v >= 0 and N % (16 * int(gh.w4.w4a16_gemm_variant_name(v).split("_nt")[1].split("_")[0])):
+            continue  # this variant's column tiles do not divide N
+        Y = _bf16_f32(_gemm_bf16(gh, bits, packed, M, N, K, v, splits, group=64))
+        ok, info = oracle.accept(Y, Yref, B, rel_fro=BF16_FRO)
+        assert ok, (v, splits, info)
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_bf16_groups_of_64_onehot_exact(gh, asym):
+    """One-hot bf16 rows with groups of 64 select RNE_bf16((q - z) * s) bit for bit."""
+    M, K, N = 16, 1024, 768
+    _, d, _, _ = _case_bf16(M, K, N, asym, group=64)
+    ks = [0, 1, 7, 8, 9, 63, 64, 127, 128, 255, 300, 511, 640, 777, 900, 1023]
+    bits = np.zeros((M, K), np.uint16)
+    bits[np.arange(M), ks] = 0x3F80  # 1.0
+    W = oracle.dequant(d["Qp"], d["s"], d["Zp"], K, N, 64)
+    exp = _f32_bf16_rne(W[ks].astype(np.float32))
+    packed = gh.repack(d, K, N, 64)
+    for nm, splits in [("skinny_xr16_nt1_wk8_d2", 1), ("skinny_xr16_nt4_wk4_d2", 3)]:
+        Y = _gemm_bf16(gh, bits, packed, M, N, K, gh.variant_index(nm), splits, group=64)
+        assert np.array_equal(Y, exp), nm

@@ -22,14 +22,14 @@ def gh(lib):
     return gpu_helpers
 
 
-def _case(M, K, N, asym=False, seed=0, cfg=9):
-    w = Workload(cfg=cfg, M=M, K=K, N=N, asym=asym)
+def _case(M, K, N, asym=False, seed=0, cfg=9, group=128):
+    w = Workload(cfg=cfg, M=M, K=K, N=N, asym=asym, group=group)
     d = weights(w, seed=7000 + seed + K + N)
     X8, a = activations_fp8(w, seed=8000 + seed + M)
     return d, X8, a
 
 
-def _gemm8(gh, X8, a, packed, M, N, K, variant=-1, splits=0, rows_alloc=None):
+def _gemm8(gh, X8, a, packed, M, N, K, variant=-1, splits=0, rows_alloc=None, group=128):
     """Run w4a8_gemm(_plan); Y is the first M rows of a NaN-filled buffer of
     rows_alloc rows so that writes past row M-1 show up.  Returns (Y[:M], whole)."""
     import w4a16_mixed_precision_offline_amd as w4
@@ -39,19 +39,19 @@ def _gemm8(gh, X8, a, packed, M, N, K, variant=-1, splits=0, rows_alloc=None):
     x = gh.dev(X8)
     s = gh.dev(a) if a is not None else None
     if variant == -1 and splits == 0:
-        w4.w4a8_gemm(x, s, wp, sp, zp, Y, M, N, K, 128)
+        w4.w4a8_gemm(x, s, wp, sp, zp, Y, M, N, K, group)
     else:
-        w4.w4a8_gemm_plan(x, s, wp, sp, zp, Y, M, N, K, 128, variant, splits)
+        w4.w4a8_gemm_plan(x, s, wp, sp, zp, Y, M, N, K, group, variant, splits)
     whole = gh.host(Yall)
     return whole[:M], whole
 
 
-def _accept(Y, X8, a, d, rows=None, cols=None):
+def _accept(Y, X8, a, d, rows=None, cols=None, group=128):
     if rows is None:
-        Yref = oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 128)
-        B = oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 128)
+        Yref = oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], group)
+        B = oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], group)
         return oracle.accept(Y, Yref, B)
-    Yref, B = oracle.gemm_w4a8_sampled(X8, a, d["Qp"], d["s"], d["Zp"], 128, rows, cols)
+    Yref, B = oracle.gemm_w4a8_sampled(X8, a, d["Qp"], d["s"], d["Zp"], group, rows, cols)
     return oracle.accept(Y[np.ix_(rows, cols)], Yref, B)
 
 
@@ -60,23 +60,24 @@ def _sample_idx(rng, n, k):
     return sorted(idx)
 
 
+@pytest.mark.parametrize("group", [128, 64])
 @pytest.mark.parametrize("asym", [False, True])
-def test_w4a8_onehot_exact(gh, asym):
+def test_w4a8_onehot_exact(gh, asym, group):
     """x8 = 1.0 (code 0x38) at one k per row and a power-of-two row scale select
     RNE_fp16(a * (q - z) * s) bit for bit: the fp8 weights are the exact integers q - z
     and a single term is exact in fp32."""
     M, K, N = 16, 1024, 768
-    d, _, _ = _case(M, K, N, asym)
-    ks = [0, 1, 7, 8, 9, 127, 128, 255, 300, 511, 512, 640, 777, 900, 1022, 1023]
+    d, _, _ = _case(M, K, N, asym, group=group)
+    ks = [0, 1, 7, 8, 9, 63, 64, 127, 128, 255, 300, 511, 640, 777, 900, 1023]
     X8 = np.zeros((M, K), np.uint8)
     X8[np.arange(M), ks] = 0x38
     a = np.array([2.0 ** ((m % 5) - 2) for m in range(M)], dtype=np.float32)
-    W = oracle.dequant(d["Qp"], d["s"], d["Zp"], K, N, 128)       # exact (q - z) * s
+    W = oracle.dequant(d["Qp"], d["s"], d["Zp"], K, N, group)     # exact (q - z) * s
     exp = (W[ks] * a[:, None].astype(np.float64)).astype(np.float16)  # exact, one rounding
-    packed = gh.repack(d, K, N)
+    packed = gh.repack(d, K, N, group)
     for nm, splits in [("skinny_xr16_nt1_wk8_d2", 1), ("skinny_xr16_nt4_wk4_d2", 3),
                        ("skinny_xr16_nt2_wk8_d2", 2), ("skinny_xr16_nt3_wk4_d2", 1)]:
-        Y, _ = _gemm8(gh, X8, a, packed, M, N, K, gh.variant_index(nm), splits)
+        Y, _ = _gemm8(gh, X8, a, packed, M, N, K, gh.variant_index(nm), splits, group=group)
         assert np.array_equal(Y.view(np.uint16), exp.view(np.uint16)), nm
 
 
@@ -183,3 +184,25 @@ def test_w4a8_large_layers(gh, M, K, N):
     rng = np.random.default_rng(M + N)
     ok, info = _accept(Y, X8, a, d, _sample_idx(rng, M, 24), _sample_idx(rng, N, 48))
     assert ok, info
+
+
+@pytest.mark.parametrize("M,K,N,asym", [(5, 1152, 528, True), (33, 2048, 1040, False),
+                                        (16, 4096, 11008, True)])
+def test_w4a8_groups_of_64(gh, M, K, N, asym):
+    """Groups of 64 rows: two scale (and zero-point) rows per 128-row block, one fp32
+    partial per half; automatic plan and a spread of explicit variants and K splits."""
+    d, X8, a = _case(M, K, N, asym, group=64)
+    packed = gh.repack(d, K, N, 64)
+    Yref = oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 64)
+    B = oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 64)
+    plans = [(-1, 0), (gh.variant_index("skinny_xr4_nt1_wk8_d4"), 3),
+             (gh.variant_index("skinny_xr16_nt2_wk8_d2"), 1),
+             (gh.variant_index("skinny_xr32_nt1_wk4_d2"), 2),
+             (gh.variant_index("skinny_xr64_nt1_wk4_d2"), 1)]
+    for v, splits in plans:
+        if v >= 0 and N % (16 * int(gh.w4.w4a16_gemm_variant_name(v).split("_nt")[1].split("_")[0])):
+            continue  # this variant's column tiles do not divide N
+        Y, whole = _gemm8(gh, X8, a, packed, M, N, K, v, splits, rows_alloc=M + 2, group=64)
+        ok, info = oracle.accept(Y, Yref, B)
+        assert ok, (v, splits, info)
+        assert np.all(np.isnan(whole[M:]))

@@ -463,10 +463,9 @@ int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, 
                          void* stream) {
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
-  if (group == 64) return W4A16_ERR_SHAPE;  // bf16: groups of 128 rows or more
   if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
-  return run_skinny(zp ? W_ASYMB : W_SYMB, X, wp, sp, zp, Y, M, N, K, group, variant, splits,
-                    stream);
+  const int mode = group == 64 ? (zp ? W_ASYMB64 : W_SYMB64) : (zp ? W_ASYMB : W_SYMB);
+  return run_skinny(mode, X, wp, sp, zp, Y, M, N, K, group, variant, splits, stream);
 }
 
 int w4a16_gemm_bf16(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
@@ -481,11 +480,10 @@ int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const
   const uint16_t* X = reinterpret_cast<const uint16_t*>(X8);
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
-  if (group == 64) return W4A16_ERR_SHAPE;  // fp8 activations: groups of 128 rows or more
   if (xscale && (reinterpret_cast<uintptr_t>(xscale) & 3u) != 0) return W4A16_ERR_ALIGN;
   if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
-  return run_skinny(zp ? W_ASYM8 : W_SYM8, X, wp, sp, zp, Y, M, N, K, group, variant, splits,
-                    stream, xscale);
+  const int mode = group == 64 ? (zp ? W_ASYM8G64 : W_SYM8G64) : (zp ? W_ASYM8 : W_SYM8);
+  return run_skinny(mode, X, wp, sp, zp, Y, M, N, K, group, variant, splits, stream, xscale);
 }
 
 int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,

@@ -223,6 +223,31 @@ __device__ __forceinline__ void load_stage(Stage<XR, NT, MODE>& S, int kb, bool 
     S.x[c] = bload16<false>(R.x, xoff[c], (uint32_t)kb * KBLK * x_elem_bytes(MODE));
 }
 
+// The lane's column's zero-point code (8 when symmetric) and fp32 scale for half h of
+// column tile t (h = 0 unless the groups are 64 rows: then words j = 2h, 2h + 1 of the
+// block belong to half h).
+template <int XR, int NT, int MODE>
+__device__ __forceinline__ int zero_code(const Stage<XR, NT, MODE>& S, int t, int h, int lane) {
+  if constexpr (!mode_asym(MODE)) {
+    return 8;
+  } else {
+    const int c = lane & 15;
+    uint32_t zw;
+    if constexpr (mode_g64(MODE))
+      zw = h == 0 ? (c < 8 ? S.z64[t].x : S.z64[t].y) : (c < 8 ? S.z64[t].z : S.z64[t].w);
+    else
+      zw = c < 8 ? S.z[t].x : S.z[t].y;
+    return (int)((zw >> (4 * (c & 7))) & 15u);
+  }
+}
+template <int XR, int NT, int MODE>
+__device__ __forceinline__ float block_scale(const Stage<XR, NT, MODE>& S, int t, int h) {
+  if constexpr (mode_g64(MODE))
+    return (float)__builtin_bit_cast(half2v, S.s64[t])[h];
+  else
+    return (float)__builtin_bit_cast(_Float16, S.s[t]);
+}
+
 // Compute one k-block: lay the X rows into the wave's LDS tile, read them back as
 // MFMA fragments (lane l: row 16mt + l%16, 8 halves at 32j + 8(l/16)), dequantize
 // the codes and run the four MFMAs per (row tile, column tile).
@@ -246,30 +271,35 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
       for (int j = 0; j < 4; ++j)
         a8[mt][j] = *reinterpret_cast<const long*>(xlds + (mt * 16 + (lane & 15)) * XSTRIDE +
                                                     32 * j + 8 * (lane >> 4));
+    constexpr int SH = mode_g64(MODE) ? 2 : 1;  // scale / zero-point halves per block
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      int zq = 8;
-      if constexpr (mode_asym(MODE)) {
-        const int c = lane & 15;
-        const uint32_t zw = c < 8 ? S.z[t].x : S.z[t].y;
-        zq = (int)((zw >> (4 * (c & 7))) & 15u);
+      half2v c0[SH], c1[SH];
+      float sc[SH];
+#pragma unroll
+      for (int h = 0; h < SH; ++h) {
+        const int zq = zero_code(S, t, h, lane);
+        const _Float16 a0 = (_Float16)(float)(-1024 - zq);
+        const _Float16 a1 = (_Float16)(float)(-64 - zq);
+        c0[h] = half2v{a0, a0};
+        c1[h] = half2v{a1, a1};
+        sc[h] = block_scale(S, t, h);
       }
-      const _Float16 a0 = (_Float16)(float)(-1024 - zq);
-      const _Float16 a1 = (_Float16)(float)(-64 - zq);
-      const half2v c0 = {a0, a0}, c1 = {a1, a1};
       long b[4];
-      b[0] = (long)dequant_word_fp8(S.w[t][0].x, c0, c1, magic);
-      b[1] = (long)dequant_word_fp8(S.w[t][0].y, c0, c1, magic);
-      b[2] = (long)dequant_word_fp8(S.w[t][0].z, c0, c1, magic);
-      b[3] = (long)dequant_word_fp8(S.w[t][0].w, c0, c1, magic);
-      const float sc = (float)__builtin_bit_cast(_Float16, S.s[t]);
+      b[0] = (long)dequant_word_fp8(S.w[t][0].x, c0[0], c1[0], magic);
+      b[1] = (long)dequant_word_fp8(S.w[t][0].y, c0[0], c1[0], magic);
+      b[2] = (long)dequant_word_fp8(S.w[t][0].z, c0[SH - 1], c1[SH - 1], magic);
+      b[3] = (long)dequant_word_fp8(S.w[t][0].w, c0[SH - 1], c1[SH - 1], magic);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        float4v g = {0.f, 0.f, 0.f, 0.f};
+        // one fp32 partial per half (k-steps 0-1 and 2-3), each with its group's scale
+        float4v g[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          g = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8[mt][j], b[j], g, 0, 0, 0);
-        acc[t][mt] += sc * g;
+          g[SH == 2 ? j >> 1 : 0] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+              a8[mt][j], b[j], g[SH == 2 ? j >> 1 : 0], 0, 0, 0);
+        acc[t][mt] += sc[0] * g[0];
+        if constexpr (SH == 2) acc[t][mt] += sc[1] * g[1];
       }
     }
     return;
@@ -316,16 +346,20 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
     // sum of the activations over the block (one more matrix instruction per k-step
     // against ones) removes the offset: sum x (q - z) = sum x (128 + q) - (128 + z) sum x.
     // The weights stay exact integers and the scale applies in fp32, as in the fp16 path.
+    // With groups of 64 rows, everything is kept per half of the block (k-steps 0-1 and
+    // 2-3): activation sums, partial products, offsets and scales.
+    constexpr int SH = mode_g64(MODE) ? 2 : 1;
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
                                                          0x3F803F80u});
-    float4v xs[MT];
+    float4v xs[MT][SH];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      xs[mt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < SH; ++h) xs[mt][h] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][j]), ones,
-                                                          xs[mt], 0, 0, 0);
+        xs[mt][SH == 2 ? j >> 1 : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, a[mt][j]), ones, xs[mt][SH == 2 ? j >> 1 : 0], 0, 0, 0);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -334,22 +368,23 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
       b[1] = offset_codes_bf16(S.w[t][0].y);
       b[2] = offset_codes_bf16(S.w[t][0].z);
       b[3] = offset_codes_bf16(S.w[t][0].w);
-      int zq = 8;
-      if constexpr (mode_asym(MODE)) {
-        const int c = lane & 15;
-        const uint32_t zw = c < 8 ? S.z[t].x : S.z[t].y;
-        zq = (int)((zw >> (4 * (c & 7))) & 15u);
+      float off[SH], sc[SH];
+#pragma unroll
+      for (int h = 0; h < SH; ++h) {
+        off[h] = (float)(128 + zero_code(S, t, h, lane));
+        sc[h] = block_scale(S, t, h);
       }
-      const float off = (float)(128 + zq);
-      const float sc = (float)__builtin_bit_cast(_Float16, S.s[t]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        float4v g = {0.f, 0.f, 0.f, 0.f};
+        float4v g[SH];
+#pragma unroll
+        for (int h = 0; h < SH; ++h) g[h] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][j]), b[j], g,
-                                                       0, 0, 0);
-        acc[t][mt] += sc * (g - off * xs[mt]);
+          g[SH == 2 ? j >> 1 : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, a[mt][j]), b[j], g[SH == 2 ? j >> 1 : 0], 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < SH; ++h) acc[t][mt] += sc[h] * (g[h] - off[h] * xs[mt][h]);
       }
     }
     return;
@@ -662,7 +697,8 @@ typedef void (*KernelFn)(const uint16_t*, const uint4*, const uint16_t*, const u
 
 struct Variant {
   int XR, NT, WK, D;
-  KernelFn sym, asym, f16, sp24, sym64, asym64, symb, asymb, sym8, asym8;
+  KernelFn sym, asym, f16, sp24, sym64, asym64, symb, asymb, sym8, asym8, symb64, asymb64,
+      sym8g64, asym8g64;
   const char* name;
 };
 
@@ -673,6 +709,9 @@ struct Variant {
         skinny_kernel<XR, NT, WK, D, W_SYM64>, skinny_kernel<XR, NT, WK, D, W_ASYM64>,   \
         skinny_kernel<XR, NT, WK, D, W_SYMB>, skinny_kernel<XR, NT, WK, D, W_ASYMB>,     \
         skinny_kernel<XR, NT, WK, D, W_SYM8>, skinny_kernel<XR, NT, WK, D, W_ASYM8>,     \
+        skinny_kernel<XR, NT, WK, D, W_SYMB64>, skinny_kernel<XR, NT, WK, D, W_ASYMB64>, \
+        skinny_kernel<XR, NT, WK, D, W_SYM8G64>,                                         \
+        skinny_kernel<XR, NT, WK, D, W_ASYM8G64>,                                        \
         "skinny_xr" #XR "_nt" #NT "_wk" #WK "_d" #D                                      \
   }
 
@@ -795,6 +834,10 @@ hipError_t skinny_launch(const SkinnyPlan& p, const uint16_t* X, const void* w,
                : p.mode == W_ASYMB  ? v.asymb
                : p.mode == W_SYM8   ? v.sym8
                : p.mode == W_ASYM8  ? v.asym8
+               : p.mode == W_SYMB64 ? v.symb64
+               : p.mode == W_ASYMB64 ? v.asymb64
+               : p.mode == W_SYM8G64 ? v.sym8g64
+               : p.mode == W_ASYM8G64 ? v.asym8g64
                                     : v.sym;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint4*>(w), sp, reinterpret_cast<const uint2*>(zp), Y,

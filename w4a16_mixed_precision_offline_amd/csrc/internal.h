@@ -64,21 +64,29 @@ hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
 // weight format of a launch; the *64 modes are the same formats with groups of 64 rows,
 // the *B modes take bf16 activations and write bf16 outputs, the *8 modes take fp8
 // (OCP E4M3) activations with an optional fp32 scale per row and write fp16 outputs
-// (both skinny kernel only)
+// (both skinny kernel only); W_*B64 and W_*8G64 are those two with groups of 64 rows
 enum WMode {
   W_SYM = 0, W_ASYM = 1, W_FP16 = 2, W_SP24 = 3, W_SYM64 = 4, W_ASYM64 = 5, W_SYMB = 6,
-  W_ASYMB = 7, W_SYM8 = 8, W_ASYM8 = 9
+  W_ASYMB = 7, W_SYM8 = 8, W_ASYM8 = 9, W_SYMB64 = 10, W_ASYMB64 = 11, W_SYM8G64 = 12,
+  W_ASYM8G64 = 13
 };
 __host__ __device__ constexpr bool mode_asym(int m) {
-  return m == W_ASYM || m == W_ASYM64 || m == W_ASYMB || m == W_ASYM8;
+  return m == W_ASYM || m == W_ASYM64 || m == W_ASYMB || m == W_ASYM8 || m == W_ASYMB64 ||
+         m == W_ASYM8G64;
 }
-__host__ __device__ constexpr bool mode_g64(int m) { return m == W_SYM64 || m == W_ASYM64; }
-__host__ __device__ constexpr bool mode_bf16(int m) { return m == W_SYMB || m == W_ASYMB; }
-__host__ __device__ constexpr bool mode_fp8(int m) { return m == W_SYM8 || m == W_ASYM8; }
+__host__ __device__ constexpr bool mode_g64(int m) {
+  return m == W_SYM64 || m == W_ASYM64 || m == W_SYMB64 || m == W_ASYMB64 || m == W_SYM8G64 ||
+         m == W_ASYM8G64;
+}
+__host__ __device__ constexpr bool mode_bf16(int m) {
+  return m == W_SYMB || m == W_ASYMB || m == W_SYMB64 || m == W_ASYMB64;
+}
+__host__ __device__ constexpr bool mode_fp8(int m) {
+  return m == W_SYM8 || m == W_ASYM8 || m == W_SYM8G64 || m == W_ASYM8G64;
+}
 // packed 4-bit codes with scales (and zero-points): the dense repacked formats
 __host__ __device__ constexpr bool mode_dense4(int m) {
-  return m == W_SYM || m == W_ASYM || m == W_SYM64 || m == W_ASYM64 || m == W_SYMB ||
-         m == W_ASYMB || m == W_SYM8 || m == W_ASYM8;
+  return m != W_FP16 && m != W_SP24 && m >= 0 && m <= W_ASYM8G64;
 }
 struct SkinnyPlan {
   int variant;   // index into the variant table
