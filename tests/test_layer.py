@@ -19,6 +19,15 @@ def test_layer_rejects_bad_shapes_on_the_host():
     with pytest.raises(TypeError):
         W4A16Linear.from_quantized(torch.zeros((16, 64), dtype=torch.int64),
                                    torch.zeros((1, 64), dtype=torch.float16))
+    layer = W4A16Linear(128, 16, device="cpu")  # buffers only; forward never launches here
+    with pytest.raises(TypeError):
+        layer(torch.zeros((2, 128), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        layer(torch.zeros((2, 64), dtype=torch.float16))
+    with pytest.raises(ValueError):  # a row scale belongs to fp8 activations
+        layer(torch.zeros((2, 128), dtype=torch.float16), torch.ones(2))
+    with pytest.raises(ValueError):  # one fp32 scale per row
+        layer(torch.zeros((2, 128), dtype=torch.float8_e4m3fn), torch.ones(3))
 
 
 @pytest.mark.gpu
@@ -49,3 +58,31 @@ def test_layer_forward_matches_oracle(lib, group, asym):
         assert np.array_equal(z.cpu().numpy(), d["Zp"])
     # an empty batch is fine and launches nothing
     assert layer(torch.zeros((0, K), dtype=torch.float16, device="cuda")).shape == (0, N)
+
+
+@pytest.mark.gpu
+def test_layer_forward_bf16_and_fp8(lib):
+    """The same layer fed bf16 activations (bf16 out) and per-row-quantized FP8 E4M3
+    activations with their fp32 row scales (fp16 out)."""
+    import torch
+    from gen import activations_bf16, activations_fp8
+    from w4a16_mixed_precision_offline_amd.layer import W4A16Linear
+    K, N, group = 2048, 1040, 128
+    w = Workload(cfg=9, M=6, K=K, N=N, group=group, asym=True)
+    d = weights(w, seed=79)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    layer = W4A16Linear.from_quantized(dev(d["Qp"]), dev(d["s"]), dev(d["Zp"]), group=group)
+    bits, vals = activations_bf16(w, seed=80)
+    yb = layer(dev(bits.view(np.int16)).view(torch.bfloat16).reshape(2, 3, K))
+    assert yb.shape == (2, 3, N) and yb.dtype == torch.bfloat16
+    ok, info = oracle.accept(yb.reshape(6, N).float().cpu().numpy(),
+                             oracle.gemm(vals, d["Qp"], d["s"], d["Zp"], group),
+                             oracle.error_bound(vals, d["Qp"], d["s"], d["Zp"], group), rel_fro=4e-3)
+    assert ok, info
+    X8, a = activations_fp8(w, seed=81)
+    y8 = layer(dev(X8).view(torch.float8_e4m3fn).reshape(3, 2, K), dev(a).reshape(3, 2))
+    assert y8.shape == (3, 2, N) and y8.dtype == torch.float16
+    ok, info = oracle.accept(y8.reshape(6, N).cpu().numpy(),
+                             oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], group),
+                             oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], group))
+    assert ok, info

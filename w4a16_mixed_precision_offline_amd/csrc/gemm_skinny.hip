@@ -770,12 +770,16 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
     }
     if (XR == 4) {
       // one or two rows on a wide layer: eight waves per tile, two k-blocks in flight
-      // each (5% faster than four waves with four at M = 1 on 4096 x 11008 / 12288)
+      // each (5% faster than four waves with four at M = 1 on 4096 x 11008 / 12288);
+      // narrower layers: eight waves, four k-blocks in flight (timed over graph replays:
+      // 2-10% faster than sixteen waves with two on 11008 x 4096 at M = 1-4)
       variant = wide ? (M <= 2 ? find_variant(4, 1, 8, 2) : find_variant(4, 1, 4, 4))
-                     : (longk ? find_variant(4, 1, 16, 2) : find_variant(4, 1, 8, 4));
+                     : find_variant(4, 1, 8, 4);
     } else if (XR == 8) {
+      // narrow layers with few k-blocks per tile (4096 x 4096): four waves per tile
+      // (9% faster than eight over graph replays at M = 8)
       variant = wide ? (ntw == 2 ? find_variant(8, 2, 8, 4) : find_variant(8, ntw, 4, 2))
-                     : find_variant(8, 1, 8, 4);
+                     : (longk ? find_variant(8, 1, 8, 4) : find_variant(8, 1, 4, 4));
     } else if (XR == 16) {
       variant = wide ? (ntw == 2 ? find_variant(16, 2, 8, 2) : find_variant(16, ntw, 4, 2))
                      : find_variant(16, 1, 8, 2);

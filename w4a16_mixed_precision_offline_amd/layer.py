@@ -16,13 +16,18 @@ from __future__ import annotations
 
 import torch
 
-from . import (alloc_packed, w4a16_gemm, w4a16_packed_bytes, w4a16_repack, w4a16_unpack,
-               BUF_W)
+from . import (alloc_packed, w4a8_gemm, w4a16_gemm, w4a16_gemm_bf16, w4a16_packed_bytes,
+               w4a16_repack, w4a16_unpack, BUF_W)
 
 
 class W4A16Linear(torch.nn.Module):
-    """y = x @ W for fp16 x [..., in_features] and a group-quantized 4-bit W
-    [in_features, out_features] (w = (q - z) * s, z = 8 without zero-points)."""
+    """y = x @ W for x [..., in_features] and a group-quantized 4-bit W [in_features,
+    out_features] (w = (q - z) * s, z = 8 without zero-points).
+
+    x may be fp16 (y fp16, w4a16_gemm), bf16 (y bf16, w4a16_gemm_bf16) or already
+    quantized FP8 E4M3 (torch.float8_e4m3fn) with an optional fp32 scale per row
+    `xscale` of shape x.shape[:-1] (y fp16, w4a8_gemm: INT4 weights times FP8
+    activations, "Marlin", dingiv.github.io, section "CUTLASS W4A8（混合精度）")."""
 
     def __init__(self, in_features: int, out_features: int, group: int = 128,
                  zero_points: bool = False, device="cuda"):
@@ -65,18 +70,33 @@ class W4A16Linear(torch.nn.Module):
         w4a16_unpack(self.wp, self.sp, self.zp, q, s, z, K, N, g)
         return q, s, z
 
-    def forward(self, x: torch.Tensor) -> torch.Tensor:
-        if x.dtype != torch.float16:
-            raise TypeError(f"expected float16 activations, got {x.dtype}")
+    def forward(self, x: torch.Tensor, xscale: torch.Tensor | None = None) -> torch.Tensor:
+        fp8 = x.dtype == torch.float8_e4m3fn
+        if x.dtype not in (torch.float16, torch.bfloat16) and not fp8:
+            raise TypeError(f"expected float16, bfloat16 or float8_e4m3fn activations, got {x.dtype}")
         if x.shape[-1] != self.in_features:
             raise ValueError(f"last dimension {x.shape[-1]} != in_features {self.in_features}")
         lead = x.shape[:-1]
+        if xscale is not None:
+            if not fp8:
+                raise ValueError("xscale applies to float8_e4m3fn activations only")
+            if xscale.dtype != torch.float32 or tuple(xscale.shape) != tuple(lead):
+                raise ValueError(f"xscale must be float32 of shape {tuple(lead)}")
         x2 = x.reshape(-1, self.in_features).contiguous()
         M = x2.shape[0]
-        y = torch.empty((M, self.out_features), dtype=torch.float16, device=x.device)
+        y = torch.empty((M, self.out_features),
+                        dtype=torch.bfloat16 if x.dtype == torch.bfloat16 else torch.float16,
+                        device=x.device)
         if M > 0:
-            w4a16_gemm(x2, self.wp, self.sp, self.zp, y, M, self.out_features,
-                       self.in_features, self.group)
+            args = (self.wp, self.sp, self.zp, y, M, self.out_features, self.in_features,
+                    self.group)
+            if fp8:
+                a = None if xscale is None else xscale.reshape(-1).contiguous()
+                w4a8_gemm(x2, a, *args)
+            elif x.dtype == torch.bfloat16:
+                w4a16_gemm_bf16(x2, *args)
+            else:
+                w4a16_gemm(x2, *args)
         return y.reshape(*lead, self.out_features)
 
     def extra_repr(self) -> str:
