@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 FP16_PEAK_TFLOPS = 2516.6
+FP8_PEAK_TFLOPS = 5033.2  # dense fp8 matrix peak (twice fp16)
 ROTATE_BYTES = 1 << 30
 
 
@@ -417,7 +418,7 @@ def w4a8_leg(w4, torch):
     gen.manual_seed(18)
     runs = []
     for (K, N), Ms in [((4096, 4096), (1, 16, 32)), ((4096, 12288), (1, 16, 32)),
-                       ((11008, 4096), (1, 16, 32)), ((8192, 28672), (16, 64, 256))]:
+                       ((11008, 4096), (1, 16, 32)), ((8192, 28672), (16, 64, 256, 1024, 4096))]:
         q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
                           generator=gen)
         s = (torch.rand((K // 128, N), device="cuda", generator=gen) * 0.018 + 0.002).half()
@@ -436,14 +437,23 @@ def w4a8_leg(w4, torch):
             t8 = time_rotated(torch, [lambda c=c: w4.w4a8_gemm(X8, a, c[0], c[1], None, Y, M, N, K, 128)
                                       for c in copies])
             wb = K * N // 2 + 2 * (K // 128) * N
+            fl = 2.0 * M * N * K
+            # roofline of the fp8 path: weight + fp8 activation + fp16 output bytes at 8 TB/s
+            # against fp8 matrix work at the dense fp8 peak
+            t_mem = (wb + M * K + 2 * M * N) / (HBM_PEAK_GBPS * 1e9)
+            t_mfma = fl / (FP8_PEAK_TFLOPS * 1e12)
             runs.append(dict(M=M, K=K, N=N, fp16_us=round(th * 1e6, 2), fp8_us=round(t8 * 1e6, 2),
                              fp8_over_fp16_time=round(t8 / th, 3),
                              fp8_weight_GBps=round(wb / t8 / 1e9, 1),
-                             fp8_TFLOPs=round(2.0 * M * N * K / t8 / 1e12, 1)))
+                             fp8_TFLOPs=round(fl / t8 / 1e12, 1),
+                             bound="hbm" if t_mem >= t_mfma else "mfma_fp8",
+                             roofline_frac=round(max(t_mem, t_mfma) / t8, 4),
+                             plan=w4.w4a16_gemm_describe(M, N, K, 128)["name"]))
         del q, s, pk, copies
         torch.cuda.empty_cache()
-    return dict(kernel="w4a8_gemm (E4M3 activations, v_mfma_f32_16x16x32_fp8_fp8) vs w4a16_gemm "
-                       "(same weights)", runs=runs)
+    return dict(kernel="w4a8_gemm (E4M3 activations: skinny kernel v_mfma_f32_16x16x32_fp8_fp8, "
+                       "tiled kernel v_mfma_scale_f32_16x16x128_f8f6f4) vs w4a16_gemm (same weights)",
+                fp8_peak_TFLOPs=FP8_PEAK_TFLOPS, runs=runs)
 
 
 def offline_leg(w4, torch):

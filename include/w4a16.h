@@ -228,13 +228,17 @@ int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, 
  *   group  as for w4a16_gemm: 64, or a multiple of 128 dividing K.
  *   Every other rule (shapes, 16-byte alignment of X8, wp, sp, zp and Y, error codes,
  *   asynchronous execution on `stream`, library-owned split-K workspace, Y fully
- *   overwritten) is that of w4a16_gemm.  Every M runs on the skinny kernel.  The
- *   weights enter v_mfma_f32_16x16x32_fp8_fp8 as the exact E4M3 integers q - z, the
- *   scale s applies in fp32 per 128-row block (per 64-row half for groups of 64), and
- *   a[m] in fp32 before the one rounding of Y to fp16 (nearest-even).  Bitwise
- *   reproducible like w4a16_gemm.
- * w4a8_gemm_plan: the same with an explicit skinny variant (< the number of "skinny_*"
- *   variants of w4a16_gemm_variants) and `splits` as in w4a16_gemm_plan. */
+ *   overwritten) is that of w4a16_gemm, and so is the kernel choice (skinny kernel for
+ *   small M, tiled kernel above), except that groups of 64 rows run on the skinny kernel
+ *   for every M.  The weights enter the fp8 matrix instructions
+ *   (v_mfma_f32_16x16x32_fp8_fp8 in the skinny kernel, v_mfma_scale_f32_16x16x128_f8f6f4
+ *   with unit block scales in the tiled one) as the exact E4M3 integers q - z, the scale
+ *   s applies in fp32 per 128-row block (per 64-row half for groups of 64), and a[m] in
+ *   fp32 before the one rounding of Y to fp16 (nearest-even).  Bitwise reproducible like
+ *   w4a16_gemm.
+ * w4a8_gemm_plan: the same with an explicit variant and `splits`, numbered and read as in
+ *   w4a16_gemm_plan; the tiled variants need an even number of 16-row tiles (not
+ *   "tiled_bm16_*": W4A16_ERR_ARG) and groups of 128 rows or more. */
 int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,
               const void* zp, uint16_t* Y, int M, int N, int K, int group, void* stream);
 int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,

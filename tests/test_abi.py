@@ -222,7 +222,9 @@ def test_w4a8_validation(raw):
     raw.w4a16_gemm_variant_name.restype = ctypes.c_char_p
     nskinny = sum(1 for v in range(raw.w4a16_gemm_variants())
                   if not raw.w4a16_gemm_variant_name(v).startswith(b"tiled"))
-    assert f(A, None, A, A, None, A, 16, 1024, 1024, 128, nskinny, 0, None) == -8  # skinny only
+    nall = raw.w4a16_gemm_variants()
+    assert nskinny < nall
+    assert f(A, None, A, A, None, A, 16, 1024, 1024, 128, nall, 0, None) == -8  # out of range
     assert f(A, None, A, A, None, A, 16, 1024, 1024, 128, -1, -1, None) == -8
     g = raw.w4a8_gemm
     g.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_void_p]

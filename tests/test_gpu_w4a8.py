@@ -206,3 +206,71 @@ def test_w4a8_groups_of_64(gh, M, K, N, asym):
         ok, info = oracle.accept(Y, Yref, B)
         assert ok, (v, splits, info)
         assert np.all(np.isnan(whole[M:]))
+
+
+# ---- tiled kernel (larger M): v_mfma_scale_f32_16x16x128_f8f6f4, fp32 scales per block ----
+W4A8_TILED = [(300, 2048, 1040, False), (257, 1536, 512, True), (130, 3072, 272, False),
+              (64, 1024, 768, True), (1, 1024, 512, False), (1000, 1024, 2048, True)]
+
+
+def _tiled_variants(w4):
+    return [v for v in range(w4.w4a16_gemm_variants())
+            if w4.w4a16_gemm_variant_name(v).startswith("tiled")
+            and not w4.w4a16_gemm_variant_name(v).startswith("tiled_bm16")]
+
+
+@pytest.mark.parametrize("M,K,N,asym", W4A8_TILED)
+def test_w4a8_tiled_grids(gh, M, K, N, asym):
+    """Every tiled variant with an even number of 16-row tiles, at workgroup counts that
+    leave whole tiles data-parallel and counts that cut tiles into stream-K stripes (the
+    row scales then apply in the second pass); each run repeats bit for bit and leaves the
+    rows past M untouched."""
+    import w4a16_mixed_precision_offline_amd as w4
+    d, X8, a = _case(M, K, N, asym)
+    packed = gh.repack(d, K, N)
+    Yref = oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 128)
+    B = oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], 128)
+    tiled = _tiled_variants(w4)
+    assert len(tiled) >= 3
+    for v in tiled:
+        for grid in (0, 1, 3, 5, 8, 24):
+            Y, whole = _gemm8(gh, X8, a, packed, M, N, K, v, grid, rows_alloc=M + 2)
+            ok, info = oracle.accept(Y, Yref, B)
+            assert ok, (w4.w4a16_gemm_variant_name(v), grid, info)
+            assert np.all(np.isnan(whole[M:]))
+            Y2, _ = _gemm8(gh, X8, a, packed, M, N, K, v, grid)
+            assert np.array_equal(Y2.view(np.uint16), Y.view(np.uint16)), (v, grid)
+
+
+def test_w4a8_tiled_rejects_odd_row_tiles(gh):
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 64, 1024, 512
+    d, X8, a = _case(M, K, N)
+    packed = gh.repack(d, K, N)
+    v16 = [v for v in range(w4.w4a16_gemm_variants())
+           if w4.w4a16_gemm_variant_name(v).startswith("tiled_bm16")]
+    with pytest.raises(w4.W4A16Error):
+        _gemm8(gh, X8, a, packed, M, N, K, v16[0], 0)
+    with pytest.raises(w4.W4A16Error):  # groups of 64: skinny kernel only
+        _gemm8(gh, X8, a, gh.repack(_case(M, K, N, group=64)[0], K, N, 64), M, N, K,
+               _tiled_variants(w4)[0], 0, group=64)
+
+
+def test_w4a8_tiled_onehot_exact(gh):
+    """One-hot fp8 rows with power-of-two row scales through the tiled kernel (stripes
+    included): Y[m, :] = RNE_fp16(a[m] * (q - z) * s) of row k_m bit for bit."""
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 200, 1024, 528
+    d, _, _ = _case(M, K, N, True)
+    rng = np.random.default_rng(8)
+    ks = rng.integers(0, K, size=M)
+    X8 = np.zeros((M, K), np.uint8)
+    X8[np.arange(M), ks] = 0x38
+    a = np.array([2.0 ** ((m % 7) - 3) for m in range(M)], dtype=np.float32)
+    W = oracle.dequant(d["Qp"], d["s"], d["Zp"], K, N, 128)
+    exp = (W[ks] * a[:, None].astype(np.float64)).astype(np.float16)
+    packed = gh.repack(d, K, N)
+    for v in _tiled_variants(w4):
+        for grid in (1, 7):
+            Y, _ = _gemm8(gh, X8, a, packed, M, N, K, v, grid)
+            assert np.array_equal(Y.view(np.uint16), exp.view(np.uint16)), (v, grid)

@@ -145,7 +145,8 @@ bool use_tiled(int M, int N, int K) {
 }
 
 int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
-              uint16_t* Y, int M, int N, int K, int variant, int grid, void* stream) {
+              uint16_t* Y, int M, int N, int K, int variant, int grid, void* stream,
+              const float* xscale = nullptr) {
   TiledPlan plan;
   int rc = tiled_make_plan(M, N, K, mode, variant, grid, &plan);
   if (rc) return rc;
@@ -155,7 +156,8 @@ int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
   int* cnt;
   float* part;
   if ((rc = get_workspace(dev, st, 0, plan.part_floats, &cnt, &part))) return rc;
-  return launched(tiled_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, st));
+  return launched(
+      tiled_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, st, xscale));
 }
 
 // Variant numbering of the ABI: the skinny variants first, then the tiled ones.
@@ -481,8 +483,18 @@ int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
   if (xscale && (reinterpret_cast<uintptr_t>(xscale) & 3u) != 0) return W4A16_ERR_ALIGN;
-  if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
+  if (variant < -1 || variant >= w4a16_gemm_variants() || splits < 0) return W4A16_ERR_ARG;
   const int mode = group == 64 ? (zp ? W_ASYM8G64 : W_SYM8G64) : (zp ? W_ASYM8 : W_SYM8);
+  // the same variant numbering and kernel choice as w4a16_gemm_plan; groups of 64 rows
+  // run on the skinny kernel for every M
+  const int ns = skinny_variant_count();
+  if (variant >= ns)
+    return run_tiled(mode, X, wp, sp, zp, Y, M, N, K, variant - ns, splits, stream, xscale);
+  if (variant < 0 && splits == 0 && group != 64 && use_tiled(M, N, K)) {
+    TiledPlan t;
+    if (tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0)
+      return run_tiled(mode, X, wp, sp, zp, Y, M, N, K, -1, 0, stream, xscale);
+  }
   return run_skinny(mode, X, wp, sp, zp, Y, M, N, K, group, variant, splits, stream, xscale);
 }
 

@@ -123,6 +123,29 @@ __device__ __forceinline__ half8 dequant_scaled(uint32_t w, half2v c0, half2v c1
 
 constexpr int WAVES = 4;
 
+typedef short short2v __attribute__((ext_vector_type(2)));
+typedef int int8v __attribute__((ext_vector_type(8)));
+
+// fp8 activations: 8 codes of one repacked word -> the 8 OCP E4M3 bytes of the exact
+// integers q - z (rows 0..7 in bytes 0..7): exact q - z in fp16 by the 0x6400 trick, then
+// a unit-scale conversion per pair (every integer in [-15, 15] is exact in E4M3).
+__device__ __forceinline__ uint2 dequant_fp8(uint32_t w, half2v c0, half2v c1, uint32_t magic) {
+  const half2v sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t w8 = w >> 8;
+  const half2v h0 = __builtin_bit_cast(half2v, and_or(w, 0x000F000Fu, magic)) + c0;
+  const half2v h1 =
+      __builtin_elementwise_fma(__builtin_bit_cast(half2v, and_or(w, 0x00F000F0u, magic)), sixteenth, c1);
+  const half2v h2 = __builtin_bit_cast(half2v, and_or(w8, 0x000F000Fu, magic)) + c0;
+  const half2v h3 =
+      __builtin_elementwise_fma(__builtin_bit_cast(half2v, and_or(w8, 0x00F000F0u, magic)), sixteenth, c1);
+  short2v lo = {0, 0}, hi = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(lo, h0, 1.0f, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(lo, h1, 1.0f, true);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(hi, h2, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(hi, h3, 1.0f, true);
+  return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
 // Per-wave weight sources of the current tile: resources over the wave's valid
 // column tiles, per-lane offsets of the column-tile part of each address
 // (kOutOfRange for tiles past N and for idle lanes: they read zeros), the
@@ -159,6 +182,14 @@ struct WLds {
 // chunk positions, i.e. all 64 banks once.
 __device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 256 + ((c ^ (r & 15)) << 4)); }
 
+// fp8 activations: BM rows of 128 bytes; chunk c of row r at chunk position c ^ ((r >> 1) & 7).
+// A fragment read (lane l: row 16i + l%16, the 8 bytes at 32j + 8(l/16)) then puts the 16
+// rows of one lane group on 16 different (row parity, chunk position) pairs and the 4
+// groups on different dwords of them: every bank is read exactly twice per instruction.
+__device__ __forceinline__ uint32_t swz8(int r, int c) {
+  return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+}
+
 // Direct-to-LDS loads of one k-block of X: each wave instruction writes 1 KiB of
 // LDS (lane L -> bytes 16L..16L+15 after the destination base), i.e. 4 rows; lane L
 // of instruction c therefore fetches row 4(wave*MT + c) + L/16 and the global chunk
@@ -172,33 +203,36 @@ __device__ __forceinline__ uint32_t swz(int r, int c) { return (uint32_t)(r * 25
 // the waves before their MFMAs start).
 template <int MT, int NTW, int MODE>
 struct DmaPlan {
+  // activation loads per wave: 1 KiB each, 4 rows of fp16 or 8 rows of fp8
+  static constexpr int NX = mode_fp8(MODE) ? MT / 2 : MT;
+  static constexpr uint32_t XKB = mode_fp8(MODE) ? 128u : 256u;  // X bytes per row and k-block
   // 2:4: two tiles' kept codes per 16-byte load, all four tiles' positions in one
   static constexpr int NW = MODE == W_SP24 ? NTW / 2 + NTW / 4 : MODE == W_FP16 ? 4 * NTW : NTW;
-  static constexpr int NV = MT + NW + (mode_asym(MODE) ? 2 : MODE == W_FP16 ? 0 : 1);
+  static constexpr int NV = NX + NW + (mode_asym(MODE) ? 2 : MODE == W_FP16 ? 0 : 1);
   static constexpr uint32_t SH = mode_g64(MODE) ? 2u : 1u;  // scale / zero rows per block
   u32x4 rx;
-  uint32_t xoff[MT];
+  uint32_t xoff[NX];
   WSrc<NTW> R;
   uint32_t xdst, wdst;  // LDS addresses: activation stage, this wave's weight slot
   int wave, kb;
   __device__ __forceinline__ void issue(int q) const {
     typedef WLds<NTW, MODE> L;
-    if (q < MT) {
-      dma16(rx, xdst + (wave * MT + q) * 1024, xoff[q], (uint32_t)kb * 256u);
-    } else if (MODE == W_SP24 && q < MT + NTW / 2) {
-      const int c = q - MT;  // kept codes of tiles 2c, 2c+1
+    if (q < NX) {
+      dma16(rx, xdst + (wave * NX + q) * 1024, xoff[q], (uint32_t)kb * XKB);
+    } else if (MODE == W_SP24 && q < NX + NTW / 2) {
+      const int c = q - NX;  // kept codes of tiles 2c, 2c+1
       dma16(R.w, wdst + c * 1024, R.wo[c], (uint32_t)kb * 512u);
-    } else if (MODE == W_SP24 && q < MT + NW) {
-      dma16(R.z, wdst + L::META + (q - MT - NTW / 2) * 1024, R.zo, (uint32_t)kb * 256u);
-    } else if (MODE == W_FP16 && q < MT + NW) {
-      const int t = (q - MT) >> 2, j = (q - MT) & 3;  // rows 32j.. of column tile t
+    } else if (MODE == W_SP24 && q < NX + NW) {
+      dma16(R.z, wdst + L::META + (q - NX - NTW / 2) * 1024, R.zo, (uint32_t)kb * 256u);
+    } else if (MODE == W_FP16 && q < NX + NW) {
+      const int t = (q - NX) >> 2, j = (q - NX) & 3;  // rows 32j.. of column tile t
       dma16(R.w, wdst + (t * 4 + j) * 1024, R.wo[t], (uint32_t)kb * 256u + 64u * j);
-    } else if (mode_dense4(MODE) && q < MT + NTW) {
-      const int t = q - MT;
+    } else if (mode_dense4(MODE) && q < NX + NTW) {
+      const int t = q - NX;
       dma16(R.w, wdst + t * 1024, R.wo[t], (uint32_t)kb * 1024u);
-    } else if (MODE != W_FP16 && q == MT + NW) {
+    } else if (MODE != W_FP16 && q == NX + NW) {
       dma4(R.s, wdst + L::SCALES, R.so, (uint32_t)kb * 32u * SH);
-    } else if (mode_asym(MODE) && q == MT + NW + 1) {
+    } else if (mode_asym(MODE) && q == NX + NW + 1) {
       dma4(R.z, wdst + L::ZEROS, R.zo, (uint32_t)kb * 8u * SH);
     }
   }
@@ -394,6 +428,89 @@ __device__ __forceinline__ void compute_kblock_fp16(const char* xb, const char* 
   }
 }
 
+// One k-block with fp8 activations.  The weights enter the matrix instruction as the
+// exact E4M3 integers q - z, so the group scale cannot ride on them (3 mantissa bits):
+// each (row tile, column tile) gets one v_mfma_scale_f32_16x16x128_f8f6f4 over the whole
+// 128-row block (unit E8M0 scales) into a temporary, then acc += s * g in fp32 with the
+// scales of the lane's four output columns.  Lane (l%16, q = l/16) holds k-slot 8j + e
+// = row 32j + 8q + e of the block in both operands: the repacked word j of the weights
+// and the activation bytes at 32j + 8q of its row.  Column tiles are the outer loop: the
+// unpacking of tile t + 1 overlaps the matrix instructions of tile t.
+template <int MT, int NTW, int MODE>
+__device__ __forceinline__ void compute_kblock_fp8(const char* xb, const char* wl,
+                                                   float4v (&acc)[MT][NTW],
+                                                   const uint32_t (&aoff)[4], int lane,
+                                                   uint32_t magic,
+                                                   const DmaPlan<MT, NTW, MODE>& dma) {
+  typedef WLds<NTW, MODE> L;
+  constexpr int NVL = DmaPlan<MT, NTW, MODE>::NV;
+  constexpr int G = NTW;  // groups per k-block: one per column tile
+  int8v xa[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 v = *reinterpret_cast<const uint2*>(xb + aoff[j] + i * 2048);
+      xa[i][2 * j] = (int)v.x;
+      xa[i][2 * j + 1] = (int)v.y;
+    }
+  u32x4 wv[NTW];
+  half2v c0[NTW], c1[NTW];
+  float4v sc[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    wv[t] = *reinterpret_cast<const u32x4*>(wl + t * 1024 + lane * 16);
+    int zq = 8;
+    if (mode_asym(MODE)) {
+      const int c = lane & 15;
+      const uint32_t zw = *reinterpret_cast<const uint32_t*>(wl + L::ZEROS + t * 8 + (c >> 3) * 4);
+      zq = (int)((zw >> (4 * (c & 7))) & 15u);
+    }
+    const _Float16 a0 = (_Float16)(float)(-1024 - zq);
+    const _Float16 a1 = (_Float16)(float)(-64 - zq);
+    c0[t] = half2v{a0, a0};
+    c1[t] = half2v{a1, a1};
+    const uint2 s4 = *reinterpret_cast<const uint2*>(wl + L::SCALES + t * 32 + 8 * (lane >> 4));
+    const half2v s01 = __builtin_bit_cast(half2v, s4.x), s23 = __builtin_bit_cast(half2v, s4.y);
+    sc[t] = float4v{(float)s01[0], (float)s01[1], (float)s23[0], (float)s23[1]};
+  }
+  auto unpack = [&](int t) {
+    int8v b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 v = dequant_fp8(wv[t][j], c0[t], c1[t], magic);
+      b[2 * j] = (int)v.x;
+      b[2 * j + 1] = (int)v.y;
+    }
+    return b;
+  };
+  // group t: unpack tile t + 1, the matrix instructions of tile t, and the rescale of
+  // tile t - 1 (whose products were issued one group earlier, so nothing waits on them)
+  int8v b[2];
+  float4v g[2][MT];
+  b[0] = unpack(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t <= NTW; ++t) {
+    if (t < NTW) {
+#pragma unroll
+      for (int q = t; q < NVL; q += G) dma.issue(q);
+    }
+    if (t + 1 < NTW) b[(t + 1) & 1] = unpack(t + 1);
+    if (t < NTW) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        g[t & 1][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            b[t & 1], xa[i], float4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+    }
+    if (t >= 1) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[i][t - 1] += sc[t - 1] * g[(t - 1) & 1][i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // vmcnt(n) with the other counters left alone (gfx9 encoding)
 __device__ __forceinline__ constexpr int vmcnt_enc(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
@@ -443,8 +560,11 @@ __device__ __forceinline__ void store_rows(uint16_t* __restrict__ Y, const Tiled
       const uint32_t off = r < rows ? (uint32_t)(((size_t)r * a.N + (t_first + t) * 16 +
                                                   4 * (lane >> 4)) * 2)
                                     : kOutOfRange;
+      // fp8 activations: the scale of the row, applied once to the finished sum
+      const float xs = (a.xscale != nullptr && r < rows) ? a.xscale[m0 + r] : 1.0f;
+      const float4v o = a.xscale != nullptr ? acc[ii][t] * xs : acc[ii][t];
       typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 v = {pack_h2(acc[ii][t][0], acc[ii][t][1]), pack_h2(acc[ii][t][2], acc[ii][t][3])};
+      const u32x2 v = {pack_h2(o[0], o[1]), pack_h2(o[2], o[3])};
       __builtin_amdgcn_raw_buffer_store_b64(v, ry, off, 0u, 0);
     }
   }
@@ -468,12 +588,14 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     float* __restrict__ part, TiledArgs a) {
   constexpr int BM = 16 * MT;
   constexpr int BN = WAVES * 16 * NTW;
-  constexpr int XBUF = BM * 256;   // one k-block of the activation tile
+  constexpr bool F8 = mode_fp8(MODE);
+  constexpr int XBUF = BM * (F8 ? 128 : 256);  // one k-block of the activation tile
   constexpr int NSTAGE = NS;       // LDS pipeline stages
   constexpr int AHEAD = NS - 1;    // k-blocks in flight ahead of the one computed
   constexpr int PIECE = BM * BN;   // floats of one partial tile
   constexpr int STAGE = XBUF + WAVES * WLds<NTW, MODE>::BYTES;  // LDS bytes of one stage
   constexpr int NV = DmaPlan<MT, NTW, MODE>::NV;  // loads per stage per thread
+  constexpr int NX = DmaPlan<MT, NTW, MODE>::NX;  // activation loads per stage per thread
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];
 
   const int tid = threadIdx.x;
@@ -484,9 +606,12 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
   const uint32_t magic = 0x64006400u;
   // per-lane LDS offsets of the fragment reads of k-step j (row tile 0; row tile i
   // adds 16 rows = 4096 bytes): row lane%16, chunk 4j + lane/16
+  // (fp8: the 8 bytes at 32j + 8(lane/16) of row lane%16, row tile i adds 2048 bytes)
   uint32_t aoff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) aoff[j] = swz(lane & 15, 4 * j + (lane >> 4));
+  for (int j = 0; j < 4; ++j)
+    aoff[j] = F8 ? swz8(lane & 15, 2 * j + (lane >> 5)) + 8 * ((lane >> 4) & 1)
+                 : swz(lane & 15, 4 * j + (lane >> 4));
 
   // logical workgroup index: consecutive indices on one XCD (the hardware deals
   // workgroups to the 8 XCDs round-robin)
@@ -499,13 +624,22 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     tile_coords(tt, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
     const int m0 = tm * BM;
     const int rows = a.M - m0 < BM ? a.M - m0 : BM;
-    const u32x4 rx = rsrc_words(X + (size_t)m0 * a.K, (uint32_t)((size_t)rows * a.K * 2));
-    uint32_t xoff[MT];
+    constexpr int XB = F8 ? 1 : 2;  // bytes per activation
+    const u32x4 rx = rsrc_words(reinterpret_cast<const char*>(X) + (size_t)m0 * a.K * XB,
+                                (uint32_t)((size_t)rows * a.K * XB));
+    uint32_t xoff[NX];
 #pragma unroll
-    for (int c = 0; c < MT; ++c) {
-      const int r = 4 * (wave * MT + c) + (lane >> 4);
-      const int cg = (lane & 15) ^ (r & 15);  // global chunk stored at position lane%16
-      xoff[c] = r < rows ? (uint32_t)(((size_t)r * a.K + 8 * cg) * 2) : kOutOfRange;
+    for (int c = 0; c < NX; ++c) {
+      if constexpr (F8) {
+        // lane L: row 8(wave*NX + c) + L/8, the global chunk stored at position L%8
+        const int r = 8 * (wave * NX + c) + (lane >> 3);
+        const int cg = (lane & 7) ^ ((r >> 1) & 7);
+        xoff[c] = r < rows ? (uint32_t)((size_t)r * a.K + 16 * cg) : kOutOfRange;
+      } else {
+        const int r = 4 * (wave * MT + c) + (lane >> 4);
+        const int cg = (lane & 15) ^ (r & 15);  // global chunk stored at position lane%16
+        xoff[c] = r < rows ? (uint32_t)(((size_t)r * a.K + 8 * cg) * 2) : kOutOfRange;
+      }
     }
     const int t_first = tn * (BN / 16) + wave * NTW;  // first 16-column tile of this wave
     int nvalid = ntiles16 - t_first;
@@ -595,7 +729,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       DmaPlan<MT, NTW, MODE> plan;
       plan.rx = live ? rx : rx0;
 #pragma unroll
-      for (int c = 0; c < MT; ++c) plan.xoff[c] = xoff[c];
+      for (int c = 0; c < NX; ++c) plan.xoff[c] = xoff[c];
       plan.R = live ? R : R0;
       plan.xdst = lds0 + p * STAGE;
       plan.wdst = wl0 + p * STAGE;
@@ -622,7 +756,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       DmaPlan<MT, NTW, MODE> plan;
       plan.rx = issue_live ? rx : rx0;
 #pragma unroll
-      for (int c = 0; c < MT; ++c) plan.xoff[c] = xoff[c];
+      for (int c = 0; c < NX; ++c) plan.xoff[c] = xoff[c];
       plan.R = issue_live ? R : R0;
       plan.xdst = lds0 + dn * STAGE;
       plan.wdst = wl0 + dn * STAGE;
@@ -636,6 +770,10 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
         compute_kblock_sp24<MT, NTW>(lds + d * STAGE,
                                      lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES, acc,
                                      aoff, lane, magic, plan);
+      else if constexpr (F8)
+        compute_kblock_fp8<MT, NTW, MODE>(lds + d * STAGE,
+                                          lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES,
+                                          acc, aoff, lane, magic, plan);
       else
         compute_kblock<MT, NTW, MODE>(lds + d * STAGE,
                                       lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES, acc,
@@ -755,22 +893,30 @@ typedef void (*FixupFn)(const float*, uint16_t*, TiledArgs);
 
 struct TVariant {
   int MT, NTW, NS;
-  TiledFn sym, asym, sp24, f16, sym64, asym64;
+  TiledFn sym, asym, sp24, f16, sym64, asym64, sym8, asym8;
   FixupFn fixup;
   const char* name;
 };
+
+// fp8 activations need an even number of 16-row tiles (one 1 KiB load covers 8 rows)
+template <int MT, int NTW, int NS, int MODE>
+constexpr TiledFn fp8_tiled() {
+  if constexpr (MT % 2 == 0) return tiled_kernel<MT, NTW, NS, MODE>;
+  else return nullptr;
+}
 
 #define W4A16_TILED(MT, NTW, NS, NAME)                                                       \
   TVariant {                                                                               \
     MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>,       \
         tiled_kernel<MT, NTW, NS, W_SP24>, nullptr, tiled_kernel<MT, NTW, NS, W_SYM64>,     \
-        tiled_kernel<MT, NTW, NS, W_ASYM64>, tiled_fixup_kernel<MT, NTW>, NAME              \
+        tiled_kernel<MT, NTW, NS, W_ASYM64>, fp8_tiled<MT, NTW, NS, W_SYM8>(),             \
+        fp8_tiled<MT, NTW, NS, W_ASYM8>(), tiled_fixup_kernel<MT, NTW>, NAME                \
   }
 // the fp16 baseline moves four times the weight bytes: its own LDS-sized tiles
 #define W4A16_TILED_F16(MT, NTW, NS, NAME)                                                    \
   TVariant {                                                                               \
     MT, NTW, NS, nullptr, nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_FP16>, nullptr,     \
-        nullptr, tiled_fixup_kernel<MT, NTW>, NAME                                         \
+        nullptr, nullptr, nullptr, tiled_fixup_kernel<MT, NTW>, NAME                       \
   }
 
 const TVariant kTiled[] = {
@@ -796,8 +942,11 @@ const char* tiled_variant_name(int mode, int v) {
 }
 
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p) {
-  if ((!mode_dense4(mode) && mode != W_SP24 && mode != W_FP16) || mode_bf16(mode) || mode_fp8(mode))
+  // fp8 activations: groups of 128 rows or more (one scale per 128-row block)
+  if ((!mode_dense4(mode) && mode != W_SP24 && mode != W_FP16) || mode_bf16(mode) ||
+      mode == W_SYM8G64 || mode == W_ASYM8G64)
     return -8;
+  const bool f8 = mode_fp8(mode);
   const bool f16 = mode == W_FP16;
   const TVariant* table = f16 ? kTiledF16 : kTiled;
   const int count = f16 ? kNumTiledF16 : kNumTiled;
@@ -815,11 +964,12 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
       const TVariant& d = table[variant];
       const long long units = (long long)((M + 16 * d.MT - 1) / (16 * d.MT)) *
                               ((N + WAVES * 16 * d.NTW - 1) / (WAVES * 16 * d.NTW)) * (K / KBLK);
-      if (units < 1024) variant = 4;
+      if (units < 1024) variant = f8 ? 3 : 4;  // fp8: the 32-row tile (an even row-tile count)
     }
   }
   if (variant >= count) return -8;
   const TVariant& v = table[variant];
+  if (f8 && v.MT % 2 != 0) return -8;
   const int BM = 16 * v.MT, BN = WAVES * 16 * v.NTW;
   const int Gk = K / KBLK;
   TiledPlan q;
@@ -834,6 +984,7 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   // workgroups of an XCD then share 4 row tiles of X and 8 column tiles of W in its L2
   // (measured 0-8% faster than groups of 8 on the 70B-class layers)
   q.args.group_m = 4;
+  q.args.xscale = nullptr;
   const long T = (long)q.args.tiles_m * q.args.tiles_n;
   if (T > (1L << 30)) return -2;
   // buffer offsets are 32-bit: the rows of X and Y one tile touches, and the fp16
@@ -874,20 +1025,26 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
 }
 
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
-                        const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st) {
+                        const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st,
+                        const float* xscale) {
   const TVariant& v = p.mode == W_FP16 ? kTiledF16[p.variant] : kTiled[p.variant];
   TiledFn fn = p.mode == W_ASYM     ? v.asym
                : p.mode == W_SP24   ? v.sp24
                : p.mode == W_FP16   ? v.f16
                : p.mode == W_SYM64  ? v.sym64
                : p.mode == W_ASYM64 ? v.asym64
+               : p.mode == W_SYM8   ? v.sym8
+               : p.mode == W_ASYM8  ? v.asym8
                                     : v.sym;
+  if (fn == nullptr) return hipErrorInvalidValue;  // not reachable through tiled_make_plan
+  TiledArgs args = p.args;
+  args.xscale = mode_fp8(p.mode) ? xscale : nullptr;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
-                     reinterpret_cast<const uint32_t*>(w), sp, zp, Y, part, p.args);
+                     reinterpret_cast<const uint32_t*>(w), sp, zp, Y, part, args);
   if (p.fixup_wgs > 0) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(v.fixup, dim3(p.fixup_wgs), dim3(p.threads), 0, st, part, Y, p.args);
+    hipLaunchKernelGGL(v.fixup, dim3(p.fixup_wgs), dim3(p.threads), 0, st, part, Y, args);
   }
   return hipGetLastError();
 }

@@ -121,6 +121,7 @@ struct TiledArgs {
   int dp_rounds;   // rounds of whole tiles handed out data-parallel
   long long sk_units;   // (tile, k-block) units of the remaining tiles
   long long sk_per_wg;  // units per workgroup stripe
+  const float* xscale;  // fp8 activations: fp32 scale per row of X (nullptr: 1)
 };
 struct TiledPlan {
   int variant;  // index into the tiled variant table
@@ -135,8 +136,10 @@ int tiled_variant_count(int mode);
 const char* tiled_variant_name(int mode, int v);
 // variant < 0: automatic; grid <= 0: automatic number of workgroups.
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p);
+// X holds fp8 codes in the fp8 modes, with xscale their optional per-row scale.
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
-                        const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st);
+                        const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st,
+                        const float* xscale = nullptr);
 
 // Calibration kernels (probes.hip).
 hipError_t launch_probe_read(const void* p, size_t bytes, uint32_t* out, hipStream_t st);
