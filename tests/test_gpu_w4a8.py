@@ -274,3 +274,42 @@ def test_w4a8_tiled_onehot_exact(gh):
         for grid in (1, 7):
             Y, _ = _gemm8(gh, X8, a, packed, M, N, K, v, grid)
             assert np.array_equal(Y.view(np.uint16), exp.view(np.uint16)), (v, grid)
+
+
+def test_w4a8_hip_graph_replays_match_eager(gh):
+    """Captured W4A8 launches (skinny with and without a K split, tiled with stream-K
+    stripes and the fixup pass) reproduce the eager result bit for bit on every replay,
+    with eager work and synchronizations in between."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    st = torch.cuda.Stream()
+    plans = [(1, 4096, 4096, -1, 0), (8, 11008, 4096, gh.variant_index("skinny_xr8_nt1_wk8_d4"), 3),
+             (300, 2048, 1040, -1, 0), (130, 1024, 768, gh.variant_index("tiled_bm64_bn256_s3"), 7)]
+    cases = []
+    for (M, K, N, v, sp) in plans:
+        d, X8, a = _case(M, K, N, asym=(M % 2 == 0))
+        cases.append((M, K, N, v, sp, gh.dev(X8), gh.dev(a), gh.repack(d, K, N),
+                      torch.empty((M, N), dtype=torch.float16, device="cuda")))
+
+    def run_all():
+        for (M, K, N, v, sp, x, s, packed, Y) in cases:
+            w4.w4a8_gemm_plan(x, s, *packed, Y, M, N, K, 128, v, sp)
+
+    with torch.cuda.stream(st):
+        run_all()
+    torch.cuda.synchronize()
+    eager = [gh.host(c[-1]).view(np.uint16).copy() for c in cases]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        run_all()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for c in cases:
+            c[-1].fill_(0)
+        junk, _ = _gemm8(gh, np.zeros((2, 1024), np.uint8), None, cases[3][7], 2, 768, 1024)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            g.replay()
+        torch.cuda.synchronize()
+        for c, e in zip(cases, eager):
+            assert np.array_equal(gh.host(c[-1]).view(np.uint16), e), rep
