@@ -272,7 +272,8 @@ def test_two_streams_concurrently(gh):
 
 
 # ---- unfused baseline ---------------------------------------------------------------
-@pytest.mark.parametrize("K,N,asym", [(1024, 512, False), (1152, 528, True)])
+@pytest.mark.parametrize("K,N,asym", [(1024, 512, False), (1152, 528, True), (128, 16, True),
+                                      (4096, 1040, False)])
 def test_dequant_bit_exact(gh, K, N, asym):
     import torch
     import w4a16_mixed_precision_offline_amd as w4

@@ -98,33 +98,62 @@ __global__ void zeros_kernel(const uint32_t* __restrict__ src, uint32_t* __restr
 }
 
 // Unfused baseline dequantization: Wt[n][k] = RNE((q[k][n] - z[k/g][n]) * s[k/g][n]).
-// One thread per canonical word (8 rows of one column).  (q - z) * s is exact in
-// fp32 (a 5-bit integer times an 11-bit significand), so the single conversion to
-// fp16 rounds the exact value to nearest-even.
-__global__ void dequant_kernel(const uint32_t* __restrict__ q, const uint16_t* __restrict__ s,
-                               const uint32_t* __restrict__ z, uint16_t* __restrict__ Wt,
-                               long total, int K, int N, int group) {
-  for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
-       o += (long)gridDim.x * blockDim.x) {
-    const long i = o / N;          // canonical row of words
-    const int n = (int)(o - i * N);
-    const int g = (int)((8 * i) / group);
-    const uint32_t v = q[o];
-    const float sc = (float)__builtin_bit_cast(_Float16, s[(long)g * N + n]);
-    int zz = 8;
-    if (z) zz = (int)((z[(long)g * (N / 8) + n / 8] >> (4 * (n & 7))) & 15u);
-    uint16_t out[8];
+// (q - z) * s is exact in fp32 (a 5-bit integer times an 11-bit significand), so the
+// single conversion to fp16 rounds the exact value to nearest-even.
+// A workgroup transposes a tile of 32 canonical word rows (256 K) x 64 columns through
+// LDS: the words are read along N (256 contiguous bytes per row) and the fp16 rows of Wt
+// are written along K (512 contiguous bytes per column), so both sides coalesce.
+constexpr int DQ_ROWS = 32, DQ_COLS = 64;
+constexpr int DQ_STRIDE = DQ_ROWS * 16 + 16;  // LDS bytes per column (+16 against conflicts)
+__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ s,
+                                                      const uint32_t* __restrict__ z,
+                                                      uint16_t* __restrict__ Wt, int K, int N,
+                                                      int group) {
+  __shared__ __attribute__((aligned(16))) char tile[DQ_COLS * DQ_STRIDE];
+  const int t = threadIdx.x;
+  const int n0 = blockIdx.x * DQ_COLS;
+  const long i0 = (long)blockIdx.y * DQ_ROWS;
+  const long rows = K / 8;
+  // read and dequantize: thread t takes column n0 + t%64 of rows i0 + t/64 + 4r
+  {
+    const int c = t & 63;
+    const int n = n0 + c;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int qq = (int)((v >> (4 * e)) & 15u);
-      out[e] = __builtin_bit_cast(uint16_t, (_Float16)((float)(qq - zz) * sc));
+    for (int r = 0; r < DQ_ROWS / 4; ++r) {
+      const int il = (t >> 6) + 4 * r;
+      const long i = i0 + il;
+      if (n >= N || i >= rows) continue;
+      const int g = (int)((8 * i) / group);
+      const uint32_t v = q[i * N + n];
+      const float sc = (float)__builtin_bit_cast(_Float16, s[(long)g * N + n]);
+      int zz = 8;
+      if (z) zz = (int)((z[(long)g * (N / 8) + n / 8] >> (4 * (n & 7))) & 15u);
+      uint16_t out[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int qq = (int)((v >> (4 * e)) & 15u);
+        out[e] = __builtin_bit_cast(uint16_t, (_Float16)((float)(qq - zz) * sc));
+      }
+      uint4 pk;
+      pk.x = out[0] | ((uint32_t)out[1] << 16);
+      pk.y = out[2] | ((uint32_t)out[3] << 16);
+      pk.z = out[4] | ((uint32_t)out[5] << 16);
+      pk.w = out[6] | ((uint32_t)out[7] << 16);
+      *reinterpret_cast<uint4*>(tile + c * DQ_STRIDE + il * 16) = pk;
     }
-    uint4 pk;
-    pk.x = out[0] | ((uint32_t)out[1] << 16);
-    pk.y = out[2] | ((uint32_t)out[3] << 16);
-    pk.z = out[4] | ((uint32_t)out[5] << 16);
-    pk.w = out[6] | ((uint32_t)out[7] << 16);
-    *reinterpret_cast<uint4*>(Wt + (long)n * K + 8 * i) = pk;
+  }
+  __syncthreads();
+  // write: element e = t + 256r of the tile is column e / 32, word row e % 32
+#pragma unroll
+  for (int r = 0; r < DQ_ROWS * DQ_COLS / 256; ++r) {
+    const int e = t + 256 * r;
+    const int c = e / DQ_ROWS, il = e % DQ_ROWS;
+    const int n = n0 + c;
+    const long i = i0 + il;
+    if (n >= N || i >= rows) continue;
+    *reinterpret_cast<uint4*>(Wt + (long)n * K + 8 * i) =
+        *reinterpret_cast<const uint4*>(tile + c * DQ_STRIDE + il * 16);
   }
 }
 
@@ -279,10 +308,10 @@ hipError_t launch_sparse_decompress(const uint32_t* vp, const uint32_t* meta, co
 
 hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z, uint16_t* Wt,
                           int K, int N, int group, hipStream_t st) {
-  const long tot = (long)K * N / 8;
-  dequant_kernel<<<grid_for(tot, 256), 256, 0, st>>>(
-      reinterpret_cast<const uint32_t*>(q), s, reinterpret_cast<const uint32_t*>(z), Wt, tot, K,
-      N, group);
+  const dim3 grid((unsigned)((N + DQ_COLS - 1) / DQ_COLS),
+                  (unsigned)((K / 8 + DQ_ROWS - 1) / DQ_ROWS));
+  dequant_kernel<<<grid, 256, 0, st>>>(reinterpret_cast<const uint32_t*>(q), s,
+                                       reinterpret_cast<const uint32_t*>(z), Wt, K, N, group);
   return hipGetLastError();
 }
 
