@@ -213,24 +213,53 @@ def large_m_sweep(w4, torch, group):
                 runs=out)
 
 
-def time_rotated(torch, calls, min_reps=20, target_s=0.02):
-    """Seconds per call, cycling through `calls` (one per weight copy) back to back
-    after a 20 ms warmup."""
+_SIDE = {}
+
+
+def time_rotated(torch, calls, min_reps=20, target_s=0.02, graph=True):
+    """Seconds per call, cycling through `calls` (one per weight copy) back to back.
+    After a 20 ms eager warmup on a side stream (which also sizes the library's
+    per-stream split-K workspace), the calls are captured once into a HIP graph that is
+    replayed until at least `min_reps` calls ran: eager launches from Python would time
+    the host's launch rate, not the GPU, for kernels of a few microseconds.  graph=False
+    times eager launches (calls that synchronize with the host cannot be captured)."""
+    s = _SIDE.setdefault("s", torch.cuda.Stream())
     t0 = time.perf_counter()
     i = 0
-    while time.perf_counter() - t0 < 0.02:
-        calls[i % len(calls)]()
-        i += 1
+    with torch.cuda.stream(s):
+        while time.perf_counter() - t0 < 0.02:
+            calls[i % len(calls)]()
+            i += 1
     torch.cuda.synchronize()
+    g = None
+    try:
+        if not graph:
+            raise RuntimeError("not captured")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for c in calls:
+                c()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+    except Exception as e:  # capture unsupported: time eager launches instead
+        if graph:
+            print(f"bench.py: graph capture failed ({e}); timing eager launches", file=sys.stderr)
+        g = None
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    reps = max(min_reps, len(calls))
-    e0.record()
-    for r in range(reps):
-        calls[r % len(calls)]()
-    e1.record()
+    reps = max(1, -(-min_reps // len(calls)))
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(reps):
+            if g is not None:
+                g.replay()
+            else:
+                for c in calls:
+                    c()
+        e1.record(s)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1e3 / reps
+    return e0.elapsed_time(e1) / 1e3 / (reps * len(calls))
 
 
 def config_legs(w4, torch, group):
@@ -481,7 +510,7 @@ def offline_leg(w4, torch):
         q24 = q24 | torch.tensor(0x88008800 - (1 << 32), dtype=torch.int32, device="cuda")  # ...to code 8
         sv = w4.alloc_sparse24(K, N, 128)
         kn2, gn2 = K * N // 2, 2 * G * N
-        items = [
+        items = [  # (name, call, bytes, capturable: the 2:4 compress reads its check back)
             ("w4a16_repack", lambda: w4.w4a16_repack(q, s, None, *pk, K, N, 128), 2 * (kn2 + gn2)),
             ("w4a16_repack_zero_points", lambda: w4.w4a16_repack(q, s, z, *pz, K, N, 128),
              2 * (kn2 + gn2 + G * N // 2)),
@@ -491,7 +520,8 @@ def offline_leg(w4, torch):
              kn2 + gn2 + K * N // 4 + K * N // 8 + gn2),
         ]
         for name, fn, nbytes in items:
-            t = time_rotated(torch, [fn], min_reps=10)
+            # ten calls per captured graph, so the graph launch itself is amortized
+            t = time_rotated(torch, [fn] * 10, min_reps=10, graph=name != "w4a16_sparse24_repack")
             runs.append(dict(kernel=name, K=K, N=N, us=round(t * 1e6, 2), bytes=nbytes,
                              GBps=round(nbytes / t / 1e9, 1),
                              frac_of_hbm_peak=round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 3)))
@@ -638,26 +668,43 @@ def main():
 
     t_step, mode = time_steps(run_step_w4, args.steps, args.warmup, not args.no_graph)
 
-    # ---- per-launch durations (eager, launches queued behind a spin so that the GPU
-    #      runs them back to back), for the per-shape table ----------------------------
+    # ---- per-shape durations for the per-run table: for each GEMM of the step, one HIP
+    #      graph of back-to-back launches over all R weight copies, replayed; eager launches
+    #      from Python would time the host's launch rate, not the GPU, at these sizes -----
     per_launch = []
-    with torch.cuda.stream(stream):
-        launches = step_launches(0)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+    launches = step_launches(0)
+    for (M, K, N, _) in launches:
+        calls = [(lambda wp=wp, sp=sp, M=M, K=K, N=N: w4.w4a16_gemm_plan(
+            Xs[(M, K, N)], wp, sp, None, Ys[(M, K, N)], M, N, K, group, args.variant, args.splits,
+            stream=stream.cuda_stream)) for (wp, sp) in packed[(K, N)]]
+        with torch.cuda.stream(stream):
+            for f in calls[:2]:
+                f()
         torch.cuda.synchronize()
-        try:
-            torch.cuda._sleep(20_000_000)
-        except Exception:
-            pass
-        evs[0].record(stream)
-        for i, (M, K, N, c) in enumerate(launches):
-            wp, sp = packed[(K, N)][c]
-            w4.w4a16_gemm_plan(Xs[(M, K, N)], wp, sp, None, Ys[(M, K, N)], M, N, K, group,
-                               args.variant, args.splits)
-            evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    for i, (M, K, N, c) in enumerate(launches):
-        us = evs[i].elapsed_time(evs[i + 1]) * 1e3
+        if args.no_graph:
+            g = None
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for f in calls:
+                    f()
+            g.replay()
+            torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = 3
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                if g is not None:
+                    g.replay()
+                else:
+                    for f in calls:
+                        f()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
+        del g
         wb, ab, fl = algorithmic(M, K, N)
         plan = w4.w4a16_gemm_describe(M, N, K, group)
         per_launch.append(dict(M=M, K=K, N=N, us=round(us, 3), weight_GBps=round(wb / us / 1e3, 1),
