@@ -139,6 +139,24 @@ const char* w4a16_gemm_variant_name(int variant);
  * memory ahead of time.  Host only. */
 size_t w4a16_workspace_bytes(int M, int N, int K);
 
+/* Caller-owned workspace (the pages leave workspace ownership open; this lets a caller such
+ * as a framework allocator own all device memory).  Hands the library the device buffer
+ * ptr of `bytes` bytes to use, instead of allocating its own, for every GEMM launched on
+ * `stream` on the current device.  Layout: the first W4A16_WS_COUNTER_BYTES hold the
+ * split-K arrival counters, the rest the fp32 partial sums; bytes >= that prefix plus
+ * w4a16_workspace_bytes(M, N, K) covers every automatic plan of a shape.  The call
+ * clears the counter prefix (hipMemsetAsync on `stream`, so it must not be captured into a
+ * graph); the kernels leave the counters at zero again, so no later call clears anything.
+ * The library never frees ptr; the caller keeps it alive, and does not use it otherwise,
+ * until it is replaced or until ptr = NULL hands the stream back to library-owned
+ * workspaces (a buffer the library had allocated for the stream is freed here, after the
+ * stream has drained).  A launch on the stream whose plan needs more than the buffer holds
+ * returns W4A16_ERR_WORKSPACE.  Errors: W4A16_ERR_ALIGN (ptr not 256-byte aligned),
+ * W4A16_ERR_WORKSPACE (ptr non-NULL with bytes below W4A16_WS_COUNTER_BYTES + 256),
+ * W4A16_ERR_DEVICE, W4A16_ERR_LAUNCH (the clearing failed). */
+#define W4A16_WS_COUNTER_BYTES 65536
+int w4a16_set_workspace(void* ptr, size_t bytes, void* stream);
+
 /* Describe the automatic plan for a shape: out[0] = variant, out[1] = the splits
  * value that reproduces it in w4a16_gemm_plan,
  * out[2] = workgroups launched, out[3] = threads per workgroup.  Host only. */

@@ -209,6 +209,13 @@ def test_bf16_validation(raw):
     assert f(A, A, A, None, A, 16, 1024, 1024, 128, -2, 0, None) == -8
 
 
+def test_set_workspace_validation(raw):
+    f = raw.w4a16_set_workspace
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(A + 16, 1 << 20, None) == -3          # not 256-byte aligned
+    assert f(A, 65536, None) == -6                 # no room past the counter prefix
+
+
 def test_w4a8_validation(raw):
     f = raw.w4a8_gemm_plan
     f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 + [ctypes.c_void_p]

@@ -706,3 +706,46 @@ def test_bf16_groups_of_64_onehot_exact(gh, asym):
     for nm, splits in [("skinny_xr16_nt1_wk8_d2", 1), ("skinny_xr16_nt4_wk4_d2", 3)]:
         Y = _gemm_bf16(gh, bits, packed, M, N, K, gh.variant_index(nm), splits, group=64)
         assert np.array_equal(Y, exp), nm
+
+
+def test_caller_owned_workspace(gh):
+    """w4a16_set_workspace: split-K (skinny) and stream-K (tiled) launches on a stream with a
+    caller-owned buffer give the same bits as on a stream with a library-owned one, twice in
+    a row (the counters come back to zero); a buffer too small for a plan is refused with
+    an error instead of grown; NULL hands the stream back to the library."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    cases = [(8, 11008, 4096, gh.variant_index("skinny_xr8_nt1_wk8_d4"), 3),
+             (300, 2048, 1040, gh.variant_index("tiled_bm128_bn256_s3"), 7)]
+    prepared = []
+    for (M, K, N, v, sp) in cases:
+        _, d, X = _case(M, K, N, asym=True)
+        prepared.append((M, K, N, v, sp, gh.dev(X), gh.repack(d, K, N)))
+    ref = []
+    for (M, K, N, v, sp, Xd, packed) in prepared:
+        ref.append(gh.host(gh.gemm(Xd, packed, M, N, K, variant=v, splits=sp)).view(np.uint16).copy())
+    st = torch.cuda.Stream()
+    buf = torch.empty(w4.WS_COUNTER_BYTES + (8 << 20), dtype=torch.uint8, device="cuda")
+    w4.w4a16_set_workspace(buf, buf.numel(), stream=st)
+    try:
+        for _ in range(2):
+            with torch.cuda.stream(st):
+                outs = [gh.gemm(Xd, packed, M, N, K, variant=v, splits=sp)
+                        for (M, K, N, v, sp, Xd, packed) in prepared]
+            torch.cuda.synchronize()
+            for o, r in zip(outs, ref):
+                assert np.array_equal(gh.host(o).view(np.uint16), r)
+        small = torch.empty(w4.WS_COUNTER_BYTES + 256, dtype=torch.uint8, device="cuda")
+        w4.w4a16_set_workspace(small, small.numel(), stream=st)
+        M, K, N, v, sp, Xd, packed = prepared[1]
+        with torch.cuda.stream(st), pytest.raises(w4.W4A16Error):
+            gh.gemm(Xd, packed, M, N, K, variant=v, splits=sp)
+        torch.cuda.synchronize()
+    finally:
+        w4.w4a16_set_workspace(None, 0, stream=st)
+    with torch.cuda.stream(st):
+        outs = [gh.gemm(Xd, packed, M, N, K, variant=v, splits=sp)
+                for (M, K, N, v, sp, Xd, packed) in prepared]
+    torch.cuda.synchronize()
+    for o, r in zip(outs, ref):
+        assert np.array_equal(gh.host(o).view(np.uint16), r)

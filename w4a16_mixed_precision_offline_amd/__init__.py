@@ -47,6 +47,7 @@ _SIGS = {
     "w4a16_gemm_bf16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "w4a16_gemm_bf16_plan": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "w4a8_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "w4a16_set_workspace": (_I, [_P, ctypes.c_size_t, _P]),
     "w4a8_gemm_plan": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "w4a16_probe_read": (_I, [_P, _SZ, _P, _P]),
     "w4a16_probe_mfma": (_I, [_I, _I, _P, _P]),
@@ -201,6 +202,14 @@ def w4a16_gemm_bf16_plan(X, wp, sp, zp, Y, M, N, K, group, variant=-1, splits=0,
     _check("w4a16_gemm_bf16_plan", _lib.w4a16_gemm_bf16_plan(
         _ptr(X), _ptr(wp), _ptr(sp), _ptr(zp), _ptr(Y), M, N, K, group, variant, splits,
         _stream(stream)))
+
+
+WS_COUNTER_BYTES = 65536  # W4A16_WS_COUNTER_BYTES
+
+
+def w4a16_set_workspace(ptr, nbytes, stream=None):
+    """Caller-owned workspace for launches on `stream` (ptr None: library-owned again)."""
+    _check("w4a16_set_workspace", _lib.w4a16_set_workspace(_ptr(ptr), nbytes, _stream(stream)))
 
 
 # ---- fp8 (E4M3) activations: W4A8 ---------------------------------------------------

@@ -60,6 +60,7 @@ struct Workspace {
   void* ptr = nullptr;
   size_t counter_ints = 0;
   size_t part_floats = 0;
+  bool external = false;  // caller-owned (w4a16_set_workspace): never grown or freed
 };
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
@@ -70,7 +71,9 @@ int get_workspace(int dev, hipStream_t st, size_t counters, size_t floats, int**
   if (counters == 0 && floats == 0) return W4A16_OK;
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace& ws = g_ws[std::make_pair(dev, st)];
-  if (ws.ptr == nullptr || ws.counter_ints < counters || ws.part_floats < floats) {
+  if (ws.external) {
+    if (ws.counter_ints < counters || ws.part_floats < floats) return W4A16_ERR_WORKSPACE;
+  } else if (ws.ptr == nullptr || ws.counter_ints < counters || ws.part_floats < floats) {
     size_t c = counters > ws.counter_ints ? counters : ws.counter_ints;
     size_t f = floats > ws.part_floats ? floats : ws.part_floats;
     c = (c + 63) / 64 * 64;  // keep the partials 256-byte aligned
@@ -473,6 +476,35 @@ int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, 
 int w4a16_gemm_bf16(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                     uint16_t* Y, int M, int N, int K, int group, void* stream) {
   return w4a16_gemm_bf16_plan(X, wp, sp, zp, Y, M, N, K, group, -1, 0, stream);
+}
+
+// ---- caller-owned workspace -----------------------------------------------------------
+int w4a16_set_workspace(void* ptr, size_t bytes, void* stream) {
+  if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0) return W4A16_ERR_ALIGN;
+  if (ptr && bytes < (size_t)W4A16_WS_COUNTER_BYTES + 256) return W4A16_ERR_WORKSPACE;
+  int dev;
+  int rc = check_device(&dev);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace& ws = g_ws[std::make_pair(dev, st)];
+  // earlier launches on this stream may still use the current buffer
+  if (ws.ptr && hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return W4A16_ERR_LAUNCH;
+  }
+  if (ws.ptr && !ws.external) (void)hipFree(ws.ptr);
+  ws = Workspace();
+  if (!ptr) return W4A16_OK;
+  if (hipMemsetAsync(ptr, 0, W4A16_WS_COUNTER_BYTES, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return W4A16_ERR_LAUNCH;
+  }
+  ws.ptr = ptr;
+  ws.external = true;
+  ws.counter_ints = W4A16_WS_COUNTER_BYTES / sizeof(int);
+  ws.part_floats = (bytes - W4A16_WS_COUNTER_BYTES) / sizeof(float);
+  return W4A16_OK;
 }
 
 // ---- fp8 (E4M3) activations: W4A8 ------------------------------------------------------
