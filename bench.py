@@ -531,6 +531,39 @@ def offline_leg(w4, torch):
                 runs=runs)
 
 
+def profile_tiled(w4, torch):
+    """A short workload for counter runs: W4A16 (fp16 activations) and W4A8 (fp8 E4M3
+    activations) on the tiled kernel, 8192 x 28672 at M = 4096, three eager launches each
+    after one warmup launch; prints the per-launch times."""
+    K, N, M = 8192, 28672, 4096
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(21)
+    q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
+                      generator=gen)
+    s = (torch.rand((K // 128, N), device="cuda", generator=gen) * 0.009 + 0.001).half()
+    pk = w4.alloc_packed(K, N, 128, False)
+    w4.w4a16_repack(q, s, None, *pk, K, N, 128)
+    x = torch.randn((M, K), device="cuda", generator=gen)
+    Xh = x.half()
+    a = (x.abs().amax(dim=1) / 448.0).float()
+    X8 = (x / a[:, None]).cpu().to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    out = {}
+    for name, fn in (("w4a16_gemm", lambda: w4.w4a16_gemm(Xh, pk[0], pk[1], None, Y, M, N, K, 128)),
+                     ("w4a8_gemm", lambda: w4.w4a8_gemm(X8, a, pk[0], pk[1], None, Y, M, N, K, 128))):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) / 3 * 1e3, 1)
+    print(json.dumps(dict(profile_tiled=dict(M=M, K=K, N=N, us_per_launch=out))), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -546,6 +579,8 @@ def main():
                     help="skip the large-M (70B-class, MFMA-bound) sweep")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the 2:4-sparse and zero-point workload legs")
+    ap.add_argument("--profile-tiled", action="store_true",
+                    help="only a short W4A16 / W4A8 tiled-kernel workload (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain device copies of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -570,6 +605,9 @@ def main():
     from gen import CONFIGS, activations, config_runs, weights
 
     torch.cuda.set_device(0)
+    if args.profile_tiled:
+        profile_tiled(w4, torch)
+        return
     runs = config_runs(1)
     shapes = []
     for w in runs:
