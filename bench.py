@@ -214,6 +214,7 @@ def large_m_sweep(w4, torch, group):
 
 
 _SIDE = {}
+STEP_STATS = {}  # per-step time percentiles (ms) of each timed step function
 
 
 def time_rotated(torch, calls, min_reps=20, target_s=0.02, graph=True):
@@ -682,19 +683,24 @@ def main():
                 print(f"bench.py: graph capture failed ({e}); timing eager launches",
                       file=sys.stderr)
                 graphs = None
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        # one event between consecutive steps: the first and last bracket the timed steps,
+        # the ones between give the per-step distribution
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
-            e0.record(stream)
+            evs[0].record(stream)
             for i in range(nsteps):
                 if graphs is not None:
                     graphs[i % steps_per_cycle].replay()
                 else:
                     run_step(i)
-            e1.record(stream)
+                evs[i + 1].record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3 / nsteps, ("hip_graph" if graphs is not None else "eager")
+        per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(nsteps))
+        pct = lambda f: per_step[min(nsteps - 1, int(f * (nsteps - 1) + 0.5))]
+        STEP_STATS[run_step.__name__] = dict(p10=round(pct(0.1), 5), p50=round(pct(0.5), 5),
+                                             p90=round(pct(0.9), 5))
+        return evs[0].elapsed_time(evs[-1]) / 1e3 / nsteps, ("hip_graph" if graphs is not None else "eager")
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
@@ -868,6 +874,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(t_step * 1e3, 5),
+        "ms_per_step_percentiles": STEP_STATS.get("run_step_w4"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
