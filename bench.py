@@ -580,6 +580,8 @@ def main():
                     help="skip the large-M (70B-class, MFMA-bound) sweep")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the 2:4-sparse and zero-point workload legs")
+    ap.add_argument("--no-table", action="store_true",
+                    help="skip the per-shape table (a kernel trace then holds only the step's launches)")
     ap.add_argument("--profile-tiled", action="store_true",
                     help="only a short W4A16 / W4A8 tiled-kernel workload (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -717,7 +719,7 @@ def main():
     #      from Python would time the host's launch rate, not the GPU, at these sizes -----
     per_launch = []
     launches = step_launches(0)
-    for (M, K, N, _) in launches:
+    for (M, K, N, _) in ([] if args.no_table else launches):
         calls = [(lambda wp=wp, sp=sp, M=M, K=K, N=N: w4.w4a16_gemm_plan(
             Xs[(M, K, N)], wp, sp, None, Ys[(M, K, N)], M, N, K, group, args.variant, args.splits,
             stream=stream.cuda_stream)) for (wp, sp) in packed[(K, N)]]
