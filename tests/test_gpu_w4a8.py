@@ -313,3 +313,21 @@ def test_w4a8_hip_graph_replays_match_eager(gh):
         torch.cuda.synchronize()
         for c, e in zip(cases, eager):
             assert np.array_equal(gh.host(c[-1]).view(np.uint16), e), rep
+
+
+def test_w4a8_tiled_without_row_scales(gh):
+    """The tiled fp8 path with xscale = NULL (scale 1): matches the oracle, and equals a
+    run with unit row scales bit for bit, through data-parallel tiles and stream-K pieces."""
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 257, 1536, 512
+    d, X8, _ = _case(M, K, N, asym=True)
+    packed = gh.repack(d, K, N)
+    ok, info = _accept(_gemm8(gh, X8, None, packed, M, N, K)[0], X8, None, d)
+    assert ok, info
+    for v in _tiled_variants(w4):
+        for grid in (0, 5):
+            Y0, _ = _gemm8(gh, X8, None, packed, M, N, K, v, grid)
+            Y1, _ = _gemm8(gh, X8, np.ones(M, np.float32), packed, M, N, K, v, grid)
+            assert np.array_equal(Y0.view(np.uint16), Y1.view(np.uint16)), (v, grid)
+            ok, info = _accept(Y0, X8, None, d)
+            assert ok, (v, grid, info)
