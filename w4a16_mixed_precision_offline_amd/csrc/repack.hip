@@ -250,6 +250,62 @@ __global__ void sparse_decompress_kernel(const uint32_t* __restrict__ vp,
 
 __global__ void zero_int_kernel(int* p) { *p = 0; }
 
+// The whole repack in one launch.  Workgroups [0, nA) repack codes: workgroup
+// kb * pairs + p takes the 16-column tiles 2p and 2p + 1 of the 128-row block kb, so that
+// for each word j its 128 threads read 4 canonical rows x 32 columns, i.e. whole 128-byte
+// lines, and consecutive workgroups read neighbouring lines of the same rows.  Thread
+// (h = tile of the pair, lane l) writes lane l's 16 bytes of its block: words j = 0..3
+// hold rows 16kb + 4j + l/16 of column 32p + 16h + l%16.  The workgroups after nA copy the
+// scales, then the zero-points, one element per thread (layouts as in scales_kernel and
+// zeros_kernel).
+__global__ __launch_bounds__(128) void repack_all_kernel(
+    const uint32_t* __restrict__ q, uint32_t* __restrict__ wp, const uint16_t* __restrict__ s,
+    uint16_t* __restrict__ sp, const uint32_t* __restrict__ z, uint32_t* __restrict__ zp, int Gk,
+    int N, int gpb, int SH, long nA, long nS, long stot, long ztot) {
+  const long b = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (b < nA) {
+    const int tiles = N / 16;
+    const long pairs = (tiles + 1) / 2;
+    const long kb = b / pairs;
+    const long p = b - kb * pairs;
+    const int h = tid >> 6, l = tid & 63;
+    const long t = 2 * p + h;
+    if (t >= tiles) return;  // odd tile count: the last pair has one tile
+    const long n = 16 * t + (l & 15);
+    uint4 v;
+    uint32_t* vw = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long i = 16 * kb + 4 * j + (l >> 4);
+      vw[j] = shuffle_to_repacked(q[i * N + n]);
+    }
+    *reinterpret_cast<uint4*>(wp + (t * Gk + kb) * 256 + 4 * l) = v;
+    return;
+  }
+  if (b < nA + nS) {
+    const long o = (b - nA) * 128 + tid;
+    if (o >= stot) return;
+    const int hh = SH == 2 ? (int)(o & 1) : 0;
+    const long oc = SH == 2 ? o >> 1 : o;
+    const int c = (int)(oc & 15);
+    const long tk = oc >> 4;
+    const long tt = tk / Gk;
+    const int kb = (int)(tk - tt * Gk);
+    sp[o] = s[group_row(kb, hh, SH, gpb) * N + 16 * tt + c];
+    return;
+  }
+  const long o = (b - nA - nS) * 128 + tid;
+  if (o >= ztot) return;
+  const int w = (int)(o & 1);
+  const long oh = o >> 1;
+  const int hh = SH == 2 ? (int)(oh & 1) : 0;
+  const long tk = SH == 2 ? oh >> 1 : oh;
+  const long tt = tk / Gk;
+  const int kb = (int)(tk - tt * Gk);
+  zp[o] = z[group_row(kb, hh, SH, gpb) * (N / 8) + 2 * tt + w];
+}
+
 inline int grid_for(long total, int threads) {
   long b = (total + threads - 1) / threads;
   if (b > 65536) b = 65536;
@@ -262,12 +318,11 @@ inline int grid_for(long total, int threads) {
 hipError_t launch_repack(const int32_t* q, const uint16_t* s, const int32_t* z, uint32_t* wp,
                          uint16_t* sp, uint32_t* zp, int K, int N, int group, hipStream_t st) {
   const int Gk = K / KBLK, SH = group == 64 ? 2 : 1, gpb = SH == 2 ? 1 : group / KBLK;
-  const long wtot = (long)K * N / 8, stot = (long)Gk * N * SH, ztot = (long)Gk * N / 8 * SH;
-  codes_kernel<true><<<grid_for(wtot, 256), 256, 0, st>>>(
-      reinterpret_cast<const uint32_t*>(q), wp, wtot, Gk, N);
-  scales_kernel<true><<<grid_for(stot, 256), 256, 0, st>>>(s, sp, stot, Gk, gpb, SH, N);
-  if (z) zeros_kernel<true><<<grid_for(ztot, 256), 256, 0, st>>>(
-      reinterpret_cast<const uint32_t*>(z), zp, ztot, Gk, gpb, SH, N);
+  const long stot = (long)Gk * N * SH, ztot = z ? (long)Gk * N / 8 * SH : 0;
+  const long nA = (long)((N / 16 + 1) / 2) * Gk, nS = (stot + 127) / 128, nZ = (ztot + 127) / 128;
+  repack_all_kernel<<<(unsigned)(nA + nS + nZ), 128, 0, st>>>(
+      reinterpret_cast<const uint32_t*>(q), wp, s, sp, reinterpret_cast<const uint32_t*>(z), zp,
+      Gk, N, gpb, SH, nA, nS, stot, ztot);
   return hipGetLastError();
 }
 
