@@ -957,6 +957,10 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   // 64 rows, 64 x 128 up to 64.
   if (variant < 0) {
     variant = M > 64 ? 0 : (f16 ? 1 : 2);
+    // 128-row tiles would pad M by more than an eighth (M % 128 in 1..64, M < 512): 64-row
+    // tiles instead (measured 1.05-1.26x faster at M = 192 on six 7B/70B-class layers, and
+    // 1.08-1.18x slower at M = 256 / 384 where 128-row tiles pad nothing)
+    if (!f16 && M > 128 && M < 512 && M % 128 != 0 && M % 128 <= 64) variant = 2;
     if (!f16) {
       // a layer too small to give the chip a thousand (tile, k-block) units with these
       // tiles (3072 x 768: 72 at M = 128) runs on 16-row tiles instead, which gives
