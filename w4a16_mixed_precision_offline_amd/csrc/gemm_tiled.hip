@@ -933,6 +933,19 @@ const TVariant kTiledF16[] = {
 };
 constexpr int kNumTiledF16 = sizeof(kTiledF16) / sizeof(kTiledF16[0]);
 
+// the kernel of a variant for a weight format (nullptr where the variant does not run it)
+TiledFn variant_fn(const TVariant& v, int mode) {
+  return mode == W_ASYM     ? v.asym
+         : mode == W_SP24   ? v.sp24
+         : mode == W_FP16   ? v.f16
+         : mode == W_SYM64  ? v.sym64
+         : mode == W_ASYM64 ? v.asym64
+         : mode == W_SYM8   ? v.sym8
+         : mode == W_ASYM8  ? v.asym8
+         : mode == W_SYM    ? v.sym
+                            : nullptr;
+}
+
 }  // namespace
 
 int tiled_variant_count(int mode) { return mode == W_FP16 ? kNumTiledF16 : kNumTiled; }
@@ -973,7 +986,7 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   }
   if (variant >= count) return -8;
   const TVariant& v = table[variant];
-  if (f8 && v.MT % 2 != 0) return -8;
+  if (variant_fn(v, mode) == nullptr) return -8;  // e.g. fp8 with odd row tiles
   const int BM = 16 * v.MT, BN = WAVES * 16 * v.NTW;
   const int Gk = K / KBLK;
   TiledPlan q;
@@ -1032,14 +1045,7 @@ hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, co
                         const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st,
                         const float* xscale) {
   const TVariant& v = p.mode == W_FP16 ? kTiledF16[p.variant] : kTiled[p.variant];
-  TiledFn fn = p.mode == W_ASYM     ? v.asym
-               : p.mode == W_SP24   ? v.sp24
-               : p.mode == W_FP16   ? v.f16
-               : p.mode == W_SYM64  ? v.sym64
-               : p.mode == W_ASYM64 ? v.asym64
-               : p.mode == W_SYM8   ? v.sym8
-               : p.mode == W_ASYM8  ? v.asym8
-                                    : v.sym;
+  TiledFn fn = variant_fn(v, p.mode);
   if (fn == nullptr) return hipErrorInvalidValue;  // not reachable through tiled_make_plan
   TiledArgs args = p.args;
   args.xscale = mode_fp8(p.mode) ? xscale : nullptr;
