@@ -1,0 +1,49 @@
+"""The automatic plans the measurements chose (host-only queries of the C ABI, no GPU):
+which kernel and variant each workload shape gets, and the workspace the plans report."""
+import pytest
+
+w4 = pytest.importorskip("w4a16_mixed_precision_offline_amd")
+
+
+def plan(M, N, K, group=128):
+    d = w4.w4a16_gemm_describe(M, N, K, group)
+    return d["name"], d["splits"]
+
+
+@pytest.mark.parametrize("M,K,N,name", [
+    # decode sweep: eight waves with four k-blocks in flight for 1-4 rows on narrow layers
+    (1, 4096, 4096, "skinny_xr4_nt1_wk8_d4"), (4, 11008, 4096, "skinny_xr4_nt1_wk8_d4"),
+    # wide layers at 1-2 rows: eight waves, two k-blocks in flight
+    (1, 4096, 12288, "skinny_xr4_nt1_wk8_d2"), (2, 4096, 11008, "skinny_xr4_nt1_wk8_d2"),
+    # four waves for eight rows on 4096 x 4096
+    (8, 4096, 4096, "skinny_xr8_nt1_wk4_d4"),
+    # three column tiles per wave where that fills the 256 compute units (N = 12288)
+    (16, 4096, 12288, "skinny_xr16_nt3_wk4_d2"), (32, 4096, 12288, "skinny_xr32_nt3_wk4_d2"),
+    # narrow layers at 17-32 rows: two 16-row blocks
+    (32, 4096, 4096, "skinny_xr16_nt2_wk8_d2"), (20, 11008, 4096, "skinny_xr16_nt2_wk8_d2"),
+    # above 32 rows on large layers: the tiled kernel, 64-row tiles up to 64 rows ...
+    (48, 8192, 28672, "tiled_bm64_bn256_s3"), (64, 28672, 8192, "tiled_bm64_bn256_s3"),
+    # ... 128-row tiles above, except where they would pad M by more than an eighth
+    (128, 8192, 28672, "tiled_bm128_bn256_s3"), (192, 8192, 28672, "tiled_bm64_bn256_s3"),
+    (256, 8192, 10240, "tiled_bm128_bn256_s3"), (4096, 8192, 28672, "tiled_bm128_bn256_s3"),
+    # small wide layers stay on the skinny kernel at 33-255 rows
+    (48, 2560, 2560, "skinny_xr64_nt1_wk4_d2"),
+    # layers too small for a thousand (tile, k-block) units: 16-row tiles
+    (128, 3072, 768, "tiled_bm16_bn256_s4"),
+])
+def test_automatic_plans(M, K, N, name):
+    assert plan(M, N, K)[0] == name
+
+
+def test_k_split_only_where_columns_leave_compute_units_idle():
+    # 4096 x 4096 at M = 1: 256 column tiles, no split; 3072 x 768 at M = 1: 48 tiles, split
+    assert plan(1, 4096, 4096)[1] == 1
+    name, splits = plan(1, 768, 3072)
+    assert name.startswith("skinny") and splits > 1
+
+
+def test_workspace_query_covers_the_split_plans():
+    assert w4.w4a16_workspace_bytes(1, 4096, 4096) == 0          # no reduction across workgroups
+    assert w4.w4a16_workspace_bytes(1, 768, 3072) > 0            # K split
+    assert w4.w4a16_workspace_bytes(256, 10240, 8192) > 0        # stream-K pieces
+    assert w4.w4a16_workspace_bytes(0, 4096, 4096) == 0          # invalid shape
