@@ -111,9 +111,11 @@ def test_parity_every_variant_and_split(gh, M, K, N):
         name = w4.w4a16_gemm_variant_name(v)
         # tiled variants take any N % 16; their `splits` is the number of workgroups
         nt = 1 if name.startswith("tiled") else int(name.split("_nt")[1].split("_")[0])
+        # the 2:4 tiled kernel needs four column tiles per wave (256-column tiles)
+        refused = N % (16 * nt) != 0 or (name.startswith("tiled") and "_bn256_" not in name)
         for splits in (1, 2, 3):
             Y = gh.nan_filled(M, N)
-            if N % (16 * nt):
+            if refused:
                 with pytest.raises(w4.W4A16Error):
                     _sgemm(gh, Xd, comp, M, N, K, variant=v, splits=splits, Y=Y)
                 continue
@@ -157,8 +159,10 @@ def test_tiled_sparse_grids(gh, M, K, N):
     Xd = gh.dev(X)
     Yref = oracle.gemm(X, d["Qp"], d["s"], None, 128)
     B = oracle.error_bound(X, d["Qp"], d["s"], None, 128)
+    # the 2:4 format runs on the tiled variants with four column tiles per wave (256 columns)
     tiled = [v for v in range(w4.w4a16_gemm_variants())
-             if w4.w4a16_gemm_variant_name(v).startswith("tiled")]
+             if w4.w4a16_gemm_variant_name(v).startswith("tiled")
+             and "_bn256_" in w4.w4a16_gemm_variant_name(v)]
     assert tiled
     for v in tiled:
         for grid in (0, 1, 3, 6, 16):
@@ -185,8 +189,29 @@ def test_tiled_sparse_onehot_exact(gh):
     W16 = oracle.dequant_fp16(d["Qp"], d["s"], None, K, N, 128)
     comp = _compress(gh, d, K, N)
     for v in range(w4.w4a16_gemm_variants()):
-        if not w4.w4a16_gemm_variant_name(v).startswith("tiled"):
+        name = w4.w4a16_gemm_variant_name(v)
+        if not name.startswith("tiled") or "_bn256_" not in name:
             continue
         for grid in (1, 7):
             Y = gh.host(_sgemm(gh, gh.dev(X), comp, M, N, K, variant=v, splits=grid))
             assert np.array_equal(Y.view(np.uint16), W16[ks].view(np.uint16)), (v, grid)
+
+
+def test_sparse_refuses_tiles_without_four_column_tiles_per_wave(gh):
+    """The 2:4 format's loads are laid out for four column tiles per wave: the 128 x 128
+    tiled variant refuses it (an error, nothing launched), and the automatic plan of a
+    shape where dense weights take 128 x 128 tiles still runs and matches the oracle."""
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 128, 5120, 1024
+    _, d, X = _case(M, K, N)
+    comp = _compress(gh, d, K, N)
+    v = [v for v in range(w4.w4a16_gemm_variants())
+         if w4.w4a16_gemm_variant_name(v) == "tiled_bm128_bn128_s3"]
+    assert v
+    with pytest.raises(w4.W4A16Error):
+        _sgemm(gh, gh.dev(X), comp, M, N, K, variant=v[0], splits=0)
+    Y = gh.host(_sgemm(gh, gh.dev(X), comp, M, N, K))
+    Yref = oracle.gemm(X, d["Qp"], d["s"], None, 128)
+    B = oracle.error_bound(X, d["Qp"], d["s"], None, 128)
+    ok, info = oracle.accept(Y, Yref, B)
+    assert ok, info

@@ -17,6 +17,14 @@ LIB_PATH = os.path.join(_HERE, "libw4a16.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                       "(or python -m w4a16_mixed_precision_offline_amd.build_lib)")
+# One HIP runtime per process.  torch's ROCm build ships its own libamdhip64 with the same
+# soname as the system one this library links against: loaded after torch, the library
+# binds to the runtime torch already holds; loaded before it, the process ends up with two
+# runtimes and this library's finds no usable device.  So torch, when present, goes first.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p

@@ -904,11 +904,18 @@ constexpr TiledFn fp8_tiled() {
   if constexpr (MT % 2 == 0) return tiled_kernel<MT, NTW, NS, MODE>;
   else return nullptr;
 }
+// the 2:4 format's loads are laid out for four column tiles per wave (two tiles' kept codes
+// per 16-byte load, all four tiles' positions in one)
+template <int MT, int NTW, int NS>
+constexpr TiledFn sp24_tiled() {
+  if constexpr (NTW == 4) return tiled_kernel<MT, NTW, NS, W_SP24>;
+  else return nullptr;
+}
 
 #define W4A16_TILED(MT, NTW, NS, NAME)                                                       \
   TVariant {                                                                               \
     MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>,       \
-        tiled_kernel<MT, NTW, NS, W_SP24>, nullptr, tiled_kernel<MT, NTW, NS, W_SYM64>,     \
+        sp24_tiled<MT, NTW, NS>(), nullptr, tiled_kernel<MT, NTW, NS, W_SYM64>,            \
         tiled_kernel<MT, NTW, NS, W_ASYM64>, fp8_tiled<MT, NTW, NS, W_SYM8>(),             \
         fp8_tiled<MT, NTW, NS, W_ASYM8>(), tiled_fixup_kernel<MT, NTW>, NAME                \
   }
@@ -925,6 +932,7 @@ const TVariant kTiled[] = {
     W4A16_TILED(4, 4, 3, "tiled_bm64_bn256_s3"),
     W4A16_TILED(2, 4, 4, "tiled_bm32_bn256_s4"),
     W4A16_TILED(1, 4, 4, "tiled_bm16_bn256_s4"),
+    W4A16_TILED(8, 2, 3, "tiled_bm128_bn128_s3"),
 };
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
 const TVariant kTiledF16[] = {
@@ -970,6 +978,12 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   // 64 rows, 64 x 128 up to 64.
   if (variant < 0) {
     variant = M > 64 ? 0 : (f16 ? 1 : 2);
+    // layers up to 128 Mi weights at 65-256 rows: 128 x 128 tiles, twice the tiles of
+    // 128 x 256 for the 256 compute units (measured 1.04-1.14x at M = 128 and 1.02-1.06x at
+    // M = 256 on 8192 x 10240, 5120 x 13824, 13824 x 5120, 4096 x 11008; slower on the
+    // 235 Mi-weight layers and at M >= 1024)
+    if (!f16 && mode != W_SP24 && M > 64 && M <= 256 && (long long)K * N <= (128LL << 20))
+      variant = 5;
     // 128-row tiles would pad M by more than an eighth (M % 128 in 1..64, M < 512): 64-row
     // tiles instead (measured 1.05-1.26x faster at M = 192 on six 7B/70B-class layers, and
     // 1.08-1.18x slower at M = 256 / 384 where 128-row tiles pad nothing)
