@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the W4A16 GEMM (shared by tests, smoke and bench).
 
 This package produces inputs only: activations, 4-bit weight codes, fp16 scales,
-4-bit zero-points and 2:4 keep-masks, plus the canonical packing of the 4-bit
+4-bit zero-points, 2:4 keep-masks, MXFP4 codes and E8M0 scale bytes, plus the canonical packing of the 4-bit
 codes into int32 words (the storage format the library accepts).  It holds none
 of the method's arithmetic: no dequantization, no matrix product, no repack.
 """
@@ -17,4 +17,5 @@ from .inputs import (  # noqa: F401
     seed_for_activations,
     seed_for_weights,
     weights,
+    weights_mxfp4,
 )

@@ -178,3 +178,17 @@ def activations_fp8(w: Workload, seed: Optional[int] = None):
     xs = torch.from_numpy(x / a[:, None])
     codes = xs.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
     return codes, a
+
+
+def weights_mxfp4(w: Workload, seed: Optional[int] = None) -> dict:
+    """MXFP4 weights for the block-scaled entry points: E2M1 codes uniform over all
+    16 (every code is a valid value) packed 8 per int32 along K like the 4-bit
+    codes of `weights`, and one E8M0 scale byte per 32 rows of a column, uniform in
+    [119, 124] (scales 2^-8 .. 2^-3: weights up to 6 * 2^-3, the range of the
+    group-quantized weights).  Returns {"q": uint8 [K, N], "Qp": int32 [K/8, N],
+    "E": uint8 [K/32, N]}."""
+    rng = np.random.Generator(np.random.PCG64(
+        seed_for_weights(w.cfg, w.K, w.N) + 17 if seed is None else seed))
+    q = rng.integers(0, 16, size=(w.K, w.N), dtype=np.uint8)
+    E = rng.integers(119, 125, size=(w.K // 32, w.N), dtype=np.uint8)
+    return {"q": q, "Qp": pack_nibbles_along_k(q), "E": E}

@@ -11,14 +11,20 @@ definitions it implements and the passages they follow.
 from .w4a16_ref import (  # noqa: F401
     accept,
     activations_w4a8,
+    decode_e2m1,
     decode_e4m3,
+    decode_e8m0,
+    dequant_mxfp4,
     check_24,
     dequant,
     dequant_fp16,
     error_bound,
+    error_bound_mxfp4,
     error_bound_w4a8,
     gemm,
     gemm_exact,
+    gemm_mxfp4,
+    gemm_mxfp4_sampled,
     gemm_sampled,
     gemm_w4a8,
     gemm_w4a8_sampled,

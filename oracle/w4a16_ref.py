@@ -31,6 +31,14 @@ Readings where the pages are silent (each is also listed in the design notes):
     activations are OCP E4M3 codes with an optional fp32 scale per row; the
     product is the same definition on their exact values (decode_e4m3 and
     gemm_w4a8 below).
+  * Dequantization inside the matrix unit ([P1] section "与 Blackwell NVFP4 的对比":
+    FP4 weights with micro-block scales, turned into real values inside the matrix
+    instruction): the FP4 format here is the OCP Microscaling one, MXFP4 -- E2M1
+    codes, one E8M0 (power-of-two) scale per 32 consecutive weights along K.  It is
+    the micro-block format that gfx950's block-scaled matrix instructions take; the
+    page's NVFP4 (E4M3 scales per 16) has no such instruction there.  Codes are
+    packed 8 per int32 along K as above; scales E[K/32, N] are bytes.  The
+    activations are those of W4A8 (decode_e2m1, decode_e8m0, gemm_mxfp4 below).
 
 Pinned by tests/test_oracle.py (exhaustive nibble tables, exact-rational brute
 force, closed forms and invariants); no function here is "parity unpinned".
@@ -232,6 +240,65 @@ def gemm_w4a8_sampled(X8, xscale, Qp, s, Zp, group, rows, cols):
     K = X8.shape[1]
     N = Qp.shape[1]
     W = dequant(Qp, s, Zp, K, N, group, cols=cols)
+    r = np.asarray(rows)
+    Xr = activations_w4a8(X8[r], None if xscale is None else np.asarray(xscale)[r])
+    return Xr @ W, np.abs(Xr) @ np.abs(W)
+
+
+# -- MXFP4 weights (dequantization inside the matrix instruction) ---------------
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """Real values (float64) of OCP E2M1 4-bit codes (OCP Microscaling Formats v1.0,
+    FP4 element): sign bit 3, exponent bits 2-1 (bias 1), mantissa bit 0.
+
+    exponent field e = 0: (-1)^sign * m/2 (subnormal: 0 or 0.5);
+    otherwise:            (-1)^sign * 2^(e-1) * (1 + m/2).
+    No infinities or NaN: the 16 codes are +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+    """
+    c = np.asarray(codes).astype(np.int64) & 15
+    sign = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    normal = np.ldexp(1.0 + m / 2.0, (e - 1).astype(np.int64))
+    return sign * np.where(e == 0, m / 2.0, normal)
+
+
+def decode_e8m0(codes: np.ndarray) -> np.ndarray:
+    """Real values (float64) of OCP E8M0 scale bytes: 2^(e - 127), e = 255 is NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))
+
+
+def dequant_mxfp4(Qp: np.ndarray, E: np.ndarray, K: int, N: int,
+                  cols: Optional[Sequence[int]] = None) -> np.ndarray:
+    """W[k, n] = e2m1(q[k, n]) * 2^(E[k // 32, n] - 127) in float64 (exact)."""
+    q = unpack_codes_k(Qp, K, cols)
+    Ec = E if cols is None else E[:, np.asarray(cols)]
+    scale = np.repeat(decode_e8m0(Ec), 32, axis=0)
+    return decode_e2m1(q) * scale
+
+
+def gemm_mxfp4(X8: np.ndarray, xscale: Optional[np.ndarray], Qp: np.ndarray,
+               E: np.ndarray) -> np.ndarray:
+    """Y[m, n] = a[m] * sum_k x8[m, k] * e2m1(q[k, n]) * 2^(E[k // 32, n] - 127),
+    float64 [M, N]; x8 are E4M3 activation codes with optional fp32 row scales a."""
+    K = X8.shape[1]
+    N = Qp.shape[1]
+    return activations_w4a8(X8, xscale) @ dequant_mxfp4(Qp, E, K, N)
+
+
+def error_bound_mxfp4(X8: np.ndarray, xscale: Optional[np.ndarray], Qp: np.ndarray,
+                      E: np.ndarray) -> np.ndarray:
+    """Bnd[m, n] = sum_k |a[m] * x8[m, k] * W[k, n]|."""
+    K = X8.shape[1]
+    N = Qp.shape[1]
+    return np.abs(activations_w4a8(X8, xscale)) @ np.abs(dequant_mxfp4(Qp, E, K, N))
+
+
+def gemm_mxfp4_sampled(X8, xscale, Qp, E, rows, cols):
+    """Y and Bnd of the MXFP4 product at the cross product rows x cols only."""
+    K = X8.shape[1]
+    N = Qp.shape[1]
+    W = dequant_mxfp4(Qp, E, K, N, cols=cols)
     r = np.asarray(rows)
     Xr = activations_w4a8(X8[r], None if xscale is None else np.asarray(xscale)[r])
     return Xr @ W, np.abs(Xr) @ np.abs(W)

@@ -661,3 +661,194 @@ def test_generator_fp8_activations():
     assert codes.dtype == np.uint8 and a.dtype == np.float32 and not np.isnan(v).any()
     # every row uses the full E4M3 range: its largest magnitude is 448
     assert np.all(np.abs(v).max(axis=1) == 448.0)
+
+
+# ---- MXFP4 weights (block scales applied inside the matrix instruction) ---------
+def _e2m1_fixture():
+    out = []
+    with open(os.path.join(GOLD, "e2m1_values.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                code, val = line.split()
+                out.append((int(code, 16), float(val)))
+    return out
+
+
+def test_e2m1_golden_fixture_is_every_code():
+    fx = _e2m1_fixture()
+    assert sorted(c for c, _ in fx) == list(range(16))
+    for code, val in fx:
+        v = float(oracle.decode_e2m1(np.array([code]))[0])
+        assert v == val and np.signbit(v) == np.signbit(val), code
+
+
+def test_e8m0_vs_library():
+    # every scale byte against torch's float8_e8m0fnu (a library decode of the format)
+    import torch
+    c = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(c).view(torch.float8_e8m0fnu).float().double().numpy()
+    assert np.array_equal(oracle.decode_e8m0(c), lib, equal_nan=True)
+    assert oracle.decode_e8m0(np.array([127], np.uint8))[0] == 1.0
+
+
+def _mx_exact(X8, a, Qp, E):
+    """Brute force in exact rationals with Python integers: unpack nibble k % 8 of word
+    k // 8, E2M1 from its bit fields, the block scale 2^(E[k // 32] - 127)."""
+    M, K = X8.shape
+    N = Qp.shape[1]
+    fx = dict(_e2m1_fixture())
+    e4 = dict(_e4m3_exact_table())
+    out = []
+    for m in range(M):
+        row = []
+        am = Fraction(float(a[m])) if a is not None else Fraction(1)
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                code = (int(Qp[k // 8, n]) & 0xFFFFFFFF) >> (4 * (k % 8)) & 15
+                e = int(E[k // 32, n]) - 127
+                sc = Fraction(2) ** e
+                acc += e4[int(X8[m, k])] * Fraction(fx[code]) * sc
+            row.append(am * acc)
+        out.append(row)
+    return out
+
+
+def _e4m3_exact_table():
+    # exact values of every finite E4M3 code from its bit fields (no float arithmetic)
+    t = []
+    for c in range(256):
+        s, e, mm = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and mm == 7:
+            continue
+        v = Fraction(mm, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(mm, 8)) * Fraction(2) ** (e - 7)
+        t.append((c, -v if s else v))
+    return t
+
+
+@pytest.mark.parametrize("M,K,N,scaled", [(1, 64, 8, False), (3, 128, 8, True), (2, 96, 16, True)])
+def test_mxfp4_gemm_vs_exact_rationals(M, K, N, scaled):
+    rng = np.random.default_rng(11 * M + K + N)
+    X8 = _random_e4m3(rng, (M, K))
+    a = rng.uniform(0.001, 0.01, size=M).astype(np.float32) if scaled else None
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    E = rng.integers(110, 140, size=(K // 32, N), dtype=np.uint8)
+    Y = oracle.gemm_mxfp4(X8, a, Qp, E)
+    B = oracle.error_bound_mxfp4(X8, a, Qp, E)
+    Ex = _mx_exact(X8, a, Qp, E)
+    for m in range(M):
+        for n in range(N):
+            assert abs(Fraction(Y[m, n]) - Ex[m][n]) <= Fraction((K + 2) * 2.0 ** -53) * Fraction(B[m, n])
+
+
+def test_mxfp4_onehot_rows_select_scaled_codes():
+    # x8 = 1.0 at row k: row m of Y is e2m1(q[k, n]) * 2^(E[k // 32, n] - 127) exactly;
+    # rows on both sides of every 32-row boundary pin the block index
+    K, N = 128, 16
+    q = np.array([[(3 * k + 5 * n) % 16 for n in range(N)] for k in range(K)], dtype=np.uint8)
+    E = np.array([[120 + (b + n) % 7 for n in range(N)] for b in range(K // 32)], dtype=np.uint8)
+    ks = [0, 1, 31, 32, 33, 63, 64, 95, 96, 127]
+    X8 = np.zeros((len(ks), K), dtype=np.uint8)
+    for m, k in enumerate(ks):
+        X8[m, k] = 0x38
+    fx = dict(_e2m1_fixture())
+    Y = oracle.gemm_mxfp4(X8, None, words_from_codes_k(q), E)
+    for m, k in enumerate(ks):
+        for n in range(N):
+            assert Y[m, n] == fx[(3 * k + 5 * n) % 16] * 2.0 ** (int(E[k // 32, n]) - 127)
+
+
+def test_mxfp4_unit_scales_reduce_to_an_integer_product():
+    # with every block scale 2^0 and codes restricted to the integer values {0, 1, 2,
+    # 3, 4, 6} (and negatives), Y is an integer matrix product (exact in int64)
+    rng = np.random.default_rng(8)
+    M, K, N = 4, 256, 24
+    ints = {2: 1, 4: 2, 5: 3, 6: 4, 7: 6, 10: -1, 12: -2, 13: -3, 14: -4, 15: -6, 0: 0}
+    codes = np.array(list(ints.keys()), dtype=np.uint8)
+    q = rng.choice(codes, size=(K, N))
+    Wi = np.vectorize(ints.get)(q).astype(np.int64)
+    Xi = rng.integers(-8, 9, size=(M, K))
+    X8 = np.array([[dict((int(v), c) for c, v in _e4m3_exact_table() if v.denominator == 1
+                          and -8 <= v <= 8 and not (v == 0 and c == 0x80))[int(x)] for x in r]
+                   for r in Xi], dtype=np.uint8)
+    E = np.full((K // 32, N), 127, dtype=np.uint8)
+    Y = oracle.gemm_mxfp4(X8, None, words_from_codes_k(q), E)
+    assert np.array_equal(Y, (Xi @ Wi).astype(np.float64))
+
+
+def _pins_mx_pass(mod):
+    checks = []
+    for code, val in _e2m1_fixture():
+        checks.append(float(mod.decode_e2m1(np.array([code]))[0]) == val)
+    rng = np.random.default_rng(9)
+    M, K, N = 2, 128, 8
+    X8 = _random_e4m3(rng, (M, K))
+    a = np.array([0.5, 0.003], dtype=np.float32)
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    E = rng.integers(115, 135, size=(K // 32, N), dtype=np.uint8)
+    Y = mod.gemm_mxfp4(X8, a, Qp, E)
+    Ex = _mx_exact(X8, a, Qp, E)
+    checks.append(all(abs(Fraction(Y[m, n]) - Ex[m][n]) < Fraction(1, 10 ** 9)
+                      for m in range(M) for n in range(N)))
+    return all(checks)
+
+
+def test_mxfp4_planted_mistakes_are_caught():
+    import types
+    assert _pins_mx_pass(ref)
+
+    def mutant(**overrides):
+        m = types.ModuleType("mutant")
+        m.__dict__.update({k: getattr(ref, k) for k in dir(ref) if not k.startswith("__")})
+        m.__dict__.update(overrides)
+        for name in ("dequant_mxfp4", "gemm_mxfp4"):
+            if name not in overrides:
+                f = getattr(ref, name)
+                m.__dict__[name] = types.FunctionType(f.__code__, m.__dict__, name, f.__defaults__)
+        return m
+
+    def e2m1_bias0(codes):  # exponent bias 0 instead of 1
+        return ref.decode_e2m1(codes) * 2.0
+
+    def e2m1_no_subnormal(codes):  # e = 0 read as 2^-1 * (1 + m/2)
+        c = np.asarray(codes).astype(np.int64) & 15
+        v = ref.decode_e2m1(c)
+        e0 = ((c >> 1) & 3) == 0
+        mag = 0.5 * (1 + (c & 1) / 2.0)
+        return np.where(e0, np.where(c >> 3, -mag, mag), v)
+
+    def e8m0_bias128(codes):
+        return ref.decode_e8m0(codes) / 2.0
+
+    def dq_block16(Qp, E, K, N, cols=None):  # the scale block read as 16 rows
+        q = ref.unpack_codes_k(Qp, K, cols)
+        Ec = E if cols is None else E[:, np.asarray(cols)]
+        sc = np.repeat(ref.decode_e8m0(Ec), 16, axis=0)
+        sc = np.concatenate([sc, sc])[:K]
+        return ref.decode_e2m1(q) * sc
+
+    def dq_nibbles_swapped(Qp, E, K, N, cols=None):  # high nibble of each byte first
+        q = ref.unpack_codes_k(Qp, K, cols)
+        q = q.reshape(K // 2, 2, -1)[:, ::-1, :].reshape(K, -1)
+        Ec = E if cols is None else E[:, np.asarray(cols)]
+        return ref.decode_e2m1(q) * np.repeat(ref.decode_e8m0(Ec), 32, axis=0)
+
+    mutants = [
+        mutant(decode_e2m1=e2m1_bias0),
+        mutant(decode_e2m1=e2m1_no_subnormal),
+        mutant(decode_e8m0=e8m0_bias128),
+        mutant(dequant_mxfp4=dq_block16),
+        mutant(dequant_mxfp4=dq_nibbles_swapped),
+    ]
+    for i, m in enumerate(mutants):
+        assert not _pins_mx_pass(m), f"MXFP4 mutant {i} survived the pins"
+
+
+def test_generator_mxfp4_weights():
+    from gen import Workload, weights_mxfp4
+    d = weights_mxfp4(Workload(cfg=9, M=1, K=256, N=32), seed=3)
+    assert d["Qp"].shape == (32, 32) and d["E"].shape == (8, 32)
+    assert d["E"].min() >= 119 and d["E"].max() <= 124
+    assert np.array_equal(ref.unpack_codes_k(d["Qp"], 256), d["q"])
+    assert len(np.unique(d["q"])) == 16
