@@ -263,6 +263,45 @@ int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const
                    const void* zp, uint16_t* Y, int M, int N, int K, int group, int variant,
                    int splits, void* stream);
 
+/* ---- MXFP4 weights x fp8 activations: dequantization inside the matrix instruction ---
+ * FP4 weights with micro-block scales that the matrix unit applies itself, instead of
+ * unpacking the weights in registers first (dingiv.github.io "Marlin", section "与
+ * Blackwell NVFP4 的对比").  The format is OCP MXFP4, the micro-block format of gfx950's
+ * block-scaled matrix instruction: weight w[k][n] = e2m1(q[k][n]) * 2^(e[k/32][n] - 127),
+ * E2M1 codes (sign, 2-bit exponent of bias 1, 1 mantissa bit: +-{0, .5, 1, 1.5, 2, 3, 4,
+ * 6}) and one E8M0 scale byte per 32 rows along K (255 is NaN: unspecified outputs).
+ * w4a8_mx_repack: one-time layout change, like w4a16_repack:
+ *   q  (device, in)  int32 [K/8][N]: code of row k, column n in bits 4(k%8) .. +3 of
+ *      word [k/8][n] (the canonical packing of w4a16_repack);
+ *   e  (device, in)  uint8 [K/32][N]: E8M0 scale of rows 32b .. 32b+31 of column n;
+ *   wp (device, out) K*N/2 bytes: code blocks [N/16][K/128] of 1 KiB, lane l of a block
+ *      holding column l%16, rows 32(l/16) .. +31, two codes per byte, low nibble first
+ *      (the instruction's operand order; each word is a canonical word, unchanged);
+ *   sp (device, out) K*N/32 bytes: scale blocks [N/16][K/128] of 64 bytes, byte l the
+ *      scale of lane l's 32 rows.
+ *   K % 128 == 0, N % 16 == 0, K*N/8 < 2^31; q, wp, sp 16-byte aligned.  Asynchronous
+ *   on `stream`; the caller owns every buffer.
+ * w4a8_mx_gemm: Y (device, out) fp16 [M][N] = diag(a) * X (device, in) * W, with X8 and
+ *   xscale exactly as in w4a8_gemm and wp, sp from w4a8_mx_repack.  Runs on the tiled
+ *   kernel for every M (v_mfma_scale_f32_16x16x128_f8f6f4: codes as the FP4 operand with
+ *   the lane's E8M0 byte as its block scale, X as the FP8 operand with unit scale), fp32
+ *   accumulation, a[m] in fp32 before the one rounding of Y to fp16 (nearest-even).
+ *   Shapes, 16-byte alignment of X8, wp, sp and Y, error codes, asynchronous execution,
+ *   the library-owned (or w4a16_set_workspace) stream-K workspace and bitwise
+ *   reproducibility are those of w4a16_gemm.
+ * w4a8_mx_gemm_plan: the same with an explicit tiled variant (0 .. w4a8_mx_variants()-1,
+ *   named by w4a8_mx_variant_name, the tiled variants of w4a16_gemm_variants in the same
+ *   order; -1 = automatic) and `grid` persistent workgroups (0 = automatic).  Variants
+ *   with an odd number of 16-row tiles return W4A16_ERR_ARG. */
+int w4a8_mx_repack(const int32_t* q, const uint8_t* e, void* wp, void* sp, int K, int N,
+                   void* stream);
+int w4a8_mx_gemm(const uint8_t* X8, const float* xscale, const void* wp, const void* sp,
+                 uint16_t* Y, int M, int N, int K, void* stream);
+int w4a8_mx_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const void* sp,
+                      uint16_t* Y, int M, int N, int K, int variant, int grid, void* stream);
+int w4a8_mx_variants(void);
+const char* w4a8_mx_variant_name(int variant);
+
 /* ---- calibration kernels (measurement only) ---------------------------------------
  * The achievable ceilings the GEMM's rates are set against, beside the published peaks.
  * w4a16_probe_read: one plain streaming read of `bytes` bytes at device pointer p

@@ -108,3 +108,21 @@ def sparse24_compress(q: np.ndarray, K: int, N: int):
                     meta[:, :, lanes] |= (kk.transpose(1, 0, 2).astype(np.uint32)
                                           << np.uint32(16 * h + 2 * e))
     return vp, meta
+
+
+def mx_repack(Qp: np.ndarray, E: np.ndarray, K: int, N: int):
+    """The MXFP4 layout, written as loops over the documented index map: code block
+    (t, kb) of 1 KiB, lane l, word w = canonical word kb*16 + 4(l//16) + w of column
+    16t + l%16; scale block (t, kb) of 64 bytes, byte l = E[kb*4 + l//16, 16t + l%16]."""
+    T, Gk = N // 16, K // 128
+    words = np.zeros((T, Gk, 64, 4), dtype=np.uint32)
+    scales = np.zeros((T, Gk, 64), dtype=np.uint8)
+    Qu = Qp.view(np.uint32)
+    for t in range(T):
+        for kb in range(Gk):
+            for l in range(64):
+                col = 16 * t + l % 16
+                for w in range(4):
+                    words[t, kb, l, w] = Qu[kb * 16 + 4 * (l // 16) + w, col]
+                scales[t, kb, l] = E[kb * 4 + l // 16, col]
+    return words.reshape(-1), scales.reshape(-1)

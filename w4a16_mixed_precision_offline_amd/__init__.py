@@ -57,6 +57,11 @@ _SIGS = {
     "w4a8_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "w4a16_set_workspace": (_I, [_P, ctypes.c_size_t, _P]),
     "w4a8_gemm_plan": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "w4a8_mx_repack": (_I, [_P, _P, _P, _P, _I, _I, _P]),
+    "w4a8_mx_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P]),
+    "w4a8_mx_gemm_plan": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "w4a8_mx_variants": (_I, []),
+    "w4a8_mx_variant_name": (ctypes.c_char_p, [_I]),
     "w4a16_probe_read": (_I, [_P, _SZ, _P, _P]),
     "w4a16_probe_mfma": (_I, [_I, _I, _P, _P]),
     "w4a16_probe_mfma_flops": (ctypes.c_double, [_I, _I]),
@@ -231,6 +236,40 @@ def w4a8_gemm_plan(X8, xscale, wp, sp, zp, Y, M, N, K, group, variant=-1, splits
     _check("w4a8_gemm_plan", _lib.w4a8_gemm_plan(
         _ptr(X8), _ptr(xscale), _ptr(wp), _ptr(sp), _ptr(zp), _ptr(Y), M, N, K, group, variant,
         splits, _stream(stream)))
+
+
+# ---- MXFP4 weights x fp8 activations (block scales inside the matrix instruction) --
+def w4a8_mx_repack(q, e, wp, sp, K, N, stream=None):
+    _check("w4a8_mx_repack", _lib.w4a8_mx_repack(_ptr(q), _ptr(e), _ptr(wp), _ptr(sp), K, N,
+                                                 _stream(stream)))
+
+
+def w4a8_mx_gemm(X8, xscale, wp, sp, Y, M, N, K, stream=None):
+    _check("w4a8_mx_gemm", _lib.w4a8_mx_gemm(_ptr(X8), _ptr(xscale), _ptr(wp), _ptr(sp),
+                                             _ptr(Y), M, N, K, _stream(stream)))
+
+
+def w4a8_mx_gemm_plan(X8, xscale, wp, sp, Y, M, N, K, variant=-1, grid=0, stream=None):
+    _check("w4a8_mx_gemm_plan", _lib.w4a8_mx_gemm_plan(
+        _ptr(X8), _ptr(xscale), _ptr(wp), _ptr(sp), _ptr(Y), M, N, K, variant, grid,
+        _stream(stream)))
+
+
+def w4a8_mx_variants() -> int:
+    return _lib.w4a8_mx_variants()
+
+
+def w4a8_mx_variant_name(variant: int):
+    n = _lib.w4a8_mx_variant_name(variant)
+    return None if n is None else n.decode()
+
+
+def alloc_mx(K: int, N: int, device="cuda"):
+    """Empty device buffers (torch uint8) for the MXFP4 codes wp (K*N/2 bytes) and block
+    scales sp (K*N/32 bytes) of w4a8_mx_repack."""
+    import torch
+    return (torch.empty(K * N // 2, dtype=torch.uint8, device=device),
+            torch.empty(K * N // 32, dtype=torch.uint8, device=device))
 
 
 # ---- calibration kernels ---------------------------------------------------------

@@ -535,6 +535,37 @@ int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint
   return w4a8_gemm_plan(X8, xscale, wp, sp, zp, Y, M, N, K, group, -1, 0, stream);
 }
 
+// ---- MXFP4 weights x fp8 activations: scales applied inside the matrix instruction ----
+int w4a8_mx_repack(const int32_t* q, const uint8_t* e, void* wp, void* sp, int K, int N,
+                   void* stream) {
+  if (!q || !e || !wp || !sp) return W4A16_ERR_NULL;
+  int rc = check_weight_shape(K, N, KBLK);
+  if (rc) return rc;
+  if (!aligned16(q) || !aligned16(wp) || !aligned16(sp)) return W4A16_ERR_ALIGN;
+  if ((rc = check_device(nullptr))) return rc;
+  return launched(launch_mx_repack(q, e, static_cast<uint32_t*>(wp), static_cast<uint8_t*>(sp),
+                                   K, N, static_cast<hipStream_t>(stream)));
+}
+
+int w4a8_mx_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const void* sp,
+                      uint16_t* Y, int M, int N, int K, int variant, int grid, void* stream) {
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(X8);
+  const uint16_t* S = static_cast<const uint16_t*>(sp);
+  int rc = check_gemm_args(X, wp, S, nullptr, Y, M, N, K, KBLK);
+  if (rc) return rc;
+  if (xscale && (reinterpret_cast<uintptr_t>(xscale) & 3u) != 0) return W4A16_ERR_ALIGN;
+  if (variant < -1 || variant >= tiled_variant_count(W_MX4) || grid < 0) return W4A16_ERR_ARG;
+  return run_tiled(W_MX4, X, wp, S, nullptr, Y, M, N, K, variant, grid, stream, xscale);
+}
+
+int w4a8_mx_variants(void) { return tiled_variant_count(W_MX4); }
+const char* w4a8_mx_variant_name(int variant) { return tiled_variant_name(W_MX4, variant); }
+
+int w4a8_mx_gemm(const uint8_t* X8, const float* xscale, const void* wp, const void* sp,
+                 uint16_t* Y, int M, int N, int K, void* stream) {
+  return w4a8_mx_gemm_plan(X8, xscale, wp, sp, Y, M, N, K, -1, 0, stream);
+}
+
 // ---- calibration kernels -------------------------------------------------------------
 int w4a16_probe_read(const void* p, size_t bytes, uint32_t* out, void* stream) {
   if (!p || !out) return W4A16_ERR_NULL;

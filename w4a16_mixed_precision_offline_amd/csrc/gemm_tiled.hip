@@ -209,7 +209,7 @@ struct DmaPlan {
   // 2:4: two tiles' kept codes per 16-byte load, all four tiles' positions in one
   static constexpr int NW = MODE == W_SP24 ? NTW / 2 + NTW / 4 : MODE == W_FP16 ? 4 * NTW : NTW;
   static constexpr int NV = NX + NW + (mode_asym(MODE) ? 2 : MODE == W_FP16 ? 0 : 1);
-  static constexpr uint32_t SH = mode_g64(MODE) ? 2u : 1u;  // scale / zero rows per block
+  static constexpr uint32_t SH = mode_scale64(MODE) ? 2u : 1u;  // 32-byte scale rows per block
   u32x4 rx;
   uint32_t xoff[NX];
   WSrc<NTW> R;
@@ -511,6 +511,53 @@ __device__ __forceinline__ void compute_kblock_fp8(const char* xb, const char* w
   }
 }
 
+// One k-block of MXFP4 weights: the codes go to the block-scaled matrix instruction as
+// they are (E2M1 operand A), with the lane's E8M0 byte as its scale, and the fp8 rows of
+// X as operand B (unit scale); the instruction applies the scales of the 32-row blocks
+// itself, so there is no unpacking and no rescaling.  The two operands place K
+// differently: an FP4 lane (l/16 = g) holds rows 32g .. 32g+31 in order (so its scale
+// byte covers exactly its own codes: lane l of the 1 KiB block holds column l%16, rows
+// 32g .. +31), while an FP8 lane holds rows 16g .. 16g+15 in its first 16 bytes and
+// 64+16g .. +15 in its last 16 (measured with one-hot activations).  The X fragment of
+// lane l is therefore chunks g and 4+g of row 16i + l%16 of the swizzled tile (two
+// 16-byte reads).  The loads of a later k-block are spread over the row tiles' groups.
+template <int MT, int NTW, int MODE>
+__device__ __forceinline__ void compute_kblock_mx(const char* xb, const char* wl,
+                                                  float4v (&acc)[MT][NTW],
+                                                  const uint32_t (&aoff)[4], int lane,
+                                                  const DmaPlan<MT, NTW, MODE>& dma) {
+  typedef WLds<NTW, MODE> L;
+  constexpr int NVL = DmaPlan<MT, NTW, MODE>::NV;
+  int8v b[NTW];
+  int sc[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(wl + t * 1024 + lane * 16);
+    b[t] = int8v{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+    sc[t] = (int)*reinterpret_cast<const uint8_t*>(wl + L::SCALES + t * 64 + lane);
+  }
+  auto frag = [&](int i) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(xb + aoff[0] + i * 2048);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(xb + aoff[1] + i * 2048);
+    return int8v{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  int8v xa[2];
+  xa[0] = frag(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int q = i; q < NVL; q += MT) dma.issue(q);
+    if (i + 1 < MT) xa[(i + 1) & 1] = frag(i + 1);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+      acc[i][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          b[t], xa[i & 1], acc[i][t], 4, 0, 0, sc[t], 0, 127);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // vmcnt(n) with the other counters left alone (gfx9 encoding)
 __device__ __forceinline__ constexpr int vmcnt_enc(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
@@ -610,8 +657,9 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
   uint32_t aoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    aoff[j] = F8 ? swz8(lane & 15, 2 * j + (lane >> 5)) + 8 * ((lane >> 4) & 1)
-                 : swz(lane & 15, 4 * j + (lane >> 4));
+    aoff[j] = MODE == W_MX4 ? swz8(lane & 15, (lane >> 4) + 4 * (j & 1))
+              : F8          ? swz8(lane & 15, 2 * j + (lane >> 5)) + 8 * ((lane >> 4) & 1)
+                            : swz(lane & 15, 4 * j + (lane >> 4));
 
   // logical workgroup index: consecutive indices on one XCD (the hardware deals
   // workgroups to the 8 XCDs round-robin)
@@ -645,7 +693,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
     int nvalid = ntiles16 - t_first;
     nvalid = nvalid < 0 ? 0 : (nvalid > NTW ? NTW : nvalid);
     WSrc<NTW> R;
-    constexpr int SH = mode_g64(MODE) ? 2 : 1;  // scale / zero-point rows per block
+    constexpr int SH = mode_scale64(MODE) ? 2 : 1;  // 32-byte scale rows per block
     if (MODE != W_FP16) {
       // scales: lane L < 8*SH*NTW loads bytes 4(L % 8SH) .. +3 of tile L / 8SH's row(s)
       R.s = rsrc_words(Sp + (size_t)t_first * Gk * 16 * SH, (uint32_t)(nvalid * Gk * 32 * SH));
@@ -770,6 +818,10 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
         compute_kblock_sp24<MT, NTW>(lds + d * STAGE,
                                      lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES, acc,
                                      aoff, lane, magic, plan);
+      else if constexpr (MODE == W_MX4)
+        compute_kblock_mx<MT, NTW, MODE>(lds + d * STAGE,
+                                         lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES,
+                                         acc, aoff, lane, plan);
       else if constexpr (F8)
         compute_kblock_fp8<MT, NTW, MODE>(lds + d * STAGE,
                                           lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES,
@@ -893,7 +945,7 @@ typedef void (*FixupFn)(const float*, uint16_t*, TiledArgs);
 
 struct TVariant {
   int MT, NTW, NS;
-  TiledFn sym, asym, sp24, f16, sym64, asym64, sym8, asym8;
+  TiledFn sym, asym, sp24, f16, sym64, asym64, sym8, asym8, mx4;
   FixupFn fixup;
   const char* name;
 };
@@ -917,13 +969,14 @@ constexpr TiledFn sp24_tiled() {
     MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>,       \
         sp24_tiled<MT, NTW, NS>(), nullptr, tiled_kernel<MT, NTW, NS, W_SYM64>,            \
         tiled_kernel<MT, NTW, NS, W_ASYM64>, fp8_tiled<MT, NTW, NS, W_SYM8>(),             \
-        fp8_tiled<MT, NTW, NS, W_ASYM8>(), tiled_fixup_kernel<MT, NTW>, NAME                \
+        fp8_tiled<MT, NTW, NS, W_ASYM8>(), fp8_tiled<MT, NTW, NS, W_MX4>(),                \
+        tiled_fixup_kernel<MT, NTW>, NAME                                                   \
   }
 // the fp16 baseline moves four times the weight bytes: its own LDS-sized tiles
 #define W4A16_TILED_F16(MT, NTW, NS, NAME)                                                    \
   TVariant {                                                                               \
     MT, NTW, NS, nullptr, nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_FP16>, nullptr,     \
-        nullptr, nullptr, nullptr, tiled_fixup_kernel<MT, NTW>, NAME                       \
+        nullptr, nullptr, nullptr, nullptr, tiled_fixup_kernel<MT, NTW>, NAME              \
   }
 
 const TVariant kTiled[] = {
@@ -950,6 +1003,7 @@ TiledFn variant_fn(const TVariant& v, int mode) {
          : mode == W_ASYM64 ? v.asym64
          : mode == W_SYM8   ? v.sym8
          : mode == W_ASYM8  ? v.asym8
+         : mode == W_MX4    ? v.mx4
          : mode == W_SYM    ? v.sym
                             : nullptr;
 }
@@ -988,6 +1042,8 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // tiles instead (measured 1.05-1.26x faster at M = 192 on six 7B/70B-class layers, and
     // 1.08-1.18x slower at M = 256 / 384 where 128-row tiles pad nothing)
     if (!f16 && M > 128 && M < 512 && M % 128 != 0 && M % 128 <= 64) variant = 2;
+    // MXFP4 has no skinny kernel: up to 32 rows take the 32-row tile
+    if (mode == W_MX4 && M <= 32) variant = 3;
     if (!f16) {
       // a layer too small to give the chip a thousand (tile, k-block) units with these
       // tiles (3072 x 768: 72 at M = 128) runs on 16-row tiles instead, which gives

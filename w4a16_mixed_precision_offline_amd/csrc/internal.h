@@ -57,6 +57,12 @@ hipError_t launch_sparse_compress(const int32_t* q, const uint16_t* s, uint32_t*
 hipError_t launch_sparse_decompress(const uint32_t* vp, const uint32_t* meta, const uint16_t* sp,
                                     int32_t* q, uint16_t* s, int K, int N, int group,
                                     hipStream_t st);
+// MXFP4: canonical E2M1 codes (int32 [K/8, N], 8 along K) and E8M0 scales (bytes
+// [K/32, N]) -> 1 KiB code blocks [N/16][K/128] (lane l: column l%16, rows 32(l/16) ..
+// +31, two codes per byte, low nibble first) and scale blocks [N/16][K/128][64 bytes]
+// (byte l: the scale of lane l's 32 rows).
+hipError_t launch_mx_repack(const int32_t* q, const uint8_t* e, uint32_t* wp, uint8_t* sp,
+                            int K, int N, hipStream_t st);
 hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
                           uint16_t* W, int K, int N, int group, hipStream_t st);
 
@@ -68,7 +74,10 @@ hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
 enum WMode {
   W_SYM = 0, W_ASYM = 1, W_FP16 = 2, W_SP24 = 3, W_SYM64 = 4, W_ASYM64 = 5, W_SYMB = 6,
   W_ASYMB = 7, W_SYM8 = 8, W_ASYM8 = 9, W_SYMB64 = 10, W_ASYMB64 = 11, W_SYM8G64 = 12,
-  W_ASYM8G64 = 13
+  W_ASYM8G64 = 13,
+  // MXFP4 weights (E2M1 codes, one E8M0 scale per 32 rows along K) with fp8 activations;
+  // the scales go to the block-scaled matrix instruction (tiled kernel only)
+  W_MX4 = 14
 };
 __host__ __device__ constexpr bool mode_asym(int m) {
   return m == W_ASYM || m == W_ASYM64 || m == W_ASYMB || m == W_ASYM8 || m == W_ASYMB64 ||
@@ -82,11 +91,14 @@ __host__ __device__ constexpr bool mode_bf16(int m) {
   return m == W_SYMB || m == W_ASYMB || m == W_SYMB64 || m == W_ASYMB64;
 }
 __host__ __device__ constexpr bool mode_fp8(int m) {
-  return m == W_SYM8 || m == W_ASYM8 || m == W_SYM8G64 || m == W_ASYM8G64;
+  return m == W_SYM8 || m == W_ASYM8 || m == W_SYM8G64 || m == W_ASYM8G64 || m == W_MX4;
 }
+// 64 scale bytes per 1 KiB code block: two fp16 rows (groups of 64) or the 64 E8M0 bytes
+// of MXFP4 (one per lane of the block)
+__host__ __device__ constexpr bool mode_scale64(int m) { return mode_g64(m) || m == W_MX4; }
 // packed 4-bit codes with scales (and zero-points): the dense repacked formats
 __host__ __device__ constexpr bool mode_dense4(int m) {
-  return m != W_FP16 && m != W_SP24 && m >= 0 && m <= W_ASYM8G64;
+  return m != W_FP16 && m != W_SP24 && m >= 0 && m <= W_MX4;
 }
 struct SkinnyPlan {
   int variant;   // index into the variant table

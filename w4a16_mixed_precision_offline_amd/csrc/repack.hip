@@ -361,6 +361,56 @@ hipError_t launch_sparse_decompress(const uint32_t* vp, const uint32_t* meta, co
   return hipGetLastError();
 }
 
+namespace {
+
+// MXFP4 (OCP Microscaling FP4: E2M1 codes, one E8M0 scale per 32 rows along K), for
+// the block-scaled matrix instruction, which takes the micro-block scales itself (the
+// pages' FP4-with-micro-block-scales design, dingiv.github.io "Marlin", section "与
+// Blackwell NVFP4 的对比").  Code word o = ((t*Gk + kb)*64 + l)*4 + w of the repacked
+// array is canonical word kb*16 + 4(l/16) + w of column 16t + l%16, unchanged: its
+// nibbles already hold rows 8w .. 8w+7 of lane l's 32 rows, low nibble first, which is
+// the operand order of the instruction.  Scale byte ((t*Gk + kb)*64 + l) is
+// e[kb*4 + l/16][16t + l%16]; each thread writes the 4 bytes of lanes 4j .. 4j+3.
+__global__ void mx_codes_kernel(const uint32_t* __restrict__ q, uint32_t* __restrict__ wp,
+                                long total, int Gk, int N) {
+  for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int w = (int)(o & 3), l = (int)((o >> 2) & 63);
+    const long blk = o >> 8;  // t*Gk + kb
+    const long t = blk / Gk, kb = blk - t * Gk;
+    wp[o] = q[(kb * 16 + 4 * (l >> 4) + w) * (long)N + 16 * t + (l & 15)];
+  }
+}
+__global__ void mx_scales_kernel(const uint8_t* __restrict__ e, uint32_t* __restrict__ sp,
+                                 long total, int Gk, int N) {
+  for (long o = blockIdx.x * (long)blockDim.x + threadIdx.x; o < total;
+       o += (long)gridDim.x * blockDim.x) {
+    const int j = (int)(o & 15);
+    const long blk = o >> 4;
+    const long t = blk / Gk, kb = blk - t * Gk;
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int l = 4 * j + b;
+      v |= (uint32_t)e[(kb * 4 + (l >> 4)) * (long)N + 16 * t + (l & 15)] << (8 * b);
+    }
+    sp[o] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mx_repack(const int32_t* q, const uint8_t* e, uint32_t* wp, uint8_t* sp,
+                            int K, int N, hipStream_t st) {
+  const int Gk = K / KBLK;
+  const long wtot = (long)K * N / 8, stot = (long)K * N / 128;
+  mx_codes_kernel<<<grid_for(wtot, 256), 256, 0, st>>>(reinterpret_cast<const uint32_t*>(q), wp,
+                                                       wtot, Gk, N);
+  mx_scales_kernel<<<grid_for(stot, 256), 256, 0, st>>>(e, reinterpret_cast<uint32_t*>(sp), stot,
+                                                        Gk, N);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z, uint16_t* Wt,
                           int K, int N, int group, hipStream_t st) {
   const dim3 grid((unsigned)((N + DQ_COLS - 1) / DQ_COLS),
