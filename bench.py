@@ -486,6 +486,61 @@ def w4a8_leg(w4, torch):
                 fp8_peak_TFLOPs=FP8_PEAK_TFLOPS, runs=runs)
 
 
+def mxfp4_leg(w4, torch):
+    """MXFP4 weights (E2M1 codes, E8M0 scale per 32 rows; w4a8_mx_gemm, the scales applied
+    by the block-scaled matrix instruction, no unpacking) against INT4 weights with fp8
+    activations (w4a8_gemm) and with fp16 activations (w4a16_gemm), same shapes and the
+    same fp8 activations: the 70B-class layers at decode and prefill M.  Seeded synthetic
+    inputs generated on the device (codes uniform, scale bytes uniform in [119, 124],
+    X ~ N(0,1) quantized per row); weights rotate over copies totalling at least 512 MiB."""
+    rot = 512 << 20
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20)
+    runs = []
+    for (K, N) in [(8192, 28672), (28672, 8192), (8192, 10240)]:
+        q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
+                          generator=gen)
+        s = (torch.rand((K // 128, N), device="cuda", generator=gen) * 0.018 + 0.002).half()
+        e = torch.randint(119, 125, (K // 32, N), dtype=torch.uint8, device="cuda", generator=gen)
+        pk = w4.alloc_packed(K, N, 128, False)
+        w4.w4a16_repack(q, s, None, *pk, K, N, 128)
+        mx = w4.alloc_mx(K, N)
+        w4.w4a8_mx_repack(q, e, *mx, K, N)
+        n = max(2, -(-rot // (K * N // 2)))
+        copies = [(pk, mx)] + [((pk[0].clone(), pk[1].clone()), (mx[0].clone(), mx[1].clone()))
+                               for _ in range(n - 1)]
+        for M in (1, 16, 256, 1024, 4096):
+            x = torch.randn((M, K), device="cuda", generator=gen)
+            Xh = x.half()
+            a = (x.abs().amax(dim=1) / 448.0).float()
+            X8 = (x / a[:, None]).cpu().to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            th = time_rotated(torch, [lambda c=c: w4.w4a16_gemm(Xh, c[0][0], c[0][1], None, Y, M, N,
+                                                                 K, 128) for c in copies])
+            t8 = time_rotated(torch, [lambda c=c: w4.w4a8_gemm(X8, a, c[0][0], c[0][1], None, Y, M,
+                                                                N, K, 128) for c in copies])
+            tm = time_rotated(torch, [lambda c=c: w4.w4a8_mx_gemm(X8, a, c[1][0], c[1][1], Y, M, N,
+                                                                   K) for c in copies])
+            wb = K * N // 2 + K * N // 32
+            fl = 2.0 * M * N * K
+            # roofline: weight + fp8 activation + fp16 output bytes at 8 TB/s against the
+            # matrix work at the dense fp8 peak (the instruction's rate with an fp8 operand)
+            t_mem = (wb + M * K + 2 * M * N) / (HBM_PEAK_GBPS * 1e9)
+            t_mfma = fl / (FP8_PEAK_TFLOPS * 1e12)
+            runs.append(dict(M=M, K=K, N=N, w4a16_us=round(th * 1e6, 2), w4a8_us=round(t8 * 1e6, 2),
+                             mxfp4_us=round(tm * 1e6, 2), mxfp4_TFLOPs=round(fl / tm / 1e12, 1),
+                             mxfp4_weight_GBps=round(wb / tm / 1e9, 1),
+                             w4a8_over_mxfp4_time=round(t8 / tm, 3),
+                             w4a16_over_mxfp4_time=round(th / tm, 3),
+                             bound="hbm" if t_mem >= t_mfma else "mfma_fp8",
+                             roofline_frac=round(max(t_mem, t_mfma) / tm, 4)))
+        del q, s, e, pk, mx, copies
+        torch.cuda.empty_cache()
+    return dict(kernel="w4a8_mx_gemm (tiled kernel, v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 "
+                       "codes and their E8M0 block scales) vs w4a8_gemm and w4a16_gemm",
+                fp8_peak_TFLOPs=FP8_PEAK_TFLOPS, runs=runs)
+
+
 def offline_leg(w4, torch):
     """The load-time kernels, timed apart from the GEMM (they run once per weight
     matrix): w4a16_repack (codes + scales, and zero-points), w4a16_unpack, the 2:4
@@ -834,11 +889,12 @@ def main():
     if not args.no_configs:
         sparse24, asym, tiny = config_legs(w4, torch, group)
 
-    group64 = bf16 = fp8 = offline = None
+    group64 = bf16 = fp8 = mxfp4 = offline = None
     if not args.no_configs:
         group64 = group64_leg(w4, torch)
         bf16 = bf16_leg(w4, torch)
         fp8 = w4a8_leg(w4, torch)
+        mxfp4 = mxfp4_leg(w4, torch)
         offline = offline_leg(w4, torch)
 
     # ---- CPU oracle on this host over one step (bounded sample) -----------------------
@@ -913,6 +969,7 @@ def main():
         "group64": group64,
         "bf16_activations": bf16,
         "w4a8_fp8_activations": fp8,
+        "mxfp4_in_mfma_dequant": mxfp4,
         "load_time_kernels": offline,
         "per_launch_us": [[p["M"], p["K"], p["N"], p["us"]] for p in per_launch],
         "decode_runs": [dict(M=p["M"], K=p["K"], N=p["N"], us=p["us"], weight_GBps=p["weight_GBps"],
