@@ -588,8 +588,9 @@ def offline_leg(w4, torch):
 
 
 def profile_tiled(w4, torch):
-    """A short workload for counter runs: W4A16 (fp16 activations) and W4A8 (fp8 E4M3
-    activations) on the tiled kernel, 8192 x 28672 at M = 4096, three eager launches each
+    """A short workload for counter runs: W4A16 (fp16 activations), W4A8 (fp8 E4M3
+    activations) and MXFP4 weights with fp8 activations (block scales inside the matrix
+    instruction) on the tiled kernel, 8192 x 28672 at M = 4096, three eager launches each
     after one warmup launch; prints the per-launch times."""
     K, N, M = 8192, 28672, 4096
     gen = torch.Generator(device="cuda")
@@ -599,6 +600,9 @@ def profile_tiled(w4, torch):
     s = (torch.rand((K // 128, N), device="cuda", generator=gen) * 0.009 + 0.001).half()
     pk = w4.alloc_packed(K, N, 128, False)
     w4.w4a16_repack(q, s, None, *pk, K, N, 128)
+    e = torch.randint(119, 125, (K // 32, N), dtype=torch.uint8, device="cuda", generator=gen)
+    mx = w4.alloc_mx(K, N)
+    w4.w4a8_mx_repack(q, e, *mx, K, N)
     x = torch.randn((M, K), device="cuda", generator=gen)
     Xh = x.half()
     a = (x.abs().amax(dim=1) / 448.0).float()
@@ -606,7 +610,8 @@ def profile_tiled(w4, torch):
     Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
     out = {}
     for name, fn in (("w4a16_gemm", lambda: w4.w4a16_gemm(Xh, pk[0], pk[1], None, Y, M, N, K, 128)),
-                     ("w4a8_gemm", lambda: w4.w4a8_gemm(X8, a, pk[0], pk[1], None, Y, M, N, K, 128))):
+                     ("w4a8_gemm", lambda: w4.w4a8_gemm(X8, a, pk[0], pk[1], None, Y, M, N, K, 128)),
+                     ("w4a8_mx_gemm", lambda: w4.w4a8_mx_gemm(X8, a, mx[0], mx[1], Y, M, N, K))):
         fn()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
