@@ -282,17 +282,21 @@ int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const
  *   K % 128 == 0, N % 16 == 0, K*N/8 < 2^31; q, wp, sp 16-byte aligned.  Asynchronous
  *   on `stream`; the caller owns every buffer.
  * w4a8_mx_gemm: Y (device, out) fp16 [M][N] = diag(a) * X (device, in) * W, with X8 and
- *   xscale exactly as in w4a8_gemm and wp, sp from w4a8_mx_repack.  Runs on the tiled
- *   kernel for every M (v_mfma_scale_f32_16x16x128_f8f6f4: codes as the FP4 operand with
- *   the lane's E8M0 byte as its block scale, X as the FP8 operand with unit scale), fp32
+ *   xscale exactly as in w4a8_gemm and wp, sp from w4a8_mx_repack.  Every kernel runs
+ *   v_mfma_scale_f32_16x16x128_f8f6f4 with the codes as the FP4 operand and the lane's
+ *   E8M0 byte as its block scale, X as the FP8 operand with unit scale; fp32
  *   accumulation, a[m] in fp32 before the one rounding of Y to fp16 (nearest-even).
+ *   M <= 16 runs on the decode kernel (codes streamed straight to registers, 4 waves
+ *   splitting K, summed in LDS in wave order), larger M on the tiled kernel.
  *   Shapes, 16-byte alignment of X8, wp, sp and Y, error codes, asynchronous execution,
  *   the library-owned (or w4a16_set_workspace) stream-K workspace and bitwise
  *   reproducibility are those of w4a16_gemm.
- * w4a8_mx_gemm_plan: the same with an explicit tiled variant (0 .. w4a8_mx_variants()-1,
- *   named by w4a8_mx_variant_name, the tiled variants of w4a16_gemm_variants in the same
- *   order; -1 = automatic) and `grid` persistent workgroups (0 = automatic).  Variants
- *   with an odd number of 16-row tiles return W4A16_ERR_ARG. */
+ * w4a8_mx_gemm_plan: the same with an explicit variant (0 .. w4a8_mx_variants()-1, named
+ *   by w4a8_mx_variant_name: first the tiled variants of w4a16_gemm_variants in the same
+ *   order, then the decode kernels "mx_decode_nt1/2/4" with 1, 2 or 4 column tiles per
+ *   workgroup; -1 = automatic) and, for a tiled variant, `grid` persistent workgroups
+ *   (0 = automatic; the decode kernels ignore it).  Tiled variants with an odd number of
+ *   16-row tiles, and decode kernels with M > 16, return W4A16_ERR_ARG. */
 int w4a8_mx_repack(const int32_t* q, const uint8_t* e, void* wp, void* sp, int K, int N,
                    void* stream);
 int w4a8_mx_gemm(const uint8_t* X8, const float* xscale, const void* wp, const void* sp,

@@ -50,3 +50,15 @@ def test_workspace_query_covers_the_split_plans():
     assert w4.w4a16_workspace_bytes(1, 768, 3072) > 0            # K split
     assert w4.w4a16_workspace_bytes(256, 10240, 8192) > 0        # stream-K pieces
     assert w4.w4a16_workspace_bytes(0, 4096, 4096) == 0          # invalid shape
+
+
+def test_mxfp4_variant_table():
+    """The MXFP4 entry points number the tiled variants first (the order of
+    w4a16_gemm_variants) and then the three decode kernels."""
+    import w4a16_mixed_precision_offline_amd as w4
+    names = [w4.w4a8_mx_variant_name(v) for v in range(w4.w4a8_mx_variants())]
+    tiled = [w4.w4a16_gemm_variant_name(v) for v in range(w4.w4a16_gemm_variants())
+             if w4.w4a16_gemm_variant_name(v).startswith("tiled_")]
+    assert names == tiled + ["mx_decode_nt1", "mx_decode_nt2", "mx_decode_nt4"]
+    assert w4.w4a8_mx_variant_name(len(names)) is None
+    assert w4.w4a8_mx_variant_name(-1) is None

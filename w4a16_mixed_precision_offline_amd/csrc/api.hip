@@ -536,6 +536,17 @@ int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint
 }
 
 // ---- MXFP4 weights x fp8 activations: scales applied inside the matrix instruction ----
+// decode kernel taken by the automatic plan at M <= 16 (index among the decode variants:
+// 1, 2 or 4 column tiles per workgroup).  Measured on the 7B/70B-class layers: one tile
+// (the most workgroups) is best or within 6% at M <= 8 and wherever N <= 4096; at M = 9-16
+// more columns per workgroup cut the re-reads of X from L2: two tiles for N <= 8192 (512
+// tiles), four above (1.1-1.4x over one tile on 4096 x 12288, 8192 x 10240, 8192 x 28672).
+static int mx_decode_default(int M, int N) {
+  const int tiles = N / 16;
+  if (M <= 8 || tiles <= 256) return 0;
+  return tiles <= 512 ? 1 : 2;
+}
+
 int w4a8_mx_repack(const int32_t* q, const uint8_t* e, void* wp, void* sp, int K, int N,
                    void* stream) {
   if (!q || !e || !wp || !sp) return W4A16_ERR_NULL;
@@ -554,12 +565,26 @@ int w4a8_mx_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, co
   int rc = check_gemm_args(X, wp, S, nullptr, Y, M, N, K, KBLK);
   if (rc) return rc;
   if (xscale && (reinterpret_cast<uintptr_t>(xscale) & 3u) != 0) return W4A16_ERR_ALIGN;
-  if (variant < -1 || variant >= tiled_variant_count(W_MX4) || grid < 0) return W4A16_ERR_ARG;
+  const int nt = tiled_variant_count(W_MX4);
+  if (variant < -1 || variant >= nt + mx_decode_variant_count() || grid < 0) return W4A16_ERR_ARG;
+  // up to 16 rows: the decode kernel (measured 1.3-2.3x faster than 32-row tiles at
+  // M = 1-16 on the 7B/70B-class layers)
+  if (variant < 0 && grid == 0 && M <= 16) variant = nt + mx_decode_default(M, N);
+  if (variant >= nt) {
+    if (M > 16) return W4A16_ERR_ARG;
+    int dev;
+    if ((rc = check_device(&dev))) return rc;
+    return launched(mx_decode_launch(variant - nt, X8, xscale, wp, static_cast<const uint8_t*>(sp),
+                                     Y, M, N, K, static_cast<hipStream_t>(stream)));
+  }
   return run_tiled(W_MX4, X, wp, S, nullptr, Y, M, N, K, variant, grid, stream, xscale);
 }
 
-int w4a8_mx_variants(void) { return tiled_variant_count(W_MX4); }
-const char* w4a8_mx_variant_name(int variant) { return tiled_variant_name(W_MX4, variant); }
+int w4a8_mx_variants(void) { return tiled_variant_count(W_MX4) + mx_decode_variant_count(); }
+const char* w4a8_mx_variant_name(int variant) {
+  const int nt = tiled_variant_count(W_MX4);
+  return variant >= nt ? mx_decode_variant_name(variant - nt) : tiled_variant_name(W_MX4, variant);
+}
 
 int w4a8_mx_gemm(const uint8_t* X8, const float* xscale, const void* wp, const void* sp,
                  uint16_t* Y, int M, int N, int K, void* stream) {

@@ -144,6 +144,11 @@ struct TiledPlan {
   int fixup_wgs;       // workgroups of the second pass (stream-K tiles x row tiles), 0 if none
 };
 // The fp16 baseline (W_FP16) has its own variant table; the packed formats share one.
+// MXFP4 x fp8 for M <= 16: weights streamed straight to registers, 4 waves split K
+int mx_decode_variant_count();
+const char* mx_decode_variant_name(int v);
+hipError_t mx_decode_launch(int variant, const uint8_t* X, const float* xscale, const void* wp,
+                            const uint8_t* sp, uint16_t* Y, int M, int N, int K, hipStream_t st);
 int tiled_variant_count(int mode);
 const char* tiled_variant_name(int mode, int v);
 // variant < 0: automatic; grid <= 0: automatic number of workgroups.
