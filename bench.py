@@ -644,6 +644,8 @@ def main():
                     help="skip the per-shape table (a kernel trace then holds only the step's launches)")
     ap.add_argument("--profile-tiled", action="store_true",
                     help="only a short W4A16 / W4A8 tiled-kernel workload (for counter runs)")
+    ap.add_argument("--only-mxfp4", action="store_true",
+                    help="only the MXFP4 leg (for a kernel trace of its kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain device copies of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -670,6 +672,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_tiled:
         profile_tiled(w4, torch)
+        return
+    if args.only_mxfp4:
+        print(json.dumps(dict(mxfp4_in_mfma_dequant=mxfp4_leg(w4, torch))), flush=True)
         return
     runs = config_runs(1)
     shapes = []

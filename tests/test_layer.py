@@ -86,3 +86,49 @@ def test_layer_forward_bf16_and_fp8(lib):
                              oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], group),
                              oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], group))
     assert ok, info
+
+
+def test_mxfp4_layer_rejects_bad_inputs_on_the_host():
+    import torch
+    from w4a16_mixed_precision_offline_amd.layer import MXFP4Linear
+    with pytest.raises(ValueError):
+        MXFP4Linear(100, 64)
+    with pytest.raises(ValueError):
+        MXFP4Linear(256, 40)
+    with pytest.raises(TypeError):
+        MXFP4Linear.from_quantized(torch.zeros((32, 16), dtype=torch.int32),
+                                   torch.zeros((8, 16), dtype=torch.int8))
+    with pytest.raises(ValueError):
+        MXFP4Linear.from_quantized(torch.zeros((32, 16), dtype=torch.int32),
+                                   torch.zeros((4, 16), dtype=torch.uint8))
+    layer = MXFP4Linear(128, 16, device="cpu")  # buffers only; forward never launches here
+    assert layer.wp.numel() == 128 * 16 // 2 and layer.sp.numel() == 128 * 16 // 32
+    with pytest.raises(TypeError):
+        layer(torch.zeros((2, 128), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        layer(torch.zeros((2, 64), dtype=torch.float8_e4m3fn))
+    with pytest.raises(ValueError):
+        layer(torch.zeros((2, 128), dtype=torch.float8_e4m3fn), torch.ones(3))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M", [6, 40])
+def test_mxfp4_layer_forward_matches_oracle(lib, M):
+    """Decode-sized (6 rows: the decode kernel) and larger (40 rows: the tiled kernel)
+    batches through the MXFP4 layer, shaped [2, M/2, K], against the oracle."""
+    import torch
+    from gen import activations_fp8, weights_mxfp4
+    from w4a16_mixed_precision_offline_amd.layer import MXFP4Linear
+    K, N = 2048, 1040
+    w = Workload(cfg=9, M=M, K=K, N=N)
+    d = weights_mxfp4(w, seed=82)
+    X8, a = activations_fp8(w, seed=83)
+    dev = lambda t: torch.from_numpy(np.ascontiguousarray(t)).cuda()
+    layer = MXFP4Linear.from_quantized(dev(d["Qp"]), dev(d["E"]))
+    y = layer(dev(X8).view(torch.float8_e4m3fn).reshape(2, M // 2, K), dev(a).reshape(2, M // 2))
+    assert y.shape == (2, M // 2, N) and y.dtype == torch.float16
+    ok, info = oracle.accept(y.reshape(M, N).cpu().numpy(),
+                             oracle.gemm_mxfp4(X8, a, d["Qp"], d["E"]),
+                             oracle.error_bound_mxfp4(X8, a, d["Qp"], d["E"]))
+    assert ok, info
+    assert layer(torch.zeros((0, K), dtype=torch.float8_e4m3fn, device="cuda")).shape == (0, N)

@@ -16,8 +16,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (alloc_packed, w4a8_gemm, w4a16_gemm, w4a16_gemm_bf16, w4a16_packed_bytes,
-               w4a16_repack, w4a16_unpack, BUF_W)
+from . import (alloc_mx, alloc_packed, w4a8_gemm, w4a8_mx_gemm, w4a8_mx_repack, w4a16_gemm,
+               w4a16_gemm_bf16, w4a16_packed_bytes, w4a16_repack, w4a16_unpack, BUF_W)
 
 
 class W4A16Linear(torch.nn.Module):
@@ -102,3 +102,56 @@ class W4A16Linear(torch.nn.Module):
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
                 f"group={self.group}, zero_points={self.zp is not None}")
+
+
+class MXFP4Linear(torch.nn.Module):
+    """y = x @ W for FP8 E4M3 activations x [..., in_features] (torch.float8_e4m3fn, with
+    an optional fp32 scale per row `xscale` of shape x.shape[:-1]) and MXFP4 weights W
+    [in_features, out_features]: w = e2m1(q) * 2^(e - 127), one E8M0 byte e per 32 rows of
+    a column.  The block scales are applied by the matrix instruction itself (FP4 weights
+    with micro-block scales, "Marlin", dingiv.github.io, section "与 Blackwell NVFP4 的对比");
+    forward is one w4a8_mx_gemm call, y is fp16.  Weights are repacked once, when the
+    layer is built."""
+
+    def __init__(self, in_features: int, out_features: int, device="cuda"):
+        super().__init__()
+        if in_features <= 0 or in_features % 128 or out_features <= 0 or out_features % 16:
+            raise ValueError(f"unsupported shape: in_features={in_features} (multiple of 128), "
+                             f"out_features={out_features} (multiple of 16)")
+        self.in_features = in_features
+        self.out_features = out_features
+        wp, sp = alloc_mx(in_features, out_features, device=device)
+        self.register_buffer("wp", wp)
+        self.register_buffer("sp", sp)
+
+    @classmethod
+    def from_quantized(cls, q: torch.Tensor, e: torch.Tensor) -> "MXFP4Linear":
+        """Build from canonical device tensors: q int32 [K/8, N] (8 E2M1 codes per word along
+        K, low nibble first), e uint8 [K/32, N] (E8M0 scale bytes); repacks them once."""
+        if q.dtype != torch.int32 or e.dtype != torch.uint8:
+            raise TypeError("q must be int32 and e uint8")
+        K, N = q.shape[0] * 8, q.shape[1]
+        if tuple(e.shape) != (K // 32, N):
+            raise ValueError("e must be [K/32, N]")
+        layer = cls(K, N, device=q.device)
+        w4a8_mx_repack(q.contiguous(), e.contiguous(), layer.wp, layer.sp, K, N)
+        return layer
+
+    def forward(self, x: torch.Tensor, xscale: torch.Tensor | None = None) -> torch.Tensor:
+        if x.dtype != torch.float8_e4m3fn:
+            raise TypeError(f"expected float8_e4m3fn activations, got {x.dtype}")
+        if x.shape[-1] != self.in_features:
+            raise ValueError(f"last dimension {x.shape[-1]} != in_features {self.in_features}")
+        lead = x.shape[:-1]
+        if xscale is not None and (xscale.dtype != torch.float32 or tuple(xscale.shape) != tuple(lead)):
+            raise ValueError(f"xscale must be float32 of shape {tuple(lead)}")
+        x2 = x.reshape(-1, self.in_features).contiguous()
+        M = x2.shape[0]
+        y = torch.empty((M, self.out_features), dtype=torch.float16, device=x.device)
+        if M > 0:
+            a = None if xscale is None else xscale.reshape(-1).contiguous()
+            w4a8_mx_gemm(x2, a, self.wp, self.sp, y, M, self.out_features, self.in_features)
+        return y.reshape(*lead, self.out_features)
+
+    def extra_repr(self) -> str:
+        return f"in_features={self.in_features}, out_features={self.out_features}, format=mxfp4"
