@@ -286,8 +286,9 @@ int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const
  *   v_mfma_scale_f32_16x16x128_f8f6f4 with the codes as the FP4 operand and the lane's
  *   E8M0 byte as its block scale, X as the FP8 operand with unit scale; fp32
  *   accumulation, a[m] in fp32 before the one rounding of Y to fp16 (nearest-even).
- *   M <= 16 runs on the decode kernel (codes streamed straight to registers, 4 waves
- *   splitting K, summed in LDS in wave order), larger M on the tiled kernel.
+ *   M <= 32 runs on the decode kernel (codes streamed straight to registers, one or two
+ *   16-row tiles, 4 waves splitting K, summed in LDS in wave order), larger M on the
+ *   tiled kernel.
  *   Shapes, 16-byte alignment of X8, wp, sp and Y, error codes, asynchronous execution,
  *   the library-owned (or w4a16_set_workspace) stream-K workspace and bitwise
  *   reproducibility are those of w4a16_gemm.
@@ -296,7 +297,7 @@ int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const
  *   order, then the decode kernels "mx_decode_nt1/2/4" with 1, 2 or 4 column tiles per
  *   workgroup; -1 = automatic) and, for a tiled variant, `grid` persistent workgroups
  *   (0 = automatic; the decode kernels ignore it).  Tiled variants with an odd number of
- *   16-row tiles, and decode kernels with M > 16, return W4A16_ERR_ARG. */
+ *   16-row tiles, and decode kernels with M > 32, return W4A16_ERR_ARG. */
 int w4a8_mx_repack(const int32_t* q, const uint8_t* e, void* wp, void* sp, int K, int N,
                    void* stream);
 int w4a8_mx_gemm(const uint8_t* X8, const float* xscale, const void* wp, const void* sp,

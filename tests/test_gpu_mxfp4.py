@@ -43,9 +43,9 @@ def _mx(gh, X8d, ad, packed, M, N, K, variant=-1, grid=0, Y=None):
 
 
 def _runs(variant_name, M):
-    # fp8 activations need an even number of 16-row tiles; the decode kernel takes M <= 16
+    # fp8 activations need an even number of 16-row tiles; the decode kernel takes M <= 32
     if variant_name.startswith("mx_decode_"):
-        return M <= 16
+        return M <= 32
     return not variant_name.startswith("tiled_bm16_")
 
 
@@ -99,28 +99,29 @@ def test_onehot_rows_bit_exact(gh):
 
 SMALL = [(1, 128, 16), (5, 1152, 512), (16, 1024, 528), (33, 1280, 512), (64, 1024, 512),
          (100, 1536, 1040), (130, 1024, 512), (300, 2048, 1040), (3, 384, 48), (16, 640, 80),
-         (9, 2048, 4112)]
+         (9, 2048, 4112), (24, 640, 80), (32, 1152, 512), (17, 2048, 4112)]
 
 
 def test_decode_kernel_onehot_rows_bit_exact(gh):
-    """The decode kernel (M <= 16): one-hot rows at scale-block and k-block boundaries and
-    on the last row give exact fp16 weight rows, for every decode variant, at M = 16 and at
-    a ragged M = 7 (rows past M untouched)."""
+    """The decode kernel (M <= 32): one-hot rows at scale-block and k-block boundaries and
+    on the last row give exact fp16 weight rows, for every decode variant, at M = 16 and 32
+    (one and two 16-row tiles) and at a ragged M = 7 and 23 (rows past M untouched)."""
     import w4a16_mixed_precision_offline_amd as w4
     K, N = 1280, 80
-    d, _, _ = _case(16, K, N, seed=4)
+    d, _, _ = _case(32, K, N, seed=4)
     W = oracle.dequant_mxfp4(d["Qp"], d["E"], K, N) + 0.0
     packed = _pack(gh, d, K, N)
     dec = [v for v in range(w4.w4a8_mx_variants())
            if w4.w4a8_mx_variant_name(v).startswith("mx_decode_")]
     assert dec
     for M, ks in ((16, [0, 31, 32, 63, 64, 127, 128, 255, 256, 640, 641, 1000, 1151, 1152, 1200,
-                        1279]), (7, [5, 96, 200, 511, 512, 900, 1278])):
+                        1279]), (7, [5, 96, 200, 511, 512, 900, 1278]),
+                   (32, list(range(0, 1280, 40))), (23, list(range(3, 1280, 55))[:23])):
         X8 = np.zeros((M, K), np.uint8)
         X8[np.arange(M), ks] = 0x38
         want = W[ks].astype(np.float16)
         for v in dec:
-            Y = gh.nan_filled(16, N)
+            Y = gh.nan_filled(32, N)
             _mx(gh, gh.dev(X8), None, packed, M, N, K, v, 0, Y=Y)
             Yh = gh.host(Y)
             assert np.array_equal(Yh[:M].view(np.uint16), want.view(np.uint16)), (v, M)

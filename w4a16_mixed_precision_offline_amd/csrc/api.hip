@@ -536,9 +536,9 @@ int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint
 }
 
 // ---- MXFP4 weights x fp8 activations: scales applied inside the matrix instruction ----
-// decode kernel taken by the automatic plan at M <= 16 (index among the decode variants:
+// decode kernel taken by the automatic plan at M <= 32 (index among the decode variants:
 // 1, 2 or 4 column tiles per workgroup).  Measured on the 7B/70B-class layers: one tile
-// (the most workgroups) is best or within 6% at M <= 8 and wherever N <= 4096; at M = 9-16
+// (the most workgroups) is best or within 6% at M <= 8 and wherever N <= 4096; at M = 9-32
 // more columns per workgroup cut the re-reads of X from L2: two tiles for N <= 8192 (512
 // tiles), four above (1.1-1.4x over one tile on 4096 x 12288, 8192 x 10240, 8192 x 28672).
 static int mx_decode_default(int M, int N) {
@@ -567,11 +567,16 @@ int w4a8_mx_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, co
   if (xscale && (reinterpret_cast<uintptr_t>(xscale) & 3u) != 0) return W4A16_ERR_ALIGN;
   const int nt = tiled_variant_count(W_MX4);
   if (variant < -1 || variant >= nt + mx_decode_variant_count() || grid < 0) return W4A16_ERR_ARG;
-  // up to 16 rows: the decode kernel (measured 1.3-2.3x faster than 32-row tiles at
-  // M = 1-16 on the 7B/70B-class layers)
-  if (variant < 0 && grid == 0 && M <= 16) variant = nt + mx_decode_default(M, N);
+  // up to 32 rows: the decode kernel (measured 1.3-2.3x faster than 32-row tiles at
+  // M = 1-16 and 1.0-1.7x at M = 17-32 on the 7B/70B-class layers), except at 17-32 rows
+  // with 257-512 column tiles, where the 32-row tiles' shared X tile wins (1.05-1.12x on
+  // 28672 x 8192)
+  if (variant < 0 && grid == 0 && M <= 32) {
+    const int tiles = N / 16;
+    if (M <= 16 || tiles <= 256 || tiles > 512) variant = nt + mx_decode_default(M, N);
+  }
   if (variant >= nt) {
-    if (M > 16) return W4A16_ERR_ARG;
+    if (M > 32) return W4A16_ERR_ARG;
     int dev;
     if ((rc = check_device(&dev))) return rc;
     return launched(mx_decode_launch(variant - nt, X8, xscale, wp, static_cast<const uint8_t*>(sp),

@@ -144,7 +144,7 @@ struct TiledPlan {
   int fixup_wgs;       // workgroups of the second pass (stream-K tiles x row tiles), 0 if none
 };
 // The fp16 baseline (W_FP16) has its own variant table; the packed formats share one.
-// MXFP4 x fp8 for M <= 16: weights streamed straight to registers, 4 waves split K
+// MXFP4 x fp8 for M <= 32: weights streamed straight to registers, 4 waves split K
 int mx_decode_variant_count();
 const char* mx_decode_variant_name(int v);
 hipError_t mx_decode_launch(int variant, const uint8_t* X, const float* xscale, const void* wp,
