@@ -204,3 +204,42 @@ def test_bad_arguments_are_rejected_before_launch(gh):
             c()
     torch.cuda.synchronize()
     assert torch.isnan(Y.float()).all()  # nothing was written
+
+
+def test_hip_graph_replays_match_eager(gh):
+    """Captured MXFP4 launches (decode kernel at one and two row tiles, tiled kernel with
+    stream-K stripes and the fixup pass) reproduce the eager result bit for bit on every
+    replay, with eager work and synchronizations in between."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    st = torch.cuda.Stream()
+    cases = []
+    for (M, K, N) in [(1, 4096, 4096), (24, 2048, 4112), (300, 2048, 1040), (130, 1024, 768)]:
+        d, X8, a = _case(M, K, N, seed=7)
+        cases.append((M, K, N, gh.dev(X8), gh.dev(a), _pack(gh, d, K, N),
+                      torch.empty((M, N), dtype=torch.float16, device="cuda")))
+
+    def run_all():
+        for (M, K, N, x, s, packed, Y) in cases:
+            w4.w4a8_mx_gemm(x, s, packed[0], packed[1], Y, M, N, K)
+
+    with torch.cuda.stream(st):
+        run_all()
+    torch.cuda.synchronize()
+    eager = [gh.host(c[-1]).view(np.uint16).copy() for c in cases]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        run_all()
+    torch.cuda.synchronize()
+    M3, K3, N3, x3, s3, p3, _ = cases[3]
+    for rep in range(4):
+        for c in cases:
+            c[-1].fill_(0)
+        junk = torch.empty((M3, N3), dtype=torch.float16, device="cuda")
+        w4.w4a8_mx_gemm(x3, None, p3[0], p3[1], junk, M3, N3, K3)  # eager work between replays
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            g.replay()
+        torch.cuda.synchronize()
+        for c, e in zip(cases, eager):
+            assert np.array_equal(gh.host(c[-1]).view(np.uint16), e), rep
