@@ -239,6 +239,33 @@ def test_w4a8_validation(raw):
     assert g(A, None, A, A, None, A, 16, 1024, 1000, 128, None) == -2
 
 
+def test_mxfp4_validation(raw):
+    """MXFP4 entry points: every host-side check returns its code before any HIP call."""
+    f = raw.w4a8_mx_gemm_plan
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    assert f(None, None, A, A, A, 16, 1024, 1024, -1, 0, None) == -1
+    assert f(A, None, A, None, A, 16, 1024, 1024, -1, 0, None) == -1   # no scales
+    assert f(A, None, A, A, None, 16, 1024, 1024, -1, 0, None) == -1   # no output
+    assert f(A, None, A, A, A, 16, 1000, 1024, -1, 0, None) == -2      # N % 16
+    assert f(A, None, A, A, A, 16, 1024, 1000, -1, 0, None) == -2      # K % 128
+    assert f(A, None, A, A, A, 0, 1024, 1024, -1, 0, None) == -2       # M = 0
+    assert f(MIS, None, A, A, A, 16, 1024, 1024, -1, 0, None) == -3
+    assert f(A, A + 2, A, A, A, 16, 1024, 1024, -1, 0, None) == -3     # row scales
+    nv = raw.w4a8_mx_variants()
+    assert f(A, None, A, A, A, 16, 1024, 1024, nv, 0, None) == -8      # out of range
+    assert f(A, None, A, A, A, 16, 1024, 1024, -2, 0, None) == -8
+    assert f(A, None, A, A, A, 16, 1024, 1024, 0, -1, None) == -8      # negative grid
+    assert f(A, None, A, A, A, 33, 1024, 1024, nv - 1, 0, None) == -8  # decode kernel, M > 32
+    r = raw.w4a8_mx_repack
+    r.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + [ctypes.c_void_p]
+    assert r(None, A, A, A, 1024, 1024, None) == -1
+    assert r(A, None, A, A, 1024, 1024, None) == -1
+    assert r(A, A, A, A, 1000, 1024, None) == -2
+    assert r(A, A, A, A, 1024, 1000, None) == -2
+    assert r(A, A, A, A, 1 << 20, 1 << 14, None) == -2                 # K*N/8 >= 2^31
+    assert r(MIS, A, A, A, 1024, 1024, None) == -3
+
+
 def test_baseline_validation(raw):
     f = raw.w4a16_fp16_gemm
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
