@@ -131,10 +131,10 @@ int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const
 int w4a16_gemm_variants(void);
 const char* w4a16_gemm_variant_name(int variant);
 
-/* Bytes of device workspace the automatic plans of w4a16_gemm, w4a16_sparse24_gemm and
- * w4a16_fp16_gemm need for an (M, N, K) GEMM on one stream (the largest over the weight
- * formats; 0 when no plan for the shape reduces across workgroups, or for an invalid
- * shape).  The library allocates this itself, per (device, stream), on the first call
+/* Bytes of device workspace the automatic plans of w4a16_gemm, w4a16_sparse24_gemm,
+ * w4a16_fp16_gemm, w4a16_gemm_bf16, w4a8_gemm and w4a8_mx_gemm need for an (M, N, K) GEMM
+ * on one stream (the largest over the entry points; 0 when no plan for the shape reduces
+ * across workgroups, or for an invalid shape).  The library allocates this itself, per (device, stream), on the first call
  * that needs it and keeps it for later calls; the query lets a caller budget device
  * memory ahead of time.  Host only. */
 size_t w4a16_workspace_bytes(int M, int N, int K);

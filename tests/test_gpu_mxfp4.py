@@ -243,3 +243,29 @@ def test_hip_graph_replays_match_eager(gh):
         torch.cuda.synchronize()
         for c, e in zip(cases, eager):
             assert np.array_equal(gh.host(c[-1]).view(np.uint16), e), rep
+
+
+def test_caller_owned_workspace_sized_by_the_query(gh):
+    """A caller-owned workspace of W4A16_WS_COUNTER_BYTES + w4a16_workspace_bytes(M, N, K)
+    runs the MXFP4 automatic plan of a shape whose 32-row tiles are all cut into stream-K
+    pieces (M = 24 on 28672 x 8192), with the same bits as a library-owned one."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 24, 28672, 8192
+    d, X8, a = _case(M, K, N, seed=8)
+    packed = _pack(gh, d, K, N)
+    X8d, ad = gh.dev(X8), gh.dev(a)
+    ref = gh.host(_mx(gh, X8d, ad, packed, M, N, K)).view(np.uint16).copy()
+    st = torch.cuda.Stream()
+    nbytes = w4.WS_COUNTER_BYTES + w4.w4a16_workspace_bytes(M, N, K)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    w4.w4a16_set_workspace(buf, nbytes, stream=st)
+    try:
+        for _ in range(2):
+            with torch.cuda.stream(st):
+                Y = _mx(gh, X8d, ad, packed, M, N, K)
+            torch.cuda.synchronize()
+            assert np.array_equal(gh.host(Y).view(np.uint16), ref)
+    finally:
+        w4.w4a16_set_workspace(None, 0, stream=st)
+    torch.cuda.synchronize()

@@ -62,3 +62,13 @@ def test_mxfp4_variant_table():
     assert names == tiled + ["mx_decode_nt1", "mx_decode_nt2", "mx_decode_nt4"]
     assert w4.w4a8_mx_variant_name(len(names)) is None
     assert w4.w4a8_mx_variant_name(-1) is None
+
+
+def test_workspace_query_covers_the_fp8_and_mxfp4_plans():
+    """At 17-32 rows on a 28672 x 8192 layer w4a16_gemm runs on the skinny kernel, while
+    w4a8_mx_gemm keeps the 32-row tiled tile, whose 32 tiles are all cut into stream-K
+    pieces over 256 workgroups: two 32 x 256 fp32 pieces per workgroup."""
+    need = 2 * 256 * 32 * 256 * 4
+    assert w4.w4a16_workspace_bytes(24, 8192, 28672) >= need
+    # the decode kernel (M <= 16) reduces inside its workgroups only
+    assert w4.w4a16_workspace_bytes(16, 28672, 8192) < need

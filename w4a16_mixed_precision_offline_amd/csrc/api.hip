@@ -147,6 +147,15 @@ bool use_tiled(int M, int N, int K) {
   return !(kn < (32LL << 20) && N >= 2048);
 }
 
+// MXFP4 automatic plan: the decode kernel up to 32 rows (measured 1.3-2.3x faster than
+// 32-row tiles at M = 1-16 and 1.0-1.7x at M = 17-32 on the 7B/70B-class layers), except
+// at 17-32 rows with 257-512 column tiles, where the 32-row tiles' shared X tile wins
+// (1.05-1.12x on 28672 x 8192); the tiled kernel above.
+bool mx_uses_decode(int M, int N) {
+  const int tiles = N / 16;
+  return M <= 32 && (M <= 16 || tiles <= 256 || tiles > 512);
+}
+
 int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
               uint16_t* Y, int M, int N, int K, int variant, int grid, void* stream,
               const float* xscale = nullptr) {
@@ -326,12 +335,24 @@ size_t w4a16_workspace_bytes(int M, int N, int K) {
     const size_t bytes = (counters + 63) / 64 * 64 * sizeof(int) + floats * sizeof(float);
     if (bytes > need) need = bytes;
   }
-  // the bf16- and fp8-activation entry points run every M on the skinny kernel
+  // w4a16_gemm_bf16, and w4a8_gemm with groups of 64, run every M on the skinny kernel;
+  // w4a8_gemm with larger groups takes the tiled kernel where w4a16_gemm does (its tiled
+  // plans differ: fp8 needs an even number of 16-row tiles)
   SkinnyPlan p;
   if (skinny_make_plan(M, N, K, KBLK, W_SYM8, -1, 0, &p) == 0) {
     const size_t bytes =
         ((size_t)p.counters + 63) / 64 * 64 * sizeof(int) + p.part_floats * sizeof(float);
     if ((p.counters || p.part_floats) && bytes > need) need = bytes;
+  }
+  TiledPlan t;
+  if (use_tiled(M, N, K) && tiled_make_plan(M, N, K, W_SYM8, -1, 0, &t) == 0) {
+    const size_t bytes = t.part_floats * sizeof(float);
+    if (bytes > need) need = bytes;
+  }
+  // w4a8_mx_gemm: the decode kernel needs none, the tiled kernel its stream-K partials
+  if (!mx_uses_decode(M, N) && tiled_make_plan(M, N, K, W_MX4, -1, 0, &t) == 0) {
+    const size_t bytes = t.part_floats * sizeof(float);
+    if (bytes > need) need = bytes;
   }
   return need;
 }
@@ -567,14 +588,7 @@ int w4a8_mx_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, co
   if (xscale && (reinterpret_cast<uintptr_t>(xscale) & 3u) != 0) return W4A16_ERR_ALIGN;
   const int nt = tiled_variant_count(W_MX4);
   if (variant < -1 || variant >= nt + mx_decode_variant_count() || grid < 0) return W4A16_ERR_ARG;
-  // up to 32 rows: the decode kernel (measured 1.3-2.3x faster than 32-row tiles at
-  // M = 1-16 and 1.0-1.7x at M = 17-32 on the 7B/70B-class layers), except at 17-32 rows
-  // with 257-512 column tiles, where the 32-row tiles' shared X tile wins (1.05-1.12x on
-  // 28672 x 8192)
-  if (variant < 0 && grid == 0 && M <= 32) {
-    const int tiles = N / 16;
-    if (M <= 16 || tiles <= 256 || tiles > 512) variant = nt + mx_decode_default(M, N);
-  }
+  if (variant < 0 && grid == 0 && mx_uses_decode(M, N)) variant = nt + mx_decode_default(M, N);
   if (variant >= nt) {
     if (M > 32) return W4A16_ERR_ARG;
     int dev;
