@@ -118,12 +118,11 @@ def pmc_summary(fetch_csv, write_csv):
                fetch_kib_per_launch=round(res["fetch"]["kib_per_launch"], 1),
                write_kib_per_launch=round(res["write"]["kib_per_launch"], 1),
                launches=res["fetch"]["launches"],
-               commands=["rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch -o run --output-format csv -- "
-                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph --no-large --no-configs --copy-calibration",
-                         "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_write -o run --output-format csv -- "
-                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph --no-large --no-configs --copy-calibration",
-                         "python bench.py --pmc-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
-                         "gpurun_out/pmc_write/run_counter_collection.csv"])
+               commands=[f"rocprofv3 --pmc {c} -d {os.path.dirname(p)} -o run --output-format csv -- "
+                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph "
+                         "--no-large --no-configs --copy-calibration"
+                         for c, p in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv))]
+               + [f"python bench.py --pmc-summary {fetch_csv} {write_csv}"])
     with open(TRAFFIC_JSON, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
@@ -658,7 +657,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; the W4A16 GEMM has no multi-GPU "
+        print("bench.py measures one GPU only; the W4A16 GEMM has no multi-GPU "
               "path here (it would shard by output columns with no exchange). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
