@@ -852,3 +852,20 @@ def test_generator_mxfp4_weights():
     assert d["E"].min() >= 119 and d["E"].max() <= 124
     assert np.array_equal(ref.unpack_codes_k(d["Qp"], 256), d["q"])
     assert len(np.unique(d["q"])) == 16
+
+
+def test_mxfp4_sampled_equals_full_at_the_samples():
+    # the full-size GPU tests compare against the sampled oracle: it must be the full one
+    # restricted to the sampled rows and columns (row scales follow their rows)
+    rng = np.random.default_rng(31)
+    M, K, N = 7, 256, 48
+    X8 = _random_e4m3(rng, (M, K))
+    a = rng.uniform(0.001, 0.01, size=M).astype(np.float32)
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    E = rng.integers(115, 135, size=(K // 32, N), dtype=np.uint8)
+    rows, cols = [0, 3, 6], [1, 17, 32, 47]
+    Y, B = oracle.gemm_mxfp4_sampled(X8, a, Qp, E, rows, cols)
+    # equal up to the fp64 rounding of a different summation order inside the library matmul
+    Bf = oracle.error_bound_mxfp4(X8, a, Qp, E)[np.ix_(rows, cols)]
+    assert np.all(np.abs(Y - oracle.gemm_mxfp4(X8, a, Qp, E)[np.ix_(rows, cols)]) <= 1e-12 * Bf)
+    assert np.allclose(B, Bf, rtol=1e-12, atol=0)
