@@ -869,3 +869,215 @@ def test_mxfp4_sampled_equals_full_at_the_samples():
     Bf = oracle.error_bound_mxfp4(X8, a, Qp, E)[np.ix_(rows, cols)]
     assert np.all(np.abs(Y - oracle.gemm_mxfp4(X8, a, Qp, E)[np.ix_(rows, cols)]) <= 1e-12 * Bf)
     assert np.allclose(B, Bf, rtol=1e-12, atol=0)
+
+
+# ---- the tolerance scale Bnd = sum_k |X[m,k] * W[k,n]| --------------------------
+# Every per-element acceptance limit in the GPU tests is 5e-3 * Bnd + 1e-4, so the
+# bound functions are pinned against an exact-rational sum built here from the bit
+# fields with Python integers (no NumPy unpacking, no matrix product), and planted
+# mistakes in them (abs dropped, a constant factor, fp16-rounded weights with slack,
+# a dropped scale) must each fail.
+def _exact_abs_sum(xvals, Qp, wval):
+    """[[sum_k |x[m][k]| * |w(k, n)|]] in Fractions; x as Fractions, w(k, n) a callable
+    returning the exact weight of row k, column n."""
+    M, K = len(xvals), len(xvals[0])
+    N = Qp.shape[1]
+    return [[sum((abs(xvals[m][k]) * abs(wval(k, n)) for k in range(K)), Fraction(0))
+             for n in range(N)] for m in range(M)]
+
+
+def _int4_weight(Qp, s, Zp, g):
+    Qw = [[int(v) & 0xFFFFFFFF for v in row] for row in np.asarray(Qp, dtype=np.int64)]
+    Zw = None if Zp is None else [[int(v) & 0xFFFFFFFF for v in row]
+                                  for row in np.asarray(Zp, dtype=np.int64)]
+    Sf = [[Fraction(float(v)) for v in row] for row in np.asarray(s, dtype=np.float16)]
+
+    def w(k, n):
+        q = (Qw[k // 8][n] >> (4 * (k % 8))) % 16
+        z = 8 if Zw is None else (Zw[k // g][n // 8] >> (4 * (n % 8))) % 16
+        return (q - z) * Sf[k // g][n]
+    return w
+
+
+def _mx_weight(Qp, E):
+    fx = dict(_e2m1_fixture())
+
+    def w(k, n):
+        code = ((int(Qp[k // 8, n]) & 0xFFFFFFFF) >> (4 * (k % 8))) & 15
+        return Fraction(fx[code]) * Fraction(2) ** (int(E[k // 32, n]) - 127)
+    return w
+
+
+def _e4m3_rows(X8, a):
+    """Exact activation values a[m] * x8[m, k] from the bit-field table."""
+    e4 = dict(_e4m3_exact_table())
+    return [[(Fraction(1) if a is None else Fraction(float(np.float32(a[m])))) * e4[int(c)]
+             for c in row] for m, row in enumerate(np.asarray(X8))]
+
+
+def _bound_close(B, exact, K):
+    """B (fp64) equals the exact positive sum up to the fp64 rounding of K additions."""
+    B = np.asarray(B)
+    for m in range(B.shape[0]):
+        for n in range(B.shape[1]):
+            e = exact[m][n]
+            if abs(Fraction(float(B[m, n])) - e) > Fraction((K + 2) * 2.0 ** -53) * e:
+                return False
+    return True
+
+
+def _bound_cases():
+    rng = np.random.default_rng(77)
+    cases = []
+    for (M, K, N, asym, g) in [(2, 256, 8, False, 128), (3, 256, 16, True, 128),
+                               (2, 128, 8, True, 64), (2, 512, 8, True, 256)]:
+        X = rng.standard_normal((M, K)).astype(np.float16)
+        Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+        s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+        Zp = words_from_codes_n(rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)) if asym else None
+        cases.append((X, Qp, s, Zp, g))
+    return cases
+
+
+def _pins_bounds_pass(mod):
+    checks = []
+    # W4A16: full bound and the sampled one, sym / asym, groups of 64, 128, 256
+    for X, Qp, s, Zp, g in _bound_cases():
+        M, K = X.shape
+        N = Qp.shape[1]
+        xv = [[Fraction(float(v)) for v in row] for row in X]
+        ex = _exact_abs_sum(xv, Qp, _int4_weight(Qp, s, Zp, g))
+        checks.append(_bound_close(mod.error_bound(X, Qp, s, Zp, g), ex, K))
+        rows, cols = [M - 1, 0], [N - 1, 2, 5]
+        _, Bs = mod.gemm_sampled(X, Qp, s, Zp, g, rows, cols)
+        checks.append(_bound_close(Bs, [[ex[r][c] for c in cols] for r in rows], K))
+    # W4A8: fp32 row scales (or none), sym / asym, full and sampled
+    rng = np.random.default_rng(78)
+    for (M, K, N, asym, scaled) in [(3, 256, 8, True, True), (2, 128, 16, False, False),
+                                    (3, 128, 8, False, True)]:
+        g = 128
+        X8 = _random_e4m3(rng, (M, K))
+        a = np.array([0.5, 0.0039, 7.25][:M], dtype=np.float32) if scaled else None
+        Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+        s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+        Zp = words_from_codes_n(rng.integers(0, 16, size=(K // g, N), dtype=np.uint8)) if asym else None
+        xv = _e4m3_rows(X8, a)
+        ex = _exact_abs_sum(xv, Qp, _int4_weight(Qp, s, Zp, g))
+        checks.append(_bound_close(mod.error_bound_w4a8(X8, a, Qp, s, Zp, g), ex, K))
+        rows, cols = [M - 1, 0], [N - 1, 3]
+        Ys, Bs = mod.gemm_w4a8_sampled(X8, a, Qp, s, Zp, g, rows, cols)
+        checks.append(_bound_close(Bs, [[ex[r][c] for c in cols] for r in rows], K))
+        ey = _w4a8_exact(X8, a, Qp, s, Zp, g)
+        checks.append(all(abs(Fraction(float(Ys[i, j])) - ey[r][c])
+                          <= Fraction((K + 2) * 2.0 ** -53) * ex[r][c]
+                          for i, r in enumerate(rows) for j, c in enumerate(cols)))
+    # MXFP4: E8M0 block scales and row scales, full and sampled
+    for (M, K, N, scaled) in [(2, 128, 8, True), (3, 64, 16, False)]:
+        X8 = _random_e4m3(rng, (M, K))
+        a = np.array([0.75, 0.0061, 3.0][:M], dtype=np.float32) if scaled else None
+        Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+        E = rng.integers(110, 140, size=(K // 32, N), dtype=np.uint8)
+        ex = _exact_abs_sum(_e4m3_rows(X8, a), Qp, _mx_weight(Qp, E))
+        checks.append(_bound_close(mod.error_bound_mxfp4(X8, a, Qp, E), ex, K))
+        rows, cols = [M - 1, 0], [N - 1, 1]
+        _, Bs = mod.gemm_mxfp4_sampled(X8, a, Qp, E, rows, cols)
+        checks.append(_bound_close(Bs, [[ex[r][c] for c in cols] for r in rows], K))
+    return all(checks)
+
+
+def test_error_bounds_equal_exact_rational_sums():
+    assert _pins_bounds_pass(ref)
+
+
+def test_w4a8_sampled_matches_full_at_the_samples():
+    # the full-size W4A8 GPU tests compare against the sampled oracle
+    rng = np.random.default_rng(32)
+    M, K, N, g = 6, 256, 40, 128
+    X8 = _random_e4m3(rng, (M, K))
+    a = rng.uniform(0.001, 0.01, size=M).astype(np.float32)
+    Qp = words_from_codes_k(rng.integers(0, 16, size=(K, N), dtype=np.uint8))
+    s = rng.uniform(0.002, 0.02, size=(K // g, N)).astype(np.float16)
+    Zp = words_from_codes_n(rng.integers(0, 16, size=(K // g, N), dtype=np.uint8))
+    rows, cols = [5, 0, 3], [39, 8, 1, 16]
+    Y, B = oracle.gemm_w4a8_sampled(X8, a, Qp, s, Zp, g, rows, cols)
+    Bf = oracle.error_bound_w4a8(X8, a, Qp, s, Zp, g)[np.ix_(rows, cols)]
+    assert np.all(np.abs(Y - oracle.gemm_w4a8(X8, a, Qp, s, Zp, g)[np.ix_(rows, cols)]) <= 1e-12 * Bf)
+    assert np.allclose(B, Bf, rtol=1e-12, atol=0)
+
+
+def test_bound_planted_mistakes_are_caught():
+    import types
+
+    def mutant(**overrides):
+        m = types.ModuleType("mutant")
+        m.__dict__.update({k: getattr(ref, k) for k in dir(ref) if not k.startswith("__")})
+        m.__dict__.update(overrides)
+        return m
+
+    def eb_abs_dropped_on_w(X, Qp, s, Zp, group, rows_per_chunk=1024):
+        K, N = X.shape[1], Qp.shape[1]
+        return np.abs(X.astype(np.float64)) @ ref.dequant(Qp, s, Zp, K, N, group)
+
+    def eb_times_10(X, Qp, s, Zp, group, rows_per_chunk=1024):
+        return 10.0 * ref.error_bound(X, Qp, s, Zp, group)
+
+    def eb_fp16_weights_slack(X, Qp, s, Zp, group, rows_per_chunk=1024):
+        K, N = X.shape[1], Qp.shape[1]
+        W16 = ref.dequant_fp16(Qp, s, Zp, K, N, group).astype(np.float64)
+        return 2.0 * (np.abs(X.astype(np.float64)) @ np.abs(W16))
+
+    def eb_abs_of_sum(X, Qp, s, Zp, group, rows_per_chunk=1024):
+        return np.abs(ref.gemm(X, Qp, s, Zp, group))
+
+    def eb_scale_dropped(X, Qp, s, Zp, group, rows_per_chunk=1024):
+        return ref.error_bound(X, Qp, np.ones_like(s), Zp, group)
+
+    def sampled_abs_dropped_on_x(X, Qp, s, Zp, group, rows, cols):
+        K, N = X.shape[1], Qp.shape[1]
+        W = ref.dequant(Qp, s, Zp, K, N, group, cols=cols)
+        Xr = X[np.asarray(rows)].astype(np.float64)
+        return Xr @ W, Xr @ np.abs(W)
+
+    def w8_row_scale_dropped(X8, xscale, Qp, s, Zp, group):
+        return ref.error_bound_w4a8(X8, None, Qp, s, Zp, group)
+
+    def w8_times_10(X8, xscale, Qp, s, Zp, group):
+        return 10.0 * ref.error_bound_w4a8(X8, xscale, Qp, s, Zp, group)
+
+    def w8_sampled_row_scale_unsliced(X8, xscale, Qp, s, Zp, group, rows, cols):
+        K, N = X8.shape[1], Qp.shape[1]
+        W = ref.dequant(Qp, s, Zp, K, N, group, cols=cols)
+        r = np.asarray(rows)
+        a = None if xscale is None else np.asarray(xscale)[:len(r)]
+        Xr = ref.activations_w4a8(X8[r], a)
+        return Xr @ W, np.abs(Xr) @ np.abs(W)
+
+    def mx_times_10(X8, xscale, Qp, E):
+        return 10.0 * ref.error_bound_mxfp4(X8, xscale, Qp, E)
+
+    def mx_block_scale_dropped(X8, xscale, Qp, E):
+        return ref.error_bound_mxfp4(X8, xscale, Qp, np.full_like(E, 127))
+
+    def mx_sampled_abs_dropped(X8, xscale, Qp, E, rows, cols):
+        K, N = X8.shape[1], Qp.shape[1]
+        W = ref.dequant_mxfp4(Qp, E, K, N, cols=cols)
+        r = np.asarray(rows)
+        Xr = ref.activations_w4a8(X8[r], None if xscale is None else np.asarray(xscale)[r])
+        return Xr @ W, np.abs(Xr @ W)
+
+    mutants = [
+        mutant(error_bound=eb_abs_dropped_on_w),
+        mutant(error_bound=eb_times_10),
+        mutant(error_bound=eb_fp16_weights_slack),
+        mutant(error_bound=eb_abs_of_sum),
+        mutant(error_bound=eb_scale_dropped),
+        mutant(gemm_sampled=sampled_abs_dropped_on_x),
+        mutant(error_bound_w4a8=w8_row_scale_dropped),
+        mutant(error_bound_w4a8=w8_times_10),
+        mutant(gemm_w4a8_sampled=w8_sampled_row_scale_unsliced),
+        mutant(error_bound_mxfp4=mx_times_10),
+        mutant(error_bound_mxfp4=mx_block_scale_dropped),
+        mutant(gemm_mxfp4_sampled=mx_sampled_abs_dropped),
+    ]
+    for i, m in enumerate(mutants):
+        assert not _pins_bounds_pass(m), f"bound mutant {i} survived the pins"
