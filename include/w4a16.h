@@ -107,7 +107,16 @@ int w4a16_unpack(const void* wp, const uint16_t* sp, const void* zp,
  * Shape rules: M >= 1 plus the repack rules.  X, Y, wp, sp, zp 16-byte aligned.
  * Results are bitwise reproducible from run to run for a given shape.
  * The first call for a (device, stream) may allocate the reduction workspace
- * (hipMalloc); later calls allocate only when a larger shape needs more.
+ * (hipMalloc, plus a hipMemsetAsync of its counters on `stream`); later calls
+ * allocate only when a larger shape needs more, at least doubling it.  A buffer
+ * replaced that way is kept until the process ends, never freed, because launches
+ * in flight and HIP graphs captured earlier may still use it.  While `stream` is
+ * being captured into a graph nothing is allocated: a call whose plan needs more
+ * workspace than the stream already holds returns W4A16_ERR_WORKSPACE and enqueues
+ * nothing.  So make one call of each shape (or a larger one) on the stream before
+ * capturing it, or hand the stream a buffer with w4a16_set_workspace.  A captured
+ * graph keeps using the workspace it was captured with, and graphs replayed
+ * concurrently on one stream's workspace race.
  */
 int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                uint16_t* Y, int M, int N, int K, int group, void* stream);
@@ -149,11 +158,14 @@ size_t w4a16_workspace_bytes(int M, int N, int K);
  * graph); the kernels leave the counters at zero again, so no later call clears anything.
  * The library never frees ptr; the caller keeps it alive, and does not use it otherwise,
  * until it is replaced or until ptr = NULL hands the stream back to library-owned
- * workspaces (a buffer the library had allocated for the stream is freed here, after the
- * stream has drained).  A launch on the stream whose plan needs more than the buffer holds
- * returns W4A16_ERR_WORKSPACE.  Errors: W4A16_ERR_ALIGN (ptr not 256-byte aligned),
- * W4A16_ERR_WORKSPACE (ptr non-NULL with bytes below W4A16_WS_COUNTER_BYTES + 256),
- * W4A16_ERR_DEVICE, W4A16_ERR_LAUNCH (the clearing failed). */
+ * workspaces.  Replacing a caller-owned buffer first waits for the stream to drain, so the
+ * caller may free the old one once this returns (graphs captured with it must then not be
+ * replayed); a buffer the library had allocated for the stream is kept, not freed.  A
+ * launch on the stream whose plan needs more than the buffer holds returns
+ * W4A16_ERR_WORKSPACE.  Errors: W4A16_ERR_ALIGN (ptr not 256-byte aligned),
+ * W4A16_ERR_WORKSPACE (ptr non-NULL with bytes below W4A16_WS_COUNTER_BYTES + 256, or
+ * `stream` being captured into a graph), W4A16_ERR_DEVICE, W4A16_ERR_LAUNCH (the clearing
+ * or the wait failed). */
 #define W4A16_WS_COUNTER_BYTES 65536
 int w4a16_set_workspace(void* ptr, size_t bytes, void* stream);
 

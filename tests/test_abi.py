@@ -304,3 +304,24 @@ def test_sparse_validation(raw):
     p = raw.w4a16_sparse24_gemm_plan
     p.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_void_p]
     assert p(A, A, A, A, A, 16, 1024, 1024, 128, 999, 0, None) == -8
+
+
+def test_shapes_past_32_bit_descriptors_are_rejected_on_the_host(raw):
+    """M = 64, K = 2^25, N = 16 passes the weight-shape rules (K*N/8 = 2^26 words), but 64
+    rows of X span 2^32 bytes: neither kernel's 32-bit buffer descriptors can address
+    them, so the plan query and the GEMM itself must return W4A16_ERR_SHAPE (before any
+    device call; the pointers below are never dereferenced)."""
+    out = (ctypes.c_int * 4)()
+    K, N = 1 << 25, 16
+    assert raw.w4a16_gemm_describe(64, N, K, 128, out) == -2
+    assert raw.w4a16_gemm_describe(1, N, K, 128, out) == 0     # 4 rows: 2^28 bytes, fine
+    p = ctypes.c_void_p(1 << 20)  # 16-byte aligned, never touched
+    fn = raw.w4a16_gemm
+    fn.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+    assert fn(p, p, p, None, p, 64, N, K, 128, None) == -2
+    # groups of 64 rows run the skinny kernel at every M: the same guard applies
+    assert raw.w4a16_gemm_describe(64, N, K, 64, out) == -2
+    # the fp16 baseline: one workgroup's weight rows (16 columns x K fp16) past 2 GiB
+    fp = raw.w4a16_fp16_gemm
+    fp.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
+    assert fp(p, p, p, 1, 16, 1 << 26, None) == -2

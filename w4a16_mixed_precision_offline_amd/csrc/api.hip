@@ -7,6 +7,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "../../include/w4a16.h"
 #include "internal.h"
@@ -63,6 +64,21 @@ struct Workspace {
   bool external = false;  // caller-owned (w4a16_set_workspace): never grown or freed
 };
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Library-owned buffers replaced by a larger one.  They are never freed: launches still in
+// flight, and HIP graphs captured earlier, may hold their addresses.  Growth at least
+// doubles the buffer, so what is kept here stays below the size of the live buffer.
+std::vector<void*> g_retired;
+
+// True when `st` is being captured into a graph (or its capture state is unknown): no
+// allocation, clearing or synchronization may be issued then.
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
 
 int get_workspace(int dev, hipStream_t st, size_t counters, size_t floats, int** cnt,
                   float** part) {
@@ -74,18 +90,16 @@ int get_workspace(int dev, hipStream_t st, size_t counters, size_t floats, int**
   if (ws.external) {
     if (ws.counter_ints < counters || ws.part_floats < floats) return W4A16_ERR_WORKSPACE;
   } else if (ws.ptr == nullptr || ws.counter_ints < counters || ws.part_floats < floats) {
+    // a graph being captured cannot take the allocation and the clearing of the counters:
+    // the first call of a shape on a stream must come before any capture on it
+    if (capturing(st)) return W4A16_ERR_WORKSPACE;
     size_t c = counters > ws.counter_ints ? counters : ws.counter_ints;
     size_t f = floats > ws.part_floats ? floats : ws.part_floats;
-    c = (c + 63) / 64 * 64;  // keep the partials 256-byte aligned
     if (ws.ptr) {
-      // earlier launches on this stream may still read the old buffer
-      if (hipStreamSynchronize(st) != hipSuccess || hipFree(ws.ptr) != hipSuccess) {
-        (void)hipGetLastError();
-        ws = Workspace();
-        return W4A16_ERR_WORKSPACE;
-      }
-      ws = Workspace();
+      if (c > ws.counter_ints && c < 2 * ws.counter_ints) c = 2 * ws.counter_ints;
+      if (f > ws.part_floats && f < 2 * ws.part_floats) f = 2 * ws.part_floats;
     }
+    c = (c + 63) / 64 * 64;  // keep the partials 256-byte aligned
     void* p = nullptr;
     if (hipMalloc(&p, c * sizeof(int) + f * sizeof(float)) != hipSuccess) {
       (void)hipGetLastError();
@@ -96,6 +110,7 @@ int get_workspace(int dev, hipStream_t st, size_t counters, size_t floats, int**
       (void)hipFree(p);
       return W4A16_ERR_WORKSPACE;
     }
+    if (ws.ptr) g_retired.push_back(ws.ptr);
     ws.ptr = p;
     ws.counter_ints = c;
     ws.part_floats = f;
@@ -507,14 +522,16 @@ int w4a16_set_workspace(void* ptr, size_t bytes, void* stream) {
   int rc = check_device(&dev);
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (capturing(st)) return W4A16_ERR_WORKSPACE;
   std::lock_guard<std::mutex> lk(g_mu);
   Workspace& ws = g_ws[std::make_pair(dev, st)];
-  // earlier launches on this stream may still use the current buffer
-  if (ws.ptr && hipStreamSynchronize(st) != hipSuccess) {
+  // the caller may free its old buffer once this returns: let launches on it drain first
+  if (ws.ptr && ws.external && hipStreamSynchronize(st) != hipSuccess) {
     (void)hipGetLastError();
     return W4A16_ERR_LAUNCH;
   }
-  if (ws.ptr && !ws.external) (void)hipFree(ws.ptr);
+  // a library-owned buffer is kept, not freed (graphs captured earlier may use it)
+  if (ws.ptr && !ws.external) g_retired.push_back(ws.ptr);
   ws = Workspace();
   if (!ptr) return W4A16_OK;
   if (hipMemsetAsync(ptr, 0, W4A16_WS_COUNTER_BYTES, st) != hipSuccess) {

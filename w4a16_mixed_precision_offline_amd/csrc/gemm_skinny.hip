@@ -799,6 +799,14 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
   if (N % (16 * v.NT) != 0) return -2;
   const int Gk = K / KBLK;
   const int MT = (v.XR + 15) / 16;
+  // buffer descriptors and the offsets through them are 32-bit: the X rows of one block,
+  // and the weight bytes of one workgroup's column tiles, must stay below 2 GiB
+  const long long lim = 1LL << 31;
+  if ((long long)v.XR * K * x_elem_bytes(mode) >= lim) return -2;
+  const long long wbytes = mode == W_FP16 ? (long long)v.NT * 16 * K * 2
+                           : mode == W_SP24 ? (long long)v.NT * Gk * 512
+                                            : (long long)v.NT * Gk * 1024;
+  if (wbytes >= lim) return -2;
   p->variant = variant;
   p->mode = mode;
   p->MT = MT;
@@ -820,6 +828,7 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
   if (splits > maxs) splits = maxs;
   if (splits < 1) splits = 1;
   p->splits = splits;
+  if ((long long)p->mblocks * p->nblocks * splits >= lim) return -2;
   p->wgs = p->mblocks * p->nblocks * splits;
   p->threads = 64 * v.WK;
   p->part_floats = splits > 1 ? (size_t)p->mblocks * p->nblocks * splits * v.NT * MT * 256 : 0;
