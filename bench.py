@@ -1,22 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the fused W4A16 GEMM on one MI355X.
 
-Workload (one "step"): the 7B-class decode sweep -- every (K, N) in
-{(4096,4096), (4096,12288), (4096,11008), (11008,4096)} times every M in
-{1,2,4,8,16,32}, group 128 along K, symmetric INT4, fp16 activations ~N(0,1),
-scales uniform in [0.002, 0.02]: 24 launches of w4a16_gemm through the C ABI.
-Inputs are seeded, synthetic, repacked once and resident in HBM before timing.
+Workload (one "step"): the 70B-class large-layer sweep -- every (K, N) in
+{(8192,28672), (28672,8192), (8192,10240)} times every M in {16, 64, 256, 1024, 4096},
+group 128 along K, symmetric INT4, fp16 activations ~N(0,1), scales uniform in
+[0.001, 0.01]: 15 launches of w4a16_gemm (automatic plans) through the C ABI, spanning
+the memory-bound (M = 16, 64) and the matrix-bound (M >= 256) regimes.  Inputs are
+seeded, synthetic, repacked once and resident in HBM before timing; every launch of a
+step reads its own copy of the weights (1.36 GiB in all), so none finds them in L2 or
+the 256 MiB Infinity Cache.
 
-Weights are rotated over enough distinct device copies that no launch reads
-weights an earlier launch left in L2 or the 256 MiB Infinity Cache (every weight
-byte a launch reads was last touched more than 1 GiB of weight traffic earlier),
-as in decoding where each layer's weights are read once per token.  Activations
-may stay cached.
-
-Prints ONE JSON line.  `value` is the packed-weight HBM throughput of the whole
-step (weight bytes of the 24 GEMMs / step time); the same line carries TFLOP/s,
-the per-launch roofline figure, the fp16 (dequantize-then-GEMM) baseline on the
-same shapes, and the CPU oracle timed on this host over one step.
+Prints ONE JSON line (the last line of stdout).  `value` is the step's algorithmic
+TFLOP/s (2MNK summed over the 15 GEMMs / step time); the line also carries the weight
+GB/s, per-M figures with their roofline fractions, the roofline object of the dominant
+kernel (the tiled kernel at M >= 256, timed with HIP events on its stream), the CPU
+oracle timed on this host, the hand-written fp16 dequantize-then-GEMM baseline on the
+same step, and a compact summary of the 7B-class decode sweep (M = 1..32, memory-bound).
+Per-launch tables and the side legs go to --detail.
 """
 import argparse
 import hashlib
@@ -58,35 +58,46 @@ def roof(M, K, N, t, group=128, sparse=False, zero_points=False):
                 roofline_frac=round(max(t_mem, t_mfma) / t, 4))
 
 
-def kernel_sha():
+KERNEL_SOURCES = {"skinny": ("gemm_skinny.hip", "internal.h"),
+                  "tiled": ("gemm_tiled.hip", "internal.h")}
+TRAFFIC_JSON = {"skinny": os.path.join(ROOT, "profiles", "w4a16_gemm_decode_sweep_traffic.json"),
+                "tiled": os.path.join(ROOT, "profiles", "w4a16_tiled_70b_traffic.json")}
+
+
+def kernel_sha(kind="skinny"):
     h = hashlib.sha256()
-    for f in ("gemm_skinny.hip", "internal.h"):
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "w4a16_mixed_precision_offline_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles():
+def traffic_from_profiles(kind="tiled"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "w4a16_gemm_decode_sweep_traffic.json")
+    p = TRAFFIC_JSON[kind]
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("kernel_sha") != kernel_sha():
+    if t.get("kernel_sha") != kernel_sha(kind):
         return None
     return t.get("hbm_bytes_per_launch")
 
 
 COPY_BYTES = 256 << 20
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "w4a16_gemm_decode_sweep_traffic.json")
+PMC_COMMANDS = {
+    "tiled": "python -u bench.py --roofline-only --steps 2 --warmup 1 --copy-calibration",
+    "skinny": "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --copy-calibration",
+}
 
 
-def pmc_summary(fetch_csv, write_csv):
-    """HBM bytes per fused-GEMM launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
+def pmc_summary(fetch_csv, write_csv, kind="tiled"):
+    """HBM bytes per fused-GEMM call from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by the factor that makes the same counter read the known
-    size of a plain 256 MiB device copy in the same run."""
+    size of a plain 256 MiB device copy in the same run.  kind "tiled": the calls of the
+    roofline set (a tiled_kernel dispatch plus, where tiles are cut, its tiled_fixup_kernel
+    dispatch); kind "skinny": the skinny_kernel dispatches of the decode sweep."""
     import csv
 
     def per_dispatch(path, counter):
@@ -98,122 +109,100 @@ def pmc_summary(fetch_csv, write_csv):
             d["v"] += float(r["Counter_Value"])
         return out
 
+    main = "skinny_kernel" if kind == "skinny" else "tiled_kernel"
+    extra = None if kind == "skinny" else "tiled_fixup_kernel"
     res = {}
     for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         disp = per_dispatch(path, counter)
         copies = [d["v"] for d in disp.values() if "copyBuffer" in d["name"]]
-        gemms = [d["v"] for d in disp.values() if "skinny_kernel" in d["name"]]
-        if not copies or not gemms:
+        calls = [d["v"] for d in disp.values() if main in d["name"]]
+        fix = [d["v"] for d in disp.values() if extra and extra in d["name"]]
+        if not copies or not calls:
             raise SystemExit(f"{path}: no copy or no GEMM dispatches with {counter}")
         # the copies are the largest copyBuffer dispatches (the known-size calibration)
         copies.sort()
         calib = copies[-3:]
         factor = (COPY_BYTES / 1024.0) / (sum(calib) / len(calib))
-        res[tag] = dict(factor=factor, kib_per_launch=sum(gemms) / len(gemms), launches=len(gemms),
-                        copy_kib=sum(calib) / len(calib))
+        res[tag] = dict(factor=factor, kib_per_launch=(sum(calls) + sum(fix)) / len(calls),
+                        launches=len(calls), fixups=len(fix), copy_kib=sum(calib) / len(calib))
     hbm = (res["fetch"]["kib_per_launch"] * res["fetch"]["factor"] +
            res["write"]["kib_per_launch"] * res["write"]["factor"]) * 1024.0
-    out = dict(kernel_sha=kernel_sha(), hbm_bytes_per_launch=int(hbm),
+    cmd = PMC_COMMANDS[kind]
+    out = dict(kernel_sha=kernel_sha(kind), hbm_bytes_per_launch=int(hbm),
                fetch_factor=round(res["fetch"]["factor"], 4), write_factor=round(res["write"]["factor"], 4),
                fetch_kib_per_launch=round(res["fetch"]["kib_per_launch"], 1),
                write_kib_per_launch=round(res["write"]["kib_per_launch"], 1),
-               launches=res["fetch"]["launches"],
-               commands=[f"rocprofv3 --pmc {c} -d {os.path.dirname(p)} -o run --output-format csv -- "
-                         "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --no-graph "
-                         "--no-large --no-configs --copy-calibration"
+               launches=res["fetch"]["launches"], fixup_dispatches=res["fetch"]["fixups"],
+               commands=[f"rocprofv3 --pmc {c} -d {os.path.dirname(p)} -o run --output-format csv -- {cmd}"
                          for c, p in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv))]
-               + [f"python bench.py --pmc-summary {fetch_csv} {write_csv}"])
-    with open(TRAFFIC_JSON, "w") as f:
+               + [f"python bench.py --pmc-kind {kind} --pmc-summary {fetch_csv} {write_csv}"])
+    with open(TRAFFIC_JSON[kind], "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
-def large_m_sweep(w4, torch, group):
-    """TFLOP/s of w4a16_gemm (automatic plan) on the 70B-class shapes at M >= 256, next to
-    the hand-written fp16 GEMM on the dequantized weights (w4a16_fp16_gemm, the unfused
-    baseline's GEMM) and torch's fp16 matmul on the same weights (context).  Inputs are seeded and
-    synthetic with the workload's distributions (codes uniform 0..15, scales U[0.001,
-    0.01], X ~ N(0,1)), generated on the device; each shape is timed over back-to-back
-    launches after a warmup."""
-    shapes = [(8192, 28672), (28672, 8192), (8192, 10240)]
-    Ms = [16, 64, 256, 1024, 4096]
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(2024)
-    out = []
+TRACE_MD = os.path.join(ROOT, "profiles", "w4a16_tiled_70b_kernel_trace.md")
+TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kt -o run --output-format csv "
+                 "-- python -u bench.py --steps 20 --warmup 3 --no-cpu --no-baseline --no-decode")
 
-    def timed(fn, reps):
-        # warm up for ~50 ms: the clock ramps under sustained matrix load
-        t0 = time.perf_counter()
-        while True:
-            fn()
-            torch.cuda.synchronize()
-            if time.perf_counter() - t0 > 0.05:
-                break
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3 / reps
 
-    # measured ceiling: dense fp16 matrix instructions with no memory traffic, after the
-    # same 50 ms warmup (the clock settles lower under sustained matrix load)
-    probe_out = torch.zeros(4, dtype=torch.float32, device="cuda")
-    pw, pi = 1024, 2000  # about 0.4 ms per launch
-    tp = timed(lambda: w4.w4a16_probe_mfma(pw, pi, probe_out), 5)
-    mfma_probe = w4.w4a16_probe_mfma_flops(pw, pi) / tp / 1e12
-
-    for (K, N) in shapes:
-        q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
-                          generator=gen)
-        s = (torch.rand((K // group, N), device="cuda", generator=gen) * 0.009 + 0.001).half()
-        wp, sp, _ = w4.alloc_packed(K, N, group, False)
-        w4.w4a16_repack(q, s, None, wp, sp, None, K, N, group)
-        Wt = torch.empty((N, K), dtype=torch.float16, device="cuda")
-        w4.w4a16_dequant(q, s, None, Wt, K, N, group)
-        del q
-        # the memory-bound runs (M = 16, 64) rotate over weight copies totalling at least
-        # 512 MiB, so that no launch finds its weights in the 256 MiB Infinity Cache
-        ncop = max(2, -(-(512 << 20) // (K * N // 2)))
-        copies = [(wp, sp)] + [(wp.clone(), sp.clone()) for _ in range(ncop - 1)]
-        for M in Ms:
-            X = torch.randn((M, K), device="cuda", generator=gen).half()
-            Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-            fl = 2.0 * M * N * K
-            reps = max(3, min(50, int(2e13 / fl)))
-            if M < 256:
-                t = time_rotated(torch, [lambda c=c: w4.w4a16_gemm(X, c[0], c[1], None, Y, M, N, K,
-                                                                   group) for c in copies])
-            else:
-                t = timed(lambda: w4.w4a16_gemm(X, wp, sp, None, Y, M, N, K, group), reps)
-            tb = timed(lambda: w4.w4a16_fp16_gemm(X, Wt, Y, M, N, K), reps)
-            tt = timed(lambda: torch.nn.functional.linear(X, Wt), reps)
-            plan = w4.w4a16_gemm_describe(M, N, K, group)
-            wbytes = algorithmic(M, K, N, group)[0]
-            out.append(dict(M=M, K=K, N=N, us=round(t * 1e6, 2), TFLOPs=round(fl / t / 1e12, 1),
-                            weight_GBps=round(wbytes / t / 1e9, 1), **roof(M, K, N, t, group),
-                            mfma_frac=round(fl / t / 1e12 / FP16_PEAK_TFLOPS, 4),
-                            frac_of_mfma_probe=round(fl / t / 1e12 / mfma_probe, 4),
-                            plan=plan["name"],
-                            fp16_baseline_TFLOPs=round(fl / tb / 1e12, 1),
-                            torch_fp16_TFLOPs=round(fl / tt / 1e12, 1)))
-            del X, Y
-        del wp, sp, s, Wt, copies
-    torch.cuda.synchronize()
-    big = [r for r in out if r["M"] >= 1024]
-    small = [r for r in out if r["M"] <= 32]
-    return dict(peak_TFLOPs=FP16_PEAK_TFLOPS, unit="TFLOP/s",
-                mfma_probe_TFLOPs=round(mfma_probe, 1),
-                min_mfma_frac_M_ge_1024=min(r["mfma_frac"] for r in big),
-                mean_mfma_frac_M_ge_1024=round(sum(r["mfma_frac"] for r in big) / len(big), 4),
-                mean_hbm_frac_M_le_32=round(sum(r["roofline_frac"] for r in small) / len(small), 4),
-                runs=out)
+def trace_summary(csv_path, bench_line_path=None):
+    """Per-kernel durations from a rocprofv3 kernel trace (CSV) of the headline step, and
+    the per-call duration of the roofline set: the packed-weight tiled kernel with 128-row
+    tiles (template <8, *, *, 0>, the M >= 256 launches) plus the stream-K fixup passes of
+    those calls (<8, *>), divided by the number of such tiled-kernel launches.  Writes the
+    markdown summary into profiles/ next to the bench line of the same command."""
+    import csv
+    import re
+    rows = list(csv.DictReader(open(csv_path)))
+    stats = {}
+    roof_t, roof_calls = 0.0, 0
+    for r in rows:
+        name = r.get("Kernel_Name", "")
+        t = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3  # ns -> us
+        m = re.search(r"(\w+_kernel)<([^>]*)>", name)
+        short = f"{m.group(1)}<{m.group(2)}>" if m else name[:60]
+        st = stats.setdefault(short, [0, 0.0, 1e30, 0.0])
+        st[0] += 1
+        st[1] += t
+        st[2] = min(st[2], t)
+        st[3] = max(st[3], t)
+        if m and m.group(1) == "tiled_kernel":
+            a = [int(x) for x in m.group(2).split(",")]
+            if a[0] == 8 and a[3] == 0:
+                roof_t += t
+                roof_calls += 1
+        elif m and m.group(1) == "tiled_fixup_kernel":
+            a = [int(x) for x in m.group(2).split(",")]
+            if a[0] == 8:
+                roof_t += t
+    lines = ["# Tiled kernel on the 70B-class sweep: kernel durations (rocprofv3 kernel trace)", "",
+             "Command (repository root, one MI355X):", "", "```", TRACE_COMMAND,
+             f"python bench.py --trace-summary gpurun_out/prof_kt/<host>/run_kernel_trace.csv"
+             + (" gpurun_out/bench_trace.json" if bench_line_path else ""), "```", "",
+             "| kernel (template args) | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for k in sorted(stats):
+        c, tot, mn, mx = stats[k]
+        lines.append(f"| `{k}` | {c} | {tot / c:.3f} | {mn:.3f} | {mx:.3f} |")
+    per_call = roof_t / max(1, roof_calls)
+    lines += ["", f"Roofline set (w4a16_gemm at M >= 256: `tiled_kernel<8, *, *, 0>` plus its "
+                  f"`tiled_fixup_kernel<8, *>` passes): {roof_calls} calls, **{per_call:.2f} us** "
+                  "per call (warmup and timed steps; each step has the same launches)."]
+    if bench_line_path:
+        line = json.load(open(bench_line_path))
+        ev = line["roofline"]["avg_launch_us"]
+        lines += ["", f"The bench line of the same command measured {ev:.2f} us per call with HIP "
+                      f"events on the kernels' stream (`roofline.avg_launch_us`): "
+                      f"{100 * (ev / per_call - 1):+.1f}% from the kernel durations above "
+                      "(the events also hold the gaps between launches, and tracing widens them).",
+                  "", "```", json.dumps(line["roofline"]), "```"]
+    out = "\n".join(lines) + "\n"
+    with open(TRACE_MD, "w") as f:
+        f.write(out)
+    print(out)
 
 
 _SIDE = {}
-STEP_STATS = {}  # per-step time percentiles (ms) of each timed step function
 
 
 def time_rotated(torch, calls, min_reps=20, target_s=0.02, graph=True):
@@ -357,20 +346,20 @@ def config_legs(w4, torch, group):
 
 
 def group64_leg(w4, torch):
-    """Groups of 64 rows (two scale rows per 128-row block) against groups of 128 on the
-    same codes: decode shapes from the 7B-class sweep and one large-M layer, symmetric
-    and with zero-points.  Seeded synthetic weights (codes uniform 0..15, scales
-    U[0.002, 0.02], zero-points uniform 0..15) generated on the device; weights rotate
-    over copies totalling at least 512 MiB."""
+    """Groups of 64 and of 256 rows against groups of 128 on the same codes: decode shapes
+    from the 7B-class sweep and one large-M layer, symmetric and with zero-points.  Seeded
+    synthetic weights (codes uniform 0..15, scales U[0.002, 0.02], zero-points uniform
+    0..15) generated on the device; weights rotate over copies totalling at least 512 MiB."""
     rot = 512 << 20
     gen = torch.Generator(device="cuda")
     gen.manual_seed(64)
     runs = []
+    groups = (128, 64, 256)
     for (K, N, Ms) in [(4096, 11008, (1, 16, 32)), (8192, 10240, (1024,))]:
         q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
                           generator=gen)
         packs = {}
-        for g in (128, 64):
+        for g in groups:
             s = (torch.rand((K // g, N), device="cuda", generator=gen) * 0.018 + 0.002).half()
             z = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // g, N // 8), dtype=torch.int32,
                               device="cuda", generator=gen)
@@ -385,20 +374,18 @@ def group64_leg(w4, torch):
             Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
             for asym in (False, True):
                 t = {}
-                for g in (128, 64):
+                for g in groups:
                     t[g] = time_rotated(torch, [lambda c=c, g=g: w4.w4a16_gemm(X, c[0], c[1], c[2], Y,
                                                                              M, N, K, g)
                                                 for c in packs[(g, asym)]])
-                wb64 = K * N // 2 + 4 * (K // 128) * N + ((K // 64) * N // 2 if asym else 0)
                 runs.append(dict(M=M, K=K, N=N, zero_points=asym, g128_us=round(t[128] * 1e6, 2),
-                                 g64_us=round(t[64] * 1e6, 2),
+                                 g64_us=round(t[64] * 1e6, 2), g256_us=round(t[256] * 1e6, 2),
                                  g64_over_g128_time=round(t[64] / t[128], 3),
-                                 g64_weight_GBps=round(wb64 / t[64] / 1e9, 1),
-                                 g64_TFLOPs=round(2.0 * M * N * K / t[64] / 1e12, 1)))
+                                 g256_over_g128_time=round(t[256] / t[128], 3)))
             del X, Y
         del q, packs
         torch.cuda.empty_cache()
-    return dict(kernel="w4a16_gemm with groups of 64 rows vs 128", runs=runs)
+    return dict(kernel="w4a16_gemm with groups of 64 and 256 rows vs 128", runs=runs)
 
 
 def bf16_leg(w4, torch):
@@ -624,23 +611,341 @@ def profile_tiled(w4, torch):
     print(json.dumps(dict(profile_tiled=dict(M=M, K=K, N=N, us_per_launch=out))), flush=True)
 
 
+HEADLINE_CFG = 2  # the large-layer sweep: 70B-class shapes, M = 16 .. 4096
+ROOF_MIN_M = 256  # launches at or above this M form the roofline set (tiled kernel, MFMA-bound)
+
+
+def headline_inputs(w4, torch, roofline_only=False):
+    """Seeded synthetic inputs of the 70B-class large-layer sweep, resident in HBM: the
+    three shapes' weights repacked once, one distinct device copy per launch of a step
+    (15 copies, 1.36 GiB, so that no launch finds its weights in L2 or the 256 MiB
+    Infinity Cache), X and Y for every (M, K, N), and the dequantized fp16 weights of the
+    unfused baseline.  The launch list of one step is M outer, shape inner."""
+    from gen import CONFIGS, activations, config_runs, weights
+    runs = config_runs(HEADLINE_CFG)
+    shapes = []
+    for w in runs:
+        if (w.K, w.N) not in shapes:
+            shapes.append((w.K, w.N))
+    Ms = [M for M in CONFIGS[HEADLINE_CFG]["Ms"] if M >= ROOF_MIN_M or not roofline_only]
+    group = 128
+    packed, fp16w, host = {}, {}, {}
+    for (K, N) in shapes:
+        w = next(r for r in runs if (r.K, r.N) == (K, N))
+        d = weights(w)
+        host[(K, N)] = dict(Qp=d["Qp"], s=d["s"])
+        q = torch.from_numpy(d["Qp"]).cuda()
+        s = torch.from_numpy(d["s"]).cuda()
+        wp, sp, _ = w4.alloc_packed(K, N, group, False)
+        w4.w4a16_repack(q, s, None, wp, sp, None, K, N, group)
+        packed[(K, N)] = [(wp, sp)] + [(wp.clone(), sp.clone()) for _ in range(len(Ms) - 1)]
+        if not roofline_only:
+            Wt = torch.empty((N, K), dtype=torch.float16, device="cuda")
+            w4.w4a16_dequant(q, s, None, Wt, K, N, group)
+            fp16w[(K, N)] = Wt
+        del q, s, d
+    X, Y, Xh = {}, {}, {}
+    for w in runs:
+        if w.M not in Ms:
+            continue
+        a = activations(w)
+        if w.M == ROOF_MIN_M:
+            Xh[(w.K, w.N)] = a  # the CPU oracle's sample
+        X[(w.M, w.K, w.N)] = torch.from_numpy(a).cuda()
+        Y[(w.M, w.K, w.N)] = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    launches = [(M, K, N, i) for i, M in enumerate(Ms) for (K, N) in shapes]
+    return dict(shapes=shapes, Ms=Ms, packed=packed, fp16w=fp16w, host=host, X=X, Y=Y, Xh=Xh,
+                launches=launches, group=group)
+
+
+def time_eager_steps(torch, stream, launch_fns, steps, warmup):
+    """Runs `warmup` untimed steps, then `steps` timed steps of the launch functions in
+    order on `stream`, with a HIP event recorded after every launch.  Returns (seconds per
+    step, per-launch durations in seconds as [steps][launches]).  The durations are GPU
+    event deltas on the stream the kernels run on; the host enqueues far ahead of the GPU
+    (a step takes milliseconds of GPU time), so no host gap enters them after the first
+    launches of the first step."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            for f in launch_fns:
+                f()
+    torch.cuda.synchronize()
+    n = len(launch_fns)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for st in range(steps):
+            for i, f in enumerate(launch_fns):
+                f()
+                evs[st][i].record(stream)
+    torch.cuda.synchronize()
+    dur = []
+    prev = e0
+    for st in range(steps):
+        row = []
+        for i in range(n):
+            row.append(prev.elapsed_time(evs[st][i]) / 1e3)
+            prev = evs[st][i]
+        dur.append(row)
+    total = e0.elapsed_time(evs[-1][-1]) / 1e3
+    return total / steps, dur
+
+
+def roof_times(M, K, N, group=128):
+    """(t_mem, t_mfma) in seconds: algorithmic bytes at the HBM peak, flops at the fp16
+    dense matrix peak."""
+    _, ab, fl = algorithmic(M, K, N, group)
+    return ab / (HBM_PEAK_GBPS * 1e9), fl / (FP16_PEAK_TFLOPS * 1e12)
+
+
+def headline_leg(w4, torch, inp, stream, steps, warmup, roofline_only=False):
+    """The timed step of the 70B-class sweep through w4a16_gemm (automatic plans)."""
+    group = inp["group"]
+    fns = []
+    for (M, K, N, c) in inp["launches"]:
+        wp, sp = inp["packed"][(K, N)][c]
+        fns.append(lambda X=inp["X"][(M, K, N)], Y=inp["Y"][(M, K, N)], wp=wp, sp=sp, M=M, K=K, N=N:
+                   w4.w4a16_gemm(X, wp, sp, None, Y, M, N, K, group))
+    t_step, dur = time_eager_steps(torch, stream, fns, steps, warmup)
+    launches = inp["launches"]
+    per_launch = [sum(d[i] for d in dur) / len(dur) for i in range(len(launches))]
+    step_fl = sum(algorithmic(M, K, N)[2] for (M, K, N, _) in launches)
+    step_w = sum(algorithmic(M, K, N)[0] for (M, K, N, _) in launches)
+    # per M: the three shapes together
+    per_m = {}
+    for M in inp["Ms"]:
+        idx = [i for i, l in enumerate(launches) if l[0] == M]
+        t = sum(per_launch[i] for i in idx)
+        fl = sum(algorithmic(*launches[i][:3])[2] for i in idx)
+        wb = sum(algorithmic(*launches[i][:3])[0] for i in idx)
+        tr = sum(max(roof_times(*launches[i][:3])) for i in idx)
+        per_m[str(M)] = dict(us=round(t * 1e6, 1), TFLOPs=round(fl / t / 1e12, 1),
+                             weight_GBps=round(wb / t / 1e9, 1), roofline_frac=round(tr / t, 3))
+    # the roofline kernel: the tiled kernel at M >= 256 (MFMA-bound), one w4a16_gemm call
+    # = its launch plus, where stripes cut tiles, the stream-K fixup launch
+    ridx = [i for i, l in enumerate(launches) if l[0] >= ROOF_MIN_M]
+    r_t = sum(per_launch[i] for i in ridx)
+    r_fl = sum(algorithmic(*launches[i][:3])[2] for i in ridx)
+    r_ab = sum(algorithmic(*launches[i][:3])[1] for i in ridx)
+    table = [dict(M=M, K=K, N=N, us=round(per_launch[i] * 1e6, 2),
+                  TFLOPs=round(algorithmic(M, K, N)[2] / per_launch[i] / 1e12, 1),
+                  roofline_frac=round(max(roof_times(M, K, N)) / per_launch[i], 4),
+                  plan=w4.w4a16_gemm_describe(M, N, K, group)["name"])
+             for i, (M, K, N, _) in enumerate(launches)]
+    return dict(t_step=t_step, step_flops=step_fl, step_wbytes=step_w, per_m=per_m, table=table,
+                roof=dict(n=len(ridx), t=r_t, flops=r_fl, alg_bytes=r_ab),
+                frac_all=sum(max(roof_times(*l[:3])) for l in launches) / sum(per_launch))
+
+
+def fp16_baseline_leg(w4, torch, inp, stream, steps):
+    """The unfused baseline on the same step: the fp16 weights the hand-written dequant
+    kernel wrote (once, not timed), then the hand-written fp16 GEMM; torch's fp16 matmul
+    (hipBLASLt) on the same weights as context.  fp16 weights are 4x the bytes, so the
+    other shapes' weights between two uses of one shape's weights exceed the Infinity
+    Cache: no copies are needed."""
+    fns = [lambda X=inp["X"][(M, K, N)], Y=inp["Y"][(M, K, N)], Wt=inp["fp16w"][(K, N)], M=M, K=K, N=N:
+           w4.w4a16_fp16_gemm(X, Wt, Y, M, N, K) for (M, K, N, _) in inp["launches"]]
+    t16, dur = time_eager_steps(torch, stream, fns, steps, 1)
+    tfn = [lambda X=inp["X"][(M, K, N)], Wt=inp["fp16w"][(K, N)]: torch.nn.functional.linear(X, Wt)
+           for (M, K, N, _) in inp["launches"]]
+    tt, _ = time_eager_steps(torch, stream, tfn, max(2, steps // 2), 1)
+    per_launch = [sum(d[i] for d in dur) / len(dur) for i in range(len(fns))]
+    per_m = {}
+    for M in inp["Ms"]:
+        idx = [i for i, l in enumerate(inp["launches"]) if l[0] == M]
+        t = sum(per_launch[i] for i in idx)
+        fl = sum(algorithmic(*inp["launches"][i][:3])[2] for i in idx)
+        per_m[str(M)] = round(fl / t / 1e12, 1)
+    return dict(t_step=t16, t_torch=tt, per_m_TFLOPs=per_m)
+
+
+def decode_sweep_leg(w4, torch, steps, warmup, use_graph=True):
+    """The 7B-class decode sweep (24 GEMMs, M = 1..32, memory-bound), weights rotated over
+    copies totalling over 1 GiB, timed over HIP-graph replays; beside it a plain streaming
+    read of the same packed codes, launch for launch (the achievable ceiling at these
+    sizes).  Returns a compact summary and the per-launch table."""
+    from gen import CONFIGS, activations, config_runs, weights
+    runs = config_runs(1)
+    shapes = []
+    for w in runs:
+        if (w.K, w.N) not in shapes:
+            shapes.append((w.K, w.N))
+    Ms = CONFIGS[1]["Ms"]
+    group = 128
+    step_wbytes = sum(algorithmic(1, K, N)[0] for (K, N) in shapes)
+    per_step = len(Ms)
+    cycle = max(1, -(-ROTATE_BYTES // (step_wbytes * per_step)))
+    R = per_step * cycle
+    packed = {}
+    for (K, N) in shapes:
+        d = weights(next(r for r in runs if (r.K, r.N) == (K, N)))
+        q = torch.from_numpy(d["Qp"]).cuda()
+        s = torch.from_numpy(d["s"]).cuda()
+        wp, sp, _ = w4.alloc_packed(K, N, group, False)
+        w4.w4a16_repack(q, s, None, wp, sp, None, K, N, group)
+        packed[(K, N)] = [(wp, sp)] + [(wp.clone(), sp.clone()) for _ in range(R - 1)]
+        del q, s
+    Xs = {(w.M, w.K, w.N): torch.from_numpy(activations(w)).cuda() for w in runs}
+    Ys = {k: torch.empty((k[0], k[2]), dtype=torch.float16, device="cuda") for k in Xs}
+    stream = torch.cuda.Stream()
+    probe_out = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def launches(step_idx):
+        cyc = step_idx % cycle
+        return [(M, K, N, cyc * per_step + i) for i, M in enumerate(Ms) for (K, N) in shapes]
+
+    def gemm_step(step_idx):
+        for (M, K, N, c) in launches(step_idx):
+            wp, sp = packed[(K, N)][c]
+            w4.w4a16_gemm(Xs[(M, K, N)], wp, sp, None, Ys[(M, K, N)], M, N, K, group)
+
+    def read_step(step_idx):
+        for (M, K, N, c) in launches(step_idx):
+            w4.w4a16_probe_read(packed[(K, N)][c][0], K * N // 2, probe_out)
+
+    def timed(run_step, nsteps):
+        with torch.cuda.stream(stream):
+            for i in range(max(warmup, cycle)):
+                run_step(i)
+        torch.cuda.synchronize()
+        graphs = None
+        if use_graph:
+            graphs = []
+            for c in range(cycle):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    run_step(c)
+                graphs.append(g)
+            with torch.cuda.stream(stream):
+                for i in range(warmup):
+                    graphs[i % cycle].replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for i in range(nsteps):
+                if graphs is not None:
+                    graphs[i % cycle].replay()
+                else:
+                    run_step(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / nsteps
+
+    t = timed(gemm_step, steps)
+    tr = timed(read_step, max(5, steps // 2))
+    L = launches(0)
+    n = len(L)
+    wb = sum(algorithmic(M, K, N)[0] for (M, K, N, _) in L)
+    ab = sum(algorithmic(M, K, N)[1] for (M, K, N, _) in L)
+    out = dict(workload="decode-shape sweep, 7B-class: (K,N) in {(4096,4096),(4096,12288),"
+                        "(4096,11008),(11008,4096)} x M in {1,2,4,8,16,32}; 24 GEMMs per step",
+               ms_per_step=round(t * 1e3, 4), weight_GBps=round(wb / t / 1e9, 1),
+               avg_launch_us=round(t / n * 1e6, 3),
+               hbm_frac=round(ab / n / (t / n) / 1e9 / HBM_PEAK_GBPS, 4),
+               read_ceiling_us_per_launch=round(tr / n * 1e6, 3),
+               gemm_over_read_time=round(t / tr, 3), launch="hip_graph" if use_graph else "eager")
+    del packed, Xs, Ys
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_oracle_leg(inp):
+    """The CPU oracle as it stands, on this host: the three 70B-class shapes at M = 256
+    (unpack + exact fp64 dequant + fp64 matmul, NumPy), repeated until at least 10 s of
+    work (bounded at 30 s); reported in TFLOP/s of the GEMM's algorithmic flops."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    passes = 0
+    fl = 0
+    while True:
+        for (K, N) in inp["shapes"]:
+            h = inp["host"][(K, N)]
+            oracle.gemm(inp["Xh"][(K, N)], h["Qp"], h["s"], None, inp["group"])
+            fl += 2.0 * ROOF_MIN_M * K * N
+        passes += 1
+        tc = time.perf_counter() - t0
+        if tc >= 10.0 or tc * (passes + 1) / passes > 30.0:
+            break
+    return dict(value=round(fl / tc / 1e12, 6), unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{passes} pass(es) over the three 70B-class shapes at M = {ROOF_MIN_M} "
+                       "(unpack + exact fp64 dequant + fp64 matmul, NumPy)",
+                seconds=round(tc, 2))
+
+
+def build_line(h, steps, warmup, traffic, cpu, base, decode):
+    """The one JSON line of the run (kept compact: the driver reads the tail of stdout)."""
+    t_step = h["t_step"]
+    r = h["roof"]
+    n_roof = r["n"]
+    roof_avg_s = r["t"] / n_roof
+    achieved = r["flops"] / r["t"] / 1e12
+    return {
+        "metric": "W4A16 GEMM TFLOP/s + weight HBM GB/s vs M (1..4096), % of roofline",
+        "value": round(h["step_flops"] / t_step / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "large-layer sweep, 70B-class: (K,N) in {(8192,28672),(28672,8192),"
+                        "(8192,10240)} x M in {%s}, group 128 along K, symmetric INT4, fp16 X ~ "
+                        "N(0,1), scales U[0.001,0.01]; %d GEMMs per step"
+                        % (",".join(str(m) for m in inp_ms(h)), len(h["table"])),
+            "launch": "eager, one HIP event after each launch",
+            "weight_copies": len(h["table"]),
+            "parallelism": "single GPU",
+        },
+        "weight_GBps": round(h["step_wbytes"] / t_step / 1e9, 1),
+        "roofline_frac_all_launches": round(h["frac_all"], 4),
+        "per_M": h["per_m"],
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": FP16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / FP16_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "tiled_kernel (+ its stream-K fixup where tiles are cut): the w4a16_gemm "
+                      "launches at M >= %d, %d per step" % (ROOF_MIN_M, n_roof),
+            "avg_launch_us": round(roof_avg_s * 1e6, 2),
+            "algorithmic_bytes_per_launch": int(r["alg_bytes"] / n_roof),
+        },
+        "cpu_baseline": cpu,
+        "fp16_baseline": base,
+        "decode_sweep": decode,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of HIP graphs")
     ap.add_argument("--no-baseline", action="store_true", help="skip the fp16 baseline")
-    ap.add_argument("--variant", type=int, default=-1, help="force a kernel variant (tuning)")
-    ap.add_argument("--splits", type=int, default=0, help="force split-K slices (tuning)")
-    ap.add_argument("--detail", default=None, help="write per-launch detail JSON here")
-    ap.add_argument("--no-large", action="store_true",
-                    help="skip the large-M (70B-class, MFMA-bound) sweep")
-    ap.add_argument("--no-configs", action="store_true",
-                    help="skip the 2:4-sparse and zero-point workload legs")
-    ap.add_argument("--no-table", action="store_true",
-                    help="skip the per-shape table (a kernel trace then holds only the step's launches)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-sweep leg")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the roofline set (M >= 256 launches of the step), for profiler runs")
+    ap.add_argument("--detail", default=None, help="write per-launch tables and extra legs (JSON) here")
+    ap.add_argument("--all-legs", action="store_true",
+                    help="also run the side legs (configs 0/3/4, groups of 64/256, bf16, fp8, "
+                         "MXFP4, load-time kernels) into the --detail file")
     ap.add_argument("--profile-tiled", action="store_true",
                     help="only a short W4A16 / W4A8 tiled-kernel workload (for counter runs)")
     ap.add_argument("--only-mxfp4", action="store_true",
@@ -650,9 +955,17 @@ def main():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="summarize two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "this script into profiles/ and exit")
+    ap.add_argument("--pmc-kind", choices=("tiled", "skinny"), default="tiled",
+                    help="which kernel --pmc-summary summarizes")
+    ap.add_argument("--trace-summary", nargs="+", metavar="CSV", default=None,
+                    help="summarize a rocprofv3 kernel trace of the headline run (and the "
+                         "bench line it printed, as a JSON file) into profiles/ and exit")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
+        pmc_summary(*args.pmc_summary, kind=args.pmc_kind)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -662,11 +975,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import w4a16_mixed_precision_offline_amd as w4
-    from gen import CONFIGS, activations, config_runs, weights
 
     torch.cuda.set_device(0)
     if args.profile_tiled:
@@ -675,99 +986,9 @@ def main():
     if args.only_mxfp4:
         print(json.dumps(dict(mxfp4_in_mfma_dequant=mxfp4_leg(w4, torch))), flush=True)
         return
-    runs = config_runs(1)
-    shapes = []
-    for w in runs:
-        if (w.K, w.N) not in shapes:
-            shapes.append((w.K, w.N))
-    Ms = CONFIGS[1]["Ms"]
-    group = 128
-
-    # ---- inputs, resident in HBM -----------------------------------------------------
-    step_wbytes = sum(algorithmic(1, K, N)[0] for (K, N) in shapes)
-    copies_per_step = len(Ms)  # each launch of a shape within a step uses a distinct copy
-    steps_per_cycle = max(1, -(-ROTATE_BYTES // (step_wbytes * copies_per_step)))
-    R = copies_per_step * steps_per_cycle
-    host = {}
-    packed = {}
-    for (K, N) in shapes:
-        w = next(r for r in runs if (r.K, r.N) == (K, N))
-        d = weights(w)
-        host[(K, N)] = d
-        q = torch.from_numpy(d["Qp"]).cuda()
-        s = torch.from_numpy(d["s"]).cuda()
-        wp, sp, _ = w4.alloc_packed(K, N, group, False)
-        w4.w4a16_repack(q, s, None, wp, sp, None, K, N, group)
-        packed[(K, N)] = [(wp, sp)] + [(wp.clone(), sp.clone()) for _ in range(R - 1)]
-        del q, s
-    Xs, Ys, Xh = {}, {}, {}
-    for w in runs:
-        X = activations(w)
-        Xh[(w.M, w.K, w.N)] = X
-        Xs[(w.M, w.K, w.N)] = torch.from_numpy(X).cuda()
-        Ys[(w.M, w.K, w.N)] = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
-    torch.cuda.synchronize()
-
-    # launch list of one step: M outer, shape inner; copy index advances per launch
-    def step_launches(step_idx):
-        out = []
-        cyc = step_idx % steps_per_cycle
-        for i, M in enumerate(Ms):
-            for (K, N) in shapes:
-                out.append((M, K, N, cyc * copies_per_step + i))
-        return out
-
-    def run_step_w4(step_idx):
-        for (M, K, N, c) in step_launches(step_idx):
-            wp, sp = packed[(K, N)][c]
-            w4.w4a16_gemm_plan(Xs[(M, K, N)], wp, sp, None, Ys[(M, K, N)], M, N, K, group,
-                               args.variant, args.splits)
 
     stream = torch.cuda.Stream()
-
-    def time_steps(run_step, nsteps, warmup, use_graph):
-        """Returns (seconds per step, mode)."""
-        with torch.cuda.stream(stream):
-            for i in range(max(warmup, steps_per_cycle if use_graph else 0)):
-                run_step(i)
-        torch.cuda.synchronize()
-        graphs = None
-        if use_graph:
-            try:
-                graphs = []
-                for c in range(steps_per_cycle):
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g, stream=stream):
-                        run_step(c)
-                    graphs.append(g)
-                torch.cuda.synchronize()
-                with torch.cuda.stream(stream):
-                    for i in range(warmup):
-                        graphs[i % steps_per_cycle].replay()
-                torch.cuda.synchronize()
-            except Exception as e:  # capture unsupported: fall back to eager launches
-                print(f"bench.py: graph capture failed ({e}); timing eager launches",
-                      file=sys.stderr)
-                graphs = None
-        # one event between consecutive steps: the first and last bracket the timed steps,
-        # the ones between give the per-step distribution
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            evs[0].record(stream)
-            for i in range(nsteps):
-                if graphs is not None:
-                    graphs[i % steps_per_cycle].replay()
-                else:
-                    run_step(i)
-                evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(nsteps))
-        pct = lambda f: per_step[min(nsteps - 1, int(f * (nsteps - 1) + 0.5))]
-        STEP_STATS[run_step.__name__] = dict(p10=round(pct(0.1), 5), p50=round(pct(0.5), 5),
-                                             p90=round(pct(0.9), 5))
-        return evs[0].elapsed_time(evs[-1]) / 1e3 / nsteps, ("hip_graph" if graphs is not None else "eager")
-
+    inp = headline_inputs(w4, torch, roofline_only=args.roofline_only)
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
         dst = torch.empty_like(src)
@@ -775,220 +996,61 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    print(f"bench.py: inputs resident, timing {args.steps} steps", file=sys.stderr, flush=True)
+    h = headline_leg(w4, torch, inp, stream, args.steps, args.warmup, args.roofline_only)
+    t_step = h["t_step"]
+    traffic = traffic_from_profiles("tiled")
 
-    t_step, mode = time_steps(run_step_w4, args.steps, args.warmup, not args.no_graph)
-
-    # ---- per-shape durations for the per-run table: for each GEMM of the step, one HIP
-    #      graph of back-to-back launches over all R weight copies, replayed; eager launches
-    #      from Python would time the host's launch rate, not the GPU, at these sizes -----
-    per_launch = []
-    launches = step_launches(0)
-    for (M, K, N, _) in ([] if args.no_table else launches):
-        calls = [(lambda wp=wp, sp=sp, M=M, K=K, N=N: w4.w4a16_gemm_plan(
-            Xs[(M, K, N)], wp, sp, None, Ys[(M, K, N)], M, N, K, group, args.variant, args.splits,
-            stream=stream.cuda_stream)) for (wp, sp) in packed[(K, N)]]
-        with torch.cuda.stream(stream):
-            for f in calls[:2]:
-                f()
-        torch.cuda.synchronize()
-        if args.no_graph:
-            g = None
-        else:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                for f in calls:
-                    f()
-            g.replay()
-            torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        reps = 3
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for _ in range(reps):
-                if g is not None:
-                    g.replay()
-                else:
-                    for f in calls:
-                        f()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
-        del g
-        wb, ab, fl = algorithmic(M, K, N)
-        plan = w4.w4a16_gemm_describe(M, N, K, group)
-        per_launch.append(dict(M=M, K=K, N=N, us=round(us, 3), weight_GBps=round(wb / us / 1e3, 1),
-                               TFLOPs=round(fl / us / 1e6, 2), hbm_frac=round(ab / us / 1e3 / HBM_PEAK_GBPS, 4),
-                               plan=plan["name"], splits=plan["splits"]))
-
-    n_launch = len(launches)
-    step_w = sum(algorithmic(M, K, N)[0] for (M, K, N, _) in launches)
-    step_alg = sum(algorithmic(M, K, N)[1] for (M, K, N, _) in launches)
-    step_fl = sum(algorithmic(M, K, N)[2] for (M, K, N, _) in launches)
-    value = step_w / t_step / 1e9
-    avg_launch_s = t_step / n_launch
-    achieved = step_alg / n_launch / avg_launch_s / 1e9
-    traffic = traffic_from_profiles()
-
-    # ---- fp16 baseline: hand-written dequant once, then the hand-written fp16 GEMM ----
-    baseline = None
-    if not args.no_baseline:
-        Wt = {}
-        for (K, N) in shapes:
-            d = host[(K, N)]
-            t0 = torch.empty((N, K), dtype=torch.float16, device="cuda")
-            w4.w4a16_dequant(torch.from_numpy(d["Qp"]).cuda(), torch.from_numpy(d["s"]).cuda(),
-                             None, t0, K, N, group)
-            Wt[(K, N)] = [t0] + [t0.clone() for _ in range(copies_per_step - 1)]
-        torch.cuda.synchronize()
-
-        def run_step_fp16(step_idx):
-            for i, M in enumerate(Ms):
-                for (K, N) in shapes:
-                    w4.w4a16_fp16_gemm(Xs[(M, K, N)], Wt[(K, N)][i], Ys[(M, K, N)], M, N, K)
-
-        t16, _ = time_steps(run_step_fp16, max(5, args.steps // 2), 2, not args.no_graph)
-
-        def run_step_torch(step_idx):
-            for i, M in enumerate(Ms):
-                for (K, N) in shapes:
-                    torch.nn.functional.linear(Xs[(M, K, N)], Wt[(K, N)][i])
-
-        ttorch, _ = time_steps(run_step_torch, max(5, args.steps // 2), 2, False)
-        baseline = dict(kind="w4a16_dequant + w4a16_fp16_gemm (hand-written, fp16 weights)",
-                        ms_per_step=round(t16 * 1e3, 4),
-                        fp16_weight_GBps=round(sum(2 * K * N for (_, K, N, _) in launches) / t16 / 1e9, 1),
-                        w4_speedup=round(t16 / t_step, 3),
-                        speedup_ceiling_bytes=round(16 / (4 + 16 / 128), 3),
-                        torch_matmul_ms_per_step=round(ttorch * 1e3, 4),
-                        w4_speedup_vs_torch_matmul=round(ttorch / t_step, 3))
-        del Wt
-
-    # ---- measured ceiling: a plain streaming read of each launch's packed codes -------
-    # (calibration kernel of the library, same launch list, weight rotation and HIP
-    # graphs): at 8-25 MiB per launch, launch and ramp keep any kernel far below the
-    # 8 TB/s spec, so the GEMM is also set against what a read-only kernel achieves
-    plain_read = None
-    if not args.no_baseline:
-        probe_out = torch.zeros(4, dtype=torch.int32, device="cuda")
-
-        def run_step_read(step_idx):
-            cyc = step_idx % steps_per_cycle
-            for i, M in enumerate(Ms):
-                for (K, N) in shapes:
-                    wp, _ = packed[(K, N)][cyc * copies_per_step + i]
-                    w4.w4a16_probe_read(wp, K * N // 2, probe_out)
-
-        tread, _ = time_steps(run_step_read, max(5, args.steps // 2), 2, not args.no_graph)
-        code_bytes = sum(K * N // 2 for (_, K, N, _) in launches)
-        plain_read = dict(kernel="w4a16_probe_read over each launch's packed codes (16-byte "
-                                 "non-temporal streaming read, nothing else)",
-                          GBps=round(code_bytes / tread / 1e9, 1),
-                          us_per_launch=round(tread / n_launch * 1e6, 3),
-                          frac_of_peak=round(code_bytes / tread / 1e9 / HBM_PEAK_GBPS, 4),
-                          gemm_time_over_read_time=round(t_step / tread, 3))
-
-    # ---- large-M sweep: 70B-class single-GPU shapes, where the matrix cores bound ------
-    large = None
-    if not args.no_large:
-        large = large_m_sweep(w4, torch, group)
-
-    # ---- 2:4 sparse vs dense on the same pruned weights; zero-point workload ---------
-    sparse24 = asym = tiny = None
-    if not args.no_configs:
-        sparse24, asym, tiny = config_legs(w4, torch, group)
-
-    group64 = bf16 = fp8 = mxfp4 = offline = None
-    if not args.no_configs:
-        group64 = group64_leg(w4, torch)
-        bf16 = bf16_leg(w4, torch)
-        fp8 = w4a8_leg(w4, torch)
-        mxfp4 = mxfp4_leg(w4, torch)
-        offline = offline_leg(w4, torch)
-
-    # ---- CPU oracle on this host over one step (bounded sample) -----------------------
+    base = None
+    if not args.no_baseline and not args.roofline_only:
+        b = fp16_baseline_leg(w4, torch, inp, stream, max(3, args.steps // 2))
+        base = dict(kind="w4a16_dequant (once) + w4a16_fp16_gemm, hand-written, fp16 weights",
+                    ms_per_step=round(b["t_step"] * 1e3, 3),
+                    TFLOPs=round(h["step_flops"] / b["t_step"] / 1e12, 1),
+                    w4_speedup=round(b["t_step"] / t_step, 3),
+                    per_m_TFLOPs=b["per_m_TFLOPs"],
+                    torch_matmul_ms_per_step=round(b["t_torch"] * 1e3, 3),
+                    w4_speedup_vs_torch_matmul=round(b["t_torch"] / t_step, 3))
     cpu = None
-    if not args.no_cpu:
-        import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:
-            threads = len(os.sched_getaffinity(0))
-        # repeat whole steps until at least 10 s of oracle work (bounded at 30 s)
-        t0 = time.perf_counter()
-        passes = 0
-        while True:
-            for (M, K, N, _) in launches:
-                d = host[(K, N)]
-                oracle.gemm(Xh[(M, K, N)], d["Qp"], d["s"], None, group)
-            passes += 1
-            tc = time.perf_counter() - t0
-            if tc >= 10.0 or tc * (passes + 1) / passes > 30.0:
-                break
-        cpu = dict(value=round(passes * step_w / tc / 1e9, 4), unit="GB/s", cores=threads,
-                   kind="oracle",
-                   sample=f"{passes} full step(s) of the decode sweep (24 GEMMs each): unpack + "
-                          "exact fp64 dequant + fp64 matmul, NumPy/OpenBLAS",
-                   seconds=round(tc, 3))
+    if not args.no_cpu and not args.roofline_only:
+        print("bench.py: CPU oracle leg", file=sys.stderr, flush=True)
+        cpu = cpu_oracle_leg(inp)
+    detail = dict(headline_table=h["table"])
+    del inp
+    torch.cuda.empty_cache()
 
-    line = {
-        "metric": "W4A16 GEMM TFLOP/s + weight HBM GB/s vs M (1..4096), % of roofline",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "value_is": "packed INT4 weights + fp16 scales of the 24 GEMMs / step time",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(t_step * 1e3, 5),
-        "ms_per_step_percentiles": STEP_STATS.get("run_step_w4"),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp16",
-        "data": "synthetic",
-        "config": {
-            "workload": "decode-shape sweep, 7B-class linear layers: (K,N) in "
-                        "{(4096,4096),(4096,12288),(4096,11008),(11008,4096)} x M in "
-                        "{1,2,4,8,16,32}, group 128 along K, symmetric INT4, fp16 X ~ N(0,1), "
-                        "scales U[0.002,0.02]; 24 GEMMs per step",
-            "launch": mode,
-            "weight_copies_rotated": R,
-            "parallelism": "single GPU",
-        },
-        "tflops": round(step_fl / t_step / 1e12, 3),
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "kernel": "w4a16 fused GEMM (skinny_kernel), mean over the 24 launches of a step",
-            "algorithmic_bytes_per_launch": int(step_alg / n_launch),
-            "avg_launch_us": round(avg_launch_s * 1e6, 3),
-            "measured_ceiling": plain_read,
-        },
-        "cpu_baseline": cpu,
-        "fp16_baseline": baseline,
-        "large_m_sweep": large,
-        "sparse24_vs_dense": sparse24,
-        "asym_zero_point": asym,
-        "tiny_config": tiny,
-        "group64": group64,
-        "bf16_activations": bf16,
-        "w4a8_fp8_activations": fp8,
-        "mxfp4_in_mfma_dequant": mxfp4,
-        "load_time_kernels": offline,
-        "per_launch_us": [[p["M"], p["K"], p["N"], p["us"]] for p in per_launch],
-        "decode_runs": [dict(M=p["M"], K=p["K"], N=p["N"], us=p["us"], weight_GBps=p["weight_GBps"],
-                             TFLOPs=p["TFLOPs"], bound="hbm", roofline_frac=p["hbm_frac"],
-                             plan=p["plan"]) for p in per_launch],
-    }
-    if args.detail:
-        with open(args.detail, "w") as f:
-            json.dump(dict(line=line, per_launch=per_launch, kernel_sha=kernel_sha()), f, indent=1)
+    decode = None
+    if not args.no_decode and not args.roofline_only:
+        print("bench.py: decode-sweep leg", file=sys.stderr, flush=True)
+        decode = decode_sweep_leg(w4, torch, 30, 5)
+
+    if args.all_legs:
+        print("bench.py: side legs", file=sys.stderr, flush=True)
+        sparse24, asym, tiny = config_legs(w4, torch, 128)
+        detail.update(sparse24_vs_dense=sparse24, asym_zero_point=asym, tiny_config=tiny,
+                      group64_and_256=group64_leg(w4, torch), bf16_activations=bf16_leg(w4, torch),
+                      w4a8_fp8_activations=w4a8_leg(w4, torch),
+                      mxfp4_in_mfma_dequant=mxfp4_leg(w4, torch),
+                      load_time_kernels=offline_leg(w4, torch))
+    detail_path = args.detail
+    if detail_path is None and args.all_legs:
+        os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+        detail_path = os.path.join(ROOT, "gpurun_out", "bench_detail.json")
+
+    line = build_line(h, args.steps, args.warmup, traffic, cpu, base, decode)
+    if detail_path:
+        with open(detail_path, "w") as f:
+            json.dump(dict(line=line, **detail, kernel_sha_tiled=kernel_sha("tiled"),
+                           kernel_sha_skinny=kernel_sha("skinny")), f, indent=1)
     print(json.dumps(line), flush=True)
+
+
+def inp_ms(h):
+    ms = []
+    for row in h["table"]:
+        if row["M"] not in ms:
+            ms.append(row["M"])
+    return ms
 
 
 if __name__ == "__main__":

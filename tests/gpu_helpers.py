@@ -44,3 +44,14 @@ def variant_index(name: str) -> int:
         if w4.w4a16_gemm_variant_name(v) == name:
             return v
     raise KeyError(name)
+
+
+def tile_samples(M: int, N: int):
+    """One row in every 16-row tile and one column in every 16-column tile (at a
+    position that moves through the tile from one tile to the next), plus the last row
+    and column: comparing Y on this cross product against the oracle reaches every
+    output tile of every kernel (16 x 16 matrix tiles and everything built from them),
+    every wave's columns and every stream-K piece."""
+    rows = sorted({min(M - 1, 16 * i + (7 * i) % 16) for i in range((M + 15) // 16)} | {M - 1})
+    cols = sorted({16 * j + (5 * j) % 16 for j in range(N // 16)} | {N - 1})
+    return rows, cols

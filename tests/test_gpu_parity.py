@@ -207,11 +207,12 @@ def _sample_idx(rng, n, k):
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_configs_full_size(gh, cfg):
     """Every run of configs 1-4 at full size, automatic plan (the one bench.py times).
-    Small outputs are checked whole; large ones on sampled rows x columns.  Config 4
-    runs the dense kernel on the 2:4-pruned weights."""
+    Y starts NaN-filled and must come back finite everywhere; small outputs are checked
+    whole, large ones on one row per 16-row tile x one column per 16-column tile, which
+    reaches every output tile and stream-K piece.  Config 4 runs the dense kernel on the
+    2:4-pruned weights."""
     runs = config_runs(cfg)
     cache = {}
-    rng = np.random.default_rng(cfg)
     for w in runs:
         key = (w.K, w.N)
         if key not in cache:
@@ -220,13 +221,14 @@ def test_configs_full_size(gh, cfg):
             cache[key] = (d, gh.repack(d, w.K, w.N))
         d, packed = cache[key]
         X = activations(w)
-        Y = gh.host(gh.gemm(gh.dev(X), packed, w.M, w.N, w.K))
+        Yd = gh.nan_filled(w.M, w.N)
+        gh.gemm(gh.dev(X), packed, w.M, w.N, w.K, Y=Yd)
+        Y = gh.host(Yd)
         assert np.all(np.isfinite(Y)), w.name
         if w.M * w.N * w.K <= 4096 * 4096 * 32:
             ok, info = _accept(Y, X, d)
         else:
-            rows = _sample_idx(rng, w.M, 24)
-            cols = _sample_idx(rng, w.N, 48)
+            rows, cols = gh.tile_samples(w.M, w.N)
             ok, info = _accept(Y, X, d, rows=rows, cols=cols)
         assert ok, (w.name, info)
 
@@ -576,10 +578,10 @@ def test_group64_onehot_exact(gh, asym):
                                         (32, 11008, 4096, False), (1024, 8192, 10240, True)])
 def test_group64_full_size(gh, M, K, N, asym):
     _, d, X = _case64(M, K, N, asym)
-    Y = gh.host(gh.gemm(gh.dev(X), gh.repack(d, K, N, 64), M, N, K, group=64))
-    rng = np.random.default_rng(M + K)
-    rows = _sample_idx(rng, M, 24)
-    cols = _sample_idx(rng, N, 48)
+    Y = gh.host(gh.gemm(gh.dev(X), gh.repack(d, K, N, 64), M, N, K, group=64,
+                        Y=gh.nan_filled(M, N)))
+    assert np.all(np.isfinite(Y))
+    rows, cols = gh.tile_samples(M, N)
     Yref, B = oracle.gemm_sampled(X, d["Qp"], d["s"], d["Zp"], 64, rows, cols)
     ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, B)
     assert ok, info
@@ -610,7 +612,7 @@ def _gemm_bf16(gh, Xbits, packed, M, N, K, variant=-1, splits=0, group=128):
     import torch
     import w4a16_mixed_precision_offline_amd as w4
     wp, sp, zp = packed
-    Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+    Y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")  # 0xFFFF: a bf16 NaN
     w4.w4a16_gemm_bf16_plan(gh.dev(Xbits.view(np.int16)), wp, sp, zp, Y, M, N, K, group, variant,
                             splits)
     return gh.host(Y).view(np.uint16)
@@ -662,10 +664,9 @@ def test_bf16_onehot_exact(gh, asym):
                                         (32, 11008, 4096, False)])
 def test_bf16_full_size(gh, M, K, N, asym):
     _, d, bits, vals = _case_bf16(M, K, N, asym)
-    Y = _bf16_f32(_gemm_bf16(gh, bits, gh.repack(d, K, N), M, N, K))
-    rng = np.random.default_rng(M + N)
-    rows = _sample_idx(rng, M, 24)
-    cols = _sample_idx(rng, N, 48)
+    Y = _bf16_f32(_gemm_bf16(gh, bits, gh.repack(d, K, N), M, N, K))  # NaN-filled before
+    assert np.all(np.isfinite(Y))
+    rows, cols = gh.tile_samples(M, N)
     Yref, B = oracle.gemm_sampled(vals, d["Qp"], d["s"], d["Zp"], 128, rows, cols)
     ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, B, rel_fro=BF16_FRO)
     assert ok, info
@@ -749,3 +750,136 @@ def test_caller_owned_workspace(gh):
     torch.cuda.synchronize()
     for o, r in zip(outs, ref):
         assert np.array_equal(gh.host(o).view(np.uint16), r)
+
+
+# ---- groups of more than 128 rows: 256, and one group spanning all of K ----------------
+# The repacked layout stores one scale (and zero-point) row per 128-row block, a group of
+# 256 or more rows once per block it spans, so every kernel and entry point sees the same
+# format as for groups of 128; the repack's replication, the unpack's choice of copy and
+# the oracle's group indexing are what these tests pin.
+def _case_big(M, K, N, group, asym=False, seed=0):
+    w = Workload(cfg=9, M=M, K=K, N=N, group=group, asym=asym)
+    d = weights(w, seed=9000 + seed + K + N + group)
+    X = activations(w, seed=9500 + seed + M)
+    return w, d, X
+
+
+BIG_GROUPS = [256, "K"]
+
+
+def _g(group, K):
+    return K if group == "K" else group
+
+
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("group", BIG_GROUPS)
+def test_big_group_repack_layout_and_roundtrip(gh, group, asym):
+    import torch
+    import layout_model as lm
+    import w4a16_mixed_precision_offline_amd as w4
+    K, N = 1536, 528
+    g = _g(group, K)
+    _, d, _ = _case_big(1, K, N, g, asym)
+    wp, sp, zp = gh.repack(d, K, N, g)
+    assert np.array_equal(gh.host(wp).view(np.uint32), lm.repack_codes(d["Qp"], K, N))
+    assert np.array_equal(gh.host(sp).view(np.uint16),
+                          lm.repack_scales(d["s"], N, g // 128).view(np.uint16))
+    if asym:
+        assert np.array_equal(gh.host(zp).view(np.uint32), lm.repack_zeros(d["Zp"], N, g // 128))
+    q = torch.zeros((K // 8, N), dtype=torch.int32, device="cuda")
+    s = torch.zeros((K // g, N), dtype=torch.float16, device="cuda")
+    z = torch.zeros((K // g, N // 8), dtype=torch.int32, device="cuda") if asym else None
+    w4.w4a16_unpack(wp, sp, zp, q, s, z, K, N, g)
+    assert np.array_equal(gh.host(q), d["Qp"])
+    assert np.array_equal(gh.host(s).view(np.uint16), d["s"].view(np.uint16))
+    if asym:
+        assert np.array_equal(gh.host(z), d["Zp"])
+
+
+@pytest.mark.parametrize("group", BIG_GROUPS)
+@pytest.mark.parametrize("M,K,N,asym", [(5, 1536, 528, True), (33, 1024, 512, False),
+                                        (300, 2048, 1040, True), (1, 512, 48, False)])
+def test_big_group_every_variant(gh, group, M, K, N, asym):
+    import w4a16_mixed_precision_offline_amd as w4
+    g = _g(group, K)
+    _, d, X = _case_big(M, K, N, g, asym)
+    packed = gh.repack(d, K, N, g)
+    Xd = gh.dev(X)
+    Yref = oracle.gemm(X, d["Qp"], d["s"], d["Zp"], g)
+    B = oracle.error_bound(X, d["Qp"], d["s"], d["Zp"], g)
+    ran = 0
+    for v in [-1] + list(range(w4.w4a16_gemm_variants())):
+        name = w4.w4a16_gemm_variant_name(v) if v >= 0 else "auto"
+        nt = 1 if not name.startswith("skinny") else int(name.split("_nt")[1].split("_")[0])
+        if N % (16 * nt):
+            continue
+        for splits in ((0,) if v < 0 else (1, 3)):
+            Y = gh.nan_filled(M, N)
+            gh.gemm(Xd, packed, M, N, K, group=g, variant=v, splits=splits, Y=Y)
+            ok, info = oracle.accept(gh.host(Y), Yref, B)
+            assert ok, (group, name, splits, info)
+            ran += 1
+    assert ran > 1
+
+
+@pytest.mark.parametrize("asym", [False, True])
+@pytest.mark.parametrize("group", BIG_GROUPS)
+def test_big_group_onehot_exact(gh, group, asym):
+    """One-hot rows on both sides of every 128-row block boundary select RNE((q - z) * s)
+    of their group, through the skinny paths (fp32 rescale and fp16-scaled weights) and
+    the tiled kernel."""
+    M, K, N = 16, 1024, 768
+    g = _g(group, K)
+    _, d, _ = _case_big(M, K, N, g, asym)
+    ks = [0, 1, 127, 128, 129, 255, 256, 257, 383, 384, 511, 512, 640, 767, 768, 1023]
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1.0
+    W16 = oracle.dequant_fp16(d["Qp"], d["s"], d["Zp"], K, N, g)
+    packed = gh.repack(d, K, N, g)
+    names = ["skinny_xr16_nt2_wk8_d2", "skinny_xr16_nt4_wk4_d2", "tiled_bm128_bn256_s3",
+             "tiled_bm16_bn256_s4"]
+    for nm in names:
+        for splits in (1, 3):
+            Y = gh.host(gh.gemm(gh.dev(X), packed, M, N, K, group=g,
+                                variant=gh.variant_index(nm), splits=splits))
+            assert np.array_equal(Y.view(np.uint16), W16[ks].view(np.uint16)), (nm, splits)
+
+
+@pytest.mark.parametrize("group", BIG_GROUPS)
+@pytest.mark.parametrize("M,K,N,asym", [(16, 4096, 11008, True), (1024, 8192, 10240, False)])
+def test_big_group_full_size(gh, group, M, K, N, asym):
+    g = _g(group, K)
+    _, d, X = _case_big(M, K, N, g, asym)
+    Y = gh.host(gh.gemm(gh.dev(X), gh.repack(d, K, N, g), M, N, K, group=g,
+                        Y=gh.nan_filled(M, N)))
+    assert np.all(np.isfinite(Y))
+    rows, cols = gh.tile_samples(M, N)
+    Yref, B = oracle.gemm_sampled(X, d["Qp"], d["s"], d["Zp"], g, rows, cols)
+    ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, B)
+    assert ok, info
+
+
+@pytest.mark.parametrize("group", BIG_GROUPS)
+@pytest.mark.parametrize("M,K,N,asym", [(5, 1536, 528, True), (300, 2048, 1040, False)])
+def test_big_group_bf16_and_fp8_activations(gh, group, M, K, N, asym):
+    """The bf16 and the fp8 (W4A8) entry points on the same repacked weights with a group
+    of 256 rows or one group spanning K, automatic plans, against the oracle."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    from gen import activations_bf16, activations_fp8
+    g = _g(group, K)
+    w, d, _ = _case_big(M, K, N, g, asym)
+    wp, sp, zp = gh.repack(d, K, N, g)
+    bits, vals = activations_bf16(w, seed=9600 + M)
+    Yb = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+    w4.w4a16_gemm_bf16(gh.dev(bits.view(np.int16)), wp, sp, zp, Yb, M, N, K, g)
+    ok, info = oracle.accept(_bf16_f32(gh.host(Yb).view(np.uint16)),
+                             oracle.gemm(vals, d["Qp"], d["s"], d["Zp"], g),
+                             oracle.error_bound(vals, d["Qp"], d["s"], d["Zp"], g), rel_fro=BF16_FRO)
+    assert ok, ("bf16", info)
+    X8, a = activations_fp8(w, seed=9700 + M)
+    Y8 = gh.nan_filled(M, N)
+    w4.w4a8_gemm(gh.dev(X8), gh.dev(a), wp, sp, zp, Y8, M, N, K, g)
+    ok, info = oracle.accept(gh.host(Y8), oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], g),
+                             oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], d["Zp"], g))
+    assert ok, ("fp8", info)

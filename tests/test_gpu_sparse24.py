@@ -129,7 +129,6 @@ def test_parity_every_variant_and_split(gh, M, K, N):
 def test_config4_sparse_and_dense_on_same_weights(gh):
     """Every run of the 2:4 configuration at full size, sparse kernel and dense kernel
     on the same pruned weights; both against the oracle (sampled for large outputs)."""
-    rng = np.random.default_rng(4)
     cache = {}
     for w in config_runs(4):
         if (w.K, w.N) not in cache:
@@ -139,12 +138,14 @@ def test_config4_sparse_and_dense_on_same_weights(gh):
         d, comp, dense = cache[(w.K, w.N)]
         X = activations(w)
         Xd = gh.dev(X)
-        Ys = gh.host(_sgemm(gh, Xd, comp, w.M, w.N, w.K))
-        Yd = gh.host(gh.gemm(Xd, dense, w.M, w.N, w.K))
-        rows = sorted(set([0, w.M - 1]) | set(rng.choice(w.M, size=min(w.M, 16), replace=False).tolist()))
-        cols = sorted(set([0, w.N - 1]) | set(rng.choice(w.N, size=64, replace=False).tolist()))
+        Ys = gh.host(_sgemm(gh, Xd, comp, w.M, w.N, w.K, Y=gh.nan_filled(w.M, w.N)))
+        Yd = gh.host(gh.gemm(Xd, dense, w.M, w.N, w.K, Y=gh.nan_filled(w.M, w.N)))
+        # every output written (NaN-filled before), then one row per 16-row tile x one
+        # column per 16-column tile against the oracle: every output tile is reached
+        rows, cols = gh.tile_samples(w.M, w.N)
         Yref, Bd = oracle.gemm_sampled(X, d["Qp"], d["s"], None, 128, rows, cols)
         for Y in (Ys, Yd):
+            assert np.all(np.isfinite(Y)), w.name
             ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, Bd)
             assert ok, (w.name, info)
 
@@ -215,3 +216,37 @@ def test_sparse_refuses_tiles_without_four_column_tiles_per_wave(gh):
     B = oracle.error_bound(X, d["Qp"], d["s"], None, 128)
     ok, info = oracle.accept(Y, Yref, B)
     assert ok, info
+
+
+@pytest.mark.parametrize("group", [256, 1024])
+def test_sparse_groups_larger_than_128(gh, group):
+    """2:4 weights with a group of 256 rows and with one group spanning K (= 1024):
+    compress round-trip bit-exact, and the sparse GEMM (automatic plan, and the skinny and
+    tiled variants with a K split / stripes) against the oracle on the pruned codes."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    K, N = 1024, 512
+    w = Workload(cfg=9, M=1, K=K, N=N, sparse24=True, group=group)
+    d = weights(w, seed=3500 + group)
+    assert oracle.check_24(d["Qp"], K, group=group)
+    vp, idx, sp = w4.alloc_sparse24(K, N, group)
+    w4.w4a16_sparse24_repack(gh.dev(d["Qp"]), gh.dev(d["s"]), vp, idx, sp, K, N, group)
+    q = torch.zeros((K // 8, N), dtype=torch.int32, device="cuda")
+    s = torch.zeros((K // group, N), dtype=torch.float16, device="cuda")
+    w4.w4a16_sparse24_unpack(vp, idx, sp, q, s, K, N, group)
+    assert np.array_equal(gh.host(q), d["Qp"])
+    assert np.array_equal(gh.host(s).view(np.uint16), d["s"].view(np.uint16))
+    for M in (5, 300):
+        X = activations(Workload(cfg=9, M=M, K=K, N=N), seed=3600 + M)
+        Xd = gh.dev(X)
+        Yref = oracle.gemm(X, d["Qp"], d["s"], None, group)
+        B = oracle.error_bound(X, d["Qp"], d["s"], None, group)
+        for v, sp_ in [(-1, 0), (gh.variant_index("skinny_xr16_nt4_wk4_d2"), 3),
+                       (gh.variant_index("tiled_bm128_bn256_s3"), 7)]:
+            Y = gh.nan_filled(M, N)
+            if v < 0:
+                w4.w4a16_sparse24_gemm(Xd, vp, idx, sp, Y, M, N, K, group)
+            else:
+                w4.w4a16_sparse24_gemm_plan(Xd, vp, idx, sp, Y, M, N, K, group, v, sp_)
+            ok, info = oracle.accept(gh.host(Y), Yref, B)
+            assert ok, (group, M, v, info)
