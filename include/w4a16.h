@@ -121,6 +121,25 @@ int w4a16_unpack(const void* wp, const uint16_t* sp, const void* zp,
 int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                uint16_t* Y, int M, int N, int K, int group, void* stream);
 
+/* ---- the same GEMM without any allocation, for callers that cannot allocate: code
+ *      under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc ----
+ * w4a16_gemm_noalloc: w4a16_gemm with the same arguments, rules, automatic plans, kernels
+ *   and results (bit for bit), except where the split-K / stream-K workspace lives: a
+ *   fixed scratch array of W4A16_NOALLOC_SCRATCH_BYTES in the library's device memory
+ *   (one per device, held until the process ends; the first W4A16_WS_COUNTER_BYTES are
+ *   arrival counters, the rest fp32 partials) instead of a per-stream buffer.  The call
+ *   never allocates or frees memory and issues no memset.  Its first call on a device
+ *   looks the array up and clears the counters with a small kernel on `stream`; the
+ *   kernels leave them at zero again.  Every call on one device shares the array and
+ *   finds it as the last call left it: calls that overlap in time on one device (on
+ *   different streams, or concurrent replays of graphs holding such calls) race and give
+ *   wrong results.  A plan needing more workspace than the array holds returns
+ *   W4A16_ERR_WORKSPACE and enqueues nothing (no automatic plan of a valid shape needs
+ *   more: the largest takes two 128 x 256 fp32 pieces for each of 256 workgroups). */
+#define W4A16_NOALLOC_SCRATCH_BYTES (65536 + (64u << 20))
+int w4a16_gemm_noalloc(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+                       uint16_t* Y, int M, int N, int K, int group, void* stream);
+
 /* Same as w4a16_gemm with an explicit kernel plan (tuning and tests):
  *   variant : -1 = automatic, else an index < w4a16_gemm_variants();
  *   splits  : 0 = automatic.  For a "skinny_*" variant (one workgroup per

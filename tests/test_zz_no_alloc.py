@@ -1,0 +1,68 @@
+"""w4a16_gemm_noalloc, the entry point for callers that cannot allocate: the same GEMM
+as w4a16_gemm with its workspace in the library's fixed device scratch array.  Its
+results must equal w4a16_gemm's bit for bit (same plans, same kernels), on calls in a
+row of decreasing size that use the scratch array (stream-K pieces of the tiled kernel,
+split-K partials and arrival counters of the skinny kernel), and both must pass the
+oracle's acceptance rule."""
+import numpy as np
+import pytest
+
+import oracle
+from gen import Workload, activations, weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gh(lib):
+    import gpu_helpers
+    return gpu_helpers
+
+
+def _run(gh, w4, M, K, N, asym, seed):
+    w = Workload(cfg=9, M=M, K=K, N=N, asym=asym)
+    d = weights(w, seed=11000 + seed)
+    X = activations(w, seed=11500 + seed)
+    packed = gh.repack(d, K, N)
+    Xd = gh.dev(X)
+    wp, sp, zp = packed
+    Y_ref = gh.nan_filled(M, N)
+    w4.w4a16_gemm(Xd, wp, sp, zp, Y_ref, M, N, K, 128)
+    Y_na = gh.nan_filled(M, N)
+    w4.w4a16_gemm_noalloc(Xd, wp, sp, zp, Y_na, M, N, K, 128)
+    a = gh.host(Y_ref).view(np.uint16)
+    b = gh.host(Y_na).view(np.uint16)
+    assert np.array_equal(a, b), (M, K, N)
+    rows, cols = gh.tile_samples(M, N)
+    Yref, B = oracle.gemm_sampled(X, d["Qp"], d["s"], d["Zp"], 128, rows, cols)
+    ok, info = oracle.accept(b.view(np.float16)[np.ix_(rows, cols)], Yref, B)
+    assert ok, info
+
+
+def test_noalloc_matches_gemm_on_calls_of_decreasing_size(gh):
+    import w4a16_mixed_precision_offline_amd as w4
+    # 1) tiled kernel, 320 tiles on 256 workgroups: stream-K pieces in the scratch array
+    # 2) a smaller tiled launch: fewer pieces, the first call's partials still there
+    # 3) skinny kernel with a K split (48 column tiles): partials and arrival counters
+    # 4) the same again: the counters must have come back to zero
+    cases = [(1024, 8192, 10240, False), (300, 2048, 1040, True), (1, 3072, 768, True),
+             (1, 3072, 768, True)]
+    for i, (M, K, N, asym) in enumerate(cases):
+        assert w4.w4a16_gemm_describe(M, N, K, 128)["name"].startswith("tiled" if i < 2 else "skinny")
+        _run(gh, w4, M, K, N, asym, i)
+    assert w4.w4a16_gemm_describe(1, 768, 3072, 128)["splits"] > 1
+
+
+def test_noalloc_rejects_plans_larger_than_its_array(gh):
+    """Validation is shared with w4a16_gemm: bad shapes and alignment are refused on the
+    host; no automatic plan of a valid shape needs more than the array."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    X = torch.zeros((4, 1024), dtype=torch.float16, device="cuda")
+    Y = torch.zeros((4, 1024), dtype=torch.float16, device="cuda")
+    wp, sp, _ = w4.alloc_packed(1024, 1024, 128, False)
+    with pytest.raises(w4.W4A16Error) as e:
+        w4.w4a16_gemm_noalloc(X, wp, sp, None, Y, 4, 1000, 1024, 128)
+    assert e.value.code == -2
+    for (M, K, N) in [(4096, 8192, 28672), (256, 28672, 8192), (1, 768, 3072)]:
+        assert w4.w4a16_workspace_bytes(M, N, K) <= w4.NOALLOC_SCRATCH_BYTES

@@ -38,6 +38,7 @@ _SIGS = {
     "w4a16_repack": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "w4a16_unpack": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
     "w4a16_gemm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "w4a16_gemm_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "w4a16_gemm_plan": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "w4a16_gemm_variants": (_I, []),
     "w4a16_gemm_variant_name": (ctypes.c_char_p, [_I]),
@@ -161,6 +162,14 @@ def w4a16_unpack(wp, sp, zp, q, s, z, K, N, group, stream=None):
 def w4a16_gemm(X, wp, sp, zp, Y, M, N, K, group, stream=None):
     _check("w4a16_gemm", _lib.w4a16_gemm(_ptr(X), _ptr(wp), _ptr(sp), _ptr(zp), _ptr(Y),
                                          M, N, K, group, _stream(stream)))
+
+
+def w4a16_gemm_noalloc(X, wp, sp, zp, Y, M, N, K, group, stream=None):
+    _check("w4a16_gemm_noalloc", _lib.w4a16_gemm_noalloc(_ptr(X), _ptr(wp), _ptr(sp), _ptr(zp),
+                                                         _ptr(Y), M, N, K, group, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 65536 + (64 << 20)  # W4A16_NOALLOC_SCRATCH_BYTES
 
 
 def w4a16_gemm_plan(X, wp, sp, zp, Y, M, N, K, group, variant=-1, splits=0, stream=None):

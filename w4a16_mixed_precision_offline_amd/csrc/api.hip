@@ -120,6 +120,70 @@ int get_workspace(int dev, hipStream_t st, size_t counters, size_t floats, int**
   return W4A16_OK;
 }
 
+// ---- fixed device scratch for w4a16_gemm_noalloc ----------------------------------------
+// [counters (W4A16_WS_COUNTER_BYTES, zero at rest) | fp32 partials].  64 MiB of partials
+// hold the largest automatic plan: two 128 x 256 fp32 stream-K pieces per persistent
+// workgroup, 256 workgroups.  In host code `scratch` only stands in for the symbol; the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchPartBytes = (size_t)64 << 20;
+constexpr size_t kScratchBytes = (size_t)W4A16_WS_COUNTER_BYTES + kScratchPartBytes;
+static_assert(kScratchBytes == W4A16_NOALLOC_SCRATCH_BYTES, "header and library disagree");
+std::map<int, char*> g_scratch;  // device -> device address of its copy of `scratch`
+
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+// The device address of this device's scratch array; on the first call for a device it
+// is looked up and its counter region cleared by a small kernel on `st` (no memset node,
+// so the clearing may also be captured into a graph and replayed).
+int scratch_for_device(int dev, hipStream_t st, char** out) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_scratch.find(dev);
+  if (it != g_scratch.end()) {
+    *out = it->second;
+    return W4A16_OK;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return W4A16_ERR_DEVICE;
+  }
+  const int words = W4A16_WS_COUNTER_BYTES / 4;
+  hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st,
+                     static_cast<uint32_t*>(ptr), words);
+  if (hipGetLastError() != hipSuccess) return W4A16_ERR_LAUNCH;
+  g_scratch.emplace(dev, static_cast<char*>(ptr));
+  *out = static_cast<char*>(ptr);
+  return W4A16_OK;
+}
+
+// Workspace of one launch: the per-stream buffer, or (noalloc) the fixed scratch array,
+// refused with W4A16_ERR_WORKSPACE when the plan needs more than it holds.
+int launch_workspace(int dev, hipStream_t st, size_t counters, size_t floats, bool noalloc,
+                     int** cnt, float** part) {
+  if (!noalloc) return get_workspace(dev, st, counters, floats, cnt, part);
+  *cnt = nullptr;
+  *part = nullptr;
+  if (counters == 0 && floats == 0) return W4A16_OK;
+  if (counters * sizeof(int) > (size_t)W4A16_WS_COUNTER_BYTES ||
+      floats * sizeof(float) > kScratchPartBytes)
+    return W4A16_ERR_WORKSPACE;
+  char* base = nullptr;
+  int rc = scratch_for_device(dev, st, &base);
+  if (rc) return rc;
+  *cnt = reinterpret_cast<int*>(base);
+  *part = reinterpret_cast<float*>(base + W4A16_WS_COUNTER_BYTES);
+  return W4A16_OK;
+}
+
 // Weight format of a dense launch: zero-points or not, groups of 64 rows or not.
 inline int dense_mode(bool asym, int group) {
   return group == 64 ? (asym ? W_ASYM64 : W_SYM64) : (asym ? W_ASYM : W_SYM);
@@ -135,7 +199,7 @@ inline int launched(hipError_t e) {
 
 int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
                uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
-               void* stream, const float* xscale = nullptr) {
+               void* stream, const float* xscale = nullptr, bool noalloc = false) {
   SkinnyPlan plan;
   int rc = skinny_make_plan(M, N, K, group, mode, variant, splits, &plan);
   if (rc) return rc;
@@ -144,7 +208,8 @@ int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, c
   hipStream_t st = static_cast<hipStream_t>(stream);
   int* cnt;
   float* part;
-  if ((rc = get_workspace(dev, st, plan.counters, plan.part_floats, &cnt, &part))) return rc;
+  if ((rc = launch_workspace(dev, st, plan.counters, plan.part_floats, noalloc, &cnt, &part)))
+    return rc;
   return launched(skinny_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, cnt,
                                 M, N, K, group, st, xscale));
 }
@@ -173,7 +238,7 @@ bool mx_uses_decode(int M, int N) {
 
 int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
               uint16_t* Y, int M, int N, int K, int variant, int grid, void* stream,
-              const float* xscale = nullptr) {
+              const float* xscale = nullptr, bool noalloc = false) {
   TiledPlan plan;
   int rc = tiled_make_plan(M, N, K, mode, variant, grid, &plan);
   if (rc) return rc;
@@ -182,7 +247,7 @@ int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   int* cnt;
   float* part;
-  if ((rc = get_workspace(dev, st, 0, plan.part_floats, &cnt, &part))) return rc;
+  if ((rc = launch_workspace(dev, st, 0, plan.part_floats, noalloc, &cnt, &part))) return rc;
   return launched(
       tiled_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, st, xscale));
 }
@@ -191,17 +256,19 @@ int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
 // For a tiled variant the `splits` argument is the number of persistent workgroups.
 int run_fused(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
               uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
-              void* stream) {
+              void* stream, bool noalloc = false) {
   const int ns = skinny_variant_count();
   if (variant >= ns)
-    return run_tiled(mode, X, w, sp, zp, Y, M, N, K, variant - ns, splits, stream);
+    return run_tiled(mode, X, w, sp, zp, Y, M, N, K, variant - ns, splits, stream, nullptr,
+                     noalloc);
   if (variant < 0 && splits == 0 && use_tiled(M, N, K)) {
     // shapes whose tiles would need buffer offsets past 2 GiB stay on the skinny kernel
     TiledPlan t;
     if (tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0)
-      return run_tiled(mode, X, w, sp, zp, Y, M, N, K, -1, 0, stream);
+      return run_tiled(mode, X, w, sp, zp, Y, M, N, K, -1, 0, stream, nullptr, noalloc);
   }
-  return run_skinny(mode, X, w, sp, zp, Y, M, N, K, group, variant, splits, stream);
+  return run_skinny(mode, X, w, sp, zp, Y, M, N, K, group, variant, splits, stream, nullptr,
+                    noalloc);
 }
 
 int check_gemm_args(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
@@ -289,6 +356,14 @@ int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void
   if (rc) return rc;
   return run_fused(dense_mode(zp != nullptr, group), X, wp, sp, zp, Y, M, N, K, group, -1, 0,
                    stream);
+}
+
+int w4a16_gemm_noalloc(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
+                       uint16_t* Y, int M, int N, int K, int group, void* stream) {
+  int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
+  if (rc) return rc;
+  return run_fused(dense_mode(zp != nullptr, group), X, wp, sp, zp, Y, M, N, K, group, -1, 0,
+                   stream, true);
 }
 
 int w4a16_gemm_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
