@@ -325,3 +325,13 @@ def test_shapes_past_32_bit_descriptors_are_rejected_on_the_host(raw):
     fp = raw.w4a16_fp16_gemm
     fp.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
     assert fp(p, p, p, 1, 16, 1 << 26, None) == -2
+
+
+def test_binding_refuses_a_probe_read_past_a_tensor():
+    """The streaming-read probe cannot see its buffer's size; the binding refuses, on the
+    host, a byte count larger than the tensor it is given (nothing reaches the library)."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    buf = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        w4.w4a16_probe_read(buf, 32, buf)

@@ -283,6 +283,10 @@ def alloc_mx(K: int, N: int, device="cuda"):
 
 # ---- calibration kernels ---------------------------------------------------------
 def w4a16_probe_read(p, nbytes, out, stream=None):
+    # the C entry point cannot see the buffer's size: refuse a read past a tensor's end
+    if hasattr(p, "numel") and nbytes > p.numel() * p.element_size():
+        raise ValueError(f"w4a16_probe_read: {nbytes} bytes past a {p.numel() * p.element_size()}"
+                         "-byte tensor")
     _check("w4a16_probe_read", _lib.w4a16_probe_read(_ptr(p), nbytes, _ptr(out), _stream(stream)))
 
 
