@@ -92,12 +92,12 @@ def test_describe_plans(raw):
     for (N, K, name) in [(5120, 13824, b"skinny_xr16_nt2_wk8_d2"), (8192, 28672, b"skinny_xr16_nt2_wk8_d2")]:
         assert raw.w4a16_gemm_describe(16, N, K, 128, out) == 0
         assert raw.w4a16_gemm_variant_name(out[0]) == name
-    # above 32 rows: the tiled kernel, except on small layers with many columns; a layer
-    # with under a thousand (tile, k-block) units gets 16-row tiles
-    for (M, N, K, name) in [(48, 13824, 5120, b"tiled_bm64_bn256_s3"), (48, 768, 3072, b"tiled_bm16_bn256_s4"),
-                            (128, 768, 3072, b"tiled_bm16_bn256_s4"),
-                            (128, 8192, 8192, b"tiled_bm128_bn128_s3"), (128, 8192, 28672, b"tiled_bm128_bn256_s3"), (48, 2560, 2560, b"skinny_xr64_nt1_wk4_d2"),
-                            (128, 4096, 4096, b"skinny_xr64_nt1_wk4_d2"), (32, 28672, 8192, b"skinny_xr32_nt4_wk4_d2")]:
+    # above 32 rows: the tiled kernel, except on layers under 32 Mi weights below 256 rows,
+    # which take the skinny kernel in blocks of 16 or 32 rows
+    for (M, N, K, name) in [(48, 13824, 5120, b"tiled_bm64_bn256_s3"), (48, 768, 3072, b"skinny_xr16_nt1_wk8_d2"),
+                            (128, 768, 3072, b"skinny_xr32_nt1_wk4_d2"),
+                            (128, 8192, 8192, b"tiled_bm128_bn128_s3"), (128, 8192, 28672, b"tiled_bm128_bn256_s3"), (48, 2560, 2560, b"skinny_xr16_nt2_wk8_d2"),
+                            (128, 4096, 4096, b"skinny_xr32_nt4_wk4_d2"), (32, 28672, 8192, b"skinny_xr32_nt4_wk4_d2")]:
         assert raw.w4a16_gemm_describe(M, N, K, 128, out) == 0
         assert raw.w4a16_gemm_variant_name(out[0]) == name, (M, N, K)
     assert raw.w4a16_gemm_describe(0, 4096, 4096, 128, out) == -2
@@ -307,20 +307,23 @@ def test_sparse_validation(raw):
 
 
 def test_shapes_past_32_bit_descriptors_are_rejected_on_the_host(raw):
-    """M = 64, K = 2^25, N = 16 passes the weight-shape rules (K*N/8 = 2^26 words), but 64
-    rows of X span 2^32 bytes: neither kernel's 32-bit buffer descriptors can address
-    them, so the plan query and the GEMM itself must return W4A16_ERR_SHAPE (before any
-    device call; the pointers below are never dereferenced)."""
+    """K = 2^25, N = 16 passes the weight-shape rules (K*N/8 = 2^26 words).  At M = 128 the
+    tiled kernel's 128-row tiles and the skinny kernel's 32-row blocks of X span 2^33 and
+    2^31 bytes: neither kernel's 32-bit buffer descriptors can address them, so the plan
+    query and the GEMM itself must return W4A16_ERR_SHAPE (before any device call; the
+    pointers below are never dereferenced).  At M = 64 (16-row blocks: 2^30 bytes) the
+    skinny kernel serves the shape."""
     out = (ctypes.c_int * 4)()
     K, N = 1 << 25, 16
-    assert raw.w4a16_gemm_describe(64, N, K, 128, out) == -2
+    assert raw.w4a16_gemm_describe(128, N, K, 128, out) == -2
+    assert raw.w4a16_gemm_describe(64, N, K, 128, out) == 0
     assert raw.w4a16_gemm_describe(1, N, K, 128, out) == 0     # 4 rows: 2^28 bytes, fine
     p = ctypes.c_void_p(1 << 20)  # 16-byte aligned, never touched
     fn = raw.w4a16_gemm
     fn.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_void_p]
-    assert fn(p, p, p, None, p, 64, N, K, 128, None) == -2
+    assert fn(p, p, p, None, p, 128, N, K, 128, None) == -2
     # groups of 64 rows run the skinny kernel at every M: the same guard applies
-    assert raw.w4a16_gemm_describe(64, N, K, 64, out) == -2
+    assert raw.w4a16_gemm_describe(128, N, K, 64, out) == -2
     # the fp16 baseline: one workgroup's weight rows (16 columns x K fp16) past 2 GiB
     fp = raw.w4a16_fp16_gemm
     fp.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p]

@@ -29,25 +29,37 @@ def plan(M, N, K, group=128):
     (1024, 8192, 10240, "tiled_bm128_bn256_s3"),
     # layers up to 128 Mi weights at 65-256 rows: 128 x 128 tiles
     (128, 5120, 13824, "tiled_bm128_bn128_s3"), (256, 8192, 10240, "tiled_bm128_bn128_s3"),
-    # small wide layers stay on the skinny kernel at 33-255 rows
-    (48, 2560, 2560, "skinny_xr64_nt1_wk4_d2"),
-    # layers too small for a thousand (tile, k-block) units: 16-row tiles
-    (128, 3072, 768, "tiled_bm16_bn256_s4"),
+    # layers under 32 Mi weights stay on the skinny kernel at 33-255 rows, in blocks of 16
+    # rows (up to 64) or 32, with the most column tiles per wave that keep 128 workgroups
+    (48, 2560, 2560, "skinny_xr16_nt2_wk8_d2"), (128, 2560, 2560, "skinny_xr32_nt4_wk4_d2"),
+    (48, 1024, 1024, "skinny_xr16_nt1_wk8_d2"), (128, 3072, 768, "skinny_xr32_nt1_wk4_d2"),
+    (128, 4096, 4096, "skinny_xr32_nt4_wk4_d2"),
+    # fewer than 128 column tiles: up to 16 rows in blocks of 4; two k-blocks in flight
+    # when each wave has fewer than four
+    (16, 3072, 768, "skinny_xr4_nt1_wk8_d2"), (1, 1024, 1024, "skinny_xr4_nt1_wk8_d2"),
+    (1, 2560, 2560, "skinny_xr4_nt1_wk8_d2"),
 ])
 def test_automatic_plans(M, K, N, name):
     assert plan(M, N, K)[0] == name
 
 
-def test_k_split_only_where_columns_leave_compute_units_idle():
-    # 4096 x 4096 at M = 1: 256 column tiles, no split; 3072 x 768 at M = 1: 48 tiles, split
+def test_k_split_only_where_workgroups_leave_most_of_the_chip_idle():
+    # 4096 x 4096 at M = 1: 256 column tiles, no split; 3072 x 768 at M = 1: 48 workgroups,
+    # no split either (the hand-off costs more); 4096 x 256: 16 workgroups, split
     assert plan(1, 4096, 4096)[1] == 1
-    name, splits = plan(1, 768, 3072)
+    assert plan(1, 768, 3072)[1] == 1
+    name, splits = plan(1, 256, 4096)
     assert name.startswith("skinny") and splits > 1
+
+
+def test_2to4_takes_the_small_tiled_tiles_on_large_layers():
+    d = w4.w4a16_workspace_bytes(16, 28672, 8192)
+    assert d > 0  # stream-K pieces of the 16-row tiles of the 2:4 plan
 
 
 def test_workspace_query_covers_the_split_plans():
     assert w4.w4a16_workspace_bytes(1, 4096, 4096) == 0          # no reduction across workgroups
-    assert w4.w4a16_workspace_bytes(1, 768, 3072) > 0            # K split
+    assert w4.w4a16_workspace_bytes(1, 256, 4096) > 0            # K split
     assert w4.w4a16_workspace_bytes(256, 10240, 8192) > 0        # stream-K pieces
     assert w4.w4a16_workspace_bytes(0, 4096, 4096) == 0          # invalid shape
 

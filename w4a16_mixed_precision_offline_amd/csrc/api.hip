@@ -216,15 +216,18 @@ int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, c
 
 // Which kernel an automatic plan uses, from sweeps on MI355X: the skinny (memory-bound)
 // kernel up to 32 rows; above that the tiled kernel (1.6-2.1x faster at M = 48-64 on
-// layers of 70-235 Mi weights, and on narrow layers such as 3072 x 768), except on
-// layers under 32 Mi weights with at least 2048 columns (2560 x 2560, 4096 x 4096),
-// where the tiled kernel has too few tiles and the skinny kernel's one workgroup per
-// column tile still fills the chip.
-bool use_tiled(int M, int N, int K) {
+// layers of 70-235 Mi weights), except on layers under 32 Mi weights below 256 rows
+// (1024 x 1024, 2560 x 2560, 3072 x 768, 4096 x 4096), where the tiled kernel has too few
+// tiles and the skinny kernel with several row blocks fills the chip (2.2-2.6x faster
+// than 16-row tiles on 1024 x 1024 and 3072 x 768 at M = 48-128).  The 2:4 format on
+// layers of 128 Mi weights or more takes the tiled kernel's 16- and 32-row tiles from 9
+// rows on (1.07x / 1.16x over the skinny kernel at M = 16 / 32 on 8192 x 28672).
+bool use_tiled(int M, int N, int K, int mode = W_SYM) {
   const long long kn = (long long)K * N;
+  if (mode == W_SP24 && M > 8 && kn >= (128LL << 20)) return true;
   if (M <= 32) return false;
   if (M >= 256) return true;
-  return !(kn < (32LL << 20) && N >= 2048);
+  return kn >= (32LL << 20);
 }
 
 // MXFP4 automatic plan: the decode kernel up to 32 rows (measured 1.3-2.3x faster than
@@ -261,7 +264,7 @@ int run_fused(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
   if (variant >= ns)
     return run_tiled(mode, X, w, sp, zp, Y, M, N, K, variant - ns, splits, stream, nullptr,
                      noalloc);
-  if (variant < 0 && splits == 0 && use_tiled(M, N, K)) {
+  if (variant < 0 && splits == 0 && use_tiled(M, N, K, mode)) {
     // shapes whose tiles would need buffer offsets past 2 GiB stay on the skinny kernel
     TiledPlan t;
     if (tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0)
@@ -413,7 +416,7 @@ size_t w4a16_workspace_bytes(int M, int N, int K) {
   for (int mode : modes) {
     size_t counters = 0, floats = 0;
     TiledPlan t;
-    if (use_tiled(M, N, K) && tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0) {
+    if (use_tiled(M, N, K, mode) && tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0) {
       floats = t.part_floats;
     } else {
       SkinnyPlan p;

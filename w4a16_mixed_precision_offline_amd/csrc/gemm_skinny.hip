@@ -768,13 +768,18 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
       if (N % 48 == 0 && N / 48 >= 160 && fill(N / 48) > fill(N / 64)) ntw = 3;
       if (N / (16 * ntw) < 160) ntw = 2;
     }
-    if (XR == 4) {
+    const int tiles = N / 16;
+    if (XR == 4 || (tiles < 128 && M <= 16)) {
       // one or two rows on a wide layer: eight waves per tile, two k-blocks in flight
       // each (5% faster than four waves with four at M = 1 on 4096 x 11008 / 12288);
       // narrower layers: eight waves, four k-blocks in flight (timed over graph replays:
-      // 2-10% faster than sixteen waves with two on 11008 x 4096 at M = 1-4)
+      // 2-10% faster than sixteen waves with two on 11008 x 4096 at M = 1-4), two when
+      // each wave has fewer than four k-blocks (1024 x 1024, 2560 x 2560: 11-16% faster).
+      // Layers with fewer than 128 column tiles take up to 16 rows in blocks of 4 rows,
+      // which multiplies the workgroups (3072 x 768 at M = 16: 1.9x faster than one
+      // 16-row block split along K)
       variant = wide ? (M <= 2 ? find_variant(4, 1, 8, 2) : find_variant(4, 1, 4, 4))
-                     : find_variant(4, 1, 8, 4);
+                     : find_variant(4, 1, 8, K / KBLK >= 32 && XR == 4 ? 4 : 2);
     } else if (XR == 8) {
       // narrow layers with few k-blocks per tile (4096 x 4096): four waves per tile
       // (9% faster than eight over graph replays at M = 8)
@@ -789,9 +794,25 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
       // on 11008 x 4096 at M = 32 over one 32-row block; the second row block finds the
       // weights in the Infinity Cache).  Wide layers keep one 32-row block.
       variant = wide ? (ntw == 2 ? find_variant(32, 2, 8, 2) : find_variant(32, ntw, 4, 2))
+                     : tiles < 128    ? find_variant(16, 1, 8, 2)
                      : (N % 32 == 0 ? find_variant(16, 2, 8, 2) : find_variant(32, 1, 4, 2));
     } else {
-      variant = find_variant(64, 1, 4, 2);
+      // above 32 rows (layers too small for the tiled kernel): blocks of 16 rows up to 64
+      // rows, of 32 above, and the most column tiles per wave (4, 2, 1) that still give
+      // at least 128 workgroups.  Measured 1.3-2.6x faster than one 64-row block or the
+      // 16-row tiled kernel on 1024 x 1024, 2560 x 2560, 3072 x 768 and 4096 x 4096 (2:4)
+      // at M = 48-128
+      const int xr = M <= 64 ? 16 : 32;
+      const long mb = (M + xr - 1) / xr;
+      int nt = 1;
+      for (int c : {4, 2}) {
+        if (N % (16 * c) == 0 && mb * (tiles / c) >= 128) {
+          nt = c;
+          break;
+        }
+      }
+      variant = nt == 4 ? find_variant(xr, 4, 4, 2)
+                        : (xr == 16 ? find_variant(16, nt, 8, 2) : find_variant(32, nt, 4, 2));
     }
   }
   if (variant < 0 || variant >= kNumVariants) return -8;
@@ -817,12 +838,13 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
   int maxs = Gk / v.WK;
   if (maxs < 1) maxs = 1;
   if (splits <= 0) {
-    // split K only when the column tiles leave more than a third of the compute units
-    // without a workgroup; the reduction costs more than a partly idle chip above that
-    // (measured: 192 four-tile workgroups beat 384 split ones by 2x on 4096x12288)
+    // split K only when the workgroups would leave most of the chip idle: the hand-off
+    // of the partial sums costs more than partly idle compute units (measured: 192
+    // four-tile workgroups beat 384 split ones by 2x on 4096 x 12288; 48 workgroups on
+    // 3072 x 768 beat 144 split ones by 2.1x; no split won on any decode or small layer)
     const long base = (long)p->mblocks * p->nblocks;
     const long target = 256;
-    long sp = base >= 160 ? 1 : (target + base - 1) / base;
+    long sp = base >= 32 ? 1 : (target + base - 1) / base;
     splits = (int)(sp < 1 ? 1 : sp);
   }
   if (splits > maxs) splits = maxs;

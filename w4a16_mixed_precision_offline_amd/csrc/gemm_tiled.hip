@@ -1042,8 +1042,11 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // tiles instead (measured 1.05-1.26x faster at M = 192 on six 7B/70B-class layers, and
     // 1.08-1.18x slower at M = 256 / 384 where 128-row tiles pad nothing)
     if (!f16 && M > 128 && M < 512 && M % 128 != 0 && M % 128 <= 64) variant = 2;
-    // MXFP4 has no skinny kernel: up to 32 rows take the 32-row tile
+    // MXFP4 has no skinny kernel: up to 32 rows take the 32-row tile; the 2:4 format
+    // (tiled from 9 rows on on large layers) takes 16-row tiles up to 16 rows and 32-row
+    // tiles up to 32 (measured fastest at M = 16 / 32 on 8192 x 28672)
     if (mode == W_MX4 && M <= 32) variant = 3;
+    if (mode == W_SP24 && M <= 32) variant = M <= 16 ? 4 : 3;
     if (!f16) {
       // a layer too small to give the chip a thousand (tile, k-block) units with these
       // tiles (3072 x 768: 72 at M = 128) runs on 16-row tiles instead, which gives
