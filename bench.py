@@ -88,7 +88,7 @@ def traffic_from_profiles(kind="tiled"):
 COPY_BYTES = 256 << 20
 PMC_COMMANDS = {
     "tiled": "python -u bench.py --roofline-only --steps 2 --warmup 1 --copy-calibration",
-    "skinny": "python -u bench.py --steps 2 --warmup 1 --no-cpu --no-baseline --copy-calibration",
+    "skinny": "python -u bench.py --only-decode --copy-calibration",
 }
 
 
@@ -138,20 +138,50 @@ def pmc_summary(fetch_csv, write_csv, kind="tiled"):
                + [f"python bench.py --pmc-kind {kind} --pmc-summary {fetch_csv} {write_csv}"])
     with open(TRAFFIC_JSON[kind], "w") as f:
         json.dump(out, f, indent=1)
+    # the same figures as a short table beside the JSON
+    alg = (20562816 if kind == "skinny" else 205258752)  # algorithmic bytes per call
+    what = ("the 24 decode-sweep GEMMs (`skinny_kernel`), each equally often" if kind == "skinny"
+            else "the w4a16_gemm calls at M >= 256 of the 70B-class step (`tiled_kernel` "
+                 "dispatches, with the bytes of their `tiled_fixup_kernel` passes counted in)")
+    md = [f"# {'Skinny' if kind == 'skinny' else 'Tiled'} kernel: HBM traffic per call "
+          "(rocprofv3 counters)", "", "Commands (repository root, one MI355X):", "", "```",
+          *out["commands"], "```", "",
+          "Calibration: the same runs copy 256 MiB device-to-device three times "
+          f"(`--copy-calibration`); FETCH_SIZE reads {1 / out['fetch_factor']:.4f} of the known "
+          f"copy size and WRITE_SIZE {1 / out['write_factor']:.4f} of it, so the per-dispatch "
+          f"figures are scaled by {out['fetch_factor']} and {out['write_factor']}.", "",
+          "| quantity | value |", "|---|---|",
+          f"| calls measured | {out['launches']}: {what} |",
+          f"| FETCH_SIZE per call (raw) | {out['fetch_kib_per_launch']} KiB |",
+          f"| WRITE_SIZE per call (raw) | {out['write_kib_per_launch']} KiB |",
+          f"| HBM bytes per call (scaled) | {out['hbm_bytes_per_launch']} |",
+          f"| algorithmic bytes per call | {alg} |",
+          f"| traffic / algorithmic | {out['hbm_bytes_per_launch'] / alg:.3f} |", "",
+          f"Kernel source hash the counters belong to: `{out['kernel_sha']}` (bench.py reports "
+          "`traffic` only while the sources hash to it)."]
+    with open(TRAFFIC_JSON[kind][:-5] + ".md", "w") as f:
+        f.write("\n".join(md) + "\n")
     print(json.dumps(out))
 
 
-TRACE_MD = os.path.join(ROOT, "profiles", "w4a16_tiled_70b_kernel_trace.md")
-TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kt -o run --output-format csv "
-                 "-- python -u bench.py --steps 20 --warmup 3 --no-cpu --no-baseline --no-decode")
+TRACE_MD = {"tiled": os.path.join(ROOT, "profiles", "w4a16_tiled_70b_kernel_trace.md"),
+            "skinny": os.path.join(ROOT, "profiles", "w4a16_skinny_decode_sweep_kernel_trace.md")}
+TRACE_COMMAND = {
+    "tiled": ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kt -o run --output-format csv "
+              "-- python -u bench.py --steps 20 --warmup 3 --no-cpu --no-baseline --no-decode"),
+    "skinny": ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kd -o run --output-format csv "
+               "-- python -u bench.py --only-decode"),
+}
 
 
-def trace_summary(csv_path, bench_line_path=None):
-    """Per-kernel durations from a rocprofv3 kernel trace (CSV) of the headline step, and
-    the per-call duration of the roofline set: the packed-weight tiled kernel with 128-row
-    tiles (template <8, *, *, 0>, the M >= 256 launches) plus the stream-K fixup passes of
-    those calls (<8, *>), divided by the number of such tiled-kernel launches.  Writes the
-    markdown summary into profiles/ next to the bench line of the same command."""
+def trace_summary(csv_path, bench_line_path=None, kind="tiled"):
+    """Per-kernel durations from a rocprofv3 kernel trace (CSV), and the per-call duration
+    of the kernel the bench line's roofline figure covers.  kind "tiled" (the headline): the
+    packed-weight tiled kernel with 128-row tiles (template <8, *, *, 0>, the M >= 256
+    launches) plus the stream-K fixup passes of those calls (<8, *>), divided by the number
+    of such tiled-kernel launches.  kind "skinny" (the decode sweep, --only-decode): every
+    skinny_kernel launch.  Writes the markdown summary into profiles/ next to the bench line
+    of the same command."""
     import csv
     import re
     rows = list(csv.DictReader(open(csv_path)))
@@ -167,7 +197,11 @@ def trace_summary(csv_path, bench_line_path=None):
         st[1] += t
         st[2] = min(st[2], t)
         st[3] = max(st[3], t)
-        if m and m.group(1) == "tiled_kernel":
+        if kind == "skinny":
+            if m and m.group(1) == "skinny_kernel":
+                roof_t += t
+                roof_calls += 1
+        elif m and m.group(1) == "tiled_kernel":
             a = [int(x) for x in m.group(2).split(",")]
             if a[0] == 8 and a[3] == 0:
                 roof_t += t
@@ -176,28 +210,42 @@ def trace_summary(csv_path, bench_line_path=None):
             a = [int(x) for x in m.group(2).split(",")]
             if a[0] == 8:
                 roof_t += t
-    lines = ["# Tiled kernel on the 70B-class sweep: kernel durations (rocprofv3 kernel trace)", "",
-             "Command (repository root, one MI355X):", "", "```", TRACE_COMMAND,
-             f"python bench.py --trace-summary gpurun_out/prof_kt/<host>/run_kernel_trace.csv"
-             + (" gpurun_out/bench_trace.json" if bench_line_path else ""), "```", "",
+    title = ("Tiled kernel on the 70B-class sweep" if kind == "tiled"
+             else "Skinny kernel on the 7B-class decode sweep")
+    lines = [f"# {title}: kernel durations (rocprofv3 kernel trace)", "",
+             "Command (repository root, one MI355X):", "", "```", TRACE_COMMAND[kind],
+             f"python bench.py --trace-kind {kind} --trace-summary "
+             f"gpurun_out/{'prof_kt' if kind == 'tiled' else 'prof_kd'}/run_kernel_trace.csv"
+             + (" <the bench line of that run, as a JSON file>" if bench_line_path else ""),
+             "```", "",
              "| kernel (template args) | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     for k in sorted(stats):
         c, tot, mn, mx = stats[k]
         lines.append(f"| `{k}` | {c} | {tot / c:.3f} | {mn:.3f} | {mx:.3f} |")
     per_call = roof_t / max(1, roof_calls)
-    lines += ["", f"Roofline set (w4a16_gemm at M >= 256: `tiled_kernel<8, *, *, 0>` plus its "
-                  f"`tiled_fixup_kernel<8, *>` passes): {roof_calls} calls, **{per_call:.2f} us** "
-                  "per call (warmup and timed steps; each step has the same launches)."]
+    what = ("Roofline set (w4a16_gemm at M >= 256: `tiled_kernel<8, *, *, 0>` plus its "
+            "`tiled_fixup_kernel<8, *>` passes)" if kind == "tiled"
+            else "Every `skinny_kernel` launch (the 24 GEMMs of the decode sweep, each equally often)")
+    lines += ["", f"{what}: {roof_calls} calls, **{per_call:.2f} us** per call (warmup and timed "
+                  "steps; each step has the same launches)."]
     if bench_line_path:
         line = json.load(open(bench_line_path))
-        ev = line["roofline"]["avg_launch_us"]
-        lines += ["", f"The bench line of the same command measured {ev:.2f} us per call with HIP "
-                      f"events on the kernels' stream (`roofline.avg_launch_us`): "
+        if kind == "skinny":
+            line = line["decode_sweep"]
+            ev = line["avg_launch_us"]
+        else:
+            line = line["roofline"]
+            ev = line["avg_launch_us"]
+        src = ("the run traced above" if kind == "tiled" else
+               "a run of the same workload without the profiler (under the tracer the "
+               "graph replays of these few-microsecond kernels gain gaps between launches)")
+        lines += ["", f"The bench line of {src} measured {ev:.2f} us per call with HIP "
+                      f"events on the kernels' stream (`avg_launch_us`): "
                       f"{100 * (ev / per_call - 1):+.1f}% from the kernel durations above "
-                      "(the events also hold the gaps between launches, and tracing widens them).",
-                  "", "```", json.dumps(line["roofline"]), "```"]
+                      "(the events also hold the gaps between launches).",
+                  "", "```", json.dumps(line), "```"]
     out = "\n".join(lines) + "\n"
-    with open(TRACE_MD, "w") as f:
+    with open(TRACE_MD[kind], "w") as f:
         f.write(out)
     print(out)
 
@@ -848,7 +896,9 @@ def decode_sweep_leg(w4, torch, steps, warmup, use_graph=True):
                avg_launch_us=round(t / n * 1e6, 3),
                hbm_frac=round(ab / n / (t / n) / 1e9 / HBM_PEAK_GBPS, 4),
                read_ceiling_us_per_launch=round(tr / n * 1e6, 3),
-               gemm_over_read_time=round(t / tr, 3), launch="hip_graph" if use_graph else "eager")
+               gemm_over_read_time=round(t / tr, 3), launch="hip_graph" if use_graph else "eager",
+               algorithmic_bytes_per_launch=int(ab / n),
+               traffic=traffic_from_profiles("skinny"))
     del packed, Xs, Ys
     torch.cuda.empty_cache()
     return out
@@ -932,6 +982,17 @@ def build_line(h, steps, warmup, traffic, cpu, base, decode):
     }
 
 
+def copy_calibration(torch):
+    """Three plain device copies of COPY_BYTES: the known-size traffic that scales the
+    FETCH_SIZE / WRITE_SIZE counters of the same run."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -950,6 +1011,8 @@ def main():
                     help="only a short W4A16 / W4A8 tiled-kernel workload (for counter runs)")
     ap.add_argument("--only-mxfp4", action="store_true",
                     help="only the MXFP4 leg (for a kernel trace of its kernels)")
+    ap.add_argument("--only-decode", action="store_true",
+                    help="only the decode-sweep leg (for counter runs of the skinny kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain device copies of known size (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -957,6 +1020,8 @@ def main():
                          "this script into profiles/ and exit")
     ap.add_argument("--pmc-kind", choices=("tiled", "skinny"), default="tiled",
                     help="which kernel --pmc-summary summarizes")
+    ap.add_argument("--trace-kind", choices=("tiled", "skinny"), default="tiled",
+                    help="which kernel --trace-summary summarizes")
     ap.add_argument("--trace-summary", nargs="+", metavar="CSV", default=None,
                     help="summarize a rocprofv3 kernel trace of the headline run (and the "
                          "bench line it printed, as a JSON file) into profiles/ and exit")
@@ -965,7 +1030,7 @@ def main():
         pmc_summary(*args.pmc_summary, kind=args.pmc_kind)
         return
     if args.trace_summary:
-        trace_summary(*args.trace_summary)
+        trace_summary(*args.trace_summary, kind=args.trace_kind)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -986,16 +1051,16 @@ def main():
     if args.only_mxfp4:
         print(json.dumps(dict(mxfp4_in_mfma_dequant=mxfp4_leg(w4, torch))), flush=True)
         return
+    if args.only_decode:
+        if args.copy_calibration:
+            copy_calibration(torch)
+        print(json.dumps(dict(decode_sweep=decode_sweep_leg(w4, torch, 5, 2))), flush=True)
+        return
 
     stream = torch.cuda.Stream()
     inp = headline_inputs(w4, torch, roofline_only=args.roofline_only)
     if args.copy_calibration:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch)
     print(f"bench.py: inputs resident, timing {args.steps} steps", file=sys.stderr, flush=True)
     h = headline_leg(w4, torch, inp, stream, args.steps, args.warmup, args.roofline_only)
     t_step = h["t_step"]
