@@ -135,8 +135,8 @@ int w4a16_gemm(const uint16_t* X, const void* wp, const uint16_t* sp, const void
  *   different streams, or concurrent replays of graphs holding such calls) race and give
  *   wrong results.  A plan needing more workspace than the array holds returns
  *   W4A16_ERR_WORKSPACE and enqueues nothing (no automatic plan of a valid shape needs
- *   more: the largest takes two 128 x 256 fp32 pieces for each of 256 workgroups). */
-#define W4A16_NOALLOC_SCRATCH_BYTES (65536 + (64u << 20))
+ *   more: the largest takes two 128 x 512 fp32 pieces for each of 256 workgroups). */
+#define W4A16_NOALLOC_SCRATCH_BYTES (65536 + (128u << 20))
 int w4a16_gemm_noalloc(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                        uint16_t* Y, int M, int N, int K, int group, void* stream);
 

@@ -47,6 +47,15 @@ def test_binding_covers_every_declared_symbol():
         assert n in w4.EXPORTED and callable(getattr(w4, n)), n
 
 
+def test_binding_constants_match_the_header():
+    import w4a16_mixed_precision_offline_amd as w4
+    text = open(HEADER).read()
+    m = re.search(r"#define W4A16_NOALLOC_SCRATCH_BYTES \((\d+) \+ \((\d+)u << (\d+)\)\)", text)
+    assert m, "W4A16_NOALLOC_SCRATCH_BYTES not found"
+    a, b, c = (int(g) for g in m.groups())
+    assert w4.NOALLOC_SCRATCH_BYTES == a + (b << c)
+
+
 def test_queries(raw):
     raw.w4a16_strerror.restype = ctypes.c_char_p
     raw.w4a16_packed_bytes.restype = ctypes.c_size_t
@@ -165,10 +174,15 @@ def test_fp16_plan_validation(raw):
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5 + [ctypes.c_void_p]
     raw.w4a16_fp16_gemm_variant_name.restype = ctypes.c_char_p
     n = raw.w4a16_fp16_gemm_variants()
-    assert n > raw.w4a16_gemm_variants() - 5  # skinny variants plus the fp16 tiled ones
     names = [raw.w4a16_fp16_gemm_variant_name(v) for v in range(n)]
     assert all(names) and raw.w4a16_fp16_gemm_variant_name(n) is None
-    assert sum(nm.startswith(b"tiled_f16") for nm in names) >= 2
+    # the skinny variants (numbered as in w4a16_gemm_variants) plus the fp16 tiled ones
+    raw.w4a16_gemm_variant_name.restype = ctypes.c_char_p
+    skinny = [raw.w4a16_gemm_variant_name(v) for v in range(raw.w4a16_gemm_variants())
+              if not raw.w4a16_gemm_variant_name(v).startswith(b"tiled")]
+    assert names[:len(skinny)] == skinny
+    assert len(names) - len(skinny) >= 2
+    assert all(nm.startswith(b"tiled_f16") for nm in names[len(skinny):])
     assert f(None, A, A, 1, 16, 128, -1, 0, None) == -1
     assert f(A, A, A, 1, 16, 100, -1, 0, None) == -2
     assert f(A, A, A, 1, 16, 128, n, 0, None) == -8

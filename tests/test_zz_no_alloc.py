@@ -41,15 +41,19 @@ def _run(gh, w4, M, K, N, asym, seed):
 
 def test_noalloc_matches_gemm_on_calls_of_decreasing_size(gh):
     import w4a16_mixed_precision_offline_amd as w4
-    # 1) tiled kernel, 320 tiles on 256 workgroups: stream-K pieces in the scratch array
-    # 2) a smaller tiled launch: fewer pieces, the first call's partials still there
-    # 3) skinny kernel with a K split (16 column tiles): partials and arrival counters
-    # 4) the same again: the counters must have come back to zero
-    cases = [(1024, 8192, 10240, False), (300, 2048, 1040, True), (1, 4096, 256, True),
-             (1, 4096, 256, True)]
+    # 1) eight-wave tiles, 640 tiles on 256 workgroups: 384 tiles in stream-K pieces, the
+    #    whole array of partials
+    # 2) four-wave tiles, 320 tiles on 256 workgroups: stream-K pieces in the scratch array
+    # 3) a smaller tiled launch: fewer pieces, the earlier calls' partials still there
+    # 4) skinny kernel with a K split (16 column tiles): partials and arrival counters
+    # 5) the same again: the counters must have come back to zero
+    cases = [(4096, 8192, 10240, False), (1024, 8192, 10240, False), (300, 2048, 1040, True),
+             (1, 4096, 256, True), (1, 4096, 256, True)]
+    kinds = ["tiled_bm128_bn512_w8", "tiled", "tiled", "skinny", "skinny"]
     for i, (M, K, N, asym) in enumerate(cases):
-        assert w4.w4a16_gemm_describe(M, N, K, 128)["name"].startswith("tiled" if i < 2 else "skinny")
+        assert w4.w4a16_gemm_describe(M, N, K, 128)["name"].startswith(kinds[i])
         _run(gh, w4, M, K, N, asym, i)
+    assert w4.w4a16_workspace_bytes(4096, 10240, 8192) == 128 << 20
     assert w4.w4a16_gemm_describe(1, 256, 4096, 128)["splits"] > 1
 
 
@@ -64,5 +68,6 @@ def test_noalloc_rejects_plans_larger_than_its_array(gh):
     with pytest.raises(w4.W4A16Error) as e:
         w4.w4a16_gemm_noalloc(X, wp, sp, None, Y, 4, 1000, 1024, 128)
     assert e.value.code == -2
-    for (M, K, N) in [(4096, 8192, 28672), (256, 28672, 8192), (1, 4096, 256)]:
+    for (M, K, N) in [(4096, 8192, 28672), (4096, 8192, 10240), (256, 28672, 8192),
+                      (1, 4096, 256)]:
         assert w4.w4a16_workspace_bytes(M, N, K) <= w4.NOALLOC_SCRATCH_BYTES

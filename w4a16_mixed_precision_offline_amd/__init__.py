@@ -169,7 +169,7 @@ def w4a16_gemm_noalloc(X, wp, sp, zp, Y, M, N, K, group, stream=None):
                                                          _ptr(Y), M, N, K, group, _stream(stream)))
 
 
-NOALLOC_SCRATCH_BYTES = 65536 + (64 << 20)  # W4A16_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 65536 + (128 << 20)  # W4A16_NOALLOC_SCRATCH_BYTES
 
 
 def w4a16_gemm_plan(X, wp, sp, zp, Y, M, N, K, group, variant=-1, splits=0, stream=None):

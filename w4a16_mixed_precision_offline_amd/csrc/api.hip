@@ -121,11 +121,11 @@ int get_workspace(int dev, hipStream_t st, size_t counters, size_t floats, int**
 }
 
 // ---- fixed device scratch for w4a16_gemm_noalloc ----------------------------------------
-// [counters (W4A16_WS_COUNTER_BYTES, zero at rest) | fp32 partials].  64 MiB of partials
-// hold the largest automatic plan: two 128 x 256 fp32 stream-K pieces per persistent
-// workgroup, 256 workgroups.  In host code `scratch` only stands in for the symbol; the
+// [counters (W4A16_WS_COUNTER_BYTES, zero at rest) | fp32 partials].  128 MiB of partials
+// hold the largest automatic plan: two 128 x 512 fp32 stream-K pieces per persistent
+// workgroup of the eight-wave tiles, 256 workgroups.  In host code `scratch` only stands in for the symbol; the
 // device address comes from hipGetSymbolAddress, once per device.
-constexpr size_t kScratchPartBytes = (size_t)64 << 20;
+constexpr size_t kScratchPartBytes = (size_t)128 << 20;
 constexpr size_t kScratchBytes = (size_t)W4A16_WS_COUNTER_BYTES + kScratchPartBytes;
 static_assert(kScratchBytes == W4A16_NOALLOC_SCRATCH_BYTES, "header and library disagree");
 std::map<int, char*> g_scratch;  // device -> device address of its copy of `scratch`

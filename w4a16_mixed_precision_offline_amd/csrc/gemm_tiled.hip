@@ -201,10 +201,12 @@ __device__ __forceinline__ uint32_t swz8(int r, int c) {
 // matrix work of the preceding k-block instead of being issued in one burst
 // (a burst of 4 waves x NV loads fills the address queue of the CU and stalls
 // the waves before their MFMAs start).
-template <int MT, int NTW, int MODE>
+template <int MT, int NTW, int MODE, int NWV = WAVES>
 struct DmaPlan {
-  // activation loads per wave: 1 KiB each, 4 rows of fp16 or 8 rows of fp8
-  static constexpr int NX = mode_fp8(MODE) ? MT / 2 : MT;
+  // activation loads per wave: 1 KiB each, 4 rows of fp16 or 8 rows of fp8; the NWV waves
+  // share the BM-row tile
+  static constexpr int NX = (mode_fp8(MODE) ? MT / 2 : MT) * WAVES / NWV;
+  static_assert(NX >= 1, "every wave loads part of the activation tile");
   static constexpr uint32_t XKB = mode_fp8(MODE) ? 128u : 256u;  // X bytes per row and k-block
   // 2:4: two tiles' kept codes per 16-byte load, all four tiles' positions in one
   static constexpr int NW = MODE == W_SP24 ? NTW / 2 + NTW / 4 : MODE == W_FP16 ? 4 * NTW : NTW;
@@ -244,12 +246,12 @@ struct DmaPlan {
 // LDS read of the fragment three groups ahead, unpacks its share of the column tiles
 // of step j+1 (tiles t = i, i + MT, ...), and runs the NTW MFMAs of (j, i).  Scheduling barriers between the groups
 // keep that order, so LDS latency hides behind the matrix work.
-template <int MT, int NTW, int MODE>
+template <int MT, int NTW, int MODE, class DP>
 __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
                                                float4v (&acc)[MT][NTW], const uint32_t (&aoff)[4],
                                                int lane, uint32_t magic,
-                                               const DmaPlan<MT, NTW, MODE>& dma) {
-  constexpr int NVL = DmaPlan<MT, NTW, MODE>::NV;
+                                               const DP& dma) {
+  constexpr int NVL = DP::NV;
   constexpr int G = 4 * MT;  // groups per k-block
   u32x4 wv[NTW];
   half2v c0[NTW], c1[NTW], s2[NTW];
@@ -324,15 +326,15 @@ __device__ __forceinline__ void compute_kblock(const char* xb, const char* wl,
 // row tile i and runs v_smfmac_f32_16x16x64_f16 with the unpacked weights as the
 // sparse operand: half the matrix instructions and half the unpacking of the dense
 // format for the same k-block.
-template <int MT, int NTW>
+template <int MT, int NTW, class DP>
 __device__ __forceinline__ void compute_kblock_sp24(const char* xb, const char* wl,
                                                     float4v (&acc)[MT][NTW],
                                                     const uint32_t (&aoff)[4], int lane,
                                                     uint32_t magic,
-                                                    const DmaPlan<MT, NTW, W_SP24>& dma) {
+                                                    const DP& dma) {
   typedef WLds<NTW, W_SP24> L;
   constexpr int G = 2 * MT;  // groups per k-block
-  constexpr int NVL = DmaPlan<MT, NTW, W_SP24>::NV;
+  constexpr int NVL = DP::NV;
   uint2 wv[NTW];
   int meta[NTW];
   half2v s2[NTW];
@@ -386,13 +388,13 @@ __device__ __forceinline__ void compute_kblock_sp24(const char* xb, const char* 
 
 // One k-block of the fp16 baseline: weight fragments come straight from LDS (no
 // unpacking); same group pipeline as the packed formats.
-template <int MT, int NTW>
+template <int MT, int NTW, class DP>
 __device__ __forceinline__ void compute_kblock_fp16(const char* xb, const char* wl,
                                                     float4v (&acc)[MT][NTW],
                                                     const uint32_t (&aoff)[4], int lane,
-                                                    const DmaPlan<MT, NTW, W_FP16>& dma) {
+                                                    const DP& dma) {
   constexpr int G = 4 * MT;
-  constexpr int NVL = DmaPlan<MT, NTW, W_FP16>::NV;
+  constexpr int NVL = DP::NV;
   constexpr int PF = 3;
   half8 ar[PF + 1];
 #pragma unroll
@@ -436,14 +438,14 @@ __device__ __forceinline__ void compute_kblock_fp16(const char* xb, const char* 
 // = row 32j + 8q + e of the block in both operands: the repacked word j of the weights
 // and the activation bytes at 32j + 8q of its row.  Column tiles are the outer loop: the
 // unpacking of tile t + 1 overlaps the matrix instructions of tile t.
-template <int MT, int NTW, int MODE>
+template <int MT, int NTW, int MODE, class DP>
 __device__ __forceinline__ void compute_kblock_fp8(const char* xb, const char* wl,
                                                    float4v (&acc)[MT][NTW],
                                                    const uint32_t (&aoff)[4], int lane,
                                                    uint32_t magic,
-                                                   const DmaPlan<MT, NTW, MODE>& dma) {
+                                                   const DP& dma) {
   typedef WLds<NTW, MODE> L;
-  constexpr int NVL = DmaPlan<MT, NTW, MODE>::NV;
+  constexpr int NVL = DP::NV;
   constexpr int G = NTW;  // groups per k-block: one per column tile
   int8v xa[MT];
 #pragma unroll
@@ -521,13 +523,13 @@ __device__ __forceinline__ void compute_kblock_fp8(const char* xb, const char* w
 // 64+16g .. +15 in its last 16 (measured with one-hot activations).  The X fragment of
 // lane l is therefore chunks g and 4+g of row 16i + l%16 of the swizzled tile (two
 // 16-byte reads).  The loads of a later k-block are spread over the row tiles' groups.
-template <int MT, int NTW, int MODE>
+template <int MT, int NTW, int MODE, class DP>
 __device__ __forceinline__ void compute_kblock_mx(const char* xb, const char* wl,
                                                   float4v (&acc)[MT][NTW],
                                                   const uint32_t (&aoff)[4], int lane,
-                                                  const DmaPlan<MT, NTW, MODE>& dma) {
+                                                  const DP& dma) {
   typedef WLds<NTW, MODE> L;
-  constexpr int NVL = DmaPlan<MT, NTW, MODE>::NV;
+  constexpr int NVL = DP::NV;
   int8v b[NTW];
   int sc[NTW];
 #pragma unroll
@@ -585,12 +587,12 @@ __device__ __forceinline__ void tile_coords(int tt, int tiles_m, int tiles_n, in
 // Y store of row tiles i0 .. i0 + NI - 1 of a finished tile tt: lane holds row 16i +
 // lane%16 and the four columns 16t + 4(lane/16) .. +3 of each of the wave's NTW column
 // tiles.
-template <int MT, int NTW, int NI>
+template <int MT, int NTW, int NI, int NWV>
 __device__ __forceinline__ void store_rows(uint16_t* __restrict__ Y, const TiledArgs& a, int tt,
                                            int i0, int wave, int lane,
                                            const float4v (&acc)[NI][NTW]) {
   constexpr int BM = 16 * MT;
-  constexpr int BN = WAVES * 16 * NTW;
+  constexpr int BN = NWV * 16 * NTW;
   int tm, tn;
   tile_coords(tt, a.tiles_m, a.tiles_n, a.group_m, tm, tn);
   const int m0 = tm * BM;
@@ -616,10 +618,10 @@ __device__ __forceinline__ void store_rows(uint16_t* __restrict__ Y, const Tiled
     }
   }
 }
-template <int MT, int NTW>
+template <int MT, int NTW, int NWV>
 __device__ __forceinline__ void store_tile(uint16_t* __restrict__ Y, const TiledArgs& a, int tt,
                                            int wave, int lane, const float4v (&acc)[MT][NTW]) {
-  store_rows<MT, NTW, MT>(Y, a, tt, 0, wave, lane, acc);
+  store_rows<MT, NTW, MT, NWV>(Y, a, tt, 0, wave, lane, acc);
 }
 
 // Byte offset of one lane's float4 of (row tile i, column tile t) inside a partial piece.
@@ -628,21 +630,22 @@ __device__ __forceinline__ uint32_t piece_off(int wave, int i, int t, int lane) 
   return (uint32_t)((((wave * MT + i) * NTW + t) * 64 + lane) * 16);
 }
 
-template <int MT, int NTW, int NS, int MODE>
-__global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
+template <int MT, int NTW, int NS, int MODE, int NWV>
+__global__ __launch_bounds__(64 * NWV) void tiled_kernel(
     const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,
     const uint16_t* __restrict__ Sp, const uint32_t* __restrict__ Zp, uint16_t* __restrict__ Y,
     float* __restrict__ part, TiledArgs a) {
   constexpr int BM = 16 * MT;
-  constexpr int BN = WAVES * 16 * NTW;
+  constexpr int BN = NWV * 16 * NTW;
   constexpr bool F8 = mode_fp8(MODE);
   constexpr int XBUF = BM * (F8 ? 128 : 256);  // one k-block of the activation tile
   constexpr int NSTAGE = NS;       // LDS pipeline stages
   constexpr int AHEAD = NS - 1;    // k-blocks in flight ahead of the one computed
   constexpr int PIECE = BM * BN;   // floats of one partial tile
-  constexpr int STAGE = XBUF + WAVES * WLds<NTW, MODE>::BYTES;  // LDS bytes of one stage
-  constexpr int NV = DmaPlan<MT, NTW, MODE>::NV;  // loads per stage per thread
-  constexpr int NX = DmaPlan<MT, NTW, MODE>::NX;  // activation loads per stage per thread
+  constexpr int STAGE = XBUF + NWV * WLds<NTW, MODE>::BYTES;  // LDS bytes of one stage
+  typedef DmaPlan<MT, NTW, MODE, NWV> DP;
+  constexpr int NV = DP::NV;  // loads per stage per thread
+  constexpr int NX = DP::NX;  // activation loads per stage per thread
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE];
 
   const int tid = threadIdx.x;
@@ -684,7 +687,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
         const int cg = (lane & 7) ^ ((r >> 1) & 7);
         xoff[c] = r < rows ? (uint32_t)((size_t)r * a.K + 16 * cg) : kOutOfRange;
       } else {
-        const int r = 4 * (wave * MT + c) + (lane >> 4);
+        const int r = 4 * (wave * NX + c) + (lane >> 4);
         const int cg = (lane & 15) ^ (r & 15);  // global chunk stored at position lane%16
         xoff[c] = r < rows ? (uint32_t)(((size_t)r * a.K + 8 * cg) * 2) : kOutOfRange;
       }
@@ -774,7 +777,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
 #pragma unroll
     for (int p = 0; p < AHEAD; ++p) {
       const bool live = p < nk;
-      DmaPlan<MT, NTW, MODE> plan;
+      DP plan;
       plan.rx = live ? rx : rx0;
 #pragma unroll
       for (int c = 0; c < NX; ++c) plan.xoff[c] = xoff[c];
@@ -784,7 +787,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       plan.wave = wave;
       plan.kb = kb0 + p;
 #pragma unroll
-      for (int q = 0; q < DmaPlan<MT, NTW, MODE>::NV; ++q) plan.issue(q);
+      for (int q = 0; q < NV; ++q) plan.issue(q);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -801,7 +804,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_sched_barrier(0);
       const int dn = (d + AHEAD) % NSTAGE;
-      DmaPlan<MT, NTW, MODE> plan;
+      DP plan;
       plan.rx = issue_live ? rx : rx0;
 #pragma unroll
       for (int c = 0; c < NX; ++c) plan.xoff[c] = xoff[c];
@@ -846,7 +849,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
   };
 
   auto store_y = [&](int tt, const float4v (&acc)[MT][NTW]) {
-    store_tile<MT, NTW>(Y, a, tt, wave, lane, acc);
+    store_tile<MT, NTW, NWV>(Y, a, tt, wave, lane, acc);
   };
 
 
@@ -897,11 +900,11 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_kernel(
 // stripe order (a fixed order, so results are bitwise reproducible) and written to Y.
 // Tiles done by a single workgroup were stored by it directly.  The loads of up to four
 // pieces are in flight together.
-template <int MT, int NTW>
-__global__ __launch_bounds__(64 * WAVES) void tiled_fixup_kernel(const float* __restrict__ part,
-                                                                 uint16_t* __restrict__ Y,
-                                                                 TiledArgs a) {
-  constexpr int PIECE = 16 * MT * WAVES * 16 * NTW;
+template <int MT, int NTW, int NWV>
+__global__ __launch_bounds__(64 * NWV) void tiled_fixup_kernel(const float* __restrict__ part,
+                                                               uint16_t* __restrict__ Y,
+                                                               TiledArgs a) {
+  constexpr int PIECE = 16 * MT * NWV * 16 * NTW;
   constexpr int CH = 4;  // pieces per batch of loads
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -936,7 +939,7 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_fixup_kernel(const float* __
       for (int t = 0; t < NTW; ++t) sum[0][t] = wp + c == w_first ? v[c][t] : sum[0][t] + v[c][t];
     }
   }
-  store_rows<MT, NTW, 1>(Y, a, a.dp_rounds * a.grid + tl, i, wave, lane, sum);
+  store_rows<MT, NTW, 1, NWV>(Y, a, a.dp_rounds * a.grid + tl, i, wave, lane, sum);
 }
 
 typedef void (*TiledFn)(const uint16_t*, const uint32_t*, const uint16_t*, const uint32_t*,
@@ -944,7 +947,7 @@ typedef void (*TiledFn)(const uint16_t*, const uint32_t*, const uint16_t*, const
 typedef void (*FixupFn)(const float*, uint16_t*, TiledArgs);
 
 struct TVariant {
-  int MT, NTW, NS;
+  int MT, NTW, NS, NWV;  // row tiles, column tiles per wave, pipeline stages, waves
   TiledFn sym, asym, sp24, f16, sym64, asym64, sym8, asym8, mx4;
   FixupFn fixup;
   const char* name;
@@ -953,30 +956,39 @@ struct TVariant {
 // fp8 activations need an even number of 16-row tiles (one 1 KiB load covers 8 rows)
 template <int MT, int NTW, int NS, int MODE>
 constexpr TiledFn fp8_tiled() {
-  if constexpr (MT % 2 == 0) return tiled_kernel<MT, NTW, NS, MODE>;
+  if constexpr (MT % 2 == 0) return tiled_kernel<MT, NTW, NS, MODE, WAVES>;
   else return nullptr;
 }
 // the 2:4 format's loads are laid out for four column tiles per wave (two tiles' kept codes
 // per 16-byte load, all four tiles' positions in one)
 template <int MT, int NTW, int NS>
 constexpr TiledFn sp24_tiled() {
-  if constexpr (NTW == 4) return tiled_kernel<MT, NTW, NS, W_SP24>;
+  if constexpr (NTW == 4) return tiled_kernel<MT, NTW, NS, W_SP24, WAVES>;
   else return nullptr;
 }
 
 #define W4A16_TILED(MT, NTW, NS, NAME)                                                       \
   TVariant {                                                                               \
-    MT, NTW, NS, tiled_kernel<MT, NTW, NS, W_SYM>, tiled_kernel<MT, NTW, NS, W_ASYM>,       \
-        sp24_tiled<MT, NTW, NS>(), nullptr, tiled_kernel<MT, NTW, NS, W_SYM64>,            \
-        tiled_kernel<MT, NTW, NS, W_ASYM64>, fp8_tiled<MT, NTW, NS, W_SYM8>(),             \
-        fp8_tiled<MT, NTW, NS, W_ASYM8>(), fp8_tiled<MT, NTW, NS, W_MX4>(),                \
-        tiled_fixup_kernel<MT, NTW>, NAME                                                   \
+    MT, NTW, NS, WAVES, tiled_kernel<MT, NTW, NS, W_SYM, WAVES>,                            \
+        tiled_kernel<MT, NTW, NS, W_ASYM, WAVES>, sp24_tiled<MT, NTW, NS>(), nullptr,       \
+        tiled_kernel<MT, NTW, NS, W_SYM64, WAVES>, tiled_kernel<MT, NTW, NS, W_ASYM64, WAVES>, \
+        fp8_tiled<MT, NTW, NS, W_SYM8>(), fp8_tiled<MT, NTW, NS, W_ASYM8>(),                \
+        fp8_tiled<MT, NTW, NS, W_MX4>(), tiled_fixup_kernel<MT, NTW, WAVES>, NAME           \
+  }
+// eight waves (two per SIMD) sharing a BM-row activation tile, each with the same 16*NTW
+// columns of work as in the four-wave variants: the packed fp16-activation formats only
+#define W4A16_TILED_W8(MT, NTW, NS, NAME)                                                    \
+  TVariant {                                                                               \
+    MT, NTW, NS, 8, tiled_kernel<MT, NTW, NS, W_SYM, 8>, tiled_kernel<MT, NTW, NS, W_ASYM, 8>, \
+        nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_SYM64, 8>,                            \
+        tiled_kernel<MT, NTW, NS, W_ASYM64, 8>, nullptr, nullptr, nullptr,                  \
+        tiled_fixup_kernel<MT, NTW, 8>, NAME                                                \
   }
 // the fp16 baseline moves four times the weight bytes: its own LDS-sized tiles
 #define W4A16_TILED_F16(MT, NTW, NS, NAME)                                                    \
   TVariant {                                                                               \
-    MT, NTW, NS, nullptr, nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_FP16>, nullptr,     \
-        nullptr, nullptr, nullptr, nullptr, tiled_fixup_kernel<MT, NTW>, NAME              \
+    MT, NTW, NS, WAVES, nullptr, nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_FP16, WAVES>, \
+        nullptr, nullptr, nullptr, nullptr, nullptr, tiled_fixup_kernel<MT, NTW, WAVES>, NAME \
   }
 
 const TVariant kTiled[] = {
@@ -986,6 +998,7 @@ const TVariant kTiled[] = {
     W4A16_TILED(2, 4, 4, "tiled_bm32_bn256_s4"),
     W4A16_TILED(1, 4, 4, "tiled_bm16_bn256_s4"),
     W4A16_TILED(8, 2, 3, "tiled_bm128_bn128_s3"),
+    W4A16_TILED_W8(8, 4, 2, "tiled_bm128_bn512_w8_s2"),
 };
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
 const TVariant kTiledF16[] = {
@@ -1047,20 +1060,30 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // tiles up to 32 (measured fastest at M = 16 / 32 on 8192 x 28672)
     if (mode == W_MX4 && M <= 32) variant = 3;
     if (mode == W_SP24 && M <= 32) variant = M <= 16 ? 4 : 3;
+    // eight-wave 128 x 512 tiles once they fill the 256 compute units at least twice over,
+    // or exactly once (no stream-K stripes): the second wave on each SIMD issues its
+    // unpacking and LDS reads while the first one's MFMAs run (measured 1.06-1.11x at
+    // M = 2048-4096 on 8192 x 28672, 1.09-1.11x at M = 2048 / 4096 on 28672 x 8192,
+    // 1.0-1.02x on 8192 x 10240; 0.97-1.0x at M = 1024, where the larger tiles leave
+    // between one and two rounds, all striped, and 0.88-0.93x at M = 256)
+    if (variant == 0 && (mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64)) {
+      const long long t8 = (long long)((M + 127) / 128) * ((N + 511) / 512);
+      if (t8 >= 512 || t8 == 256) variant = 6;
+    }
     if (!f16) {
       // a layer too small to give the chip a thousand (tile, k-block) units with these
       // tiles (3072 x 768: 72 at M = 128) runs on 16-row tiles instead, which gives
       // it 8x the units (measured 1.2-1.6x faster there)
       const TVariant& d = table[variant];
       const long long units = (long long)((M + 16 * d.MT - 1) / (16 * d.MT)) *
-                              ((N + WAVES * 16 * d.NTW - 1) / (WAVES * 16 * d.NTW)) * (K / KBLK);
+                              ((N + d.NWV * 16 * d.NTW - 1) / (d.NWV * 16 * d.NTW)) * (K / KBLK);
       if (units < 1024) variant = f8 ? 3 : 4;  // fp8: the 32-row tile (an even row-tile count)
     }
   }
   if (variant >= count) return -8;
   const TVariant& v = table[variant];
   if (variant_fn(v, mode) == nullptr) return -8;  // e.g. fp8 with odd row tiles
-  const int BM = 16 * v.MT, BN = WAVES * 16 * v.NTW;
+  const int BM = 16 * v.MT, BN = v.NWV * 16 * v.NTW;
   const int Gk = K / KBLK;
   TiledPlan q;
   q.variant = variant;
@@ -1109,7 +1132,7 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   q.fixup_wgs = (int)sk_tiles * v.MT;  // one workgroup per (stream-K tile, row tile)
   q.part_floats = sk_tiles ? (size_t)2 * grid * BM * BN : 0;
   q.wgs = grid;
-  q.threads = 64 * WAVES;
+  q.threads = 64 * v.NWV;
   *p = q;
   return 0;
 }
