@@ -108,12 +108,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // the two halves (bf16 has only 7 mantissa bits, so the 16q trick of fp16 does not
 // apply).  The offset 128 + z is removed after the matrix instruction, in fp32, with
 // the block's activation row sums (see compute_stage).
+// These words go straight into a matrix instruction, so they are formed in plain code
+// rather than with the and_or asm above: the compiler inserts the wait states a matrix
+// instruction needs after a VALU write of its operands only for instructions it knows
+// (a bf16 kernel whose schedule put the asm right before the matrix instruction read
+// stale operands on MI355X).
 __device__ __forceinline__ bf16x8 offset_codes_bf16(uint32_t w) {
   const uint32_t magic = 0x43004300u;
-  const uint32_t t0 = and_or(w, 0x000F000Fu, magic);          // rows 0, 1
-  const uint32_t t1 = and_or(w >> 4, 0x000F000Fu, magic);     // rows 2, 3
-  const uint32_t t2 = and_or(w >> 8, 0x000F000Fu, magic);     // rows 4, 5
-  const uint32_t t3 = and_or(w >> 12, 0x000F000Fu, magic);    // rows 6, 7
+  const uint32_t t0 = (w & 0x000F000Fu) | magic;          // rows 0, 1
+  const uint32_t t1 = ((w >> 4) & 0x000F000Fu) | magic;   // rows 2, 3
+  const uint32_t t2 = ((w >> 8) & 0x000F000Fu) | magic;   // rows 4, 5
+  const uint32_t t3 = ((w >> 12) & 0x000F000Fu) | magic;  // rows 6, 7
   typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
   return __builtin_bit_cast(bf16x8, u32x4v{t0, t1, t2, t3});
 }
@@ -157,6 +162,7 @@ __host__ __device__ constexpr int x_loads(int XR, int MODE) {
   return mode_fp8(MODE) ? (XR + 7) / 8 : XR / 4;
 }
 __host__ __device__ constexpr int x_elem_bytes(int MODE) { return mode_fp8(MODE) ? 1 : 2; }
+
 
 template <int XR, int NT, int MODE>
 struct Stage {
@@ -461,12 +467,15 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
         const half2v s01 = __builtin_bit_cast(half2v, S.s64[t]);
         acc[t][mt] += (float)s01[0] * g0 + (float)s01[1] * g1;
       } else {
-        float4v g = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          g = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][j], b[j], g, 0, 0, 0);
+        // two accumulation chains of two matrix instructions each (the k-steps j = 0, 2
+        // and 1, 3): half the dependent latency of one chain of four
+        const float4v z = {0.f, 0.f, 0.f, 0.f};
+        float4v g0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][0], b[0], z, 0, 0, 0);
+        float4v g1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][1], b[1], z, 0, 0, 0);
+        g0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][2], b[2], g0, 0, 0, 0);
+        g1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][3], b[3], g1, 0, 0, 0);
         const float sc = (float)__builtin_bit_cast(_Float16, S.s[t]);
-        acc[t][mt] += sc * g;
+        acc[t][mt] += sc * (g0 + g1);
       }
     }
   }
@@ -496,19 +505,29 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   constexpr int MT = (XR + 15) / 16;
   constexpr int XTILE = MT * 16 * XSTRIDE;  // bytes of one wave's X tile
   // per-wave X tiles; after the main loop the same memory holds the reduction
+  static_assert((WK - 1) * 64 * NT * MT * 16 <= WK * XTILE, "reduction does not fit");
   __shared__ __attribute__((aligned(16))) char lds[WK * XTILE];
   const int lane = threadIdx.x & 63;
   // wave index made uniform so that all k-block bookkeeping stays on the scalar unit
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // workgroup -> (row block, column tiles, K slice).  The loads wait for this, so the
+  // common plans (one K slice, one row block) skip the divisions; Gk * splits < 2^31
+  // (the plan refuses more), so the slice bounds need no 64-bit division.
   int bid = blockIdx.x;
-  const int sl = bid % splits;
-  bid /= splits;
-  const int nb = bid % nblocks;
-  const int mb = bid / nblocks;
   const int Gk = K / KBLK;
+  int sl = 0, kb0 = 0, kb1 = Gk;
+  if (splits > 1) {
+    sl = bid % splits;
+    bid /= splits;
+    kb0 = Gk * sl / splits;
+    kb1 = Gk * (sl + 1) / splits;
+  }
+  int nb = bid, mb = 0;
+  if (bid >= nblocks) {
+    nb = bid % nblocks;
+    mb = bid / nblocks;
+  }
   // K range of this workgroup's slice, then this wave's k-blocks in it
-  const int kb0 = (int)(((long)Gk * sl) / splits);
-  const int kb1 = (int)(((long)Gk * (sl + 1)) / splits);
   const int nk_wg = kb1 - kb0;
   // wave w takes the k-blocks kb0 + w, kb0 + w + WK, ...: the waves of a workgroup read
   // neighbouring 1 KiB blocks at the same time (measured 1-6% faster on the decode
@@ -554,11 +573,6 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     const int cb = mode_fp8(MODE) ? 16 * (lane & 7) : 16 * (lane & 15);
     xoff[c] = r < rows ? (uint32_t)(r * K * XB + cb) : kOutOfRange;
   }
-  // rows XR..15 of the LDS tile are never written by the loads: keep them zero
-  if (XR % 16 != 0) {
-    for (int i = lane; i < (16 - XR) * XSTRIDE / 16; i += 64)
-      *reinterpret_cast<u32x4*>(xlds + XR * XSTRIDE + 16 * i) = u32x4{0, 0, 0, 0};
-  }
   const uint32_t magic = 0x64006400u;
 
   float4v acc[NT][MT];
@@ -583,6 +597,12 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   for (int d = 0; d < D; ++d) {
     load_stage(S[d], kw0 + d * WK, d < nk, lane, Gk, K, R, Rnull, xoff);
     __builtin_amdgcn_sched_barrier(0);  // issue the stages in order
+  }
+  // rows XR..15 of the LDS tile are never written by the loads: keep them zero (after
+  // the first loads are on their way)
+  if (XR % 16 != 0) {
+    for (int i = lane; i < (16 - XR) * XSTRIDE / 16; i += 64)
+      *reinterpret_cast<u32x4*>(xlds + XR * XSTRIDE + 16 * i) = u32x4{0, 0, 0, 0};
   }
   for (int i = 0; i < nk; i += D) {
 #pragma unroll
@@ -637,18 +657,26 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     old = __shfl(old, 0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (old != splits - 1) return;
+    // slice by slice, in slice order; the NACC loads of a slice are independent and go
+    // out together, so the hand-off costs one memory round trip per slice (a loop over
+    // slices inside each element would wait once per element and slice)
     const float* base = part + tile_id * splits * (NACC * 64);
+    float sum[NACC];
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) sum[i] = 0.f;
+    for (int s2 = 0; s2 < splits; ++s2) {
+      float v[NACC];
+#pragma unroll
+      for (int i = 0; i < NACC; ++i) v[i] = load_coherent(base + (long)s2 * (NACC * 64) + i * 64 + lane);
+#pragma unroll
+      for (int i = 0; i < NACC; ++i) sum[i] += v[i];
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = 0.f;
-          for (int s2 = 0; s2 < splits; ++s2)
-            v += load_coherent(base + (long)s2 * (NACC * 64) + ((t * MT + mt) * 4 + r) * 64 + lane);
-          acc[t][mt][r] = v;
-        }
+        for (int r = 0; r < 4; ++r) acc[t][mt][r] = sum[(t * MT + mt) * 4 + r];
     if (lane == 0)
       __hip_atomic_store(counters + tile_id, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -849,6 +877,7 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
   }
   if (splits > maxs) splits = maxs;
   if (splits < 1) splits = 1;
+  if ((long long)Gk * splits >= (1LL << 31)) return -2;  // the kernel's slice bounds are 32-bit
   p->splits = splits;
   if ((long long)p->mblocks * p->nblocks * splits >= lim) return -2;
   p->wgs = p->mblocks * p->nblocks * splits;
