@@ -25,10 +25,11 @@ def plan(M, N, K, group=128):
     (48, 8192, 28672, "tiled_bm64_bn256_s3"), (64, 28672, 8192, "tiled_bm64_bn256_s3"),
     # ... 128-row tiles above, except where they would pad M by more than an eighth
     (128, 8192, 28672, "tiled_bm128_bn256_s3"), (192, 8192, 28672, "tiled_bm64_bn256_s3"),
-    (256, 28672, 8192, "tiled_bm128_bn256_s3"), (1024, 8192, 28672, "tiled_bm128_bn256_s3"),
+    (256, 28672, 8192, "tiled_bm128_bn256_s3"),
     (1024, 8192, 10240, "tiled_bm128_bn256_s3"), (1024, 28672, 8192, "tiled_bm128_bn256_s3"),
     # eight-wave 128 x 512 tiles from two rounds of them on the 256 compute units on, or
-    # exactly one round
+    # in whole rounds of 224-256 workgroups
+    (1024, 8192, 28672, "tiled_bm128_bn512_w8_s2"),
     (4096, 8192, 28672, "tiled_bm128_bn512_w8_s2"), (4096, 28672, 8192, "tiled_bm128_bn512_w8_s2"),
     (4096, 8192, 10240, "tiled_bm128_bn512_w8_s2"), (2048, 8192, 28672, "tiled_bm128_bn512_w8_s2"),
     (2048, 28672, 8192, "tiled_bm128_bn512_w8_s2"), (2048, 8192, 10240, "tiled_bm128_bn256_s3"),
@@ -46,6 +47,17 @@ def plan(M, N, K, group=128):
 ])
 def test_automatic_plans(M, K, N, name):
     assert plan(M, N, K)[0] == name
+
+
+def test_eight_wave_tiles_take_whole_rounds_where_the_tile_count_allows():
+    # 8 x 56 = 448 tiles: two rounds of 224 workgroups, no stream-K stripes; 32 x 56 = 1792:
+    # seven rounds of 256; 32 x 20 = 640 tiles divide by nothing in 224..256: stream-K on 256
+    # (the workspace query is the largest over the weight formats, so it is not checked
+    # for the data-parallel case)
+    assert w4.w4a16_gemm_describe(1024, 28672, 8192, 128)["workgroups"] == 224
+    assert w4.w4a16_gemm_describe(4096, 28672, 8192, 128)["workgroups"] == 256
+    assert w4.w4a16_gemm_describe(4096, 10240, 8192, 128)["workgroups"] == 256
+    assert w4.w4a16_workspace_bytes(4096, 10240, 8192) > 0
 
 
 def test_k_split_only_where_workgroups_leave_most_of_the_chip_idle():

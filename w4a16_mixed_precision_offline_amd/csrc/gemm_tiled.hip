@@ -1029,6 +1029,14 @@ const char* tiled_variant_name(int mode, int v) {
   return mode == W_FP16 ? kTiledF16[v].name : kTiled[v].name;
 }
 
+// A workgroup count between 224 and 256 that divides `tiles` exactly (the largest), or 0:
+// with it every workgroup takes whole tiles, in equal numbers, and no tile is cut.
+static long dp_grid(long tiles) {
+  for (long g = 256; g >= 224; --g)
+    if (tiles % g == 0) return g;
+  return 0;
+}
+
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p) {
   // fp8 activations: groups of 128 rows or more (one scale per 128-row block)
   if ((!mode_dense4(mode) && mode != W_SP24 && mode != W_FP16) || mode_bf16(mode) ||
@@ -1061,14 +1069,15 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     if (mode == W_MX4 && M <= 32) variant = 3;
     if (mode == W_SP24 && M <= 32) variant = M <= 16 ? 4 : 3;
     // eight-wave 128 x 512 tiles once they fill the 256 compute units at least twice over,
-    // or exactly once (no stream-K stripes): the second wave on each SIMD issues its
-    // unpacking and LDS reads while the first one's MFMAs run (measured 1.06-1.11x at
-    // M = 2048-4096 on 8192 x 28672, 1.09-1.11x at M = 2048 / 4096 on 28672 x 8192,
-    // 1.0-1.02x on 8192 x 10240; 0.97-1.0x at M = 1024, where the larger tiles leave
-    // between one and two rounds, all striped, and 0.88-0.93x at M = 256)
+    // or in whole rounds of 224-256 workgroups (no stream-K stripes): the second wave on
+    // each SIMD issues its unpacking and LDS reads while the first one's MFMAs run
+    // (measured 1.06-1.11x at M = 2048-4096 on 8192 x 28672, 1.09-1.11x at M = 2048 / 4096
+    // on 28672 x 8192, 1.0-1.02x on 8192 x 10240; at M = 1024 on 8192 x 28672, 448 tiles
+    // as two rounds of 224 workgroups: 1.10x, where 256 workgroups and stream-K stripes
+    // were 0.96x; 0.88-0.93x at M = 256)
     if (variant == 0 && (mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64)) {
       const long long t8 = (long long)((M + 127) / 128) * ((N + 511) / 512);
-      if (t8 >= 512 || t8 == 256) variant = 6;
+      if (t8 >= 512 || dp_grid(t8) > 0) variant = 6;
     }
     if (!f16) {
       // a layer too small to give the chip a thousand (tile, k-block) units with these
@@ -1110,6 +1119,9 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     const long min_units = 8;
     long g = (T * Gk + min_units - 1) / min_units;
     grid = (int)(g < 256 ? (g < 1 ? 1 : g) : 256);
+    // the eight-wave tiles: whole rounds of 224-256 workgroups where the tile count allows
+    // (their stream-K pieces cost about half a tile's work per workgroup)
+    if (v.NWV == 8 && dp_grid(T) > 0) grid = (int)dp_grid(T);
   }
   if ((long long)grid > (long long)T * Gk) grid = (int)(T * Gk);  // at least one unit each
   q.args.grid = grid;
