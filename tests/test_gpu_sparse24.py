@@ -111,8 +111,9 @@ def test_parity_every_variant_and_split(gh, M, K, N):
         name = w4.w4a16_gemm_variant_name(v)
         # tiled variants take any N % 16; their `splits` is the number of workgroups
         nt = 1 if name.startswith("tiled") else int(name.split("_nt")[1].split("_")[0])
-        # the 2:4 tiled kernel needs four column tiles per wave (256-column tiles)
-        refused = N % (16 * nt) != 0 or (name.startswith("tiled") and "_bn256_" not in name)
+        # the 2:4 tiled kernel needs four column tiles per wave (four-wave 256-column tiles)
+        refused = N % (16 * nt) != 0 or (name.startswith("tiled") and ("_bn256_" not in name or
+                                                                      "_w8_" in name))
         for splits in (1, 2, 3):
             Y = gh.nan_filled(M, N)
             if refused:
@@ -163,7 +164,8 @@ def test_tiled_sparse_grids(gh, M, K, N):
     # the 2:4 format runs on the tiled variants with four column tiles per wave (256 columns)
     tiled = [v for v in range(w4.w4a16_gemm_variants())
              if w4.w4a16_gemm_variant_name(v).startswith("tiled")
-             and "_bn256_" in w4.w4a16_gemm_variant_name(v)]
+             and "_bn256_" in w4.w4a16_gemm_variant_name(v)
+             and "_w8_" not in w4.w4a16_gemm_variant_name(v)]
     assert tiled
     for v in tiled:
         for grid in (0, 1, 3, 6, 16):
@@ -191,7 +193,7 @@ def test_tiled_sparse_onehot_exact(gh):
     comp = _compress(gh, d, K, N)
     for v in range(w4.w4a16_gemm_variants()):
         name = w4.w4a16_gemm_variant_name(v)
-        if not name.startswith("tiled") or "_bn256_" not in name:
+        if not name.startswith("tiled") or "_bn256_" not in name or "_w8_" in name:
             continue
         for grid in (1, 7):
             Y = gh.host(_sgemm(gh, gh.dev(X), comp, M, N, K, variant=v, splits=grid))

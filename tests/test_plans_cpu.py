@@ -26,13 +26,16 @@ def plan(M, N, K, group=128):
     # ... 128-row tiles above, except where they would pad M by more than an eighth
     (128, 8192, 28672, "tiled_bm128_bn256_s3"), (192, 8192, 28672, "tiled_bm64_bn256_s3"),
     (256, 28672, 8192, "tiled_bm128_bn256_s3"),
-    (1024, 8192, 10240, "tiled_bm128_bn256_s3"), (1024, 28672, 8192, "tiled_bm128_bn256_s3"),
+    # from a full round of 128 x 256 tiles on (where the 128 x 512 ones below do not fit
+    # the chip in whole rounds): the same tiles with eight waves
+    (1024, 8192, 10240, "tiled_bm128_bn256_w8_s3"), (1024, 28672, 8192, "tiled_bm128_bn256_w8_s3"),
+    (2048, 8192, 10240, "tiled_bm128_bn256_w8_s3"),
     # eight-wave 128 x 512 tiles from two rounds of them on the 256 compute units on, or
     # in whole rounds of 224-256 workgroups
     (1024, 8192, 28672, "tiled_bm128_bn512_w8_s2"),
     (4096, 8192, 28672, "tiled_bm128_bn512_w8_s2"), (4096, 28672, 8192, "tiled_bm128_bn512_w8_s2"),
     (4096, 8192, 10240, "tiled_bm128_bn512_w8_s2"), (2048, 8192, 28672, "tiled_bm128_bn512_w8_s2"),
-    (2048, 28672, 8192, "tiled_bm128_bn512_w8_s2"), (2048, 8192, 10240, "tiled_bm128_bn256_s3"),
+    (2048, 28672, 8192, "tiled_bm128_bn512_w8_s2"),
     # layers up to 128 Mi weights at 65-256 rows: 128 x 128 tiles
     (128, 5120, 13824, "tiled_bm128_bn128_s3"), (256, 8192, 10240, "tiled_bm128_bn128_s3"),
     # layers under 32 Mi weights stay on the skinny kernel at 33-255 rows, in blocks of 16

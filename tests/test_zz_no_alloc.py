@@ -43,7 +43,8 @@ def test_noalloc_matches_gemm_on_calls_of_decreasing_size(gh):
     import w4a16_mixed_precision_offline_amd as w4
     # 1) eight-wave tiles, 640 tiles on 256 workgroups: 384 tiles in stream-K pieces, the
     #    whole array of partials
-    # 2) four-wave tiles, 320 tiles on 256 workgroups: stream-K pieces in the scratch array
+    # 2) eight-wave 128 x 256 tiles, 320 tiles on 256 workgroups: stream-K pieces in the
+    #    scratch array
     # 3) a smaller tiled launch: fewer pieces, the earlier calls' partials still there
     # 4) skinny kernel with a K split (16 column tiles): partials and arrival counters
     # 5) the same again: the counters must have come back to zero

@@ -999,6 +999,7 @@ const TVariant kTiled[] = {
     W4A16_TILED(1, 4, 4, "tiled_bm16_bn256_s4"),
     W4A16_TILED(8, 2, 3, "tiled_bm128_bn128_s3"),
     W4A16_TILED_W8(8, 4, 2, "tiled_bm128_bn512_w8_s2"),
+    W4A16_TILED_W8(8, 2, 3, "tiled_bm128_bn256_w8_s3"),
 };
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
 const TVariant kTiledF16[] = {
@@ -1077,7 +1078,14 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // were 0.96x; 0.88-0.93x at M = 256)
     if (variant == 0 && (mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64)) {
       const long long t8 = (long long)((M + 127) / 128) * ((N + 511) / 512);
-      if (t8 >= 512 || dp_grid(t8) > 0) variant = 6;
+      if (t8 >= 512 || dp_grid(t8) > 0) {
+        variant = 6;
+      } else if ((long long)((M + 127) / 128) * ((N + 255) / 256) >= 256) {
+        // otherwise, from one full round of 128 x 256 tiles on, the same tiles with eight
+        // waves (two per SIMD, 32 columns each): 1.04x at M = 1024 on 28672 x 8192, 1.01-1.03x
+        // on 8192 x 10240
+        variant = 7;
+      }
     }
     if (!f16) {
       // a layer too small to give the chip a thousand (tile, k-block) units with these
