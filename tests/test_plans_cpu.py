@@ -60,6 +60,10 @@ def test_eight_wave_tiles_take_whole_rounds_where_the_tile_count_allows():
     assert w4.w4a16_gemm_describe(1024, 28672, 8192, 128)["workgroups"] == 224
     assert w4.w4a16_gemm_describe(4096, 28672, 8192, 128)["workgroups"] == 256
     assert w4.w4a16_gemm_describe(4096, 10240, 8192, 128)["workgroups"] == 256
+    # 200-255 tiles of any variant: one round, one workgroup per tile
+    assert w4.w4a16_gemm_describe(256, 28672, 8192, 128)["workgroups"] == 224
+    assert w4.w4a16_gemm_describe(256, 13824, 5120, 128)["workgroups"] == 216
+    assert w4.w4a16_gemm_describe(256, 10240, 8192, 128)["workgroups"] == 256
     assert w4.w4a16_workspace_bytes(4096, 10240, 8192) > 0
 
 
