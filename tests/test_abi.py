@@ -162,9 +162,9 @@ def test_workspace_bytes(raw):
     assert f(0, 4096, 4096) == 0 and f(16, 4000, 4096) == 0 and f(16, 4096, 100) == 0
     # a wide decode layer runs without cross-workgroup reduction
     assert f(1, 12288, 4096) == 0
-    # 8192 x 28672 at M = 256: 224 tiles of 128 x 256 on 256 workgroups, all striped:
+    # 8192 x 10240 at M = 256: 160 tiles of 128 x 128 on 256 workgroups, all striped:
     # two fp32 partial tiles per workgroup
-    assert f(256, 28672, 8192) >= 2 * 256 * 128 * 256 * 4
+    assert f(256, 10240, 8192) >= 2 * 256 * 128 * 128 * 4
     # M = 4096 on the same layer: 14 (fp16 tiles: 28) whole rounds of tiles, no stripes
     assert f(4096, 28672, 8192) == 0
 
