@@ -401,6 +401,54 @@ def test_hip_graph_replays_match_eager(gh):
         del junk
 
 
+def test_graph_keeps_its_workspace_when_the_stream_grows_it(gh):
+    """A graph captured with a split-K launch holds the stream's workspace of that time.
+    A larger eager launch on the same stream afterwards grows the workspace; the old buffer
+    is retired, not freed, so every later replay still reproduces the eager result bit for
+    bit.  A capture that would need the workspace to grow is refused before anything is
+    enqueued (W4A16_ERR_WORKSPACE)."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    st = torch.cuda.Stream()
+    M, K, N = 1, 4096, 256  # skinny kernel, K split across workgroups
+    assert w4.w4a16_gemm_describe(M, N, K, 128)["splits"] > 1
+    _, d, X = _case(M, K, N)
+    Xd, packed = gh.dev(X), gh.repack(d, K, N)
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    with torch.cuda.stream(st):
+        gh.gemm(Xd, packed, M, N, K, Y=Y)
+    torch.cuda.synchronize()
+    eager = gh.host(Y).view(np.uint16).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        gh.gemm(Xd, packed, M, N, K, Y=Y)
+    torch.cuda.synchronize()
+    # a tiled launch with stream-K pieces (64 MiB of partials) grows the stream's buffer
+    Mb, Kb, Nb = 1024, 2048, 4096
+    assert w4.w4a16_workspace_bytes(Mb, Nb, Kb) > w4.w4a16_workspace_bytes(M, N, K)
+    _, db, Xb = _case(Mb, Kb, Nb)
+    Xbd, packedb = gh.dev(Xb), gh.repack(db, Kb, Nb)
+    for rep in range(3):
+        Yb = torch.empty((Mb, Nb), dtype=torch.float16, device="cuda")
+        with torch.cuda.stream(st):
+            gh.gemm(Xbd, packedb, Mb, Nb, Kb, Y=Yb)
+            Y.fill_(0)
+            g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gh.host(Y).view(np.uint16), eager), rep
+    rows, cols = gh.tile_samples(Mb, Nb)
+    Yref, B = oracle.gemm_sampled(Xb, db["Qp"], db["s"], db["Zp"], 128, rows, cols)
+    ok, info = oracle.accept(gh.host(Yb)[np.ix_(rows, cols)], Yref, B)
+    assert ok, info
+    # a fresh stream has no workspace yet: capturing a split-K launch on it is refused
+    st2 = torch.cuda.Stream()
+    g2 = torch.cuda.CUDAGraph()
+    with pytest.raises(w4.W4A16Error) as e:
+        with torch.cuda.graph(g2, stream=st2):
+            gh.gemm(Xd, packed, M, N, K, Y=Y)
+    assert e.value.code == -6
+
+
 # ---- degenerate and boundary cases ----------------------------------------------------
 def _pack_k(q: np.ndarray) -> np.ndarray:
     """uint8 codes [K, N] -> int32 [K/8, N], nibble j of word i = row 8i + j."""
