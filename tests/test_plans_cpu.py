@@ -23,6 +23,9 @@ def plan(M, N, K, group=128):
     (32, 4096, 4096, "skinny_xr16_nt2_wk8_d2"), (20, 11008, 4096, "skinny_xr16_nt2_wk8_d2"),
     # above 32 rows on large layers: the tiled kernel, 64-row tiles up to 64 rows ...
     (48, 8192, 28672, "tiled_bm64_bn256_s3"), (64, 28672, 8192, "tiled_bm64_bn256_s3"),
+    # ... 64 x 128 tiles on layers up to 128 Mi weights
+    (48, 5120, 13824, "tiled_bm64_bn128_s4"), (64, 8192, 10240, "tiled_bm64_bn128_s4"),
+    (48, 13824, 5120, "tiled_bm64_bn128_s4"),
     # ... 128-row tiles above, except where they would pad M by more than an eighth
     (128, 8192, 28672, "tiled_bm128_bn256_s3"), (192, 8192, 28672, "tiled_bm64_bn256_s3"),
     (256, 28672, 8192, "tiled_bm128_bn256_s3"),

@@ -1001,9 +1001,6 @@ const TVariant kTiled[] = {
     W4A16_TILED_W8(8, 4, 2, "tiled_bm128_bn512_w8_s2"),
     W4A16_TILED_W8(8, 2, 3, "tiled_bm128_bn256_w8_s3"),
     W4A16_TILED(4, 2, 4, "tiled_bm64_bn128_s4"),
-    W4A16_TILED(4, 1, 4, "tiled_bm64_bn64_s4"),
-    W4A16_TILED(2, 2, 4, "tiled_bm32_bn128_s4"),
-    W4A16_TILED(8, 1, 4, "tiled_bm128_bn64_s4"),
 };
 constexpr int kNumTiled = sizeof(kTiled) / sizeof(kTiled[0]);
 const TVariant kTiledF16[] = {
@@ -1064,6 +1061,12 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // 235 Mi-weight layers and at M >= 1024)
     if (!f16 && mode != W_SP24 && M > 64 && M <= 256 && (long long)K * N <= (128LL << 20))
       variant = 5;
+    // 33-64 rows on layers up to 128 Mi weights: 64 x 128 tiles, four k-blocks deep
+    // (measured 1.04-1.09x over 64 x 256 at M = 48 and 64 on 8192 x 10240, 5120 x 13824
+    // and 13824 x 5120; slower on the 235 Mi-weight layers)
+    if (variant == 2 && (mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64) &&
+        (long long)K * N <= (128LL << 20))
+      variant = 8;
     // 128-row tiles would pad M by more than an eighth (M % 128 in 1..64, M < 512): 64-row
     // tiles instead (measured 1.05-1.26x faster at M = 192 on six 7B/70B-class layers, and
     // 1.08-1.18x slower at M = 256 / 384 where 128-row tiles pad nothing)
