@@ -43,11 +43,10 @@ def _mx(gh, X8d, ad, packed, M, N, K, variant=-1, grid=0, Y=None):
 
 
 def _runs(variant_name, M):
-    # fp8 activations need an even number of 16-row tiles; the decode kernel takes M <= 32;
-    # the eight-wave tiles run the fp16-activation formats only
+    # fp8 activations need an even number of 16-row tiles; the decode kernel takes M <= 32
     if variant_name.startswith("mx_decode_"):
         return M <= 32
-    return not variant_name.startswith("tiled_bm16_") and "_w8_" not in variant_name
+    return not variant_name.startswith("tiled_bm16_")
 
 
 def _grids(variant_name):

@@ -214,12 +214,12 @@ W4A8_TILED = [(300, 2048, 1040, False), (257, 1536, 512, True), (130, 3072, 272,
 
 
 def _tiled_variants(w4):
-    # 16-row tiles are odd for fp8 (8 rows per load); the eight-wave tiles run the
-    # fp16-activation formats only
+    # 16-row tiles are odd for fp8 (8 rows per load); the eight-wave 128 x 512 tiles run
+    # the fp16-activation formats only (fp8 needs two column tiles per wave there)
     return [v for v in range(w4.w4a16_gemm_variants())
             if w4.w4a16_gemm_variant_name(v).startswith("tiled")
             and not w4.w4a16_gemm_variant_name(v).startswith("tiled_bm16")
-            and "_w8_" not in w4.w4a16_gemm_variant_name(v)]
+            and not w4.w4a16_gemm_variant_name(v).startswith("tiled_bm128_bn512_w8")]
 
 
 @pytest.mark.parametrize("M,K,N,asym", W4A8_TILED)
@@ -254,7 +254,7 @@ def test_w4a8_tiled_rejects_odd_row_tiles(gh):
            if w4.w4a16_gemm_variant_name(v).startswith("tiled_bm16")]
     with pytest.raises(w4.W4A16Error):
         _gemm8(gh, X8, a, packed, M, N, K, v16[0], 0)
-    with pytest.raises(w4.W4A16Error):  # eight-wave tiles: fp16 activations only
+    with pytest.raises(w4.W4A16Error):  # eight-wave 128 x 512 tiles: no fp8 mode
         _gemm8(gh, X8, a, packed, M, N, K, gh.variant_index("tiled_bm128_bn512_w8_s2"), 0)
     with pytest.raises(w4.W4A16Error):  # groups of 64: skinny kernel only
         _gemm8(gh, X8, a, gh.repack(_case(M, K, N, group=64)[0], K, N, 64), M, N, K,

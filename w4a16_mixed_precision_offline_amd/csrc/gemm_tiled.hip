@@ -954,9 +954,9 @@ struct TVariant {
 };
 
 // fp8 activations need an even number of 16-row tiles (one 1 KiB load covers 8 rows)
-template <int MT, int NTW, int NS, int MODE>
+template <int MT, int NTW, int NS, int MODE, int NWV = WAVES>
 constexpr TiledFn fp8_tiled() {
-  if constexpr (MT % 2 == 0) return tiled_kernel<MT, NTW, NS, MODE, WAVES>;
+  if constexpr (MT % 2 == 0) return tiled_kernel<MT, NTW, NS, MODE, NWV>;
   else return nullptr;
 }
 // the 2:4 format's loads are laid out for four column tiles per wave (two tiles' kept codes
@@ -976,12 +976,21 @@ constexpr TiledFn sp24_tiled() {
         fp8_tiled<MT, NTW, NS, W_MX4>(), tiled_fixup_kernel<MT, NTW, WAVES>, NAME           \
   }
 // eight waves (two per SIMD) sharing a BM-row activation tile, each with the same 16*NTW
-// columns of work as in the four-wave variants: the packed fp16-activation formats only
+// columns of work as in the four-wave variants: the packed formats except 2:4.  The
+// fp8-activation INT4 modes only with two column tiles per wave (with four, their
+// unpacking and rescale do not fit the registers of two waves per SIMD: the main loop
+// spills).
+template <int MT, int NTW, int NS, int MODE>
+constexpr TiledFn fp8_tiled_w8() {
+  if constexpr (NTW <= 2) return fp8_tiled<MT, NTW, NS, MODE, 8>();
+  else return nullptr;
+}
 #define W4A16_TILED_W8(MT, NTW, NS, NAME)                                                    \
   TVariant {                                                                               \
     MT, NTW, NS, 8, tiled_kernel<MT, NTW, NS, W_SYM, 8>, tiled_kernel<MT, NTW, NS, W_ASYM, 8>, \
         nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_SYM64, 8>,                            \
-        tiled_kernel<MT, NTW, NS, W_ASYM64, 8>, nullptr, nullptr, nullptr,                  \
+        tiled_kernel<MT, NTW, NS, W_ASYM64, 8>, fp8_tiled_w8<MT, NTW, NS, W_SYM8>(),        \
+        fp8_tiled_w8<MT, NTW, NS, W_ASYM8>(), fp8_tiled<MT, NTW, NS, W_MX4, 8>(),           \
         tiled_fixup_kernel<MT, NTW, 8>, NAME                                                \
   }
 // the fp16 baseline moves four times the weight bytes: its own LDS-sized tiles
@@ -1076,23 +1085,31 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // tiles up to 32 (measured fastest at M = 16 / 32 on 8192 x 28672)
     if (mode == W_MX4 && M <= 32) variant = 3;
     if (mode == W_SP24 && M <= 32) variant = M <= 16 ? 4 : 3;
-    // eight-wave 128 x 512 tiles once they fill the 256 compute units at least twice over,
-    // or in whole rounds of 224-256 workgroups (no stream-K stripes): the second wave on
-    // each SIMD issues its unpacking and LDS reads while the first one's MFMAs run
-    // (measured 1.06-1.11x at M = 2048-4096 on 8192 x 28672, 1.09-1.11x at M = 2048 / 4096
-    // on 28672 x 8192, 1.0-1.02x on 8192 x 10240; at M = 1024 on 8192 x 28672, 448 tiles
-    // as two rounds of 224 workgroups: 1.10x, where 256 workgroups and stream-K stripes
-    // were 0.96x; 0.88-0.93x at M = 256)
-    if (variant == 0 && (mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64)) {
+    // Eight waves (two per SIMD): the second wave on each SIMD issues its unpacking and LDS
+    // reads while the first one's MFMAs run.
+    // fp16 activations: 128 x 512 tiles once they fill the 256 compute units at least twice
+    // over, or in whole rounds of 224-256 workgroups (no stream-K stripes): measured
+    // 1.06-1.11x at M = 2048-4096 on 8192 x 28672, 1.09-1.11x at M = 2048 / 4096 on
+    // 28672 x 8192, 1.0-1.02x on 8192 x 10240; at M = 1024 on 8192 x 28672, 448 tiles as two
+    // rounds of 224 workgroups: 1.10x, where 256 workgroups and stream-K stripes were 0.96x;
+    // 0.88-0.93x at M = 256.  Otherwise, from one full round of 128 x 256 tiles on, the
+    // same tiles with eight waves (32 columns each): 1.04x at M = 1024 on 28672 x 8192,
+    // 1.01-1.03x on 8192 x 10240.
+    // MXFP4: 128 x 512 tiles in whole rounds only (1.04-1.18x at M = 1024 / 4096 on the
+    // 235 Mi-weight layers; with stream-K stripes 0.86-0.93x), else 128 x 256 with eight
+    // waves from a full round on (1.06x at M = 1024 and 4096 on 8192 x 10240).
+    // fp8 activations (INT4 codes): no 128 x 512 eight-wave tiles (they spill); 128 x 256
+    // with eight waves where those tiles make whole rounds of 256 (1.01-1.04x at M = 4096;
+    // 0.90-0.93x at M = 1024 on 8192 x 28672 with its 896 tiles as four rounds of 224).
+    const bool dense16 = mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64;
+    const bool int4fp8 = mode == W_SYM8 || mode == W_ASYM8;
+    if (variant == 0 && (dense16 || int4fp8 || mode == W_MX4)) {
       const long long t8 = (long long)((M + 127) / 128) * ((N + 511) / 512);
-      if (t8 >= 512 || dp_grid(t8) > 0) {
+      const long long t4 = (long long)((M + 127) / 128) * ((N + 255) / 256);
+      if ((dense16 && (t8 >= 512 || dp_grid(t8) > 0)) || (mode == W_MX4 && dp_grid(t8) > 0))
         variant = 6;
-      } else if ((long long)((M + 127) / 128) * ((N + 255) / 256) >= 256) {
-        // otherwise, from one full round of 128 x 256 tiles on, the same tiles with eight
-        // waves (two per SIMD, 32 columns each): 1.04x at M = 1024 on 28672 x 8192, 1.01-1.03x
-        // on 8192 x 10240
+      else if ((!int4fp8 && t4 >= 256) || (int4fp8 && t4 % 256 == 0))
         variant = 7;
-      }
     }
     if (!f16) {
       // a layer too small to give the chip a thousand (tile, k-block) units with these
