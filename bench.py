@@ -167,9 +167,9 @@ def pmc_summary(fetch_csv, write_csv, kind="tiled"):
 TRACE_MD = {"tiled": os.path.join(ROOT, "profiles", "w4a16_tiled_70b_kernel_trace.md"),
             "skinny": os.path.join(ROOT, "profiles", "w4a16_skinny_decode_sweep_kernel_trace.md")}
 TRACE_COMMAND = {
-    "tiled": ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kt -o run --output-format csv "
+    "tiled": ("rocprofv3 --kernel-trace --stats -d rocprof/kt_tiled -o run --output-format csv "
               "-- python -u bench.py --steps 20 --warmup 3 --no-cpu --no-baseline --no-decode"),
-    "skinny": ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_kd -o run --output-format csv "
+    "skinny": ("rocprofv3 --kernel-trace --stats -d rocprof/kt_skinny -o run --output-format csv "
                "-- python -u bench.py --only-decode"),
 }
 
@@ -215,7 +215,7 @@ def trace_summary(csv_path, bench_line_path=None, kind="tiled"):
     lines = [f"# {title}: kernel durations (rocprofv3 kernel trace)", "",
              "Command (repository root, one MI355X):", "", "```", TRACE_COMMAND[kind],
              f"python bench.py --trace-kind {kind} --trace-summary "
-             f"gpurun_out/{'prof_kt' if kind == 'tiled' else 'prof_kd'}/run_kernel_trace.csv"
+             f"rocprof/{'kt_tiled' if kind == 'tiled' else 'kt_skinny'}/run_kernel_trace.csv"
              + (" <the bench line of that run, as a JSON file>" if bench_line_path else ""),
              "```", "",
              "| kernel (template args) | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
@@ -1099,8 +1099,8 @@ def main():
                       load_time_kernels=offline_leg(w4, torch))
     detail_path = args.detail
     if detail_path is None and args.all_legs:
-        os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-        detail_path = os.path.join(ROOT, "gpurun_out", "bench_detail.json")
+        os.makedirs(os.path.join(ROOT, "bench_out"), exist_ok=True)
+        detail_path = os.path.join(ROOT, "bench_out", "bench_detail.json")
 
     line = build_line(h, args.steps, args.warmup, traffic, cpu, base, decode)
     if detail_path:
