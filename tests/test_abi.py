@@ -97,8 +97,10 @@ def test_describe_plans(raw):
     for (N, name) in [(12288, b"skinny_xr16_nt3_wk4_d2"), (11008, b"skinny_xr16_nt4_wk4_d2")]:
         assert raw.w4a16_gemm_describe(16, N, 4096, 128, out) == 0
         assert raw.w4a16_gemm_variant_name(out[0]) == name
-    # wide layers where four tiles per wave would leave under 160 workgroups: two
-    for (N, K, name) in [(5120, 13824, b"skinny_xr16_nt2_wk8_d2"), (8192, 28672, b"skinny_xr16_nt2_wk8_d2")]:
+    # wide layers where four tiles per wave would leave under 160 workgroups: two, unless
+    # K is long enough to split (K >= 12288: four tiles, K in slices)
+    for (N, K, name) in [(5120, 8192, b"skinny_xr16_nt2_wk8_d2"), (8192, 8192, b"skinny_xr16_nt2_wk8_d2"),
+                         (5120, 13824, b"skinny_xr16_nt4_wk4_d2"), (8192, 28672, b"skinny_xr16_nt4_wk4_d2")]:
         assert raw.w4a16_gemm_describe(16, N, K, 128, out) == 0
         assert raw.w4a16_gemm_variant_name(out[0]) == name
     # above 32 rows: the tiled kernel, except on layers under 32 Mi weights below 256 rows,

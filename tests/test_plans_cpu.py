@@ -70,6 +70,21 @@ def test_eight_wave_tiles_take_whole_rounds_where_the_tile_count_allows():
     assert w4.w4a16_workspace_bytes(4096, 10240, 8192) > 0
 
 
+@pytest.mark.parametrize("M,K,N,name,splits", [
+    # long K on layers with fewer than 160 blocks of 64 columns: four column tiles per
+    # wave and K cut into slices that keep one round of workgroups (128 x 2, 80 x 3)
+    (16, 28672, 8192, "skinny_xr16_nt4_wk4_d2", 2),
+    (32, 28672, 8192, "skinny_xr32_nt4_wk4_d2", 2), (16, 13824, 5120, "skinny_xr16_nt4_wk4_d2", 3),
+    (8, 13824, 5120, "skinny_xr8_nt4_wk4_d2", 3),
+    # at 8 rows on N = 8192 two tiles per wave already fill the chip: no split
+    (8, 28672, 8192, "skinny_xr8_nt2_wk8_d4", 1),
+    # K = 8192 keeps two tiles per wave over the whole K; one to four rows are unchanged
+    (16, 8192, 8192, "skinny_xr16_nt2_wk8_d2", 1), (1, 28672, 8192, "skinny_xr4_nt1_wk8_d2", 1),
+])
+def test_long_k_decode_plans_split_k(M, K, N, name, splits):
+    assert plan(M, N, K) == (name, splits)
+
+
 def test_k_split_only_where_workgroups_leave_most_of_the_chip_idle():
     # 4096 x 4096 at M = 1: 256 column tiles, no split; 3072 x 768 at M = 1: 48 workgroups,
     # no split either (the hand-off costs more); 4096 x 256: 16 workgroups, split

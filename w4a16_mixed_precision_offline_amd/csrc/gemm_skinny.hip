@@ -797,7 +797,25 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
       if (N / (16 * ntw) < 160) ntw = 2;
     }
     const int tiles = N / 16;
-    if (XR == 4 || (tiles < 128 && M <= 16)) {
+    // Long K on layers with too few 64-column blocks for one per compute unit (N = 5120,
+    // 8192 at K >= 12288): four column tiles per wave, four waves, and K cut into as many
+    // slices as keep the workgroups within one round.  Each wave then streams its tiles
+    // along half or a third of K, and the partial sums are few.  Graph-timed over 600
+    // calls: 1.08-1.28x faster than two tiles per wave over the whole K at 16-32 rows on
+    // 28672 x 8192 and 13824 x 5120, and at 8 rows (or on fp16 weights) where two tiles
+    // per wave leave compute units idle (N = 5120: 1.10x, fp16 1.31x); where they fill the
+    // chip (N = 8192) the unsplit plan is 4% (8 rows) and 11% (fp16) faster.  At K = 8192
+    // two tiles still win.
+    const bool fills2 = N / 32 >= 256;
+    const bool longsplit = wide && ntw == 2 && XR >= 8 && XR <= 32 && K / KBLK >= 96 &&
+                           (!fills2 || (XR >= 16 && mode != W_FP16));
+    if (longsplit) {
+      variant = find_variant(XR, 4, 4, 2);
+      if (splits <= 0) {
+        const long wgs = (long)((M + XR - 1) / XR) * (N / 64);
+        splits = (int)(256 / wgs < 1 ? 1 : 256 / wgs);
+      }
+    } else if (XR == 4 || (tiles < 128 && M <= 16)) {
       // one or two rows on a wide layer: eight waves per tile, two k-blocks in flight
       // each (5% faster than four waves with four at M = 1 on 4096 x 11008 / 12288);
       // narrower layers: eight waves, four k-blocks in flight (timed over graph replays:
@@ -869,7 +887,8 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
     // split K only when the workgroups would leave most of the chip idle: the hand-off
     // of the partial sums costs more than partly idle compute units (measured: 192
     // four-tile workgroups beat 384 split ones by 2x on 4096 x 12288; 48 workgroups on
-    // 3072 x 768 beat 144 split ones by 2.1x; no split won on any decode or small layer)
+    // 3072 x 768 beat 144 split ones by 2.1x; no split won on any other decode or small
+    // layer than the long-K ones above)
     const long base = (long)p->mblocks * p->nblocks;
     const long target = 256;
     long sp = base >= 32 ? 1 : (target + base - 1) / base;
