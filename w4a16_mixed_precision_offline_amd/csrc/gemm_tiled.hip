@@ -1161,13 +1161,17 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   }
   if ((long long)grid > (long long)T * Gk) grid = (int)(T * Gk);  // at least one unit each
   q.args.grid = grid;
-  // all but the last one or two rounds of tiles are data-parallel; the rest (between
-  // one and two rounds' worth) is striped.  Measured: striping only the remainder
-  // (shorter stripes, all ending together) was 3-5% slower on the 70B shapes.
+  // four-wave tiles: all but the last one or two rounds of tiles are data-parallel, the
+  // rest (between one and two rounds' worth) is striped; striping only the remainder
+  // (shorter stripes, all ending together) was 3-5% slower on the 70B shapes.  Eight-wave
+  // tiles: every full round is data-parallel and only the remainder is striped, which
+  // halves the fp32 pieces their larger tiles write and the second pass reads (measured
+  // 1.05x at M = 1024 and 1.04x at M = 4096 on 8192 x 10240, 1.02x at M = 1024 on
+  // 5120 x 13824, within 1% elsewhere).
   const long full = T / grid;
   long dp_tiles;
   if (T % grid == 0) dp_tiles = T;
-  else if (full >= 1) dp_tiles = (full - 1) * grid;
+  else if (full >= 1) dp_tiles = (v.NWV == 8 ? full : full - 1) * grid;
   else dp_tiles = 0;
   q.args.dp_rounds = (int)(dp_tiles / grid);
   const long sk_tiles = T - dp_tiles;
