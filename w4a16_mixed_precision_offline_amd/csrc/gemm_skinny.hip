@@ -154,7 +154,10 @@ __device__ __forceinline__ uint16_t out_bits(float v) {
   }
 }
 
-constexpr int XSTRIDE = 272;  // bytes per X row in the LDS tile (256 + 16 against bank conflicts)
+// bytes per X row in the LDS tile: 256 + 32, the smallest padding whose 16-byte fragment
+// reads (16 rows, one column of chunks) are free of bank conflicts on gfx950 (counted with
+// SQ_LDS_BANK_CONFLICT: 256 + 16 and 256 + 64 conflict, 256 + 32 reads 0)
+constexpr int XSTRIDE = 288;
 
 // 16-byte activation loads per k-block: one covers 4 rows x 256 bytes of fp16 / bf16, or
 // 8 rows x 128 bytes of fp8
@@ -619,13 +622,16 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   // (reuses the X tiles: wait until every wave is done with its tile)
   constexpr int NACC = NT * MT * 4;
   if (WK > 1) {
-    float4v* red = reinterpret_cast<float4v*>(lds);  // [wave-1][lane][t][mt]
+    // [wave-1][t][mt][lane]: the 64 lanes of one access write or read 1 KiB in a row,
+    // which spreads them over every bank (a [lane][t][mt] order puts the lanes NT*MT*16
+    // bytes apart: an 8-way bank conflict for NT*MT = 8)
+    float4v* red = reinterpret_cast<float4v*>(lds);
     __syncthreads();
     if (wave > 0) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) red[((wave - 1) * 64 + lane) * NT * MT + t * MT + mt] = acc[t][mt];
+        for (int mt = 0; mt < MT; ++mt) red[(((wave - 1) * NT + t) * MT + mt) * 64 + lane] = acc[t][mt];
     }
     __syncthreads();
     if (wave > 0) return;
@@ -634,7 +640,7 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] += red[((w - 1) * 64 + lane) * NT * MT + t * MT + mt];
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] += red[(((w - 1) * NT + t) * MT + mt) * 64 + lane];
   }
 
   // ---- split-K: coherent partial, arrival counter, last arriver sums in slice order ----
