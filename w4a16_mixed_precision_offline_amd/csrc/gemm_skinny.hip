@@ -154,10 +154,15 @@ __device__ __forceinline__ uint16_t out_bits(float v) {
   }
 }
 
-// bytes per X row in the LDS tile: 256 + 32, the smallest padding whose 16-byte fragment
-// reads (16 rows, one column of chunks) are free of bank conflicts on gfx950 (counted with
-// SQ_LDS_BANK_CONFLICT: 256 + 16 and 256 + 64 conflict, 256 + 32 reads 0)
-constexpr int XSTRIDE = 288;
+// bytes per X row in the LDS tile.  fp16 / bf16: 256 + 32, the smallest padding whose
+// 16-byte fragment reads (16 rows, one column of chunks) are free of bank conflicts on
+// gfx950 (counted with SQ_LDS_BANK_CONFLICT: 256 + 16, + 48 and + 64 conflict, + 32 reads
+// 0).  fp8 rows (128 bytes used): 256 + 16, which gives its 8-byte fragment reads a third
+// of the conflicts that 256 + 32 does.
+template <int MODE>
+__host__ __device__ constexpr int x_stride() {
+  return mode_fp8(MODE) ? 272 : 288;
+}
 
 // 16-byte activation loads per k-block: one covers 4 rows x 256 bytes of fp16 / bf16, or
 // 8 rows x 128 bytes of fp8
@@ -272,13 +277,13 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
     // scale applies in fp32 per block, for any number of column tiles.
 #pragma unroll
     for (int c = 0; c < x_loads(XR, MODE); ++c)
-      *reinterpret_cast<u32x4*>(xlds + (8 * c + (lane >> 3)) * XSTRIDE + (lane & 7) * 16) = S.x[c];
+      *reinterpret_cast<u32x4*>(xlds + (8 * c + (lane >> 3)) * x_stride<MODE>() + (lane & 7) * 16) = S.x[c];
     long a8[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        a8[mt][j] = *reinterpret_cast<const long*>(xlds + (mt * 16 + (lane & 15)) * XSTRIDE +
+        a8[mt][j] = *reinterpret_cast<const long*>(xlds + (mt * 16 + (lane & 15)) * x_stride<MODE>() +
                                                     32 * j + 8 * (lane >> 4));
     constexpr int SH = mode_g64(MODE) ? 2 : 1;  // scale / zero-point halves per block
 #pragma unroll
@@ -315,13 +320,13 @@ __device__ __forceinline__ void compute_stage(const Stage<XR, NT, MODE>& S,
   }
 #pragma unroll
   for (int c = 0; c < XR / 4; ++c)
-    *reinterpret_cast<u32x4*>(xlds + (4 * c + (lane >> 4)) * XSTRIDE + (lane & 15) * 16) = S.x[c];
+    *reinterpret_cast<u32x4*>(xlds + (4 * c + (lane >> 4)) * x_stride<MODE>() + (lane & 15) * 16) = S.x[c];
   half8 a[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      a[mt][j] = *reinterpret_cast<const half8*>(xlds + (mt * 16 + (lane & 15)) * XSTRIDE +
+      a[mt][j] = *reinterpret_cast<const half8*>(xlds + (mt * 16 + (lane & 15)) * x_stride<MODE>() +
                                                   64 * j + 16 * (lane >> 4));
   if (MODE == W_SP24) {
     // 2:4: W is the sparse A operand (lane: column 4(l/16)+r ... see the epilogue), X the
@@ -506,7 +511,7 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     int* __restrict__ counters, int M, int N, int K, int splits, int nblocks,
     const float* __restrict__ xscale) {
   constexpr int MT = (XR + 15) / 16;
-  constexpr int XTILE = MT * 16 * XSTRIDE;  // bytes of one wave's X tile
+  constexpr int XTILE = MT * 16 * x_stride<MODE>();  // bytes of one wave's X tile
   // per-wave X tiles; after the main loop the same memory holds the reduction
   static_assert((WK - 1) * 64 * NT * MT * 16 <= WK * XTILE, "reduction does not fit");
   __shared__ __attribute__((aligned(16))) char lds[WK * XTILE];
@@ -604,8 +609,8 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
   // rows XR..15 of the LDS tile are never written by the loads: keep them zero (after
   // the first loads are on their way)
   if (XR % 16 != 0) {
-    for (int i = lane; i < (16 - XR) * XSTRIDE / 16; i += 64)
-      *reinterpret_cast<u32x4*>(xlds + XR * XSTRIDE + 16 * i) = u32x4{0, 0, 0, 0};
+    for (int i = lane; i < (16 - XR) * x_stride<MODE>() / 16; i += 64)
+      *reinterpret_cast<u32x4*>(xlds + XR * x_stride<MODE>() + 16 * i) = u32x4{0, 0, 0, 0};
   }
   for (int i = 0; i < nk; i += D) {
 #pragma unroll
