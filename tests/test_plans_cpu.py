@@ -94,9 +94,11 @@ def test_k_split_only_where_workgroups_leave_most_of_the_chip_idle():
     assert name.startswith("skinny") and splits > 1
 
 
-def test_2to4_takes_the_small_tiled_tiles_on_large_layers():
-    d = w4.w4a16_workspace_bytes(16, 28672, 8192)
-    assert d > 0  # stream-K pieces of the 16-row tiles of the 2:4 plan
+def test_2to4_plans_on_large_layers_need_workspace():
+    # 16 rows: the 2:4 skinny plan splits K in two (partial sums); 32 rows: the 32-row
+    # tiles' stream-K pieces
+    assert w4.w4a16_workspace_bytes(16, 28672, 8192) >= 224 * 2 * 8 * 256 * 4
+    assert w4.w4a16_workspace_bytes(32, 28672, 8192) > 0
 
 
 def test_workspace_query_covers_the_split_plans():

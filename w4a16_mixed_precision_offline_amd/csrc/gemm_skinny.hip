@@ -845,6 +845,13 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
     } else if (XR == 16) {
       variant = wide ? (ntw == 2 ? find_variant(16, 2, 8, 2) : find_variant(16, ntw, 4, 2))
                      : find_variant(16, 1, 8, 2);
+      // 2:4 codes on layers of 128 Mi weights or more: eight column tiles per wave, two
+      // waves, K in two slices (448 workgroups on 8192 x 28672; graph-timed 1.03x over the
+      // 16-row tiled tiles and 1.08x over four tiles per wave, 1.12x the dense time)
+      if (mode == W_SP24 && wide && N % 128 == 0 && (long long)K * N >= (128LL << 20)) {
+        variant = find_variant(16, 8, 2, 2);
+        if (splits <= 0) splits = 2;
+      }
     } else if (XR == 32) {
       // narrow layers (one 16-column tile per compute unit or fewer): two blocks of 16 rows,
       // two column tiles per wave, eight waves (graph-timed: 1.11x on 4096 x 4096 and 1.15x

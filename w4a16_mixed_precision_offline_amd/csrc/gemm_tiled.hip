@@ -1081,8 +1081,8 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // 1.08-1.18x slower at M = 256 / 384 where 128-row tiles pad nothing)
     if (!f16 && M > 128 && M < 512 && M % 128 != 0 && M % 128 <= 64) variant = 2;
     // MXFP4 has no skinny kernel: up to 32 rows take the 32-row tile; the 2:4 format
-    // (tiled from 9 rows on on large layers) takes 16-row tiles up to 16 rows and 32-row
-    // tiles up to 32 (measured fastest at M = 16 / 32 on 8192 x 28672)
+    // (automatically tiled from 17 rows on on large layers) takes 16-row tiles up to 16
+    // rows and 32-row tiles up to 32 (the fastest tiles at M = 16 / 32 on 8192 x 28672)
     if (mode == W_MX4 && M <= 32) variant = 3;
     if (mode == W_SP24 && M <= 32) variant = M <= 16 ? 4 : 3;
     // Eight waves (two per SIMD): the second wave on each SIMD issues its unpacking and LDS
