@@ -95,9 +95,8 @@ def test_k_split_only_where_workgroups_leave_most_of_the_chip_idle():
 
 
 def test_2to4_plans_on_large_layers_need_workspace():
-    # 16 rows: the 2:4 skinny plan splits K in two (partial sums); 32 rows: the 32-row
-    # tiles' stream-K pieces
-    assert w4.w4a16_workspace_bytes(16, 28672, 8192) >= 224 * 2 * 8 * 256 * 4
+    # 32 rows: the 32-row tiles' stream-K pieces (16 rows: the 2:4 skinny plan reduces
+    # inside its workgroups; the dense plans' needs are covered by the query too)
     assert w4.w4a16_workspace_bytes(32, 28672, 8192) > 0
 
 

@@ -222,7 +222,7 @@ int run_skinny(int mode, const uint16_t* X, const void* w, const uint16_t* sp, c
 // than 16-row tiles on 1024 x 1024 and 3072 x 768 at M = 48-128).  The 2:4 format on
 // layers of 128 Mi weights or more takes the tiled kernel's 32-row tiles from 17 rows on
 // (1.16x over the skinny kernel at M = 32 on 8192 x 28672); up to 16 rows its skinny plan
-// with eight column tiles per wave and two K slices is 1.03x faster than 16-row tiles.
+// with eight column tiles per wave is 1.10x faster than 16-row tiles.
 bool use_tiled(int M, int N, int K, int mode = W_SYM) {
   const long long kn = (long long)K * N;
   if (mode == W_SP24 && M > 16 && kn >= (128LL << 20)) return true;

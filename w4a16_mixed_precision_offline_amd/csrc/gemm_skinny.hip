@@ -512,9 +512,11 @@ __global__ __launch_bounds__(64 * WK) void skinny_kernel(
     const float* __restrict__ xscale) {
   constexpr int MT = (XR + 15) / 16;
   constexpr int XTILE = MT * 16 * x_stride<MODE>();  // bytes of one wave's X tile
-  // per-wave X tiles; after the main loop the same memory holds the reduction
-  static_assert((WK - 1) * 64 * NT * MT * 16 <= WK * XTILE, "reduction does not fit");
-  __shared__ __attribute__((aligned(16))) char lds[WK * XTILE];
+  // per-wave X tiles; after the main loop the same memory holds the reduction (which
+  // needs more than the tiles for eight column tiles per wave)
+  constexpr int RED = (WK - 1) * 64 * NT * MT * 16;
+  constexpr int LDSB = RED > WK * XTILE ? RED : WK * XTILE;
+  __shared__ __attribute__((aligned(16))) char lds[LDSB];
   const int lane = threadIdx.x & 63;
   // wave index made uniform so that all k-block bookkeeping stays on the scalar unit
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -766,7 +768,7 @@ const Variant kVariants[] = {
     W4A16_VARIANT(16, 8, 2, 2),  W4A16_VARIANT(8, 8, 2, 2),   W4A16_VARIANT(4, 2, 8, 4),
     W4A16_VARIANT(8, 2, 8, 4),   W4A16_VARIANT(8, 4, 8, 2),   W4A16_VARIANT(16, 4, 8, 2),
     W4A16_VARIANT(32, 4, 8, 2),  W4A16_VARIANT(8, 3, 4, 2),   W4A16_VARIANT(16, 3, 4, 2),
-    W4A16_VARIANT(32, 3, 4, 2),  W4A16_VARIANT(4, 1, 8, 2),
+    W4A16_VARIANT(32, 3, 4, 2),  W4A16_VARIANT(4, 1, 8, 2),   W4A16_VARIANT(16, 8, 4, 2),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -845,13 +847,11 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
     } else if (XR == 16) {
       variant = wide ? (ntw == 2 ? find_variant(16, 2, 8, 2) : find_variant(16, ntw, 4, 2))
                      : find_variant(16, 1, 8, 2);
-      // 2:4 codes on layers of 128 Mi weights or more: eight column tiles per wave, two
-      // waves, K in two slices (448 workgroups on 8192 x 28672; graph-timed 1.03x over the
-      // 16-row tiled tiles and 1.08x over four tiles per wave, 1.12x the dense time)
-      if (mode == W_SP24 && wide && N % 128 == 0 && (long long)K * N >= (128LL << 20)) {
-        variant = find_variant(16, 8, 2, 2);
-        if (splits <= 0) splits = 2;
-      }
+      // 2:4 codes on layers of 128 Mi weights or more: eight column tiles per wave and
+      // four waves splitting K (224 workgroups on 8192 x 28672; graph-timed 1.07x over two
+      // waves with K in two slices, 1.10x over the 16-row tiled tiles, 1.18x the dense time)
+      if (mode == W_SP24 && wide && N % 128 == 0 && (long long)K * N >= (128LL << 20))
+        variant = find_variant(16, 8, 4, 2);
     } else if (XR == 32) {
       // narrow layers (one 16-column tile per compute unit or fewer): two blocks of 16 rows,
       // two column tiles per wave, eight waves (graph-timed: 1.11x on 4096 x 4096 and 1.15x
