@@ -852,6 +852,9 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
       // waves with K in two slices, 1.10x over the 16-row tiled tiles, 1.18x the dense time)
       if (mode == W_SP24 && wide && N % 128 == 0 && (long long)K * N >= (128LL << 20))
         variant = find_variant(16, 8, 4, 2);
+      // 2:4 codes on narrow layers: four waves with four k-blocks in flight (each k-block
+      // carries 3/4 of the dense bytes; 1.02-1.05x on 4096 x 4096 at M = 16)
+      if (mode == W_SP24 && !wide && tiles >= 128) variant = find_variant(16, 1, 4, 4);
     } else if (XR == 32) {
       // narrow layers (one 16-column tile per compute unit or fewer): two blocks of 16 rows,
       // two column tiles per wave, eight waves (graph-timed: 1.11x on 4096 x 4096 and 1.15x
@@ -860,6 +863,8 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
       variant = wide ? (ntw == 2 ? find_variant(32, 2, 8, 2) : find_variant(32, ntw, 4, 2))
                      : tiles < 128    ? find_variant(16, 1, 8, 2)
                      : (N % 32 == 0 ? find_variant(16, 2, 8, 2) : find_variant(32, 1, 4, 2));
+      // 2:4 codes there: four waves with four k-blocks in flight (1.02-1.03x on 4096 x 4096)
+      if (mode == W_SP24 && !wide && tiles >= 128 && N % 32 == 0) variant = find_variant(16, 2, 4, 4);
     } else {
       // above 32 rows (layers too small for the tiled kernel): blocks of 16 rows up to 64
       // rows, of 32 above, and the most column tiles per wave (4, 2, 1) that still give
