@@ -108,7 +108,7 @@ def test_describe_plans(raw):
     for (M, N, K, name) in [(48, 13824, 5120, b"tiled_bm64_bn128_s4"), (48, 768, 3072, b"skinny_xr16_nt1_wk8_d2"),
                             (48, 28672, 8192, b"tiled_bm64_bn256_s3"),
                             (128, 768, 3072, b"skinny_xr32_nt1_wk4_d2"),
-                            (128, 8192, 8192, b"tiled_bm128_bn128_s3"), (128, 8192, 28672, b"tiled_bm128_bn256_s3"), (48, 2560, 2560, b"skinny_xr16_nt2_wk8_d2"),
+                            (128, 8192, 8192, b"tiled_bm128_bn128_s3"), (128, 8192, 28672, b"tiled_bm128_bn256_w8_s3"), (48, 2560, 2560, b"skinny_xr16_nt2_wk8_d2"),
                             (128, 4096, 4096, b"skinny_xr32_nt4_wk4_d2"), (32, 28672, 8192, b"skinny_xr32_nt4_wk4_d2")]:
         assert raw.w4a16_gemm_describe(M, N, K, 128, out) == 0
         assert raw.w4a16_gemm_variant_name(out[0]) == name, (M, N, K)

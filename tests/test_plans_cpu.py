@@ -26,9 +26,12 @@ def plan(M, N, K, group=128):
     # ... 64 x 128 tiles on layers up to 128 Mi weights
     (48, 5120, 13824, "tiled_bm64_bn128_s4"), (64, 8192, 10240, "tiled_bm64_bn128_s4"),
     (48, 13824, 5120, "tiled_bm64_bn128_s4"),
-    # ... 128-row tiles above, except where they would pad M by more than an eighth
-    (128, 8192, 28672, "tiled_bm128_bn256_s3"), (192, 8192, 28672, "tiled_bm64_bn256_s3"),
-    (256, 28672, 8192, "tiled_bm128_bn256_s3"),
+    # ... 128-row tiles above, except where they would pad M by more than an eighth on
+    # layers under 128 Mi weights up to 384 rows; on larger layers with eight waves
+    (128, 8192, 28672, "tiled_bm128_bn256_w8_s3"), (192, 8192, 28672, "tiled_bm128_bn256_w8_s3"),
+    (256, 28672, 8192, "tiled_bm128_bn256_w8_s3"), (192, 8192, 10240, "tiled_bm64_bn256_s3"),
+    (320, 8192, 10240, "tiled_bm64_bn256_s3"), (448, 8192, 10240, "tiled_bm128_bn256_s3"),
+    (448, 8192, 28672, "tiled_bm128_bn512_w8_s2"),
     # from a full round of 128 x 256 tiles on (where the 128 x 512 ones below do not fit
     # the chip in whole rounds): the same tiles with eight waves
     (1024, 8192, 10240, "tiled_bm128_bn256_w8_s3"), (1024, 28672, 8192, "tiled_bm128_bn256_w8_s3"),

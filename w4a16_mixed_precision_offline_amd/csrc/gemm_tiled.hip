@@ -1076,10 +1076,18 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     if (variant == 2 && (mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64) &&
         (long long)K * N <= (128LL << 20))
       variant = 8;
+    const bool dense16 = mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64;
+    const bool large = (long long)K * N >= (128LL << 20);
     // 128-row tiles would pad M by more than an eighth (M % 128 in 1..64, M < 512): 64-row
     // tiles instead (measured 1.05-1.26x faster at M = 192 on six 7B/70B-class layers, and
-    // 1.08-1.18x slower at M = 256 / 384 where 128-row tiles pad nothing)
-    if (!f16 && M > 128 && M < 512 && M % 128 != 0 && M % 128 <= 64) variant = 2;
+    // 1.08-1.18x slower at M = 256 / 384 where 128-row tiles pad nothing), except for the
+    // packed formats with fp16 activations on layers of 128 Mi weights or more from 129
+    // rows on, and on every layer above 384 rows, where the eight-wave 128-row tiles below
+    // win despite the padding (1.05-1.26x at M = 160-448 on 8192 x 28672 and 28672 x 8192,
+    // 1.10x at M = 448 on 8192 x 10240)
+    if (!f16 && M > 128 && M < 512 && M % 128 != 0 && M % 128 <= 64 &&
+        !(dense16 && (large || M > 384)))
+      variant = 2;
     // MXFP4 has no skinny kernel: up to 32 rows take the 32-row tile; the 2:4 format
     // (automatically tiled from 17 rows on on large layers) takes 16-row tiles up to 16
     // rows and 32-row tiles up to 32 (the fastest tiles at M = 16 / 32 on 8192 x 28672)
@@ -1094,21 +1102,21 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // rounds of 224 workgroups: 1.10x, where 256 workgroups and stream-K stripes were 0.96x;
     // 0.88-0.93x at M = 256.  Otherwise, from one full round of 128 x 256 tiles on, the
     // same tiles with eight waves (32 columns each): 1.04x at M = 1024 on 28672 x 8192,
-    // 1.01-1.03x on 8192 x 10240.
+    // 1.01-1.03x on 8192 x 10240; on layers of 128 Mi weights or more also below a full
+    // round (1.01-1.05x at M = 128-256 on 8192 x 28672 and 28672 x 8192).
     // MXFP4: 128 x 512 tiles in whole rounds only (1.04-1.18x at M = 1024 / 4096 on the
     // 235 Mi-weight layers; with stream-K stripes 0.86-0.93x), else 128 x 256 with eight
     // waves from a full round on (1.06x at M = 1024 and 4096 on 8192 x 10240).
     // fp8 activations (INT4 codes): no 128 x 512 eight-wave tiles (they spill); 128 x 256
     // with eight waves where those tiles make whole rounds of 256 (1.01-1.04x at M = 4096;
     // 0.90-0.93x at M = 1024 on 8192 x 28672 with its 896 tiles as four rounds of 224).
-    const bool dense16 = mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64;
     const bool int4fp8 = mode == W_SYM8 || mode == W_ASYM8;
     if (variant == 0 && (dense16 || int4fp8 || mode == W_MX4)) {
       const long long t8 = (long long)((M + 127) / 128) * ((N + 511) / 512);
       const long long t4 = (long long)((M + 127) / 128) * ((N + 255) / 256);
       if ((dense16 && (t8 >= 512 || dp_grid(t8) > 0)) || (mode == W_MX4 && dp_grid(t8) > 0))
         variant = 6;
-      else if ((!int4fp8 && t4 >= 256) || (int4fp8 && t4 % 256 == 0))
+      else if ((!int4fp8 && t4 >= 256) || (int4fp8 && t4 % 256 == 0) || (dense16 && large))
         variant = 7;
     }
     if (!f16) {
