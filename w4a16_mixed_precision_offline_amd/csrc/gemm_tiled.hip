@@ -1064,20 +1064,21 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   // 64 rows, 64 x 128 up to 64.
   if (variant < 0) {
     variant = M > 64 ? 0 : (f16 ? 1 : 2);
+    const bool dense16 = mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64;
+    const bool int4fp8 = mode == W_SYM8 || mode == W_ASYM8;
+    const bool large = (long long)K * N >= (128LL << 20);
     // layers up to 128 Mi weights at 65-256 rows: 128 x 128 tiles, twice the tiles of
     // 128 x 256 for the 256 compute units (measured 1.04-1.14x at M = 128 and 1.02-1.06x at
     // M = 256 on 8192 x 10240, 5120 x 13824, 13824 x 5120, 4096 x 11008; slower on the
-    // 235 Mi-weight layers and at M >= 1024)
-    if (!f16 && mode != W_SP24 && M > 64 && M <= 256 && (long long)K * N <= (128LL << 20))
+    // 235 Mi-weight layers and at M >= 1024; with fp8 activations 0.88x at M = 256 on
+    // 8192 x 10240, so those keep 128 x 256)
+    if (!f16 && mode != W_SP24 && !int4fp8 && M > 64 && M <= 256 &&
+        (long long)K * N <= (128LL << 20))
       variant = 5;
     // 33-64 rows on layers up to 128 Mi weights: 64 x 128 tiles, four k-blocks deep
     // (measured 1.04-1.09x over 64 x 256 at M = 48 and 64 on 8192 x 10240, 5120 x 13824
     // and 13824 x 5120; slower on the 235 Mi-weight layers)
-    if (variant == 2 && (mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64) &&
-        (long long)K * N <= (128LL << 20))
-      variant = 8;
-    const bool dense16 = mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64;
-    const bool large = (long long)K * N >= (128LL << 20);
+    if (variant == 2 && dense16 && (long long)K * N <= (128LL << 20)) variant = 8;
     // 128-row tiles would pad M by more than an eighth (M % 128 in 1..64, M < 512): 64-row
     // tiles instead (measured 1.05-1.26x faster at M = 192 on six 7B/70B-class layers, and
     // 1.08-1.18x slower at M = 256 / 384 where 128-row tiles pad nothing), except for the
@@ -1085,9 +1086,15 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // rows on, and on every layer above 384 rows, where the eight-wave 128-row tiles below
     // win despite the padding (1.05-1.26x at M = 160-448 on 8192 x 28672 and 28672 x 8192,
     // 1.10x at M = 448 on 8192 x 10240)
+    // (MXFP4 and the 2:4 format keep 128-row tiles there on layers of 128 Mi weights or
+    // more: 1.25-1.45x and 1.02-1.14x at M = 192 on 8192 x 28672 and 28672 x 8192)
     if (!f16 && M > 128 && M < 512 && M % 128 != 0 && M % 128 <= 64 &&
-        !(dense16 && (large || M > 384)))
+        !(dense16 && (large || M > 384)) && !((mode == W_MX4 || mode == W_SP24) && large))
       variant = 2;
+    // MXFP4 takes the 64-row tiles as 64 x 128 up to 256 rows on every layer (1.08-1.21x
+    // at M = 48-64 on the three 70B-class layers, 1.10x at M = 192 on 8192 x 10240; at
+    // M = 320 there the 200 tiles of 64 x 256 in one round are 1.28x faster)
+    if (variant == 2 && mode == W_MX4 && M <= 256) variant = 8;
     // MXFP4 has no skinny kernel: up to 32 rows take the 32-row tile; the 2:4 format
     // (automatically tiled from 17 rows on on large layers) takes 16-row tiles up to 16
     // rows and 32-row tiles up to 32 (the fastest tiles at M = 16 / 32 on 8192 x 28672)
@@ -1109,14 +1116,15 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // waves from a full round on (1.06x at M = 1024 and 4096 on 8192 x 10240).
     // fp8 activations (INT4 codes): no 128 x 512 eight-wave tiles (they spill); 128 x 256
     // with eight waves where those tiles make whole rounds of 256 (1.01-1.04x at M = 4096;
-    // 0.90-0.93x at M = 1024 on 8192 x 28672 with its 896 tiles as four rounds of 224).
-    const bool int4fp8 = mode == W_SYM8 || mode == W_ASYM8;
+    // 0.90-0.93x at M = 1024 on 8192 x 28672 with its 896 tiles as four rounds of 224), or
+    // number 200-511 (1.04x at M = 256 on 8192 x 28672 and at M = 1024 on 8192 x 10240).
     if (variant == 0 && (dense16 || int4fp8 || mode == W_MX4)) {
       const long long t8 = (long long)((M + 127) / 128) * ((N + 511) / 512);
       const long long t4 = (long long)((M + 127) / 128) * ((N + 255) / 256);
       if ((dense16 && (t8 >= 512 || dp_grid(t8) > 0)) || (mode == W_MX4 && dp_grid(t8) > 0))
         variant = 6;
-      else if ((!int4fp8 && t4 >= 256) || (int4fp8 && t4 % 256 == 0) || (dense16 && large))
+      else if ((!int4fp8 && t4 >= 256) || (dense16 && large) ||
+               (int4fp8 && (t4 % 256 == 0 || (t4 >= 200 && t4 < 512))))
         variant = 7;
     }
     if (!f16) {
