@@ -820,8 +820,22 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
     // chip (N = 8192) the unsplit plan is 4% (8 rows) and 11% (fp16) faster.  At K = 8192
     // two tiles still win.
     const bool fills2 = N / 32 >= 256;
-    const bool longsplit = wide && ntw == 2 && XR >= 8 && XR <= 32 && K / KBLK >= 96 &&
-                           (!fills2 || (XR >= 16 && mode != W_FP16));
+    const bool longk_split = wide && ntw == 2 && XR >= 8 && XR <= 32 && K / KBLK >= 96 &&
+                             (!fills2 || (XR >= 16 && mode != W_FP16));
+    // fp8 activations at 5-32 rows (16-32 rows only on layers under 1024 column tiles):
+    // one column tile per wave.  They rescale every (column tile, row tile) partial in fp32 per k-block, so
+    // several tiles per wave only lengthen a wave's chain, and their 1-byte activations
+    // leave little to share (graph-timed 1.06-1.47x faster than three or four tiles per
+    // wave at M = 8-32 on 4096 x 12288, 4096 x 11008 and 8192 x 10240, and 1.02-1.18x at
+    // M = 8-16 than the long-K split on 13824 x 5120; one 32-row block 1.02-1.03x
+    // faster than two 16-row blocks on 4096 x 4096 and 11008 x 4096; 1.12x at M = 8 on
+    // 8192 x 28672).  Above 8 rows the 1792 tiles of 8192 x 28672 keep four tiles per wave
+    // (0.88-0.98x with one at M = 16-32), 32 rows keep the long-K split (0.93-0.96x with
+    // one tile), and layers of 8192 columns keep their two tiles per wave (0.88-0.99x with
+    // one at M = 8-32 on 8192 x 8192 and 28672 x 8192).
+    const bool fp8_one = mode_fp8(mode) && XR >= 8 && XR <= 32 && (tiles < 1024 || XR == 8) &&
+                         !(XR == 32 && longk_split) && !(wide && ntw == 2 && fills2);
+    const bool longsplit = longk_split && !fp8_one;
     if (longsplit) {
       variant = find_variant(XR, 4, 4, 2);
       if (splits <= 0) {
@@ -882,6 +896,11 @@ int skinny_make_plan(int M, int N, int K, int group, int mode, int variant, int 
       }
       variant = nt == 4 ? find_variant(xr, 4, 4, 2)
                         : (xr == 16 ? find_variant(16, nt, 8, 2) : find_variant(32, nt, 4, 2));
+    }
+    if (fp8_one) {
+      if (XR == 8 && wide) variant = find_variant(8, 1, 4, 4);
+      if (XR == 16 && wide) variant = find_variant(16, 1, 8, 2);
+      if (XR == 32) variant = wide ? find_variant(32, 1, 4, 2) : find_variant(32, 1, 8, 2);
     }
   }
   if (variant < 0 || variant >= kNumVariants) return -8;
