@@ -1174,6 +1174,14 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
     // at M = 256 on 8192 x 28672 with 224 tiles, 1.07x at M = 128 on 8192 x 28672 with
     // 128 x 128 tiles, 1.12x at M = 256 on 5120 x 13824 with 216 tiles)
     if (T >= 200 && T < 256 && grid == 256) grid = (int)T;
+    // fewer tiles than that: k = 256 / T workgroups per tile when they cut every tile into
+    // k equal whole-k-block pieces and still fill 200-256 compute units (1.04-1.10x for the
+    // zero-point layers of 5120 x 13824 and 13824 x 5120 at M = 48 / 128, 1.06x for the
+    // 2:4 32-row tiles and 1.04x at M = 128 on 8192 x 28672; with fp8 activations 0.95x)
+    if (T < 200 && grid == 256 && mode != W_SYM8 && mode != W_ASYM8) {
+      const long k = 256 / T;
+      if (T * k >= 200 && Gk % k == 0) grid = (int)(T * k);
+    }
   }
   if ((long long)grid > (long long)T * Gk) grid = (int)(T * Gk);  // at least one unit each
   q.args.grid = grid;
