@@ -655,12 +655,15 @@ int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint
 // ---- MXFP4 weights x fp8 activations: scales applied inside the matrix instruction ----
 // decode kernel taken by the automatic plan at M <= 32 (index among the decode variants:
 // 1, 2 or 4 column tiles per workgroup).  Measured on the 7B/70B-class layers: one tile
-// (the most workgroups) is best or within 6% at M <= 8 and wherever N <= 4096; at M = 9-32
-// more columns per workgroup cut the re-reads of X from L2: two tiles for N <= 8192 (512
-// tiles), four above (1.1-1.4x over one tile on 4096 x 12288, 8192 x 10240, 8192 x 28672).
+// (the most workgroups) is best or within 6% at M <= 8 and wherever N <= 4096, except at
+// 2-8 rows on layers of more than 1024 column tiles (8192 x 28672: four tiles 1.14x faster
+// at M = 8); at M = 9-32 more columns per workgroup cut the re-reads of X from L2: two
+// tiles for N <= 8192 (512 tiles), four above (1.1-1.4x over one tile on 4096 x 12288,
+// 8192 x 10240, 8192 x 28672).
 static int mx_decode_default(int M, int N) {
   const int tiles = N / 16;
-  if (M <= 8 || tiles <= 256) return 0;
+  if (M <= 8) return M > 1 && tiles > 1024 ? 2 : 0;
+  if (tiles <= 256) return 0;
   return tiles <= 512 ? 1 : 2;
 }
 
