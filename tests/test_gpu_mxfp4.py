@@ -165,7 +165,8 @@ def test_row_scales_and_no_row_scales(gh):
 
 @pytest.mark.parametrize("M,K,N", [(1, 8192, 10240), (16, 8192, 28672), (32, 8192, 10240),
                                    (24, 28672, 8192), (256, 8192, 10240), (1024, 28672, 8192),
-                                   (4096, 8192, 10240)])
+                                   (4096, 8192, 10240), (8, 8192, 28672), (64, 8192, 28672),
+                                   (192, 28672, 8192), (192, 8192, 10240)])
 def test_full_size_layers_sampled(gh, M, K, N):
     """70B-class layers at decode and prefill sizes, in the launch configuration the
     benchmark times; rows and columns sampled (first, last and random) against the oracle."""

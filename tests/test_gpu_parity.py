@@ -233,6 +233,35 @@ def test_configs_full_size(gh, cfg):
         assert ok, (w.name, info)
 
 
+# automatic plans at the boundaries of their rules, full 70B-class / configuration-3 sizes:
+# 128-row eight-wave tiles at padded row counts (192, 448) and below a full round with two
+# pieces per tile (128), 128 x 512 tiles in two rounds of 224 (448), k workgroups per tile on
+# a zero-point layer (48, 128 on 13824 x 5120), and the long-K split of the decode kernel (16)
+BOUNDARY = [(192, 8192, 28672, False), (448, 8192, 28672, False), (448, 28672, 8192, False),
+            (128, 8192, 28672, False), (48, 13824, 5120, True), (128, 13824, 5120, True),
+            (16, 28672, 8192, False), (320, 8192, 10240, False)]
+
+
+@pytest.mark.parametrize("M,K,N,asym", BOUNDARY)
+def test_automatic_plans_at_rule_boundaries(gh, M, K, N, asym):
+    """NaN-prefilled Y must come back finite everywhere, and match the oracle on one row
+    per 16-row tile x one column per 16-column tile (every tile and stream-K piece); a
+    second launch repeats the bits."""
+    _, d, X = _case(M, K, N, asym, s_lo=0.001, s_hi=0.01)
+    packed = gh.repack(d, K, N)
+    Xd = gh.dev(X)
+    Yd = gh.nan_filled(M, N)
+    gh.gemm(Xd, packed, M, N, K, Y=Yd)
+    Y = gh.host(Yd)
+    assert np.all(np.isfinite(Y)), (M, K, N)
+    rows, cols = gh.tile_samples(M, N)
+    ok, info = _accept(Y, X, d, rows=rows, cols=cols)
+    assert ok, (M, K, N, info)
+    Y2 = gh.nan_filled(M, N)
+    gh.gemm(Xd, packed, M, N, K, Y=Y2)
+    assert np.array_equal(gh.host(Y2).view(np.uint16), Y.view(np.uint16))
+
+
 def test_determinism_and_guards(gh):
     import torch
     M, K, N = 16, 4096, 4096

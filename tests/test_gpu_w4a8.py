@@ -174,7 +174,8 @@ def test_w4a8_config_shapes(gh, cfg):
         assert ok, (w.name, info)
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 8192, 28672), (256, 8192, 10240), (64, 28672, 8192)])
+@pytest.mark.parametrize("M,K,N", [(16, 8192, 28672), (256, 8192, 10240), (64, 28672, 8192),
+                                   (8, 8192, 28672), (1024, 8192, 10240)])
 def test_w4a8_large_layers(gh, M, K, N):
     """70B-class layer shapes (several 64-row blocks at M = 256), sampled outputs."""
     w = Workload(cfg=2, M=M, K=K, N=N, s_lo=0.001, s_hi=0.01)
