@@ -982,6 +982,184 @@ def build_line(h, steps, warmup, traffic, cpu, base, decode):
     }
 
 
+SMALL_LAUNCHES = 24  # eager launches per case of --profile-small
+SMALL_MD = os.path.join(ROOT, "profiles", "small_layers_and_2to4_counters.md")
+SMALL_SQ = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_VALU_MFMA_BUSY_CYCLES "
+            "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE")
+
+
+def small_cases():
+    """Configuration 0 (tiny), every run of configuration 3 (zero-points, awkward shapes)
+    and configuration 4 with the dense and the 2:4 kernel on the same pruned weights."""
+    from gen import config_runs
+    out = [(w, "dense") for w in config_runs(0)] + [(w, "dense") for w in config_runs(3)]
+    for w in config_runs(4):
+        out += [(w, "dense"), (w, "2:4")]
+    return out
+
+
+def profile_small(w4, torch, group=128):
+    """--profile-small: SMALL_LAUNCHES eager launches of each case of small_cases(), one
+    case after the other, weights rotated over copies of at least 512 MiB; for rocprofv3
+    traces and counters, which --small-summary splits back into the cases by dispatch
+    order.  Prints the case list as the last stdout line."""
+    from gen import activations, weights
+    rot = 512 << 20
+    cases, cache = [], {}
+    for w, kind in small_cases():
+        K, N, M = w.K, w.N, w.M
+        key = (w.cfg, K, N)
+        if key not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            d = weights(w)
+            q = torch.from_numpy(d["Qp"]).cuda()
+            s = torch.from_numpy(d["s"]).cuda()
+            z = torch.from_numpy(d["Zp"]).cuda() if d["Zp"] is not None else None
+            dense = w4.alloc_packed(K, N, group, z is not None)
+            w4.w4a16_repack(q, s, z, *dense, K, N, group)
+            nd = max(2, -(-rot // (K * N // 2)))
+            ent = dict(dense=[dense] + [tuple(t.clone() if t is not None else None for t in dense)
+                                        for _ in range(nd - 1)])
+            if w.sparse24:
+                sp = w4.alloc_sparse24(K, N, group)
+                w4.w4a16_sparse24_repack(q, s, *sp, K, N, group)
+                ns = max(2, -(-rot // (K * N // 4 + K * N // 8)))
+                ent["2:4"] = [sp] + [tuple(t.clone() for t in sp) for _ in range(ns - 1)]
+            cache[key] = ent
+            del q, s, z
+        X = torch.from_numpy(activations(w)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        if kind == "dense":
+            calls = [lambda c=c: w4.w4a16_gemm(X, c[0], c[1], c[2], Y, M, N, K, group)
+                     for c in cache[key]["dense"]]
+        else:
+            calls = [lambda c=c: w4.w4a16_sparse24_gemm(X, c[0], c[1], c[2], Y, M, N, K, group)
+                     for c in cache[key]["2:4"]]
+        for i in range(SMALL_LAUNCHES):
+            calls[i % len(calls)]()
+        torch.cuda.synchronize()
+        cases.append(dict(cfg=w.cfg, K=K, N=N, M=M, kind=kind, zero_points=w.asym))
+    print(json.dumps(dict(profile_small=cases, launches=SMALL_LAUNCHES)), flush=True)
+
+
+def small_summary(cases_path, trace_csv, sq_csv, fetch_csv, write_csv):
+    """Per-case figures of a --profile-small run: kernel and duration per call from the
+    kernel trace (the stream-K second pass counted in), HBM traffic from FETCH_SIZE /
+    WRITE_SIZE scaled by a plain 256 MiB copy in the same run, and SQ counters.  The
+    GEMM dispatches are assigned to the cases in order, SMALL_LAUNCHES each; a second-pass
+    dispatch belongs to the call before it.  Writes SMALL_MD."""
+    import csv
+    import re
+    info = None
+    for ln in open(cases_path):
+        if ln.startswith('{"profile_small"'):
+            info = json.loads(ln)
+    if info is None:
+        raise SystemExit(f"{cases_path}: no profile_small line")
+    cases, L = info["profile_small"], info["launches"]
+
+    def is_main(n):
+        return "skinny_kernel" in n or "tiled_kernel<" in n
+
+    def assign(disp):
+        """disp: [(name, value)] in dispatch order -> per case [main values], [fixup values]."""
+        per = [([], [], []) for _ in cases]
+        c, n = 0, 0
+        for name, v in disp:
+            if is_main(name):
+                if n == L:
+                    c, n = c + 1, 0
+                per[c][0].append(v)
+                per[c][2].append(name)
+                n += 1
+            elif "tiled_fixup_kernel" in name and n > 0:
+                per[c][1].append(v)
+        if c != len(cases) - 1 or n != L:
+            raise SystemExit(f"dispatches do not split into {len(cases)} cases of {L}")
+        return per
+
+    def counters(path):
+        by = {}
+        for r in csv.DictReader(open(path)):
+            d = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return [by[k] for k in sorted(by)]
+
+    trace = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"]))
+    tper = assign([(r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                   for r in trace])
+    sq = counters(sq_csv)
+    sper = assign([(d["name"], d) for d in sq])
+    traffic = []
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        disp = counters(path)
+        cop = sorted(d[counter] for d in disp if "copyBuffer" in d["name"] and counter in d)[-3:]
+        factor = (COPY_BYTES / 1024.0) / (sum(cop) / len(cop))
+        traffic.append((assign([(d["name"], d.get(counter, 0.0)) for d in disp]), factor))
+    rows = []
+    for i, cs in enumerate(cases):
+        M, K, N = cs["M"], cs["K"], cs["N"]
+        main_t, fix_t, names = tper[i]
+        t_us = (sum(main_t) + sum(fix_t)) / L
+        m = re.search(r"(skinny_kernel|tiled_kernel)<([^>]*)>", names[0])
+        kern = f"{m.group(1)}<{m.group(2)}>" if m else names[0][:40]
+        wb, ab, fl = algorithmic(M, K, N)
+        if cs["zero_points"]:
+            ab += K * N // 256
+        if cs["kind"] == "2:4":
+            ab += K * N // 4 + K * N // 8 - K * N // 2
+        hbm = 0.0
+        for per, factor in traffic:
+            hbm += (sum(per[i][0]) + sum(per[i][1])) / L * factor * 1024.0
+        sm = sper[i][0]
+
+        def avg(c):
+            return sum(d.get(c, 0.0) for d in sm) / len(sm)
+        grbm = avg("GRBM_GUI_ACTIVE") / 8
+        rows.append(dict(cfg=cs["cfg"], shape=f"{K}x{N}", M=M, kind=cs["kind"], kernel=kern,
+                         us=round(t_us, 2),
+                         fixup_share=round(sum(fix_t) / L / t_us, 3) if fix_t else 0.0,
+                         alg_frac=round(ab / (t_us * 1e-6) / (HBM_PEAK_GBPS * 1e9), 3),
+                         traffic_ratio=round(hbm / ab, 3), waves=int(avg("SQ_WAVES")),
+                         mfma_busy=round(avg("SQ_VALU_MFMA_BUSY_CYCLES") / 1024 / grbm, 3) if grbm else 0,
+                         valu_k=round(avg("SQ_INSTS_VALU") / 1e3, 1),
+                         lds_conflict_k=round(avg("SQ_LDS_BANK_CONFLICT") / 1e3, 1)))
+    cmds = [f"rocprofv3 --kernel-trace --stats -d {os.path.dirname(trace_csv)} -o run --output-format csv "
+            "-- python -u bench.py --profile-small",
+            f"rocprofv3 --pmc {SMALL_SQ} -d {os.path.dirname(sq_csv)} -o run --output-format csv "
+            "-- python -u bench.py --profile-small"]
+    cmds += [f"rocprofv3 --pmc {c} -d {os.path.dirname(p_)} -o run --output-format csv -- python -u "
+             "bench.py --profile-small --copy-calibration"
+             for c, p_ in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv))]
+    cmds.append(f"python bench.py --small-summary <the last stdout line of the trace run, as a file> "
+                f"{trace_csv} {sq_csv} {fetch_csv} {write_csv}")
+    md = ["# Small and awkward layers (configurations 0 and 3) and 2:4 against dense "
+          "(configuration 4): kernel trace and counters", "",
+          "Commands (repository root, one MI355X; each counter pass in its own run):", "", "```",
+          *cmds, "```", "",
+          f"Each case runs {L} eager launches of the automatic plan (weights rotated over copies of "
+          "at least 512 MiB); the figures are means per call. `us`: kernel duration from the "
+          "trace, the stream-K second pass included (`2nd pass`: its share). `HBM frac`: "
+          "algorithmic bytes (codes, scales, zero-points, X and Y) / duration / 8 TB/s. "
+          "`traffic`: FETCH_SIZE and WRITE_SIZE of the call, scaled by a plain 256 MiB copy in "
+          f"the same runs (factors {traffic[0][1]:.4f} and {traffic[1][1]:.4f}), over the "
+          "algorithmic bytes. `MFMA busy`: SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over "
+          "GRBM_GUI_ACTIVE / 8 XCDs. `VALU`: SQ_INSTS_VALU per call (thousands, MFMA "
+          "included). `LDS conflicts`: SQ_LDS_BANK_CONFLICT cycles per call (thousands). "
+          "Counter runs serialize dispatches, so durations come from the trace run only.", "",
+          "| cfg | layer | M | weights | kernel | us | 2nd pass | HBM frac | traffic | waves | "
+          "MFMA busy | VALU (k) | LDS conflicts (k) |",
+          "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append(f"| {r['cfg']} | {r['shape']} | {r['M']} | {r['kind']} | `{r['kernel']}` | {r['us']} | "
+                  f"{r['fixup_share']} | {r['alg_frac']} | {r['traffic_ratio']} | {r['waves']} | "
+                  f"{r['mfma_busy']} | {r['valu_k']} | {r['lds_conflict_k']} |")
+    with open(SMALL_MD, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(rows))
+
+
 def copy_calibration(torch):
     """Three plain device copies of COPY_BYTES: the known-size traffic that scales the
     FETCH_SIZE / WRITE_SIZE counters of the same run."""
@@ -1011,6 +1189,12 @@ def main():
                     help="only a short W4A16 / W4A8 tiled-kernel workload (for counter runs)")
     ap.add_argument("--only-mxfp4", action="store_true",
                     help="only the MXFP4 leg (for a kernel trace of its kernels)")
+    ap.add_argument("--profile-small", action="store_true",
+                    help="configurations 0, 3 and 4 (dense and 2:4), a fixed number of eager "
+                         "launches each, for rocprofv3 traces and counters")
+    ap.add_argument("--small-summary", nargs=5,
+                    metavar=("CASES", "TRACE_CSV", "SQ_CSV", "FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="summarize the rocprofv3 runs of --profile-small into profiles/ and exit")
     ap.add_argument("--only-decode", action="store_true",
                     help="only the decode-sweep leg (for counter runs of the skinny kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -1032,6 +1216,9 @@ def main():
     if args.trace_summary:
         trace_summary(*args.trace_summary, kind=args.trace_kind)
         return
+    if args.small_summary:
+        small_summary(*args.small_summary)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1050,6 +1237,11 @@ def main():
         return
     if args.only_mxfp4:
         print(json.dumps(dict(mxfp4_in_mfma_dequant=mxfp4_leg(w4, torch))), flush=True)
+        return
+    if args.profile_small:
+        if args.copy_calibration:
+            copy_calibration(torch)
+        profile_small(w4, torch)
         return
     if args.only_decode:
         if args.copy_calibration:

@@ -113,3 +113,57 @@ def test_the_bench_line_is_compact_and_complete():
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert line["value"] == round(6.05e12 / 5e-3 / 1e12, 2) and line["unit"] == "TFLOP/s"
     assert "workload" in line["config"] and line["dtype"] == "fp16"
+
+
+def test_small_summary_splits_the_dispatches_into_the_cases(tmp_path, monkeypatch):
+    """--small-summary: GEMM dispatches go to the cases in order, `launches` each; a
+    second-pass dispatch belongs to the call before it; other kernels (repack, copies) are
+    skipped; durations come from the trace, bytes are scaled by the copy calibration."""
+    sys.path.insert(0, ROOT)
+    import bench
+    md = tmp_path / "small.md"
+    monkeypatch.setattr(bench, "SMALL_MD", str(md))
+    cases = tmp_path / "cases.json"
+    cases.write_text("noise\n" + json.dumps(dict(
+        profile_small=[dict(cfg=3, K=1024, N=512, M=1, kind="dense", zero_points=True),
+                       dict(cfg=4, K=2048, N=1024, M=64, kind="2:4", zero_points=False)],
+        launches=2)) + "\n")
+    sk = "void w4a16::(anonymous namespace)::skinny_kernel<4, 1, 8, 2, 1>(...)"
+    tk = "void w4a16::(anonymous namespace)::tiled_kernel<4, 4, 3, 3, 4>(...)"
+    fx = "void w4a16::(anonymous namespace)::tiled_fixup_kernel<4, 4, 4>(...)"
+    rp = "void w4a16::(anonymous namespace)::repack_all_kernel(...)"
+    trace = tmp_path / "t.csv"
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
+                                          "End_Timestamp"])
+        w.writeheader()
+        for d, name, ns in [(1, rp, 5000), (2, sk, 3000), (3, sk, 5000), (4, rp, 9000),
+                            (5, tk, 10000), (6, fx, 2000), (7, tk, 12000), (8, fx, 4000)]:
+            w.writerow(dict(Dispatch_Id=d, Kernel_Name=name, Start_Timestamp=100, End_Timestamp=100 + ns))
+    copy_kib = (256 << 20) / 1024.0
+    seq = [(1, rp), (2, sk), (3, sk), (4, rp), (5, tk), (6, fx), (7, tk), (8, fx)]
+    fetch, write, sq = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "s.csv"
+    _write(fetch, "FETCH_SIZE", [(10, "copyBuffer", copy_kib / 2)] * 1 +
+           [(11, "copyBuffer", copy_kib / 2), (12, "copyBuffer", copy_kib / 2)] +
+           [(d, n, 100.0 if n != fx else 50.0) for d, n in seq])
+    _write(write, "WRITE_SIZE", [(10, "copyBuffer", copy_kib), (11, "copyBuffer", copy_kib),
+                                 (12, "copyBuffer", copy_kib)] + [(d, n, 10.0) for d, n in seq])
+    rows = []
+    for d, n in seq:
+        rows += [(d, n, "SQ_WAVES", 64.0), (d, n, "GRBM_GUI_ACTIVE", 8000.0),
+                 (d, n, "SQ_VALU_MFMA_BUSY_CYCLES", 512000.0), (d, n, "SQ_INSTS_VALU", 2000.0),
+                 (d, n, "SQ_LDS_BANK_CONFLICT", 0.0)]
+    with open(sq, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for d, n, c, v in rows:
+            w.writerow(dict(Dispatch_Id=d, Kernel_Name=n, Counter_Name=c, Counter_Value=v))
+    bench.small_summary(str(cases), str(trace), str(sq), str(fetch), str(write))
+    text = md.read_text()
+    assert "`skinny_kernel<4, 1, 8, 2, 1>` | 4.0 | 0.0 |" in text      # (3 + 5) / 2 us
+    assert "`tiled_kernel<4, 4, 3, 3, 4>` | 14.0 | 0.214 |" in text    # (10 + 2 + 12 + 4) / 2 us
+    # traffic: fetch x2 (half the copy read), write x1; tiled call = kernel + second pass
+    wb, ab, _ = bench.algorithmic(64, 2048, 1024)
+    ab += 2048 * 1024 // 4 + 2048 * 1024 // 8 - 2048 * 1024 // 2
+    assert f"| {round(((150.0 * 2 + 20.0) * 1024) / ab, 3)} |" in text
+    assert "| 0.5 |" in text  # MFMA busy: 512000 / 1024 / (8000 / 8)
