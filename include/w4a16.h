@@ -252,13 +252,16 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
 
 /* ---- bf16 activations ---------------------------------------------------------------
  * w4a16_gemm_bf16: Y (device, out) bf16 [M][N] = X (device, in) bf16 [M][K] * dequant(W),
- *   same repacked weights and rules as w4a16_gemm (groups of 64 rows included) except
- *   that every M runs on the skinny kernel.  The weights enter the bf16 matrix
- *   instructions as the exact integers 128 + q; the offset 128 + z is removed and the
- *   scale applied in fp32 per 128-row block (per 64-row half for groups of 64), and Y is
- *   rounded once to bf16 (nearest-even).  Bitwise reproducible like w4a16_gemm.
- * w4a16_gemm_bf16_plan: the same with an explicit skinny variant (< the number of
- *   "skinny_*" variants of w4a16_gemm_variants) and `splits` as in w4a16_gemm_plan. */
+ *   same repacked weights and rules as w4a16_gemm (groups of 64 rows included): the
+ *   skinny kernel up to 32 rows and for groups of 64 rows, the tiled kernel above where
+ *   w4a16_gemm takes it (four-wave tiles only).  The weights enter the bf16 matrix
+ *   instructions as the exact integers 128 + q; the offset 128 + z is removed with the
+ *   block's activation row sums and the scale applied in fp32 per 128-row block (per
+ *   64-row half for groups of 64), and Y is rounded once to bf16 (nearest-even).
+ *   Bitwise reproducible like w4a16_gemm.
+ * w4a16_gemm_bf16_plan: the same with an explicit variant in w4a16_gemm_plan's numbering
+ *   (the eight-wave tiled variants, and any tiled variant with groups of 64 rows, return
+ *   W4A16_ERR_ARG) and `splits` as there (for a tiled variant: workgroups). */
 int w4a16_gemm_bf16(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                     uint16_t* Y, int M, int N, int K, int group, void* stream);
 int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,

@@ -222,7 +222,19 @@ def test_bf16_validation(raw):
     raw.w4a16_gemm_variant_name.restype = ctypes.c_char_p
     nskinny = sum(1 for v in range(raw.w4a16_gemm_variants())
                   if not raw.w4a16_gemm_variant_name(v).startswith(b"tiled"))
-    assert f(A, A, A, None, A, 16, 1024, 1024, 128, nskinny, 0, None) == -8  # tiled: not bf16
+    total = raw.w4a16_gemm_variants()
+    w8 = [v for v in range(total) if b"_w8_" in raw.w4a16_gemm_variant_name(v)]
+    assert w8
+    # tiled variants take bf16 activations (four-wave tiles: without a GPU the plan passes
+    # and the missing device is reported; with one this call would launch on the fake
+    # pointers, so it only runs where there is none), not the eight-wave ones, and not with
+    # groups of 64 rows
+    import os
+    if not os.path.exists("/dev/kfd"):
+        assert f(A, A, A, None, A, 256, 1024, 1024, 128, nskinny, 0, None) == -4
+    assert f(A, A, A, None, A, 256, 1024, 1024, 128, w8[0], 0, None) == -8
+    assert f(A, A, A, None, A, 256, 1024, 1024, 64, nskinny, 0, None) == -8
+    assert f(A, A, A, None, A, 16, 1024, 1024, 128, total, 0, None) == -8
     assert f(A, A, A, None, A, 16, 1024, 1024, 128, -2, 0, None) == -8
 
 

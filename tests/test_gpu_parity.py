@@ -664,7 +664,7 @@ def test_group64_full_size(gh, M, K, N, asym):
     assert ok, info
 
 
-# ---- bf16 activations (skinny kernel; Y rounded once to bf16) ---------------------------
+# ---- bf16 activations (skinny kernel up to 32 rows, tiled above; Y rounded once to bf16) -
 BF16_FRO = 4e-3  # one bf16 rounding of Y costs up to 2^-9 of |Y|: the Frobenius limit is 4x looser
 
 
@@ -737,8 +737,57 @@ def test_bf16_onehot_exact(gh, asym):
         assert np.array_equal(Y, exp), nm
 
 
+@pytest.mark.parametrize("M,K,N,asym", [(300, 2048, 1040, False), (257, 1536, 512, True),
+                                        (130, 1024, 256, True), (64, 1024, 512, False)])
+def test_bf16_tiled_every_variant_and_grid(gh, M, K, N, asym):
+    """bf16 activations on the tiled kernel: every four-wave tiled variant at several
+    workgroup counts (whole tiles, stream-K stripes at odd k-blocks), ragged M and N; the
+    eight-wave variants are refused before any launch.  Each run repeats bit for bit."""
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, bits, vals = _case_bf16(M, K, N, asym)
+    packed = gh.repack(d, K, N)
+    Yref = oracle.gemm(vals, d["Qp"], d["s"], d["Zp"], 128)
+    B = oracle.error_bound(vals, d["Qp"], d["s"], d["Zp"], 128)
+    ran = 0
+    for v in range(w4.w4a16_gemm_variants()):
+        name = w4.w4a16_gemm_variant_name(v)
+        if not name.startswith("tiled"):
+            continue
+        if "_w8_" in name:
+            with pytest.raises(w4.W4A16Error):
+                _gemm_bf16(gh, bits, packed, M, N, K, v, 0)
+            continue
+        for grid in (0, 1, 3, 5, 8, 24):
+            Y1 = _gemm_bf16(gh, bits, packed, M, N, K, v, grid)
+            ok, info = oracle.accept(_bf16_f32(Y1), Yref, B, rel_fro=BF16_FRO)
+            assert ok, (name, grid, info)
+            assert np.array_equal(_gemm_bf16(gh, bits, packed, M, N, K, v, grid), Y1), (name, grid)
+            ran += 1
+    assert ran >= 6 * 7
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_bf16_tiled_onehot_exact(gh, asym):
+    """One-hot bf16 rows through the tiled kernel select RNE_bf16((q - z) * s) bit for bit,
+    with whole tiles and with stream-K pieces (the second pass writes bf16 too)."""
+    M, K, N = 16, 1024, 768
+    _, d, _, _ = _case_bf16(M, K, N, asym)
+    ks = [0, 1, 7, 8, 9, 127, 128, 255, 300, 511, 512, 640, 777, 900, 1022, 1023]
+    bits = np.zeros((M, K), np.uint16)
+    bits[np.arange(M), ks] = 0x3F80  # 1.0
+    W = oracle.dequant(d["Qp"], d["s"], d["Zp"], K, N, 128)
+    exp = _f32_bf16_rne(W[ks].astype(np.float32))
+    packed = gh.repack(d, K, N)
+    for nm in ["tiled_bm16_bn256_s4", "tiled_bm64_bn128_s4", "tiled_bm128_bn256_s3",
+               "tiled_bm128_bn128_s3"]:
+        for grid in (1, 7):
+            Y = _gemm_bf16(gh, bits, packed, M, N, K, gh.variant_index(nm), grid)
+            assert np.array_equal(Y, exp), (nm, grid)
+
+
 @pytest.mark.parametrize("M,K,N,asym", [(1, 4096, 11008, False), (16, 4096, 11008, True),
-                                        (32, 11008, 4096, False)])
+                                        (32, 11008, 4096, False), (256, 8192, 10240, False),
+                                        (1024, 28672, 8192, True), (192, 8192, 28672, False)])
 def test_bf16_full_size(gh, M, K, N, asym):
     _, d, bits, vals = _case_bf16(M, K, N, asym)
     Y = _bf16_f32(_gemm_bf16(gh, bits, gh.repack(d, K, N), M, N, K))  # NaN-filled before

@@ -429,9 +429,9 @@ size_t w4a16_workspace_bytes(int M, int N, int K) {
     const size_t bytes = (counters + 63) / 64 * 64 * sizeof(int) + floats * sizeof(float);
     if (bytes > need) need = bytes;
   }
-  // w4a16_gemm_bf16, and w4a8_gemm with groups of 64, run every M on the skinny kernel;
-  // w4a8_gemm with larger groups takes the tiled kernel where w4a16_gemm does (its tiled
-  // plans differ: fp8 needs an even number of 16-row tiles)
+  // w4a16_gemm_bf16 and w4a8_gemm with groups of 64 run every M on the skinny kernel;
+  // with larger groups they take the tiled kernel where w4a16_gemm does (their tiled plans
+  // differ: fp8 needs an even number of 16-row tiles, bf16 has no eight-wave tiles)
   SkinnyPlan p;
   if (skinny_make_plan(M, N, K, KBLK, W_SYM8, -1, 0, &p) == 0) {
     const size_t bytes =
@@ -439,6 +439,15 @@ size_t w4a16_workspace_bytes(int M, int N, int K) {
     if ((p.counters || p.part_floats) && bytes > need) need = bytes;
   }
   TiledPlan t;
+  if (skinny_make_plan(M, N, K, KBLK, W_SYMB, -1, 0, &p) == 0) {
+    const size_t bytes =
+        ((size_t)p.counters + 63) / 64 * 64 * sizeof(int) + p.part_floats * sizeof(float);
+    if ((p.counters || p.part_floats) && bytes > need) need = bytes;
+  }
+  if (use_tiled(M, N, K) && tiled_make_plan(M, N, K, W_SYMB, -1, 0, &t) == 0) {
+    const size_t bytes = t.part_floats * sizeof(float);
+    if (bytes > need) need = bytes;
+  }
   if (use_tiled(M, N, K) && tiled_make_plan(M, N, K, W_SYM8, -1, 0, &t) == 0) {
     const size_t bytes = t.part_floats * sizeof(float);
     if (bytes > need) need = bytes;
@@ -583,8 +592,21 @@ int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, 
                          void* stream) {
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
-  if (variant < -1 || variant >= skinny_variant_count() || splits < 0) return W4A16_ERR_ARG;
+  const int ns = skinny_variant_count();
+  if (variant < -1 || variant >= ns + tiled_variant_count(W_SYMB) || splits < 0)
+    return W4A16_ERR_ARG;
   const int mode = group == 64 ? (zp ? W_ASYMB64 : W_SYMB64) : (zp ? W_ASYMB : W_SYMB);
+  // the same variant numbering and kernel choice as w4a16_gemm_plan; groups of 64 rows
+  // run on the skinny kernel for every M
+  if (variant >= ns) {
+    if (group == 64) return W4A16_ERR_ARG;
+    return run_tiled(mode, X, wp, sp, zp, Y, M, N, K, variant - ns, splits, stream);
+  }
+  if (variant < 0 && splits == 0 && group != 64 && use_tiled(M, N, K)) {
+    TiledPlan t;
+    if (tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0)
+      return run_tiled(mode, X, wp, sp, zp, Y, M, N, K, -1, 0, stream);
+  }
   return run_skinny(mode, X, wp, sp, zp, Y, M, N, K, group, variant, splits, stream);
 }
 

@@ -513,6 +513,107 @@ __device__ __forceinline__ void compute_kblock_fp8(const char* xb, const char* w
   }
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 8 codes of one repacked word -> the 8 exact bf16 values 128 + q (rows 0..7, the k order of
+// the fp16 fragment): every nibble moved to bits 0-3 of its half and or-ed into the bits of
+// 128 (bf16 keeps 7 mantissa bits, so the fp16 route through 1024 + 16q does not apply).
+// Plain C: the compiler then knows these values feed a matrix instruction.
+__device__ __forceinline__ bf16x8 codes_bf16(uint32_t w) {
+  const uint32_t magic = 0x43004300u;
+  const u32x4 r = {(w & 0x000F000Fu) | magic, ((w >> 4) & 0x000F000Fu) | magic,
+                   ((w >> 8) & 0x000F000Fu) | magic, ((w >> 12) & 0x000F000Fu) | magic};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// One k-block with bf16 activations: the matrix instructions (v_mfma_f32_16x16x32_bf16)
+// see the exact 128 + q, and per (row tile, column tile) the block's partial sum g is
+// rescaled in fp32: acc += s (g - (128 + z) xs), with xs the sum of the lane's activation
+// row over the block, taken on the matrix cores against a ones operand (the same four
+// values in every lane of a row).  Weights stay exact integers and the scale applies once
+// in fp32.  Software pipeline as for fp8: group t unpacks tile t + 1, runs the matrix
+// instructions of tile t and rescales tile t - 1.
+template <int MT, int NTW, int MODE, class DP>
+__device__ __forceinline__ void compute_kblock_bf16(const char* xb, const char* wl,
+                                                    float4v (&acc)[MT][NTW],
+                                                    const uint32_t (&aoff)[4], int lane,
+                                                    const DP& dma) {
+  typedef WLds<NTW, MODE> L;
+  constexpr int NVL = DP::NV;
+  constexpr int G = NTW;  // groups per k-block: one per column tile
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                       0x3F803F80u});
+  bf16x8 xa[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xa[i][j] = *reinterpret_cast<const bf16x8*>(xb + aoff[j] + i * 4096);
+  float xs[MT];
+  {
+    float4v v[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) v[i] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        v[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, xa[i][j], v[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) xs[i] = v[i][0];
+  }
+  u32x4 wv[NTW];
+  float4v sc[NTW], so[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    wv[t] = *reinterpret_cast<const u32x4*>(wl + t * 1024 + lane * 16);
+    // the lane's four columns 16t + 4(lane/16) + r: scales and offsets 128 + z
+    const uint2 s4 = *reinterpret_cast<const uint2*>(wl + L::SCALES + t * 32 + 8 * (lane >> 4));
+    const half2v s01 = __builtin_bit_cast(half2v, s4.x), s23 = __builtin_bit_cast(half2v, s4.y);
+    sc[t] = float4v{(float)s01[0], (float)s01[1], (float)s23[0], (float)s23[1]};
+    float4v off = {136.f, 136.f, 136.f, 136.f};
+    if constexpr (mode_asym(MODE)) {
+      const uint2 zw = *reinterpret_cast<const uint2*>(wl + L::ZEROS + t * 8);
+      const uint32_t z16 = (((lane >> 4) < 2 ? zw.x : zw.y) >> (16 * ((lane >> 4) & 1))) & 0xFFFFu;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) off[r] = (float)(128 + (int)((z16 >> (4 * r)) & 15u));
+    }
+    so[t] = sc[t] * off;
+  }
+  bf16x8 b[2][4];
+  float4v g[2][MT];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[0][j] = codes_bf16(wv[0][j]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t <= NTW; ++t) {
+    if (t < NTW) {
+#pragma unroll
+      for (int q = t; q < NVL; q += G) dma.issue(q);
+    }
+    if (t + 1 < NTW) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[(t + 1) & 1][j] = codes_bf16(wv[t + 1][j]);
+    }
+    if (t < NTW) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) g[t & 1][i] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          g[t & 1][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[t & 1][j], xa[i][j],
+                                                                g[t & 1][i], 0, 0, 0);
+    }
+    if (t >= 1) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        acc[i][t - 1] += sc[t - 1] * g[(t - 1) & 1][i] - so[t - 1] * xs[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One k-block of MXFP4 weights: the codes go to the block-scaled matrix instruction as
 // they are (E2M1 operand A), with the lane's E8M0 byte as its scale, and the fp8 rows of
 // X as operand B (unit scale); the instruction applies the scales of the 32-row blocks
@@ -569,6 +670,15 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
+// bf16 outputs: round to nearest even from fp32 (finite values)
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_b2(float a, float b) {
+  return bf16_bits(a) | (bf16_bits(b) << 16);
+}
 
 // Tile index -> (row tile, column tile), rows grouped by `group_m` so that the
 // workgroups running at the same time share activation rows and weight columns.
@@ -613,7 +723,8 @@ __device__ __forceinline__ void store_rows(uint16_t* __restrict__ Y, const Tiled
       const float xs = (a.xscale != nullptr && r < rows) ? a.xscale[m0 + r] : 1.0f;
       const float4v o = a.xscale != nullptr ? acc[ii][t] * xs : acc[ii][t];
       typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 v = {pack_h2(o[0], o[1]), pack_h2(o[2], o[3])};
+      const u32x2 v = a.out_bf16 ? u32x2{pack_b2(o[0], o[1]), pack_b2(o[2], o[3])}
+                                 : u32x2{pack_h2(o[0], o[1]), pack_h2(o[2], o[3])};
       __builtin_amdgcn_raw_buffer_store_b64(v, ry, off, 0u, 0);
     }
   }
@@ -825,6 +936,10 @@ __global__ __launch_bounds__(64 * NWV) void tiled_kernel(
         compute_kblock_mx<MT, NTW, MODE>(lds + d * STAGE,
                                          lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES,
                                          acc, aoff, lane, plan);
+      else if constexpr (mode_bf16(MODE))
+        compute_kblock_bf16<MT, NTW, MODE>(lds + d * STAGE,
+                                           lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES,
+                                           acc, aoff, lane, plan);
       else if constexpr (F8)
         compute_kblock_fp8<MT, NTW, MODE>(lds + d * STAGE,
                                           lds + d * STAGE + XBUF + wave * WLds<NTW, MODE>::BYTES,
@@ -948,7 +1063,7 @@ typedef void (*FixupFn)(const float*, uint16_t*, TiledArgs);
 
 struct TVariant {
   int MT, NTW, NS, NWV;  // row tiles, column tiles per wave, pipeline stages, waves
-  TiledFn sym, asym, sp24, f16, sym64, asym64, sym8, asym8, mx4;
+  TiledFn sym, asym, sp24, f16, sym64, asym64, sym8, asym8, mx4, symb, asymb;
   FixupFn fixup;
   const char* name;
 };
@@ -973,10 +1088,12 @@ constexpr TiledFn sp24_tiled() {
         tiled_kernel<MT, NTW, NS, W_ASYM, WAVES>, sp24_tiled<MT, NTW, NS>(), nullptr,       \
         tiled_kernel<MT, NTW, NS, W_SYM64, WAVES>, tiled_kernel<MT, NTW, NS, W_ASYM64, WAVES>, \
         fp8_tiled<MT, NTW, NS, W_SYM8>(), fp8_tiled<MT, NTW, NS, W_ASYM8>(),                \
-        fp8_tiled<MT, NTW, NS, W_MX4>(), tiled_fixup_kernel<MT, NTW, WAVES>, NAME           \
+        fp8_tiled<MT, NTW, NS, W_MX4>(), tiled_kernel<MT, NTW, NS, W_SYMB, WAVES>,          \
+        tiled_kernel<MT, NTW, NS, W_ASYMB, WAVES>, tiled_fixup_kernel<MT, NTW, WAVES>, NAME \
   }
 // eight waves (two per SIMD) sharing a BM-row activation tile, each with the same 16*NTW
-// columns of work as in the four-wave variants: the packed formats except 2:4.  The
+// columns of work as in the four-wave variants: the packed formats except 2:4 and bf16
+// activations (their X fragments, partial sums and rescale do not fit two waves).  The
 // fp8-activation INT4 modes only with two column tiles per wave (with four, their
 // unpacking and rescale do not fit the registers of two waves per SIMD: the main loop
 // spills).
@@ -990,14 +1107,15 @@ constexpr TiledFn fp8_tiled_w8() {
     MT, NTW, NS, 8, tiled_kernel<MT, NTW, NS, W_SYM, 8>, tiled_kernel<MT, NTW, NS, W_ASYM, 8>, \
         nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_SYM64, 8>,                            \
         tiled_kernel<MT, NTW, NS, W_ASYM64, 8>, fp8_tiled_w8<MT, NTW, NS, W_SYM8>(),        \
-        fp8_tiled_w8<MT, NTW, NS, W_ASYM8>(), fp8_tiled<MT, NTW, NS, W_MX4, 8>(),           \
-        tiled_fixup_kernel<MT, NTW, 8>, NAME                                                \
+        fp8_tiled_w8<MT, NTW, NS, W_ASYM8>(), fp8_tiled<MT, NTW, NS, W_MX4, 8>(), nullptr,  \
+        nullptr, tiled_fixup_kernel<MT, NTW, 8>, NAME                                       \
   }
 // the fp16 baseline moves four times the weight bytes: its own LDS-sized tiles
 #define W4A16_TILED_F16(MT, NTW, NS, NAME)                                                    \
   TVariant {                                                                               \
     MT, NTW, NS, WAVES, nullptr, nullptr, nullptr, tiled_kernel<MT, NTW, NS, W_FP16, WAVES>, \
-        nullptr, nullptr, nullptr, nullptr, nullptr, tiled_fixup_kernel<MT, NTW, WAVES>, NAME \
+        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,                      \
+        tiled_fixup_kernel<MT, NTW, WAVES>, NAME                                            \
   }
 
 const TVariant kTiled[] = {
@@ -1028,6 +1146,8 @@ TiledFn variant_fn(const TVariant& v, int mode) {
          : mode == W_SYM8   ? v.sym8
          : mode == W_ASYM8  ? v.asym8
          : mode == W_MX4    ? v.mx4
+         : mode == W_SYMB   ? v.symb
+         : mode == W_ASYMB  ? v.asymb
          : mode == W_SYM    ? v.sym
                             : nullptr;
 }
@@ -1049,9 +1169,9 @@ static long dp_grid(long tiles) {
 }
 
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p) {
-  // fp8 activations: groups of 128 rows or more (one scale per 128-row block)
-  if ((!mode_dense4(mode) && mode != W_SP24 && mode != W_FP16) || mode_bf16(mode) ||
-      mode == W_SYM8G64 || mode == W_ASYM8G64)
+  // fp8 and bf16 activations: groups of 128 rows or more (one scale per 128-row block)
+  if ((!mode_dense4(mode) && mode != W_SP24 && mode != W_FP16) || mode == W_SYMB64 ||
+      mode == W_ASYMB64 || mode == W_SYM8G64 || mode == W_ASYM8G64)
     return -8;
   const bool f8 = mode_fp8(mode);
   const bool f16 = mode == W_FP16;
@@ -1155,6 +1275,7 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
   // (measured 0-8% faster than groups of 8 on the 70B-class layers)
   q.args.group_m = 4;
   q.args.xscale = nullptr;
+  q.args.out_bf16 = mode_bf16(mode) ? 1 : 0;
   const long T = (long)q.args.tiles_m * q.args.tiles_n;
   if (T > (1L << 30)) return -2;
   // buffer offsets are 32-bit: the rows of X and Y one tile touches, and the fp16

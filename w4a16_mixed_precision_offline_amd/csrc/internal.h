@@ -69,8 +69,8 @@ hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
 // Fused skinny GEMM.  `part` / `counters` form the split-K workspace.
 // weight format of a launch; the *64 modes are the same formats with groups of 64 rows,
 // the *B modes take bf16 activations and write bf16 outputs, the *8 modes take fp8
-// (OCP E4M3) activations with an optional fp32 scale per row and write fp16 outputs
-// (both skinny kernel only); W_*B64 and W_*8G64 are those two with groups of 64 rows
+// (OCP E4M3) activations with an optional fp32 scale per row and write fp16 outputs;
+// W_*B64 and W_*8G64 are those two with groups of 64 rows (skinny kernel only)
 enum WMode {
   W_SYM = 0, W_ASYM = 1, W_FP16 = 2, W_SP24 = 3, W_SYM64 = 4, W_ASYM64 = 5, W_SYMB = 6,
   W_ASYMB = 7, W_SYM8 = 8, W_ASYM8 = 9, W_SYMB64 = 10, W_ASYMB64 = 11, W_SYM8G64 = 12,
@@ -134,6 +134,7 @@ struct TiledArgs {
   long long sk_units;   // (tile, k-block) units of the remaining tiles
   long long sk_per_wg;  // units per workgroup stripe
   const float* xscale;  // fp8 activations: fp32 scale per row of X (nullptr: 1)
+  int out_bf16;         // bf16 activations: Y is written in bf16 (else fp16)
 };
 struct TiledPlan {
   int variant;  // index into the tiled variant table
