@@ -437,15 +437,17 @@ def group64_leg(w4, torch):
 
 
 def bf16_leg(w4, torch):
-    """bf16 activations (w4a16_gemm_bf16, skinny kernel for every M) against fp16
-    activations (w4a16_gemm) on the same repacked weights, at the decode-sweep shapes and
-    M = 1 / 16 / 32.  Seeded synthetic inputs on the device; weights rotate over copies
+    """bf16 activations (w4a16_gemm_bf16: skinny kernel up to 32 rows, fp16 rows on the
+    tiled kernel above) against fp16 activations (w4a16_gemm) on the same repacked weights,
+    at the decode-sweep shapes with M = 1 / 16 / 32 and on 8192 x 10240 with M = 64 / 256 /
+    1024 / 4096.  Seeded synthetic inputs on the device; weights rotate over copies
     totalling at least 512 MiB."""
     rot = 512 << 20
     gen = torch.Generator(device="cuda")
     gen.manual_seed(16)
     runs = []
-    for (K, N) in [(4096, 4096), (4096, 12288), (11008, 4096)]:
+    for (K, N, Ms) in [(4096, 4096, (1, 16, 32)), (4096, 12288, (1, 16, 32)),
+                       (11008, 4096, (1, 16, 32)), (8192, 10240, (64, 256, 1024, 4096))]:
         q = torch.randint(-2 ** 31, 2 ** 31 - 1, (K // 8, N), dtype=torch.int32, device="cuda",
                           generator=gen)
         s = (torch.rand((K // 128, N), device="cuda", generator=gen) * 0.018 + 0.002).half()
@@ -453,7 +455,7 @@ def bf16_leg(w4, torch):
         w4.w4a16_repack(q, s, None, *pk, K, N, 128)
         n = max(2, -(-rot // (K * N // 2)))
         copies = [pk] + [tuple(t.clone() if t is not None else None for t in pk) for _ in range(n - 1)]
-        for M in (1, 16, 32):
+        for M in Ms:
             x = torch.randn((M, K), device="cuda", generator=gen)
             Xh, Xb = x.half(), x.bfloat16()
             Y = torch.empty((M, N), dtype=torch.float16, device="cuda")

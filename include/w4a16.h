@@ -252,21 +252,33 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
 
 /* ---- bf16 activations ---------------------------------------------------------------
  * w4a16_gemm_bf16: Y (device, out) bf16 [M][N] = X (device, in) bf16 [M][K] * dequant(W),
- *   same repacked weights and rules as w4a16_gemm (groups of 64 rows included): the
- *   skinny kernel up to 32 rows and for groups of 64 rows, the tiled kernel above where
- *   w4a16_gemm takes it (four-wave tiles only).  The weights enter the bf16 matrix
- *   instructions as the exact integers 128 + q; the offset 128 + z is removed with the
- *   block's activation row sums and the scale applied in fp32 per 128-row block (per
- *   64-row half for groups of 64), and Y is rounded once to bf16 (nearest-even).
- *   Bitwise reproducible like w4a16_gemm.
- * w4a16_gemm_bf16_plan: the same with an explicit variant in w4a16_gemm_plan's numbering
- *   (the eight-wave tiled variants, and any tiled variant with groups of 64 rows, return
- *   W4A16_ERR_ARG) and `splits` as there (for a tiled variant: workgroups). */
+ *   same repacked weights and rules as w4a16_gemm (groups of 64 rows included), Y rounded
+ *   once to bf16 (nearest-even).  Bitwise reproducible like w4a16_gemm.  Two paths:
+ *   - skinny kernel (up to 32 rows, and where w4a16_gemm keeps the skinny kernel): the
+ *     weights enter the bf16 matrix instructions as the exact integers 128 + q; the offset
+ *     128 + z is removed with the block's activation row sums and the scale applied in
+ *     fp32 per 128-row block (per 64-row half for groups of 64);
+ *   - above: each row of X is first rewritten in fp16 as X * 2^d, with the power of two d
+ *     chosen from the row's largest finite magnitude (exact for every value within 2^32 of
+ *     it; smaller ones round to the fp16 subnormal grid), then the fp16 tiled kernel of
+ *     w4a16_gemm runs and applies 2^-d to each finished fp32 sum before the bf16 store.
+ *     The fp16 rows live in the per-stream workspace (M*K*2 bytes more, counted by
+ *     w4a16_workspace_bytes).
+ * w4a16_gemm_bf16_plan: the same with an explicit variant < w4a16_gemm_bf16_variants():
+ *   the skinny variants, then the bf16 tiled variants (indices as in w4a16_gemm_plan; the
+ *   eight-wave ones, and any of them with groups of 64 rows, return W4A16_ERR_ARG; the
+ *   weights enter as 128 + q and the offset and scale are applied per k-block in fp32,
+ *   as in the skinny path), then the fp16 tiled variants on rewritten rows ("rows16_*");
+ *   `splits` as in w4a16_gemm_plan (for a tiled variant: workgroups).
+ * w4a16_gemm_bf16_variants / _variant_name: their number, and a static name for one
+ *   (NULL if out of range). */
 int w4a16_gemm_bf16(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                     uint16_t* Y, int M, int N, int K, int group, void* stream);
 int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                          uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
                          void* stream);
+int w4a16_gemm_bf16_variants(void);
+const char* w4a16_gemm_bf16_variant_name(int variant);
 
 /* ---- fp8 activations: W4A8 ---------------------------------------------------------
  * INT4 weights times FP8 activations, the mixed-precision variant that runs the product

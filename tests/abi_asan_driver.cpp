@@ -61,6 +61,8 @@ int main(int argc, char** argv) {
   for (int v = -2; v <= w4a16_gemm_variants() + 1; ++v) (void)w4a16_gemm_variant_name(v);
   for (int v = -2; v <= w4a16_fp16_gemm_variants() + 1; ++v) (void)w4a16_fp16_gemm_variant_name(v);
   for (int v = -2; v <= w4a8_mx_variants() + 1; ++v) (void)w4a8_mx_variant_name(v);
+  for (int v = -2; v <= w4a16_gemm_bf16_variants() + 1; ++v) (void)w4a16_gemm_bf16_variant_name(v);
+  EXPECT(w4a16_gemm_bf16_variant_name(w4a16_gemm_bf16_variants()) == nullptr);
   EXPECT(w4a16_gemm_variant_name(-1) == nullptr);
 
   // argument validation: refused on the host, nothing enqueued
@@ -96,8 +98,8 @@ int main(int argc, char** argv) {
   EXPECT(w4a16_sparse24_gemm(X, A, A, X, Y, 16, 1024, 1024, 64, nullptr) == W4A16_ERR_SHAPE);
   EXPECT(w4a16_sparse24_repack(static_cast<const int32_t*>(A), X, A, A, Y, 1024, 1024, 64,
                                nullptr) == W4A16_ERR_SHAPE);
-  EXPECT(w4a16_gemm_bf16_plan(X, A, X, nullptr, Y, 16, 1024, 1024, 128, w4a16_gemm_variants(),
-                              0, nullptr) == W4A16_ERR_ARG);
+  EXPECT(w4a16_gemm_bf16_plan(X, A, X, nullptr, Y, 16, 1024, 1024, 128,
+                              w4a16_gemm_bf16_variants(), 0, nullptr) == W4A16_ERR_ARG);
   const uint8_t* X8 = static_cast<const uint8_t*>(A);
   EXPECT(w4a8_gemm(X8, reinterpret_cast<const float*>(buf + 2), A, X, nullptr, Y, 16, 1024, 1024,
                    128, nullptr) == W4A16_ERR_ALIGN);

@@ -168,8 +168,9 @@ def test_workspace_bytes(raw):
     # 8192 x 10240 at M = 256: 160 tiles of 128 x 128 on 256 workgroups, all striped:
     # two fp32 partial tiles per workgroup
     assert f(256, 10240, 8192) >= 2 * 256 * 128 * 128 * 4
-    # M = 4096 on the same layer: 14 (fp16 tiles: 28) whole rounds of tiles, no stripes
-    assert f(4096, 28672, 8192) == 0
+    # M = 4096 on the same layer: 14 (fp16 tiles: 28) whole rounds of tiles, no stripes;
+    # what remains is w4a16_gemm_bf16's fp16 rows (M*K*2 bytes) and fp32 row scales
+    assert f(4096, 28672, 8192) == 4096 * 4 + 4096 * 8192 * 2
 
 
 def test_fp16_plan_validation(raw):
@@ -234,7 +235,20 @@ def test_bf16_validation(raw):
         assert f(A, A, A, None, A, 256, 1024, 1024, 128, nskinny, 0, None) == -4
     assert f(A, A, A, None, A, 256, 1024, 1024, 128, w8[0], 0, None) == -8
     assert f(A, A, A, None, A, 256, 1024, 1024, 64, nskinny, 0, None) == -8
-    assert f(A, A, A, None, A, 16, 1024, 1024, 128, total, 0, None) == -8
+    # then the fp16 tiled variants on rows rewritten in fp16, every group size included
+    raw.w4a16_gemm_bf16_variants.restype = ctypes.c_int
+    raw.w4a16_gemm_bf16_variant_name.restype = ctypes.c_char_p
+    nb = raw.w4a16_gemm_bf16_variants()
+    assert nb == total + (total - nskinny)
+    names = [raw.w4a16_gemm_bf16_variant_name(v) for v in range(nb)]
+    assert names[:total] == [raw.w4a16_gemm_variant_name(v) for v in range(total)]
+    assert names[total:] == [b"rows16_" + raw.w4a16_gemm_variant_name(v)
+                             for v in range(nskinny, total)]
+    assert raw.w4a16_gemm_bf16_variant_name(nb) is None
+    assert raw.w4a16_gemm_bf16_variant_name(-1) is None
+    if not os.path.exists("/dev/kfd"):
+        assert f(A, A, A, None, A, 256, 1024, 1024, 64, total, 0, None) == -4
+    assert f(A, A, A, None, A, 16, 1024, 1024, 128, nb, 0, None) == -8
     assert f(A, A, A, None, A, 16, 1024, 1024, 128, -2, 0, None) == -8
 
 

@@ -785,6 +785,127 @@ def test_bf16_tiled_onehot_exact(gh, asym):
             assert np.array_equal(Y, exp), (nm, grid)
 
 
+def _rows16_variants(w4):
+    """(index, name) of the fp16 tiled variants on rows rewritten in fp16."""
+    nb = w4.w4a16_gemm_bf16_variants()
+    return [(v, w4.w4a16_gemm_bf16_variant_name(v)) for v in range(nb)
+            if w4.w4a16_gemm_bf16_variant_name(v).startswith("rows16_")]
+
+
+@pytest.mark.parametrize("M,K,N,asym,group", [(300, 2048, 1040, False, 128),
+                                              (257, 1536, 512, True, 128),
+                                              (130, 1024, 256, True, 64),
+                                              (64, 1024, 512, False, 256),
+                                              (40, 2048, 768, True, 64)])
+def test_bf16_rows16_every_variant_and_grid(gh, M, K, N, asym, group):
+    """bf16 rows rewritten in fp16 (a power of two per row) on the fp16 tiled kernel: every
+    tiled variant, eight-wave ones and groups of 64 included, at several workgroup counts
+    (whole tiles, stream-K stripes), ragged M and N.  Each run repeats bit for bit."""
+    import w4a16_mixed_precision_offline_amd as w4
+    _, d, bits, vals = _case_bf16(M, K, N, asym, group=group)
+    packed = gh.repack(d, K, N, group)
+    Yref = oracle.gemm(vals, d["Qp"], d["s"], d["Zp"], group)
+    B = oracle.error_bound(vals, d["Qp"], d["s"], d["Zp"], group)
+    ran = 0
+    for v, name in _rows16_variants(w4):
+        for grid in (0, 1, 3, 8, 24):
+            Y1 = _gemm_bf16(gh, bits, packed, M, N, K, v, grid, group=group)
+            ok, info = oracle.accept(_bf16_f32(Y1), Yref, B, rel_fro=BF16_FRO)
+            assert ok, (name, grid, info)
+            assert np.array_equal(_gemm_bf16(gh, bits, packed, M, N, K, v, grid, group=group),
+                                  Y1), (name, grid)
+            ran += 1
+    assert ran >= 9 * 5
+    # the automatic plan (rows16 where w4a16_gemm takes the tiled kernel)
+    Y = _bf16_f32(_gemm_bf16(gh, bits, packed, M, N, K, -1, 0, group=group))
+    ok, info = oracle.accept(Y, Yref, B, rel_fro=BF16_FRO)
+    assert ok, ("auto", info)
+
+
+@pytest.mark.parametrize("asym,group", [(False, 128), (True, 128), (True, 64)])
+def test_bf16_rows16_onehot_exact(gh, asym, group):
+    """One-hot bf16 rows through the fp16 path select RNE_bf16(RNE_fp16((q - z) * s)) bit
+    for bit: the row scale 2^15 and its inverse are exact, the weight is the fp16 one of
+    w4a16_gemm, and Y is rounded once from it to bf16."""
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 16, 1024, 768
+    _, d, _, _ = _case_bf16(M, K, N, asym, group=group)
+    ks = [0, 1, 7, 8, 9, 63, 64, 128, 255, 300, 511, 512, 640, 777, 900, 1023]
+    bits = np.zeros((M, K), np.uint16)
+    bits[np.arange(M), ks] = 0x3F80  # 1.0
+    W16 = oracle.dequant_fp16(d["Qp"], d["s"], d["Zp"], K, N, group)
+    exp = _f32_bf16_rne(W16[ks].astype(np.float32))
+    packed = gh.repack(d, K, N, group)
+    rows16 = dict((n, v) for v, n in _rows16_variants(w4))
+    for nm in ["rows16_tiled_bm16_bn256_s4", "rows16_tiled_bm64_bn128_s4",
+               "rows16_tiled_bm128_bn256_s3", "rows16_tiled_bm128_bn512_w8_s2"]:
+        for grid in (1, 7):
+            Y = _gemm_bf16(gh, bits, packed, M, N, K, rows16[nm], grid, group=group)
+            assert np.array_equal(Y, exp), (nm, grid)
+
+
+def test_bf16_power_of_two_rows_zero_rows_and_outliers(gh):
+    """Every bf16 path: a row times 2^k gives exactly 2^k times that row's output, for k
+    from -60 to 60, and an all-zero row gives zeros.  A row holding one value far above the
+    rest passes the oracle's test within each path's range: 2^24 above the rest on fp16
+    rows (exact within 2^32 of the row's maximum), 2^12 on the bf16 variants (the offset
+    128 + z leaves the block's fp32 sums, which carry the large value times 128 + q; the
+    error reaches the elementwise limit near 2^18)."""
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 96, 4096, 8192  # 32 Mi weights: the automatic plan takes fp16 rows
+    _, d, bits, vals = _case_bf16(M, K, N, True)
+    packed = gh.repack(d, K, N)
+    base = bits[0].copy()
+    ks = [-60, -33, -20, -1, 0, 1, 20, 33, 60]
+    rows = np.tile(base, (M, 1))
+    for i in range(M):
+        k = ks[i % len(ks)]
+        e = ((rows[i] >> 7) & 0xFF).astype(np.int32)
+        nz = e > 0
+        rows[i][nz] = (rows[i][nz] & 0x807F) | ((e[nz] + k).astype(np.uint16) << 7)
+    rows[5] = 0
+    rows[6, :] = bits[1]
+    rows[6, 17] = (rows[6, 17] & 0x8000) | ((127 + 24) << 7) | 0x40  # +-1.5 * 2^24
+    rows[7, :] = bits[2]
+    rows[7, 40] = (rows[7, 40] & 0x8000) | ((127 + 12) << 7) | 0x40  # +-1.5 * 2^12
+
+    def check_row(Y, i, v):
+        vi = _bf16_f32(rows[i:i + 1]).astype(np.float64)
+        Yref = oracle.gemm(vi, d["Qp"], d["s"], d["Zp"], 128)
+        B = oracle.error_bound(vi, d["Qp"], d["s"], d["Zp"], 128)
+        ok, info = oracle.accept(_bf16_f32(Y[i:i + 1]), Yref, B, rel_fro=BF16_FRO)
+        assert ok, (v, i, info)
+
+    rows16 = [v for v, n in _rows16_variants(w4) if n in ("rows16_tiled_bm128_bn256_s3",
+                                                          "rows16_tiled_bm64_bn128_s4")]
+    native = [gh.variant_index("skinny_xr16_nt2_wk8_d2"), gh.variant_index("tiled_bm128_bn256_s3")]
+    for v in [-1] + rows16 + native:
+        Y = _gemm_bf16(gh, rows, packed, M, N, K, v, 0 if v < 0 else 5)
+        y0 = _bf16_f32(Y[ks.index(0)])
+        for i in range(M):
+            if i in (5, 6, 7):
+                continue
+            k = ks[i % len(ks)]
+            assert np.array_equal(_bf16_f32(Y[i]), y0 * np.float32(2.0 ** k)), (v, i, k)
+        assert np.all(_bf16_f32(Y[5]) == 0), v
+        check_row(Y, 7, v)
+        if v not in native:
+            check_row(Y, 6, v)
+
+
+@pytest.mark.parametrize("M,K,N,asym", [(1024, 8192, 10240, True), (48, 28672, 8192, False)])
+def test_bf16_rows16_groups_of_64_full_size(gh, M, K, N, asym):
+    """Groups of 64 rows with bf16 activations above 32 rows: fp16 rows on the tiled kernel
+    (the skinny kernel is kept up to 32 rows)."""
+    _, d, bits, vals = _case_bf16(M, K, N, asym, group=64)
+    Y = _bf16_f32(_gemm_bf16(gh, bits, gh.repack(d, K, N, 64), M, N, K, group=64))
+    assert np.all(np.isfinite(Y))
+    rows, cols = gh.tile_samples(M, N)
+    Yref, B = oracle.gemm_sampled(vals, d["Qp"], d["s"], d["Zp"], 64, rows, cols)
+    ok, info = oracle.accept(Y[np.ix_(rows, cols)], Yref, B, rel_fro=BF16_FRO)
+    assert ok, info
+
+
 @pytest.mark.parametrize("M,K,N,asym", [(1, 4096, 11008, False), (16, 4096, 11008, True),
                                         (32, 11008, 4096, False), (256, 8192, 10240, False),
                                         (1024, 28672, 8192, True), (192, 8192, 28672, False)])

@@ -54,7 +54,9 @@ def test_noalloc_matches_gemm_on_calls_of_decreasing_size(gh):
     for i, (M, K, N, asym) in enumerate(cases):
         assert w4.w4a16_gemm_describe(M, N, K, 128)["name"].startswith(kinds[i])
         _run(gh, w4, M, K, N, asym, i)
-    assert w4.w4a16_workspace_bytes(4096, 10240, 8192) == 128 << 20
+    # the first call's stream-K partials fill the array (the query also counts
+    # w4a16_gemm_bf16's fp16 rows, which this entry point does not use)
+    assert w4.w4a16_workspace_bytes(4096, 10240, 8192) >= 128 << 20
     assert w4.w4a16_gemm_describe(1, 256, 4096, 128)["splits"] > 1
 
 
@@ -69,6 +71,16 @@ def test_noalloc_rejects_plans_larger_than_its_array(gh):
     with pytest.raises(w4.W4A16Error) as e:
         w4.w4a16_gemm_noalloc(X, wp, sp, None, Y, 4, 1000, 1024, 128)
     assert e.value.code == -2
+    # the automatic plans of the largest layers fit (a call that does not returns
+    # W4A16_ERR_WORKSPACE and raises); zero weights and activations give zero outputs
     for (M, K, N) in [(4096, 8192, 28672), (4096, 8192, 10240), (256, 28672, 8192),
                       (1, 4096, 256)]:
-        assert w4.w4a16_workspace_bytes(M, N, K) <= w4.NOALLOC_SCRATCH_BYTES
+        X = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+        Y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+        wp, sp, _ = w4.alloc_packed(K, N, 128, False)
+        wp.zero_()
+        sp.zero_()
+        w4.w4a16_gemm_noalloc(X, wp, sp, None, Y, M, N, K, 128)
+        torch.cuda.synchronize()
+        assert bool((Y == 0).all()), (M, K, N)
+        del X, Y, wp, sp

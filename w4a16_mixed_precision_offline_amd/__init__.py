@@ -55,6 +55,8 @@ _SIGS = {
     "w4a16_sparse24_gemm_plan": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "w4a16_gemm_bf16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "w4a16_gemm_bf16_plan": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "w4a16_gemm_bf16_variants": (_I, []),
+    "w4a16_gemm_bf16_variant_name": (ctypes.c_char_p, [_I]),
     "w4a8_gemm": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "w4a16_set_workspace": (_I, [_P, ctypes.c_size_t, _P]),
     "w4a8_gemm_plan": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
@@ -224,6 +226,15 @@ def w4a16_gemm_bf16_plan(X, wp, sp, zp, Y, M, N, K, group, variant=-1, splits=0,
     _check("w4a16_gemm_bf16_plan", _lib.w4a16_gemm_bf16_plan(
         _ptr(X), _ptr(wp), _ptr(sp), _ptr(zp), _ptr(Y), M, N, K, group, variant, splits,
         _stream(stream)))
+
+
+def w4a16_gemm_bf16_variants() -> int:
+    return _lib.w4a16_gemm_bf16_variants()
+
+
+def w4a16_gemm_bf16_variant_name(v: int):
+    r = _lib.w4a16_gemm_bf16_variant_name(v)
+    return None if r is None else r.decode()
 
 
 WS_COUNTER_BYTES = 65536  # W4A16_WS_COUNTER_BYTES

@@ -6,6 +6,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <string>
 #include <utility>
 #include <vector>
 
@@ -256,6 +257,37 @@ int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
       tiled_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, st, xscale));
 }
 
+// bf16 activations on the fp16 tiled kernel: the rows of X are rewritten in fp16 with a
+// power-of-two scale each (exact, see bf16_rows.hip), then the dense fp16 tiled plan runs
+// with the inverse scales applied to its fp32 sums and a bf16 store.  Workspace floats:
+// [stream-K partials | row scales | fp16 rows], each part 256-byte aligned.
+inline size_t round64(size_t n) { return (n + 63) / 64 * 64; }
+// Automatic bf16 plan: the skinny kernel up to 32 rows (and where w4a16_gemm keeps it), the
+// fp16 tiled kernel on rows rewritten in fp16 above.
+bool bf16_uses_rows(int M, int N, int K) { return use_tiled(M, N, K); }
+size_t bf16_rows_floats(const TiledPlan& t, int M, int K) {
+  return round64(t.part_floats) + round64((size_t)M) + (size_t)M * K / 2;
+}
+
+int run_bf16_rows(int mode16, const uint16_t* X, const void* w, const uint16_t* sp,
+                  const void* zp, uint16_t* Y, int M, int N, int K, int variant, int grid,
+                  void* stream) {
+  TiledPlan plan;
+  int rc = tiled_make_plan(M, N, K, mode16, variant, grid, &plan);
+  if (rc) return rc;
+  int dev;
+  if ((rc = check_device(&dev))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int* cnt;
+  float* part;
+  if ((rc = get_workspace(dev, st, 0, bf16_rows_floats(plan, M, K), &cnt, &part))) return rc;
+  float* rscale = part + round64(plan.part_floats);
+  uint16_t* xh = reinterpret_cast<uint16_t*>(rscale + round64((size_t)M));
+  if ((rc = launched(launch_bf16_rows_to_f16(X, xh, rscale, M, K, st)))) return rc;
+  return launched(tiled_launch(plan, xh, w, sp, static_cast<const uint32_t*>(zp), Y, part, st,
+                               rscale, true));
+}
+
 // Variant numbering of the ABI: the skinny variants first, then the tiled ones.
 // For a tiled variant the `splits` argument is the number of persistent workgroups.
 int run_fused(int mode, const uint16_t* X, const void* w, const uint16_t* sp, const void* zp,
@@ -444,9 +476,12 @@ size_t w4a16_workspace_bytes(int M, int N, int K) {
         ((size_t)p.counters + 63) / 64 * 64 * sizeof(int) + p.part_floats * sizeof(float);
     if ((p.counters || p.part_floats) && bytes > need) need = bytes;
   }
-  if (use_tiled(M, N, K) && tiled_make_plan(M, N, K, W_SYMB, -1, 0, &t) == 0) {
-    const size_t bytes = t.part_floats * sizeof(float);
-    if (bytes > need) need = bytes;
+  // w4a16_gemm_bf16 above 32 rows: partials, row scales and the fp16 rows (every group)
+  for (int mode16 : {W_SYM, W_ASYM, W_SYM64, W_ASYM64}) {
+    if (bf16_uses_rows(M, N, K) && tiled_make_plan(M, N, K, mode16, -1, 0, &t) == 0) {
+      const size_t bytes = bf16_rows_floats(t, M, K) * sizeof(float);
+      if (bytes > need) need = bytes;
+    }
   }
   if (use_tiled(M, N, K) && tiled_make_plan(M, N, K, W_SYM8, -1, 0, &t) == 0) {
     const size_t bytes = t.part_floats * sizeof(float);
@@ -587,25 +622,52 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
 }  // extern "C"
 
 // ---- bf16 activations ----------------------------------------------------------------
+namespace {
+// "rows16_" + the fp16-path tiled variant's name, built once
+const char* rows_variant_name(int v) {
+  static const std::vector<std::string> names = [] {
+    std::vector<std::string> n;
+    for (int i = 0; i < tiled_variant_count(W_SYM); ++i)
+      n.push_back(std::string("rows16_") + tiled_variant_name(W_SYM, i));
+    return n;
+  }();
+  return v >= 0 && v < (int)names.size() ? names[v].c_str() : nullptr;
+}
+}  // namespace
+
+int w4a16_gemm_bf16_variants(void) {
+  return skinny_variant_count() + tiled_variant_count(W_SYMB) + tiled_variant_count(W_SYM);
+}
+
+const char* w4a16_gemm_bf16_variant_name(int variant) {
+  const int ns = skinny_variant_count(), nb = tiled_variant_count(W_SYMB);
+  if (variant < 0) return nullptr;
+  if (variant < ns) return skinny_variant_name(variant);
+  if (variant < ns + nb) return tiled_variant_name(W_SYMB, variant - ns);
+  return rows_variant_name(variant - ns - nb);
+}
+
 int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, const void* zp,
                          uint16_t* Y, int M, int N, int K, int group, int variant, int splits,
                          void* stream) {
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
-  const int ns = skinny_variant_count();
-  if (variant < -1 || variant >= ns + tiled_variant_count(W_SYMB) || splits < 0)
-    return W4A16_ERR_ARG;
+  const int ns = skinny_variant_count(), nb = tiled_variant_count(W_SYMB);
+  if (variant < -1 || variant >= w4a16_gemm_bf16_variants() || splits < 0) return W4A16_ERR_ARG;
   const int mode = group == 64 ? (zp ? W_ASYMB64 : W_SYMB64) : (zp ? W_ASYMB : W_SYMB);
-  // the same variant numbering and kernel choice as w4a16_gemm_plan; groups of 64 rows
-  // run on the skinny kernel for every M
+  const int mode16 = dense_mode(zp != nullptr, group);
+  // skinny variants first, then the bf16 tiled ones (w4a16_gemm_plan's numbering), then the
+  // fp16 tiled ones on rewritten rows
+  if (variant >= ns + nb)
+    return run_bf16_rows(mode16, X, wp, sp, zp, Y, M, N, K, variant - ns - nb, splits, stream);
   if (variant >= ns) {
     if (group == 64) return W4A16_ERR_ARG;
     return run_tiled(mode, X, wp, sp, zp, Y, M, N, K, variant - ns, splits, stream);
   }
-  if (variant < 0 && splits == 0 && group != 64 && use_tiled(M, N, K)) {
+  if (variant < 0 && splits == 0 && bf16_uses_rows(M, N, K)) {
     TiledPlan t;
-    if (tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0)
-      return run_tiled(mode, X, wp, sp, zp, Y, M, N, K, -1, 0, stream);
+    if (tiled_make_plan(M, N, K, mode16, -1, 0, &t) == 0)
+      return run_bf16_rows(mode16, X, wp, sp, zp, Y, M, N, K, -1, 0, stream);
   }
   return run_skinny(mode, X, wp, sp, zp, Y, M, N, K, group, variant, splits, stream);
 }

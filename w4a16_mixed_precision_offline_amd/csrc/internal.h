@@ -65,6 +65,9 @@ hipError_t launch_mx_repack(const int32_t* q, const uint8_t* e, uint32_t* wp, ui
                             int K, int N, hipStream_t st);
 hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
                           uint16_t* W, int K, int N, int group, hipStream_t st);
+// bf16 X [M][K] -> fp16 Xh [M][K] = X * 2^d per row, rscale[row] = 2^-d (bf16_rows.hip)
+hipError_t launch_bf16_rows_to_f16(const uint16_t* X, uint16_t* Xh, float* rscale, int M, int K,
+                                   hipStream_t st);
 
 // Fused skinny GEMM.  `part` / `counters` form the split-K workspace.
 // weight format of a launch; the *64 modes are the same formats with groups of 64 rows,
@@ -133,7 +136,8 @@ struct TiledArgs {
   int dp_rounds;   // rounds of whole tiles handed out data-parallel
   long long sk_units;   // (tile, k-block) units of the remaining tiles
   long long sk_per_wg;  // units per workgroup stripe
-  const float* xscale;  // fp8 activations: fp32 scale per row of X (nullptr: 1)
+  const float* xscale;  // fp32 scale per row of X (nullptr: 1): fp8 activations, or the
+                        // inverse power of two of bf16 rows rewritten in fp16
   int out_bf16;         // bf16 activations: Y is written in bf16 (else fp16)
 };
 struct TiledPlan {
@@ -155,9 +159,11 @@ const char* tiled_variant_name(int mode, int v);
 // variant < 0: automatic; grid <= 0: automatic number of workgroups.
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p);
 // X holds fp8 codes in the fp8 modes, with xscale their optional per-row scale.
+// bf16_out (dense fp16 modes): X holds bf16 rows rewritten in fp16 (launch_bf16_rows_to_f16),
+// xscale their inverse row scales, and Y is written in bf16.
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
                         const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st,
-                        const float* xscale = nullptr);
+                        const float* xscale = nullptr, bool bf16_out = false);
 
 // Calibration kernels (probes.hip).
 hipError_t launch_probe_read(const void* p, size_t bytes, uint32_t* out, hipStream_t st);
