@@ -893,6 +893,45 @@ def test_bf16_power_of_two_rows_zero_rows_and_outliers(gh):
             check_row(Y, 6, v)
 
 
+def test_bf16_rows16_caller_owned_workspace(gh):
+    """The fp16 rows of w4a16_gemm_bf16 live in the stream's workspace: a caller-owned buffer
+    of W4A16_WS_COUNTER_BYTES + w4a16_workspace_bytes(M, N, K) runs the automatic plan with
+    the same bits as a library-owned one, twice in a row; the smallest accepted buffer is
+    refused with W4A16_ERR_WORKSPACE before any launch."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 300, 2048, 1040
+    _, d, bits, vals = _case_bf16(M, K, N, True)
+    packed = gh.repack(d, K, N)
+    ref = _gemm_bf16(gh, bits, packed, M, N, K)
+    need = w4.w4a16_workspace_bytes(M, N, K)
+    assert need >= M * K * 2 + M * 4
+    st = torch.cuda.Stream()
+    nbytes = w4.WS_COUNTER_BYTES + need
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    w4.w4a16_set_workspace(buf, nbytes, stream=st)
+    try:
+        for _ in range(2):
+            with torch.cuda.stream(st):
+                Y = _gemm_bf16(gh, bits, packed, M, N, K)
+            torch.cuda.synchronize()
+            assert np.array_equal(Y, ref)
+    finally:
+        w4.w4a16_set_workspace(None, 0, stream=st)
+    small = torch.empty(w4.WS_COUNTER_BYTES + 256, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    w4.w4a16_set_workspace(small, small.numel(), stream=st)
+    try:
+        with torch.cuda.stream(st):
+            with pytest.raises(w4.W4A16Error) as e:
+                _gemm_bf16(gh, bits, packed, M, N, K)
+        assert e.value.code == -6
+    finally:
+        w4.w4a16_set_workspace(None, 0, stream=st)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("M,K,N,asym", [(1024, 8192, 10240, True), (48, 28672, 8192, False)])
 def test_bf16_rows16_groups_of_64_full_size(gh, M, K, N, asym):
     """Groups of 64 rows with bf16 activations above 32 rows: fp16 rows on the tiled kernel
