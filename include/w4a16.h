@@ -162,7 +162,8 @@ const char* w4a16_gemm_variant_name(int variant);
 /* Bytes of device workspace the automatic plans of w4a16_gemm, w4a16_sparse24_gemm,
  * w4a16_fp16_gemm, w4a16_gemm_bf16, w4a8_gemm and w4a8_mx_gemm need for an (M, N, K) GEMM
  * on one stream (the largest over the entry points; 0 when no plan for the shape reduces
- * across workgroups, or for an invalid shape).  The library allocates this itself, per (device, stream), on the first call
+ * across workgroups or rewrites its activations, or for an invalid shape).  Above 32 rows
+ * this includes w4a16_gemm_bf16's fp16 copy of X (M*K*2 bytes) and its M fp32 row scales.  The library allocates this itself, per (device, stream), on the first call
  * that needs it and keeps it for later calls; the query lets a caller budget device
  * memory ahead of time.  Host only. */
 size_t w4a16_workspace_bytes(int M, int N, int K);
