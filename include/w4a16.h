@@ -292,18 +292,25 @@ const char* w4a16_gemm_bf16_variant_name(int variant);
  *   wp, sp, zp           the repacked weights of w4a16_repack (zp NULL: symmetric, z = 8);
  *   group  as for w4a16_gemm: 64, or a multiple of 128 dividing K.
  *   Every other rule (shapes, 16-byte alignment of X8, wp, sp, zp and Y, error codes,
- *   asynchronous execution on `stream`, library-owned split-K workspace, Y fully
- *   overwritten) is that of w4a16_gemm, and so is the kernel choice (skinny kernel for
- *   small M, tiled kernel above), except that groups of 64 rows run on the skinny kernel
- *   for every M.  The weights enter the fp8 matrix instructions
- *   (v_mfma_f32_16x16x32_fp8_fp8 in the skinny kernel, v_mfma_scale_f32_16x16x128_f8f6f4
- *   with unit block scales in the tiled one) as the exact E4M3 integers q - z, the scale
- *   s applies in fp32 per 128-row block (per 64-row half for groups of 64), and a[m] in
- *   fp32 before the one rounding of Y to fp16 (nearest-even).  Bitwise reproducible like
- *   w4a16_gemm.
- * w4a8_gemm_plan: the same with an explicit variant and `splits`, numbered and read as in
- *   w4a16_gemm_plan; the tiled variants need an even number of 16-row tiles (not
- *   "tiled_bm16_*": W4A16_ERR_ARG) and groups of 128 rows or more. */
+ *   asynchronous execution on `stream`, library-owned workspace, Y fully overwritten) is
+ *   that of w4a16_gemm.  Bitwise reproducible like w4a16_gemm.  Two paths:
+ *   - skinny kernel (up to 32 rows, and where w4a16_gemm keeps the skinny kernel): the
+ *     weights enter v_mfma_f32_16x16x32_fp8_fp8 as the exact E4M3 integers q - z, the
+ *     scale s applies in fp32 per 128-row block (per 64-row half for groups of 64), and
+ *     a[m] in fp32 before the one rounding of Y to fp16 (nearest-even);
+ *   - above: the codes are first rewritten as fp16 (every E4M3 value is one, so this is
+ *     exact; M*K*2 bytes of workspace, counted by w4a16_workspace_bytes), then the fp16
+ *     tiled kernel of w4a16_gemm runs (weights RNE_fp16((q - z) * s), fp32 sums) and
+ *     applies a[m] to each finished sum before the rounding of Y.  On gfx950 this is
+ *     faster than the fp8 matrix instructions there, whose per-block fp32 rescale and
+ *     E4M3 conversion of every weight keep them bound by the vector unit.
+ * w4a8_gemm_plan: the same with an explicit variant and `splits`, numbered like
+ *   w4a16_gemm_bf16_plan (w4a16_gemm_bf16_variants / _variant_name give the count and
+ *   names): the skinny variants; the fp8 tiled variants (v_mfma_scale_f32_16x16x128_f8f6f4
+ *   with unit block scales, the weights as E4M3 integers q - z, s per block in fp32; they
+ *   need an even number of 16-row tiles, so not "tiled_bm16_*", and groups of 128 rows or
+ *   more, else W4A16_ERR_ARG); then the fp16 tiled variants on rewritten rows
+ *   ("rows16_*", every group). */
 int w4a8_gemm(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,
               const void* zp, uint16_t* Y, int M, int N, int K, int group, void* stream);
 int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const uint16_t* sp,

@@ -274,7 +274,15 @@ def test_w4a8_validation(raw):
                   if not raw.w4a16_gemm_variant_name(v).startswith(b"tiled"))
     nall = raw.w4a16_gemm_variants()
     assert nskinny < nall
-    assert f(A, None, A, A, None, A, 16, 1024, 1024, 128, nall, 0, None) == -8  # out of range
+    # numbered like w4a16_gemm_bf16_plan: skinny, fp8 tiled, then fp16 tiled on rewritten
+    # rows (those pass the host checks: without a GPU the missing device is reported; with
+    # one this call would launch on the fake pointers, so it only runs where there is none)
+    nb = raw.w4a16_gemm_bf16_variants()
+    assert nb == nall + (nall - nskinny)
+    import os
+    if not os.path.exists("/dev/kfd"):
+        assert f(A, None, A, A, None, A, 64, 1024, 1024, 64, nall, 0, None) == -4
+    assert f(A, None, A, A, None, A, 16, 1024, 1024, 128, nb, 0, None) == -8  # out of range
     assert f(A, None, A, A, None, A, 16, 1024, 1024, 128, -1, -1, None) == -8
     g = raw.w4a8_gemm
     g.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 4 + [ctypes.c_void_p]

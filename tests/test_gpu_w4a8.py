@@ -337,3 +337,85 @@ def test_w4a8_tiled_without_row_scales(gh):
             assert np.array_equal(Y0.view(np.uint16), Y1.view(np.uint16)), (v, grid)
             ok, info = _accept(Y0, X8, None, d)
             assert ok, (v, grid, info)
+
+
+# ---- above 32 rows: fp8 rows rewritten in fp16 (exact), the fp16 tiled kernel --------------
+def _rows16_variants(w4):
+    """(index, name) of the fp16 tiled variants on rewritten rows (w4a8_gemm_plan shares
+    w4a16_gemm_bf16_plan's numbering)."""
+    nb = w4.w4a16_gemm_bf16_variants()
+    return [(v, w4.w4a16_gemm_bf16_variant_name(v)) for v in range(nb)
+            if w4.w4a16_gemm_bf16_variant_name(v).startswith("rows16_")]
+
+
+@pytest.mark.parametrize("M,K,N,asym,group", [(300, 2048, 1040, False, 128),
+                                              (257, 1536, 512, True, 128),
+                                              (130, 1024, 256, True, 64),
+                                              (40, 2048, 768, False, 256)])
+def test_w4a8_rows16_every_variant_and_grid(gh, M, K, N, asym, group):
+    """fp8 rows rewritten in fp16 on the fp16 tiled kernel: every tiled variant (eight-wave
+    ones and groups of 64 included) at several workgroup counts, ragged M and N, with row
+    scales; nothing is written past row M - 1, and each run repeats bit for bit."""
+    import w4a16_mixed_precision_offline_amd as w4
+    d, X8, a = _case(M, K, N, asym, group=group)
+    packed = gh.repack(d, K, N, group)
+    ran = 0
+    for v, name in _rows16_variants(w4):
+        for grid in (0, 1, 3, 8, 24):
+            Y, whole = _gemm8(gh, X8, a, packed, M, N, K, v, grid, rows_alloc=M + 3, group=group)
+            assert np.all(np.isnan(whole[M:].astype(np.float32))), (name, grid)
+            ok, info = _accept(Y, X8, a, d, group=group)
+            assert ok, (name, grid, info)
+            Y2, _ = _gemm8(gh, X8, a, packed, M, N, K, v, grid, group=group)
+            assert np.array_equal(Y2.view(np.uint16), Y.view(np.uint16)), (name, grid)
+            ran += 1
+    assert ran >= 9 * 5
+    Y, _ = _gemm8(gh, X8, a, packed, M, N, K, group=group)  # the automatic plan
+    ok, info = _accept(Y, X8, a, d, group=group)
+    assert ok, ("auto", info)
+
+
+@pytest.mark.parametrize("asym,group", [(False, 128), (True, 128), (True, 64)])
+def test_w4a8_rows16_every_code_exact(gh, asym, group):
+    """Every non-NaN E4M3 code, alone in its row, through the fp16 path gives
+    RNE_fp16(a * x * RNE_fp16((q - z) * s)) bit for bit (the code's fp16 value is exact, a
+    is a power of two or absent): the conversion of all 254 codes is pinned against the
+    oracle's decoding.  Outputs below the fp16 normal range are held to one subnormal
+    step."""
+    import w4a16_mixed_precision_offline_amd as w4
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    M, K, N = len(codes), 1024, 768
+    d, _, _ = _case(M, K, N, asym, group=group)
+    rng = np.random.default_rng(11)
+    ks = rng.integers(0, K, size=M)
+    X8 = np.zeros((M, K), np.uint8)
+    X8[np.arange(M), ks] = codes
+    W16 = oracle.dequant_fp16(d["Qp"], d["s"], d["Zp"], K, N, group).astype(np.float64)
+    vals = oracle.decode_e4m3(codes)
+    packed = gh.repack(d, K, N, group)
+    rows16 = dict((n, v) for v, n in _rows16_variants(w4))
+    for a in (None, np.array([2.0 ** ((m % 7) - 3) for m in range(M)], dtype=np.float32)):
+        av = np.ones(M) if a is None else a.astype(np.float64)
+        exp = (av[:, None] * vals[:, None] * W16[ks]).astype(np.float16)  # exact, one rounding
+        normal = (np.abs(exp) >= np.float16(2.0 ** -14)) | (exp == 0)
+        for nm in ["rows16_tiled_bm128_bn256_s3", "rows16_tiled_bm64_bn128_s4",
+                   "rows16_tiled_bm128_bn512_w8_s2"]:
+            for grid in (0, 5):
+                Y, _ = _gemm8(gh, X8, a, packed, M, N, K, rows16[nm], grid, group=group)
+                assert np.array_equal(Y[normal], exp[normal]), (nm, grid)
+                diff = np.abs(Y[~normal].astype(np.float64) - exp[~normal].astype(np.float64))
+                assert np.all(diff <= 2.0 ** -24), (nm, grid)
+
+
+@pytest.mark.parametrize("M,K,N,asym,group", [(256, 8192, 28672, False, 128),
+                                              (1024, 28672, 8192, True, 128),
+                                              (48, 8192, 10240, False, 64)])
+def test_w4a8_rows16_full_size(gh, M, K, N, asym, group):
+    """The automatic plan above 32 rows at 70B-class sizes (fp16 rows; groups of 64 too),
+    NaN-filled output, sampled rows x columns against the oracle."""
+    d, X8, a = _case(M, K, N, asym, group=group)
+    Y, _ = _gemm8(gh, X8, a, gh.repack(d, K, N, group), M, N, K, group=group)
+    assert np.all(np.isfinite(Y.astype(np.float32)))
+    rows, cols = gh.tile_samples(M, N)
+    ok, info = _accept(Y, X8, a, d, rows, cols, group=group)
+    assert ok, info

@@ -257,21 +257,25 @@ int run_tiled(int mode, const uint16_t* X, const void* w, const uint16_t* sp, co
       tiled_launch(plan, X, w, sp, static_cast<const uint32_t*>(zp), Y, part, st, xscale));
 }
 
-// bf16 activations on the fp16 tiled kernel: the rows of X are rewritten in fp16 with a
-// power-of-two scale each (exact, see bf16_rows.hip), then the dense fp16 tiled plan runs
-// with the inverse scales applied to its fp32 sums and a bf16 store.  Workspace floats:
-// [stream-K partials | row scales | fp16 rows], each part 256-byte aligned.
+// bf16 and fp8 activations on the fp16 tiled kernel: the rows of X are rewritten in fp16
+// (bf16: with a power-of-two scale each, exact within 2^32 of the row's maximum; fp8 E4M3:
+// exactly, see bf16_rows.hip), then the dense fp16 tiled plan runs with the row scales
+// applied to its fp32 sums (bf16: the inverse powers of two, and a bf16 store; fp8: the
+// caller's scales, or none).  Workspace floats: [stream-K partials | row scales | fp16 rows],
+// each part 256-byte aligned.
 inline size_t round64(size_t n) { return (n + 63) / 64 * 64; }
-// Automatic bf16 plan: the skinny kernel up to 32 rows (and where w4a16_gemm keeps it), the
-// fp16 tiled kernel on rows rewritten in fp16 above.
-bool bf16_uses_rows(int M, int N, int K) { return use_tiled(M, N, K); }
-size_t bf16_rows_floats(const TiledPlan& t, int M, int K) {
+// Automatic bf16 and fp8 plans: the skinny kernel up to 32 rows (and where w4a16_gemm keeps
+// it), the fp16 tiled kernel on rewritten rows above.
+bool uses_rows16(int M, int N, int K) { return use_tiled(M, N, K); }
+size_t rows16_floats(const TiledPlan& t, int M, int K) {
   return round64(t.part_floats) + round64((size_t)M) + (size_t)M * K / 2;
 }
 
-int run_bf16_rows(int mode16, const uint16_t* X, const void* w, const uint16_t* sp,
-                  const void* zp, uint16_t* Y, int M, int N, int K, int variant, int grid,
-                  void* stream) {
+enum RowsSource { ROWS_BF16, ROWS_FP8 };
+
+int run_rows16(RowsSource src, int mode16, const void* X, const float* xscale, const void* w,
+               const uint16_t* sp, const void* zp, uint16_t* Y, int M, int N, int K, int variant,
+               int grid, void* stream) {
   TiledPlan plan;
   int rc = tiled_make_plan(M, N, K, mode16, variant, grid, &plan);
   if (rc) return rc;
@@ -280,12 +284,20 @@ int run_bf16_rows(int mode16, const uint16_t* X, const void* w, const uint16_t* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   int* cnt;
   float* part;
-  if ((rc = get_workspace(dev, st, 0, bf16_rows_floats(plan, M, K), &cnt, &part))) return rc;
+  if ((rc = get_workspace(dev, st, 0, rows16_floats(plan, M, K), &cnt, &part))) return rc;
   float* rscale = part + round64(plan.part_floats);
   uint16_t* xh = reinterpret_cast<uint16_t*>(rscale + round64((size_t)M));
-  if ((rc = launched(launch_bf16_rows_to_f16(X, xh, rscale, M, K, st)))) return rc;
+  if (src == ROWS_BF16) {
+    if ((rc = launched(launch_bf16_rows_to_f16(static_cast<const uint16_t*>(X), xh, rscale, M,
+                                               K, st))))
+      return rc;
+    xscale = rscale;
+  } else if ((rc = launched(launch_fp8_rows_to_f16(static_cast<const uint8_t*>(X), xh,
+                                                   (size_t)M * K, st)))) {
+    return rc;
+  }
   return launched(tiled_launch(plan, xh, w, sp, static_cast<const uint32_t*>(zp), Y, part, st,
-                               rscale, true));
+                               xscale, true, src == ROWS_BF16));
 }
 
 // Variant numbering of the ABI: the skinny variants first, then the tiled ones.
@@ -476,10 +488,11 @@ size_t w4a16_workspace_bytes(int M, int N, int K) {
         ((size_t)p.counters + 63) / 64 * 64 * sizeof(int) + p.part_floats * sizeof(float);
     if ((p.counters || p.part_floats) && bytes > need) need = bytes;
   }
-  // w4a16_gemm_bf16 above 32 rows: partials, row scales and the fp16 rows (every group)
+  // w4a16_gemm_bf16 and w4a8_gemm above 32 rows: partials, row scales and the fp16 rows
+  // (every group)
   for (int mode16 : {W_SYM, W_ASYM, W_SYM64, W_ASYM64}) {
-    if (bf16_uses_rows(M, N, K) && tiled_make_plan(M, N, K, mode16, -1, 0, &t) == 0) {
-      const size_t bytes = bf16_rows_floats(t, M, K) * sizeof(float);
+    if (uses_rows16(M, N, K) && tiled_make_plan(M, N, K, mode16, -1, 0, &t) == 0) {
+      const size_t bytes = rows16_floats(t, M, K) * sizeof(float);
       if (bytes > need) need = bytes;
     }
   }
@@ -659,15 +672,16 @@ int w4a16_gemm_bf16_plan(const uint16_t* X, const void* wp, const uint16_t* sp, 
   // skinny variants first, then the bf16 tiled ones (w4a16_gemm_plan's numbering), then the
   // fp16 tiled ones on rewritten rows
   if (variant >= ns + nb)
-    return run_bf16_rows(mode16, X, wp, sp, zp, Y, M, N, K, variant - ns - nb, splits, stream);
+    return run_rows16(ROWS_BF16, mode16, X, nullptr, wp, sp, zp, Y, M, N, K, variant - ns - nb,
+                      splits, stream);
   if (variant >= ns) {
     if (group == 64) return W4A16_ERR_ARG;
     return run_tiled(mode, X, wp, sp, zp, Y, M, N, K, variant - ns, splits, stream);
   }
-  if (variant < 0 && splits == 0 && bf16_uses_rows(M, N, K)) {
+  if (variant < 0 && splits == 0 && uses_rows16(M, N, K)) {
     TiledPlan t;
     if (tiled_make_plan(M, N, K, mode16, -1, 0, &t) == 0)
-      return run_bf16_rows(mode16, X, wp, sp, zp, Y, M, N, K, -1, 0, stream);
+      return run_rows16(ROWS_BF16, mode16, X, nullptr, wp, sp, zp, Y, M, N, K, -1, 0, stream);
   }
   return run_skinny(mode, X, wp, sp, zp, Y, M, N, K, group, variant, splits, stream);
 }
@@ -716,17 +730,21 @@ int w4a8_gemm_plan(const uint8_t* X8, const float* xscale, const void* wp, const
   int rc = check_gemm_args(X, wp, sp, zp, Y, M, N, K, group);
   if (rc) return rc;
   if (xscale && (reinterpret_cast<uintptr_t>(xscale) & 3u) != 0) return W4A16_ERR_ALIGN;
-  if (variant < -1 || variant >= w4a16_gemm_variants() || splits < 0) return W4A16_ERR_ARG;
+  if (variant < -1 || variant >= w4a16_gemm_bf16_variants() || splits < 0) return W4A16_ERR_ARG;
   const int mode = group == 64 ? (zp ? W_ASYM8G64 : W_SYM8G64) : (zp ? W_ASYM8 : W_SYM8);
-  // the same variant numbering and kernel choice as w4a16_gemm_plan; groups of 64 rows
-  // run on the skinny kernel for every M
-  const int ns = skinny_variant_count();
+  const int mode16 = dense_mode(zp != nullptr, group);
+  // numbered like w4a16_gemm_bf16_plan: the skinny variants, the fp8 tiled ones (groups of
+  // 128 rows or more), then the fp16 tiled ones on rewritten rows (every group)
+  const int ns = skinny_variant_count(), nt = tiled_variant_count(W_SYM8);
+  if (variant >= ns + nt)
+    return run_rows16(ROWS_FP8, mode16, X8, xscale, wp, sp, zp, Y, M, N, K, variant - ns - nt,
+                      splits, stream);
   if (variant >= ns)
     return run_tiled(mode, X, wp, sp, zp, Y, M, N, K, variant - ns, splits, stream, xscale);
-  if (variant < 0 && splits == 0 && group != 64 && use_tiled(M, N, K)) {
+  if (variant < 0 && splits == 0 && uses_rows16(M, N, K)) {
     TiledPlan t;
-    if (tiled_make_plan(M, N, K, mode, -1, 0, &t) == 0)
-      return run_tiled(mode, X, wp, sp, zp, Y, M, N, K, -1, 0, stream, xscale);
+    if (tiled_make_plan(M, N, K, mode16, -1, 0, &t) == 0)
+      return run_rows16(ROWS_FP8, mode16, X8, xscale, wp, sp, zp, Y, M, N, K, -1, 0, stream);
   }
   return run_skinny(mode, X, wp, sp, zp, Y, M, N, K, group, variant, splits, stream, xscale);
 }

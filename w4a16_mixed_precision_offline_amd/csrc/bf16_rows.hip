@@ -1,4 +1,4 @@
-// bf16 activations rewritten as fp16 rows for the fp16 tiled kernel.
+// bf16 and fp8 activations rewritten as fp16 rows for the fp16 tiled kernel.
 //
 // The pages run the fused product on 16-bit activations ("Marlin / GPTQ-Marlin",
 // brain.gartu.xyz, section "1. Le problème": W4A16 means fp16/bf16 activations).  With bf16
@@ -16,6 +16,10 @@
 // of at most 2^-40 of the row's maximum).  d is kept in [-126, 126] so both powers are
 // normal fp32 numbers; only a row whose maximum lies below 2^-111 is then scaled less.
 // Infinities and NaNs are left out of the maximum and stay infinities and NaNs.
+//
+// FP8 activations (the W4A8 variant, dingiv.github.io "Marlin", section "CUTLASS W4A8
+// （混合精度）") take the same route above 32 rows: every E4M3 code is an fp16 value, so
+// their rows are converted as they are and the caller's fp32 row scale goes to the sums.
 #include "internal.h"
 
 namespace w4a16 {
@@ -112,7 +116,48 @@ __global__ __launch_bounds__(kRowThreads) void bf16_rows_kernel(const uint16_t* 
   }
 }
 
+// OCP FP8 E4M3 (sign, 4 exponent bits of bias 7, 3 mantissa bits, no infinities, S.1111.111
+// NaN) to fp16 bits.  Every E4M3 value is an fp16 value: normal codes (1 + m/8) * 2^(e-7)
+// with e = 1..15 land on fp16 exponents -6..8, subnormal codes m * 2^-9 on fp16 normals, so
+// the conversion is exact and the row needs no scale of its own (the caller's row scale,
+// if any, is applied to the finished sums).
+__device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t b) {
+  const uint32_t sign = (b & 0x80u) << 8;
+  const uint32_t em = b & 0x7Fu;
+  if (em == 0x7Fu) return sign | 0x7E00u;
+  const int e = (int)(em >> 3);
+  const uint32_t m = em & 7u;
+  const float v = e > 0 ? __builtin_ldexpf((float)(8u | m), e - 10)
+                        : __builtin_ldexpf((float)m, -9);
+  return sign | (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
+}
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w, int sh) {
+  return e4m3_to_f16_bits((w >> sh) & 0xFFu) | (e4m3_to_f16_bits((w >> (sh + 8)) & 0xFFu) << 16);
+}
+
+// 16 codes per thread per step (one 16-byte load, two 16-byte stores), grid-stride.
+__global__ __launch_bounds__(256) void fp8_rows_kernel(const uint4* __restrict__ X8,
+                                                       uint4* __restrict__ Xh, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const uint4 v = X8[i];
+    Xh[2 * i] = uint4{e4m3_pair(v.x, 0), e4m3_pair(v.x, 16), e4m3_pair(v.y, 0), e4m3_pair(v.y, 16)};
+    Xh[2 * i + 1] =
+        uint4{e4m3_pair(v.z, 0), e4m3_pair(v.z, 16), e4m3_pair(v.w, 0), e4m3_pair(v.w, 16)};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fp8_rows_to_f16(const uint8_t* X8, uint16_t* Xh, size_t elems, hipStream_t st) {
+  if (elems == 0 || elems % 16 != 0) return hipErrorInvalidValue;
+  const size_t n16 = elems / 16;
+  const size_t want = (n16 + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(fp8_rows_kernel, dim3(blocks), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(X8), reinterpret_cast<uint4*>(Xh), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_bf16_rows_to_f16(const uint16_t* X, uint16_t* Xh, float* rscale, int M, int K,
                                    hipStream_t st) {

@@ -719,8 +719,8 @@ __device__ __forceinline__ void store_rows(uint16_t* __restrict__ Y, const Tiled
       const uint32_t off = r < rows ? (uint32_t)(((size_t)r * a.N + (t_first + t) * 16 +
                                                   4 * (lane >> 4)) * 2)
                                     : kOutOfRange;
-      // fp8 activations, or bf16 rows rewritten in fp16: the scale of the row, applied
-      // once to the finished sum
+      // fp8 activations, or rows rewritten in fp16: the scale of the row, applied once to
+      // the finished sum
       const float xs = (a.xscale != nullptr && r < rows) ? a.xscale[m0 + r] : 1.0f;
       const float4v o = a.xscale != nullptr ? acc[ii][t] * xs : acc[ii][t];
       typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -1337,14 +1337,15 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
 
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
                         const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st,
-                        const float* xscale, bool bf16_out) {
+                        const float* xscale, bool rows16, bool bf16_out) {
   const TVariant& v = p.mode == W_FP16 ? kTiledF16[p.variant] : kTiled[p.variant];
   TiledFn fn = variant_fn(v, p.mode);
   if (fn == nullptr) return hipErrorInvalidValue;  // not reachable through tiled_make_plan
-  if (bf16_out && (mode_fp8(p.mode) || mode_bf16(p.mode) || p.mode == W_SP24))
+  if ((rows16 || bf16_out) && (mode_fp8(p.mode) || mode_bf16(p.mode) || p.mode == W_SP24 ||
+                               p.mode == W_FP16))
     return hipErrorInvalidValue;
   TiledArgs args = p.args;
-  args.xscale = mode_fp8(p.mode) || bf16_out ? xscale : nullptr;
+  args.xscale = mode_fp8(p.mode) || rows16 ? xscale : nullptr;
   if (bf16_out) args.out_bf16 = 1;
   hipLaunchKernelGGL(fn, dim3(p.wgs), dim3(p.threads), 0, st, X,
                      reinterpret_cast<const uint32_t*>(w), sp, zp, Y, part, args);

@@ -68,6 +68,8 @@ hipError_t launch_dequant(const int32_t* q, const uint16_t* s, const int32_t* z,
 // bf16 X [M][K] -> fp16 Xh [M][K] = X * 2^d per row, rscale[row] = 2^-d (bf16_rows.hip)
 hipError_t launch_bf16_rows_to_f16(const uint16_t* X, uint16_t* Xh, float* rscale, int M, int K,
                                    hipStream_t st);
+// fp8 E4M3 codes [elems] -> fp16 Xh [elems], exact (bf16_rows.hip); elems % 16 == 0
+hipError_t launch_fp8_rows_to_f16(const uint8_t* X8, uint16_t* Xh, size_t elems, hipStream_t st);
 
 // Fused skinny GEMM.  `part` / `counters` form the split-K workspace.
 // weight format of a launch; the *64 modes are the same formats with groups of 64 rows,
@@ -136,8 +138,9 @@ struct TiledArgs {
   int dp_rounds;   // rounds of whole tiles handed out data-parallel
   long long sk_units;   // (tile, k-block) units of the remaining tiles
   long long sk_per_wg;  // units per workgroup stripe
-  const float* xscale;  // fp32 scale per row of X (nullptr: 1): fp8 activations, or the
-                        // inverse power of two of bf16 rows rewritten in fp16
+  const float* xscale;  // fp32 scale per row of X (nullptr: 1): fp8 activations, or rows
+                        // rewritten in fp16 (the inverse power of two of bf16 rows, the
+                        // caller's scale of fp8 rows)
   int out_bf16;         // bf16 activations: Y is written in bf16 (else fp16)
 };
 struct TiledPlan {
@@ -159,11 +162,13 @@ const char* tiled_variant_name(int mode, int v);
 // variant < 0: automatic; grid <= 0: automatic number of workgroups.
 int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledPlan* p);
 // X holds fp8 codes in the fp8 modes, with xscale their optional per-row scale.
-// bf16_out (dense fp16 modes): X holds bf16 rows rewritten in fp16 (launch_bf16_rows_to_f16),
-// xscale their inverse row scales, and Y is written in bf16.
+// rows16 (dense fp16 modes): X holds bf16 or fp8 rows rewritten in fp16
+// (launch_bf16_rows_to_f16 / launch_fp8_rows_to_f16) and xscale, if not NULL, scales each
+// row's finished sums; bf16_out: Y is written in bf16.
 hipError_t tiled_launch(const TiledPlan& p, const uint16_t* X, const void* w, const uint16_t* sp,
                         const uint32_t* zp, uint16_t* Y, float* part, hipStream_t st,
-                        const float* xscale = nullptr, bool bf16_out = false);
+                        const float* xscale = nullptr, bool rows16 = false,
+                        bool bf16_out = false);
 
 // Calibration kernels (probes.hip).
 hipError_t launch_probe_read(const void* p, size_t bytes, uint32_t* out, hipStream_t st);
