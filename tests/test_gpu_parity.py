@@ -932,6 +932,48 @@ def test_bf16_rows16_caller_owned_workspace(gh):
     torch.cuda.synchronize()
 
 
+def test_bf16_rows16_hip_graph_replays_match_eager(gh):
+    """Captured bf16 launches above 32 rows (row conversion, fp16 tiled kernel with stream-K
+    pieces and the fixup pass, groups of 128 and 64) and one skinny launch reproduce the
+    eager result bit for bit on every replay, with eager work and synchronizations between
+    the replays."""
+    import torch
+    import w4a16_mixed_precision_offline_amd as w4
+    st = torch.cuda.Stream()
+    plans = [(300, 2048, 1040, 128, -1, 0), (64, 4096, 8192, 64, -1, 0), (16, 1024, 768, 128, -1, 0),
+             (130, 1024, 768, 128,
+              [v for v in range(w4.w4a16_gemm_bf16_variants())
+               if w4.w4a16_gemm_bf16_variant_name(v) == "rows16_tiled_bm64_bn256_s3"][0], 7)]
+    cases = []
+    for (M, K, N, group, v, sp) in plans:
+        _, d, bits, _ = _case_bf16(M, K, N, asym=(M % 2 == 0), group=group)
+        cases.append((M, K, N, group, v, sp, gh.dev(bits.view(np.int16)), gh.repack(d, K, N, group),
+                      torch.empty((M, N), dtype=torch.int16, device="cuda")))
+
+    def run_all():
+        for (M, K, N, group, v, sp, x, packed, Y) in cases:
+            w4.w4a16_gemm_bf16_plan(x, *packed, Y, M, N, K, group, v, sp)
+
+    with torch.cuda.stream(st):
+        run_all()
+    torch.cuda.synchronize()
+    eager = [gh.host(c[-1]).view(np.uint16).copy() for c in cases]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        run_all()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for c in cases:
+            c[-1].fill_(0)
+        _gemm_bf16(gh, np.zeros((40, 1024), np.uint16), cases[3][7], 40, 768, 1024)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            g.replay()
+        torch.cuda.synchronize()
+        for c, e in zip(cases, eager):
+            assert np.array_equal(gh.host(c[-1]).view(np.uint16), e), rep
+
+
 @pytest.mark.parametrize("M,K,N,asym", [(1024, 8192, 10240, True), (48, 28672, 8192, False)])
 def test_bf16_rows16_groups_of_64_full_size(gh, M, K, N, asym):
     """Groups of 64 rows with bf16 activations above 32 rows: fp16 rows on the tiled kernel
