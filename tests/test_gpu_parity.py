@@ -974,6 +974,27 @@ def test_bf16_rows16_hip_graph_replays_match_eager(gh):
             assert np.array_equal(gh.host(c[-1]).view(np.uint16), e), rep
 
 
+@pytest.mark.parametrize("asym", [False, True])
+def test_bf16_rows16_rows_longer_than_registers(gh, asym):
+    """Rows of more than 32768 values do not fit the conversion's registers and are read
+    twice (maximum, then conversion): K = 33024 and 65536 on explicit fp16-row variants,
+    whole output against the oracle, one row holding a value 2^20 above the rest."""
+    import w4a16_mixed_precision_offline_amd as w4
+    rows16 = dict((n, v) for v, n in _rows16_variants(w4))
+    for (M, K, N) in [(40, 33024, 256), (17, 65536, 128)]:
+        _, d, bits, vals = _case_bf16(M, K, N, asym)
+        bits = bits.copy()
+        bits[3, K - 5] = (bits[3, K - 5] & 0x8000) | ((127 + 20) << 7)  # +-2^20, near the end
+        vals = _bf16_f32(bits).astype(np.float64)
+        packed = gh.repack(d, K, N)
+        Yref = oracle.gemm(vals, d["Qp"], d["s"], d["Zp"], 128)
+        B = oracle.error_bound(vals, d["Qp"], d["s"], d["Zp"], 128)
+        for nm, grid in [("rows16_tiled_bm64_bn128_s4", 0), ("rows16_tiled_bm16_bn256_s4", 7)]:
+            Y = _bf16_f32(_gemm_bf16(gh, bits, packed, M, N, K, rows16[nm], grid))
+            ok, info = oracle.accept(Y, Yref, B, rel_fro=BF16_FRO)
+            assert ok, (M, K, nm, info)
+
+
 @pytest.mark.parametrize("M,K,N,asym", [(1024, 8192, 10240, True), (48, 28672, 8192, False)])
 def test_bf16_rows16_groups_of_64_full_size(gh, M, K, N, asym):
     """Groups of 64 rows with bf16 activations above 32 rows: fp16 rows on the tiled kernel
@@ -989,7 +1010,8 @@ def test_bf16_rows16_groups_of_64_full_size(gh, M, K, N, asym):
 
 @pytest.mark.parametrize("M,K,N,asym", [(1, 4096, 11008, False), (16, 4096, 11008, True),
                                         (32, 11008, 4096, False), (256, 8192, 10240, False),
-                                        (1024, 28672, 8192, True), (192, 8192, 28672, False)])
+                                        (1024, 28672, 8192, True), (192, 8192, 28672, False),
+                                        (4096, 28672, 8192, False)])
 def test_bf16_full_size(gh, M, K, N, asym):
     _, d, bits, vals = _case_bf16(M, K, N, asym)
     Y = _bf16_f32(_gemm_bf16(gh, bits, gh.repack(d, K, N), M, N, K))  # NaN-filled before

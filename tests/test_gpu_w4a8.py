@@ -409,7 +409,8 @@ def test_w4a8_rows16_every_code_exact(gh, asym, group):
 
 @pytest.mark.parametrize("M,K,N,asym,group", [(256, 8192, 28672, False, 128),
                                               (1024, 28672, 8192, True, 128),
-                                              (48, 8192, 10240, False, 64)])
+                                              (48, 8192, 10240, False, 64),
+                                              (4096, 28672, 8192, False, 128)])
 def test_w4a8_rows16_full_size(gh, M, K, N, asym, group):
     """The automatic plan above 32 rows at 70B-class sizes (fp16 rows; groups of 64 too),
     NaN-filled output, sampled rows x columns against the oracle."""
