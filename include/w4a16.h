@@ -258,7 +258,10 @@ int w4a16_sparse24_gemm_plan(const uint16_t* X, const void* vp, const void* idx,
  *   - skinny kernel (up to 32 rows, and where w4a16_gemm keeps the skinny kernel): the
  *     weights enter the bf16 matrix instructions as the exact integers 128 + q; the offset
  *     128 + z is removed with the block's activation row sums and the scale applied in
- *     fp32 per 128-row block (per 64-row half for groups of 64);
+ *     fp32 per 128-row block (per 64-row half for groups of 64).  Those fp32 sums carry
+ *     every activation times 128 + q, so one activation far above the rest of its row
+ *     (beyond about 2^18 times) costs accuracy in outputs whose weight at its position is
+ *     small;
  *   - above: each row of X is first rewritten in fp16 as X * 2^d, with the power of two d
  *     chosen from the row's largest finite magnitude (exact for every value within 2^32 of
  *     it; smaller ones round to the fp16 subnormal grid), then the fp16 tiled kernel of
