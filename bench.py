@@ -625,7 +625,8 @@ def offline_leg(w4, torch):
 
 def profile_tiled(w4, torch):
     """A short workload for counter runs: W4A16 (fp16 activations), W4A8 (fp8 E4M3
-    activations) and MXFP4 weights with fp8 activations (block scales inside the matrix
+    activations, on the fp8 tiled variant 128 x 256: the automatic plan would rewrite the
+    rows in fp16) and MXFP4 weights with fp8 activations (block scales inside the matrix
     instruction) on the tiled kernel, 8192 x 28672 at M = 4096, three eager launches each
     after one warmup launch; prints the per-launch times."""
     K, N, M = 8192, 28672, 4096
@@ -644,9 +645,12 @@ def profile_tiled(w4, torch):
     a = (x.abs().amax(dim=1) / 448.0).float()
     X8 = (x / a[:, None]).cpu().to(torch.float8_e4m3fn).view(torch.uint8).cuda()
     Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    v8 = [v for v in range(w4.w4a16_gemm_variants())
+          if w4.w4a16_gemm_variant_name(v) == "tiled_bm128_bn256_s3"][0]
     out = {}
     for name, fn in (("w4a16_gemm", lambda: w4.w4a16_gemm(Xh, pk[0], pk[1], None, Y, M, N, K, 128)),
-                     ("w4a8_gemm", lambda: w4.w4a8_gemm(X8, a, pk[0], pk[1], None, Y, M, N, K, 128)),
+                     ("w4a8_gemm", lambda: w4.w4a8_gemm_plan(X8, a, pk[0], pk[1], None, Y, M, N, K,
+                                                             128, v8, 0)),
                      ("w4a8_mx_gemm", lambda: w4.w4a8_mx_gemm(X8, a, mx[0], mx[1], Y, M, N, K))):
         fn()
         torch.cuda.synchronize()
