@@ -88,6 +88,35 @@ def test_layer_forward_bf16_and_fp8(lib):
     assert ok, info
 
 
+@pytest.mark.gpu
+def test_layer_forward_bf16_and_fp8_large_batch(lib):
+    """A batch of 300 rows through the layer: bf16 and fp8 activations take the fp16 tiled
+    kernel on rows rewritten in fp16 (the automatic plan from 256 rows on), outputs against
+    the oracle."""
+    import torch
+    from gen import activations_bf16, activations_fp8
+    from w4a16_mixed_precision_offline_amd.layer import W4A16Linear
+    M, K, N, group = 300, 2048, 1040, 128
+    w = Workload(cfg=9, M=M, K=K, N=N, group=group, asym=False)
+    d = weights(w, seed=82)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    layer = W4A16Linear.from_quantized(dev(d["Qp"]), dev(d["s"]), None, group=group)
+    bits, vals = activations_bf16(w, seed=83)
+    yb = layer(dev(bits.view(np.int16)).view(torch.bfloat16).reshape(3, 100, K))
+    assert yb.shape == (3, 100, N) and yb.dtype == torch.bfloat16
+    ok, info = oracle.accept(yb.reshape(M, N).float().cpu().numpy(),
+                             oracle.gemm(vals, d["Qp"], d["s"], None, group),
+                             oracle.error_bound(vals, d["Qp"], d["s"], None, group), rel_fro=4e-3)
+    assert ok, info
+    X8, a = activations_fp8(w, seed=84)
+    y8 = layer(dev(X8).view(torch.float8_e4m3fn).reshape(M, K), dev(a))
+    assert y8.shape == (M, N) and y8.dtype == torch.float16
+    ok, info = oracle.accept(y8.cpu().numpy(),
+                             oracle.gemm_w4a8(X8, a, d["Qp"], d["s"], None, group),
+                             oracle.error_bound_w4a8(X8, a, d["Qp"], d["s"], None, group))
+    assert ok, info
+
+
 def test_mxfp4_layer_rejects_bad_inputs_on_the_host():
     import torch
     from w4a16_mixed_precision_offline_amd.layer import MXFP4Linear
