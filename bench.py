@@ -1193,6 +1193,10 @@ def main():
                          "MXFP4, load-time kernels) into the --detail file")
     ap.add_argument("--profile-tiled", action="store_true",
                     help="only a short W4A16 / W4A8 tiled-kernel workload (for counter runs)")
+    ap.add_argument("--only-activations", action="store_true",
+                    help="run only the bf16 and fp8 activation legs (w4a16_gemm_bf16, w4a8_gemm "
+                         "beside w4a16_gemm) and print them, e.g. under a kernel trace of the "
+                         "row conversion")
     ap.add_argument("--only-mxfp4", action="store_true",
                     help="only the MXFP4 leg (for a kernel trace of its kernels)")
     ap.add_argument("--profile-small", action="store_true",
@@ -1243,6 +1247,10 @@ def main():
         return
     if args.only_mxfp4:
         print(json.dumps(dict(mxfp4_in_mfma_dequant=mxfp4_leg(w4, torch))), flush=True)
+        return
+    if args.only_activations:
+        print(json.dumps(dict(bf16_activations=bf16_leg(w4, torch))), flush=True)
+        print(json.dumps(dict(w4a8_fp8_activations=w4a8_leg(w4, torch))), flush=True)
         return
     if args.profile_small:
         if args.copy_calibration:
