@@ -995,6 +995,51 @@ def test_bf16_rows16_rows_longer_than_registers(gh, asym):
             assert ok, (M, K, nm, info)
 
 
+def _bf16_bits(sign, exp_unbiased, mant7):
+    return np.uint16((sign << 15) | ((exp_unbiased + 127) << 7) | mant7)
+
+
+def test_bf16_rows16_exact_range_of_a_row(gh):
+    """The fp16 rows carry every value within 2^32 of the row's maximum exactly.  Each row
+    holds its maximum 1.5 * 2^E and one value (255/128) * 2^(E - delta) with all eight
+    significant bits set; in the columns whose weight at the maximum's position is zero the
+    output is that value times the fp16 weight alone, so it must equal
+    RNE_bf16(value * RNE_fp16((q - z) * s)) bit for bit for delta = 1 .. 32 (the smallest
+    carried exactly lands on the fp16 subnormal grid), over maxima from 2^-60 to 2^100."""
+    import w4a16_mixed_precision_offline_amd as w4
+    M, K, N = 64, 1024, 768
+    _, d, _, _ = _case_bf16(M, K, N, False)
+    W16 = oracle.dequant_fp16(d["Qp"], d["s"], d["Zp"], K, N, 128).astype(np.float64)
+    rng = np.random.default_rng(12)
+    Es = [-60, -40, -3, 0, 7, 25, 60, 100]
+    deltas = [1, 2, 7, 8, 15, 16, 23, 24, 30, 31, 32]
+    bits = np.zeros((M, K), np.uint16)
+    big_k, small_k, small_v = [], [], []
+    for r in range(M):
+        E = Es[r % len(Es)]
+        delta = deltas[r % len(deltas)]
+        k1, k2 = rng.choice(K, size=2, replace=False)
+        bits[r, k1] = _bf16_bits(r % 2, E, 0x40)                   # 1.5 * 2^E
+        bits[r, k2] = _bf16_bits((r // 2) % 2, E - delta, 0x7F)    # (255/128) * 2^(E - delta)
+        big_k.append(k1)
+        small_k.append(k2)
+        small_v.append(float(_bf16_f32(bits[r, k2:k2 + 1])[0]))
+    packed = gh.repack(d, K, N)
+    rows16 = dict((n, v) for v, n in _rows16_variants(w4))
+    for nm in ["rows16_tiled_bm64_bn128_s4", "rows16_tiled_bm128_bn256_s3"]:
+        Y = _gemm_bf16(gh, bits, packed, M, N, K, rows16[nm], 3)
+        checked = 0
+        for r in range(M):
+            cols = np.nonzero(W16[big_k[r]] == 0.0)[0]
+            exp = _f32_bf16_rne((small_v[r] * W16[small_k[r], cols]).astype(np.float32))
+            nz = (exp & 0x7FFF) != 0                                   # +-0 compare equal
+            assert np.array_equal(Y[r, cols][nz], exp[nz]), (nm, r, Es[r % len(Es)],
+                                                             deltas[r % len(deltas)])
+            assert np.all((Y[r, cols][~nz] & 0x7FFF) == 0), (nm, r)
+            checked += len(cols)
+        assert checked > 20 * M
+
+
 @pytest.mark.parametrize("M,K,N,asym", [(1024, 8192, 10240, True), (48, 28672, 8192, False)])
 def test_bf16_rows16_groups_of_64_full_size(gh, M, K, N, asym):
     """Groups of 64 rows with bf16 activations above 32 rows: fp16 rows on the tiled kernel
