@@ -474,9 +474,10 @@ def bf16_leg(w4, torch):
 
 
 def w4a8_leg(w4, torch):
-    """FP8 E4M3 activations with per-row fp32 scales (w4a8_gemm, skinny kernel for every M)
-    against fp16 activations (w4a16_gemm, automatic plan) on the same repacked weights:
-    decode shapes at M = 1 / 16 / 32 and a 70B-class layer at M = 16 / 64 / 256.  Seeded
+    """FP8 E4M3 activations with per-row fp32 scales (w4a8_gemm, automatic plan: the fp8
+    skinny kernel up to 32 rows, fp16 rows on the fp16 tiled kernel above) against fp16
+    activations (w4a16_gemm, automatic plan) on the same repacked weights: decode shapes at
+    M = 1 / 16 / 32 and a 70B-class layer at M = 16 / 64 / 256 / 1024 / 4096.  Seeded
     synthetic inputs (activations quantized per row on the host); weights rotate over
     copies totalling at least 512 MiB."""
     rot = 512 << 20
