@@ -1304,6 +1304,15 @@ int tiled_make_plan(int M, int N, int K, int mode, int variant, int grid, TiledP
       const long k = 256 / T;
       if (T * k >= 200 && Gk % k == 0) grid = (int)(T * k);
     }
+    // short K (at most 32 k-blocks) on the four-wave 128 x 128 tiles with fp16 activations
+    // (or rows rewritten in fp16): whole pieces even when they fill only 160-199 compute
+    // units, since a stream-K stripe's fixed cost weighs more against so short a tile
+    // (1.02-1.09x at M = 128 / 256 on 4096 x 11008 and 4096 x 12288)
+    if (T < 200 && grid == 256 && Gk <= 32 && v.MT == 8 && v.NTW == 2 && v.NWV == 4 &&
+        (mode == W_SYM || mode == W_ASYM || mode == W_SYM64 || mode == W_ASYM64)) {
+      const long k = 256 / T;
+      if (T * k >= 160 && Gk % k == 0) grid = (int)(T * k);
+    }
   }
   if ((long long)grid > (long long)T * Gk) grid = (int)(T * Gk);  // at least one unit each
   q.args.grid = grid;
