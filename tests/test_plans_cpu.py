@@ -132,10 +132,9 @@ def test_workspace_query_covers_the_fp8_and_mxfp4_plans():
     assert w4.w4a16_workspace_bytes(16, 28672, 8192) < need
 
 
-def test_short_k_whole_piece_grids(lib):
+def test_short_k_whole_piece_grids():
     """Four-wave 128 x 128 tiles on short K (at most 32 k-blocks) take whole pieces when
     they fill 160-199 compute units; longer K keeps the stream-K stripes."""
-    import w4a16_mixed_precision_offline_amd as w4
     d = w4.w4a16_gemm_describe(128, 12288, 4096, 128)       # 96 tiles, two pieces each
     assert d["name"] == "tiled_bm128_bn128_s3" and d["workgroups"] == 192
     d = w4.w4a16_gemm_describe(256, 12288, 4096, 128)       # 192 tiles, whole K
